@@ -1,0 +1,253 @@
+/*
+ * snack.h -- C ABI of a truly sparse linear layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer follows "Beyond Masked Sparsity: SNACK Enables Truly Sparse
+ * Neural Networks on GPU" (Abstract): the weight W (M x K, out x in) is kept
+ * only as its nonzero connections in COO form (row, col, value), forward and
+ * backward products touch only those nonzeros, and connections can be
+ * restructured (dynamic sparse training).  The page gives the operations in
+ * words; their exact forms are stated below with each entry point.
+ *
+ * Conventions shared by every entry point
+ *   - COO: row[k], col[k] are int32 device arrays of length nnz, strictly
+ *     increasing in the linear index row*K + col (sorted row-major, no
+ *     duplicates).  0 <= row < M, 0 <= col < K.
+ *   - dtype: values and activations share one element type, SNACK_F32
+ *     (float) or SNACK_BF16 (raw bfloat16 bits, uint16).  Products
+ *     accumulate in fp32 and round once (to nearest even) to the output type.
+ *   - layout: activations of F features and batch B are either batch-major
+ *     (B x F, element [b*F + f]) or node-major (F x B, element [f*B + b]).
+ *     Outputs use the same layout as the inputs.
+ *   - memory: every array argument is caller-owned device memory unless
+ *     stated otherwise; the library never allocates device memory and keeps
+ *     no global device state.  Plans are caller-owned host structs.
+ *   - streams: `stream` is a hipStream_t (NULL = the null stream).  All
+ *     calls are stream-ordered and asynchronous, except snack_coo_prepare
+ *     and snack_prune_regrow, which read a few bytes back and synchronise
+ *     the stream before returning.
+ *   - errors: a negative snack_status.  Argument errors are detected on the
+ *     host before anything is launched and leave every output untouched.
+ *     Nothing aborts or prints.
+ *   - concurrency: calls that share a plan's arena, or a workspace, must
+ *     not overlap (they write the same scratch).
+ */
+#ifndef SNACK_H_
+#define SNACK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SNACK_API __attribute__((visibility("default")))
+#else
+#define SNACK_API
+#endif
+
+typedef int32_t snack_status;
+
+#define SNACK_OK 0
+#define SNACK_E_NULL (-1)          /* a required pointer is NULL */
+#define SNACK_E_SHAPE (-2)         /* M, K, B, nnz or tile size out of range */
+#define SNACK_E_DTYPE (-3)         /* unknown dtype */
+#define SNACK_E_LAYOUT (-4)        /* unknown layout */
+#define SNACK_E_COO_RANGE (-5)     /* a COO index lies outside [0,M) x [0,K) */
+#define SNACK_E_COO_ORDER (-6)     /* COO not strictly increasing (unsorted or duplicate) */
+#define SNACK_E_NAN (-7)           /* a NaN value where magnitudes are compared */
+#define SNACK_E_COUNT (-8)         /* n_drop > nnz or n_drop > M*K - nnz */
+#define SNACK_E_WORKSPACE (-9)     /* arena / workspace too small */
+#define SNACK_E_OVERFLOW (-10)     /* a size exceeds the int32 index range */
+#define SNACK_E_HIP (-11)          /* a HIP launch or runtime call failed */
+#define SNACK_E_NOT_PREPARED (-12) /* the plan has not been prepared */
+
+typedef enum { SNACK_F32 = 0, SNACK_BF16 = 1 } snack_dtype;
+typedef enum { SNACK_BATCH_MAJOR = 0, SNACK_NODE_MAJOR = 1 } snack_layout;
+
+/* Derived arrays of a prepared plan (see snack_plan_array). */
+typedef enum {
+  SNACK_ARR_ROW_PTR = 0,     /* int32 [M+1]   row-segment offsets */
+  SNACK_ARR_RPART_SEG = 1,   /* int32 [P_row+1] tile start: segment (row) */
+  SNACK_ARR_RPART_NZ = 2,    /* int32 [P_row+1] tile start: entry */
+  SNACK_ARR_RSPLIT = 3,      /* int32 [3*n_split_row] (row, first tile, last tile) */
+  SNACK_ARR_COL_PTR = 4,     /* int32 [K+1]   column-segment offsets */
+  SNACK_ARR_PERM = 5,        /* int32 [nnz]   row-major position of the i-th entry in (col,row) order */
+  SNACK_ARR_ROW_T = 6,       /* int32 [nnz]   row[perm[i]] */
+  SNACK_ARR_CPART_SEG = 7,   /* int32 [P_col+1] */
+  SNACK_ARR_CPART_NZ = 8,    /* int32 [P_col+1] */
+  SNACK_ARR_CSPLIT = 9,      /* int32 [3*n_split_col] */
+  SNACK_ARR_COUNT_ = 10
+} snack_array;
+
+#define SNACK_PLAN_SLOTS 16
+
+/*
+ * Plan: the prepared topology of one COO weight.  Filled by snack_plan_init
+ * (sizes) and snack_coo_prepare (derived arrays in the caller's arena).
+ * The struct is plain data; copy it freely, but the arrays live in `arena`.
+ */
+typedef struct snack_plan {
+  int32_t M, K;              /* W is M x K (out_features x in_features) */
+  int64_t nnz;
+  int32_t max_batch;         /* largest B a product call on this plan may use */
+  int32_t tile_row;          /* work items (entries + row ends) per row-view tile */
+  int32_t tile_col;          /* work items per column-view tile */
+  int32_t P_row, P_col;      /* number of tiles of each view */
+  int32_t n_split_row;       /* rows split across tiles (set by prepare) */
+  int32_t n_split_col;       /* columns split across tiles (set by prepare) */
+  int32_t prepared;          /* 1 after a successful snack_coo_prepare */
+  const int32_t* row;        /* device COO recorded by prepare (not owned) */
+  const int32_t* col;
+  void* arena;               /* device arena recorded by prepare (not owned) */
+  size_t arena_bytes;        /* bytes the arena must provide (set by init) */
+  size_t off[SNACK_PLAN_SLOTS]; /* byte offsets of the arrays in the arena */
+} snack_plan;
+
+/* Library version (major*10000 + minor*100 + patch) and sizeof(snack_plan),
+ * for bindings that mirror the struct. */
+SNACK_API int32_t snack_version(void);
+SNACK_API size_t snack_plan_sizeof(void);
+
+/* Human-readable text of a status code (static storage). */
+SNACK_API const char* snack_status_str(snack_status s);
+
+/*
+ * snack_plan_init -- host only, no device work.
+ * Computes tile sizes, tile counts and the arena layout for a weight of
+ * shape M x K with nnz nonzeros, for product calls with B <= max_batch.
+ * tile_items = 0 picks the tile size automatically (a power of two in
+ * [128, 2048] giving at most ~2048 tiles); otherwise it must lie in
+ * [1, 2048] and is used for both views.
+ * Errors: SNACK_E_NULL, SNACK_E_SHAPE (M<1, K<1, nnz<0, nnz>M*K,
+ * max_batch<1, bad tile), SNACK_E_OVERFLOW (nnz + max(M,K) >= 2^31).
+ */
+SNACK_API snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz,
+                             int32_t max_batch, int32_t tile_items);
+
+/*
+ * snack_coo_prepare -- the "device row-segment offsets and load-balanced
+ * partition" of the layer, plus the column view used by the transpose
+ * product.
+ *
+ * Builds, on the device, in `arena` (>= plan->arena_bytes bytes):
+ *   row_ptr[M+1]      row_ptr[r] = number of entries in rows < r;
+ *   row-view tiles    the merge path of row ends and entries cut every
+ *                     tile_row items, each cut moved back to the start of its
+ *                     row unless that row has >= tile_row entries (so only
+ *                     long rows are ever split across tiles);
+ *   split list        for each split row: (row, first tile, last tile);
+ *   col_ptr[K+1], perm[nnz], row_t[nnz]  the column view: entries in stable
+ *                     (col, row) order; perm[i] is the row-major position of
+ *                     the i-th one and row_t[i] its row;
+ *   column-view tiles and split list, as for rows.
+ * The load balancing answers the imbalance the "Two Lotteries" page
+ * describes (section on who does the work): every tile gets about the same
+ * number of entries + segment ends, whatever the row lengths.
+ * Validates the COO first: SNACK_E_COO_RANGE / SNACK_E_COO_ORDER.
+ * Reads back 12 bytes and synchronises `stream`.  Records row, col and
+ * arena in the plan; they must stay alive and unchanged while the plan is
+ * used.  Re-run after every change of the sparsity pattern.
+ */
+SNACK_API snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32_t* col,
+                               void* arena, size_t arena_bytes, void* stream);
+
+/* Device pointer and element count of a derived array of a prepared plan
+ * (NULL if not prepared or `which` is unknown). */
+SNACK_API const void* snack_plan_array(const snack_plan* plan, int32_t which, int64_t* count);
+
+/*
+ * snack_spmm_fwd -- forward product of the layer, Y = X W^T:
+ *     Y[b, r] = sum_{k : row[k] = r} v[k] * X[b, col[k]]
+ * for b < B, r < M; rows without entries give exactly 0.  X has K features,
+ * Y has M features, both in `layout`.  Y is overwritten (no bias, no beta).
+ * Requires a prepared plan and 0 <= B <= plan->max_batch.
+ */
+SNACK_API snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                            const void* X, snack_layout layout, int32_t B, void* Y,
+                            void* stream);
+
+/*
+ * snack_spmm_bwd_input -- gradient with respect to the layer input,
+ * dX = dY W, kept sparse (only the nonzeros are touched):
+ *     dX[b, c] = sum_{k : col[k] = c} v[k] * dY[b, row[k]]
+ * computed over the column view without atomics; columns without entries
+ * give exactly 0.  dY has M features, dX has K features.
+ */
+SNACK_API snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                  const void* dY, snack_layout layout, int32_t B, void* dX,
+                                  void* stream);
+
+/*
+ * snack_sddmm_grad_vals -- gradient with respect to the stored values
+ * only, (dY^T X) sampled at the nonzeros:
+ *     dV[k] = sum_{b < B} dY[b, row[k]] * X[b, col[k]]
+ * dV (nnz elements of `dtype`, same order as the values) is overwritten;
+ * B = 0 gives zeros.
+ */
+SNACK_API snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const void* X,
+                                   snack_dtype dtype, snack_layout layout, int32_t B,
+                                   void* dvals, void* stream);
+
+/*
+ * snack_drop_count -- number of connections one restructuring step
+ * replaces: round half up of nnz * frac_ppm / 10^6 (frac in parts per
+ * million).  Returns -1 for negative arguments.
+ */
+SNACK_API int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm);
+
+/* Workspace bytes snack_prune_regrow needs for these sizes. */
+SNACK_API snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                          size_t* bytes);
+
+/*
+ * snack_prune_regrow -- one restructuring step of dynamic sparse training
+ * (the "restructuring connections" of the SNACK abstract; the page names
+ * the operation, the rule below is this library's):
+ *   1. magnitude key of entry k = its value's bits with the sign cleared
+ *      (-0 == +0); NaN is an error (SNACK_E_NAN);
+ *   2. the n_drop entries smallest in (magnitude key, row*K+col) are dropped;
+ *      survivors keep their values;
+ *   3. n_drop new positions are grown: with SplitMix64 (Steele, Lea & Flood,
+ *      OOPSLA 2014), x_i = output i of a generator seeded with
+ *      s = output `step` of a generator seeded with `seed`;
+ *      p_i = floor(x_i * (M*K) / 2^64); p_i is taken if it is not in the
+ *      support before this step and was not taken before, until n_drop are
+ *      taken;
+ *   4. the new COO (survivors + grown, value 0) is written back in place into
+ *      row/col/vals, sorted row-major; nnz is unchanged.
+ * dropped_lin / grown_lin (nullable, int64 [n_drop]) receive the dropped and
+ * grown linear indices in increasing order.  ws must hold
+ * snack_prune_regrow_workspace bytes.  Re-run snack_coo_prepare afterwards.
+ * Errors: SNACK_E_COUNT, SNACK_E_NAN (COO left unchanged), SNACK_E_WORKSPACE.
+ * Synchronises `stream`.
+ */
+SNACK_API snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
+                                int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * GELU with the exact error function, h = z * Phi(z), and its backward
+ * dz = dh * (Phi(z) + z * phi(z)), elementwise over n fp32 values (the
+ * nonlinearity between the two sparse layers of a GPT-2-shaped MLP block).
+ */
+SNACK_API snack_status snack_gelu_fwd(const float* z, float* h, int64_t n, void* stream);
+SNACK_API snack_status snack_gelu_bwd(const float* z, const float* dh, float* dz, int64_t n,
+                            void* stream);
+
+/*
+ * Dense baselines for comparison (the "Dense+Mask" and fully dense layers
+ * the SNACK abstract measures against): Y = X (W .* mask)^T with a dense
+ * row-major W (M x K, dtype) and an optional uint8 mask (M x K, nonzero =
+ * keep; NULL = plain dense layer).  Batch-major X (B x K) and Y (B x M).
+ */
+SNACK_API snack_status snack_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dtype, int32_t M,
+                             int32_t K, const void* X, int32_t B, void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SNACK_H_ */

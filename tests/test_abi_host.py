@@ -1,0 +1,118 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load, export every entry point include/snack.h declares,
+agree with the binding on the plan struct, and reject bad arguments on the
+host before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "snack.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"SNACK_API\s+[\w\s\*]*?\b(snack_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def snk():
+    import unstructured_sparse_nn_amd as m
+    return m
+
+
+def test_library_exports_every_declared_symbol(snk):
+    from unstructured_sparse_nn_amd import binding
+    names = declared_symbols()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_plan_struct_matches(snk):
+    assert ctypes.sizeof(snk.SnackPlan) == snk.snack_plan_sizeof()
+    assert snk.snack_version() >= 100
+
+
+def test_plan_init_sizes(snk):
+    p = snk.snack_plan_init(4096, 4096, 838861, 32)
+    assert p.tile_row == 512 and p.P_row == -(-(4096 + 838861) // 512)
+    assert p.P_row <= 2048 and p.arena_bytes > 0
+    p = snk.snack_plan_init(200000, 200000, 2400000, 128)
+    assert p.tile_row == 2048
+    p = snk.snack_plan_init(7, 5, 0, 1, tile_items=3)
+    assert p.tile_row == 3 and p.P_row == 3 and p.P_col == 2
+    offs = list(p.off)[:10]
+    assert offs == sorted(offs)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 1, 1, 0), -2), ((4, 0, 1, 1, 0), -2), ((4, 4, -1, 1, 0), -2),
+    ((4, 4, 17, 1, 0), -2), ((4, 4, 1, 0, 0), -2), ((4, 4, 1, 1, 4096), -2),
+    ((2**31 - 1, 1, 1, 1, 0), -10),
+])
+def test_plan_init_rejects(snk, args, status):
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_plan_init(*args)
+    assert e.value.status == status
+
+
+def test_products_reject_unprepared_plan(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    for fn in (b.snack_spmm_fwd, b.snack_spmm_bwd_input):
+        with pytest.raises(snk.SnackError) as e:
+            fn(p, 0x1000, 0x2000, 0, 1, 0x3000, stream=0, dtype=b.F32)
+        assert e.value.status == -12
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_sddmm_grad_vals(p, 0x1000, 0x2000, 0, 1, 0x3000, stream=0, dtype=b.F32)
+    assert e.value.status == -12
+    assert b.raw_status("snack_spmm_fwd", None, 1, 0, 1, 0, 1, 1, None) == -1
+
+
+def test_prepare_rejects_small_arena_before_any_launch(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_coo_prepare(p, 0x1000, 0x2000, 0x3000, stream=0, arena_bytes=16)
+    assert e.value.status == -9
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_coo_prepare(p, None, 0x2000, 0x3000, stream=0, arena_bytes=p.arena_bytes)
+    assert e.value.status == -1
+
+
+def test_drop_count_and_prune_argument_checks(snk, orc):
+    from unstructured_sparse_nn_amd import binding as b
+    for nnz, ppm in [(6554, 100000), (235930, 300000), (23593, 300000), (5, 500000), (0, 7),
+                     (838861, 300000), (4508877, 100000)]:
+        assert snk.snack_drop_count(nnz, ppm) == orc.drop_count(nnz, ppm)
+    assert snk.snack_drop_count(-1, 5) == -1
+    # n_drop larger than nnz, or than the free positions: rejected on the host
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_prune_regrow(0x10, 0x20, 0x30, 4, 4, 3, 4, 0, 0, None, None, 0x40, stream=0,
+                             ws_bytes=1 << 20, dtype=b.F32)
+    assert e.value.status == -8
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_prune_regrow(0x10, 0x20, 0x30, 4, 4, 15, 2, 0, 0, None, None, 0x40, stream=0,
+                             ws_bytes=1 << 20, dtype=b.F32)
+    assert e.value.status == -8
+    # n_drop == 0 is a no-op that touches nothing
+    b.snack_prune_regrow(None, None, None, 4, 4, 3, 0, 0, 0, None, None, None, stream=0,
+                         ws_bytes=0, dtype=b.F32)
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_prune_regrow(0x10, 0x20, 0x30, 4, 4, 3, 1, 0, 0, None, None, 0x40, stream=0,
+                             ws_bytes=0, dtype=7)
+    assert e.value.status == -3
+    assert snk.snack_prune_regrow_workspace(256, 256, 6554, 655) > 0
+
+
+def test_status_strings(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    for code in b.STATUS:
+        assert snk.status_str(code) and snk.status_str(code) != "unknown status"

@@ -1,0 +1,395 @@
+"""GPU parity: every entry point of the HIP library against the fp64 oracle.
+
+Integer outputs (offsets, tiles, split lists, column view, post-step COO,
+dropped/grown lists) must be bit-exact; float outputs must satisfy
+|gpu - oracle| <= tol * S per output, S = sum of |term| (tol 1e-5 for fp32,
+1e-2 for bf16 values with fp32 accumulation).
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from gpuhelp import assert_within, from_dev, to_dev, topology, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only collection
+    pytest.skip("no GPU", allow_module_level=True)
+
+import unstructured_sparse_nn_amd as snk  # noqa: E402
+from unstructured_sparse_nn_amd import binding as B  # noqa: E402
+
+
+# ------------------------------------------------------------------ inputs
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    if name == "single":
+        return synth.single_layer()
+    if name.startswith("square"):
+        _, sp, b = name.split("_")
+        return synth.inference_layer(sparsity=float(sp), B=int(b))
+    if name.startswith("gpt2"):
+        return synth.gpt2_mlp(sparsity=float(name.split("_")[1]))
+    if name.startswith("llama"):
+        _, which, b = name.split("_")
+        return synth.llama_proj(which=which, B=int(b))
+    if name == "graph":
+        return synth.graph_layer()
+    raise KeyError(name)
+
+
+def check_prepare(orc, w, topo):
+    rp = orc.row_ptr(w.M, w.row)
+    assert np.array_equal(topo.array("row_ptr").cpu().numpy(), rp)
+    cp, perm, rt = orc.csc(w.K, w.row, w.col)
+    assert np.array_equal(topo.array("col_ptr").cpu().numpy(), cp)
+    if w.nnz:
+        assert np.array_equal(topo.array("perm").cpu().numpy(), perm)
+        assert np.array_equal(topo.array("row_t").cpu().numpy(), rt)
+    for view, ptr, T in (("r", rp, topo.plan.tile_row), ("c", cp, topo.plan.tile_col)):
+        ref = orc.partition(ptr, T)
+        assert ref["P"] == (topo.plan.P_row if view == "r" else topo.plan.P_col)
+        assert np.array_equal(topo.array(view + "part_seg").cpu().numpy(), ref["part_seg"])
+        assert np.array_equal(topo.array(view + "part_nz").cpu().numpy(), ref["part_nz"])
+        split = topo.array(view + "split").cpu().numpy().reshape(-1, 3)
+        exp = np.stack([ref["split_seg"], ref["split_first"], ref["split_last"]], 1)
+        assert np.array_equal(split, exp.reshape(-1, 3))
+
+
+def run_products(orc, w, X, dY, dt, layout, Bsz, tile=0, sddmm=True, repeat_check=False):
+    nm = layout == "node"
+    lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
+    topo = topology(w, max(Bsz, 1), tile)
+    vals = to_dev(w.vals, dt)
+    Xd, dYd = to_dev(X.data, dt), to_dev(dY.data, dt)
+    v64 = w.vals_f64()
+    Y = topo.fwd(vals, Xd, Bsz, lay)
+    ref, S = orc.spmm_fwd(w.M, w.K, w.row, w.col, v64, Bsz, X.f64(), nm)
+    assert_within(from_dev(Y, dt), ref, S, dt, "fwd")
+    dX = topo.bwd_input(vals, dYd, Bsz, lay)
+    ref, S = orc.spmm_bwd_input(w.M, w.K, w.row, w.col, v64, Bsz, dY.f64(), nm)
+    assert_within(from_dev(dX, dt), ref, S, dt, "bwd_input")
+    dV = None
+    if sddmm:
+        dV = topo.grad_vals(dYd, Xd, Bsz, lay)
+        ref, S = orc.sddmm(w.M, w.K, w.row, w.col, Bsz, dY.f64(), X.f64(), nm)
+        assert_within(from_dev(dV, dt), ref, S, dt, "sddmm")
+    if repeat_check:  # bitwise reproducible: no order-dependent atomics
+        assert torch.equal(topo.fwd(vals, Xd, Bsz, lay), Y)
+        assert torch.equal(topo.bwd_input(vals, dYd, Bsz, lay), dX)
+        if sddmm:
+            assert torch.equal(topo.grad_vals(dYd, Xd, Bsz, lay), dV)
+    return topo
+
+
+# --------------------------------------------------------------- prepare
+PREP_CASES = [
+    ("single", 0), ("single", 16), ("single", 1), ("square_0.95_1", 0), ("square_0.99_1", 0),
+    ("llama_up_1", 0), ("llama_down_1", 0), ("graph", 0),
+]
+
+
+@pytest.mark.parametrize("name,tile", PREP_CASES)
+def test_prepare_matches_oracle(orc, name, tile):
+    w = workload(name).weights[0]
+    topo = topology(w, 1, tile)
+    check_prepare(orc, w, topo)
+
+
+EDGE = [  # (M, K, nnz, tile)
+    (1, 1, 0, 0), (1, 1, 1, 0), (5, 7, 0, 2), (1, 64, 64, 0), (1, 64, 64, 5), (64, 1, 64, 3),
+    (13, 11, 143, 4), (300, 40, 30, 7), (257, 255, 3000, 64), (1000, 3, 2500, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,tile", EDGE)
+def test_prepare_edge_cases(orc, M, K, nnz, tile):
+    w = synth.random_case(21, M, K, nnz, 1).weights[0]
+    check_prepare(orc, w, topology(w, 1, tile))
+
+
+def test_prepare_rejects_bad_coo():
+    row = to_dev(np.array([0, 0, 1], np.int32))
+    for col, status in (([1, 1, 0], -6), ([2, 1, 0], -6), ([0, 5, 0], -5), ([-1, 1, 0], -5)):
+        c = to_dev(np.array(col, np.int32))
+        plan = snk.snack_plan_init(4, 4, 3, 1)
+        arena = torch.empty(plan.arena_bytes, dtype=torch.uint8, device="cuda")
+        with pytest.raises(snk.SnackError) as e:
+            snk.snack_coo_prepare(plan, row, c, arena)
+        assert e.value.status == status
+    rowbad = to_dev(np.array([1, 0, 2], np.int32))
+    c = to_dev(np.array([0, 1, 2], np.int32))
+    plan = snk.snack_plan_init(4, 4, 3, 1)
+    arena = torch.empty(plan.arena_bytes, dtype=torch.uint8, device="cuda")
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_coo_prepare(plan, rowbad, c, arena)
+    assert e.value.status == -6
+
+
+# --------------------------------------------------------------- products
+SMALL = [  # (M, K, nnz, B, dtype, layout, tile)
+    (1, 1, 1, 1, "f32", "batch", 0),
+    (1, 1, 0, 3, "f32", "batch", 0),
+    (5, 7, 0, 2, "bf16", "node", 2),
+    (1, 64, 64, 4, "f32", "batch", 5),      # one dense row split over many tiles
+    (64, 1, 64, 4, "f32", "node", 3),       # one dense column split over many tiles
+    (13, 11, 143, 3, "f32", "batch", 4),    # full density, odd batch
+    (37, 53, 200, 1, "bf16", "batch", 0),
+    (300, 40, 30, 2, "f32", "batch", 7),    # mostly empty rows
+    (257, 255, 3000, 8, "bf16", "batch", 64),
+    (257, 255, 3000, 12, "bf16", "node", 0),
+    (511, 129, 9000, 32, "bf16", "node", 256),
+    (511, 129, 9000, 32, "f32", "batch", 256),
+    (100, 333, 8000, 33, "f32", "node", 100),
+    (100, 333, 8000, 64, "f32", "node", 0),
+    (100, 333, 8000, 5, "bf16", "batch", 1),
+    (1000, 3, 2500, 16, "bf16", "node", 128),
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt,layout,tile", SMALL)
+def test_products_small_and_ragged(orc, M, K, nnz, Bsz, dt, layout, tile):
+    w = synth.random_case(5, M, K, nnz, Bsz, dt, layout)
+    run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile, repeat_check=True)
+
+
+def test_products_skewed_rows_with_splits(orc):
+    """Rows of 1 .. 3000 entries, tiles of 64 items: many rows span several
+    tiles and go through the carry fix-up."""
+    M, K = 400, 3000
+    deg = synth.rank_profile(M, K, 60000, 1.3)
+    rng = np.random.default_rng(3)
+    lin = np.concatenate([r * K + np.sort(rng.choice(K, d, replace=False))
+                          for r, d in enumerate(rng.permutation(deg))])
+    for dt, layout, Bsz in (("f32", "batch", 3), ("bf16", "node", 16), ("f32", "node", 32)):
+        w = synth.random_case(7, M, K, lin.size, Bsz, dt, layout, positions=lin)
+        topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile=64,
+                            repeat_check=True)
+        assert topo.plan.n_split_row > 0
+
+
+@pytest.mark.parametrize("name,B", [("single", 4)])
+def test_single_layer_config(orc, name, B):
+    w = workload(name)
+    run_products(orc, w.weights[0], w.X[0], w.dY[0], "f32", "batch", B, repeat_check=True)
+
+
+@pytest.mark.parametrize("sp", ["0.95", "0.99"])
+@pytest.mark.parametrize("Bsz", [1, 8, 32])
+def test_square_inference_configs(orc, sp, Bsz):
+    w = workload(f"square_{sp}_{Bsz}")
+    run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz, repeat_check=True)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+@pytest.mark.parametrize("Bsz", [1, 4, 16])
+def test_llama_projection_configs(orc, which, Bsz):
+    w = workload(f"llama_{which}_{Bsz}")
+    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz)
+    assert topo.plan.n_split_row > 0  # dense rows longer than a tile
+
+
+def test_graph_config(orc):
+    w = workload("graph")
+    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "f32", "node", 128, sddmm=True)
+    assert topo.plan.n_split_row > 0
+
+
+@pytest.mark.parametrize("sp", ["0.9", "0.99"])
+def test_gpt2_mlp_chain(orc, sp):
+    """fwd W1 -> GELU -> fwd W2, then the full backward, each op gated on the
+    oracle with the GPU's own intermediates as inputs."""
+    w = workload(f"gpt2_{sp}")
+    W1, W2 = w.weights
+    Bsz = w.B
+    X, G = w.X[0], w.dY[1]
+    t1, t2 = topology(W1, Bsz), topology(W2, Bsz)
+    v1, v2 = to_dev(W1.vals), to_dev(W2.vals)
+    Xd, Gd = to_dev(X.data), to_dev(G.data)
+    Z = t1.fwd(v1, Xd, Bsz)
+    ref, S = orc.spmm_fwd(W1.M, W1.K, W1.row, W1.col, W1.vals_f64(), Bsz, X.f64())
+    assert_within(from_dev(Z, "f32"), ref, S, "f32", "fwd W1")
+    H = torch.empty_like(Z)
+    snk.snack_gelu_fwd(Z, H)
+    z64 = from_dev(Z, "f32")
+    np.testing.assert_allclose(from_dev(H, "f32"), orc.gelu(z64), rtol=2e-6, atol=1e-7)
+    Y = t2.fwd(v2, H, Bsz)
+    h64 = from_dev(H, "f32")
+    ref, S = orc.spmm_fwd(W2.M, W2.K, W2.row, W2.col, W2.vals_f64(), Bsz, h64)
+    assert_within(from_dev(Y, "f32"), ref, S, "f32", "fwd W2")
+    dH = t2.bwd_input(v2, Gd, Bsz)
+    ref, S = orc.spmm_bwd_input(W2.M, W2.K, W2.row, W2.col, W2.vals_f64(), Bsz, G.f64())
+    assert_within(from_dev(dH, "f32"), ref, S, "f32", "dX W2")
+    dV2 = t2.grad_vals(Gd, H, Bsz)
+    ref, S = orc.sddmm(W2.M, W2.K, W2.row, W2.col, Bsz, G.f64(), h64)
+    assert_within(from_dev(dV2, "f32"), ref, S, "f32", "dW W2")
+    dZ = torch.empty_like(Z)
+    snk.snack_gelu_bwd(Z, dH, dZ)
+    dh64 = from_dev(dH, "f32")
+    np.testing.assert_allclose(from_dev(dZ, "f32"), orc.gelu_bwd(z64, dh64), rtol=4e-6,
+                               atol=1e-6 * np.abs(dh64).max())
+    dX = t1.bwd_input(v1, dZ, Bsz)
+    dz64 = from_dev(dZ, "f32")
+    ref, S = orc.spmm_bwd_input(W1.M, W1.K, W1.row, W1.col, W1.vals_f64(), Bsz, dz64)
+    assert_within(from_dev(dX, "f32"), ref, S, "f32", "dX W1")
+    dV1 = t1.grad_vals(dZ, Xd, Bsz)
+    ref, S = orc.sddmm(W1.M, W1.K, W1.row, W1.col, Bsz, dz64, X.f64())
+    assert_within(from_dev(dV1, "f32"), ref, S, "f32", "dW W1")
+
+
+def test_zero_batch_and_empty_weight(orc):
+    w = synth.random_case(2, 30, 20, 50, 1).weights[0]
+    topo = topology(w, 4)
+    vals = to_dev(w.vals)
+    dV = torch.full((w.nnz,), 7.0, device="cuda")
+    topo.grad_vals(torch.empty(0, device="cuda"), torch.empty(0, device="cuda"), 0, out=dV)
+    assert torch.count_nonzero(dV) == 0
+    Y = torch.full((0,), 1.0, device="cuda")
+    topo.fwd(vals, torch.empty(0, device="cuda"), 0, out=Y)
+    e = synth.random_case(2, 30, 20, 0, 3)
+    topo = topology(e.weights[0], 3)
+    Y = torch.full((3 * 30,), 5.0, device="cuda")
+    topo.fwd(torch.empty(0, device="cuda"), to_dev(e.X[0].data), 3, out=Y)
+    assert torch.count_nonzero(Y) == 0
+    with pytest.raises(snk.SnackError) as ex:
+        topo.fwd(torch.empty(0, device="cuda"), to_dev(e.X[0].data), 4, out=Y)
+    assert ex.value.status == -2
+
+
+# --------------------------------------------------------------- prune / regrow
+def gpu_prune(w, dt, n_drop, seed, step, vals=None):
+    row, col = to_dev(w.row), to_dev(w.col)
+    v = to_dev(w.vals if vals is None else vals, dt)
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+                     dtype=torch.uint8, device="cuda")
+    dl = torch.empty(max(n_drop, 1), dtype=torch.int64, device="cuda")
+    gl = torch.empty(max(n_drop, 1), dtype=torch.int64, device="cuda")
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, seed, step, dl, gl, ws)
+    return row, col, v, dl[:n_drop], gl[:n_drop]
+
+
+def check_prune(orc, w, dt, ppm, seed, step, vals=None):
+    n_drop = orc.drop_count(w.nnz, ppm)
+    vals = w.vals if vals is None else vals
+    ref = orc.prune_regrow(w.M, w.K, w.row, w.col, vals, dt, n_drop, seed, step)
+    assert ref["rc"] == 0
+    row, col, v, dl, gl = gpu_prune(w, dt, n_drop, seed, step, vals)
+    assert np.array_equal(row.cpu().numpy(), ref["row"])
+    assert np.array_equal(col.cpu().numpy(), ref["col"])
+    if dt == "bf16":
+        got = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got = v.cpu().numpy().view(np.uint32)
+        ref["vals"] = np.asarray(ref["vals"], np.float32).view(np.uint32)
+    assert np.array_equal(got, ref["vals"])
+    assert np.array_equal(dl.cpu().numpy(), ref["dropped"])
+    assert np.array_equal(gl.cpu().numpy(), ref["grown"])
+    return row, col
+
+
+def test_prune_regrow_single_layer(orc):
+    w = workload("single").weights[0]
+    check_prune(orc, w, "f32", 100000, 0, 1)
+
+
+@pytest.mark.parametrize("sp", ["0.9", "0.99"])
+def test_prune_regrow_gpt2(orc, sp):
+    for W in workload(f"gpt2_{sp}").weights:
+        row, col = check_prune(orc, W, "f32", 300000, 0, 5)
+        # the restructured COO prepares exactly as the oracle says
+        w2 = synth.SparseWeight(W.M, W.K, row.cpu().numpy(), col.cpu().numpy(), W.vals, "f32")
+        check_prepare(orc, w2, topology(w2, 1))
+
+
+def test_prune_regrow_bf16_ties_and_signed_zero(orc):
+    w = synth.random_case(8, 300, 200, 5000, 1, "bf16").weights[0]
+    vals = w.vals.copy()
+    vals[::7] = vals[3]                    # many exact ties
+    vals[1::11] = np.uint16(0x8000)        # -0
+    vals[2::13] = np.uint16(0)             # +0
+    check_prune(orc, w, "bf16", 250000, 42, 9, vals)
+
+
+def test_prune_regrow_square_bf16(orc):
+    w = workload("square_0.95_1").weights[0]
+    check_prune(orc, w, "bf16", 300000, 3, 1)
+
+
+def test_prune_regrow_nearly_full_needs_several_chunks(orc):
+    """Only a few free positions: the candidate stream runs over many chunks."""
+    M, K = 40, 60
+    nnz = M * K - 30
+    w = synth.random_case(9, M, K, nnz, 1).weights[0]
+    check_prune(orc, w, "f32", 10000, 5, 2)
+
+
+def test_prune_regrow_rejects_nan_and_keeps_coo():
+    w = synth.random_case(4, 64, 64, 400, 1).weights[0]
+    vals = w.vals.copy()
+    vals[17] = np.nan
+    row, col = to_dev(w.row), to_dev(w.col)
+    v = to_dev(vals)
+    ws = torch.empty(snk.snack_prune_regrow_workspace(64, 64, 400, 40), dtype=torch.uint8,
+                     device="cuda")
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_prune_regrow(row, col, v, 64, 64, 400, 40, 1, 1, None, None, ws)
+    assert e.value.status == -7
+    assert np.array_equal(row.cpu().numpy(), w.row) and np.array_equal(col.cpu().numpy(), w.col)
+
+
+# --------------------------------------------------------------- aux
+def test_gelu_matches_oracle(orc):
+    z = torch.linspace(-8, 8, 100003, device="cuda")
+    h = torch.empty_like(z)
+    snk.snack_gelu_fwd(z, h)
+    z64 = z.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(h.cpu().numpy(), orc.gelu(z64), rtol=2e-6, atol=1e-7)
+    dh = torch.ones_like(z)
+    dz = torch.empty_like(z)
+    snk.snack_gelu_bwd(z, dh, dz)
+    np.testing.assert_allclose(dz.cpu().numpy(), orc.gelu_bwd(z64, np.ones_like(z64)),
+                               rtol=4e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("masked", [False, True])
+def test_dense_baseline(orc, dt, masked):
+    w = synth.random_case(6, 300, 1000, 30000, 5, dt)
+    wt = w.weights[0]
+    rng = np.random.default_rng(1)
+    Wd = (rng.standard_normal(300 * 1000) * 0.02).astype(np.float32)
+    if dt == "bf16":
+        Wd = synth.f32_to_bf16_bits(Wd)
+    mask = np.zeros(300 * 1000, np.uint8)
+    mask[wt.row.astype(np.int64) * 1000 + wt.col] = 1
+    Y = torch.empty(5 * 300, dtype=torch_dtype(dt), device="cuda")
+    snk.snack_dense_fwd(to_dev(Wd, dt), to_dev(mask) if masked else None, 300, 1000,
+                        to_dev(w.X[0].data, dt), 5, Y)
+    Wf = (synth.bf16_bits_to_f32(Wd) if dt == "bf16" else Wd).astype(np.float64)
+    Wf = Wf * (mask if masked else 1)
+    Xb = w.X[0].f64().reshape(5, 1000)
+    Wm = Wf.reshape(300, 1000)
+    assert_within(from_dev(Y, dt), Xb @ Wm.T, np.abs(Xb) @ np.abs(Wm).T, dt, "dense")
+
+
+def test_sparse_linear_autograd(orc):
+    w = workload("single")
+    wt = w.weights[0]
+    layer = snk.SparseLinear(256, 256, to_dev(wt.row), to_dev(wt.col), to_dev(wt.vals), 4)
+    x = to_dev(w.X[0].data).view(4, 256).requires_grad_(True)
+    y = layer(x)
+    g = to_dev(w.dY[0].data).view(4, 256)
+    y.backward(g)
+    ref, S = orc.spmm_fwd(256, 256, wt.row, wt.col, wt.vals_f64(), 4, w.X[0].f64())
+    assert_within(from_dev(y, "f32"), ref, S, "f32", "SparseLinear fwd")
+    ref, S = orc.spmm_bwd_input(256, 256, wt.row, wt.col, wt.vals_f64(), 4, w.dY[0].f64())
+    assert_within(from_dev(x.grad, "f32"), ref, S, "f32", "SparseLinear dX")
+    ref, S = orc.sddmm(256, 256, wt.row, wt.col, 4, w.dY[0].f64(), w.X[0].f64())
+    assert_within(from_dev(layer.vals.grad, "f32"), ref, S, "f32", "SparseLinear dV")
+    dropped, grown = layer.prune_regrow(100000, 1)
+    ref = orc.prune_regrow(256, 256, wt.row, wt.col, wt.vals, "f32", 655, 0, 1)
+    assert np.array_equal(grown.cpu().numpy(), ref["grown"])
+    assert np.array_equal(layer.topo.row.cpu().numpy(), ref["row"])

@@ -1,0 +1,223 @@
+"""ctypes binding of libsnack.so (include/snack.h), argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Array arguments
+are torch tensors on the GPU (their ``data_ptr()`` is passed), raw integer
+device addresses, or ``None`` for a NULL pointer.  The element type of values
+and activations is taken from the tensors (``torch.float32`` or
+``torch.bfloat16``); ``stream=None`` means torch's current stream.  A
+negative status raises :class:`SnackError`.  No arithmetic of the layer
+happens here: every step runs in the HIP library, and importing this module
+fails loudly when that library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsnack.so")
+
+F32, BF16 = 0, 1
+BATCH_MAJOR, NODE_MAJOR = 0, 1
+PLAN_SLOTS = 16
+
+ARRAYS = {"row_ptr": 0, "rpart_seg": 1, "rpart_nz": 2, "rsplit": 3, "col_ptr": 4, "perm": 5,
+          "row_t": 6, "cpart_seg": 7, "cpart_nz": 8, "csplit": 9}
+
+STATUS = {0: "SNACK_OK", -1: "SNACK_E_NULL", -2: "SNACK_E_SHAPE", -3: "SNACK_E_DTYPE",
+          -4: "SNACK_E_LAYOUT", -5: "SNACK_E_COO_RANGE", -6: "SNACK_E_COO_ORDER",
+          -7: "SNACK_E_NAN", -8: "SNACK_E_COUNT", -9: "SNACK_E_WORKSPACE",
+          -10: "SNACK_E_OVERFLOW", -11: "SNACK_E_HIP", -12: "SNACK_E_NOT_PREPARED"}
+
+
+class SnackError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class SnackPlan(ctypes.Structure):
+    """Mirror of ``struct snack_plan``."""
+    _fields_ = [("M", ctypes.c_int32), ("K", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("max_batch", ctypes.c_int32), ("tile_row", ctypes.c_int32),
+                ("tile_col", ctypes.c_int32), ("P_row", ctypes.c_int32),
+                ("P_col", ctypes.c_int32), ("n_split_row", ctypes.c_int32),
+                ("n_split_col", ctypes.c_int32), ("prepared", ctypes.c_int32),
+                ("row", ctypes.c_void_p), ("col", ctypes.c_void_p),
+                ("arena", ctypes.c_void_p), ("arena_bytes", ctypes.c_size_t),
+                ("off", ctypes.c_size_t * PLAN_SLOTS)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                            ctypes.c_size_t)
+    plan_p = ctypes.POINTER(SnackPlan)
+    sig = {
+        "snack_version": ([], i32),
+        "snack_plan_sizeof": ([], sz),
+        "snack_status_str": ([i32], ctypes.c_char_p),
+        "snack_plan_init": ([plan_p, i32, i32, i64, i32, i32], i32),
+        "snack_coo_prepare": ([plan_p, P, P, P, sz, P], i32),
+        "snack_plan_array": ([plan_p, i32, ctypes.POINTER(i64)], P),
+        "snack_spmm_fwd": ([plan_p, P, i32, P, i32, i32, P, P], i32),
+        "snack_spmm_bwd_input": ([plan_p, P, i32, P, i32, i32, P, P], i32),
+        "snack_sddmm_grad_vals": ([plan_p, P, P, i32, i32, i32, P, P], i32),
+        "snack_drop_count": ([i64, i32], i64),
+        "snack_prune_regrow_workspace": ([i32, i32, i64, i64, ctypes.POINTER(sz)], i32),
+        "snack_prune_regrow": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz, P], i32),
+        "snack_gelu_fwd": ([P, P, i64, P], i32),
+        "snack_gelu_bwd": ([P, P, P, i64, P], i32),
+        "snack_dense_fwd": ([P, P, i32, i32, i32, P, i32, P, P], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def status_str(status: int) -> str:
+    return _lib.snack_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise SnackError(status, what)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _dtype(*cands, dtype=None) -> int:
+    """Element type: explicit ``dtype``, else that of the first tensor given."""
+    if dtype is not None:
+        return dtype
+    import torch
+    for t in cands:
+        if t is None or isinstance(t, int):
+            continue
+        if t.dtype == torch.float32:
+            return F32
+        if t.dtype == torch.bfloat16:
+            return BF16
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError("no tensor to take the dtype from; pass dtype=")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def snack_version() -> int:
+    return _lib.snack_version()
+
+
+def snack_plan_sizeof() -> int:
+    return _lib.snack_plan_sizeof()
+
+
+def snack_plan_init(M: int, K: int, nnz: int, max_batch: int, tile_items: int = 0) -> SnackPlan:
+    plan = SnackPlan()
+    _check(_lib.snack_plan_init(ctypes.byref(plan), M, K, nnz, max_batch, tile_items),
+           "snack_plan_init")
+    return plan
+
+
+def snack_coo_prepare(plan: SnackPlan, row, col, arena, stream=None, arena_bytes=None):
+    if arena_bytes is None:
+        arena_bytes = arena.numel() * arena.element_size() if arena is not None and \
+            not isinstance(arena, int) else 0
+    _check(_lib.snack_coo_prepare(ctypes.byref(plan), _ptr(row), _ptr(col), _ptr(arena),
+                                  arena_bytes, _stream(stream)), "snack_coo_prepare")
+
+
+def snack_plan_array(plan: SnackPlan, which) -> tuple:
+    """(device address, element count) of a derived array; which is a name or id."""
+    w = ARRAYS[which] if isinstance(which, str) else int(which)
+    n = ctypes.c_int64(0)
+    addr = _lib.snack_plan_array(ctypes.byref(plan), w, ctypes.byref(n))
+    return addr, n.value
+
+
+def snack_spmm_fwd(plan, vals, X, layout, B, Y, stream=None, dtype=None):
+    dt = _dtype(vals, X, Y, dtype=dtype)
+    _check(_lib.snack_spmm_fwd(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), layout, B, _ptr(Y),
+                               _stream(stream)), "snack_spmm_fwd")
+
+
+def snack_spmm_bwd_input(plan, vals, dY, layout, B, dX, stream=None, dtype=None):
+    dt = _dtype(vals, dY, dX, dtype=dtype)
+    _check(_lib.snack_spmm_bwd_input(ctypes.byref(plan), _ptr(vals), dt, _ptr(dY), layout, B,
+                                     _ptr(dX), _stream(stream)), "snack_spmm_bwd_input")
+
+
+def snack_sddmm_grad_vals(plan, dY, X, layout, B, dvals, stream=None, dtype=None):
+    dt = _dtype(dvals, dY, X, dtype=dtype)
+    _check(_lib.snack_sddmm_grad_vals(ctypes.byref(plan), _ptr(dY), _ptr(X), dt, layout, B,
+                                      _ptr(dvals), _stream(stream)), "snack_sddmm_grad_vals")
+
+
+def snack_drop_count(nnz: int, frac_ppm: int) -> int:
+    return _lib.snack_drop_count(nnz, frac_ppm)
+
+
+def snack_prune_regrow_workspace(M: int, K: int, nnz: int, n_drop: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.snack_prune_regrow_workspace(M, K, nnz, n_drop, ctypes.byref(out)),
+           "snack_prune_regrow_workspace")
+    return out.value
+
+
+def snack_prune_regrow(row, col, vals, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
+                       ws, stream=None, ws_bytes=None, dtype=None):
+    dt = _dtype(vals, dtype=dtype)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None and \
+            not isinstance(ws, int) else 0
+    _check(_lib.snack_prune_regrow(_ptr(row), _ptr(col), _ptr(vals), dt, M, K, nnz, n_drop,
+                                   seed & (2**64 - 1), step & (2**64 - 1), _ptr(dropped_lin),
+                                   _ptr(grown_lin), _ptr(ws), ws_bytes, _stream(stream)),
+           "snack_prune_regrow")
+
+
+def snack_gelu_fwd(z, h, n=None, stream=None):
+    n = z.numel() if n is None else n
+    _check(_lib.snack_gelu_fwd(_ptr(z), _ptr(h), n, _stream(stream)), "snack_gelu_fwd")
+
+
+def snack_gelu_bwd(z, dh, dz, n=None, stream=None):
+    n = z.numel() if n is None else n
+    _check(_lib.snack_gelu_bwd(_ptr(z), _ptr(dh), _ptr(dz), n, _stream(stream)),
+           "snack_gelu_bwd")
+
+
+def snack_dense_fwd(W, mask, M, K, X, B, Y, stream=None, dtype=None):
+    dt = _dtype(W, X, Y, dtype=dtype)
+    _check(_lib.snack_dense_fwd(_ptr(W), _ptr(mask), dt, M, K, _ptr(X), B, _ptr(Y),
+                                _stream(stream)), "snack_dense_fwd")
+
+
+def raw_status(name: str, *args) -> int:
+    """Call an entry point with raw ctypes arguments and return its status
+    (for tests of the host-side argument checks)."""
+    return getattr(_lib, name)(*args)
+
+
+lib = _lib

@@ -1,0 +1,367 @@
+// api.cpp -- the C ABI declared in include/snack.h: argument checks, arena
+// layout, and the launch sequences of the layer's operations.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/snack.h"
+#include "internal.h"
+
+using namespace snk;
+
+namespace {
+
+constexpr int32_t TILE_MIN = 128;
+constexpr int32_t TILE_MAX = 2048;
+constexpr int64_t TARGET_TILES = 2048;
+
+int32_t auto_tile(int64_t items) {
+  int32_t T = TILE_MIN;
+  while (cdiv(items, T) > TARGET_TILES && T < TILE_MAX) T *= 2;
+  return T;
+}
+
+inline hipStream_t to_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+__global__ void k_zero_small(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+__global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst,
+                           int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// Arena slots past the public derived arrays: the carry slots of tiles that
+// end inside a long segment, the radix-sort buffers of the column view, and
+// one slot holding the small scratch of prepare (split flags, their scan,
+// error/split counters, scan and sort temporaries).
+constexpr int SLOT_PRIV = 15;
+
+struct priv_layout {
+  size_t flags, flagscan, small, tmp, total;
+};
+
+priv_layout priv_of(const snack_plan* p) {
+  priv_layout L{};
+  int64_t Pm = std::max<int64_t>(std::max(p->P_row, p->P_col), 1);
+  int64_t n = std::max<int64_t>(p->nnz, 1);
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    size_t at = o;
+    o = align_up(o + b, 256);
+    return at;
+  };
+  L.flags = take(4 * (size_t)Pm);
+  L.flagscan = take(4 * (size_t)Pm);
+  L.small = take(64);
+  L.tmp = take(std::max(radix_tmp_bytes(n), scan_tmp_bytes(std::max<int64_t>(Pm, n))));
+  L.total = o;
+  return L;
+}
+
+enum { S_CARRY = 10, S_KEYS_A = 11, S_KEYS_B = 12, S_VALS_B = 13 };
+
+snack_status check_dtype_layout(snack_dtype dt, snack_layout lay) {
+  if (dt != SNACK_F32 && dt != SNACK_BF16) return SNACK_E_DTYPE;
+  if (lay != SNACK_BATCH_MAJOR && lay != SNACK_NODE_MAJOR) return SNACK_E_LAYOUT;
+  return SNACK_OK;
+}
+
+seg_view row_view(const snack_plan* p) {
+  char* a = (char*)p->arena;
+  seg_view v{};
+  v.ptr = (const int32_t*)(a + p->off[SNACK_ARR_ROW_PTR]);
+  v.idx = p->col;
+  v.perm = nullptr;
+  v.part_seg = (const int32_t*)(a + p->off[SNACK_ARR_RPART_SEG]);
+  v.part_nz = (const int32_t*)(a + p->off[SNACK_ARR_RPART_NZ]);
+  v.split = (const int32_t*)(a + p->off[SNACK_ARR_RSPLIT]);
+  v.S = p->M;
+  v.F = p->K;
+  v.P = p->P_row;
+  v.n_split = p->n_split_row;
+  v.nnz = p->nnz;
+  return v;
+}
+
+seg_view col_view(const snack_plan* p) {
+  char* a = (char*)p->arena;
+  seg_view v{};
+  v.ptr = (const int32_t*)(a + p->off[SNACK_ARR_COL_PTR]);
+  v.idx = (const int32_t*)(a + p->off[SNACK_ARR_ROW_T]);
+  v.perm = (const int32_t*)(a + p->off[SNACK_ARR_PERM]);
+  v.part_seg = (const int32_t*)(a + p->off[SNACK_ARR_CPART_SEG]);
+  v.part_nz = (const int32_t*)(a + p->off[SNACK_ARR_CPART_NZ]);
+  v.split = (const int32_t*)(a + p->off[SNACK_ARR_CSPLIT]);
+  v.S = p->K;
+  v.F = p->M;
+  v.P = p->P_col;
+  v.n_split = p->n_split_col;
+  v.nnz = p->nnz;
+  return v;
+}
+
+snack_status check_product(const snack_plan* p, const void* a, const void* b, const void* c,
+                           snack_dtype dt, snack_layout lay, int32_t B) {
+  if (!p) return SNACK_E_NULL;
+  if (!p->prepared || !p->arena) return SNACK_E_NOT_PREPARED;
+  snack_status st = check_dtype_layout(dt, lay);
+  if (st) return st;
+  if (B < 0 || B > p->max_batch) return SNACK_E_SHAPE;
+  if (B > 0 && (!a || !b || !c)) return SNACK_E_NULL;
+  return SNACK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t snack_version(void) { return 100; }
+size_t snack_plan_sizeof(void) { return sizeof(snack_plan); }
+
+const char* snack_status_str(snack_status s) {
+  switch (s) {
+    case SNACK_OK: return "ok";
+    case SNACK_E_NULL: return "null pointer argument";
+    case SNACK_E_SHAPE: return "shape out of range";
+    case SNACK_E_DTYPE: return "unknown dtype";
+    case SNACK_E_LAYOUT: return "unknown layout";
+    case SNACK_E_COO_RANGE: return "COO index out of range";
+    case SNACK_E_COO_ORDER: return "COO not strictly increasing row-major (unsorted or duplicate)";
+    case SNACK_E_NAN: return "NaN value";
+    case SNACK_E_COUNT: return "drop count exceeds nnz or free positions";
+    case SNACK_E_WORKSPACE: return "arena or workspace too small";
+    case SNACK_E_OVERFLOW: return "size exceeds int32 index range";
+    case SNACK_E_HIP: return "HIP launch or runtime error";
+    case SNACK_E_NOT_PREPARED: return "plan not prepared";
+    default: return "unknown status";
+  }
+}
+
+snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz,
+                             int32_t max_batch, int32_t tile_items) {
+  if (!plan) return SNACK_E_NULL;
+  if (M < 1 || K < 1 || nnz < 0 || max_batch < 1) return SNACK_E_SHAPE;
+  if ((double)nnz > (double)M * (double)K) return SNACK_E_SHAPE;
+  if (tile_items < 0 || tile_items > TILE_MAX) return SNACK_E_SHAPE;
+  if (nnz + std::max(M, K) + 2 * TILE_MAX >= (int64_t)INT32_MAX) return SNACK_E_OVERFLOW;
+  std::memset(plan, 0, sizeof(*plan));
+  plan->M = M;
+  plan->K = K;
+  plan->nnz = nnz;
+  plan->max_batch = max_batch;
+  plan->tile_row = tile_items ? tile_items : auto_tile((int64_t)M + nnz);
+  plan->tile_col = tile_items ? tile_items : auto_tile((int64_t)K + nnz);
+  plan->P_row = (int32_t)cdiv((int64_t)M + nnz, plan->tile_row);
+  plan->P_col = (int32_t)cdiv((int64_t)K + nnz, plan->tile_col);
+  const int64_t n = std::max<int64_t>(nnz, 1);
+  size_t o = 0;
+  auto take = [&](int slot, size_t bytes) {
+    plan->off[slot] = o;
+    o = align_up(o + bytes, 256);
+  };
+  take(SNACK_ARR_ROW_PTR, 4 * ((size_t)M + 1));
+  take(SNACK_ARR_RPART_SEG, 4 * ((size_t)plan->P_row + 1));
+  take(SNACK_ARR_RPART_NZ, 4 * ((size_t)plan->P_row + 1));
+  take(SNACK_ARR_RSPLIT, 12 * (size_t)std::max(plan->P_row, 1));
+  take(SNACK_ARR_COL_PTR, 4 * ((size_t)K + 1));
+  take(SNACK_ARR_PERM, 4 * (size_t)n);
+  take(SNACK_ARR_ROW_T, 4 * (size_t)n);
+  take(SNACK_ARR_CPART_SEG, 4 * ((size_t)plan->P_col + 1));
+  take(SNACK_ARR_CPART_NZ, 4 * ((size_t)plan->P_col + 1));
+  take(SNACK_ARR_CSPLIT, 12 * (size_t)std::max(plan->P_col, 1));
+  take(S_CARRY, 8 * (size_t)std::max(plan->P_row, plan->P_col) * (size_t)max_batch);
+  take(S_KEYS_A, 4 * (size_t)n);
+  take(S_KEYS_B, 4 * (size_t)n);
+  take(S_VALS_B, 4 * (size_t)n);
+  take(SLOT_PRIV, priv_of(plan).total);
+  plan->arena_bytes = o;
+  return SNACK_OK;
+}
+
+snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32_t* col,
+                               void* arena, size_t arena_bytes, void* stream) {
+  if (!plan || !arena) return SNACK_E_NULL;
+  if (plan->nnz > 0 && (!row || !col)) return SNACK_E_NULL;
+  if (plan->M < 1 || plan->arena_bytes == 0) return SNACK_E_SHAPE;
+  if (arena_bytes < plan->arena_bytes) return SNACK_E_WORKSPACE;
+  hipStream_t s = to_stream(stream);
+  plan->prepared = 0;
+  plan->row = row;
+  plan->col = col;
+  plan->arena = arena;
+  char* a = (char*)arena;
+  const priv_layout L = priv_of(plan);
+  char* priv = a + plan->off[SLOT_PRIV];
+  int32_t* small = (int32_t*)(priv + L.small);
+  int32_t* flags = (int32_t*)(priv + L.flags);
+  int32_t* flagscan = (int32_t*)(priv + L.flagscan);
+  void* tmp = priv + L.tmp;
+  const int64_t nnz = plan->nnz;
+
+  // 1. validate, read back the error bits before trusting the COO
+  hipLaunchKernelGGL(k_zero_small, dim3(1), dim3(64), 0, s, small, 16);
+  if (launch_validate(row, col, nnz, plan->M, plan->K, small, s) != hipSuccess) return SNACK_E_HIP;
+  int32_t host_small[4] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(host_small, small, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SNACK_E_HIP;
+  if (host_small[0] & 1) return SNACK_E_COO_RANGE;
+  if (host_small[0] & 2) return SNACK_E_COO_ORDER;
+
+  // 2. row view
+  int32_t* row_ptr = (int32_t*)(a + plan->off[SNACK_ARR_ROW_PTR]);
+  if (launch_seg_ptr(row, nnz, plan->M, row_ptr, s) != hipSuccess) return SNACK_E_HIP;
+  if (launch_partition(row_ptr, plan->M, nnz, plan->tile_row, plan->P_row,
+                       (int32_t*)(a + plan->off[SNACK_ARR_RPART_SEG]),
+                       (int32_t*)(a + plan->off[SNACK_ARR_RPART_NZ]), flags, flagscan,
+                       (int32_t*)(a + plan->off[SNACK_ARR_RSPLIT]), small + 1, tmp,
+                       s) != hipSuccess)
+    return SNACK_E_HIP;
+
+  // 3. column view: stable radix sort of (col, k) by col
+  int32_t* perm = (int32_t*)(a + plan->off[SNACK_ARR_PERM]);
+  int32_t* row_t = (int32_t*)(a + plan->off[SNACK_ARR_ROW_T]);
+  uint32_t* keys_a = (uint32_t*)(a + plan->off[S_KEYS_A]);
+  uint32_t* keys_b = (uint32_t*)(a + plan->off[S_KEYS_B]);
+  int32_t* vals_b = (int32_t*)(a + plan->off[S_VALS_B]);
+  int32_t* col_ptr = (int32_t*)(a + plan->off[SNACK_ARR_COL_PTR]);
+  if (nnz > 0) {
+    hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s, col,
+                       (int32_t*)keys_a, nnz);
+    if (launch_iota_i32(perm, nnz, s) != hipSuccess) return SNACK_E_HIP;
+    int bits = 0;
+    while (bits < 31 && ((uint32_t)(plan->K - 1) >> bits) != 0) ++bits;
+    uint32_t* rk;
+    int32_t* rv;
+    if (radix_sort_u32(keys_a, perm, keys_b, vals_b, nnz, bits, &rk, &rv, tmp, s) != hipSuccess)
+      return SNACK_E_HIP;
+    if (rv != perm)
+      hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s, rv, perm,
+                         nnz);
+    if (launch_seg_ptr((const int32_t*)rk, nnz, plan->K, col_ptr, s) != hipSuccess)
+      return SNACK_E_HIP;
+    if (launch_gather_i32(row, perm, row_t, nnz, s) != hipSuccess) return SNACK_E_HIP;
+  } else {
+    if (launch_seg_ptr(col, 0, plan->K, col_ptr, s) != hipSuccess) return SNACK_E_HIP;
+  }
+  if (launch_partition(col_ptr, plan->K, nnz, plan->tile_col, plan->P_col,
+                       (int32_t*)(a + plan->off[SNACK_ARR_CPART_SEG]),
+                       (int32_t*)(a + plan->off[SNACK_ARR_CPART_NZ]), flags, flagscan,
+                       (int32_t*)(a + plan->off[SNACK_ARR_CSPLIT]), small + 2, tmp,
+                       s) != hipSuccess)
+    return SNACK_E_HIP;
+
+  if (hipMemcpyAsync(host_small, small, 12, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SNACK_E_HIP;
+  plan->n_split_row = host_small[1];
+  plan->n_split_col = host_small[2];
+  plan->prepared = 1;
+  return SNACK_OK;
+}
+
+const void* snack_plan_array(const snack_plan* plan, int32_t which, int64_t* count) {
+  if (!plan || !plan->prepared || which < 0 || which >= SNACK_ARR_COUNT_) return nullptr;
+  int64_t n = 0;
+  switch (which) {
+    case SNACK_ARR_ROW_PTR: n = (int64_t)plan->M + 1; break;
+    case SNACK_ARR_RPART_SEG:
+    case SNACK_ARR_RPART_NZ: n = (int64_t)plan->P_row + 1; break;
+    case SNACK_ARR_RSPLIT: n = 3 * (int64_t)plan->n_split_row; break;
+    case SNACK_ARR_COL_PTR: n = (int64_t)plan->K + 1; break;
+    case SNACK_ARR_PERM:
+    case SNACK_ARR_ROW_T: n = plan->nnz; break;
+    case SNACK_ARR_CPART_SEG:
+    case SNACK_ARR_CPART_NZ: n = (int64_t)plan->P_col + 1; break;
+    case SNACK_ARR_CSPLIT: n = 3 * (int64_t)plan->n_split_col; break;
+  }
+  if (count) *count = n;
+  return (const char*)plan->arena + plan->off[which];
+}
+
+snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                            const void* X, snack_layout layout, int32_t B, void* Y,
+                            void* stream) {
+  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y, dtype, layout, B);
+  if (st) return st;
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  return launch_seg_spmm(row_view(plan), vals, dtype, X, layout, B, Y, carry, to_stream(stream));
+}
+
+snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                  const void* dY, snack_layout layout, int32_t B, void* dX,
+                                  void* stream) {
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  if (st) return st;
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  return launch_seg_spmm(col_view(plan), vals, dtype, dY, layout, B, dX, carry,
+                         to_stream(stream));
+}
+
+snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const void* X,
+                                   snack_dtype dtype, snack_layout layout, int32_t B,
+                                   void* dvals, void* stream) {
+  snack_status st = check_product(plan, dY, X, plan && plan->nnz ? dvals : X, dtype, layout, B);
+  if (st) return st;
+  if (plan->nnz > 0 && !dvals) return SNACK_E_NULL;
+  return launch_sddmm(row_view(plan), dY, X, dtype, layout, B, dvals, to_stream(stream));
+}
+
+int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {
+  if (nnz < 0 || frac_ppm < 0) return -1;
+  return (int64_t)(((__int128)nnz * frac_ppm + 500000) / 1000000);
+}
+
+snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                          size_t* bytes) {
+  if (!bytes) return SNACK_E_NULL;
+  if (M < 1 || K < 1 || nnz < 0 || (double)nnz > (double)M * K || n_drop < 0)
+    return SNACK_E_SHAPE;
+  if (nnz >= (int64_t)INT32_MAX) return SNACK_E_OVERFLOW;
+  *bytes = prune_regrow_ws_bytes(M, K, nnz, n_drop);
+  return SNACK_OK;
+}
+
+snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
+                                int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  if (M < 1 || K < 1 || nnz < 0 || (double)nnz > (double)M * K || n_drop < 0)
+    return SNACK_E_SHAPE;
+  if (nnz >= (int64_t)INT32_MAX) return SNACK_E_OVERFLOW;
+  if (n_drop > nnz || n_drop > (int64_t)M * K - nnz) return SNACK_E_COUNT;
+  if (n_drop == 0) return SNACK_OK;
+  if (!row || !col || !vals || !ws) return SNACK_E_NULL;
+  return prune_regrow(row, col, vals, dtype, M, K, nnz, n_drop, seed, step, dropped_lin,
+                      grown_lin, ws, ws_bytes, to_stream(stream));
+}
+
+snack_status snack_gelu_fwd(const float* z, float* h, int64_t n, void* stream) {
+  if (n < 0) return SNACK_E_SHAPE;
+  if (n > 0 && (!z || !h)) return SNACK_E_NULL;
+  return launch_gelu_fwd(z, h, n, to_stream(stream)) == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+}
+
+snack_status snack_gelu_bwd(const float* z, const float* dh, float* dz, int64_t n,
+                            void* stream) {
+  if (n < 0) return SNACK_E_SHAPE;
+  if (n > 0 && (!z || !dh || !dz)) return SNACK_E_NULL;
+  return launch_gelu_bwd(z, dh, dz, n, to_stream(stream)) == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+}
+
+snack_status snack_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dtype, int32_t M,
+                             int32_t K, const void* X, int32_t B, void* Y, void* stream) {
+  if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  if (M < 1 || K < 1 || B < 0) return SNACK_E_SHAPE;
+  if (B > 0 && (!W || !X || !Y)) return SNACK_E_NULL;
+  return launch_dense_fwd(W, mask, dtype, M, K, X, B, Y, to_stream(stream)) == hipSuccess
+             ? SNACK_OK
+             : SNACK_E_HIP;
+}
+
+}  // extern "C"

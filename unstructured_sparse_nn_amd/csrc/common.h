@@ -1,0 +1,74 @@
+// common.h -- device helpers shared by the gfx950 kernels of the sparse layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <utility>
+
+#define SNK_WAVE 64
+
+namespace snk {
+
+typedef uint16_t bf16;  // raw bfloat16 bits
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(bf16 h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round to nearest, ties to even (IEEE 754 roundTiesToEven on the 16
+// dropped mantissa bits); NaN stays a quiet NaN.
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename T> struct elem;
+template <> struct elem<float> {
+  __device__ __forceinline__ static float to_f(float x) { return x; }
+  __device__ __forceinline__ static float from_f(float x) { return x; }
+};
+template <> struct elem<bf16> {
+  __device__ __forceinline__ static float to_f(bf16 x) { return bf16_to_f32(x); }
+  __device__ __forceinline__ static bf16 from_f(float x) { return f32_to_bf16(x); }
+};
+
+// Vector of N elements of T, naturally aligned (N*sizeof(T) bytes), used to
+// move a contiguous chunk of a node-major activation row in one access.
+template <typename T, int N> struct __attribute__((aligned(N * sizeof(T)))) vec {
+  T v[N];
+};
+
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&out)[N]) {
+  vec<T, N> r = *reinterpret_cast<const vec<T, N>*>(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = elem<T>::to_f(r.v[i]);
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_vec(T* __restrict__ p, const float (&in)[N]) {
+  vec<T, N> r;
+#pragma unroll
+  for (int i = 0; i < N; ++i) r.v[i] = elem<T>::from_f(in[i]);
+  *reinterpret_cast<vec<T, N>*>(p) = r;
+}
+
+// ---------------------------------------------------------------- lanes
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace snk
+
+#define SNK_CHECK_LAUNCH()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return SNACK_E_HIP; \
+  } while (0)

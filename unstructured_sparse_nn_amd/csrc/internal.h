@@ -1,0 +1,84 @@
+// internal.h -- host-side launchers shared between the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/snack.h"
+
+namespace snk {
+
+// ---- exclusive prefix sum of int32 (device) --------------------------------
+// out[i] = sum_{j<i} in[j]; in == out is allowed.  If total != NULL the sum
+// of all n inputs is written there (device int32).  tmp must hold
+// scan_tmp_bytes(n) bytes.
+size_t scan_tmp_bytes(int64_t n);
+hipError_t exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total,
+                              void* tmp, hipStream_t s);
+
+// ---- stable LSD radix sort of (key, value) pairs ---------------------------
+// Sorts n pairs by the low `bits` bits of the key (8 bits per pass).  keys /
+// vals are the input; keys_alt / vals_alt are equally sized scratch.  The
+// sorted result ends in whichever buffer pair the last pass wrote;
+// *res_keys / *res_vals point to it.  tmp must hold radix_tmp_bytes(n).
+size_t radix_tmp_bytes(int64_t n);
+hipError_t radix_sort_u32(uint32_t* keys, int32_t* vals, uint32_t* keys_alt, int32_t* vals_alt,
+                          int64_t n, int bits, uint32_t** res_keys, int32_t** res_vals,
+                          void* tmp, hipStream_t s);
+hipError_t radix_sort_u64(uint64_t* keys, int32_t* vals, uint64_t* keys_alt, int32_t* vals_alt,
+                          int64_t n, int bits, uint64_t** res_keys, int32_t** res_vals,
+                          void* tmp, hipStream_t s);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- products (spmm.hip) ----------------------------------------------------
+struct seg_view {          // one compressed view of the sparse matrix
+  const int32_t* ptr;      // [S+1] segment offsets
+  const int32_t* idx;      // [nnz] gathered feature index of each entry
+  const int32_t* perm;     // [nnz] value permutation (NULL = identity)
+  const int32_t* part_seg; // [P+1]
+  const int32_t* part_nz;  // [P+1]
+  const int32_t* split;    // [3*n_split] (segment, first tile, last tile)
+  int32_t S;               // segments (output features)
+  int32_t F;               // gathered features (input features)
+  int32_t P;               // tiles
+  int32_t n_split;
+  int64_t nnz;
+};
+
+snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
+                             snack_layout lay, int32_t B, void* Y, float* carry,
+                             hipStream_t s);
+snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snack_dtype dt,
+                          snack_layout lay, int32_t B, void* dV, hipStream_t s);
+
+// ---- prepare (prepare.hip) ----------------------------------------------------
+hipError_t launch_validate(const int32_t* row, const int32_t* col, int64_t nnz, int32_t M,
+                           int32_t K, int32_t* err, hipStream_t s);
+hipError_t launch_seg_ptr(const int32_t* sorted_keys, int64_t nnz, int32_t S, int32_t* ptr,
+                          hipStream_t s);
+hipError_t launch_partition(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
+                            int32_t* part_seg, int32_t* part_nz, int32_t* flags_first,
+                            int32_t* flags_scan, int32_t* split, int32_t* n_split_dev,
+                            void* scan_tmp, hipStream_t s);
+hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int32_t* dst, int64_t n,
+                             hipStream_t s);
+hipError_t launch_iota_i32(int32_t* dst, int64_t n, hipStream_t s);
+
+// ---- aux kernels (aux.hip) ------------------------------------------------------
+hipError_t launch_gelu_fwd(const float* z, float* h, int64_t n, hipStream_t s);
+hipError_t launch_gelu_bwd(const float* z, const float* dh, float* dz, int64_t n,
+                           hipStream_t s);
+hipError_t launch_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dt, int32_t M,
+                            int32_t K, const void* X, int32_t B, void* Y, hipStream_t s);
+
+// ---- prune / regrow (prune.hip) ---------------------------------------------------
+size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop);
+snack_status prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
+                          int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
+                          int64_t* dropped_lin, int64_t* grown_lin, void* ws, size_t ws_bytes,
+                          hipStream_t s);
+
+}  // namespace snk

@@ -1,0 +1,243 @@
+// prims.hip -- device-wide exclusive scan and stable LSD radix sort (gfx950).
+//
+// Both are building blocks of the layer's preprocessing: the column view is a
+// stable sort of the entries by column, and the prune/regrow step sorts
+// candidate positions and counts accepted ones with scans.  Deterministic:
+// integer arithmetic only, no order-dependent atomics.
+#include "common.h"
+#include "internal.h"
+
+namespace snk {
+
+// ============================================================== scan
+constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_PER_THREAD = 4;
+constexpr int SCAN_BLOCK = SCAN_THREADS * SCAN_PER_THREAD;  // 1024 items
+
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < SNK_WAVE; d <<= 1) {
+    int32_t y = __shfl_up(x, d, SNK_WAVE);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of one value per thread over a 256-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t x, int32_t* lds4, int32_t* total) {
+  const int w = threadIdx.x / SNK_WAVE;
+  const int l = lane_id();
+  int32_t inc = wave_incl_scan(x);
+  if (l == SNK_WAVE - 1) lds4[w] = inc;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_THREADS / SNK_WAVE; ++i) {
+    int32_t t = lds4[i];
+    if (i < w) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_block_reduce(const int32_t* __restrict__ in,
+                                                               int64_t n,
+                                                               int32_t* __restrict__ sums) {
+  __shared__ int32_t lds4[SCAN_THREADS / SNK_WAVE];
+  int64_t base = (int64_t)blockIdx.x * SCAN_BLOCK + (int64_t)threadIdx.x * SCAN_PER_THREAD;
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_PER_THREAD; ++i)
+    if (base + i < n) s += in[base + i];
+  int32_t tot;
+  block_excl_scan(s, lds4, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+// One block scans the per-block sums in place (any count, chunk by chunk).
+__global__ __launch_bounds__(SCAN_THREADS) void k_scan_sums(int32_t* __restrict__ sums,
+                                                            int64_t nb,
+                                                            int32_t* __restrict__ total) {
+  __shared__ int32_t lds4[SCAN_THREADS / SNK_WAVE];
+  int32_t carry = 0;
+  for (int64_t c = 0; c < nb; c += SCAN_THREADS) {
+    int64_t i = c + threadIdx.x;
+    int32_t x = i < nb ? sums[i] : 0;
+    int32_t tot;
+    int32_t ex = block_excl_scan(x, lds4, &tot);
+    if (i < nb) sums[i] = carry + ex;
+    carry += tot;
+  }
+  if (total && threadIdx.x == 0) *total = carry;
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_block_scan(const int32_t* in, int32_t* out,
+                                                             int64_t n,
+                                                             const int32_t* __restrict__ offs) {
+  __shared__ int32_t lds4[SCAN_THREADS / SNK_WAVE];
+  int64_t base = (int64_t)blockIdx.x * SCAN_BLOCK + (int64_t)threadIdx.x * SCAN_PER_THREAD;
+  int32_t v[SCAN_PER_THREAD];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_PER_THREAD; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0;
+    s += v[i];
+  }
+  int32_t tot;
+  int32_t ex = block_excl_scan(s, lds4, &tot) + offs[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < SCAN_PER_THREAD; ++i) {
+    if (base + i < n) out[base + i] = ex;
+    ex += v[i];
+  }
+}
+
+__global__ void k_zero_i32(int32_t* p) { *p = 0; }
+
+size_t scan_tmp_bytes(int64_t n) {
+  return align_up(sizeof(int32_t) * (size_t)std::max<int64_t>(1, cdiv(n, SCAN_BLOCK)), 256);
+}
+
+hipError_t exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total,
+                              void* tmp, hipStream_t s) {
+  if (n <= 0) {
+    if (total) hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, s, total);
+    return hipGetLastError();
+  }
+  int64_t nb = cdiv(n, SCAN_BLOCK);
+  int32_t* sums = (int32_t*)tmp;
+  hipLaunchKernelGGL(k_block_reduce, dim3((unsigned)nb), dim3(SCAN_THREADS), 0, s, in, n, sums);
+  hipLaunchKernelGGL(k_scan_sums, dim3(1), dim3(SCAN_THREADS), 0, s, sums, nb, total);
+  hipLaunchKernelGGL(k_block_scan, dim3((unsigned)nb), dim3(SCAN_THREADS), 0, s, in, out, n,
+                     sums);
+  return hipGetLastError();
+}
+
+// ============================================================== radix sort
+constexpr int RS_THREADS = 256;
+constexpr int RS_ROUNDS = 8;
+constexpr int RS_BLOCK = RS_THREADS * RS_ROUNDS;  // 2048 items per block
+constexpr int RS_WAVES = RS_THREADS / SNK_WAVE;
+
+// Per-block digit histogram, stored digit-major: hist[d * nblk + blk], so that
+// an exclusive scan of hist gives each (digit, block) its stable base offset.
+template <typename KT>
+__global__ __launch_bounds__(RS_THREADS) void k_radix_hist(const KT* __restrict__ keys, int64_t n,
+                                                           int shift, int32_t* __restrict__ hist,
+                                                           int64_t nblk) {
+  __shared__ int32_t h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    int64_t i = base + r * RS_THREADS + threadIdx.x;
+    if (i < n) atomicAdd(&h[(uint32_t)(keys[i] >> shift) & 255u], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter: items of a block are taken in index order, round by round;
+// within a wave, lanes holding the same digit are found with 8 ballots (one
+// per digit bit) and ranked by lane order.
+template <typename KT>
+__global__ __launch_bounds__(RS_THREADS) void k_radix_scatter(
+    const KT* __restrict__ kin, const int32_t* __restrict__ vin, KT* __restrict__ kout,
+    int32_t* __restrict__ vout, int64_t n, int shift, const int32_t* __restrict__ offs,
+    int64_t nblk) {
+  __shared__ int32_t running[256];
+  __shared__ int32_t wcnt[RS_WAVES][256];
+  const int t = threadIdx.x;
+  const int w = t / SNK_WAVE;
+  running[t] = offs[(int64_t)t * nblk + blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < RS_WAVES; ++i) wcnt[i][t] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+  const uint64_t lt = lanemask_lt();
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    int64_t i = base + r * RS_THREADS + t;
+    bool valid = i < n;
+    KT key = valid ? kin[i] : (KT)0;
+    int32_t val = valid ? vin[i] : 0;
+    uint32_t d = (uint32_t)(key >> shift) & 255u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      uint64_t m = __ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? m : ~m;
+    }
+    int rank = __popcll(peers & lt);
+    if (valid && rank == 0) wcnt[w][d] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int32_t pos = running[d] + rank;
+      for (int j = 0; j < w; ++j) pos += wcnt[j][d];
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+    int32_t add = 0;
+#pragma unroll
+    for (int j = 0; j < RS_WAVES; ++j) {
+      add += wcnt[j][t];
+      wcnt[j][t] = 0;
+    }
+    running[t] += add;
+    __syncthreads();
+  }
+}
+
+size_t radix_tmp_bytes(int64_t n) {
+  int64_t nblk = std::max<int64_t>(1, cdiv(n, RS_BLOCK));
+  return align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256) + scan_tmp_bytes(256 * nblk);
+}
+
+template <typename KT>
+static hipError_t radix_sort(KT* keys, int32_t* vals, KT* keys_alt, int32_t* vals_alt, int64_t n,
+                             int bits, KT** res_keys, int32_t** res_vals, void* tmp,
+                             hipStream_t s) {
+  KT* ka = keys;
+  KT* kb = keys_alt;
+  int32_t* va = vals;
+  int32_t* vb = vals_alt;
+  if (n > 0) {
+    int64_t nblk = cdiv(n, RS_BLOCK);
+    int32_t* hist = (int32_t*)tmp;
+    void* stmp = (char*)tmp + align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256);
+    for (int shift = 0; shift < bits; shift += 8) {
+      hipLaunchKernelGGL(k_radix_hist<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, ka, n,
+                         shift, hist, nblk);
+      hipError_t e = exclusive_scan_i32(hist, hist, 256 * nblk, nullptr, stmp, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_radix_scatter<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, ka,
+                         va, kb, vb, n, shift, hist, nblk);
+      std::swap(ka, kb);
+      std::swap(va, vb);
+    }
+  }
+  *res_keys = ka;
+  *res_vals = va;
+  return hipGetLastError();
+}
+
+hipError_t radix_sort_u32(uint32_t* keys, int32_t* vals, uint32_t* keys_alt, int32_t* vals_alt,
+                          int64_t n, int bits, uint32_t** res_keys, int32_t** res_vals,
+                          void* tmp, hipStream_t s) {
+  return radix_sort<uint32_t>(keys, vals, keys_alt, vals_alt, n, bits, res_keys, res_vals, tmp,
+                              s);
+}
+
+hipError_t radix_sort_u64(uint64_t* keys, int32_t* vals, uint64_t* keys_alt, int32_t* vals_alt,
+                          int64_t n, int bits, uint64_t** res_keys, int32_t** res_vals,
+                          void* tmp, hipStream_t s) {
+  return radix_sort<uint64_t>(keys, vals, keys_alt, vals_alt, n, bits, res_keys, res_vals, tmp,
+                              s);
+}
+
+}  // namespace snk

@@ -1,0 +1,106 @@
+"""Torch-facing wrappers: a prepared sparse topology and the SparseLinear
+module ("a simple PyTorch API for restructuring connections and
+backpropagating gradients entirely in the sparse paradigm", SNACK abstract).
+
+Torch allocates the device buffers and supplies the stream; every product,
+gradient and restructuring step is a call into the HIP library.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class Topology:
+    """COO pattern (row, col int32 on the GPU) plus its prepared plan."""
+
+    def __init__(self, row: torch.Tensor, col: torch.Tensor, M: int, K: int, max_batch: int,
+                 tile_items: int = 0, stream=None):
+        assert row.dtype == torch.int32 and col.dtype == torch.int32 and row.is_cuda
+        self.row, self.col, self.M, self.K = row, col, M, K
+        self.max_batch, self.tile_items = max_batch, tile_items
+        self.prepare(stream)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.row.numel())
+
+    def prepare(self, stream=None):
+        self.plan = B.snack_plan_init(self.M, self.K, self.nnz, self.max_batch, self.tile_items)
+        self.arena = torch.empty(self.plan.arena_bytes, dtype=torch.uint8, device=self.row.device)
+        B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
+
+    def array(self, name: str) -> torch.Tensor:
+        """A derived array of the plan as an int32 view into the arena."""
+        _, n = B.snack_plan_array(self.plan, name)
+        off = self.plan.off[B.ARRAYS[name]]
+        return self.arena[off:off + 4 * n].view(torch.int32)
+
+    # products ------------------------------------------------------------
+    def fwd(self, vals, X, Bsz, layout=B.BATCH_MAJOR, out=None):
+        Y = out if out is not None else torch.empty(Bsz * self.M, dtype=X.dtype, device=X.device)
+        B.snack_spmm_fwd(self.plan, vals, X, layout, Bsz, Y)
+        return Y
+
+    def bwd_input(self, vals, dY, Bsz, layout=B.BATCH_MAJOR, out=None):
+        dX = out if out is not None else torch.empty(Bsz * self.K, dtype=dY.dtype,
+                                                     device=dY.device)
+        B.snack_spmm_bwd_input(self.plan, vals, dY, layout, Bsz, dX)
+        return dX
+
+    def grad_vals(self, dY, X, Bsz, layout=B.BATCH_MAJOR, out=None):
+        dV = out if out is not None else torch.empty(self.nnz, dtype=X.dtype, device=X.device)
+        B.snack_sddmm_grad_vals(self.plan, dY, X, layout, Bsz, dV)
+        return dV
+
+
+class _SparseLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, vals, topo):
+        Bsz = x.shape[0]
+        xc = x.contiguous()
+        ctx.topo = topo
+        ctx.save_for_backward(xc, vals)
+        return topo.fwd(vals, xc.view(-1), Bsz).view(Bsz, topo.M)
+
+    @staticmethod
+    def backward(ctx, gy):
+        xc, vals = ctx.saved_tensors
+        topo = ctx.topo
+        Bsz = xc.shape[0]
+        g = gy.contiguous().view(-1)
+        gx = topo.bwd_input(vals, g, Bsz).view(Bsz, topo.K) if ctx.needs_input_grad[0] else None
+        gv = topo.grad_vals(g, xc.view(-1), Bsz) if ctx.needs_input_grad[1] else None
+        return gx, gv, None
+
+
+class SparseLinear(torch.nn.Module):
+    """y = x W^T with W held only as its nonzeros (no bias).
+
+    ``prune_regrow(frac_ppm, step)`` drops the smallest-magnitude fraction of
+    the connections and regrows as many at seeded random free positions
+    (value 0), then re-prepares the topology."""
+
+    def __init__(self, in_features: int, out_features: int, row, col, vals, max_batch: int,
+                 seed: int = 0, tile_items: int = 0):
+        super().__init__()
+        self.in_features, self.out_features, self.seed = in_features, out_features, seed
+        self.topo = Topology(row, col, out_features, in_features, max_batch, tile_items)
+        self.vals = torch.nn.Parameter(vals)
+
+    def forward(self, x):
+        return _SparseLinearFn.apply(x, self.vals, self.topo)
+
+    @torch.no_grad()
+    def prune_regrow(self, frac_ppm: int, step: int):
+        t = self.topo
+        n_drop = B.snack_drop_count(t.nnz, frac_ppm)
+        ws = torch.empty(B.snack_prune_regrow_workspace(t.M, t.K, t.nnz, n_drop),
+                         dtype=torch.uint8, device=t.row.device)
+        dropped = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
+        grown = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
+        B.snack_prune_regrow(t.row, t.col, self.vals.data, t.M, t.K, t.nnz, n_drop, self.seed,
+                             step, dropped, grown, ws)
+        t.prepare()
+        return dropped[:n_drop], grown[:n_drop]
