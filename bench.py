@@ -1,0 +1,346 @@
+"""Benchmark of the truly sparse layer's hot path on one MI355X.
+
+One step = one dynamic-sparse-training step of a 4096 x 4096 layer at 95%
+sparsity (838,861 nnz, bf16 values and activations, fp32 accumulation) on a
+batch of 32:
+    forward Y = X W^T  ->  input gradient dX = dY W  ->  value gradient
+    dV = (dY^T X) at the nonzeros  ->  prune/regrow of 30% of the
+    connections  ->  re-prepare the topology (offsets, tiles, column view).
+The metric is the fwd+bwd SpMM bandwidth: algorithmic bytes of the three
+products (values + indices + offsets + activations read + outputs written)
+per second of whole-step time.  Inputs are resident in HBM before timing;
+by default the step rotates over 20 independent layer instances (~580 MB) so
+that each step reads from HBM rather than the 256 MB Infinity Cache.
+
+Prints one JSON line (see --help).  --gpus > 1 is not supported: the layer
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd SpMM GB/s and % HBM roofline at 95%/99% sparsity, batch 1–32"
+HBM_PEAK_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def algo_bytes(op: str, M: int, K: int, nnz: int, B: int, s_w: int, s_a: int,
+               s_idx: int = 4) -> int:
+    """Minimum bytes an op must move: every stored value and its index once,
+    the segment offsets, the activations read and the output written."""
+    if op == "fwd":
+        return nnz * (s_idx + s_w) + s_idx * (M + 1) + B * K * s_a + B * M * s_a
+    if op == "bwd_input":
+        return nnz * (s_idx + s_w) + s_idx * (K + 1) + B * M * s_a + B * K * s_a
+    if op == "sddmm":  # reads indices, writes one value per nonzero
+        return nnz * (s_idx + s_w) + s_idx * (M + 1) + B * K * s_a + B * M * s_a
+    raise KeyError(op)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--sparsity", type=float, default=0.95)
+    ap.add_argument("--size", type=int, default=4096)
+    ap.add_argument("--drop-ppm", type=int, default=300000)
+    ap.add_argument("--layout", choices=("node", "batch"), default="node",
+                    help="activation layout in HBM: node = feature-major K x B (the "
+                         "layer's native layout), batch = B x K (adds transposes)")
+    ap.add_argument("--rotate", type=int, default=20,
+                    help="layer instances cycled through (1 = cache-warm)")
+    ap.add_argument("--grid", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time fwd/dX/dV at 95/99%% x B in {1,8,32}")
+    ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--products-only", action="store_true",
+                    help="time only fwd/dX/dV (for profiling the product kernels)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a, bf16=False):
+    import torch
+    a = np.ascontiguousarray(a)
+    if bf16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a.copy()).cuda()
+
+
+def layout_data(act, layout):
+    """Synthetic activations are drawn batch-major (B x F); node-major keeps
+    the same values feature-major (F x B)."""
+    if layout == "node" and act.B > 1:
+        return np.ascontiguousarray(act.data.reshape(act.B, act.F).T)
+    return act.data
+
+
+class Instance:
+    """One layer: COO + values + activations + prepared topology + scratch."""
+
+    def __init__(self, w, X, dY, B, bf16, drop_ppm, layout="node"):
+        import torch
+        import unstructured_sparse_nn_amd as snk
+        wt = w
+        self.M, self.K, self.B = wt.M, wt.K, B
+        self.lay = snk.NODE_MAJOR if layout == "node" else snk.BATCH_MAJOR
+        self.row, self.col = to_dev(wt.row), to_dev(wt.col)
+        self.vals = to_dev(wt.vals, bf16)
+        self.X = to_dev(layout_data(X, layout), bf16)
+        self.dY = to_dev(layout_data(dY, layout), bf16)
+        dt = self.vals.dtype
+        self.Y = torch.empty(B * wt.M, dtype=dt, device="cuda")
+        self.dX = torch.empty(B * wt.K, dtype=dt, device="cuda")
+        self.dV = torch.empty(wt.nnz, dtype=dt, device="cuda")
+        self.topo = snk.Topology(self.row, self.col, wt.M, wt.K, B,
+                                 flags=snk.binding.PLAN_NODE_MAJOR_ONLY if layout == "node" else 0)
+        self.n_drop = snk.snack_drop_count(wt.nnz, drop_ppm)
+        self.ws = torch.empty(snk.snack_prune_regrow_workspace(wt.M, wt.K, wt.nnz, self.n_drop),
+                              dtype=torch.uint8, device="cuda")
+        self.step_no = 0
+
+    def products(self, ev=None):
+        t = self.topo
+        if ev: ev[0].record()
+        t.fwd(self.vals, self.X, self.B, self.lay, out=self.Y)
+        if ev: ev[1].record()
+        t.bwd_input(self.vals, self.dY, self.B, self.lay, out=self.dX)
+        if ev: ev[2].record()
+        t.grad_vals(self.dY, self.X, self.B, self.lay, out=self.dV)
+        if ev: ev[3].record()
+
+    def restructure(self, ev=None):
+        import unstructured_sparse_nn_amd as snk
+        self.step_no += 1
+        snk.snack_prune_regrow(self.row, self.col, self.vals, self.M, self.K, self.topo.nnz,
+                               self.n_drop, 0, self.step_no, None, None, self.ws)
+        if ev: ev[4].record()
+        snk.snack_coo_prepare(self.topo.plan, self.row, self.col, self.topo.arena)
+        if ev: ev[5].record()
+
+
+def src_hash():
+    h = hashlib.sha256()
+    for f in ("spmm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "unstructured_sparse_nn_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, launches_bytes):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha") != src_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, X, dY, B, drop_ppm, seconds):
+    """The fp64 oracle, serial on one host core, running the same step on the
+    same layer, repeated until `seconds` of CPU work."""
+    import oracle
+    import synth
+    M, K = w.M, w.K
+    v = w.vals_f64()
+    x64, g64 = X.f64(), dY.f64()
+    row, col = w.row.copy(), w.col.copy()
+    vals = w.vals.copy()
+    n_drop = oracle.drop_count(w.nnz, drop_ppm)
+    bytes_step = sum(algo_bytes(op, M, K, w.nnz, B, 2, 2) for op in ("fwd", "bwd_input", "sddmm"))
+    steps, t_total = 0, 0.0
+    T = 512
+    while t_total < seconds and steps < 50:
+        t0 = time.perf_counter()
+        oracle.spmm_fwd(M, K, row, col, v, B, x64)
+        oracle.spmm_bwd_input(M, K, row, col, v, B, g64)
+        oracle.sddmm(M, K, row, col, B, g64, x64)
+        out = oracle.prune_regrow(M, K, row, col, vals, "bf16", n_drop, 0, steps + 1)
+        rp = oracle.row_ptr(M, out["row"])
+        cp, _, _ = oracle.csc(K, out["row"], out["col"])
+        oracle.partition(rp, T)
+        oracle.partition(cp, T)
+        t_total += time.perf_counter() - t0
+        row, col, vals = out["row"], out["col"], out["vals"]
+        v = synth.bf16_bits_to_f32(vals).astype(np.float64)
+        steps += 1
+    return {"value": round(bytes_step * steps / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} full steps (fwd, dX, dV, prune/regrow, row/column views and "
+                      f"partitions) of the same {M}x{K} layer, B={B}, fp64 serial C, "
+                      f"{t_total:.1f} s on 1 of {os.cpu_count()} host threads "
+                      f"({platform.processor() or platform.machine()})"}
+
+
+def time_ops_grid(sizes, sparsities, batches, rotate, layouts=("node", "batch")):
+    """Per-op time (HIP events on the launch stream, median over launches)
+    over a grid of sparsity x batch x activation layout."""
+    import synth
+    import torch
+    out = {}
+    for sp in sparsities:
+        for B in batches:
+          w = synth.inference_layer(N=sizes, sparsity=sp, B=B)
+          for layout in (layouts if B > 1 else ("node",)):
+            log(f"grid s={sp} B={B} {layout}")
+            insts = [Instance(w.weights[0], w.X[0], w.dY[0], B, True, 0, layout)
+                     for _ in range(rotate)]
+            n = 30
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+            for i in range(5):
+                insts[i % rotate].products()
+            torch.cuda.synchronize()
+            for i in range(n):
+                insts[i % rotate].products(ev[i])
+            torch.cuda.synchronize()
+            ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)]
+                           for i in range(n)])
+            wt = w.weights[0]
+            rec = {}
+            for j, op in enumerate(("fwd", "bwd_input", "sddmm")):
+                b = algo_bytes(op, wt.M, wt.K, wt.nnz, B, 2, 2)
+                us = float(np.median(ms[:, j])) * 1e3
+                rec[op] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                           "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+            out[f"s{sp}_B{B}_{layout}"] = rec
+            del insts
+            torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; --gpus must be 1 "
+                          "(the data-parallel split of the batch is described in DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n * 4}), flush=True)
+        return
+
+    N, B, sp = args.size, args.batch, args.sparsity
+    log(f"inputs {N}x{N} s={sp} B={B}")
+    w = synth.inference_layer(N=N, sparsity=sp, B=B)
+    wt = w.weights[0]
+    R = max(1, args.rotate)
+    log(f"preparing {R} layer instances")
+    insts = [Instance(wt, w.X[0], w.dY[0], B, True, args.drop_ppm, args.layout)
+             for _ in range(R)]
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        inst = insts[i % R]
+        inst.products(ev)
+        if not args.products_only:
+            inst.restructure(ev)
+
+    log("warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K_ = args.steps
+    n_ev = 6
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K_)]
+    torch.cuda.synchronize()
+    log(f"timing {K_} steps")
+    t0 = time.perf_counter()
+    for i in range(K_):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / K_ * 1e3
+
+    n_ops = 3 if args.products_only else 5
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(n_ops)]
+                   for i in range(K_)])
+    names = ["fwd", "bwd_input", "sddmm", "prune_regrow", "prepare"][:n_ops]
+    ops = {}
+    prod_bytes = 0
+    for j, op in enumerate(names):
+        rec = {"us_mean": round(float(ms[:, j].mean()) * 1e3, 2),
+               "us_median": round(float(np.median(ms[:, j])) * 1e3, 2)}
+        if j < 3:
+            b = algo_bytes(op, wt.M, wt.K, wt.nnz, B, 2, 2)
+            prod_bytes += b
+            rec["algo_bytes"] = b
+            rec["GBps"] = round(b / (rec["us_mean"] * 1e3), 1)
+        ops[op] = rec
+    prod_us = sum(ops[o]["us_mean"] for o in ("fwd", "bwd_input", "sddmm"))
+    value = prod_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant product kernel: the one with the largest mean time
+    dom = max(("fwd", "bwd_input", "sddmm"), key=lambda o: ops[o]["us_mean"])
+    kname = {"fwd": "k_seg_spmm (row view)", "bwd_input": "k_seg_spmm (column view)",
+             "sddmm": "k_sddmm"}[dom]
+    ach = ops[dom]["algo_bytes"] / (ops[dom]["us_mean"] * 1e-6) / 1e9
+    tag = f"{dom}_square{N}_s{sp}_B{B}_bf16"
+    traffic = read_traffic(tag, ops[dom]["algo_bytes"])
+    roof = {"bound": "hbm", "kernel": kname, "op": dom, "achieved": round(ach, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+            "traffic": traffic, "algo_bytes_per_launch": ops[dom]["algo_bytes"]}
+
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": K_, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"sparse linear {N}x{N}, {sp:.0%} sparse "
+                                  f"({wt.nnz} nnz, uniform), bf16 values+activations, fp32 "
+                                  f"accumulate, batch {B}; step = fwd+dX+dV"
+                      + ("" if args.products_only else
+                         f"+prune/regrow {args.drop_ppm / 1e4:g}%+prepare"),
+                      "M": N, "K": N, "nnz": wt.nnz, "batch": B,
+                      "layout": "node-major (K x B)" if args.layout == "node" else "batch-major (B x K)",
+                      "rotate_instances": R,
+                      "cache": "cold (HBM)" if R > 1 else "warm (Infinity Cache)"},
+           "roofline": roof,
+           "ops": ops,
+           "products_only_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1)}
+    if args.grid:
+        rec["grid"] = time_ops_grid(N, (0.95, 0.99), (1, 8, 32), R)
+    if args.cpu_baseline:
+        log("cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(wt, w.X[0], w.dY[0], B, args.drop_ppm,
+                                           args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -114,18 +114,25 @@ SNACK_API size_t snack_plan_sizeof(void);
 /* Human-readable text of a status code (static storage). */
 SNACK_API const char* snack_status_str(snack_status s);
 
+/* snack_plan_init flags */
+#define SNACK_PLAN_NODE_MAJOR_ONLY 1u /* no scratch for transposing batch-major activations */
+
 /*
  * snack_plan_init -- host only, no device work.
  * Computes tile sizes, tile counts and the arena layout for a weight of
  * shape M x K with nnz nonzeros, for product calls with B <= max_batch.
  * tile_items = 0 picks the tile size automatically (a power of two in
  * [128, 2048] giving at most ~2048 tiles); otherwise it must lie in
- * [1, 2048] and is used for both views.
+ * [1, 2048] and is used for both views.  Unless flags has
+ * SNACK_PLAN_NODE_MAJOR_ONLY, the arena also holds 4*max_batch*(M+K) bytes
+ * into which product calls copy batch-major activations (B > 1) in
+ * node-major order before gathering from them.
  * Errors: SNACK_E_NULL, SNACK_E_SHAPE (M<1, K<1, nnz<0, nnz>M*K,
- * max_batch<1, bad tile), SNACK_E_OVERFLOW (nnz + max(M,K) >= 2^31).
+ * max_batch<1, bad tile), SNACK_E_OVERFLOW (nnz + max(M,K) >= 2^31),
+ * SNACK_E_LAYOUT (unknown flag).
  */
 SNACK_API snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz,
-                             int32_t max_batch, int32_t tile_items);
+                                       int32_t max_batch, int32_t tile_items, uint32_t flags);
 
 /*
  * snack_coo_prepare -- the "device row-segment offsets and load-balanced
@@ -163,7 +170,9 @@ SNACK_API const void* snack_plan_array(const snack_plan* plan, int32_t which, in
  *     Y[b, r] = sum_{k : row[k] = r} v[k] * X[b, col[k]]
  * for b < B, r < M; rows without entries give exactly 0.  X has K features,
  * Y has M features, both in `layout`.  Y is overwritten (no bias, no beta).
- * Requires a prepared plan and 0 <= B <= plan->max_batch.
+ * Requires a prepared plan and 0 <= B <= plan->max_batch.  Batch-major
+ * activations with B > 1 are first copied node-major into the plan's arena
+ * (SNACK_E_WORKSPACE if the plan was made with SNACK_PLAN_NODE_MAJOR_ONLY).
  */
 SNACK_API snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtype dtype,
                             const void* X, snack_layout layout, int32_t B, void* Y,

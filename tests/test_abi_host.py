@@ -50,12 +50,16 @@ def test_plan_init_sizes(snk):
     assert p.tile_row == 3 and p.P_row == 3 and p.P_col == 2
     offs = list(p.off)[:10]
     assert offs == sorted(offs)
+    # node-major-only plans skip the activation transpose scratch
+    a = snk.snack_plan_init(4096, 4096, 838861, 32)
+    b = snk.snack_plan_init(4096, 4096, 838861, 32, flags=1)
+    assert a.arena_bytes - b.arena_bytes >= 4 * 32 * 8192
 
 
 @pytest.mark.parametrize("args,status", [
     ((0, 4, 1, 1, 0), -2), ((4, 0, 1, 1, 0), -2), ((4, 4, -1, 1, 0), -2),
     ((4, 4, 17, 1, 0), -2), ((4, 4, 1, 0, 0), -2), ((4, 4, 1, 1, 4096), -2),
-    ((2**31 - 1, 1, 1, 1, 0), -10),
+    ((2**31 - 1, 1, 1, 1, 0), -10), ((4, 4, 1, 1, 0, 2), -4),
 ])
 def test_plan_init_rejects(snk, args, status):
     with pytest.raises(snk.SnackError) as e:

@@ -240,6 +240,21 @@ def test_gpt2_mlp_chain(orc, sp):
     assert_within(from_dev(dV1, "f32"), ref, S, "f32", "dW W1")
 
 
+def test_node_major_only_plan(orc):
+    w = synth.random_case(3, 200, 300, 5000, 8, "bf16", "node")
+    wt = w.weights[0]
+    topo = snk.Topology(to_dev(wt.row), to_dev(wt.col), wt.M, wt.K, 8, flags=1)
+    vals = to_dev(wt.vals, "bf16")
+    Y = topo.fwd(vals, to_dev(w.X[0].data, "bf16"), 8, B.NODE_MAJOR)
+    ref, S = orc.spmm_fwd(wt.M, wt.K, wt.row, wt.col, wt.vals_f64(), 8, w.X[0].f64(), True)
+    assert_within(from_dev(Y, "bf16"), ref, S, "bf16", "fwd node-major-only plan")
+    with pytest.raises(snk.SnackError) as e:
+        topo.fwd(vals, to_dev(w.X[0].data, "bf16"), 8, B.BATCH_MAJOR)
+    assert e.value.status == -9
+    # B == 1: both layouts are the same vector, no scratch needed
+    topo.fwd(vals, to_dev(w.X[0].data[:wt.K], "bf16"), 1, B.BATCH_MAJOR)
+
+
 def test_zero_batch_and_empty_weight(orc):
     w = synth.random_case(2, 30, 20, 50, 1).weights[0]
     topo = topology(w, 4)

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsnack.so")
 
 F32, BF16 = 0, 1
+PLAN_NODE_MAJOR_ONLY = 1
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
 
@@ -60,7 +61,7 @@ def _load():
         "snack_version": ([], i32),
         "snack_plan_sizeof": ([], sz),
         "snack_status_str": ([i32], ctypes.c_char_p),
-        "snack_plan_init": ([plan_p, i32, i32, i64, i32, i32], i32),
+        "snack_plan_init": ([plan_p, i32, i32, i64, i32, i32, ctypes.c_uint32], i32),
         "snack_coo_prepare": ([plan_p, P, P, P, sz, P], i32),
         "snack_plan_array": ([plan_p, i32, ctypes.POINTER(i64)], P),
         "snack_spmm_fwd": ([plan_p, P, i32, P, i32, i32, P, P], i32),
@@ -133,9 +134,10 @@ def snack_plan_sizeof() -> int:
     return _lib.snack_plan_sizeof()
 
 
-def snack_plan_init(M: int, K: int, nnz: int, max_batch: int, tile_items: int = 0) -> SnackPlan:
+def snack_plan_init(M: int, K: int, nnz: int, max_batch: int, tile_items: int = 0,
+                    flags: int = 0) -> SnackPlan:
     plan = SnackPlan()
-    _check(_lib.snack_plan_init(ctypes.byref(plan), M, K, nnz, max_batch, tile_items),
+    _check(_lib.snack_plan_init(ctypes.byref(plan), M, K, nnz, max_batch, tile_items, flags),
            "snack_plan_init")
     return plan
 

@@ -62,7 +62,7 @@ priv_layout priv_of(const snack_plan* p) {
   return L;
 }
 
-enum { S_CARRY = 10, S_KEYS_A = 11, S_KEYS_B = 12, S_VALS_B = 13 };
+enum { S_CARRY = 10, S_KEYS_A = 11, S_KEYS_B = 12, S_VALS_B = 13, S_ACT = 14 };
 
 snack_status check_dtype_layout(snack_dtype dt, snack_layout lay) {
   if (dt != SNACK_F32 && dt != SNACK_BF16) return SNACK_E_DTYPE;
@@ -83,6 +83,7 @@ seg_view row_view(const snack_plan* p) {
   v.F = p->K;
   v.P = p->P_row;
   v.n_split = p->n_split_row;
+  v.tile = p->tile_row;
   v.nnz = p->nnz;
   return v;
 }
@@ -100,8 +101,14 @@ seg_view col_view(const snack_plan* p) {
   v.F = p->M;
   v.P = p->P_col;
   v.n_split = p->n_split_col;
+  v.tile = p->tile_col;
   v.nnz = p->nnz;
   return v;
+}
+
+void* act_of(const snack_plan* p) {
+  if (p->off[S_ACT] == (size_t)-1) return nullptr;
+  return (char*)p->arena + p->off[S_ACT];
 }
 
 snack_status check_product(const snack_plan* p, const void* a, const void* b, const void* c,
@@ -142,8 +149,9 @@ const char* snack_status_str(snack_status s) {
 }
 
 snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz,
-                             int32_t max_batch, int32_t tile_items) {
+                             int32_t max_batch, int32_t tile_items, uint32_t flags) {
   if (!plan) return SNACK_E_NULL;
+  if (flags & ~(uint32_t)SNACK_PLAN_NODE_MAJOR_ONLY) return SNACK_E_LAYOUT;
   if (M < 1 || K < 1 || nnz < 0 || max_batch < 1) return SNACK_E_SHAPE;
   if ((double)nnz > (double)M * (double)K) return SNACK_E_SHAPE;
   if (tile_items < 0 || tile_items > TILE_MAX) return SNACK_E_SHAPE;
@@ -177,6 +185,10 @@ snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz
   take(S_KEYS_A, 4 * (size_t)n);
   take(S_KEYS_B, 4 * (size_t)n);
   take(S_VALS_B, 4 * (size_t)n);
+  if (!(flags & SNACK_PLAN_NODE_MAJOR_ONLY))
+    take(S_ACT, 4 * (size_t)max_batch * ((size_t)M + K) + 512);
+  else
+    plan->off[S_ACT] = (size_t)-1;
   take(SLOT_PRIV, priv_of(plan).total);
   plan->arena_bytes = o;
   return SNACK_OK;
@@ -289,7 +301,8 @@ snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtyp
   snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y, dtype, layout, B);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
-  return launch_seg_spmm(row_view(plan), vals, dtype, X, layout, B, Y, carry, to_stream(stream));
+  return launch_seg_spmm(row_view(plan), vals, dtype, X, layout, B, Y, carry, act_of(plan),
+                         to_stream(stream));
 }
 
 snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
@@ -298,7 +311,7 @@ snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snac
   snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
-  return launch_seg_spmm(col_view(plan), vals, dtype, dY, layout, B, dX, carry,
+  return launch_seg_spmm(col_view(plan), vals, dtype, dY, layout, B, dX, carry, act_of(plan),
                          to_stream(stream));
 }
 
@@ -308,7 +321,8 @@ snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const
   snack_status st = check_product(plan, dY, X, plan && plan->nnz ? dvals : X, dtype, layout, B);
   if (st) return st;
   if (plan->nnz > 0 && !dvals) return SNACK_E_NULL;
-  return launch_sddmm(row_view(plan), dY, X, dtype, layout, B, dvals, to_stream(stream));
+  return launch_sddmm(row_view(plan), dY, X, dtype, layout, B, dvals, act_of(plan),
+                      to_stream(stream));
 }
 
 int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {

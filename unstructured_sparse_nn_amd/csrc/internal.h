@@ -45,14 +45,21 @@ struct seg_view {          // one compressed view of the sparse matrix
   int32_t F;               // gathered features (input features)
   int32_t P;               // tiles
   int32_t n_split;
+  int32_t tile;            // items per tile of this view
   int64_t nnz;
 };
 
+// act_tmp: scratch for the node-major copy of batch-major activations
+// (B > 1); >= elem * B * (F + S) + 256 bytes, or NULL when only node-major
+// activations are used.
 snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
-                             snack_layout lay, int32_t B, void* Y, float* carry,
+                             snack_layout lay, int32_t B, void* Y, float* carry, void* act_tmp,
                              hipStream_t s);
 snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snack_dtype dt,
-                          snack_layout lay, int32_t B, void* dV, hipStream_t s);
+                          snack_layout lay, int32_t B, void* dV, void* act_tmp, hipStream_t s);
+hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
+                             const void* in1, void* out1, int32_t R1, int32_t C1,
+                             hipStream_t s);
 
 // ---- prepare (prepare.hip) ----------------------------------------------------
 hipError_t launch_validate(const int32_t* row, const int32_t* col, int64_t nnz, int32_t M,

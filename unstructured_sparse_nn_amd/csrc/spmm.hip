@@ -11,57 +11,38 @@
 //
 // Work split (answers "Two Lotteries", paragraphs on gathers and on who does
 // the work):
-//   * one 256-thread workgroup per load-balanced tile of < 2T merge-path
-//     items (segment ends + entries), so a long row costs the same per tile
-//     as many short ones;
-//   * inside a tile, G lanes form an item group that owns CH consecutive batch
-//     columns each (one 4-16 byte access per entry for node-major
-//     activations); the 256/G groups cut the tile's merge path into equal
-//     runs and walk them serially, keeping the running sum in registers and
-//     writing each segment they finish;
+//   * one workgroup per load-balanced tile of < 2T merge-path items (segment
+//     ends + entries), so a long row costs the same per tile as many short
+//     ones;
+//   * activations are gathered from a node-major copy (feature-major, batch
+//     contiguous), so the B values an entry needs are one contiguous 2..16
+//     byte chunk per lane instead of B scattered rows;
+//   * G lanes form an item group owning CH consecutive batch columns each;
+//     the groups cut the tile's merge path into equal runs of ~8 items and
+//     walk them serially, keeping the running sum in registers and writing
+//     each segment they finish;
 //   * entries of a run are fetched RC at a time: indices and values first,
 //     then all RC activation gathers, so each wave keeps many loads in
 //     flight;
-//   * a segment cut by a run boundary is finished deterministically: partial
-//     sums of the groups before it are added in group order through LDS, and
-//     a segment cut by a tile boundary (only segments with >= T entries) goes
+//   * a segment cut by run boundaries is finished with a segmented inclusive
+//     scan of the groups' partial sums (shuffles inside a wave, one LDS step
+//     across the waves), so no serial chain of carries;
+//   * a segment cut by a tile boundary (only segments with >= T entries) goes
 //     through per-tile carry slots summed in tile order by k_fixup.
 // No floating-point atomics: results are bitwise reproducible.
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
 namespace snk {
 
-constexpr int MP_THREADS = 256;
-constexpr int MP_TMAX = 2048;              // largest tile size (items)
-constexpr int MP_SEG_LDS = 2 * MP_TMAX;    // a tile holds < 2T segment ends
-constexpr int MP_RC = 8;                   // entries fetched per step
-
-template <typename T, int CH, bool NODE>
-__device__ __forceinline__ void gather_in(const T* __restrict__ X, int32_t f, int32_t b0,
-                                          int32_t B, int32_t F, float (&out)[CH]) {
-  if constexpr (NODE) {
-    load_vec<T, CH>(X + (int64_t)f * B + b0, out);
-  } else {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) out[c] = elem<T>::to_f(X[(int64_t)(b0 + c) * F + f]);
-  }
-}
-
-template <typename T, int CH, bool NODE>
-__device__ __forceinline__ void store_out(T* __restrict__ Y, int32_t s, int32_t b0, int32_t B,
-                                          int32_t S, const float (&v)[CH]) {
-  if constexpr (NODE) {
-    store_vec<T, CH>(Y + (int64_t)s * B + b0, v);
-  } else {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) Y[(int64_t)(b0 + c) * S + s] = elem<T>::from_f(v[c]);
-  }
-}
+constexpr int MP_MAX_THREADS = 256;
+constexpr int MP_RC = 8;        // entries fetched per step of a run
+constexpr int MP_MAX_BW = 32;   // batch columns per workgroup (CH * G)
 
 // Merge-path point of local diagonal d inside a tile: the number x of
-// segment ends consumed (end x' is consumed before entry j iff
-// end[x'] <= j).
+// segment ends consumed (end x' is consumed before entry j iff end[x'] <= j).
 __device__ __forceinline__ int tile_search(const int32_t* s_end, int d, int nseg, int nz,
                                            int32_t zb) {
   int lo = max(0, d - nz), hi = min(d, nseg);
@@ -72,24 +53,87 @@ __device__ __forceinline__ int tile_search(const int32_t* s_end, int d, int nseg
   return lo;
 }
 
-template <typename T, int CH, bool NODE, bool PERM>
-__global__ __launch_bounds__(MP_THREADS) void k_seg_spmm(
+template <typename T, int CH, bool NODE_OUT>
+__device__ __forceinline__ void store_out(T* __restrict__ Y, int32_t s, int32_t b0, int32_t B,
+                                          int32_t S, const float (&v)[CH]) {
+  if constexpr (NODE_OUT) {
+    store_vec<T, CH>(Y + (int64_t)s * B + b0, v);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) Y[(int64_t)(b0 + c) * S + s] = elem<T>::from_f(v[c]);
+  }
+}
+
+// acc + sum_c a[c] * b[c] in fp32; bf16 pairs go through v_dot2_f32_bf16
+// (exact bf16 products summed into the fp32 accumulator).
+template <typename T, int CH>
+__device__ __forceinline__ float dot_acc(const vec<T, CH>& a, const vec<T, CH>& b, float acc) {
+  if constexpr (sizeof(T) == 2 && CH >= 2) {
+    typedef __bf16 __attribute__((ext_vector_type(2))) bf2;
+#pragma unroll
+    for (int c = 0; c < CH; c += 2) {
+      const uint32_t pa = (uint32_t)a.v[c] | ((uint32_t)a.v[c + 1] << 16);
+      const uint32_t pb = (uint32_t)b.v[c] | ((uint32_t)b.v[c + 1] << 16);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pa),
+                                            __builtin_bit_cast(bf2, pb), acc, false);
+    }
+    return acc;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc = fmaf(elem<T>::to_f(a.v[c]), elem<T>::to_f(b.v[c]), acc);
+    return acc;
+  }
+}
+
+// Shared-memory layout of one tile (dynamic LDS).
+struct tile_lds {
+  int32_t* end;    // [2T] segment end offsets of the tile's segments
+  int32_t* idx;    // [2T] gathered feature index of the tile's entries
+  float* val;      // [2T] value of the tile's entries (fp32)
+  int32_t* gx;     // [NT+1] run start: segment ends consumed
+  int32_t* gy;     // [NT+1] run start: entries consumed
+  float* scan;     // [threads*CH] segmented scan of run partial sums
+  float* wval;     // [4][MP_MAX_BW] per-wave scan totals
+  int32_t* wflag;  // [4] per-wave "a segment starts here" flags
+};
+
+__host__ __device__ inline size_t tile_lds_bytes(int tile_items, int threads, int g_log2, int ch) {
+  int NT = threads >> g_log2;
+  return 3 * 4 * (size_t)(2 * tile_items) + 8 * (size_t)(NT + 1) + 4 * (size_t)threads * ch +
+         4 * 4 * MP_MAX_BW + 16;
+}
+
+__device__ __forceinline__ tile_lds carve(unsigned char* smem, int tile_items, int threads,
+                                          int NT, int ch) {
+  tile_lds L;
+  L.end = (int32_t*)smem;
+  L.idx = L.end + 2 * tile_items;
+  L.val = (float*)(L.idx + 2 * tile_items);
+  L.gx = (int32_t*)(L.val + 2 * tile_items);
+  L.gy = L.gx + (NT + 1);
+  L.scan = (float*)(L.gy + (NT + 1));
+  L.wval = L.scan + threads * ch;
+  L.wflag = (int32_t*)(L.wval + 4 * MP_MAX_BW);
+  return L;
+}
+
+template <typename T, int CH, bool NODE_OUT, bool PERM>
+__global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const T* __restrict__ vals,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
-    const T* __restrict__ X, T* __restrict__ Y, float* __restrict__ carry, int32_t S, int32_t F,
-    int32_t B, int32_t P, int32_t g_log2) {
-  __shared__ int32_t s_end[MP_SEG_LDS];
-  __shared__ int32_t s_gx[MP_THREADS + 1];
-  __shared__ int32_t s_gy[MP_THREADS + 1];
-  __shared__ int32_t s_cseg[MP_THREADS];
-  __shared__ float s_cval[MP_THREADS * CH];
-
+    const T* __restrict__ Xt, T* __restrict__ Y, float* __restrict__ carry, int32_t S,
+    int32_t B, int32_t P, int32_t g_log2, int32_t tile_items) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int threads = blockDim.x;
   const int G = 1 << g_log2;
-  const int NT = MP_THREADS >> g_log2;
+  const int NT = threads >> g_log2;
+  const tile_lds L = carve(smem, tile_items, threads, NT, CH);
   const int tid = threadIdx.x;
   const int grp = tid >> g_log2;
   const int gl = tid & (G - 1);
+  const int lane = lane_id();
+  const int wave = tid >> 6;
   const int p = blockIdx.x;
   const int32_t b0 = (int32_t)blockIdx.y * (G * CH) + gl * CH;
   const bool bvalid = b0 < B;
@@ -101,24 +145,30 @@ __global__ __launch_bounds__(MP_THREADS) void k_seg_spmm(
   const int items = nseg + nz;
   const int32_t seg0_start = ptr[sb];
 
-  for (int i = tid; i < nseg; i += MP_THREADS) s_end[i] = ptr[sb + 1 + i];
+  // stage the tile: segment ends, entry indices and values (coalesced)
+  for (int i = tid; i < nseg; i += threads) L.end[i] = ptr[sb + 1 + i];
+  for (int i = tid; i < nz; i += threads) {
+    const int64_t k = (int64_t)zb + i;
+    L.idx[i] = idx[k];
+    L.val[i] = elem<T>::to_f(PERM ? vals[perm[k]] : vals[k]);
+  }
   __syncthreads();
 
   const int R = (items + NT - 1) / NT;
   if (gl == 0) {
     int d = min(grp * R, items);
-    int x = tile_search(s_end, d, nseg, nz, zb);
-    s_gx[grp] = x;
-    s_gy[grp] = d - x;
+    int x = tile_search(L.end, d, nseg, nz, zb);
+    L.gx[grp] = x;
+    L.gy[grp] = d - x;
   }
   if (tid == 0) {
-    s_gx[NT] = nseg;
-    s_gy[NT] = nz;
+    L.gx[NT] = nseg;
+    L.gy[NT] = nz;
   }
   __syncthreads();
-  const int x0 = s_gx[grp], y0 = s_gy[grp];
-  const int x1 = s_gx[grp + 1], y1 = s_gy[grp + 1];
-  const int32_t x0_start = (x0 == 0) ? seg0_start : s_end[min(x0, MP_SEG_LDS) - 1];
+  const int x0 = L.gx[grp], y0 = L.gy[grp];
+  const int x1 = L.gx[grp + 1], y1 = L.gy[grp + 1];
+  const int32_t x0_start = (x0 == 0) ? seg0_start : L.end[x0 - 1];
   const bool mid_start = (zb + y0) > x0_start;
   const bool tile_carry_in = zb > seg0_start;
 
@@ -128,103 +178,163 @@ __global__ __launch_bounds__(MP_THREADS) void k_seg_spmm(
   bool has_pend = false, first_emit = true;
   int x = x0;
 
-  auto emit = [&](int xx) {
+  auto emit = [&](int xx, const float (&v)[CH]) {
     if (first_emit && mid_start) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) pend[c] = acc[c];
+      for (int c = 0; c < CH; ++c) pend[c] = v[c];
       has_pend = true;
     } else if (bvalid) {
-      store_out<T, CH, NODE>(Y, sb + xx, b0, B, S, acc);
+      store_out<T, CH, NODE_OUT>(Y, sb + xx, b0, B, S, v);
     }
     first_emit = false;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = 0.f;
   };
 
+  // The run's entries are taken RC at a time.  Per chunk: finish the segments
+  // that end before its first entry, find which segments its entries belong
+  // to (a handful of LDS reads, no per-entry branch), then one masked FMA
+  // pass per segment touched.
   for (int y = y0; y < y1; y += MP_RC) {
     const int n = min(MP_RC, y1 - y);
+    const int32_t pos0 = zb + y;
+    while (x < x1 && L.end[x] <= pos0) {
+      emit(x++, acc);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+    }
     int32_t ci[MP_RC];
     float cv[MP_RC];
-    float xv[MP_RC][CH];
+    vec<T, CH> xv[MP_RC];  // gathered activations kept packed until use
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
-      if (u < n) {
-        int64_t k = (int64_t)zb + y + u;
-        ci[u] = idx[k];
-        cv[u] = elem<T>::to_f(PERM ? vals[perm[k]] : vals[k]);
-      }
+      const bool ok = u < n;
+      ci[u] = ok ? L.idx[y + u] : 0;
+      cv[u] = ok ? L.val[y + u] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
       if (u < n && bvalid) {
-        gather_in<T, CH, NODE>(X, ci[u], b0, B, F, xv[u]);
+        xv[u] = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)ci[u] * B + b0);
       } else {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) xv[u][c] = 0.f;
+        for (int c = 0; c < CH; ++c) xv[u].v[c] = (T)0;
       }
     }
+    // segment of entry u = x + number of ends e >= x with end[e] <= pos0 + u
+    // (ends between the chunk's entries; sd is non-decreasing in u)
+    int sd[MP_RC];
+#pragma unroll
+    for (int u = 0; u < MP_RC; ++u) sd[u] = 0;
+    int xh = x;
+    while (xh < x1 && L.end[xh] <= pos0 + n - 1) {
+      const int32_t e = L.end[xh];
+#pragma unroll
+      for (int u = 0; u < MP_RC; ++u) sd[u] += (e <= pos0 + u) ? 1 : 0;
+      ++xh;
+    }
+    // one ordered sweep: entries in order, a segment is finished when the
+    // next entry's segment offset moves past it (sd is non-decreasing)
+    int cur = 0;
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
       if (u < n) {
-        const int32_t kg = zb + y + u;
-        while (x < x1 && s_end[x] <= kg) emit(x++);
+        while (sd[u] > cur) {
+          emit(x + cur, acc);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) acc[c] = fmaf(cv[u], xv[u][c], acc[c]);
+          for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+          ++cur;
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[c] = fmaf(cv[u], elem<T>::to_f(xv[u].v[c]), acc[c]);
       }
     }
+    x = xh;
   }
-  while (x < x1) emit(x++);
-
-  s_cseg[grp] = x1;  // written by every lane of the group (same value)
+  while (x < x1) {
+    emit(x++, acc);
 #pragma unroll
-  for (int c = 0; c < CH; ++c) s_cval[tid * CH + c] = acc[c];
+    for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+  }
+
+  // Segmented inclusive scan over the groups of the running partial sums.
+  // A group "heads" a new carry segment if it finished any segment (its carry
+  // then belongs to a segment no earlier group touched).
+  int h = (x0 != x1 || grp == 0) ? 1 : 0;
+  float sc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) sc[c] = acc[c];
+  const int GW = 64 >> g_log2;  // groups per wave
+  const int gw = lane >> g_log2;
+  for (int d = 1; d < GW; d <<= 1) {
+    const int off = d << g_log2;
+    int oh = __shfl_up(h, off, 64);
+    float o[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) o[c] = __shfl_up(sc[c], off, 64);
+    if (gw >= d) {
+      if (!h) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) sc[c] += o[c];
+      }
+      h |= oh;
+    }
+  }
+  const int nwaves = threads >> 6;
+  if (nwaves > 1) {
+    if (gw == GW - 1) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) L.wval[wave * MP_MAX_BW + gl * CH + c] = sc[c];
+      if (gl == 0) L.wflag[wave] = h;
+    }
+    __syncthreads();
+    if (!h && wave > 0) {
+      float cin[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) cin[c] = 0.f;
+      for (int w = 0; w < wave; ++w) {
+        const bool f = L.wflag[w] != 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          float v = L.wval[w * MP_MAX_BW + gl * CH + c];
+          cin[c] = f ? v : cin[c] + v;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) sc[c] += cin[c];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) L.scan[tid * CH + c] = sc[c];
   __syncthreads();
 
   if (has_pend) {
-    int t = grp - 1;
-    while (t >= 0 && s_cseg[t] == x0) --t;
     float tot[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) tot[c] = 0.f;
-    for (int u = t + 1; u < grp; ++u) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) tot[c] += s_cval[(u * G + gl) * CH + c];
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) tot[c] += pend[c];
+    for (int c = 0; c < CH; ++c)
+      tot[c] = (grp > 0 ? L.scan[((grp - 1) * G + gl) * CH + c] : 0.f) + pend[c];
     if (bvalid) {
       if (x0 == 0 && tile_carry_in) {
         float* dst = carry + ((int64_t)P + p) * B + b0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) dst[c] = tot[c];
       } else {
-        store_out<T, CH, NODE>(Y, sb + x0, b0, B, S, tot);
+        store_out<T, CH, NODE_OUT>(Y, sb + x0, b0, B, S, tot);
       }
     }
   }
 
   if (grp == NT - 1 && bvalid) {
-    const int32_t trail_start = (nseg == 0) ? seg0_start : s_end[nseg - 1];
+    const int32_t trail_start = (nseg == 0) ? seg0_start : L.end[nseg - 1];
     if (ze > max(zb, trail_start)) {
-      int t = NT - 1;
-      while (t >= 0 && s_cseg[t] == nseg) --t;
-      float tot[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) tot[c] = 0.f;
-      for (int u = t + 1; u < NT; ++u) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) tot[c] += s_cval[(u * G + gl) * CH + c];
-      }
       float* dst = carry + (int64_t)p * B + b0;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) dst[c] = tot[c];
+      for (int c = 0; c < CH; ++c) dst[c] = sc[c];
     }
   }
 }
 
 // Segments cut by tile boundaries: out = sum of the carry-out slots of tiles
 // first..last-1 (in tile order) + the final piece held by tile `last`.
-template <typename T, bool NODE>
+template <typename T, bool NODE_OUT>
 __global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ split, int32_t n_split,
                                                const float* __restrict__ carry, T* __restrict__ Y,
                                                int32_t S, int32_t B, int32_t P) {
@@ -235,24 +345,26 @@ __global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ split
   float tot = 0.f;
   for (int32_t q = f; q < l; ++q) tot += carry[(int64_t)q * B + b];
   tot += carry[((int64_t)P + l) * B + b];
-  if (NODE) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
+  if (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
   else Y[(int64_t)b * S + s] = elem<T>::from_f(tot);
 }
 
 // dV[k] = sum_b dY[b, seg(k)] * X[b, idx[k]], walking the same tiles to learn
-// each entry's segment without reading a per-entry row index.
-template <typename T, int CH, bool NODE>
-__global__ __launch_bounds__(MP_THREADS) void k_sddmm(
+// each entry's segment without reading a per-entry row index.  Node-major
+// inputs: each lane dots its CH-column chunk, the G lanes of a group then
+// reduce with shuffles; batches wider than one group loop inside.  Results
+// are staged in LDS and written out coalesced.
+template <typename T, int CH>
+__global__ __launch_bounds__(MP_MAX_THREADS) void k_sddmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
-    const T* __restrict__ dY, const T* __restrict__ X, T* __restrict__ dV, int32_t S, int32_t F,
-    int32_t B, int32_t g_log2) {
-  __shared__ int32_t s_end[MP_SEG_LDS];
-  __shared__ int32_t s_gx[MP_THREADS + 1];
-  __shared__ int32_t s_gy[MP_THREADS + 1];
-
+    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t B,
+    int32_t g_log2, int32_t tile_items) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int threads = blockDim.x;
   const int G = 1 << g_log2;
-  const int NT = MP_THREADS >> g_log2;
+  const int NT = threads >> g_log2;
+  const tile_lds L = carve(smem, tile_items, threads, NT, CH);
   const int tid = threadIdx.x;
   const int grp = tid >> g_log2;
   const int gl = tid & (G - 1);
@@ -265,51 +377,58 @@ __global__ __launch_bounds__(MP_THREADS) void k_sddmm(
   const int nz = ze - zb;
   const int items = nseg + nz;
 
-  for (int i = tid; i < nseg; i += MP_THREADS) s_end[i] = ptr[sb + 1 + i];
+  for (int i = tid; i < nseg; i += threads) L.end[i] = ptr[sb + 1 + i];
+  for (int i = tid; i < nz; i += threads) L.idx[i] = idx[(int64_t)zb + i];
   __syncthreads();
   const int R = (items + NT - 1) / NT;
   if (gl == 0) {
     int d = min(grp * R, items);
-    int x = tile_search(s_end, d, nseg, nz, zb);
-    s_gx[grp] = x;
-    s_gy[grp] = d - x;
+    int x = tile_search(L.end, d, nseg, nz, zb);
+    L.gx[grp] = x;
+    L.gy[grp] = d - x;
   }
   if (tid == 0) {
-    s_gx[NT] = nseg;
-    s_gy[NT] = nz;
+    L.gx[NT] = nseg;
+    L.gy[NT] = nz;
   }
   __syncthreads();
-  const int x1 = s_gx[grp + 1], y0 = s_gy[grp], y1 = s_gy[grp + 1];
-  int x = s_gx[grp];
+  const int x1 = L.gx[grp + 1], y0 = L.gy[grp], y1 = L.gy[grp + 1];
+  int x = L.gx[grp];
 
   for (int y = y0; y < y1; y += MP_RC) {
     const int n = min(MP_RC, y1 - y);
+    const int32_t pos0 = zb + y;
+    while (x < x1 && L.end[x] <= pos0) ++x;
     int32_t ci[MP_RC], sg[MP_RC];
     float dot[MP_RC];
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
       dot[u] = 0.f;
-      ci[u] = 0;
-      sg[u] = sb;
-      if (u < n) {
-        const int32_t kg = zb + y + u;
-        ci[u] = idx[kg];
-        while (x < x1 && s_end[x] <= kg) ++x;
-        sg[u] = sb + x;
-      }
+      ci[u] = u < n ? L.idx[y + u] : 0;
+      sg[u] = sb + x;
     }
+    int xh = x;
+    while (xh < x1 && L.end[xh] <= pos0 + n - 1) {
+      const int32_t e = L.end[xh];
+#pragma unroll
+      for (int u = 0; u < MP_RC; ++u) sg[u] += (e <= pos0 + u) ? 1 : 0;
+      ++xh;
+    }
+    x = xh;
     for (int32_t bb = 0; bb < B; bb += BW) {
       const int32_t b0 = bb + gl * CH;
       if (b0 < B) {
+        vec<T, CH> xv[MP_RC], gv[MP_RC];
 #pragma unroll
         for (int u = 0; u < MP_RC; ++u) {
           if (u < n) {
-            float xv[CH], gv[CH];
-            gather_in<T, CH, NODE>(X, ci[u], b0, B, F, xv);
-            gather_in<T, CH, NODE>(dY, sg[u], b0, B, S, gv);
-#pragma unroll
-            for (int c = 0; c < CH; ++c) dot[u] = fmaf(gv[c], xv[c], dot[u]);
+            xv[u] = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)ci[u] * B + b0);
+            gv[u] = *reinterpret_cast<const vec<T, CH>*>(dYt + (int64_t)sg[u] * B + b0);
           }
+        }
+#pragma unroll
+        for (int u = 0; u < MP_RC; ++u) {
+          if (u < n) dot[u] = dot_acc<T, CH>(gv[u], xv[u], dot[u]);
         }
       }
     }
@@ -320,9 +439,11 @@ __global__ __launch_bounds__(MP_THREADS) void k_sddmm(
     if (gl == 0) {
 #pragma unroll
       for (int u = 0; u < MP_RC; ++u)
-        if (u < n) dV[(int64_t)zb + y + u] = elem<T>::from_f(dot[u]);
+        if (u < n) L.val[y + u] = dot[u];
     }
   }
+  __syncthreads();
+  for (int i = tid; i < nz; i += threads) dV[(int64_t)zb + i] = elem<T>::from_f(L.val[i]);
 }
 
 template <typename T>
@@ -331,99 +452,223 @@ __global__ void k_fill_zero(T* __restrict__ p, int64_t n) {
   if (i < n) p[i] = (T)0;
 }
 
-// ---------------------------------------------------------------- host side
-struct lane_shape {
-  int ch;      // batch columns per lane
-  int g_log2;  // lanes per item group = 1 << g_log2
-  int bw;      // batch columns per workgroup
-};
+// out (C x R) = in (R x C)^T, up to two matrices per launch.
+// R <= 64 (small batch): one thread per column c reads R values (coalesced
+// across threads: consecutive c) and writes the R contiguous outputs of its
+// row in 8-element pieces.  Larger R: 32 x 32 LDS tiles.
+constexpr int TR_TILE = 32;
+constexpr int TR_SMALL = 64;
 
-static lane_shape pick_shape(snack_dtype dt, int32_t B) {
-  const int chmax = dt == SNACK_BF16 ? 8 : 4;
-  int ch = 1;
-  while (ch < chmax && B % (ch * 2) == 0) ch *= 2;
-  int want = (int)std::min<int64_t>(cdiv(B, ch), 32 / ch);
-  int g_log2 = 0;
-  while ((1 << g_log2) < want) ++g_log2;
-  return {ch, g_log2, ch << g_log2};
+template <typename T>
+__device__ __forceinline__ void transpose_cols(const T* __restrict__ in, T* __restrict__ out,
+                                               int32_t R, int32_t C, int64_t c) {
+  if (c >= C) return;
+  for (int32_t r0 = 0; r0 < R; r0 += 8) {
+    vec<T, 8> v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v.v[j] = (r0 + j < R) ? in[(int64_t)(r0 + j) * C + c] : (T)0;
+    if ((R & 7) == 0) {
+      *reinterpret_cast<vec<T, 8>*>(out + c * R + r0) = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < R) out[c * R + r0 + j] = v.v[j];
+    }
+  }
 }
 
-template <typename T, int CH, bool NODE, bool PERM>
-static void launch_t(const seg_view& v, const void* vals, const void* X, int32_t B, void* Y,
-                     float* carry, int g_log2, int bw, hipStream_t s) {
-  dim3 grid((unsigned)v.P, (unsigned)cdiv(B, bw));
-  hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE, PERM>), grid, dim3(MP_THREADS), 0, s, v.ptr,
-                     v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)X, (T*)Y,
-                     carry, v.S, v.F, B, v.P, g_log2);
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_small(const T* __restrict__ in0,
+                                                         T* __restrict__ out0, int32_t R0,
+                                                         int32_t C0, int32_t blocks0,
+                                                         const T* __restrict__ in1,
+                                                         T* __restrict__ out1, int32_t R1,
+                                                         int32_t C1) {
+  int32_t bx = blockIdx.x;
+  if (bx < blocks0) {
+    transpose_cols<T>(in0, out0, R0, C0, (int64_t)bx * 256 + threadIdx.x);
+  } else {
+    transpose_cols<T>(in1, out1, R1, C1, (int64_t)(bx - blocks0) * 256 + threadIdx.x);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose2(const T* __restrict__ in0, T* __restrict__ out0,
+                                                    int32_t R0, int32_t C0, int32_t tiles0_x,
+                                                    int32_t tiles0, const T* __restrict__ in1,
+                                                    T* __restrict__ out1, int32_t R1, int32_t C1,
+                                                    int32_t tiles1_x) {
+  __shared__ T tile[TR_TILE][TR_TILE + 1];
+  int32_t t = blockIdx.x;
+  const T* in = in0;
+  T* out = out0;
+  int32_t R = R0, C = C0, tx_n = tiles0_x;
+  if (t >= tiles0) {
+    t -= tiles0;
+    in = in1;
+    out = out1;
+    R = R1;
+    C = C1;
+    tx_n = tiles1_x;
+  }
+  const int32_t c0 = (t % tx_n) * TR_TILE, r0 = (t / tx_n) * TR_TILE;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < TR_TILE; i += 8) {
+    int32_t r = r0 + ty + i, c = c0 + tx;
+    if (r < R && c < C) tile[ty + i][tx] = in[(int64_t)r * C + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TR_TILE; i += 8) {
+    int32_t c = c0 + ty + i, r = r0 + tx;
+    if (r < R && c < C) out[(int64_t)c * R + r] = tile[tx][ty + i];
+  }
+}
+
+// ---------------------------------------------------------------- host side
+struct lane_shape {
+  int ch;       // batch columns per lane
+  int g_log2;   // lanes per item group = 1 << g_log2
+  int bw;       // batch columns per workgroup
+  int threads;  // workgroup size
+};
+
+// Widest per-lane chunk of batch columns.  bf16 products use 4 columns
+// (8-byte gathers): measured faster than 8 at batch 32 on gfx950 because the
+// 8-column variant needs ~128 VGPRs and halves occupancy.  The bf16 SDDMM
+// keeps 8 columns, consumed pairwise by v_dot2_f32_bf16.  SNACK_BF16_CHMAX
+// (1, 2, 4 or 8) overrides the product width for experiments.
+static int bf16_chmax_products() {
+  static int v = [] {
+    const char* e = getenv("SNACK_BF16_CHMAX");
+    int c = e ? atoi(e) : 4;
+    return (c == 1 || c == 2 || c == 4 || c == 8) ? c : 4;
+  }();
+  return v;
+}
+
+static lane_shape pick_shape(snack_dtype dt, int32_t B, int32_t tile_items, bool sddmm = false) {
+  const int chmax = dt == SNACK_BF16 ? (sddmm ? 8 : bf16_chmax_products()) : 4;
+  int ch = 1;
+  while (ch < chmax && B % (ch * 2) == 0) ch *= 2;
+  int want = (int)std::min<int64_t>(cdiv(B, ch), MP_MAX_BW / ch);
+  int g_log2 = 0;
+  while ((1 << g_log2) < want) ++g_log2;
+  // ~8 merge-path items per group: groups = T/8, at least one wave
+  int64_t thr = ((int64_t)std::max(1, tile_items / 8)) << g_log2;
+  thr = std::min<int64_t>(MP_MAX_THREADS, std::max<int64_t>(64, thr));
+  thr = (thr + 63) / 64 * 64;
+  return {ch, g_log2, ch << g_log2, (int)thr};
+}
+
+template <typename T>
+static hipError_t transpose2(const void* in0, void* out0, int32_t R0, int32_t C0,
+                             const void* in1, void* out1, int32_t R1, int32_t C1,
+                             hipStream_t s) {
+  if (R0 <= TR_SMALL && (!in1 || R1 <= TR_SMALL)) {
+    int32_t b0 = (int32_t)cdiv(C0, 256), b1 = in1 ? (int32_t)cdiv(C1, 256) : 0;
+    hipLaunchKernelGGL(k_transpose_small<T>, dim3((unsigned)(b0 + b1)), dim3(256), 0, s,
+                       (const T*)in0, (T*)out0, R0, C0, b0, (const T*)in1, (T*)out1, R1, C1);
+    return hipGetLastError();
+  }
+  int32_t tx0 = (int32_t)cdiv(C0, TR_TILE), t0 = tx0 * (int32_t)cdiv(R0, TR_TILE);
+  int32_t tx1 = in1 ? (int32_t)cdiv(C1, TR_TILE) : 1;
+  int32_t t1 = in1 ? tx1 * (int32_t)cdiv(R1, TR_TILE) : 0;
+  if (t0 + t1 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_transpose2<T>, dim3((unsigned)(t0 + t1)), dim3(256), 0, s,
+                     (const T*)in0, (T*)out0, R0, C0, tx0, t0, (const T*)in1, (T*)out1, R1, C1,
+                     tx1);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
+                             const void* in1, void* out1, int32_t R1, int32_t C1,
+                             hipStream_t s) {
+  if (dt == SNACK_F32) return transpose2<float>(in0, out0, R0, C0, in1, out1, R1, C1, s);
+  return transpose2<bf16>(in0, out0, R0, C0, in1, out1, R1, C1, s);
+}
+
+template <typename T, int CH, bool NODE_OUT, bool PERM>
+static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
+                     float* carry, const lane_shape& sh, hipStream_t s) {
+  dim3 grid((unsigned)v.P, (unsigned)cdiv(B, sh.bw));
+  size_t lds = tile_lds_bytes(v.tile, sh.threads, sh.g_log2, CH);
+  hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, PERM>), grid, dim3(sh.threads), lds, s, v.ptr,
+                     v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)Xt, (T*)Y,
+                     carry, v.S, B, v.P, sh.g_log2, v.tile);
   if (v.n_split > 0) {
     int64_t n = (int64_t)v.n_split * B;
-    hipLaunchKernelGGL((k_fixup<T, NODE>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
                        v.split, v.n_split, carry, (T*)Y, v.S, B, v.P);
   }
 }
 
 template <typename T, int CH>
-static void launch_ch(const seg_view& v, const void* vals, const void* X, snack_layout lay,
-                      int32_t B, void* Y, float* carry, int g_log2, int bw, hipStream_t s) {
-  const bool node = lay == SNACK_NODE_MAJOR;
+static void launch_ch(const seg_view& v, const void* vals, const void* Xt, bool node_out,
+                      int32_t B, void* Y, float* carry, const lane_shape& sh, hipStream_t s) {
   const bool perm = v.perm != nullptr;
-  if (node && perm) launch_t<T, CH, true, true>(v, vals, X, B, Y, carry, g_log2, bw, s);
-  else if (node) launch_t<T, CH, true, false>(v, vals, X, B, Y, carry, g_log2, bw, s);
-  else if (perm) launch_t<T, CH, false, true>(v, vals, X, B, Y, carry, g_log2, bw, s);
-  else launch_t<T, CH, false, false>(v, vals, X, B, Y, carry, g_log2, bw, s);
+  if (node_out && perm) launch_t<T, CH, true, true>(v, vals, Xt, B, Y, carry, sh, s);
+  else if (node_out) launch_t<T, CH, true, false>(v, vals, Xt, B, Y, carry, sh, s);
+  else if (perm) launch_t<T, CH, false, true>(v, vals, Xt, B, Y, carry, sh, s);
+  else launch_t<T, CH, false, false>(v, vals, Xt, B, Y, carry, sh, s);
 }
 
 template <typename T>
-static void launch_dt(const seg_view& v, const void* vals, const void* X, snack_layout lay,
+static void launch_dt(const seg_view& v, const void* vals, const void* Xt, bool node_out,
                       int32_t B, void* Y, float* carry, const lane_shape& sh, hipStream_t s) {
   switch (sh.ch) {
-    case 1: launch_ch<T, 1>(v, vals, X, lay, B, Y, carry, sh.g_log2, sh.bw, s); break;
-    case 2: launch_ch<T, 2>(v, vals, X, lay, B, Y, carry, sh.g_log2, sh.bw, s); break;
-    case 4: launch_ch<T, 4>(v, vals, X, lay, B, Y, carry, sh.g_log2, sh.bw, s); break;
+    case 1: launch_ch<T, 1>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
+    case 2: launch_ch<T, 2>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
+    case 4: launch_ch<T, 4>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
     default:
-      if constexpr (sizeof(T) == 2) launch_ch<T, 8>(v, vals, X, lay, B, Y, carry, sh.g_log2, sh.bw, s);
+      if constexpr (sizeof(T) == 2) launch_ch<T, 8>(v, vals, Xt, node_out, B, Y, carry, sh, s);
       break;
   }
 }
 
 snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
-                             snack_layout lay, int32_t B, void* Y, float* carry, hipStream_t s) {
+                             snack_layout lay, int32_t B, void* Y, float* carry, void* act_tmp,
+                             hipStream_t s) {
   if (B == 0 || v.S == 0) return SNACK_OK;
-  lane_shape sh = pick_shape(dt, B);
-  if (dt == SNACK_F32) launch_dt<float>(v, vals, X, lay, B, Y, carry, sh, s);
-  else launch_dt<bf16>(v, vals, X, lay, B, Y, carry, sh, s);
+  const void* Xt = X;
+  if (lay == SNACK_BATCH_MAJOR && B > 1) {  // B x F -> F x B once, then gather chunks
+    if (!act_tmp) return SNACK_E_WORKSPACE;
+    if (launch_transpose2(dt, X, act_tmp, B, v.F, nullptr, nullptr, 0, 0, s) != hipSuccess)
+      return SNACK_E_HIP;
+    Xt = act_tmp;
+  }
+  const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
+  lane_shape sh = pick_shape(dt, B, v.tile);
+  if (dt == SNACK_F32) launch_dt<float>(v, vals, Xt, node_out, B, Y, carry, sh, s);
+  else launch_dt<bf16>(v, vals, Xt, node_out, B, Y, carry, sh, s);
   return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
 }
 
 template <typename T, int CH>
-static void launch_sddmm_ch(const seg_view& v, const void* dY, const void* X, snack_layout lay,
-                            int32_t B, void* dV, int g_log2, hipStream_t s) {
-  dim3 grid((unsigned)v.P);
-  if (lay == SNACK_NODE_MAJOR)
-    hipLaunchKernelGGL((k_sddmm<T, CH, true>), grid, dim3(MP_THREADS), 0, s, v.ptr, v.idx,
-                       v.part_seg, v.part_nz, (const T*)dY, (const T*)X, (T*)dV, v.S, v.F, B,
-                       g_log2);
-  else
-    hipLaunchKernelGGL((k_sddmm<T, CH, false>), grid, dim3(MP_THREADS), 0, s, v.ptr, v.idx,
-                       v.part_seg, v.part_nz, (const T*)dY, (const T*)X, (T*)dV, v.S, v.F, B,
-                       g_log2);
+static void launch_sddmm_ch(const seg_view& v, const void* dYt, const void* Xt, int32_t B,
+                            void* dV, const lane_shape& sh, hipStream_t s) {
+  size_t lds = tile_lds_bytes(v.tile, sh.threads, sh.g_log2, CH);
+  hipLaunchKernelGGL((k_sddmm<T, CH>), dim3((unsigned)v.P), dim3(sh.threads), lds, s, v.ptr,
+                     v.idx, v.part_seg, v.part_nz, (const T*)dYt, (const T*)Xt, (T*)dV, B,
+                     sh.g_log2, v.tile);
 }
 
 template <typename T>
-static void launch_sddmm_dt(const seg_view& v, const void* dY, const void* X, snack_layout lay,
-                            int32_t B, void* dV, const lane_shape& sh, hipStream_t s) {
+static void launch_sddmm_dt(const seg_view& v, const void* dYt, const void* Xt, int32_t B,
+                            void* dV, const lane_shape& sh, hipStream_t s) {
   switch (sh.ch) {
-    case 1: launch_sddmm_ch<T, 1>(v, dY, X, lay, B, dV, sh.g_log2, s); break;
-    case 2: launch_sddmm_ch<T, 2>(v, dY, X, lay, B, dV, sh.g_log2, s); break;
-    case 4: launch_sddmm_ch<T, 4>(v, dY, X, lay, B, dV, sh.g_log2, s); break;
+    case 1: launch_sddmm_ch<T, 1>(v, dYt, Xt, B, dV, sh, s); break;
+    case 2: launch_sddmm_ch<T, 2>(v, dYt, Xt, B, dV, sh, s); break;
+    case 4: launch_sddmm_ch<T, 4>(v, dYt, Xt, B, dV, sh, s); break;
     default:
-      if constexpr (sizeof(T) == 2) launch_sddmm_ch<T, 8>(v, dY, X, lay, B, dV, sh.g_log2, s);
+      if constexpr (sizeof(T) == 2) launch_sddmm_ch<T, 8>(v, dYt, Xt, B, dV, sh, s);
       break;
   }
 }
 
 snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snack_dtype dt,
-                          snack_layout lay, int32_t B, void* dV, hipStream_t s) {
+                          snack_layout lay, int32_t B, void* dV, void* act_tmp, hipStream_t s) {
   if (v.nnz == 0) return SNACK_OK;
   if (B == 0) {
     dim3 g((unsigned)cdiv(v.nnz, 256));
@@ -431,9 +676,20 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
     else hipLaunchKernelGGL(k_fill_zero<bf16>, g, dim3(256), 0, s, (bf16*)dV, v.nnz);
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   }
-  lane_shape sh = pick_shape(dt, B);
-  if (dt == SNACK_F32) launch_sddmm_dt<float>(v, dY, X, lay, B, dV, sh, s);
-  else launch_sddmm_dt<bf16>(v, dY, X, lay, B, dV, sh, s);
+  const void* Xt = X;
+  const void* dYt = dY;
+  if (lay == SNACK_BATCH_MAJOR && B > 1) {
+    if (!act_tmp) return SNACK_E_WORKSPACE;
+    const size_t es = dt == SNACK_F32 ? 4 : 2;
+    char* xt = (char*)act_tmp;
+    char* gt = xt + align_up(es * (size_t)B * v.F, 256);
+    if (launch_transpose2(dt, X, xt, B, v.F, dY, gt, B, v.S, s) != hipSuccess) return SNACK_E_HIP;
+    Xt = xt;
+    dYt = gt;
+  }
+  lane_shape sh = pick_shape(dt, B, v.tile, true);
+  if (dt == SNACK_F32) launch_sddmm_dt<float>(v, dYt, Xt, B, dV, sh, s);
+  else launch_sddmm_dt<bf16>(v, dYt, Xt, B, dV, sh, s);
   return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
 }
 

@@ -16,10 +16,10 @@ class Topology:
     """COO pattern (row, col int32 on the GPU) plus its prepared plan."""
 
     def __init__(self, row: torch.Tensor, col: torch.Tensor, M: int, K: int, max_batch: int,
-                 tile_items: int = 0, stream=None):
+                 tile_items: int = 0, stream=None, flags: int = 0):
         assert row.dtype == torch.int32 and col.dtype == torch.int32 and row.is_cuda
         self.row, self.col, self.M, self.K = row, col, M, K
-        self.max_batch, self.tile_items = max_batch, tile_items
+        self.max_batch, self.tile_items, self.flags = max_batch, tile_items, flags
         self.prepare(stream)
 
     @property
@@ -27,7 +27,8 @@ class Topology:
         return int(self.row.numel())
 
     def prepare(self, stream=None):
-        self.plan = B.snack_plan_init(self.M, self.K, self.nnz, self.max_batch, self.tile_items)
+        self.plan = B.snack_plan_init(self.M, self.K, self.nnz, self.max_batch, self.tile_items,
+                                      self.flags)
         self.arena = torch.empty(self.plan.arena_bytes, dtype=torch.uint8, device=self.row.device)
         B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
 
