@@ -72,13 +72,13 @@ typedef enum {
   SNACK_ARR_ROW_PTR = 0,     /* int32 [M+1]   row-segment offsets */
   SNACK_ARR_RPART_SEG = 1,   /* int32 [P_row+1] tile start: segment (row) */
   SNACK_ARR_RPART_NZ = 2,    /* int32 [P_row+1] tile start: entry */
-  SNACK_ARR_RSPLIT = 3,      /* int32 [3*n_split_row] (row, first tile, last tile) */
+  SNACK_ARR_RCUT = 3,        /* int32 [P_row+1] 1 if cut p lies inside a row (long row split) */
   SNACK_ARR_COL_PTR = 4,     /* int32 [K+1]   column-segment offsets */
   SNACK_ARR_PERM = 5,        /* int32 [nnz]   row-major position of the i-th entry in (col,row) order */
   SNACK_ARR_ROW_T = 6,       /* int32 [nnz]   row[perm[i]] */
   SNACK_ARR_CPART_SEG = 7,   /* int32 [P_col+1] */
   SNACK_ARR_CPART_NZ = 8,    /* int32 [P_col+1] */
-  SNACK_ARR_CSPLIT = 9,      /* int32 [3*n_split_col] */
+  SNACK_ARR_CCUT = 9,        /* int32 [P_col+1] 1 if cut p lies inside a column */
   SNACK_ARR_COUNT_ = 10
 } snack_array;
 
@@ -96,8 +96,8 @@ typedef struct snack_plan {
   int32_t tile_row;          /* work items (entries + row ends) per row-view tile */
   int32_t tile_col;          /* work items per column-view tile */
   int32_t P_row, P_col;      /* number of tiles of each view */
-  int32_t n_split_row;       /* rows split across tiles (set by prepare) */
-  int32_t n_split_col;       /* columns split across tiles (set by prepare) */
+  int32_t has_split_row;     /* 1 if some row spans several tiles (set by prepare) */
+  int32_t has_split_col;     /* 1 if some column spans several tiles (set by prepare) */
   int32_t prepared;          /* 1 after a successful snack_coo_prepare */
   const int32_t* row;        /* device COO recorded by prepare (not owned) */
   const int32_t* col;
@@ -145,16 +145,17 @@ SNACK_API snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, i
  *                     tile_row items, each cut moved back to the start of its
  *                     row unless that row has >= tile_row entries (so only
  *                     long rows are ever split across tiles);
- *   split list        for each split row: (row, first tile, last tile);
+ *   cut flags         1 where a cut lies inside a (long) row;
  *   col_ptr[K+1], perm[nnz], row_t[nnz]  the column view: entries in stable
  *                     (col, row) order; perm[i] is the row-major position of
  *                     the i-th one and row_t[i] its row;
- *   column-view tiles and split list, as for rows.
+ *   column-view tiles and cut flags, as for rows.
  * The load balancing answers the imbalance the "Two Lotteries" page
  * describes (section on who does the work): every tile gets about the same
  * number of entries + segment ends, whatever the row lengths.
  * Validates the COO first: SNACK_E_COO_RANGE / SNACK_E_COO_ORDER.
- * Reads back 12 bytes and synchronises `stream`.  Records row, col and
+ * Runs about a dozen kernels, then reads back 12 bytes (error bits and the
+ * two has_split flags) and synchronises `stream`.  Records row, col and
  * arena in the plan; they must stay alive and unchanged while the plan is
  * used.  Re-run after every change of the sparsity pattern.
  */

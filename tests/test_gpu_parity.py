@@ -1,6 +1,6 @@
 """GPU parity: every entry point of the HIP library against the fp64 oracle.
 
-Integer outputs (offsets, tiles, split lists, column view, post-step COO,
+Integer outputs (offsets, tiles, cut flags, column view, post-step COO,
 dropped/grown lists) must be bit-exact; float outputs must satisfy
 |gpu - oracle| <= tol * S per output, S = sum of |term| (tol 1e-5 for fp32,
 1e-2 for bf16 values with fp32 accumulation).
@@ -54,9 +54,15 @@ def check_prepare(orc, w, topo):
         assert ref["P"] == (topo.plan.P_row if view == "r" else topo.plan.P_col)
         assert np.array_equal(topo.array(view + "part_seg").cpu().numpy(), ref["part_seg"])
         assert np.array_equal(topo.array(view + "part_nz").cpu().numpy(), ref["part_nz"])
-        split = topo.array(view + "split").cpu().numpy().reshape(-1, 3)
-        exp = np.stack([ref["split_seg"], ref["split_first"], ref["split_last"]], 1)
-        assert np.array_equal(split, exp.reshape(-1, 3))
+        # cut flags: 1 where a cut lies inside a segment, i.e. the tiles
+        # first+1 .. last of every split segment the oracle lists
+        P = ref["P"]
+        exp_cut = np.zeros(P + 1, dtype=np.int32)
+        for f, l in zip(ref["split_first"], ref["split_last"]):
+            exp_cut[f + 1:l + 1] = 1
+        assert np.array_equal(topo.array(view + "cut").cpu().numpy(), exp_cut)
+        has = topo.plan.has_split_row if view == "r" else topo.plan.has_split_col
+        assert has == int(len(ref["split_seg"]) > 0)
 
 
 def run_products(orc, w, X, dY, dt, layout, Bsz, tile=0, sddmm=True, repeat_check=False):
@@ -168,7 +174,7 @@ def test_products_skewed_rows_with_splits(orc):
         w = synth.random_case(7, M, K, lin.size, Bsz, dt, layout, positions=lin)
         topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile=64,
                             repeat_check=True)
-        assert topo.plan.n_split_row > 0
+        assert topo.plan.has_split_row == 1
 
 
 @pytest.mark.parametrize("name,B", [("single", 4)])
@@ -189,13 +195,13 @@ def test_square_inference_configs(orc, sp, Bsz):
 def test_llama_projection_configs(orc, which, Bsz):
     w = workload(f"llama_{which}_{Bsz}")
     topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz)
-    assert topo.plan.n_split_row > 0  # dense rows longer than a tile
+    assert topo.plan.has_split_row == 1  # dense rows longer than a tile
 
 
 def test_graph_config(orc):
     w = workload("graph")
     topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "f32", "node", 128, sddmm=True)
-    assert topo.plan.n_split_row > 0
+    assert topo.plan.has_split_row == 1
 
 
 @pytest.mark.parametrize("sp", ["0.9", "0.99"])

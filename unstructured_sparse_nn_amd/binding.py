@@ -22,8 +22,8 @@ PLAN_NODE_MAJOR_ONLY = 1
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
 
-ARRAYS = {"row_ptr": 0, "rpart_seg": 1, "rpart_nz": 2, "rsplit": 3, "col_ptr": 4, "perm": 5,
-          "row_t": 6, "cpart_seg": 7, "cpart_nz": 8, "csplit": 9}
+ARRAYS = {"row_ptr": 0, "rpart_seg": 1, "rpart_nz": 2, "rcut": 3, "col_ptr": 4, "perm": 5,
+          "row_t": 6, "cpart_seg": 7, "cpart_nz": 8, "ccut": 9}
 
 STATUS = {0: "SNACK_OK", -1: "SNACK_E_NULL", -2: "SNACK_E_SHAPE", -3: "SNACK_E_DTYPE",
           -4: "SNACK_E_LAYOUT", -5: "SNACK_E_COO_RANGE", -6: "SNACK_E_COO_ORDER",
@@ -42,8 +42,8 @@ class SnackPlan(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int32), ("K", ctypes.c_int32), ("nnz", ctypes.c_int64),
                 ("max_batch", ctypes.c_int32), ("tile_row", ctypes.c_int32),
                 ("tile_col", ctypes.c_int32), ("P_row", ctypes.c_int32),
-                ("P_col", ctypes.c_int32), ("n_split_row", ctypes.c_int32),
-                ("n_split_col", ctypes.c_int32), ("prepared", ctypes.c_int32),
+                ("P_col", ctypes.c_int32), ("has_split_row", ctypes.c_int32),
+                ("has_split_col", ctypes.c_int32), ("prepared", ctypes.c_int32),
                 ("row", ctypes.c_void_p), ("col", ctypes.c_void_p),
                 ("arena", ctypes.c_void_p), ("arena_bytes", ctypes.c_size_t),
                 ("off", ctypes.c_size_t * PLAN_SLOTS)]

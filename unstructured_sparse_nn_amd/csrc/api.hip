@@ -35,13 +35,13 @@ __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict_
 }
 
 // Arena slots past the public derived arrays: the carry slots of tiles that
-// end inside a long segment, the radix-sort buffers of the column view, and
-// one slot holding the small scratch of prepare (split flags, their scan,
-// error/split counters, scan and sort temporaries).
+// end inside a long segment, the radix-sort buffers of the column view, the
+// node-major copy of batch-major activations, and one slot holding the small
+// scratch of prepare (error / split flags, scan and sort temporaries).
 constexpr int SLOT_PRIV = 15;
 
 struct priv_layout {
-  size_t flags, flagscan, small, tmp, total;
+  size_t small, tmp, total;
 };
 
 priv_layout priv_of(const snack_plan* p) {
@@ -54,8 +54,6 @@ priv_layout priv_of(const snack_plan* p) {
     o = align_up(o + b, 256);
     return at;
   };
-  L.flags = take(4 * (size_t)Pm);
-  L.flagscan = take(4 * (size_t)Pm);
   L.small = take(64);
   L.tmp = take(std::max(radix_tmp_bytes(n), scan_tmp_bytes(std::max<int64_t>(Pm, n))));
   L.total = o;
@@ -78,11 +76,11 @@ seg_view row_view(const snack_plan* p) {
   v.perm = nullptr;
   v.part_seg = (const int32_t*)(a + p->off[SNACK_ARR_RPART_SEG]);
   v.part_nz = (const int32_t*)(a + p->off[SNACK_ARR_RPART_NZ]);
-  v.split = (const int32_t*)(a + p->off[SNACK_ARR_RSPLIT]);
+  v.cut = (const int32_t*)(a + p->off[SNACK_ARR_RCUT]);
   v.S = p->M;
   v.F = p->K;
   v.P = p->P_row;
-  v.n_split = p->n_split_row;
+  v.has_split = p->has_split_row;
   v.tile = p->tile_row;
   v.nnz = p->nnz;
   return v;
@@ -96,11 +94,11 @@ seg_view col_view(const snack_plan* p) {
   v.perm = (const int32_t*)(a + p->off[SNACK_ARR_PERM]);
   v.part_seg = (const int32_t*)(a + p->off[SNACK_ARR_CPART_SEG]);
   v.part_nz = (const int32_t*)(a + p->off[SNACK_ARR_CPART_NZ]);
-  v.split = (const int32_t*)(a + p->off[SNACK_ARR_CSPLIT]);
+  v.cut = (const int32_t*)(a + p->off[SNACK_ARR_CCUT]);
   v.S = p->K;
   v.F = p->M;
   v.P = p->P_col;
-  v.n_split = p->n_split_col;
+  v.has_split = p->has_split_col;
   v.tile = p->tile_col;
   v.nnz = p->nnz;
   return v;
@@ -174,13 +172,13 @@ snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, int64_t nnz
   take(SNACK_ARR_ROW_PTR, 4 * ((size_t)M + 1));
   take(SNACK_ARR_RPART_SEG, 4 * ((size_t)plan->P_row + 1));
   take(SNACK_ARR_RPART_NZ, 4 * ((size_t)plan->P_row + 1));
-  take(SNACK_ARR_RSPLIT, 12 * (size_t)std::max(plan->P_row, 1));
+  take(SNACK_ARR_RCUT, 4 * ((size_t)plan->P_row + 1));
   take(SNACK_ARR_COL_PTR, 4 * ((size_t)K + 1));
   take(SNACK_ARR_PERM, 4 * (size_t)n);
   take(SNACK_ARR_ROW_T, 4 * (size_t)n);
   take(SNACK_ARR_CPART_SEG, 4 * ((size_t)plan->P_col + 1));
   take(SNACK_ARR_CPART_NZ, 4 * ((size_t)plan->P_col + 1));
-  take(SNACK_ARR_CSPLIT, 12 * (size_t)std::max(plan->P_col, 1));
+  take(SNACK_ARR_CCUT, 4 * ((size_t)plan->P_col + 1));
   take(S_CARRY, 8 * (size_t)std::max(plan->P_row, plan->P_col) * (size_t)max_batch);
   take(S_KEYS_A, 4 * (size_t)n);
   take(S_KEYS_B, 4 * (size_t)n);
@@ -208,70 +206,58 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
   char* a = (char*)arena;
   const priv_layout L = priv_of(plan);
   char* priv = a + plan->off[SLOT_PRIV];
-  int32_t* small = (int32_t*)(priv + L.small);
-  int32_t* flags = (int32_t*)(priv + L.flags);
-  int32_t* flagscan = (int32_t*)(priv + L.flagscan);
+  int32_t* small = (int32_t*)(priv + L.small);  // [0] err bits, [1] row split, [2] col split
   void* tmp = priv + L.tmp;
   const int64_t nnz = plan->nnz;
+  int32_t* row_ptr = (int32_t*)(a + plan->off[SNACK_ARR_ROW_PTR]);
+  int32_t* col_ptr = (int32_t*)(a + plan->off[SNACK_ARR_COL_PTR]);
+  int32_t* perm = (int32_t*)(a + plan->off[SNACK_ARR_PERM]);
+  int32_t* row_t = (int32_t*)(a + plan->off[SNACK_ARR_ROW_T]);
 
-  // 1. validate, read back the error bits before trusting the COO
+  // Every kernel below is safe on an invalid COO (all writes are clamped);
+  // the error bits are read back once at the end, with the split flags.
   hipLaunchKernelGGL(k_zero_small, dim3(1), dim3(64), 0, s, small, 16);
-  if (launch_validate(row, col, nnz, plan->M, plan->K, small, s) != hipSuccess) return SNACK_E_HIP;
-  int32_t host_small[4] = {0, 0, 0, 0};
-  if (hipMemcpyAsync(host_small, small, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+  // 1. validation + row offsets, then the row-view tiles
+  if (launch_seg_bounds(row, col, nnz, plan->M, plan->K, row_ptr, small, s) != hipSuccess)
+    return SNACK_E_HIP;
+  if (launch_tiles(row_ptr, plan->M, nnz, plan->tile_row, plan->P_row,
+                   (int32_t*)(a + plan->off[SNACK_ARR_RPART_SEG]),
+                   (int32_t*)(a + plan->off[SNACK_ARR_RPART_NZ]),
+                   (int32_t*)(a + plan->off[SNACK_ARR_RCUT]), small + 1, s) != hipSuccess)
+    return SNACK_E_HIP;
+  // 2. column view: stable radix sort of the entry indices by column (the
+  //    last pass also gathers row_t = row[perm]), then offsets and tiles
+  if (nnz > 0) {
+    int bits = 0;
+    while (bits < 31 && ((uint32_t)(plan->K - 1) >> bits) != 0) ++bits;
+    uint32_t* const kbuf[2] = {(uint32_t*)(a + plan->off[S_KEYS_A]),
+                               (uint32_t*)(a + plan->off[S_KEYS_B])};
+    int32_t* const vbuf[2] = {perm, (int32_t*)(a + plan->off[S_VALS_B])};
+    if (radix_sort_u32((const uint32_t*)col, nullptr, kbuf, vbuf, nnz, bits, row, row_t, tmp,
+                       s) != hipSuccess)
+      return SNACK_E_HIP;
+    if (launch_seg_bounds((const int32_t*)kbuf[0], nullptr, nnz, plan->K, plan->K, col_ptr,
+                          nullptr, s) != hipSuccess)
+      return SNACK_E_HIP;
+  } else if (launch_seg_bounds(col, nullptr, 0, plan->K, plan->K, col_ptr, nullptr, s) !=
+             hipSuccess) {
+    return SNACK_E_HIP;
+  }
+  if (launch_tiles(col_ptr, plan->K, nnz, plan->tile_col, plan->P_col,
+                   (int32_t*)(a + plan->off[SNACK_ARR_CPART_SEG]),
+                   (int32_t*)(a + plan->off[SNACK_ARR_CPART_NZ]),
+                   (int32_t*)(a + plan->off[SNACK_ARR_CCUT]), small + 2, s) != hipSuccess)
+    return SNACK_E_HIP;
+
+  int32_t host_small[3] = {0, 0, 0};
+  if (hipMemcpyAsync(host_small, small, sizeof(host_small), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return SNACK_E_HIP;
   if (host_small[0] & 1) return SNACK_E_COO_RANGE;
   if (host_small[0] & 2) return SNACK_E_COO_ORDER;
-
-  // 2. row view
-  int32_t* row_ptr = (int32_t*)(a + plan->off[SNACK_ARR_ROW_PTR]);
-  if (launch_seg_ptr(row, nnz, plan->M, row_ptr, s) != hipSuccess) return SNACK_E_HIP;
-  if (launch_partition(row_ptr, plan->M, nnz, plan->tile_row, plan->P_row,
-                       (int32_t*)(a + plan->off[SNACK_ARR_RPART_SEG]),
-                       (int32_t*)(a + plan->off[SNACK_ARR_RPART_NZ]), flags, flagscan,
-                       (int32_t*)(a + plan->off[SNACK_ARR_RSPLIT]), small + 1, tmp,
-                       s) != hipSuccess)
-    return SNACK_E_HIP;
-
-  // 3. column view: stable radix sort of (col, k) by col
-  int32_t* perm = (int32_t*)(a + plan->off[SNACK_ARR_PERM]);
-  int32_t* row_t = (int32_t*)(a + plan->off[SNACK_ARR_ROW_T]);
-  uint32_t* keys_a = (uint32_t*)(a + plan->off[S_KEYS_A]);
-  uint32_t* keys_b = (uint32_t*)(a + plan->off[S_KEYS_B]);
-  int32_t* vals_b = (int32_t*)(a + plan->off[S_VALS_B]);
-  int32_t* col_ptr = (int32_t*)(a + plan->off[SNACK_ARR_COL_PTR]);
-  if (nnz > 0) {
-    hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s, col,
-                       (int32_t*)keys_a, nnz);
-    if (launch_iota_i32(perm, nnz, s) != hipSuccess) return SNACK_E_HIP;
-    int bits = 0;
-    while (bits < 31 && ((uint32_t)(plan->K - 1) >> bits) != 0) ++bits;
-    uint32_t* rk;
-    int32_t* rv;
-    if (radix_sort_u32(keys_a, perm, keys_b, vals_b, nnz, bits, &rk, &rv, tmp, s) != hipSuccess)
-      return SNACK_E_HIP;
-    if (rv != perm)
-      hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s, rv, perm,
-                         nnz);
-    if (launch_seg_ptr((const int32_t*)rk, nnz, plan->K, col_ptr, s) != hipSuccess)
-      return SNACK_E_HIP;
-    if (launch_gather_i32(row, perm, row_t, nnz, s) != hipSuccess) return SNACK_E_HIP;
-  } else {
-    if (launch_seg_ptr(col, 0, plan->K, col_ptr, s) != hipSuccess) return SNACK_E_HIP;
-  }
-  if (launch_partition(col_ptr, plan->K, nnz, plan->tile_col, plan->P_col,
-                       (int32_t*)(a + plan->off[SNACK_ARR_CPART_SEG]),
-                       (int32_t*)(a + plan->off[SNACK_ARR_CPART_NZ]), flags, flagscan,
-                       (int32_t*)(a + plan->off[SNACK_ARR_CSPLIT]), small + 2, tmp,
-                       s) != hipSuccess)
-    return SNACK_E_HIP;
-
-  if (hipMemcpyAsync(host_small, small, 12, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
-    return SNACK_E_HIP;
-  plan->n_split_row = host_small[1];
-  plan->n_split_col = host_small[2];
+  plan->has_split_row = host_small[1] ? 1 : 0;
+  plan->has_split_col = host_small[2] ? 1 : 0;
   plan->prepared = 1;
   return SNACK_OK;
 }
@@ -283,13 +269,13 @@ const void* snack_plan_array(const snack_plan* plan, int32_t which, int64_t* cou
     case SNACK_ARR_ROW_PTR: n = (int64_t)plan->M + 1; break;
     case SNACK_ARR_RPART_SEG:
     case SNACK_ARR_RPART_NZ: n = (int64_t)plan->P_row + 1; break;
-    case SNACK_ARR_RSPLIT: n = 3 * (int64_t)plan->n_split_row; break;
+    case SNACK_ARR_RCUT: n = (int64_t)plan->P_row + 1; break;
     case SNACK_ARR_COL_PTR: n = (int64_t)plan->K + 1; break;
     case SNACK_ARR_PERM:
     case SNACK_ARR_ROW_T: n = plan->nnz; break;
     case SNACK_ARR_CPART_SEG:
     case SNACK_ARR_CPART_NZ: n = (int64_t)plan->P_col + 1; break;
-    case SNACK_ARR_CSPLIT: n = 3 * (int64_t)plan->n_split_col; break;
+    case SNACK_ARR_CCUT: n = (int64_t)plan->P_col + 1; break;
   }
   if (count) *count = n;
   return (const char*)plan->arena + plan->off[which];

@@ -66,6 +66,52 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// ---------------------------------------------------------------- scans
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < SNK_WAVE; d <<= 1) {
+    int32_t y = __shfl_up(x, d, SNK_WAVE);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix of one value per thread across a block of NTHREADS
+// threads (a multiple of 64); *total receives the block sum.  lds must hold
+// NTHREADS/64 ints.  Contains barriers: call from all threads.
+template <int NTHREADS>
+__device__ __forceinline__ int32_t block_excl_scan_i32(int32_t x, int32_t* lds, int32_t* total) {
+  const int w = threadIdx.x / SNK_WAVE;
+  const int32_t inc = wave_incl_scan_i32(x);
+  if (lane_id() == SNK_WAVE - 1) lds[w] = inc;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NTHREADS / SNK_WAVE; ++i) {
+    const int32_t t = lds[i];
+    if (i < w) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+// Add 1 to h[d] (LDS histogram of 256 bins) for every active lane with
+// valid set, aggregating equal digits across the wave first: 8 ballots find
+// the lanes sharing this lane's digit, the lowest of them adds the count.
+// Skewed digit distributions then cost one LDS atomic per distinct digit.
+__device__ __forceinline__ void wave_hist_add(int32_t* h, uint32_t d, bool valid) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t m = __ballot((d >> b) & 1u);
+    peers &= ((d >> b) & 1u) ? m : ~m;
+  }
+  if (valid && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&h[d], __popcll(peers));
+}
+
 }  // namespace snk
 
 #define SNK_CHECK_LAUNCH()                                   \

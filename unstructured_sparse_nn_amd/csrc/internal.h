@@ -18,17 +18,17 @@ hipError_t exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_
                               void* tmp, hipStream_t s);
 
 // ---- stable LSD radix sort of (key, value) pairs ---------------------------
-// Sorts n pairs by the low `bits` bits of the key (8 bits per pass).  keys /
-// vals are the input; keys_alt / vals_alt are equally sized scratch.  The
-// sorted result ends in whichever buffer pair the last pass wrote;
-// *res_keys / *res_vals point to it.  tmp must hold radix_tmp_bytes(n).
+// Sorts n pairs by the low `bits` bits of the key (8 bits per pass, at least
+// one pass).  Input (keys_in, vals_in) is read only; vals_in == NULL means
+// value = index.  kbuf/vbuf are two buffer pairs of n elements; the sorted
+// result always ends in kbuf[0] / vbuf[0].  If gsrc != NULL the last pass
+// also writes gout[i] = gsrc[value[i]].  tmp must hold radix_tmp_bytes(n).
 size_t radix_tmp_bytes(int64_t n);
-hipError_t radix_sort_u32(uint32_t* keys, int32_t* vals, uint32_t* keys_alt, int32_t* vals_alt,
-                          int64_t n, int bits, uint32_t** res_keys, int32_t** res_vals,
-                          void* tmp, hipStream_t s);
-hipError_t radix_sort_u64(uint64_t* keys, int32_t* vals, uint64_t* keys_alt, int32_t* vals_alt,
-                          int64_t n, int bits, uint64_t** res_keys, int32_t** res_vals,
-                          void* tmp, hipStream_t s);
+hipError_t radix_sort_u32(const uint32_t* keys_in, const int32_t* vals_in, uint32_t* const kbuf[2],
+                          int32_t* const vbuf[2], int64_t n, int bits, const int32_t* gsrc,
+                          int32_t* gout, void* tmp, hipStream_t s);
+hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint64_t* const kbuf[2],
+                          int32_t* const vbuf[2], int64_t n, int bits, void* tmp, hipStream_t s);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -40,11 +40,11 @@ struct seg_view {          // one compressed view of the sparse matrix
   const int32_t* perm;     // [nnz] value permutation (NULL = identity)
   const int32_t* part_seg; // [P+1]
   const int32_t* part_nz;  // [P+1]
-  const int32_t* split;    // [3*n_split] (segment, first tile, last tile)
+  const int32_t* cut;      // [P+1] 1 if the cut starting tile p lies inside a segment
   int32_t S;               // segments (output features)
   int32_t F;               // gathered features (input features)
   int32_t P;               // tiles
-  int32_t n_split;
+  int32_t has_split;       // any inner cut (some segment spans tiles)
   int32_t tile;            // items per tile of this view
   int64_t nnz;
 };
@@ -62,17 +62,11 @@ hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_
                              hipStream_t s);
 
 // ---- prepare (prepare.hip) ----------------------------------------------------
-hipError_t launch_validate(const int32_t* row, const int32_t* col, int64_t nnz, int32_t M,
-                           int32_t K, int32_t* err, hipStream_t s);
-hipError_t launch_seg_ptr(const int32_t* sorted_keys, int64_t nnz, int32_t S, int32_t* ptr,
-                          hipStream_t s);
-hipError_t launch_partition(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
-                            int32_t* part_seg, int32_t* part_nz, int32_t* flags_first,
-                            int32_t* flags_scan, int32_t* split, int32_t* n_split_dev,
-                            void* scan_tmp, hipStream_t s);
-hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int32_t* dst, int64_t n,
-                             hipStream_t s);
-hipError_t launch_iota_i32(int32_t* dst, int64_t n, hipStream_t s);
+hipError_t launch_seg_bounds(const int32_t* keys, const int32_t* col, int64_t nnz, int32_t S,
+                             int32_t K, int32_t* ptr, int32_t* err, hipStream_t s);
+hipError_t launch_tiles(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
+                        int32_t* part_seg, int32_t* part_nz, int32_t* cut, int32_t* any_split,
+                        hipStream_t s);
 
 // ---- aux kernels (aux.hip) ------------------------------------------------------
 hipError_t launch_gelu_fwd(const float* z, float* h, int64_t n, hipStream_t s);

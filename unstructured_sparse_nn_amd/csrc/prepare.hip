@@ -1,4 +1,4 @@
-// prepare.hip -- COO validation, segment offsets, load-balanced tiles (gfx950).
+// prepare.hip -- COO validation, segment offsets and load-balanced tiles (gfx950).
 //
 // The tiles cut the merge path of segment ends and entries (Merrill &
 // Garland, "Merge-based Parallel Sparse Matrix-Vector Multiplication", SC'16)
@@ -7,6 +7,13 @@
 // rows are never split, and only long rows spill across tiles -- the answer
 // to the imbalance described in "Two Lotteries: What It Takes to Make
 // Sparsity Fast" (paragraph on who does the work).
+//
+// Both kernels here are single passes over sorted data with no searches:
+// offsets are written where the sorted key changes, and the cuts are
+// enumerated per segment (segment s owns path items ptr[s]+s .. ptr[s+1]+s,
+// so the cuts inside it are the multiples of T in that range).  Every write
+// is clamped to its array, so an invalid COO is reported through `err`
+// without any out-of-bounds access.
 #include "common.h"
 #include "internal.h"
 
@@ -14,163 +21,88 @@ namespace snk {
 
 constexpr int PREP_THREADS = 256;
 
-// err bit 0: index out of range; bit 1: not strictly increasing.
-__global__ __launch_bounds__(PREP_THREADS) void k_validate(const int32_t* __restrict__ row,
-                                                           const int32_t* __restrict__ col,
-                                                           int64_t nnz, int32_t M, int32_t K,
-                                                           int32_t* __restrict__ err) {
-  int64_t k = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (k >= nnz) return;
-  int32_t r = row[k], c = col[k];
-  int32_t bits = 0;
-  if (r < 0 || r >= M || c < 0 || c >= K) bits |= 1;
-  if (k > 0) {
-    int64_t lin = (int64_t)r * K + c;
-    int64_t prev = (int64_t)row[k - 1] * K + col[k - 1];
-    if (lin <= prev) bits |= 2;
+// ptr[r] = first position k whose key is >= r, for r in [0, S], from keys
+// sorted ascending: thread k writes ptr[r] = k for key[k-1] < r <= key[k];
+// thread nnz closes the trailing segments with nnz.  With `col` non-NULL the
+// keys are the COO rows and the COO is validated: err bit 0 = index out of
+// range, bit 1 = not strictly increasing in row*K + col.
+__global__ __launch_bounds__(PREP_THREADS) void k_seg_bounds(const int32_t* __restrict__ keys,
+                                                             const int32_t* __restrict__ col,
+                                                             int64_t nnz, int32_t S, int32_t K,
+                                                             int32_t* __restrict__ ptr,
+                                                             int32_t* __restrict__ err) {
+  const int64_t k = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
+  if (k > nnz) return;
+  const int64_t prev = k > 0 ? (int64_t)keys[k - 1] : -1;
+  const int64_t key = k < nnz ? (int64_t)keys[k] : (int64_t)S;
+  const int64_t lo = std::max<int64_t>(prev + 1, 0), hi = std::min<int64_t>(key, S);
+  for (int64_t r = lo; r <= hi; ++r) ptr[r] = (int32_t)k;
+  if (col && k < nnz) {
+    const int32_t c = col[k];
+    int32_t bits = 0;
+    if (key < 0 || key >= S || c < 0 || c >= K) bits |= 1;
+    if (k > 0) {
+      const int64_t lin = key * K + c;
+      const int64_t plin = prev * K + col[k - 1];
+      if (lin <= plin) bits |= 2;
+    }
+    if (bits) atomicOr(err, bits);
   }
-  if (bits) atomicOr(err, bits);
 }
 
-// ptr[s] = first position whose key is >= s, for s in [0, S] (keys sorted).
-__global__ __launch_bounds__(PREP_THREADS) void k_seg_ptr(const int32_t* __restrict__ keys,
-                                                          int64_t nnz, int32_t S,
-                                                          int32_t* __restrict__ ptr) {
-  int64_t s = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
+// Tile start points, enumerated per segment.  Cut p (at item p*T) that falls
+// on segment s is (s, p*T - s) if s is long (>= T entries) and the cut is
+// past its first entry -- an "inner" cut, cut[p] = 1 -- else (s, ptr[s]).
+// Thread S writes the closing point (S, nnz).  any_split is set when an inner
+// cut exists.
+__global__ __launch_bounds__(PREP_THREADS) void k_tiles(const int32_t* __restrict__ ptr,
+                                                        int32_t S, int64_t nnz, int32_t T,
+                                                        int32_t P, int32_t* __restrict__ part_seg,
+                                                        int32_t* __restrict__ part_nz,
+                                                        int32_t* __restrict__ cut,
+                                                        int32_t* __restrict__ any_split) {
+  const int64_t s = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
   if (s > S) return;
-  int64_t lo = 0, hi = nnz;
-  while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
-    if (keys[mid] < s) lo = mid + 1; else hi = mid;
-  }
-  ptr[s] = (int32_t)lo;
-}
-
-// Tile start points.  Segment s owns path items ptr[s]+s .. ptr[s+1]+s (its
-// entries, then its end); the segment holding item d = p*T is the number of
-// segments whose end item lies before d.
-__global__ __launch_bounds__(PREP_THREADS) void k_partition(const int32_t* __restrict__ ptr,
-                                                            int32_t S, int64_t nnz, int32_t T,
-                                                            int32_t P,
-                                                            int32_t* __restrict__ part_seg,
-                                                            int32_t* __restrict__ part_nz) {
-  int64_t p = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (p > P) return;
-  if (p == P) {
-    part_seg[p] = S;
-    part_nz[p] = (int32_t)nnz;
+  if (s == S) {
+    part_seg[P] = S;
+    part_nz[P] = (int32_t)nnz;
+    cut[P] = 0;
     return;
   }
-  int64_t d = p * (int64_t)T;
-  int64_t lo = 0, hi = S;  // count of t with ptr[t+1] + t < d
-  while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
-    if ((int64_t)ptr[mid + 1] + mid < d) lo = mid + 1; else hi = mid;
+  const int64_t a = ptr[s], b = ptr[s + 1];
+  if (a < 0 || b < a || b > nnz) return;  // invalid COO: reported by k_seg_bounds
+  const int64_t first = a + s, last = b + s;
+  const int64_t p0 = (first + T - 1) / T;
+  const int64_t p1 = std::min<int64_t>(last / T, (int64_t)P - 1);
+  const bool is_long = (b - a) >= T;
+  bool any = false;
+  for (int64_t p = p0; p <= p1; ++p) {
+    const int64_t z = p * T - s;
+    const bool inner = is_long && z != a;
+    part_seg[p] = (int32_t)s;
+    part_nz[p] = (int32_t)(inner ? z : a);
+    cut[p] = inner ? 1 : 0;
+    any |= inner;
   }
-  int32_t s = (int32_t)lo;
-  int64_t z = d - s;
-  int32_t a = ptr[s], b = ptr[s + 1];
-  if (z != a && (b - a) < T) z = a;
-  part_seg[p] = s;
-  part_nz[p] = (int32_t)z;
-}
-
-__device__ __forceinline__ bool inner_cut(const int32_t* ptr, const int32_t* ps,
-                                          const int32_t* pz, int64_t p, int32_t P) {
-  if (p <= 0 || p >= P) return false;
-  return pz[p] > ptr[ps[p]];
-}
-
-// first[p] = 1 if tile p's start is the first cut inside a split segment.
-__global__ __launch_bounds__(PREP_THREADS) void k_split_flags(const int32_t* __restrict__ ptr,
-                                                              const int32_t* __restrict__ ps,
-                                                              const int32_t* __restrict__ pz,
-                                                              int32_t P,
-                                                              int32_t* __restrict__ first) {
-  int64_t p = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (p >= P) return;
-  bool in = inner_cut(ptr, ps, pz, p, P);
-  bool prev_same = in && inner_cut(ptr, ps, pz, p - 1, P) && ps[p - 1] == ps[p];
-  first[p] = (in && !prev_same) ? 1 : 0;
-}
-
-// Split j: (segment, tile holding its first entry, tile holding its end).
-__global__ __launch_bounds__(PREP_THREADS) void k_split_write(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ ps,
-    const int32_t* __restrict__ pz, int32_t P, const int32_t* __restrict__ first,
-    const int32_t* __restrict__ scan, int32_t* __restrict__ split) {
-  int64_t p = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (p >= P) return;
-  if (!inner_cut(ptr, ps, pz, p, P)) return;
-  int32_t j = scan[p] + first[p] - 1;
-  if (first[p]) {
-    split[3 * j + 0] = ps[p];
-    split[3 * j + 1] = (int32_t)(p - 1);
-  }
-  bool next_same = inner_cut(ptr, ps, pz, p + 1, P) && ps[p + 1] == ps[p];
-  if (!next_same) split[3 * j + 2] = (int32_t)p;
-}
-
-__global__ __launch_bounds__(PREP_THREADS) void k_gather_i32(const int32_t* __restrict__ src,
-                                                             const int32_t* __restrict__ idx,
-                                                             int32_t* __restrict__ dst,
-                                                             int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (i < n) dst[i] = src[idx[i]];
-}
-
-__global__ __launch_bounds__(PREP_THREADS) void k_iota_i32(int32_t* __restrict__ dst, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * PREP_THREADS + threadIdx.x;
-  if (i < n) dst[i] = (int32_t)i;
+  if (any) atomicOr(any_split, 1);
 }
 
 static inline dim3 grid_for(int64_t n) {
   return dim3((unsigned)std::max<int64_t>(1, cdiv(n, PREP_THREADS)));
 }
 
-hipError_t launch_validate(const int32_t* row, const int32_t* col, int64_t nnz, int32_t M,
-                           int32_t K, int32_t* err, hipStream_t s) {
-  if (nnz > 0)
-    hipLaunchKernelGGL(k_validate, grid_for(nnz), dim3(PREP_THREADS), 0, s, row, col, nnz, M, K,
-                       err);
+hipError_t launch_seg_bounds(const int32_t* keys, const int32_t* col, int64_t nnz, int32_t S,
+                             int32_t K, int32_t* ptr, int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(k_seg_bounds, grid_for(nnz + 1), dim3(PREP_THREADS), 0, s, keys, col, nnz,
+                     S, K, ptr, err);
   return hipGetLastError();
 }
 
-hipError_t launch_seg_ptr(const int32_t* keys, int64_t nnz, int32_t S, int32_t* ptr,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(k_seg_ptr, grid_for((int64_t)S + 1), dim3(PREP_THREADS), 0, s, keys, nnz,
-                     S, ptr);
-  return hipGetLastError();
-}
-
-hipError_t launch_partition(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
-                            int32_t* part_seg, int32_t* part_nz, int32_t* flags_first,
-                            int32_t* flags_scan, int32_t* split, int32_t* n_split_dev,
-                            void* scan_tmp, hipStream_t s) {
-  hipLaunchKernelGGL(k_partition, grid_for((int64_t)P + 1), dim3(PREP_THREADS), 0, s, ptr, S,
-                     nnz, T, P, part_seg, part_nz);
-  if (P > 0) {
-    hipLaunchKernelGGL(k_split_flags, grid_for(P), dim3(PREP_THREADS), 0, s, ptr, part_seg,
-                       part_nz, P, flags_first);
-  }
-  hipError_t e = exclusive_scan_i32(flags_first, flags_scan, P, n_split_dev, scan_tmp, s);
-  if (e != hipSuccess) return e;
-  if (P > 0) {
-    hipLaunchKernelGGL(k_split_write, grid_for(P), dim3(PREP_THREADS), 0, s, ptr, part_seg,
-                       part_nz, P, flags_first, flags_scan, split);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int32_t* dst, int64_t n,
-                             hipStream_t s) {
-  if (n > 0)
-    hipLaunchKernelGGL(k_gather_i32, grid_for(n), dim3(PREP_THREADS), 0, s, src, idx, dst, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_iota_i32(int32_t* dst, int64_t n, hipStream_t s) {
-  if (n > 0) hipLaunchKernelGGL(k_iota_i32, grid_for(n), dim3(PREP_THREADS), 0, s, dst, n);
+hipError_t launch_tiles(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
+                        int32_t* part_seg, int32_t* part_nz, int32_t* cut, int32_t* any_split,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_tiles, grid_for((int64_t)S + 1), dim3(PREP_THREADS), 0, s, ptr, S, nnz, T,
+                     P, part_seg, part_nz, cut, any_split);
   return hipGetLastError();
 }
 

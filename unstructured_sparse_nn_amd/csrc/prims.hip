@@ -98,6 +98,28 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_block_scan(const int32_t* in, 
 
 __global__ void k_zero_i32(int32_t* p) { *p = 0; }
 
+// One workgroup scans up to SCAN_SINGLE_MAX elements in coalesced chunks of
+// 1024 (one element per thread), carrying the running total between chunks.
+// Saves two launches against the three-kernel scan on small arrays.
+constexpr int64_t SCAN_SINGLE_MAX = 1 << 15;
+constexpr int SCAN_SINGLE_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_SINGLE_THREADS) void k_scan_single(const int32_t* in,
+                                                                     int32_t* out, int64_t n,
+                                                                     int32_t* __restrict__ total) {
+  __shared__ int32_t lds[SCAN_SINGLE_THREADS / SNK_WAVE];
+  int32_t carry = 0;
+  for (int64_t c = 0; c < n; c += SCAN_SINGLE_THREADS) {
+    const int64_t i = c + threadIdx.x;
+    const int32_t v = i < n ? in[i] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan_i32<SCAN_SINGLE_THREADS>(v, lds, &tot);
+    if (i < n) out[i] = carry + ex;
+    carry += tot;
+  }
+  if (total && threadIdx.x == 0) *total = carry;
+}
+
 size_t scan_tmp_bytes(int64_t n) {
   return align_up(sizeof(int32_t) * (size_t)std::max<int64_t>(1, cdiv(n, SCAN_BLOCK)), 256);
 }
@@ -106,6 +128,11 @@ hipError_t exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_
                               void* tmp, hipStream_t s) {
   if (n <= 0) {
     if (total) hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, s, total);
+    return hipGetLastError();
+  }
+  if (n <= SCAN_SINGLE_MAX) {
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(SCAN_SINGLE_THREADS), 0, s, in, out, n,
+                       total);
     return hipGetLastError();
   }
   int64_t nb = cdiv(n, SCAN_BLOCK);
@@ -133,53 +160,101 @@ __global__ __launch_bounds__(RS_THREADS) void k_radix_hist(const KT* __restrict_
   h[threadIdx.x] = 0;
   __syncthreads();
   int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+  KT key[RS_ROUNDS];
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
     int64_t i = base + r * RS_THREADS + threadIdx.x;
-    if (i < n) atomicAdd(&h[(uint32_t)(keys[i] >> shift) & 255u], 1);
+    key[r] = i < n ? keys[i] : (KT)0;
+  }
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    int64_t i = base + r * RS_THREADS + threadIdx.x;
+    wave_hist_add(h, (uint32_t)(key[r] >> shift) & 255u, i < n);
   }
   __syncthreads();
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
 }
 
-// Stable scatter: items of a block are taken in index order, round by round;
-// within a wave, lanes holding the same digit are found with 8 ballots (one
-// per digit bit) and ranked by lane order.
+// hist is digit-major [256][nblk].  Workgroup d turns row d into exclusive
+// prefixes over the blocks (in place) and writes the row total to
+// dtotal[d]; the scatter adds the digit's base (sum of smaller digits).
+__global__ __launch_bounds__(RS_THREADS) void k_radix_scan_digits(int32_t* __restrict__ hist,
+                                                                  int64_t nblk,
+                                                                  int32_t* __restrict__ dtotal) {
+  __shared__ int32_t lds[RS_THREADS / SNK_WAVE];
+  int32_t* row = hist + (int64_t)blockIdx.x * nblk;
+  int32_t carry = 0;
+  for (int64_t c = 0; c < nblk; c += RS_THREADS) {
+    const int64_t i = c + threadIdx.x;
+    const int32_t v = i < nblk ? row[i] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan_i32<RS_THREADS>(v, lds, &tot);
+    if (i < nblk) row[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) dtotal[blockIdx.x] = carry;
+}
+
+// Stable scatter: all items of a block are loaded up front (one round trip),
+// then ranked in index order, round by round; within a wave, lanes holding
+// the same digit are found with 8 ballots (one per digit bit) and ranked by
+// lane order.  vin == NULL means value = index.  If gsrc != NULL the pass
+// also writes gout[pos] = gsrc[value] (a gather fused into the scatter).
 template <typename KT>
 __global__ __launch_bounds__(RS_THREADS) void k_radix_scatter(
     const KT* __restrict__ kin, const int32_t* __restrict__ vin, KT* __restrict__ kout,
     int32_t* __restrict__ vout, int64_t n, int shift, const int32_t* __restrict__ offs,
-    int64_t nblk) {
+    int64_t nblk, const int32_t* __restrict__ dtotal, const int32_t* __restrict__ gsrc,
+    int32_t* __restrict__ gout) {
   __shared__ int32_t running[256];
   __shared__ int32_t wcnt[RS_WAVES][256];
+  __shared__ int32_t lds[RS_WAVES];
   const int t = threadIdx.x;
   const int w = t / SNK_WAVE;
-  running[t] = offs[(int64_t)t * nblk + blockIdx.x];
+  int32_t dsum;
+  const int32_t dbase = block_excl_scan_i32<RS_THREADS>(dtotal[t], lds, &dsum);
+  running[t] = dbase + offs[(int64_t)t * nblk + blockIdx.x];
 #pragma unroll
   for (int i = 0; i < RS_WAVES; ++i) wcnt[i][t] = 0;
-  __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
-  const uint64_t lt = lanemask_lt();
+  KT key[RS_ROUNDS];
+  int32_t val[RS_ROUNDS];
+#pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
-    int64_t i = base + r * RS_THREADS + t;
-    bool valid = i < n;
-    KT key = valid ? kin[i] : (KT)0;
-    int32_t val = valid ? vin[i] : 0;
-    uint32_t d = (uint32_t)(key >> shift) & 255u;
+    const int64_t i = base + r * RS_THREADS + t;
+    key[r] = i < n ? kin[i] : (KT)0;
+    val[r] = i < n ? (vin ? vin[i] : (int32_t)i) : 0;
+  }
+  int32_t gv[RS_ROUNDS];
+  if (gsrc) {
+#pragma unroll
+    for (int r = 0; r < RS_ROUNDS; ++r) {
+      const int64_t i = base + r * RS_THREADS + t;
+      gv[r] = i < n ? gsrc[val[r]] : 0;
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    const int64_t i = base + r * RS_THREADS + t;
+    const bool valid = i < n;
+    const uint32_t d = (uint32_t)(key[r] >> shift) & 255u;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       uint64_t m = __ballot((d >> b) & 1u);
       peers &= ((d >> b) & 1u) ? m : ~m;
     }
-    int rank = __popcll(peers & lt);
+    const int rank = __popcll(peers & lt);
     if (valid && rank == 0) wcnt[w][d] = __popcll(peers);
     __syncthreads();
     if (valid) {
       int32_t pos = running[d] + rank;
       for (int j = 0; j < w; ++j) pos += wcnt[j][d];
-      kout[pos] = key;
-      vout[pos] = val;
+      kout[pos] = key[r];
+      vout[pos] = val[r];
+      if (gsrc) gout[pos] = gv[r];
     }
     __syncthreads();
     int32_t add = 0;
@@ -195,49 +270,48 @@ __global__ __launch_bounds__(RS_THREADS) void k_radix_scatter(
 
 size_t radix_tmp_bytes(int64_t n) {
   int64_t nblk = std::max<int64_t>(1, cdiv(n, RS_BLOCK));
-  return align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256) + scan_tmp_bytes(256 * nblk);
+  return align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256) + 256 * sizeof(int32_t);
 }
 
+// Passes read (keys_in, vals_in) first, then ping-pong between the two
+// buffer pairs so that the last pass writes kbuf[0] / vbuf[0].
 template <typename KT>
-static hipError_t radix_sort(KT* keys, int32_t* vals, KT* keys_alt, int32_t* vals_alt, int64_t n,
-                             int bits, KT** res_keys, int32_t** res_vals, void* tmp,
-                             hipStream_t s) {
-  KT* ka = keys;
-  KT* kb = keys_alt;
-  int32_t* va = vals;
-  int32_t* vb = vals_alt;
-  if (n > 0) {
-    int64_t nblk = cdiv(n, RS_BLOCK);
-    int32_t* hist = (int32_t*)tmp;
-    void* stmp = (char*)tmp + align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256);
-    for (int shift = 0; shift < bits; shift += 8) {
-      hipLaunchKernelGGL(k_radix_hist<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, ka, n,
-                         shift, hist, nblk);
-      hipError_t e = exclusive_scan_i32(hist, hist, 256 * nblk, nullptr, stmp, s);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_radix_scatter<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, ka,
-                         va, kb, vb, n, shift, hist, nblk);
-      std::swap(ka, kb);
-      std::swap(va, vb);
-    }
+static hipError_t radix_sort(const KT* keys_in, const int32_t* vals_in, KT* const kbuf[2],
+                             int32_t* const vbuf[2], int64_t n, int bits, const int32_t* gsrc,
+                             int32_t* gout, void* tmp, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int passes = std::max(1, (bits + 7) / 8);
+  const int64_t nblk = cdiv(n, RS_BLOCK);
+  int32_t* hist = (int32_t*)tmp;
+  int32_t* dtotal = (int32_t*)((char*)tmp + align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256));
+  const KT* kin = keys_in;
+  const int32_t* vin = vals_in;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = 8 * p;
+    const int o = (passes - 1 - p) & 1;
+    const bool last = p == passes - 1;
+    hipLaunchKernelGGL(k_radix_hist<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, kin, n,
+                       shift, hist, nblk);
+    hipLaunchKernelGGL(k_radix_scan_digits, dim3(256), dim3(RS_THREADS), 0, s, hist, nblk,
+                       dtotal);
+    hipLaunchKernelGGL(k_radix_scatter<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, kin,
+                       vin, kbuf[o], vbuf[o], n, shift, hist, nblk, dtotal,
+                       last ? gsrc : nullptr, last ? gout : nullptr);
+    kin = kbuf[o];
+    vin = vbuf[o];
   }
-  *res_keys = ka;
-  *res_vals = va;
   return hipGetLastError();
 }
 
-hipError_t radix_sort_u32(uint32_t* keys, int32_t* vals, uint32_t* keys_alt, int32_t* vals_alt,
-                          int64_t n, int bits, uint32_t** res_keys, int32_t** res_vals,
-                          void* tmp, hipStream_t s) {
-  return radix_sort<uint32_t>(keys, vals, keys_alt, vals_alt, n, bits, res_keys, res_vals, tmp,
-                              s);
+hipError_t radix_sort_u32(const uint32_t* keys_in, const int32_t* vals_in, uint32_t* const kbuf[2],
+                          int32_t* const vbuf[2], int64_t n, int bits, const int32_t* gsrc,
+                          int32_t* gout, void* tmp, hipStream_t s) {
+  return radix_sort<uint32_t>(keys_in, vals_in, kbuf, vbuf, n, bits, gsrc, gout, tmp, s);
 }
 
-hipError_t radix_sort_u64(uint64_t* keys, int32_t* vals, uint64_t* keys_alt, int32_t* vals_alt,
-                          int64_t n, int bits, uint64_t** res_keys, int32_t** res_vals,
-                          void* tmp, hipStream_t s) {
-  return radix_sort<uint64_t>(keys, vals, keys_alt, vals_alt, n, bits, res_keys, res_vals, tmp,
-                              s);
+hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint64_t* const kbuf[2],
+                          int32_t* const vbuf[2], int64_t n, int bits, void* tmp, hipStream_t s) {
+  return radix_sort<uint64_t>(keys_in, vals_in, kbuf, vbuf, n, bits, nullptr, nullptr, tmp, s);
 }
 
 }  // namespace snk

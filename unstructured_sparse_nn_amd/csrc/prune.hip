@@ -9,43 +9,54 @@
 //   write  survivors + grown back in place, sorted row-major.
 // Everything is integer and order-independent, so the mask is bit-exact.
 //
-// Device plan: a 4-pass (8-bit digit) radix select finds the magnitude of
-// the n_drop-th smallest key and how many entries of exactly that magnitude
-// are dropped (the first ones in index order, found with a scan); survivors
-// are compacted with scans.  Regrowth draws candidates in chunks of C
-// stream positions: candidates are radix-sorted by position (stable, so equal
-// positions stay in stream order), a candidate is acceptable when it is the
-// first occurrence of its position, not in the old support and not taken by
-// an earlier chunk (binary searches), and the first `need` acceptable ones in
-// stream order are kept (a scan over stream order).  The host reads back one
-// counter per chunk.  Finally survivors and grown positions, both sorted,
-// are merged by rank.
+// Device plan (one host readback in the common case):
+//   select    radix select of the n_drop-th smallest magnitude, per 8-bit
+//             digit (2 passes for bf16, 4 for fp32): blocks build local
+//             histograms and add them into replicated global ones, then one
+//             workgroup sums them and picks the digit;
+//   classify  per 1024-entry block: count entries below / at the threshold;
+//             one workgroup turns the counts into block offsets (ties at the
+//             threshold are dropped in index order); a third kernel writes
+//             the survivors, the dropped list and the old support;
+//   regrow    candidates are drawn C stream positions at a time and radix
+//             sorted by position (stable: equal positions keep stream
+//             order); a candidate is acceptable if it is the first
+//             occurrence of its position and lies outside the old support
+//             and the positions taken by earlier chunks (binary searches);
+//             the first `need` acceptable ones in stream order are kept (a
+//             scan over stream order) and compacted in position order (a
+//             scan over sorted order);
+//   merge     survivors and grown positions, both sorted, are merged by rank
+//             straight into row/col/vals.  It is launched before the
+//             readback and does nothing unless the step is complete and no
+//             NaN was seen, so the COO is untouched on error.
 #include "common.h"
 #include "internal.h"
 
 namespace snk {
 
 constexpr int PR_THREADS = 256;
+constexpr int PR_PER_THREAD = 4;
+constexpr int PR_BLOCK = PR_THREADS * PR_PER_THREAD;  // entries per classify block
+constexpr int PR_REPL = 64;
 
 struct pr_state {
   uint32_t prefix;   // radix-select: magnitude bits fixed so far
   uint32_t mask;
-  int32_t need;      // drops still to place at the current prefix
+  int32_t need;      // drops still to place among entries matching prefix
   int32_t err;       // 1 = NaN seen
-  int32_t got;       // grown positions accepted so far
-  int32_t total_ok;  // acceptable candidates in the current chunk
-  int32_t n_new;     // positions accepted from the current chunk
+  int32_t got;       // grown positions accepted by committed chunks
+  int32_t n_new;     // positions accepted by the latest chunk
+  int32_t total_ok;  // acceptable candidates in the latest chunk
   int32_t pad;
-  int32_t hist[256];
+  // select histograms, spread over PR_REPL replicas (block b adds into
+  // replica b % PR_REPL) so that skewed digits do not serialise on a few
+  // global atomics
+  int32_t hist[4][PR_REPL][256];
 };
 
 // SplitMix64: state advances by the golden gamma; output = variant-13 mix.
-__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-static inline uint64_t sm64_mix_host(uint64_t z) {
+__host__ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
@@ -56,166 +67,262 @@ static inline dim3 g1(int64_t n) {
   return dim3((unsigned)std::max<int64_t>(1, cdiv(n, PR_THREADS)));
 }
 
-__global__ void k_pr_state_init(pr_state* st, int32_t n_drop) {
-  int t = threadIdx.x;
-  st->hist[t] = 0;
+template <typename T>
+__device__ __forceinline__ uint32_t raw_bits(T v) {
+  if constexpr (sizeof(T) == 4) return __float_as_uint(v);
+  else return (uint32_t)v;
+}
+template <typename T>
+__device__ __forceinline__ uint32_t magnitude(uint32_t bits) {
+  return sizeof(T) == 2 ? (bits & 0x7FFFu) : (bits & 0x7FFFFFFFu);
+}
+template <typename T>
+__device__ __forceinline__ bool is_nan_mag(uint32_t a) {
+  return sizeof(T) == 2 ? (a > 0x7F80u) : (a > 0x7F800000u);
+}
+
+// grid: PR_REPL blocks of 256 threads
+__global__ void k_pr_init(pr_state* st, int32_t n_drop) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) st->hist[p][blockIdx.x][t] = 0;
+  if (blockIdx.x != 0) return;
   if (t == 0) {
     st->prefix = 0;
     st->mask = 0;
     st->need = n_drop;
     st->err = 0;
     st->got = 0;
-    st->total_ok = 0;
     st->n_new = 0;
+    st->total_ok = 0;
   }
 }
 
+// One radix-select pass over the digit at `shift`: each block histograms
+// PR_BLOCK magnitudes (wave-aggregated LDS atomics) and adds its histogram
+// into replica blockIdx % PR_REPL.  No fence or last-block handshake: the
+// digit is picked by k_sel_pick after the kernel boundary (an agent-scope
+// fence per block would write back the L2).
 template <typename T>
-__global__ __launch_bounds__(PR_THREADS) void k_pr_keys(
-    const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
-    int64_t nnz, int32_t K, uint32_t* __restrict__ mag, int64_t* __restrict__ lin,
-    uint32_t* __restrict__ vbits, pr_state* st) {
-  int64_t k = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
-  if (k >= nnz) return;
-  uint32_t b;
-  if constexpr (sizeof(T) == 4) b = __float_as_uint(vals[k]);
-  else b = (uint32_t)vals[k];
-  uint32_t a = sizeof(T) == 2 ? (b & 0x7FFFu) : (b & 0x7FFFFFFFu);
-  bool nan = sizeof(T) == 2 ? (a > 0x7F80u) : (a > 0x7F800000u);
-  if (nan) atomicOr(&st->err, 1);
-  mag[k] = a;
-  vbits[k] = b;
-  lin[k] = (int64_t)row[k] * K + col[k];
-}
-
-__global__ __launch_bounds__(PR_THREADS) void k_sel_hist(const uint32_t* __restrict__ mag,
-                                                         int64_t nnz, int shift, pr_state* st) {
+__global__ __launch_bounds__(PR_THREADS) void k_sel_hist(const T* __restrict__ vals, int64_t nnz,
+                                                         int shift, int pass, pr_state* st) {
   __shared__ int32_t h[256];
-  h[threadIdx.x] = 0;
+  const int t = threadIdx.x;
+  h[t] = 0;
   __syncthreads();
   const uint32_t prefix = st->prefix, mask = st->mask;
-  for (int64_t k = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x; k < nnz;
-       k += (int64_t)gridDim.x * PR_THREADS) {
-    uint32_t m = mag[k];
-    if ((m & mask) == prefix) atomicAdd(&h[(m >> shift) & 255u], 1);
+  bool nan = false;
+  const int64_t base = (int64_t)blockIdx.x * PR_BLOCK;
+  uint32_t a[PR_PER_THREAD];
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    const int64_t k = base + j * PR_THREADS + t;
+    a[j] = k < nnz ? magnitude<T>(raw_bits(vals[k])) : 0u;
   }
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    const bool ok = base + j * PR_THREADS + t < nnz;
+    nan |= ok && is_nan_mag<T>(a[j]);
+    wave_hist_add(h, (a[j] >> shift) & 255u, ok && (a[j] & mask) == prefix);
+  }
+  if (pass == 0 && nan) atomicOr(&st->err, 1);
   __syncthreads();
-  if (h[threadIdx.x]) atomicAdd(&st->hist[threadIdx.x], h[threadIdx.x]);
+  if (h[t]) atomicAdd(&st->hist[pass][blockIdx.x % PR_REPL][t], h[t]);
 }
 
-__global__ void k_sel_pick(pr_state* st, int shift) {
-  if (threadIdx.x != 0) return;
-  int32_t need = st->need, cum = 0;
-  int d = 0;
-  for (; d < 255; ++d) {
-    if (cum + st->hist[d] >= need) break;
-    cum += st->hist[d];
-  }
-  st->need = need - cum;
-  st->prefix |= (uint32_t)d << shift;
-  st->mask |= 255u << shift;
-  for (int i = 0; i < 256; ++i) st->hist[i] = 0;
-}
-
-__global__ __launch_bounds__(PR_THREADS) void k_pr_eq(const uint32_t* __restrict__ mag,
-                                                      int64_t nnz, const pr_state* st,
-                                                      int32_t* __restrict__ eq) {
-  int64_t k = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
-  if (k < nnz) eq[k] = mag[k] == st->prefix ? 1 : 0;
-}
-
-// keep[k] = 1 for survivors; drop[k] = 1 for dropped entries.
-__global__ __launch_bounds__(PR_THREADS) void k_pr_flags(const uint32_t* __restrict__ mag,
-                                                         int64_t nnz, const pr_state* st,
-                                                         const int32_t* __restrict__ eq_rank,
-                                                         int32_t* __restrict__ keep,
-                                                         int32_t* __restrict__ drop) {
-  int64_t k = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
-  if (k >= nnz) return;
-  uint32_t m = mag[k], tau = st->prefix;
-  bool d = m < tau || (m == tau && eq_rank[k] < st->need);
-  keep[k] = d ? 0 : 1;
-  drop[k] = d ? 1 : 0;
-}
-
-__global__ __launch_bounds__(PR_THREADS) void k_pr_compact(
-    const int64_t* __restrict__ lin, const uint32_t* __restrict__ vbits, int64_t nnz,
-    const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_pos,
-    const int32_t* __restrict__ drop_pos, int64_t* __restrict__ surv_lin,
-    uint32_t* __restrict__ surv_val, int64_t* __restrict__ dropped_lin) {
-  int64_t k = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
-  if (k >= nnz) return;
-  if (keep[k]) {
-    surv_lin[keep_pos[k]] = lin[k];
-    surv_val[keep_pos[k]] = vbits[k];
-  } else if (dropped_lin) {
-    dropped_lin[drop_pos[k]] = lin[k];
+// One workgroup: total histogram of the pass, then the digit holding the
+// need-th smallest remaining magnitude.
+__global__ __launch_bounds__(256) void k_sel_pick(pr_state* st, int shift, int pass) {
+  __shared__ int32_t h[256];
+  const int t = threadIdx.x;
+  int32_t sum = 0;
+  for (int r = 0; r < PR_REPL; ++r) sum += st->hist[pass][r][t];
+  h[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    const int32_t need = st->need;
+    int32_t cum = 0;
+    int d = 0;
+    for (; d < 255; ++d) {
+      if (cum + h[d] >= need) break;
+      cum += h[d];
+    }
+    st->need = need - cum;
+    st->prefix |= (uint32_t)d << shift;
+    st->mask |= 255u << shift;
   }
 }
 
-__global__ __launch_bounds__(PR_THREADS) void k_cand_gen(uint64_t* __restrict__ key,
-                                                         int32_t* __restrict__ val, int64_t C,
-                                                         uint64_t s, uint64_t base,
-                                                         uint64_t MK) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+// Per block: entries strictly below the threshold magnitude, and at it.
+template <typename T>
+__global__ __launch_bounds__(PR_THREADS) void k_pr_count(const T* __restrict__ vals, int64_t nnz,
+                                                         const pr_state* st,
+                                                         int32_t* __restrict__ cnt_lt,
+                                                         int32_t* __restrict__ cnt_eq) {
+  __shared__ int32_t lds[PR_THREADS / SNK_WAVE];
+  const uint32_t tau = st->prefix;
+  const int64_t base = (int64_t)blockIdx.x * PR_BLOCK + (int64_t)threadIdx.x * PR_PER_THREAD;
+  int32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    if (base + j < nnz) {
+      const uint32_t a = magnitude<T>(raw_bits(vals[base + j]));
+      lt += a < tau;
+      eq += a == tau;
+    }
+  }
+  int32_t tl, te;
+  block_excl_scan_i32<PR_THREADS>(lt, lds, &tl);
+  block_excl_scan_i32<PR_THREADS>(eq, lds, &te);
+  if (threadIdx.x == 0) {
+    cnt_lt[blockIdx.x] = tl;
+    cnt_eq[blockIdx.x] = te;
+  }
+}
+
+// One workgroup: E_b = entries at the threshold in blocks before b; block b
+// drops its `lt` entries plus its tied entries of global tie rank < need;
+// D_b = drops in blocks before b.
+constexpr int PR_DECIDE_THREADS = 1024;
+__global__ __launch_bounds__(PR_DECIDE_THREADS) void k_pr_decide(
+    const int32_t* __restrict__ cnt_lt, const int32_t* __restrict__ cnt_eq, int64_t nblk,
+    const pr_state* st, int32_t* __restrict__ base_eq, int32_t* __restrict__ base_drop) {
+  __shared__ int32_t lds[PR_DECIDE_THREADS / SNK_WAVE];
+  const int32_t need = st->need;
+  int32_t run_eq = 0, run_drop = 0;
+  for (int64_t c = 0; c < nblk; c += PR_DECIDE_THREADS) {
+    const int64_t b = c + threadIdx.x;
+    const int32_t e = b < nblk ? cnt_eq[b] : 0;
+    int32_t te;
+    const int32_t E = run_eq + block_excl_scan_i32<PR_DECIDE_THREADS>(e, lds, &te);
+    const int32_t d = b < nblk ? cnt_lt[b] + min(max(need - E, 0), e) : 0;
+    int32_t td;
+    const int32_t D = run_drop + block_excl_scan_i32<PR_DECIDE_THREADS>(d, lds, &td);
+    if (b < nblk) {
+      base_eq[b] = E;
+      base_drop[b] = D;
+    }
+    run_eq += te;
+    run_drop += td;
+  }
+}
+
+// Survivors (in order) with their raw value bits, the dropped list, and the
+// sorted pre-step support as linear indices.
+template <typename T>
+__global__ __launch_bounds__(PR_THREADS) void k_pr_apply(
+    const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
+    int64_t nnz, int32_t K, const pr_state* st, const int32_t* __restrict__ base_eq,
+    const int32_t* __restrict__ base_drop, int64_t* __restrict__ sup_lin,
+    int64_t* __restrict__ surv_lin, uint32_t* __restrict__ surv_val,
+    int64_t* __restrict__ dropped_lin) {
+  __shared__ int32_t lds[PR_THREADS / SNK_WAVE];
+  const uint32_t tau = st->prefix;
+  const int32_t need = st->need;
+  const int64_t base = (int64_t)blockIdx.x * PR_BLOCK + (int64_t)threadIdx.x * PR_PER_THREAD;
+  uint32_t bits[PR_PER_THREAD], mag[PR_PER_THREAD];
+  int32_t eq = 0;
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    bits[j] = base + j < nnz ? raw_bits(vals[base + j]) : 0u;
+    mag[j] = magnitude<T>(bits[j]);
+    eq += (base + j < nnz && mag[j] == tau);
+  }
+  int32_t tmp;
+  int32_t er = base_eq[blockIdx.x] + block_excl_scan_i32<PR_THREADS>(eq, lds, &tmp);
+  bool drop[PR_PER_THREAD];
+  int32_t nd = 0;
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    const bool ok = base + j < nnz;
+    const bool is_eq = ok && mag[j] == tau;
+    drop[j] = ok && (mag[j] < tau || (is_eq && er < need));
+    er += is_eq;
+    nd += drop[j];
+  }
+  int32_t dr = base_drop[blockIdx.x] + block_excl_scan_i32<PR_THREADS>(nd, lds, &tmp);
+#pragma unroll
+  for (int j = 0; j < PR_PER_THREAD; ++j) {
+    const int64_t k = base + j;
+    if (k >= nnz) break;
+    const int64_t lin = (int64_t)row[k] * K + col[k];
+    sup_lin[k] = lin;
+    if (drop[j]) {
+      if (dropped_lin) dropped_lin[dr] = lin;
+      ++dr;
+    } else {
+      const int64_t pos = k - dr;
+      surv_lin[pos] = lin;
+      surv_val[pos] = bits[j];
+    }
+  }
+}
+
+// Candidate positions for stream indices base .. base+C-1; thread 0 first
+// commits the previous chunk's acceptances.
+__global__ __launch_bounds__(PR_THREADS) void k_cand_gen(uint64_t* __restrict__ key, int64_t C,
+                                                         uint64_t s, uint64_t base, uint64_t MK,
+                                                         pr_state* st) {
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+  if (t == 0) {
+    st->got += st->n_new;
+    st->n_new = 0;
+  }
   if (t >= C) return;
-  uint64_t i = base + (uint64_t)t;
-  uint64_t x = sm64_mix(s + (i + 1) * SM64_GAMMA);
-  key[t] = __umul64hi(x, MK);
-  val[t] = (int32_t)t;
-}
-
-__device__ __forceinline__ bool in_sorted(const int64_t* __restrict__ a, int64_t n, int64_t x) {
-  int64_t lo = 0, hi = n;
-  while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo < n && a[lo] == x;
+  const uint64_t i = base + (uint64_t)t;
+  key[t] = __umul64hi(sm64_mix(s + (i + 1) * SM64_GAMMA), MK);
 }
 
 __device__ __forceinline__ int64_t lower_bound_i64(const int64_t* __restrict__ a, int64_t n,
                                                    int64_t x) {
   int64_t lo = 0, hi = n;
   while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
+    const int64_t mid = (lo + hi) >> 1;
     if (a[mid] < x) lo = mid + 1; else hi = mid;
   }
   return lo;
 }
 
-// ok_stream[stream index] = candidate acceptable (first occurrence of its
-// position, outside the old support and the positions already grown).
+__device__ __forceinline__ bool in_sorted(const int64_t* __restrict__ a, int64_t n, int64_t x) {
+  const int64_t i = lower_bound_i64(a, n, x);
+  return i < n && a[i] == x;
+}
+
+// ok_stream[stream index] = candidate acceptable.
 __global__ __launch_bounds__(PR_THREADS) void k_cand_ok(
     const uint64_t* __restrict__ key, const int32_t* __restrict__ val, int64_t C,
     const int64_t* __restrict__ sup, int64_t nnz, const int64_t* __restrict__ acc,
     const pr_state* st, int32_t* __restrict__ ok_stream) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
   if (t >= C) return;
-  int64_t p = (int64_t)key[t];
-  bool first = t == 0 || key[t - 1] != key[t];
-  bool ok = first && !in_sorted(sup, nnz, p) && !in_sorted(acc, st->got, p);
+  const int64_t p = (int64_t)key[t];
+  const bool first = t == 0 || key[t - 1] != key[t];
+  const bool ok = first && !in_sorted(sup, nnz, p) && !in_sorted(acc, st->got, p);
   ok_stream[val[t]] = ok ? 1 : 0;
 }
 
+// sel[t] (sorted order) = acceptable and among the first `need` in stream order.
 __global__ __launch_bounds__(PR_THREADS) void k_cand_sel(const int32_t* __restrict__ val,
                                                          int64_t C,
                                                          const int32_t* __restrict__ ok_stream,
                                                          const int32_t* __restrict__ ok_rank,
                                                          const pr_state* st, int32_t n_drop,
                                                          int32_t* __restrict__ sel) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
   if (t >= C) return;
-  int32_t v = val[t];
+  const int32_t v = val[t];
   sel[t] = (ok_stream[v] && ok_rank[v] < n_drop - st->got) ? 1 : 0;
 }
 
+// Selected positions in position order; thread 0 records how many.
 __global__ __launch_bounds__(PR_THREADS) void k_cand_collect(const uint64_t* __restrict__ key,
                                                              int64_t C,
                                                              const int32_t* __restrict__ sel,
                                                              const int32_t* __restrict__ pos,
-                                                             int64_t* __restrict__ out) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+                                                             int64_t* __restrict__ out,
+                                                             pr_state* st, int32_t n_drop) {
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+  if (t == 0) st->n_new = min(st->total_ok, n_drop - st->got);
   if (t < C && sel[t]) out[pos[t]] = (int64_t)key[t];
 }
 
@@ -224,36 +331,26 @@ __global__ __launch_bounds__(PR_THREADS) void k_merge_acc(const int64_t* __restr
                                                           const int64_t* __restrict__ nw,
                                                           const pr_state* st,
                                                           int64_t* __restrict__ out) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
   const int64_t got = st->got, n_new = st->n_new;
   if (t < got) {
     out[t + lower_bound_i64(nw, n_new, acc[t])] = acc[t];
   } else if (t < got + n_new) {
-    int64_t j = t - got;
+    const int64_t j = t - got;
     out[j + lower_bound_i64(acc, got, nw[j])] = nw[j];
   }
 }
 
-__global__ void k_chunk_done(pr_state* st, int32_t n_drop) {
-  if (threadIdx.x == 0) {
-    int32_t take = min(st->total_ok, n_drop - st->got);
-    st->n_new = take;
-  }
-}
-
-__global__ void k_chunk_commit(pr_state* st) {
-  if (threadIdx.x == 0) {
-    st->got += st->n_new;
-    st->n_new = 0;
-  }
-}
-
+// New COO = survivors + grown positions (value 0), by rank; only once the
+// step is complete and clean.
 template <typename T>
 __global__ __launch_bounds__(PR_THREADS) void k_final_merge(
     const int64_t* __restrict__ surv_lin, const uint32_t* __restrict__ surv_val, int64_t n_surv,
-    const int64_t* __restrict__ grown, int64_t n_grown, int32_t K, int32_t* __restrict__ row,
-    int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ grown_out) {
-  int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+    const int64_t* __restrict__ grown, int64_t n_grown, int32_t K, const pr_state* st,
+    int32_t* __restrict__ row, int32_t* __restrict__ col, T* __restrict__ vals,
+    int64_t* __restrict__ grown_out) {
+  if (st->err || (int64_t)st->got + st->n_new < n_grown) return;
+  const int64_t t = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
   int64_t lin, pos;
   uint32_t vb;
   if (t < n_surv) {
@@ -261,7 +358,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_final_merge(
     pos = t + lower_bound_i64(grown, n_grown, lin);
     vb = surv_val[t];
   } else if (t < n_surv + n_grown) {
-    int64_t j = t - n_surv;
+    const int64_t j = t - n_surv;
     lin = grown[j];
     pos = j + lower_bound_i64(surv_lin, n_surv, lin);
     vb = 0;
@@ -280,17 +377,16 @@ __global__ __launch_bounds__(PR_THREADS) void k_final_merge(
 
 // ------------------------------------------------------------------ layout
 struct pr_layout {
-  int64_t C;
-  size_t state, mag, lin, vbits, f_a, f_b, s_a, s_b, surv_lin, surv_val;
-  size_t ckey0, ckey1, cval0, cval1, okr, acc0, acc1, nw, tmp, total;
+  int64_t C, nblk;
+  size_t state, cnt_lt, cnt_eq, base_eq, base_drop, sup, surv_lin, surv_val;
+  size_t ck0, ck1, cv0, cv1, ok, okr, sel, selpos, acc0, acc1, nw, tmp, total;
 };
 
 static int64_t chunk_size(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) {
-  double MK = (double)M * (double)K;
-  double q = (MK - (double)nnz) / MK;
+  const double MK = (double)M * (double)K;
+  const double q = (MK - (double)nnz) / MK;
   double want = q > 0 ? (double)n_drop / q * 1.15 + 2048.0 : 2048.0;
-  double cap = std::max(2048.0, 4.0 * MK + 2048.0);
-  want = std::min(want, cap);
+  want = std::min(want, std::max(2048.0, 4.0 * MK + 2048.0));
   want = std::min(want, (double)(1ll << 28));
   return (int64_t)want;
 }
@@ -298,34 +394,35 @@ static int64_t chunk_size(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) {
 static pr_layout make_layout(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) {
   pr_layout L{};
   L.C = chunk_size(M, K, nnz, n_drop);
+  L.nblk = std::max<int64_t>(1, cdiv(nnz, PR_BLOCK));
   const int64_t n1 = std::max<int64_t>(nnz, 1);
-  const int64_t nf = std::max<int64_t>(n1, L.C);
   const int64_t nd = std::max<int64_t>(n_drop, 1);
   size_t o = 0;
   auto take = [&](size_t bytes) {
-    size_t at = o;
+    const size_t at = o;
     o = align_up(o + bytes, 256);
     return at;
   };
   L.state = take(sizeof(pr_state));
-  L.mag = take(4 * (size_t)n1);
-  L.lin = take(8 * (size_t)n1);
-  L.vbits = take(4 * (size_t)n1);
-  L.f_a = take(4 * (size_t)nf);
-  L.f_b = take(4 * (size_t)n1);
-  L.s_a = take(4 * (size_t)nf);
-  L.s_b = take(4 * (size_t)n1);
+  L.cnt_lt = take(4 * (size_t)L.nblk);
+  L.cnt_eq = take(4 * (size_t)L.nblk);
+  L.base_eq = take(4 * (size_t)L.nblk);
+  L.base_drop = take(4 * (size_t)L.nblk);
+  L.sup = take(8 * (size_t)n1);
   L.surv_lin = take(8 * (size_t)n1);
   L.surv_val = take(4 * (size_t)n1);
-  L.ckey0 = take(8 * (size_t)L.C);
-  L.ckey1 = take(8 * (size_t)L.C);
-  L.cval0 = take(4 * (size_t)L.C);
-  L.cval1 = take(4 * (size_t)L.C);
+  L.ck0 = take(8 * (size_t)L.C);
+  L.ck1 = take(8 * (size_t)L.C);
+  L.cv0 = take(4 * (size_t)L.C);
+  L.cv1 = take(4 * (size_t)L.C);
+  L.ok = take(4 * (size_t)L.C);
   L.okr = take(4 * (size_t)L.C);
+  L.sel = take(4 * (size_t)L.C);
+  L.selpos = take(4 * (size_t)L.C);
   L.acc0 = take(8 * (size_t)nd);
   L.acc1 = take(8 * (size_t)nd);
   L.nw = take(8 * (size_t)nd);
-  L.tmp = take(std::max(radix_tmp_bytes(L.C), scan_tmp_bytes(nf)));
+  L.tmp = take(std::max(radix_tmp_bytes(L.C), scan_tmp_bytes(L.C)));
   L.total = o;
   return L;
 }
@@ -340,90 +437,84 @@ static snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t 
                         int64_t* grown_lin, char* ws, hipStream_t s) {
   const pr_layout L = make_layout(M, K, nnz, n_drop);
   pr_state* st = (pr_state*)(ws + L.state);
-  uint32_t* mag = (uint32_t*)(ws + L.mag);
-  int64_t* lin = (int64_t*)(ws + L.lin);
-  uint32_t* vbits = (uint32_t*)(ws + L.vbits);
-  int32_t* f_a = (int32_t*)(ws + L.f_a);
-  int32_t* f_b = (int32_t*)(ws + L.f_b);
-  int32_t* s_a = (int32_t*)(ws + L.s_a);
-  int32_t* s_b = (int32_t*)(ws + L.s_b);
+  int32_t* cnt_lt = (int32_t*)(ws + L.cnt_lt);
+  int32_t* cnt_eq = (int32_t*)(ws + L.cnt_eq);
+  int32_t* base_eq = (int32_t*)(ws + L.base_eq);
+  int32_t* base_drop = (int32_t*)(ws + L.base_drop);
+  int64_t* sup = (int64_t*)(ws + L.sup);
   int64_t* surv_lin = (int64_t*)(ws + L.surv_lin);
   uint32_t* surv_val = (uint32_t*)(ws + L.surv_val);
-  uint64_t* ck0 = (uint64_t*)(ws + L.ckey0);
-  uint64_t* ck1 = (uint64_t*)(ws + L.ckey1);
-  int32_t* cv0 = (int32_t*)(ws + L.cval0);
-  int32_t* cv1 = (int32_t*)(ws + L.cval1);
+  // sorted candidates end in kbuf[0]/vbuf[0]; the generator writes the key
+  // buffer the sort's first pass does not write (pass p writes
+  // kbuf[(passes-1-p) & 1])
+  uint64_t* const kbuf[2] = {(uint64_t*)(ws + L.ck0), (uint64_t*)(ws + L.ck1)};
+  int32_t* const vbuf[2] = {(int32_t*)(ws + L.cv0), (int32_t*)(ws + L.cv1)};
+  int32_t* ok = (int32_t*)(ws + L.ok);
   int32_t* okr = (int32_t*)(ws + L.okr);
+  int32_t* sel = (int32_t*)(ws + L.sel);
+  int32_t* selpos = (int32_t*)(ws + L.selpos);
   int64_t* acc[2] = {(int64_t*)(ws + L.acc0), (int64_t*)(ws + L.acc1)};
   int64_t* nw = (int64_t*)(ws + L.nw);
   void* tmp = ws + L.tmp;
-  hipError_t e;
+  const int64_t C = L.C;
 
-  hipLaunchKernelGGL(k_pr_state_init, dim3(1), dim3(256), 0, s, st, (int32_t)n_drop);
-  hipLaunchKernelGGL(k_pr_keys<T>, g1(nnz), dim3(PR_THREADS), 0, s, row, col, vals, nnz, K, mag,
-                     lin, vbits, st);
-  // radix select of the n_drop-th smallest magnitude (MSB digit first)
-  const unsigned sel_blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(nnz, 4096)));
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(k_sel_hist, dim3(sel_blocks), dim3(PR_THREADS), 0, s, mag, nnz, shift, st);
-    hipLaunchKernelGGL(k_sel_pick, dim3(1), dim3(64), 0, s, st, shift);
+  hipLaunchKernelGGL(k_pr_init, dim3(PR_REPL), dim3(256), 0, s, st, (int32_t)n_drop);
+  const unsigned sel_blocks = (unsigned)L.nblk;
+  int pass = 0;
+  for (int shift = sizeof(T) == 2 ? 8 : 24; shift >= 0; shift -= 8, ++pass) {
+    hipLaunchKernelGGL(k_sel_hist<T>, dim3(sel_blocks), dim3(PR_THREADS), 0, s, vals, nnz, shift,
+                       pass, st);
+    hipLaunchKernelGGL(k_sel_pick, dim3(1), dim3(256), 0, s, st, shift, pass);
   }
-  hipLaunchKernelGGL(k_pr_eq, g1(nnz), dim3(PR_THREADS), 0, s, mag, nnz, st, f_a);
-  if ((e = exclusive_scan_i32(f_a, s_a, nnz, nullptr, tmp, s)) != hipSuccess) return SNACK_E_HIP;
-  hipLaunchKernelGGL(k_pr_flags, g1(nnz), dim3(PR_THREADS), 0, s, mag, nnz, st, s_a, f_b, f_a);
-  if ((e = exclusive_scan_i32(f_b, s_b, nnz, nullptr, tmp, s)) != hipSuccess) return SNACK_E_HIP;
-  if ((e = exclusive_scan_i32(f_a, s_a, nnz, nullptr, tmp, s)) != hipSuccess) return SNACK_E_HIP;
-  hipLaunchKernelGGL(k_pr_compact, g1(nnz), dim3(PR_THREADS), 0, s, lin, vbits, nnz, f_b, s_b,
-                     s_a, surv_lin, surv_val, dropped_lin);
+  hipLaunchKernelGGL(k_pr_count<T>, dim3((unsigned)L.nblk), dim3(PR_THREADS), 0, s, vals, nnz,
+                     st, cnt_lt, cnt_eq);
+  hipLaunchKernelGGL(k_pr_decide, dim3(1), dim3(PR_DECIDE_THREADS), 0, s, cnt_lt, cnt_eq, L.nblk,
+                     st, base_eq, base_drop);
+  hipLaunchKernelGGL(k_pr_apply<T>, dim3((unsigned)L.nblk), dim3(PR_THREADS), 0, s, row, col,
+                     vals, nnz, K, st, base_eq, base_drop, sup, surv_lin, surv_val, dropped_lin);
   if (hipGetLastError() != hipSuccess) return SNACK_E_HIP;
 
-  // regrowth
   const uint64_t MK = (uint64_t)M * (uint64_t)K;
   int bits = 0;
   while (bits < 64 && ((MK - 1) >> bits) != 0) ++bits;
-  const uint64_t stream = sm64_mix_host(seed + (step + 1) * SM64_GAMMA);
-  const int64_t C = L.C;
+  const int passes = std::max(1, (bits + 7) / 8);
+  uint64_t* cand = kbuf[passes & 1];
+  const uint64_t stream = sm64_mix(seed + (step + 1) * SM64_GAMMA);
+  const int64_t n_surv = nnz - n_drop;
   int cur = 0;
   uint64_t base = 0;
-  int32_t host_state[2] = {0, 0};  // err, got
-  for (;;) {
-    hipLaunchKernelGGL(k_cand_gen, g1(C), dim3(PR_THREADS), 0, s, ck0, cv0, C, stream, base, MK);
-    uint64_t* sk;
-    int32_t* sv;
-    if ((e = radix_sort_u64(ck0, cv0, ck1, cv1, C, bits, &sk, &sv, tmp, s)) != hipSuccess)
+  for (int chunk = 0;; ++chunk) {
+    hipLaunchKernelGGL(k_cand_gen, g1(C), dim3(PR_THREADS), 0, s, cand, C, stream, base, MK, st);
+    if (radix_sort_u64(cand, nullptr, kbuf, vbuf, C, bits, tmp, s) != hipSuccess)
       return SNACK_E_HIP;
-    hipLaunchKernelGGL(k_cand_ok, g1(C), dim3(PR_THREADS), 0, s, sk, sv, C, lin, nnz, acc[cur],
-                       st, f_a);
-    if ((e = exclusive_scan_i32(f_a, okr, C, &st->total_ok, tmp, s)) != hipSuccess)
-      return SNACK_E_HIP;
-    hipLaunchKernelGGL(k_cand_sel, g1(C), dim3(PR_THREADS), 0, s, sv, C, f_a, okr, st,
-                       (int32_t)n_drop, s_a);
-    // candidates in position order -> compaction positions
-    int32_t* selpos = (sv == cv0) ? cv1 : cv0;  // free int buffer of size C
-    if ((e = exclusive_scan_i32(s_a, selpos, C, nullptr, tmp, s)) != hipSuccess)
-      return SNACK_E_HIP;
-    hipLaunchKernelGGL(k_cand_collect, g1(C), dim3(PR_THREADS), 0, s, sk, C, s_a, selpos, nw);
-    hipLaunchKernelGGL(k_chunk_done, dim3(1), dim3(64), 0, s, st, (int32_t)n_drop);
-    hipLaunchKernelGGL(k_merge_acc, g1(n_drop), dim3(PR_THREADS), 0, s, acc[cur], nw, st,
-                       acc[cur ^ 1]);
-    hipLaunchKernelGGL(k_chunk_commit, dim3(1), dim3(64), 0, s, st);
-    cur ^= 1;
+    hipLaunchKernelGGL(k_cand_ok, g1(C), dim3(PR_THREADS), 0, s, kbuf[0], vbuf[0], C, sup, nnz,
+                       acc[cur], st, ok);
+    if (exclusive_scan_i32(ok, okr, C, &st->total_ok, tmp, s) != hipSuccess) return SNACK_E_HIP;
+    hipLaunchKernelGGL(k_cand_sel, g1(C), dim3(PR_THREADS), 0, s, vbuf[0], C, ok, okr, st,
+                       (int32_t)n_drop, sel);
+    if (exclusive_scan_i32(sel, selpos, C, nullptr, tmp, s) != hipSuccess) return SNACK_E_HIP;
+    // the first chunk has nothing to merge with: collect straight into the list
+    int64_t* dst = chunk == 0 ? acc[cur ^ 1] : nw;
+    hipLaunchKernelGGL(k_cand_collect, g1(C), dim3(PR_THREADS), 0, s, kbuf[0], C, sel, selpos,
+                       dst, st, (int32_t)n_drop);
+    if (chunk > 0)
+      hipLaunchKernelGGL(k_merge_acc, g1(n_drop), dim3(PR_THREADS), 0, s, acc[cur], nw, st,
+                         acc[cur ^ 1]);
+    hipLaunchKernelGGL(k_final_merge<T>, g1(nnz), dim3(PR_THREADS), 0, s, surv_lin, surv_val,
+                       n_surv, acc[cur ^ 1], n_drop, K, st, row, col, vals, grown_lin);
     if (hipGetLastError() != hipSuccess) return SNACK_E_HIP;
-    if (hipMemcpyAsync(host_state, &st->err, sizeof(int32_t) * 2, hipMemcpyDeviceToHost, s) !=
-            hipSuccess ||
+    int32_t hs[3] = {0, 0, 0};  // err, got, n_new
+    if (hipMemcpyAsync(hs, &st->err, sizeof(hs), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       return SNACK_E_HIP;
-    if (host_state[0]) return SNACK_E_NAN;
-    if (host_state[1] >= n_drop) break;
+    if (hs[0]) return SNACK_E_NAN;
+    if ((int64_t)hs[1] + hs[2] >= n_drop) break;
+    cur ^= 1;
     base += (uint64_t)C;
     // n_drop <= free positions is checked by the caller, so the stream
     // reaches n_drop acceptances with probability 1; bound it regardless.
     if (base > (1ull << 40)) return SNACK_E_COUNT;
   }
-  const int64_t n_surv = nnz - n_drop;
-  hipLaunchKernelGGL(k_final_merge<T>, g1(nnz), dim3(PR_THREADS), 0, s, surv_lin, surv_val,
-                     n_surv, acc[cur], n_drop, K, row, col, vals, grown_lin);
-  if (hipGetLastError() != hipSuccess) return SNACK_E_HIP;
   return SNACK_OK;
 }
 

@@ -332,19 +332,27 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   }
 }
 
-// Segments cut by tile boundaries: out = sum of the carry-out slots of tiles
-// first..last-1 (in tile order) + the final piece held by tile `last`.
+// Segments cut by tile boundaries.  Tile p finishes such a segment when the
+// cut starting it is inner (cut[p]) and the next cut is not an inner cut of
+// the same segment.  The pieces start at tile f: walk back over inner cuts of
+// the same segment.  out = sum of the carry-out slots of tiles f..p-1 (in
+// tile order) + the final piece held by tile p.
 template <typename T, bool NODE_OUT>
-__global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ split, int32_t n_split,
+__global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ part_seg,
+                                               const int32_t* __restrict__ cut,
                                                const float* __restrict__ carry, T* __restrict__ Y,
                                                int32_t S, int32_t B, int32_t P) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)n_split * B) return;
-  int32_t j = (int32_t)(i / B), b = (int32_t)(i % B);
-  int32_t s = split[3 * j], f = split[3 * j + 1], l = split[3 * j + 2];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)P * B) return;
+  const int32_t p = (int32_t)(i / B), b = (int32_t)(i % B);
+  if (!cut[p]) return;
+  const int32_t s = part_seg[p];
+  if (p + 1 < P && cut[p + 1] && part_seg[p + 1] == s) return;
+  int32_t f = p - 1;
+  while (f >= 1 && cut[f] && part_seg[f] == s) --f;
   float tot = 0.f;
-  for (int32_t q = f; q < l; ++q) tot += carry[(int64_t)q * B + b];
-  tot += carry[((int64_t)P + l) * B + b];
+  for (int32_t q = f; q < p; ++q) tot += carry[(int64_t)q * B + b];
+  tot += carry[((int64_t)P + p) * B + b];
   if (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
   else Y[(int64_t)b * S + s] = elem<T>::from_f(tot);
 }
@@ -597,10 +605,10 @@ static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_
   hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, PERM>), grid, dim3(sh.threads), lds, s, v.ptr,
                      v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)Xt, (T*)Y,
                      carry, v.S, B, v.P, sh.g_log2, v.tile);
-  if (v.n_split > 0) {
-    int64_t n = (int64_t)v.n_split * B;
+  if (v.has_split) {
+    int64_t n = (int64_t)v.P * B;
     hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
-                       v.split, v.n_split, carry, (T*)Y, v.S, B, v.P);
+                       v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
   }
 }
 
