@@ -281,6 +281,17 @@ def test_zero_batch_and_empty_weight(orc):
 
 
 # --------------------------------------------------------------- prune / regrow
+@pytest.fixture(params=["auto", "sort"])
+def prune_plan(request, monkeypatch):
+    """Run a prune test with the library's own plan choice (the bitmap plan
+    for every layer density <= 1/4 here) and again forced onto the sort plan."""
+    if request.param == "sort":
+        monkeypatch.setenv("SNACK_PRUNE_PATH", "sort")
+    else:
+        monkeypatch.delenv("SNACK_PRUNE_PATH", raising=False)
+    return request.param
+
+
 def gpu_prune(w, dt, n_drop, seed, step, vals=None):
     row, col = to_dev(w.row), to_dev(w.col)
     v = to_dev(w.vals if vals is None else vals, dt)
@@ -311,13 +322,13 @@ def check_prune(orc, w, dt, ppm, seed, step, vals=None):
     return row, col
 
 
-def test_prune_regrow_single_layer(orc):
+def test_prune_regrow_single_layer(orc, prune_plan):
     w = workload("single").weights[0]
     check_prune(orc, w, "f32", 100000, 0, 1)
 
 
 @pytest.mark.parametrize("sp", ["0.9", "0.99"])
-def test_prune_regrow_gpt2(orc, sp):
+def test_prune_regrow_gpt2(orc, sp, prune_plan):
     for W in workload(f"gpt2_{sp}").weights:
         row, col = check_prune(orc, W, "f32", 300000, 0, 5)
         # the restructured COO prepares exactly as the oracle says
@@ -325,7 +336,7 @@ def test_prune_regrow_gpt2(orc, sp):
         check_prepare(orc, w2, topology(w2, 1))
 
 
-def test_prune_regrow_bf16_ties_and_signed_zero(orc):
+def test_prune_regrow_bf16_ties_and_signed_zero(orc, prune_plan):
     w = synth.random_case(8, 300, 200, 5000, 1, "bf16").weights[0]
     vals = w.vals.copy()
     vals[::7] = vals[3]                    # many exact ties
@@ -334,12 +345,12 @@ def test_prune_regrow_bf16_ties_and_signed_zero(orc):
     check_prune(orc, w, "bf16", 250000, 42, 9, vals)
 
 
-def test_prune_regrow_square_bf16(orc):
+def test_prune_regrow_square_bf16(orc, prune_plan):
     w = workload("square_0.95_1").weights[0]
     check_prune(orc, w, "bf16", 300000, 3, 1)
 
 
-def test_prune_regrow_nearly_full_needs_several_chunks(orc):
+def test_prune_regrow_nearly_full_needs_several_chunks(orc, prune_plan):
     """Only a few free positions: the candidate stream runs over many chunks."""
     M, K = 40, 60
     nnz = M * K - 30
@@ -347,7 +358,7 @@ def test_prune_regrow_nearly_full_needs_several_chunks(orc):
     check_prune(orc, w, "f32", 10000, 5, 2)
 
 
-def test_prune_regrow_rejects_nan_and_keeps_coo():
+def test_prune_regrow_rejects_nan_and_keeps_coo(prune_plan):
     w = synth.random_case(4, 64, 64, 400, 1).weights[0]
     vals = w.vals.copy()
     vals[17] = np.nan
@@ -359,6 +370,48 @@ def test_prune_regrow_rejects_nan_and_keeps_coo():
         snk.snack_prune_regrow(row, col, v, 64, 64, 400, 40, 1, 1, None, None, ws)
     assert e.value.status == -7
     assert np.array_equal(row.cpu().numpy(), w.row) and np.array_equal(col.cpu().numpy(), w.col)
+
+
+def test_prune_regrow_huge_sparse_grid_takes_sort_plan(orc):
+    """A 100,000 x 100,000 grid with 2,000 entries: a support bitmap would be
+    far larger than the COO, so the sort plan runs by itself."""
+    w = synth.random_case(11, 100000, 100000, 2000, 1, "bf16").weights[0]
+    check_prune(orc, w, "bf16", 300000, 7, 3)
+
+
+def test_prune_regrow_without_lists_and_second_step(orc, prune_plan):
+    """Nullable dropped/grown outputs, then a second step on the result."""
+    w = workload("single").weights[0]
+    n_drop = orc.drop_count(w.nnz, 100000)
+    row, col, v = to_dev(w.row), to_dev(w.col), to_dev(w.vals)
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+                     dtype=torch.uint8, device="cuda")
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 1, None, None, ws)
+    ref = orc.prune_regrow(w.M, w.K, w.row, w.col, w.vals, "f32", n_drop, 0, 1)
+    assert np.array_equal(row.cpu().numpy(), ref["row"])
+    assert np.array_equal(col.cpu().numpy(), ref["col"])
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 2, None, None, ws)
+    ref2 = orc.prune_regrow(w.M, w.K, ref["row"], ref["col"],
+                            np.asarray(ref["vals"], np.float32), "f32", n_drop, 0, 2)
+    assert np.array_equal(row.cpu().numpy(), ref2["row"])
+    assert np.array_equal(col.cpu().numpy(), ref2["col"])
+    assert np.array_equal(v.cpu().numpy().view(np.uint32),
+                          np.asarray(ref2["vals"], np.float32).view(np.uint32))
+
+
+def test_prune_regrow_rejects_invalid_coo_on_bitmap_plan():
+    """The bitmap plan validates the COO while building the support bitmap:
+    a repeated entry is reported and the COO is left as it was."""
+    w = synth.random_case(4, 64, 64, 400, 1).weights[0]
+    r, c = w.row.copy(), w.col.copy()
+    r[10], c[10] = r[9], c[9]
+    row, col, v = to_dev(r), to_dev(c), to_dev(w.vals)
+    ws = torch.empty(snk.snack_prune_regrow_workspace(64, 64, 400, 40), dtype=torch.uint8,
+                     device="cuda")
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_prune_regrow(row, col, v, 64, 64, 400, 40, 1, 1, None, None, ws)
+    assert e.value.status == -6
+    assert np.array_equal(row.cpu().numpy(), r) and np.array_equal(col.cpu().numpy(), c)
 
 
 # --------------------------------------------------------------- aux

@@ -38,8 +38,9 @@
 namespace snk {
 
 constexpr int MP_MAX_THREADS = 256;
-constexpr int MP_RC = 8;        // entries fetched per step of a run
+constexpr int MP_RC = 8;        // entries a group gathers at once (one round of its run)
 constexpr int MP_MAX_BW = 32;   // batch columns per workgroup (CH * G)
+constexpr int MP_SU = 8;        // staged items per thread per staging round
 
 // Merge-path point of local diagonal d inside a tile: the number x of
 // segment ends consumed (end x' is consumed before entry j iff end[x'] <= j).
@@ -93,13 +94,14 @@ struct tile_lds {
   int32_t* gx;     // [NT+1] run start: segment ends consumed
   int32_t* gy;     // [NT+1] run start: entries consumed
   float* scan;     // [threads*CH] segmented scan of run partial sums
+  float* pend;     // [threads*CH] partial sum of a run's first, earlier-started segment
   float* wval;     // [4][MP_MAX_BW] per-wave scan totals
   int32_t* wflag;  // [4] per-wave "a segment starts here" flags
 };
 
 __host__ __device__ inline size_t tile_lds_bytes(int tile_items, int threads, int g_log2, int ch) {
   int NT = threads >> g_log2;
-  return 3 * 4 * (size_t)(2 * tile_items) + 8 * (size_t)(NT + 1) + 4 * (size_t)threads * ch +
+  return 3 * 4 * (size_t)(2 * tile_items) + 8 * (size_t)(NT + 1) + 8 * (size_t)threads * ch +
          4 * 4 * MP_MAX_BW + 16;
 }
 
@@ -112,9 +114,54 @@ __device__ __forceinline__ tile_lds carve(unsigned char* smem, int tile_items, i
   L.gx = (int32_t*)(L.val + 2 * tile_items);
   L.gy = L.gx + (NT + 1);
   L.scan = (float*)(L.gy + (NT + 1));
-  L.wval = L.scan + threads * ch;
+  L.pend = L.scan + threads * ch;
+  L.wval = L.pend + threads * ch;
   L.wflag = (int32_t*)(L.wval + 4 * MP_MAX_BW);
   return L;
+}
+
+// Stage a tile's segment ends, entry indices and (fp32) values in LDS.  Each
+// round issues all of a thread's MP_SU loads of every array before storing
+// any, so a round costs one memory round trip (two with the value
+// permutation of the column view).
+template <typename T, bool PERM, bool VALS>
+__device__ __forceinline__ void stage_tile(const tile_lds& L, const int32_t* __restrict__ ptr,
+                                           const int32_t* __restrict__ idx,
+                                           const int32_t* __restrict__ perm,
+                                           const T* __restrict__ vals, int32_t sb, int32_t zb,
+                                           int nseg, int nz) {
+  const int tid = threadIdx.x, threads = blockDim.x;
+  const int nst = max(nseg, nz);
+  for (int base = 0; base < nst; base += threads * MP_SU) {
+    int32_t te[MP_SU], ti[MP_SU];
+    T tv[MP_SU];
+#pragma unroll
+    for (int j = 0; j < MP_SU; ++j) {
+      const int i = base + j * threads + tid;
+      te[j] = i < nseg ? ptr[sb + 1 + i] : 0;
+      ti[j] = i < nz ? idx[(int64_t)zb + i] : 0;
+      if constexpr (VALS && !PERM) tv[j] = i < nz ? vals[(int64_t)zb + i] : (T)0;
+    }
+    if constexpr (VALS && PERM) {
+      int32_t tk[MP_SU];
+#pragma unroll
+      for (int j = 0; j < MP_SU; ++j) {
+        const int i = base + j * threads + tid;
+        tk[j] = i < nz ? perm[(int64_t)zb + i] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < MP_SU; ++j) tv[j] = tk[j] >= 0 ? vals[tk[j]] : (T)0;
+    }
+#pragma unroll
+    for (int j = 0; j < MP_SU; ++j) {
+      const int i = base + j * threads + tid;
+      if (i < nseg) L.end[i] = te[j];
+      if (i < nz) {
+        L.idx[i] = ti[j];
+        if constexpr (VALS) L.val[i] = elem<T>::to_f(tv[j]);
+      }
+    }
+  }
 }
 
 template <typename T, int CH, bool NODE_OUT, bool PERM>
@@ -145,13 +192,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   const int items = nseg + nz;
   const int32_t seg0_start = ptr[sb];
 
-  // stage the tile: segment ends, entry indices and values (coalesced)
-  for (int i = tid; i < nseg; i += threads) L.end[i] = ptr[sb + 1 + i];
-  for (int i = tid; i < nz; i += threads) {
-    const int64_t k = (int64_t)zb + i;
-    L.idx[i] = idx[k];
-    L.val[i] = elem<T>::to_f(PERM ? vals[perm[k]] : vals[k]);
-  }
+  stage_tile<T, PERM, true>(L, ptr, idx, perm, vals, sb, zb, nseg, nz);
   __syncthreads();
 
   const int R = (items + NT - 1) / NT;
@@ -172,16 +213,18 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   const bool mid_start = (zb + y0) > x0_start;
   const bool tile_carry_in = zb > seg0_start;
 
-  float acc[CH], pend[CH];
+  float acc[CH];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) acc[c] = pend[c] = 0.f;
+  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
   bool has_pend = false, first_emit = true;
   int x = x0;
 
+  // The first segment a run finishes began before the run when mid_start:
+  // its partial sum is parked in LDS and completed after the scan.
   auto emit = [&](int xx, const float (&v)[CH]) {
     if (first_emit && mid_start) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) pend[c] = v[c];
+      for (int c = 0; c < CH; ++c) L.pend[tid * CH + c] = v[c];
       has_pend = true;
     } else if (bvalid) {
       store_out<T, CH, NODE_OUT>(Y, sb + xx, b0, B, S, v);
@@ -189,10 +232,10 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     first_emit = false;
   };
 
-  // The run's entries are taken RC at a time.  Per chunk: finish the segments
-  // that end before its first entry, find which segments its entries belong
-  // to (a handful of LDS reads, no per-entry branch), then one masked FMA
-  // pass per segment touched.
+  // The run's entries are taken MP_RC at a time (normally a single round):
+  // indices and values from LDS, then all activation gathers, then one
+  // ordered sweep that finishes a segment when the next entry's segment
+  // offset moves past it.
   for (int y = y0; y < y1; y += MP_RC) {
     const int n = min(MP_RC, y1 - y);
     const int32_t pos0 = zb + y;
@@ -201,19 +244,12 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
 #pragma unroll
       for (int c = 0; c < CH; ++c) acc[c] = 0.f;
     }
-    int32_t ci[MP_RC];
-    float cv[MP_RC];
     vec<T, CH> xv[MP_RC];  // gathered activations kept packed until use
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
-      const bool ok = u < n;
-      ci[u] = ok ? L.idx[y + u] : 0;
-      cv[u] = ok ? L.val[y + u] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < MP_RC; ++u) {
+      const int32_t ci = u < n ? L.idx[y + u] : 0;
       if (u < n && bvalid) {
-        xv[u] = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)ci[u] * B + b0);
+        xv[u] = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)ci * B + b0);
       } else {
 #pragma unroll
         for (int c = 0; c < CH; ++c) xv[u].v[c] = (T)0;
@@ -231,8 +267,6 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
       for (int u = 0; u < MP_RC; ++u) sd[u] += (e <= pos0 + u) ? 1 : 0;
       ++xh;
     }
-    // one ordered sweep: entries in order, a segment is finished when the
-    // next entry's segment offset moves past it (sd is non-decreasing)
     int cur = 0;
 #pragma unroll
     for (int u = 0; u < MP_RC; ++u) {
@@ -243,8 +277,9 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
           for (int c = 0; c < CH; ++c) acc[c] = 0.f;
           ++cur;
         }
+        const float cv = L.val[y + u];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) acc[c] = fmaf(cv[u], elem<T>::to_f(xv[u].v[c]), acc[c]);
+        for (int c = 0; c < CH; ++c) acc[c] = fmaf(cv, elem<T>::to_f(xv[u].v[c]), acc[c]);
       }
     }
     x = xh;
@@ -259,9 +294,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   // A group "heads" a new carry segment if it finished any segment (its carry
   // then belongs to a segment no earlier group touched).
   int h = (x0 != x1 || grp == 0) ? 1 : 0;
-  float sc[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) sc[c] = acc[c];
+  float (&sc)[CH] = acc;
   const int GW = 64 >> g_log2;  // groups per wave
   const int gw = lane >> g_log2;
   for (int d = 1; d < GW; d <<= 1) {
@@ -310,7 +343,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     float tot[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      tot[c] = (grp > 0 ? L.scan[((grp - 1) * G + gl) * CH + c] : 0.f) + pend[c];
+      tot[c] = (grp > 0 ? L.scan[((grp - 1) * G + gl) * CH + c] : 0.f) + L.pend[tid * CH + c];
     if (bvalid) {
       if (x0 == 0 && tile_carry_in) {
         float* dst = carry + ((int64_t)P + p) * B + b0;
@@ -385,8 +418,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_sddmm(
   const int nz = ze - zb;
   const int items = nseg + nz;
 
-  for (int i = tid; i < nseg; i += threads) L.end[i] = ptr[sb + 1 + i];
-  for (int i = tid; i < nz; i += threads) L.idx[i] = idx[(int64_t)zb + i];
+  stage_tile<T, false, false>(L, ptr, idx, nullptr, (const T*)nullptr, sb, zb, nseg, nz);
   __syncthreads();
   const int R = (items + NT - 1) / NT;
   if (gl == 0) {
@@ -542,11 +574,12 @@ struct lane_shape {
   int threads;  // workgroup size
 };
 
-// Widest per-lane chunk of batch columns.  bf16 products use 4 columns
-// (8-byte gathers): measured faster than 8 at batch 32 on gfx950 because the
-// 8-column variant needs ~128 VGPRs and halves occupancy.  The bf16 SDDMM
-// keeps 8 columns, consumed pairwise by v_dot2_f32_bf16.  SNACK_BF16_CHMAX
-// (1, 2, 4 or 8) overrides the product width for experiments.
+// Widest per-lane chunk of batch columns.  The bf16 products take 4 columns
+// (8-byte gathers): with 8 the product kernel needs ~114 VGPRs and runs at
+// 4 waves per SIMD, which costs more at batch 32 on gfx950 than the wider
+// loads gain.  The bf16 value gradient takes 8 (16-byte gathers), consumed
+// pairwise by v_dot2_f32_bf16.  SNACK_BF16_CHMAX (1, 2, 4 or 8) overrides the
+// product width for experiments.
 static int bf16_chmax_products() {
   static int v = [] {
     const char* e = getenv("SNACK_BF16_CHMAX");
@@ -556,6 +589,9 @@ static int bf16_chmax_products() {
   return v;
 }
 
+// Lanes per item group and workgroup size: enough groups that a run of the
+// tile's < 2T merge-path items holds at most MP_RC entries, so each group
+// gathers its whole run in one round (capped at MP_MAX_THREADS threads).
 static lane_shape pick_shape(snack_dtype dt, int32_t B, int32_t tile_items, bool sddmm = false) {
   const int chmax = dt == SNACK_BF16 ? (sddmm ? 8 : bf16_chmax_products()) : 4;
   int ch = 1;
@@ -563,8 +599,8 @@ static lane_shape pick_shape(snack_dtype dt, int32_t B, int32_t tile_items, bool
   int want = (int)std::min<int64_t>(cdiv(B, ch), MP_MAX_BW / ch);
   int g_log2 = 0;
   while ((1 << g_log2) < want) ++g_log2;
-  // ~8 merge-path items per group: groups = T/8, at least one wave
-  int64_t thr = ((int64_t)std::max(1, tile_items / 8)) << g_log2;
+  int64_t groups = cdiv(2 * (int64_t)std::max(1, tile_items), MP_RC);
+  int64_t thr = groups << g_log2;
   thr = std::min<int64_t>(MP_MAX_THREADS, std::max<int64_t>(64, thr));
   thr = (thr + 63) / 64 * 64;
   return {ch, g_log2, ch << g_log2, (int)thr};
