@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsnack.so")
-SOURCES = ["api.hip", "prims.hip", "prepare.hip", "spmm.hip", "prune.hip", "aux.hip"]
+SOURCES = ["api.hip", "prims.hip", "prepare.hip", "spmm.hip", "prune.hip", "prune_bitmap.hip",
+           "aux.hip"]
 ARCH = os.environ.get("SNACK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

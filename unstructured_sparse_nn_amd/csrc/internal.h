@@ -31,6 +31,12 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint6
                           int32_t* const vbuf[2], int64_t n, int bits, void* tmp, hipStream_t s);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A small pinned, device-mapped host buffer per calling thread (256 bytes,
+// kept until the process ends): kernels write a call's few result words
+// straight into it, so a readback costs no copy.  NULL on failure.
+int32_t* host_result_buffer();
+int32_t* host_result_device(int32_t* host);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- products (spmm.hip) ----------------------------------------------------

@@ -314,4 +314,28 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint6
   return radix_sort<uint64_t>(keys_in, vals_in, kbuf, vbuf, n, bits, nullptr, nullptr, tmp, s);
 }
 
+// ============================================================== host results
+int32_t* host_result_buffer() {
+  thread_local int32_t* buf = nullptr;
+  if (!buf) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, 256, hipHostMallocMapped | hipHostMallocPortable) == hipSuccess)
+      buf = (int32_t*)p;
+  }
+  return buf;
+}
+
+int32_t* host_result_device(int32_t* host) {
+  thread_local int32_t* h = nullptr;
+  thread_local int32_t* d = nullptr;
+  if (!host) return nullptr;
+  if (host != h) {
+    void* p = nullptr;
+    if (hipHostGetDevicePointer(&p, host, 0) != hipSuccess) return nullptr;
+    h = host;
+    d = (int32_t*)p;
+  }
+  return d;
+}
+
 }  // namespace snk

@@ -1,0 +1,868 @@
+// prune_bitmap.hip -- prune/regrow over bitmaps of the M x K grid (gfx950).
+//
+// The rule is the one of snack_prune_regrow (drop the n_drop entries
+// smallest in (|value| bits, row*K+col); grow the first n_drop positions of
+// the SplitMix64 stream that lie outside the pre-step support and were not
+// taken before; write survivors + grown back row-major).  This plan serves
+// layers of density <= 1/4 whose support bitmap stays small; it needs no
+// sort:
+//   support  S, dropped D and grown G are bitmaps (bit b of word w is
+//            position 32w + b).  Block b of the entry kernels owns the words
+//            after the word of entry base_b - 1 up to the word of its last
+//            entry, and writes each of them exactly once (zeros included),
+//            so there is no fill kernel and no atomic;
+//   select   radix select of the threshold magnitude, one 8-bit digit per
+//            pass; each kernel picks the previous pass's digit itself from
+//            the replicated histogram (a block scan), so no pick kernels;
+//   regrow   stream indices are consumed in chunks whose size is the number
+//            of positions still missing.  A chunk then cannot take more
+//            than are missing, so taking every new distinct position of the
+//            chunk (atomic test-and-set on G: order-free) gives exactly the
+//            first n_drop acceptances of the stream.  The first chunks ride
+//            on the select kernels; one workgroup finishes the tail;
+//   write    new COO = the set bits of (S & ~D) | G in position order, a
+//            survivor's value being the old value at its rank in S.
+// One readback: the last kernel writes (error, positions missing) straight
+// into pinned host memory; row/col/vals are written only on success.
+#include <cstdlib>
+
+#include "common.h"
+#include "internal.h"
+#include "prune_common.h"
+
+namespace snk {
+namespace {
+
+constexpr int BT = 256;                   // threads per entry block
+constexpr int RND = 1;                    // rounds of 4 consecutive entries per thread
+constexpr int BE = 4 * BT * RND;          // entries per block: entry r*1024 + 4t + j
+constexpr int HREPL = 64;                 // select-histogram replicas
+constexpr int AREPL = 64;                 // acceptance-count replicas
+constexpr int GAPCAP = 512;               // long zero runs recorded per block
+constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
+constexpr int WT = 1024;                  // threads (= bitmap words) per write block
+constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
+constexpr int64_t GAP_INLINE = 16;        // zero runs of up to this many words: one thread
+constexpr int64_t STREAM_BOUND = 1ll << 40;
+// Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
+// are fat (few blocks) and their counters spread over replicas.
+
+struct bm_state {
+  uint32_t pfx[4], msk[4];  // select: magnitude bits fixed after pass p
+  int32_t need[4];          // drops still to place among entries matching pfx[p]
+  int32_t err;              // 1 NaN, 2 index out of range, 4 COO order, 8 stream bound
+  int32_t rem_final;        // positions still missing after the finisher
+  int32_t pad[2];
+  int64_t ch_start[SLOTS];  // chunk c: first stream index
+  int32_t ch_rem[SLOTS];    // chunk c: positions missing at its start (= its length)
+  int32_t ch_acc[SLOTS][AREPL];  // chunk c: positions it took, over AREPL counters
+  int32_t hist[4][HREPL][256];   // select histograms; block b adds into replica b % HREPL
+};
+
+__device__ __forceinline__ int32_t chunk_taken(const bm_state* st, int c) {
+  int32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < AREPL; ++i) a += st->ch_acc[c][i];
+  return a;
+}
+
+__device__ __forceinline__ int64_t lin_of(int32_t r, int32_t c, int32_t M, int32_t K) {
+  return (r < 0 || r >= M || c < 0 || c >= K) ? -1 : (int64_t)r * K + c;
+}
+
+__global__ __launch_bounds__(256) void k_bi_init(bm_state* st) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < 4 * HREPL * 256) (&st->hist[0][0][0])[i] = 0;
+  if (i < SLOTS * AREPL) (&st->ch_acc[0][0])[i] = 0;
+  if (i == 0) {
+    st->err = 0;
+    st->rem_final = 0;
+  }
+}
+
+// Digit of select pass `pass` holding the need-th smallest remaining
+// magnitude (one digit per thread, a block scan).  Output: the select state
+// after the pass.  Block 0 records it for later kernels.  256 threads.
+__device__ void pick_digit(bm_state* st, int pass, int shift, int32_t n_drop, uint32_t& pfx,
+                          uint32_t& msk, int32_t& need) {
+  __shared__ int32_t lds[BT / SNK_WAVE];
+  __shared__ int32_t pick[2];
+  const int t = threadIdx.x;
+  const uint32_t p0 = pass ? st->pfx[pass - 1] : 0u;
+  const uint32_t m0 = pass ? st->msk[pass - 1] : 0u;
+  const int32_t n0 = pass ? st->need[pass - 1] : n_drop;
+  int32_t h = 0;
+#pragma unroll
+  for (int r = 0; r < HREPL; ++r) h += st->hist[pass][r][t];
+  int32_t tot;
+  const int32_t ex = block_excl_scan_i32<BT>(h, lds, &tot);
+  if (t == BT - 1) {  // guard: the last digit
+    pick[0] = BT - 1;
+    pick[1] = ex;
+  }
+  __syncthreads();
+  if (ex < n0 && n0 <= ex + h) {
+    pick[0] = t;
+    pick[1] = ex;
+  }
+  __syncthreads();
+  pfx = p0 | ((uint32_t)pick[0] << shift);
+  msk = m0 | (255u << shift);
+  need = n0 - pick[1];
+  if (blockIdx.x == 0 && t == 0) {
+    st->pfx[pass] = pfx;
+    st->msk[pass] = msk;
+    st->need[pass] = need;
+  }
+}
+
+// Test-and-set candidates i0 + u*stride (u < 4, below `end`) on G unless
+// they lie in S; all loads and atomics of the group are issued before any
+// result is used.  Returns how many were taken.
+__device__ __forceinline__ int32_t take_group(int64_t i0, int64_t stride, int64_t end,
+                                              uint64_t stream, uint64_t MK,
+                                              const uint32_t* __restrict__ sup,
+                                              uint32_t* __restrict__ grown) {
+  uint64_t p[4];
+  uint32_t sw[4], old[4];
+  bool ok[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + u * stride;
+    ok[u] = i < end;
+    p[u] = ok[u] ? sm64_position(stream, (uint64_t)i, MK) : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sw[u] = ok[u] ? sup[p[u] >> 5] : 0xFFFFFFFFu;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t bit = 1u << (p[u] & 31);
+    old[u] = (sw[u] & bit) ? bit : atomicOr(&grown[p[u] >> 5], bit);
+  }
+  int32_t taken = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) taken += (old[u] & (1u << (p[u] & 31))) ? 0 : 1;
+  return taken;
+}
+
+// Regrow chunk c (stream indices [start, start + rem), rem = positions still
+// missing after chunk c-1), spread over the whole grid.  A candidate is
+// taken when it lies outside S and its bit in G was clear.
+__device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, int32_t n_drop,
+                             const uint32_t* __restrict__ sup, uint32_t* __restrict__ grown) {
+  __shared__ int32_t wsum[32];
+  int64_t start = 0;
+  int32_t rem = n_drop;
+  if (c > 0) {
+    start = st->ch_start[c - 1] + st->ch_rem[c - 1];
+    rem = st->ch_rem[c - 1] - chunk_taken(st, c - 1);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    st->ch_start[c] = start;
+    st->ch_rem[c] = rem;
+  }
+  if (rem <= 0 || st->err) return;  // uniform over the grid
+  if (start > STREAM_BOUND) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&st->err, 8);
+    return;
+  }
+  int32_t acc = 0;
+  const int64_t end = start + rem;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = start + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += 4 * stride)
+    acc += take_group(i, stride, end, stream, MK, sup, grown);
+  // one atomic per block, spread over AREPL counters (same-address device
+  // atomics serialise)
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, SNK_WAVE);
+  if (lane_id() == 0) wsum[threadIdx.x / SNK_WAVE] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t b = 0;
+    for (int i = 0; i < (int)(blockDim.x / SNK_WAVE); ++i) b += wsum[i];
+    if (b) atomicAdd(&st->ch_acc[c][blockIdx.x % AREPL], b);
+  }
+}
+
+// Zero words [lo, hi) of up to two bitmaps: short runs by the calling
+// thread, longer ones recorded in LDS for the whole block (fill_gaps).
+struct gap_list {
+  int64_t* lo;
+  int64_t* hi;
+  int32_t* n;
+};
+
+__device__ __forceinline__ void zero_words(uint32_t* a, uint32_t* b, int64_t lo, int64_t hi,
+                                           const gap_list& g) {
+  if (hi - lo <= 0) return;
+  if (hi - lo <= GAP_INLINE) {
+    for (int64_t u = lo; u < hi; ++u) {
+      a[u] = 0u;
+      if (b) b[u] = 0u;
+    }
+  } else {
+    const int32_t k = atomicAdd(g.n, 1);
+    if (k < GAPCAP) {
+      g.lo[k] = lo;
+      g.hi[k] = hi;
+    } else {  // list full: this thread fills it
+      for (int64_t u = lo; u < hi; ++u) {
+        a[u] = 0u;
+        if (b) b[u] = 0u;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void fill_gaps(uint32_t* a, uint32_t* b, const gap_list& g) {
+  __syncthreads();
+  const int32_t n = min(*g.n, GAPCAP);
+  for (int32_t k = 0; k < n; ++k)
+    for (int64_t u = g.lo[k] + threadIdx.x; u < g.hi[k]; u += blockDim.x) {
+      a[u] = 0u;
+      if (b) b[u] = 0u;
+    }
+}
+
+// Write the owned bitmap words of an entry block.  L[i] = linear index of
+// entry i of the block (-1: invalid), use[i] = its bit belongs in the map;
+// edge0 = word of entry base-1 (-1 for block 0); `more(w)` returns the bits
+// of the entries past the block's end that share word w.  Called by all
+// threads after L/use are complete in LDS.
+template <typename MORE>
+__device__ void write_owned_words(const int64_t* L, const uint8_t* use, int n, int64_t edge0,
+                                  bool last_block, int64_t W, uint32_t* a, uint32_t* b,
+                                  const gap_list& g, MORE more) {
+  for (int q = 0; q < 4 * RND; ++q) {
+    const int i = (q >> 2) * (4 * BT) + 4 * threadIdx.x + (q & 3);
+    if (i >= n || L[i] < 0) continue;
+    const int64_t w = L[i] >> 5;
+    const int64_t pw = i == 0 ? edge0 : (L[i - 1] < 0 ? w - 1 : (L[i - 1] >> 5));
+    if (i > 0 && pw == w) continue;  // not the first entry of its run
+    int e = i;
+    uint32_t bits = 0;
+    while (e < n && L[e] >= 0 && (L[e] >> 5) == w) {
+      if (use[e]) bits |= 1u << (L[e] & 31);
+      ++e;
+    }
+    if (w != edge0) {  // owned (the only unowned run is a first run in edge0's word)
+      if (e == n && !last_block) bits |= more(w);
+      a[w] = bits;
+      if (b) b[w] = 0u;
+      zero_words(a, b, pw + 1, w, g);
+    }
+    if (last_block && i + (e - i) == n) zero_words(a, b, w + 1, W, g);
+  }
+}
+
+// Support bitmap S (and G cleared), a copy of the values, the NaN / index
+// checks and the first select histogram.
+template <typename T>
+__global__ __launch_bounds__(BT) void k_bi_build(
+    const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
+    int64_t nnz, int32_t M, int32_t K, int64_t W, int shift, int32_t vec_ok, bm_state* st,
+    uint32_t* __restrict__ sup, uint32_t* __restrict__ grown, T* __restrict__ vals_ws) {
+  __shared__ int32_t h[256];
+  __shared__ int64_t L[BE];
+  __shared__ uint8_t use[BE];
+  __shared__ int64_t glo[GAPCAP], ghi[GAPCAP];
+  __shared__ int32_t gn;
+  __shared__ int64_t edge0_s;
+  const int t = threadIdx.x;
+  h[t] = 0;
+  if (t == 0) gn = 0;
+  const int64_t base = (int64_t)blockIdx.x * BE;
+  const int n = (int)std::min<int64_t>(BE, nnz - base);
+  if (t == 0) {
+    const int64_t e = base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1;
+    edge0_s = e < 0 ? -1 : (e >> 5);
+  }
+  // all loads first (one round trip)
+  int32_t r4[RND][4], c4[RND][4];
+  T v4[RND][4];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+    if (vec_ok && k0 + 3 < nnz) {
+      const int4 rv = *reinterpret_cast<const int4*>(row + k0);
+      const int4 cv = *reinterpret_cast<const int4*>(col + k0);
+      const vec<T, 4> vv = *reinterpret_cast<const vec<T, 4>*>(vals + k0);
+      r4[r][0] = rv.x; r4[r][1] = rv.y; r4[r][2] = rv.z; r4[r][3] = rv.w;
+      c4[r][0] = cv.x; c4[r][1] = cv.y; c4[r][2] = cv.z; c4[r][3] = cv.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[r][j] = vv.v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = k0 + j < nnz;
+        r4[r][j] = ok ? row[k0 + j] : 0;
+        c4[r][j] = ok ? col[k0 + j] : 0;
+        v4[r][j] = ok ? vals[k0 + j] : (T)0;
+      }
+    }
+  }
+  int err = 0;
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = magnitude<T>(raw_bits(v4[r][j]));
+      const bool ok = k0 + j < nnz;
+      wave_hist_add(h, (a >> shift) & 255u, ok);
+      if (ok) {
+        vals_ws[k0 + j] = v4[r][j];
+        const int64_t l = lin_of(r4[r][j], c4[r][j], M, K);
+        if (is_nan_mag<T>(a)) err |= 1;
+        if (l < 0) err |= 2;
+        const int i = r * (4 * BT) + 4 * t + j;
+        L[i] = l;
+        use[i] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  // strictly increasing: against the previous entry (the block's left edge
+  // from global memory)
+  for (int q = 0; q < 4 * RND; ++q) {
+    const int i = (q >> 2) * (4 * BT) + 4 * t + (q & 3);
+    if (i >= n || L[i] < 0) continue;
+    const int64_t pl = i > 0 ? L[i - 1]
+                             : (base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1);
+    if (pl >= 0 && L[i] <= pl) err |= 4;
+  }
+  const gap_list g{glo, ghi, &gn};
+  const int64_t edge0 = edge0_s;
+  const bool last_block = base + n >= nnz;
+  write_owned_words(L, use, n, edge0, last_block, W, sup, grown, g, [&](int64_t w) {
+    uint32_t bits = 0;
+    for (int64_t k = base + n; k < nnz && k < base + n + 32; ++k) {
+      const int64_t l = lin_of(row[k], col[k], M, K);
+      if (l < 0 || (l >> 5) != w) break;
+      bits |= 1u << (l & 31);
+    }
+    return bits;
+  });
+  fill_gaps(sup, grown, g);
+  if (err) atomicOr(&st->err, err);
+  __syncthreads();
+  if (h[t]) atomicAdd(&st->hist[0][blockIdx.x % HREPL][t], h[t]);
+}
+
+// Select pass `pass` >= 1: pick the previous pass's digit, histogram the
+// next digit of the entries matching the prefix; then regrow chunk c.
+template <typename T>
+__global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64_t nnz,
+                                               int pass, int prev_shift, int shift,
+                                               int32_t n_drop, int32_t c, uint64_t stream,
+                                               uint64_t MK, bm_state* st,
+                                               const uint32_t* __restrict__ sup,
+                                               uint32_t* __restrict__ grown) {
+  __shared__ int32_t h[256];
+  const int t = threadIdx.x;
+  h[t] = 0;
+  const int64_t base = (int64_t)blockIdx.x * BE;
+  uint32_t a[RND][4];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[r][j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0u;
+  }
+  uint32_t pfx, msk;
+  int32_t need;
+  pick_digit(st, pass - 1, prev_shift, n_drop, pfx, msk, need);
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wave_hist_add(h, (a[r][j] >> shift) & 255u, k0 + j < nnz && (a[r][j] & msk) == pfx);
+  }
+  __syncthreads();
+  if (h[t]) atomicAdd(&st->hist[pass][blockIdx.x % HREPL][t], h[t]);
+  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
+}
+
+// Last pick (the threshold magnitude tau and the ties to drop), entries at
+// tau per block; then regrow chunk c.
+template <typename T>
+__global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int64_t nnz,
+                                                 int last_pass, int shift, int32_t n_drop,
+                                                 int32_t c, uint64_t stream, uint64_t MK,
+                                                 bm_state* st, int32_t* __restrict__ cnt_eq,
+                                                 const uint32_t* __restrict__ sup,
+                                                 uint32_t* __restrict__ grown) {
+  __shared__ int32_t lds[BT / SNK_WAVE];
+  const int64_t base = (int64_t)blockIdx.x * BE;
+  uint32_t a[RND][4];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[r][j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
+  }
+  uint32_t tau, msk;
+  int32_t need;
+  pick_digit(st, last_pass, shift, n_drop, tau, msk, need);
+  int32_t eq = 0;
+#pragma unroll
+  for (int r = 0; r < RND; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eq += a[r][j] == tau ? 1 : 0;
+  int32_t tot;
+  block_excl_scan_i32<BT>(eq, lds, &tot);
+  if (threadIdx.x == 0) cnt_eq[blockIdx.x] = tot;
+  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
+}
+
+// One workgroup: base_eq[b] = entries at tau in blocks before b (used when
+// there are too many blocks for each to sum its own prefix).
+__global__ __launch_bounds__(1024) void k_bi_eq_scan(const int32_t* __restrict__ cnt_eq,
+                                                     int32_t* __restrict__ base_eq, int64_t nblk) {
+  __shared__ int32_t lds[1024 / SNK_WAVE];
+  int32_t run = 0;
+  for (int64_t c = 0; c < nblk; c += 1024) {
+    const int64_t b = c + threadIdx.x;
+    const int32_t v = b < nblk ? cnt_eq[b] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan_i32<1024>(v, lds, &tot);
+    if (b < nblk) base_eq[b] = run + ex;
+    run += tot;
+  }
+}
+
+// Sum of v[0..n) over the block (all threads get it).
+__device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ v, int64_t n) {
+  __shared__ int32_t lds[32];
+  int32_t s = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += v[i];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, SNK_WAVE);
+  if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = s;
+  __syncthreads();
+  int32_t tot = 0;
+  for (int i = 0; i < (int)(blockDim.x / SNK_WAVE); ++i) tot += lds[i];
+  __syncthreads();
+  return tot;
+}
+
+// Dropped bitmap D: entry k is dropped if its magnitude is below tau, or at
+// tau with tie rank (index order) below need.  Then regrow chunk c.
+template <typename T>
+__global__ __launch_bounds__(BT) void k_bi_drop(
+    const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
+    int64_t nnz, int32_t M, int32_t K, int64_t W, int last_pass, const int32_t* __restrict__ cnt_eq,
+    const int32_t* __restrict__ base_eq, int32_t n_drop, int32_t c, uint64_t stream, uint64_t MK,
+    bm_state* st, uint32_t* __restrict__ dropb, const uint32_t* __restrict__ sup,
+    uint32_t* __restrict__ grown) {
+  __shared__ int32_t lds[BT / SNK_WAVE];
+  __shared__ int64_t L[BE];
+  __shared__ uint8_t use[BE];
+  __shared__ int64_t glo[GAPCAP], ghi[GAPCAP];
+  __shared__ int32_t gn;
+  __shared__ int64_t edge0_s;
+  const int t = threadIdx.x;
+  if (t == 0) gn = 0;
+  const uint32_t tau = st->pfx[last_pass];
+  const int32_t need = st->need[last_pass];
+  const int64_t base = (int64_t)blockIdx.x * BE;
+  const int n = (int)std::min<int64_t>(BE, nnz - base);
+  if (t == 0) {
+    const int64_t e = base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1;
+    edge0_s = e < 0 ? -1 : (e >> 5);
+  }
+  uint32_t a[RND][4];
+  int32_t r4[RND][4], c4[RND][4];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = k0 + j < nnz;
+      a[r][j] = ok ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
+      r4[r][j] = ok ? row[k0 + j] : -1;
+      c4[r][j] = ok ? col[k0 + j] : -1;
+    }
+  }
+  const int32_t E = base_eq ? base_eq[blockIdx.x] : block_sum_prefix(cnt_eq, blockIdx.x);
+  // tie ranks in index order: rounds in turn, a block scan each
+  int32_t run = E;
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    int32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eq += a[r][j] == tau ? 1 : 0;
+    int32_t tot;
+    int32_t er = run + block_excl_scan_i32<BT>(eq, lds, &tot);
+    run += tot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = r * (4 * BT) + 4 * t + j;
+      if (i >= n) continue;
+      const bool is_eq = a[r][j] == tau;
+      use[i] = (a[r][j] < tau || (is_eq && er < need)) ? 1 : 0;
+      er += is_eq ? 1 : 0;
+      L[i] = lin_of(r4[r][j], c4[r][j], M, K);
+    }
+  }
+  __syncthreads();
+  const gap_list g{glo, ghi, &gn};
+  const int64_t edge0 = edge0_s;
+  const bool last_block = base + n >= nnz;
+  write_owned_words(L, use, n, edge0, last_block, W, dropb, nullptr, g, [&](int64_t w) {
+    // entries of the next block in word w, with their own tie ranks
+    int32_t ern = run;
+    uint32_t bits = 0;
+    for (int64_t k = base + n; k < nnz && k < base + n + 32; ++k) {
+      const int64_t l = lin_of(row[k], col[k], M, K);
+      if (l < 0 || (l >> 5) != w) break;
+      const uint32_t m = magnitude<T>(raw_bits(vals[k]));
+      if (m < tau || (m == tau && ern < need)) bits |= 1u << (l & 31);
+      ern += m == tau ? 1 : 0;
+    }
+    return bits;
+  });
+  fill_gaps(dropb, nullptr, g);
+  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
+}
+
+// A regrow chunk on its own (only when the acceptance rate is low).
+__global__ __launch_bounds__(BT) void k_bi_chunk(int32_t c, uint64_t stream, uint64_t MK,
+                                                 int32_t n_drop, bm_state* st,
+                                                 const uint32_t* __restrict__ sup,
+                                                 uint32_t* __restrict__ grown) {
+  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
+}
+
+// One workgroup: chunks after grid chunk c-1 until nothing is missing (or
+// the stream bound).  Records the positions still missing.
+constexpr int FT = 1024;
+constexpr int FINISH_ROUNDS = 4096;
+__global__ __launch_bounds__(FT) void k_bi_finish(int32_t c, uint64_t stream, uint64_t MK,
+                                                  int32_t n_drop, bm_state* st,
+                                                  const uint32_t* __restrict__ sup,
+                                                  uint32_t* __restrict__ grown) {
+  __shared__ int32_t red[FT / SNK_WAVE];
+  const int t = threadIdx.x;
+  int64_t start = 0;
+  int32_t rem = n_drop;
+  if (c > 0) {
+    start = st->ch_start[c - 1] + st->ch_rem[c - 1];
+    rem = st->ch_rem[c - 1] - chunk_taken(st, c - 1);
+  }
+  const bool ok = st->err == 0;
+  // density <= 1/4 keeps the acceptance rate >= 1/2, so the remainder
+  // roughly halves per round; the round cap only bounds a broken state
+  for (int round = 0; ok && rem > 0; ++round) {
+    if (start > STREAM_BOUND || round >= FINISH_ROUNDS) {
+      if (t == 0) atomicOr(&st->err, 8);
+      break;
+    }
+    int32_t acc = 0;
+    for (int64_t i = start + t; i < start + rem; i += 4 * FT)
+      acc += take_group(i, FT, start + rem, stream, MK, sup, grown);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, SNK_WAVE);
+    if (lane_id() == 0) red[t / SNK_WAVE] = acc;
+    __syncthreads();
+    int32_t taken = 0;
+    for (int i = 0; i < FT / SNK_WAVE; ++i) taken += red[i];
+    __syncthreads();
+    start += rem;
+    rem -= taken;
+  }
+  if (t == 0) st->rem_final = rem;
+}
+
+__device__ __forceinline__ int4 word_counts(uint32_t S, uint32_t D, uint32_t G) {
+  return make_int4(__popc((S & ~D) | G), __popc(S), __popc(D), __popc(G));
+}
+
+__device__ __forceinline__ int4 add4(int4 a, int4 b) {
+  return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Per block of WT words: popcounts of (new support, old support, dropped,
+// grown).
+__global__ __launch_bounds__(WT) void k_bi_wsum(const uint32_t* __restrict__ sup,
+                                                const uint32_t* __restrict__ dropb,
+                                                const uint32_t* __restrict__ grown, int64_t W,
+                                                int4* __restrict__ bsum) {
+  __shared__ int4 lds[WT / SNK_WAVE];
+  const int64_t w = (int64_t)blockIdx.x * WT + threadIdx.x;
+  int4 c = w < W ? word_counts(sup[w], dropb[w], grown[w]) : make_int4(0, 0, 0, 0);
+  for (int off = 32; off > 0; off >>= 1) {
+    c.x += __shfl_xor(c.x, off, SNK_WAVE);
+    c.y += __shfl_xor(c.y, off, SNK_WAVE);
+    c.z += __shfl_xor(c.z, off, SNK_WAVE);
+    c.w += __shfl_xor(c.w, off, SNK_WAVE);
+  }
+  if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int4 tot = make_int4(0, 0, 0, 0);
+    for (int i = 0; i < WT / SNK_WAVE; ++i) tot = add4(tot, lds[i]);
+    bsum[blockIdx.x] = tot;
+  }
+}
+
+// One workgroup: exclusive prefix of n int4 block sums (thread t owns a
+// contiguous segment).  Only used for very large bitmaps.
+__global__ __launch_bounds__(1024) void k_bi_bscan(const int4* __restrict__ in,
+                                                   int4* __restrict__ out, int64_t n) {
+  __shared__ int32_t lds[1024 / SNK_WAVE];
+  const int64_t per = cdiv_dev(n, 1024);
+  const int64_t a = std::min<int64_t>(n, (int64_t)threadIdx.x * per);
+  const int64_t b = std::min<int64_t>(n, a + per);
+  int4 s = make_int4(0, 0, 0, 0);
+  for (int64_t i = a; i < b; ++i) s = add4(s, in[i]);
+  int32_t tot;
+  int4 e;
+  e.x = block_excl_scan_i32<1024>(s.x, lds, &tot);
+  e.y = block_excl_scan_i32<1024>(s.y, lds, &tot);
+  e.z = block_excl_scan_i32<1024>(s.z, lds, &tot);
+  e.w = block_excl_scan_i32<1024>(s.w, lds, &tot);
+  for (int64_t i = a; i < b; ++i) {
+    out[i] = e;
+    e = add4(e, in[i]);
+  }
+}
+
+// New COO (the set bits of (S & ~D) | G in position order), the dropped and
+// grown lists; one thread per bitmap word.  Block 0 reports (error,
+// positions missing) into pinned host memory; nothing else is written
+// unless both are 0.  Writes are clamped to nnz / n_drop.
+template <typename T>
+__global__ __launch_bounds__(WT) void k_bi_emit(
+    const uint32_t* __restrict__ sup, const uint32_t* __restrict__ dropb,
+    const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
+    const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
+    int64_t nnz, int64_t n_drop, const bm_state* st, int32_t* __restrict__ result,
+    int32_t* __restrict__ row,
+    int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
+    int64_t* __restrict__ grown_lin) {
+  __shared__ int32_t lds[WT / SNK_WAVE];
+  __shared__ int4 red[WT / SNK_WAVE];
+  const int t = threadIdx.x;
+  const int32_t err = st->err, missing = st->rem_final;
+  if (blockIdx.x == 0 && t == 0) {
+    result[0] = err;
+    result[1] = missing;
+  }
+  if (err || missing > 0) return;
+  // block base: the sum of the sums of earlier blocks
+  int4 bo;
+  if (boff) {
+    bo = boff[blockIdx.x];
+  } else {
+    int4 s = make_int4(0, 0, 0, 0);
+    for (int64_t i = t; i < (int64_t)blockIdx.x; i += WT) s = add4(s, bsum[i]);
+    for (int off = 32; off > 0; off >>= 1) {
+      s.x += __shfl_xor(s.x, off, SNK_WAVE);
+      s.y += __shfl_xor(s.y, off, SNK_WAVE);
+      s.z += __shfl_xor(s.z, off, SNK_WAVE);
+      s.w += __shfl_xor(s.w, off, SNK_WAVE);
+    }
+    if (lane_id() == 0) red[t / SNK_WAVE] = s;
+    __syncthreads();
+    bo = make_int4(0, 0, 0, 0);
+    for (int i = 0; i < WT / SNK_WAVE; ++i) bo = add4(bo, red[i]);
+  }
+  const int64_t w = (int64_t)blockIdx.x * WT + t;
+  const uint32_t S = w < W ? sup[w] : 0u, D = w < W ? dropb[w] : 0u, G = w < W ? grown[w] : 0u;
+  const int4 c = word_counts(S, D, G);
+  // a block holds at most 32 * WT = 32768 positions, so two counts share an
+  // int32 (16 bits each) and two block scans serve all four
+  int32_t tot;
+  const int32_t fs = block_excl_scan_i32<WT>(c.x | (c.y << 16), lds, &tot);
+  const int32_t dg = block_excl_scan_i32<WT>(c.z | (c.w << 16), lds, &tot);
+  int64_t qf = bo.x + (fs & 0xFFFF);
+  const int64_t qs = bo.y + (fs >> 16);
+  int64_t qd = bo.z + (dg & 0xFFFF);
+  int64_t qg = bo.w + (dg >> 16);
+  const int64_t pw = w * 32;
+  uint32_t F = (S & ~D) | G;
+  if (F) {
+    // row and column of the word's first position; the rest step from it
+    int32_t r0, c0;
+    if (small_grid) {
+      r0 = (int32_t)((uint32_t)pw / (uint32_t)K);
+      c0 = (int32_t)((uint32_t)pw - (uint32_t)r0 * (uint32_t)K);
+    } else {
+      r0 = (int32_t)(pw / K);
+      c0 = (int32_t)(pw - (int64_t)r0 * K);
+    }
+    while (F) {
+      const int b = __ffs(F) - 1;
+      F &= F - 1;
+      if (qf < nnz) {
+        int32_t r = r0, cc = c0 + b;
+        while (cc >= K) {
+          cc -= K;
+          ++r;
+        }
+        row[qf] = r;
+        col[qf] = cc;
+        vals[qf] = ((S >> b) & 1u) ? vals_ws[qs + __popc(S & ((1u << b) - 1u))] : (T)0;
+      }
+      ++qf;
+    }
+  }
+  if (dropped_lin) {
+    uint32_t Dw = D;
+    while (Dw) {
+      const int b = __ffs(Dw) - 1;
+      Dw &= Dw - 1;
+      if (qd < n_drop) dropped_lin[qd] = pw + b;
+      ++qd;
+    }
+  }
+  if (grown_lin) {
+    uint32_t Gw = G;
+    while (Gw) {
+      const int b = __ffs(Gw) - 1;
+      Gw &= Gw - 1;
+      if (qg < n_drop) grown_lin[qg] = pw + b;
+      ++qg;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host
+struct bm_layout {
+  int64_t nblk, W, nb;
+  size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff, total;
+};
+
+bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
+  bm_layout L{};
+  L.nblk = std::max<int64_t>(1, cdiv(nnz, BE));
+  L.W = cdiv((int64_t)M * K, 32);
+  L.nb = std::max<int64_t>(1, cdiv(L.W, WT));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.state = take(sizeof(bm_state));
+  L.cnt_eq = take(4 * (size_t)L.nblk);
+  L.base_eq = take(4 * (size_t)L.nblk);
+  L.sup = take(4 * (size_t)L.W);
+  L.dropb = take(4 * (size_t)L.W);
+  L.grown = take(4 * (size_t)L.W);
+  L.vals = take(4 * (size_t)std::max<int64_t>(nnz, 1));
+  L.bsum = take(16 * (size_t)L.nb);
+  L.boff = take(16 * (size_t)L.nb);
+  L.total = o;
+  return L;
+}
+
+// Grid-wide regrow chunks before the finisher: the ones riding on the select
+// kernels, plus stand-alone ones while the expected remainder
+// n_drop * (1 - q)^c stays above what one workgroup finishes quickly (q: a
+// lower bound on the acceptance rate).
+int32_t grid_chunks(int64_t MK, int64_t nnz, int64_t n_drop, int32_t riding) {
+  const double q = std::max(0.5, 1.0 - (double)(nnz + n_drop) / (double)MK);
+  int32_t c = riding;
+  double rem = (double)n_drop;
+  for (int i = 0; i < riding; ++i) rem *= 1.0 - q;
+  while (rem > 2048.0 && c < SLOTS) {
+    rem *= 1.0 - q;
+    ++c;
+  }
+  return c;
+}
+
+template <typename T>
+snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int64_t nnz,
+                 int64_t n_drop, uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                 int64_t* grown_lin, char* ws, hipStream_t s) {
+  const bm_layout L = make_layout(M, K, nnz);
+  bm_state* st = (bm_state*)(ws + L.state);
+  int32_t* cnt_eq = (int32_t*)(ws + L.cnt_eq);
+  int32_t* base_eq = (int32_t*)(ws + L.base_eq);
+  uint32_t* sup = (uint32_t*)(ws + L.sup);
+  uint32_t* dropb = (uint32_t*)(ws + L.dropb);
+  uint32_t* grown = (uint32_t*)(ws + L.grown);
+  T* vals_ws = (T*)(ws + L.vals);
+  int4* bsum = (int4*)(ws + L.bsum);
+  int4* boff = (int4*)(ws + L.boff);
+  const uint64_t MK = (uint64_t)M * (uint64_t)K;
+  const uint64_t stream = sm64_mix(seed + (step + 1) * SM64_GAMMA);
+  const int32_t nd = (int32_t)n_drop;
+  const dim3 eb((unsigned)L.nblk), et(BT);
+
+  int32_t* res_host = host_result_buffer();
+  int32_t* res_dev = host_result_device(res_host);
+  if (!res_host || !res_dev) return SNACK_E_HIP;
+  res_host[0] = res_host[1] = INT32_MIN;
+
+  hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(4 * HREPL * 256, 256)), dim3(256), 0, s, st);
+  const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
+                          (uintptr_t)vals % (4 * sizeof(T)) == 0) ? 1 : 0;
+  const int passes = sizeof(T) == 2 ? 2 : 4;
+  const int top = 8 * (passes - 1);
+  hipLaunchKernelGGL(k_bi_build<T>, eb, et, 0, s, row, col, vals, nnz, M, K, L.W, top, vec_ok, st,
+                     sup, grown, vals_ws);
+  int32_t c = 0;
+  for (int p = 1; p < passes; ++p, ++c)
+    hipLaunchKernelGGL(k_bi_sel<T>, eb, et, 0, s, vals, nnz, p, top - 8 * (p - 1), top - 8 * p,
+                       nd, c, stream, MK, st, sup, grown);
+  hipLaunchKernelGGL(k_bi_count<T>, eb, et, 0, s, vals, nnz, passes - 1, 0, nd, c, stream, MK, st,
+                     cnt_eq, sup, grown);
+  ++c;
+  const bool own_prefix = L.nblk <= PREFIX_INBLOCK_MAX;
+  if (!own_prefix)
+    hipLaunchKernelGGL(k_bi_eq_scan, dim3(1), dim3(1024), 0, s, cnt_eq, base_eq, L.nblk);
+  hipLaunchKernelGGL(k_bi_drop<T>, eb, et, 0, s, row, col, vals, nnz, M, K, L.W, passes - 1,
+                     cnt_eq, own_prefix ? nullptr : base_eq, nd, c, stream, MK, st, dropb, sup,
+                     grown);
+  ++c;
+  const int32_t total = grid_chunks((int64_t)MK, nnz, n_drop, c);
+  const unsigned cb = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(n_drop, BT)));
+  for (; c < total; ++c)
+    hipLaunchKernelGGL(k_bi_chunk, dim3(cb), dim3(BT), 0, s, c, stream, MK, nd, st, sup, grown);
+  hipLaunchKernelGGL(k_bi_finish, dim3(1), dim3(FT), 0, s, c, stream, MK, nd, st, sup, grown);
+  hipLaunchKernelGGL(k_bi_wsum, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
+                     bsum);
+  const bool own_base = L.nb <= PREFIX_INBLOCK_MAX;
+  if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
+  hipLaunchKernelGGL(k_bi_emit<T>, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
+                     bsum, own_base ? nullptr : boff, vals_ws, K,
+                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, row, col, vals,
+                     dropped_lin, grown_lin);
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return SNACK_E_HIP;
+  const int32_t err = res_host[0], missing = res_host[1];
+  if (err == INT32_MIN) return SNACK_E_HIP;
+  if (err & 1) return SNACK_E_NAN;
+  if (err & 2) return SNACK_E_COO_RANGE;
+  if (err & 4) return SNACK_E_COO_ORDER;
+  if ((err & 8) || missing > 0) return SNACK_E_COUNT;
+  return SNACK_OK;
+}
+
+}  // namespace
+
+// Density <= 1/4 (every chunk then takes at least half of what it draws,
+// up to duplicates) and three bitmaps within ~16 bytes per entry + 4 MB.
+bool prune_bitmap_ok(int32_t M, int32_t K, int64_t nnz) {
+  const int64_t MK = (int64_t)M * K;
+  return nnz > 0 && 4 * nnz <= MK && cdiv(MK, 32) <= 4 * nnz + (1 << 20);
+}
+
+size_t prune_bitmap_ws_bytes(int32_t M, int32_t K, int64_t nnz) {
+  return make_layout(M, K, nnz).total;
+}
+
+snack_status prune_bitmap(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
+                          int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
+                          int64_t* dropped_lin, int64_t* grown_lin, void* ws, hipStream_t s) {
+  if (dt == SNACK_F32)
+    return run<float>(row, col, (float*)vals, M, K, nnz, n_drop, seed, step, dropped_lin,
+                      grown_lin, (char*)ws, s);
+  return run<bf16>(row, col, (bf16*)vals, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
+                   (char*)ws, s);
+}
+
+}  // namespace snk
