@@ -5,7 +5,9 @@ sparsity (838,861 nnz, bf16 values and activations, fp32 accumulation) on a
 batch of 32:
     forward Y = X W^T  ->  input gradient dX = dY W  ->  value gradient
     dV = (dY^T X) at the nonzeros  ->  prune/regrow of 30% of the
-    connections  ->  re-prepare the topology (offsets, tiles, column view).
+    connections  ->  re-prepare the topology (offsets, tiles, column view);
+    the last two are one call (snack_prune_regrow_prepared) unless
+    --restructure separate.
 The metric is the fwd+bwd SpMM bandwidth: algorithmic bytes of the three
 products (values + indices + offsets + activations read + outputs written)
 per second of whole-step time.  Inputs are resident in HBM before timing;
@@ -66,6 +68,9 @@ def parse():
                     help="also time fwd/dX/dV at 95/99%% x B in {1,8,32}")
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--restructure", choices=("fused", "separate"), default="fused",
+                    help="prune/regrow + prepare as one call (snack_prune_regrow_prepared) or "
+                         "as two")
     ap.add_argument("--products-only", action="store_true",
                     help="time only fwd/dX/dV (for profiling the product kernels)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -127,9 +132,14 @@ class Instance:
         t.grad_vals(self.dY, self.X, self.B, self.lay, out=self.dV)
         if ev: ev[3].record()
 
-    def restructure(self, ev=None):
+    def restructure(self, ev=None, fused=True):
         import unstructured_sparse_nn_amd as snk
         self.step_no += 1
+        if fused:  # prune/regrow and re-prepare in one call
+            snk.snack_prune_regrow_prepared(self.topo.plan, self.row, self.col, self.vals,
+                                            self.n_drop, 0, self.step_no, None, None, self.ws)
+            if ev: ev[4].record()
+            return
         snk.snack_prune_regrow(self.row, self.col, self.vals, self.M, self.K, self.topo.nnz,
                                self.n_drop, 0, self.step_no, None, None, self.ws)
         if ev: ev[4].record()
@@ -311,11 +321,13 @@ def run_bench(args):
              for _ in range(R)]
     torch.cuda.synchronize()
 
+    fused = args.restructure == "fused"
+
     def step(i, ev=None):
         inst = insts[i % R]
         inst.products(ev)
         if not args.products_only:
-            inst.restructure(ev)
+            inst.restructure(ev, fused)
 
     log("warmup")
     for i in range(args.warmup):
@@ -333,10 +345,11 @@ def run_bench(args):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / K_ * 1e3
 
-    n_ops = 3 if args.products_only else 5
+    n_ops = 3 if args.products_only else (4 if fused else 5)
     ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(n_ops)]
                    for i in range(K_)])
-    names = ["fwd", "bwd_input", "sddmm", "prune_regrow", "prepare"][:n_ops]
+    names = (["fwd", "bwd_input", "sddmm", "restructure"] if fused else
+             ["fwd", "bwd_input", "sddmm", "prune_regrow", "prepare"])[:n_ops]
     ops = {}
     prod_bytes = 0
     for j, op in enumerate(names):
@@ -376,7 +389,8 @@ def run_bench(args):
                                   f"({wt.nnz} nnz, uniform), bf16 values+activations, fp32 "
                                   f"accumulate, batch {B}; step = fwd+dX+dV"
                       + ("" if args.products_only else
-                         f"+prune/regrow {args.drop_ppm / 1e4:g}%+prepare"),
+                         f"+prune/regrow {args.drop_ppm / 1e4:g}%+prepare"
+                         + (" (one fused call)" if fused else "")),
                       "M": N, "K": N, "nnz": wt.nnz, "batch": B,
                       "layout": "node-major (K x B)" if args.layout == "node" else "batch-major (B x K)",
                       "rotate_instances": R,

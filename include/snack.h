@@ -240,6 +240,29 @@ SNACK_API snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals
                                 int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * snack_prune_regrow_prepared -- snack_prune_regrow followed by
+ * snack_coo_prepare of the result, in one call with one synchronisation.
+ * `plan` must have been prepared (snack_coo_prepare) for a COO with the same
+ * M, K and nnz; on success it describes the new COO (row/col as passed) in
+ * its own arena.  When the layer has density <= 1/4 and M and K are
+ * multiples of 32, the derived arrays are built straight from the support
+ * bitmap of the new COO (row offsets from prefix popcounts, the column view
+ * from a 32 x 32 bit-tile transpose), with no sort and no re-validation;
+ * otherwise the two calls run one after the other.  Results (COO, lists,
+ * derived arrays) are identical either way.  dtype, n_drop, seed, step,
+ * dropped_lin, grown_lin, ws, ws_bytes: as for snack_prune_regrow (ws sized
+ * by snack_prune_regrow_workspace).  Errors: as for snack_prune_regrow, plus
+ * SNACK_E_NOT_PREPARED (plan never prepared) and SNACK_E_SHAPE (plan of
+ * another shape).  On error the plan must be prepared again before use.
+ * Synchronises `stream`.
+ */
+SNACK_API snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* row, int32_t* col,
+                                         void* vals, snack_dtype dtype, int64_t n_drop,
+                                         uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                         int64_t* grown_lin, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/*
  * GELU with the exact error function, h = z * Phi(z), and its backward
  * dz = dh * (Phi(z) + z * phi(z)), elementwise over n fp32 values (the
  * nonlinearity between the two sparse layers of a GPT-2-shaped MLP block).

@@ -414,6 +414,58 @@ def test_prune_regrow_rejects_invalid_coo_on_bitmap_plan():
     assert np.array_equal(row.cpu().numpy(), r) and np.array_equal(col.cpu().numpy(), c)
 
 
+PREPARED_CASES = [
+    ("single", "f32", 100000, 0, 1, 0),          # 256 x 256: fused
+    ("gpt2_0.9", "f32", 300000, 0, 5, 0),        # 3072 x 768: fused
+    ("square_0.95_32", "bf16", 300000, 3, 2, 0),  # 4096 x 4096: fused
+    ("ragged", "bf16", 250000, 4, 7, 0),         # 300 x 200: not multiples of 32, two calls
+    ("single", "f32", 100000, 2, 3, 64),         # small tiles: rows and columns split
+]
+
+
+@pytest.mark.parametrize("name,dt,ppm,seed,step,tile", PREPARED_CASES)
+def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile):
+    """The fused restructure leaves exactly the COO of the oracle's step and
+    the plan snack_coo_prepare would build for it, and the products on that
+    plan match the oracle."""
+    if name == "ragged":
+        w = synth.random_case(12, 300, 200, 6000, 1, dt).weights[0]
+    else:
+        w = workload(name).weights[0]
+    n_drop = orc.drop_count(w.nnz, ppm)
+    ref = orc.prune_regrow(w.M, w.K, w.row, w.col, w.vals, dt, n_drop, seed, step)
+    assert ref["rc"] == 0
+    topo = topology(w, 4, tile)
+    v = to_dev(w.vals, dt)
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+                     dtype=torch.uint8, device="cuda")
+    dl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
+    gl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
+    snk.snack_prune_regrow_prepared(topo.plan, topo.row, topo.col, v, n_drop, seed, step, dl, gl,
+                                    ws)
+    assert np.array_equal(topo.row.cpu().numpy(), ref["row"])
+    assert np.array_equal(topo.col.cpu().numpy(), ref["col"])
+    assert np.array_equal(dl.cpu().numpy(), ref["dropped"])
+    assert np.array_equal(gl.cpu().numpy(), ref["grown"])
+    w2 = synth.SparseWeight(w.M, w.K, ref["row"], ref["col"], ref["vals"], dt)
+    check_prepare(orc, w2, topo)
+    xf = np.random.default_rng(14).standard_normal(4 * w.K).astype(np.float32)
+    Xa = synth.Activation(xf if dt == "f32" else synth.f32_to_bf16_bits(xf), dt, 4, w.K,
+                          "batch")
+    Y = topo.fwd(v, to_dev(Xa.data, dt), 4, B.BATCH_MAJOR)
+    r, S = orc.spmm_fwd(w.M, w.K, ref["row"], ref["col"], w2.vals_f64(), 4, Xa.f64(), False)
+    assert_within(from_dev(Y, dt), r, S, dt, "fwd after restructure")
+
+
+def test_prune_regrow_prepared_rejects_unprepared_plan():
+    plan = snk.snack_plan_init(64, 64, 400, 1)
+    row = torch.zeros(400, dtype=torch.int32, device="cuda")
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_prune_regrow_prepared(plan, row, row, torch.zeros(400, device="cuda"), 40, 1, 1,
+                                        None, None, None)
+    assert e.value.status == -12
+
+
 # --------------------------------------------------------------- aux
 def test_gelu_matches_oracle(orc):
     z = torch.linspace(-8, 8, 100003, device="cuda")

@@ -70,6 +70,8 @@ def _load():
         "snack_drop_count": ([i64, i32], i64),
         "snack_prune_regrow_workspace": ([i32, i32, i64, i64, ctypes.POINTER(sz)], i32),
         "snack_prune_regrow": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz, P], i32),
+        "snack_prune_regrow_prepared": ([plan_p, P, P, P, i32, i64, u64, u64, P, P, P, sz, P],
+                                        i32),
         "snack_gelu_fwd": ([P, P, i64, P], i32),
         "snack_gelu_bwd": ([P, P, P, i64, P], i32),
         "snack_dense_fwd": ([P, P, i32, i32, i32, P, i32, P, P], i32),
@@ -197,6 +199,19 @@ def snack_prune_regrow(row, col, vals, M, K, nnz, n_drop, seed, step, dropped_li
                                    seed & (2**64 - 1), step & (2**64 - 1), _ptr(dropped_lin),
                                    _ptr(grown_lin), _ptr(ws), ws_bytes, _stream(stream)),
            "snack_prune_regrow")
+
+
+def snack_prune_regrow_prepared(plan, row, col, vals, n_drop, seed, step, dropped_lin, grown_lin,
+                                ws, stream=None, ws_bytes=None, dtype=None):
+    dt = _dtype(vals, dtype=dtype)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None and \
+            not isinstance(ws, int) else 0
+    _check(_lib.snack_prune_regrow_prepared(ctypes.byref(plan), _ptr(row), _ptr(col), _ptr(vals),
+                                            dt, n_drop, seed & (2**64 - 1), step & (2**64 - 1),
+                                            _ptr(dropped_lin), _ptr(grown_lin), _ptr(ws),
+                                            ws_bytes, _stream(stream)),
+           "snack_prune_regrow_prepared")
 
 
 def snack_gelu_fwd(z, h, n=None, stream=None):

@@ -7,6 +7,7 @@
 
 #include "../../include/snack.h"
 #include "internal.h"
+#include "prune_common.h"
 
 using namespace snk;
 
@@ -24,10 +25,6 @@ int32_t auto_tile(int64_t items) {
 
 inline hipStream_t to_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-__global__ void k_zero_small(int32_t* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
-}
-
 __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst,
                            int64_t n) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -37,11 +34,12 @@ __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict_
 // Arena slots past the public derived arrays: the carry slots of tiles that
 // end inside a long segment, the radix-sort buffers of the column view, the
 // node-major copy of batch-major activations, and one slot holding the small
-// scratch of prepare (error / split flags, scan and sort temporaries).
+// scratch of prepare (per-block error / split flags, scan and sort
+// temporaries).
 constexpr int SLOT_PRIV = 15;
 
 struct priv_layout {
-  size_t small, tmp, total;
+  size_t errs, rsplit, csplit, tmp, total;
 };
 
 priv_layout priv_of(const snack_plan* p) {
@@ -54,7 +52,9 @@ priv_layout priv_of(const snack_plan* p) {
     o = align_up(o + b, 256);
     return at;
   };
-  L.small = take(64);
+  L.errs = take(4 * (size_t)seg_bounds_blocks(p->nnz));
+  L.rsplit = take(4 * (size_t)tiles_blocks(p->M));
+  L.csplit = take(4 * (size_t)tiles_blocks(p->K));
   L.tmp = take(std::max(radix_tmp_bytes(n), scan_tmp_bytes(std::max<int64_t>(Pm, n))));
   L.total = o;
   return L;
@@ -206,7 +206,9 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
   char* a = (char*)arena;
   const priv_layout L = priv_of(plan);
   char* priv = a + plan->off[SLOT_PRIV];
-  int32_t* small = (int32_t*)(priv + L.small);  // [0] err bits, [1] row split, [2] col split
+  int32_t* errs = (int32_t*)(priv + L.errs);
+  int32_t* rsplit = (int32_t*)(priv + L.rsplit);
+  int32_t* csplit = (int32_t*)(priv + L.csplit);
   void* tmp = priv + L.tmp;
   const int64_t nnz = plan->nnz;
   int32_t* row_ptr = (int32_t*)(a + plan->off[SNACK_ARR_ROW_PTR]);
@@ -214,16 +216,20 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
   int32_t* perm = (int32_t*)(a + plan->off[SNACK_ARR_PERM]);
   int32_t* row_t = (int32_t*)(a + plan->off[SNACK_ARR_ROW_T]);
 
+  int32_t* res_host = host_result_buffer();
+  int32_t* res_dev = host_result_device(res_host);
+  if (!res_host || !res_dev) return SNACK_E_HIP;
+  res_host[0] = res_host[1] = res_host[2] = INT32_MIN;
+
   // Every kernel below is safe on an invalid COO (all writes are clamped);
-  // the error bits are read back once at the end, with the split flags.
-  hipLaunchKernelGGL(k_zero_small, dim3(1), dim3(64), 0, s, small, 16);
+  // the error bits come back once at the end, with the split flags.
   // 1. validation + row offsets, then the row-view tiles
-  if (launch_seg_bounds(row, col, nnz, plan->M, plan->K, row_ptr, small, s) != hipSuccess)
+  if (launch_seg_bounds(row, col, nnz, plan->M, plan->K, row_ptr, errs, s) != hipSuccess)
     return SNACK_E_HIP;
   if (launch_tiles(row_ptr, plan->M, nnz, plan->tile_row, plan->P_row,
                    (int32_t*)(a + plan->off[SNACK_ARR_RPART_SEG]),
                    (int32_t*)(a + plan->off[SNACK_ARR_RPART_NZ]),
-                   (int32_t*)(a + plan->off[SNACK_ARR_RCUT]), small + 1, s) != hipSuccess)
+                   (int32_t*)(a + plan->off[SNACK_ARR_RCUT]), rsplit, s) != hipSuccess)
     return SNACK_E_HIP;
   // 2. column view: stable radix sort of the entry indices by column (the
   //    last pass also gathers row_t = row[perm]), then offsets and tiles
@@ -246,18 +252,17 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
   if (launch_tiles(col_ptr, plan->K, nnz, plan->tile_col, plan->P_col,
                    (int32_t*)(a + plan->off[SNACK_ARR_CPART_SEG]),
                    (int32_t*)(a + plan->off[SNACK_ARR_CPART_NZ]),
-                   (int32_t*)(a + plan->off[SNACK_ARR_CCUT]), small + 2, s) != hipSuccess)
+                   (int32_t*)(a + plan->off[SNACK_ARR_CCUT]), csplit, s) != hipSuccess)
     return SNACK_E_HIP;
-
-  int32_t host_small[3] = {0, 0, 0};
-  if (hipMemcpyAsync(host_small, small, sizeof(host_small), hipMemcpyDeviceToHost, s) !=
-          hipSuccess ||
+  if (launch_prepare_result(errs, seg_bounds_blocks(nnz), rsplit, tiles_blocks(plan->M), csplit,
+                            tiles_blocks(plan->K), res_dev, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return SNACK_E_HIP;
-  if (host_small[0] & 1) return SNACK_E_COO_RANGE;
-  if (host_small[0] & 2) return SNACK_E_COO_ORDER;
-  plan->has_split_row = host_small[1] ? 1 : 0;
-  plan->has_split_col = host_small[2] ? 1 : 0;
+  if (res_host[0] == INT32_MIN) return SNACK_E_HIP;
+  if (res_host[0] & 1) return SNACK_E_COO_RANGE;
+  if (res_host[0] & 2) return SNACK_E_COO_ORDER;
+  plan->has_split_row = res_host[1] ? 1 : 0;
+  plan->has_split_col = res_host[2] ? 1 : 0;
   plan->prepared = 1;
   return SNACK_OK;
 }
@@ -339,6 +344,34 @@ snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dt
   if (!row || !col || !vals || !ws) return SNACK_E_NULL;
   return prune_regrow(row, col, vals, dtype, M, K, nnz, n_drop, seed, step, dropped_lin,
                       grown_lin, ws, ws_bytes, to_stream(stream));
+}
+
+snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* row, int32_t* col,
+                                         void* vals, snack_dtype dtype, int64_t n_drop,
+                                         uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                         int64_t* grown_lin, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  if (!plan) return SNACK_E_NULL;
+  if (!plan->arena || plan->arena_bytes == 0) return SNACK_E_NOT_PREPARED;
+  if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  const int32_t M = plan->M, K = plan->K;
+  const int64_t nnz = plan->nnz;
+  if (n_drop < 0) return SNACK_E_SHAPE;
+  if (n_drop > nnz || n_drop > (int64_t)M * K - nnz) return SNACK_E_COUNT;
+  if (nnz > 0 && (!row || !col || !vals)) return SNACK_E_NULL;
+  hipStream_t s = to_stream(stream);
+  if (n_drop == 0)
+    return snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream);
+  if (!ws) return SNACK_E_NULL;
+  if (ws_bytes < prune_regrow_ws_bytes(M, K, nnz, n_drop)) return SNACK_E_WORKSPACE;
+  if (use_bitmap_plan(M, K, nnz) && prune_bitmap_fused_ok(M, K, nnz))
+    return prune_bitmap_prepared(plan, row, col, vals, dtype, n_drop, seed, step, dropped_lin,
+                                 grown_lin, ws, s);
+  plan->prepared = 0;
+  const snack_status st = prune_regrow(row, col, vals, dtype, M, K, nnz, n_drop, seed, step,
+                                       dropped_lin, grown_lin, ws, ws_bytes, s);
+  if (st != SNACK_OK) return st;
+  return snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream);
 }
 
 snack_status snack_gelu_fwd(const float* z, float* h, int64_t n, void* stream) {

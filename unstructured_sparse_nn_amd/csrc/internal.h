@@ -68,11 +68,20 @@ hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_
                              hipStream_t s);
 
 // ---- prepare (prepare.hip) ----------------------------------------------------
+// Flags are per block (errs: seg_bounds_blocks(nnz) ints, splits:
+// tiles_blocks(S) ints), written by every block; launch_prepare_result ORs
+// them into res[0..2] (pinned host memory).  errs may be NULL (no
+// validation).
+int64_t seg_bounds_blocks(int64_t nnz);
+int64_t tiles_blocks(int32_t S);
 hipError_t launch_seg_bounds(const int32_t* keys, const int32_t* col, int64_t nnz, int32_t S,
-                             int32_t K, int32_t* ptr, int32_t* err, hipStream_t s);
+                             int32_t K, int32_t* ptr, int32_t* errs, hipStream_t s);
 hipError_t launch_tiles(const int32_t* ptr, int32_t S, int64_t nnz, int32_t T, int32_t P,
-                        int32_t* part_seg, int32_t* part_nz, int32_t* cut, int32_t* any_split,
+                        int32_t* part_seg, int32_t* part_nz, int32_t* cut, int32_t* splits,
                         hipStream_t s);
+hipError_t launch_prepare_result(const int32_t* errs, int64_t n_errs, const int32_t* rsplit,
+                                 int64_t n_r, const int32_t* csplit, int64_t n_c, int32_t* res,
+                                 hipStream_t s);
 
 // ---- aux kernels (aux.hip) ------------------------------------------------------
 hipError_t launch_gelu_fwd(const float* z, float* h, int64_t n, hipStream_t s);

@@ -145,18 +145,38 @@ hipError_t exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_
 }
 
 // ============================================================== radix sort
+// LSD radix sort, ceil(bits/8) passes of equal digit width (<= 8 bits: a
+// 12-bit key takes two 6-bit passes).  Per pass: block histograms, a scan of
+// each digit's row over the blocks, and a stable scatter.
 constexpr int RS_THREADS = 256;
 constexpr int RS_ROUNDS = 8;
 constexpr int RS_BLOCK = RS_THREADS * RS_ROUNDS;  // 2048 items per block
 constexpr int RS_WAVES = RS_THREADS / SNK_WAVE;
 
+// Lanes of the wave holding the same digit (dbits ballots), restricted to
+// lanes with `valid` set.
+__device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool valid, int dbits) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    if (b < dbits) {
+      const uint64_t m = __ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? m : ~m;
+    }
+  }
+  return peers;
+}
+
 // Per-block digit histogram, stored digit-major: hist[d * nblk + blk], so that
 // an exclusive scan of hist gives each (digit, block) its stable base offset.
 template <typename KT>
 __global__ __launch_bounds__(RS_THREADS) void k_radix_hist(const KT* __restrict__ keys, int64_t n,
-                                                           int shift, int32_t* __restrict__ hist,
+                                                           int shift, int dbits,
+                                                           int32_t* __restrict__ hist,
                                                            int64_t nblk) {
   __shared__ int32_t h[256];
+  const int nbins = 1 << dbits;
+  const uint32_t dmask = (uint32_t)nbins - 1u;
   h[threadIdx.x] = 0;
   __syncthreads();
   int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
@@ -168,14 +188,16 @@ __global__ __launch_bounds__(RS_THREADS) void k_radix_hist(const KT* __restrict_
   }
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
-    int64_t i = base + r * RS_THREADS + threadIdx.x;
-    wave_hist_add(h, (uint32_t)(key[r] >> shift) & 255u, i < n);
+    const int64_t i = base + r * RS_THREADS + threadIdx.x;
+    const uint32_t d = (uint32_t)(key[r] >> shift) & dmask;
+    const uint64_t peers = digit_peers(d, i < n, dbits);
+    if (i < n && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&h[d], __popcll(peers));
   }
   __syncthreads();
-  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+  if ((int)threadIdx.x < nbins) hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
 }
 
-// hist is digit-major [256][nblk].  Workgroup d turns row d into exclusive
+// hist is digit-major [nbins][nblk].  Workgroup d turns row d into exclusive
 // prefixes over the blocks (in place) and writes the row total to
 // dtotal[d]; the scatter adds the digit's base (sum of smaller digits).
 __global__ __launch_bounds__(RS_THREADS) void k_radix_scan_digits(int32_t* __restrict__ hist,
@@ -195,76 +217,104 @@ __global__ __launch_bounds__(RS_THREADS) void k_radix_scan_digits(int32_t* __res
   if (threadIdx.x == 0) dtotal[blockIdx.x] = carry;
 }
 
-// Stable scatter: all items of a block are loaded up front (one round trip),
-// then ranked in index order, round by round; within a wave, lanes holding
-// the same digit are found with 8 ballots (one per digit bit) and ranked by
-// lane order.  vin == NULL means value = index.  If gsrc != NULL the pass
-// also writes gout[pos] = gsrc[value] (a gather fused into the scatter).
+// Stable scatter.  All items of a block are loaded up front (one round
+// trip) and ranked in LDS: within a wave, lanes holding the same digit are
+// found with ballots and ranked by lane order; per (round, wave, digit)
+// counts are turned into block-local offsets by one walk per digit in index
+// order.  The block's items are then placed in LDS in digit order and
+// written out in coalesced runs.  vin == NULL means value = index.  If
+// gsrc != NULL the pass also writes gout[pos] = gsrc[value] (a gather fused
+// into the scatter).
 template <typename KT>
 __global__ __launch_bounds__(RS_THREADS) void k_radix_scatter(
     const KT* __restrict__ kin, const int32_t* __restrict__ vin, KT* __restrict__ kout,
-    int32_t* __restrict__ vout, int64_t n, int shift, const int32_t* __restrict__ offs,
+    int32_t* __restrict__ vout, int64_t n, int shift, int dbits, const int32_t* __restrict__ offs,
     int64_t nblk, const int32_t* __restrict__ dtotal, const int32_t* __restrict__ gsrc,
     int32_t* __restrict__ gout) {
-  __shared__ int32_t running[256];
-  __shared__ int32_t wcnt[RS_WAVES][256];
+  __shared__ int32_t cnt[RS_ROUNDS][RS_WAVES][256];
+  __shared__ int32_t dstart[256];  // block-local start of each digit
+  __shared__ int32_t gbase[256];   // global position of the block's first item of each digit
+  __shared__ KT skey[RS_BLOCK];
+  __shared__ int32_t sval[RS_BLOCK];
+  __shared__ int32_t sgv[RS_BLOCK];
   __shared__ int32_t lds[RS_WAVES];
   const int t = threadIdx.x;
   const int w = t / SNK_WAVE;
-  int32_t dsum;
-  const int32_t dbase = block_excl_scan_i32<RS_THREADS>(dtotal[t], lds, &dsum);
-  running[t] = dbase + offs[(int64_t)t * nblk + blockIdx.x];
-#pragma unroll
-  for (int i = 0; i < RS_WAVES; ++i) wcnt[i][t] = 0;
+  const int nbins = 1 << dbits;
+  const uint32_t dmask = (uint32_t)nbins - 1u;
   const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+  const int nvalid = (int)std::min<int64_t>(RS_BLOCK, n - base);
   KT key[RS_ROUNDS];
-  int32_t val[RS_ROUNDS];
+  int32_t val[RS_ROUNDS], gv[RS_ROUNDS];
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
     const int64_t i = base + r * RS_THREADS + t;
     key[r] = i < n ? kin[i] : (KT)0;
     val[r] = i < n ? (vin ? vin[i] : (int32_t)i) : 0;
   }
-  int32_t gv[RS_ROUNDS];
   if (gsrc) {
 #pragma unroll
-    for (int r = 0; r < RS_ROUNDS; ++r) {
-      const int64_t i = base + r * RS_THREADS + t;
-      gv[r] = i < n ? gsrc[val[r]] : 0;
+    for (int r = 0; r < RS_ROUNDS; ++r) gv[r] = base + r * RS_THREADS + t < n ? gsrc[val[r]] : 0;
+  }
+  const int32_t dt = t < nbins ? dtotal[t] : 0;
+  const int32_t off = t < nbins ? offs[(int64_t)t * nblk + blockIdx.x] : 0;
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r)
+#pragma unroll
+    for (int j = 0; j < RS_WAVES; ++j) cnt[r][j][t] = 0;
+  __syncthreads();
+  // intra-wave ranks and per (round, wave, digit) counts
+  const uint64_t lt = lanemask_lt();
+  int32_t rank[RS_ROUNDS];
+  uint32_t dig[RS_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    const bool valid = base + r * RS_THREADS + t < n;
+    dig[r] = (uint32_t)(key[r] >> shift) & dmask;
+    const uint64_t peers = digit_peers(dig[r], valid, dbits);
+    rank[r] = __popcll(peers & lt);
+    if (valid && rank[r] == 0) cnt[r][w][dig[r]] = __popcll(peers);
+  }
+  __syncthreads();
+  // per digit: exclusive offsets over (round, wave) in index order
+  int32_t tot_d = 0;
+  if (t < nbins) {
+#pragma unroll
+    for (int r = 0; r < RS_ROUNDS; ++r)
+#pragma unroll
+      for (int j = 0; j < RS_WAVES; ++j) {
+        const int32_t c = cnt[r][j][t];
+        cnt[r][j][t] = tot_d;
+        tot_d += c;
+      }
+  }
+  int32_t sum;
+  const int32_t ds = block_excl_scan_i32<RS_THREADS>(tot_d, lds, &sum);
+  const int32_t db = block_excl_scan_i32<RS_THREADS>(dt, lds, &sum);
+  if (t < nbins) {
+    dstart[t] = ds;
+    gbase[t] = db + off;
+  }
+  __syncthreads();
+  // place the block's items in digit order
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    if (base + r * RS_THREADS + t < n) {
+      const int lp = dstart[dig[r]] + cnt[r][w][dig[r]] + rank[r];
+      skey[lp] = key[r];
+      sval[lp] = val[r];
+      if (gsrc) sgv[lp] = gv[r];
     }
   }
   __syncthreads();
-  const uint64_t lt = lanemask_lt();
-#pragma unroll
-  for (int r = 0; r < RS_ROUNDS; ++r) {
-    const int64_t i = base + r * RS_THREADS + t;
-    const bool valid = i < n;
-    const uint32_t d = (uint32_t)(key[r] >> shift) & 255u;
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      uint64_t m = __ballot((d >> b) & 1u);
-      peers &= ((d >> b) & 1u) ? m : ~m;
-    }
-    const int rank = __popcll(peers & lt);
-    if (valid && rank == 0) wcnt[w][d] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int32_t pos = running[d] + rank;
-      for (int j = 0; j < w; ++j) pos += wcnt[j][d];
-      kout[pos] = key[r];
-      vout[pos] = val[r];
-      if (gsrc) gout[pos] = gv[r];
-    }
-    __syncthreads();
-    int32_t add = 0;
-#pragma unroll
-    for (int j = 0; j < RS_WAVES; ++j) {
-      add += wcnt[j][t];
-      wcnt[j][t] = 0;
-    }
-    running[t] += add;
-    __syncthreads();
+  // coalesced runs out
+  for (int slot = t; slot < nvalid; slot += RS_THREADS) {
+    const KT k = skey[slot];
+    const uint32_t d = (uint32_t)(k >> shift) & dmask;
+    const int64_t pos = (int64_t)gbase[d] + (slot - dstart[d]);
+    kout[pos] = k;
+    vout[pos] = sval[slot];
+    if (gsrc) gout[pos] = sgv[slot];
   }
 }
 
@@ -281,21 +331,22 @@ static hipError_t radix_sort(const KT* keys_in, const int32_t* vals_in, KT* cons
                              int32_t* gout, void* tmp, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int passes = std::max(1, (bits + 7) / 8);
+  const int dbits = std::max(1, (bits + passes - 1) / passes);
   const int64_t nblk = cdiv(n, RS_BLOCK);
   int32_t* hist = (int32_t*)tmp;
   int32_t* dtotal = (int32_t*)((char*)tmp + align_up(sizeof(int32_t) * 256 * (size_t)nblk, 256));
   const KT* kin = keys_in;
   const int32_t* vin = vals_in;
   for (int p = 0; p < passes; ++p) {
-    const int shift = 8 * p;
+    const int shift = dbits * p;
     const int o = (passes - 1 - p) & 1;
     const bool last = p == passes - 1;
     hipLaunchKernelGGL(k_radix_hist<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, kin, n,
-                       shift, hist, nblk);
-    hipLaunchKernelGGL(k_radix_scan_digits, dim3(256), dim3(RS_THREADS), 0, s, hist, nblk,
+                       shift, dbits, hist, nblk);
+    hipLaunchKernelGGL(k_radix_scan_digits, dim3(1u << dbits), dim3(RS_THREADS), 0, s, hist, nblk,
                        dtotal);
     hipLaunchKernelGGL(k_radix_scatter<KT>, dim3((unsigned)nblk), dim3(RS_THREADS), 0, s, kin,
-                       vin, kbuf[o], vbuf[o], n, shift, hist, nblk, dtotal,
+                       vin, kbuf[o], vbuf[o], n, shift, dbits, hist, nblk, dtotal,
                        last ? gsrc : nullptr, last ? gout : nullptr);
     kin = kbuf[o];
     vin = vbuf[o];

@@ -426,7 +426,7 @@ static pr_layout make_layout(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) 
 
 // SNACK_PRUNE_PATH=sort forces the sort plan (tests run both plans on the
 // same inputs).
-static bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz) {
+bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz) {
   const char* e = getenv("SNACK_PRUNE_PATH");
   if (e && e[0] == 's') return false;
   return prune_bitmap_ok(M, K, nnz);

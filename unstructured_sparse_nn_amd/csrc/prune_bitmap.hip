@@ -29,6 +29,7 @@
 #include "common.h"
 #include "internal.h"
 #include "prune_common.h"
+#include "tiles.h"
 
 namespace snk {
 namespace {
@@ -40,7 +41,7 @@ constexpr int HREPL = 64;                 // select-histogram replicas
 constexpr int AREPL = 64;                 // acceptance-count replicas
 constexpr int GAPCAP = 512;               // long zero runs recorded per block
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
-constexpr int WT = 1024;                  // threads (= bitmap words) per write block
+constexpr int WT = 512;                   // threads (= bitmap words) per write block
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int64_t GAP_INLINE = 16;        // zero runs of up to this many words: one thread
 constexpr int64_t STREAM_BOUND = 1ll << 40;
@@ -628,7 +629,8 @@ __global__ __launch_bounds__(1024) void k_bi_bscan(const int4* __restrict__ in,
 }
 
 // New COO (the set bits of (S & ~D) | G in position order), the dropped and
-// grown lists; one thread per bitmap word.  Block 0 reports (error,
+// grown lists, and optionally the new support F and its per-word exclusive
+// prefix counts; one thread per bitmap word.  Block 0 reports (error,
 // positions missing) into pinned host memory; nothing else is written
 // unless both are 0.  Writes are clamped to nnz / n_drop.
 template <typename T>
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
     const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
     int64_t nnz, int64_t n_drop, const bm_state* st, int32_t* __restrict__ result,
-    int32_t* __restrict__ row,
+    uint32_t* __restrict__ Fb, int32_t* __restrict__ pwb, int32_t* __restrict__ row,
     int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
     int64_t* __restrict__ grown_lin) {
   __shared__ int32_t lds[WT / SNK_WAVE];
@@ -670,8 +672,8 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   const int64_t w = (int64_t)blockIdx.x * WT + t;
   const uint32_t S = w < W ? sup[w] : 0u, D = w < W ? dropb[w] : 0u, G = w < W ? grown[w] : 0u;
   const int4 c = word_counts(S, D, G);
-  // a block holds at most 32 * WT = 32768 positions, so two counts share an
-  // int32 (16 bits each) and two block scans serve all four
+  // a block holds at most 32 * WT = 16384 positions, so two counts share an
+  // int32 (15 bits each, no overflow) and two block scans serve all four
   int32_t tot;
   const int32_t fs = block_excl_scan_i32<WT>(c.x | (c.y << 16), lds, &tot);
   const int32_t dg = block_excl_scan_i32<WT>(c.z | (c.w << 16), lds, &tot);
@@ -681,6 +683,10 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   int64_t qg = bo.w + (dg >> 16);
   const int64_t pw = w * 32;
   uint32_t F = (S & ~D) | G;
+  if (Fb && w < W) {  // the new support and its per-word prefix, for a fused prepare
+    Fb[w] = F;
+    pwb[w] = (int32_t)qf;
+  }
   if (F) {
     // row and column of the word's first position; the rest step from it
     int32_t r0, c0;
@@ -727,10 +733,166 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   }
 }
 
+// ====================================================== fused restructure + prepare
+// With K and M multiples of 32, rows of F are word-aligned and the plan's
+// derived arrays of the new COO come straight from F and its per-word
+// prefix counts pw (no sort):
+//   rows     row_ptr[s] = pw[s * K/32] (nnz at s = M); the row tiles follow;
+//   columns  FT = F transposed in 32 x 32 bit tiles (32 ballots per wave give
+//            the 32 column words of two tiles); compacting FT in
+//            column-major order lists the entries column by column, rows
+//            ascending: row_t, col_ptr, and perm = each entry's rank in F,
+//            i.e. its row-major index.
+struct fuse_ptrs {
+  int32_t *row_ptr, *rpart_seg, *rpart_nz, *rcut;
+  int32_t *col_ptr, *perm, *row_t, *cpart_seg, *cpart_nz, *ccut;
+  int32_t T_row, P_row, T_col, P_col;
+};
+
+__device__ __forceinline__ bool bm_failed(const bm_state* st) {
+  return st->err != 0 || st->rem_final > 0;
+}
+
+constexpr int FP_THREADS = 256;
+
+// Blocks [0, rb): row offsets and row tiles, thread per row s in [0, M].
+// Blocks [rb, ..): bit transpose, two 32 x 32 tiles per wave.
+__global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
+    const bm_state* st, const uint32_t* __restrict__ Fb, const int32_t* __restrict__ pwb,
+    int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ rsplit,
+    uint32_t* __restrict__ FT) {
+  if (bm_failed(st)) return;
+  const int64_t KW = K >> 5, WM = M >> 5;
+  if ((int)blockIdx.x < rb) {
+    const int64_t s = (int64_t)blockIdx.x * FP_THREADS + threadIdx.x;
+    bool any = false;
+    if (s < M) {
+      const int64_t a = pwb[s * KW];
+      const int64_t b = s + 1 < M ? (int64_t)pwb[(s + 1) * KW] : nnz;
+      f.row_ptr[s] = (int32_t)a;
+      any = tile_cuts(s, a, b, nnz, f.T_row, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
+    } else if (s == M) {
+      f.row_ptr[M] = (int32_t)nnz;
+      tile_close(M, nnz, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
+    }
+    const int any_b = __syncthreads_or(any ? 1 : 0);
+    if (threadIdx.x == 0) rsplit[blockIdx.x] = any_b ? 1 : 0;
+    return;
+  }
+  const int64_t tile = ((int64_t)(blockIdx.x - rb) * FP_THREADS + threadIdx.x) >> 5;
+  const int l = threadIdx.x & 31;
+  const bool ok = tile < WM * KW;
+  const int64_t rw = ok ? tile / KW : 0, wc = ok ? tile % KW : 0;
+  const uint32_t word = ok ? Fb[(rw * 32 + l) * KW + wc] : 0u;
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint64_t m = __ballot((word >> j) & 1u);  // bit i: row i of the lane's tile
+    if (l == j) out = (threadIdx.x & 32) ? (uint32_t)(m >> 32) : (uint32_t)m;
+  }
+  if (ok) FT[(wc * 32 + l) * WM + rw] = out;
+}
+
+// Per block of WT words of FT: popcount sums.
+__global__ __launch_bounds__(WT) void k_fp_tsum(const bm_state* st,
+                                                const uint32_t* __restrict__ FT, int64_t NT,
+                                                int4* __restrict__ tsum) {
+  __shared__ int32_t lds[WT / SNK_WAVE];
+  if (bm_failed(st)) return;
+  const int64_t i = (int64_t)blockIdx.x * WT + threadIdx.x;
+  int32_t c = i < NT ? __popc(FT[i]) : 0;
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, SNK_WAVE);
+  if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t tot = 0;
+    for (int k = 0; k < WT / SNK_WAVE; ++k) tot += lds[k];
+    tsum[blockIdx.x] = make_int4(tot, 0, 0, 0);
+  }
+}
+
+// Column view: one thread per FT word (column c, rows 32rw ..); rank of its
+// first entry = block base + block scan.
+__global__ __launch_bounds__(WT) void k_fp_temit(
+    const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int32_t M, int32_t K,
+    const int4* __restrict__ tsum, const int4* __restrict__ toff,
+    const uint32_t* __restrict__ Fb, const int32_t* __restrict__ pwb, int64_t nnz, fuse_ptrs f) {
+  __shared__ int32_t lds[WT / SNK_WAVE];
+  __shared__ int32_t red[WT / SNK_WAVE];
+  if (bm_failed(st)) return;
+  const int t = threadIdx.x;
+  int64_t base;
+  if (toff) {
+    base = toff[blockIdx.x].x;
+  } else {
+    int32_t sacc = 0;
+    for (int64_t i = t; i < (int64_t)blockIdx.x; i += WT) sacc += tsum[i].x;
+    for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off, SNK_WAVE);
+    if (lane_id() == 0) red[t / SNK_WAVE] = sacc;
+    __syncthreads();
+    base = 0;
+    for (int k = 0; k < WT / SNK_WAVE; ++k) base += red[k];
+  }
+  const int64_t KW = K >> 5, WM = M >> 5;
+  const int64_t i = (int64_t)blockIdx.x * WT + t;
+  uint32_t word = i < NT ? FT[i] : 0u;
+  int32_t tot;
+  int64_t q = base + block_excl_scan_i32<WT>(__popc(word), lds, &tot);
+  if (i >= NT) return;
+  const int64_t c = i / WM, rw = i - c * WM;
+  if (rw == 0) f.col_ptr[c] = (int32_t)q;
+  if (i == NT - 1) f.col_ptr[K] = (int32_t)nnz;
+  while (word) {
+    const int j = __ffs(word) - 1;
+    word &= word - 1;
+    if (q < nnz) {
+      const int64_t r = rw * 32 + j;
+      const int64_t pwi = r * KW + (c >> 5);
+      f.row_t[q] = (int32_t)r;
+      f.perm[q] = pwb[pwi] + __popc(Fb[pwi] & ((1u << (c & 31)) - 1u));
+    }
+    ++q;
+  }
+}
+
+// Column tiles, thread per column s in [0, K].
+__global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int32_t K,
+                                                        int64_t nnz, fuse_ptrs f,
+                                                        int32_t* __restrict__ csplit) {
+  if (bm_failed(st)) return;
+  const int64_t s = (int64_t)blockIdx.x * FP_THREADS + threadIdx.x;
+  bool any = false;
+  if (s < K) any = tile_cuts(s, f.col_ptr[s], f.col_ptr[s + 1], nnz, f.T_col, f.P_col,
+                             f.cpart_seg, f.cpart_nz, f.ccut);
+  else if (s == K) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
+  const int any_b = __syncthreads_or(any ? 1 : 0);
+  if (threadIdx.x == 0) csplit[blockIdx.x] = any_b ? 1 : 0;
+}
+
+// One workgroup: the split flags of both views into pinned host memory
+// (res[2], res[3]).
+__global__ __launch_bounds__(1024) void k_fp_result(const bm_state* st,
+                                                    const int32_t* __restrict__ rsplit,
+                                                    int64_t n_r, const int32_t* __restrict__ csplit,
+                                                    int64_t n_c, int32_t* __restrict__ res) {
+  int32_t r = 0, c = 0;
+  if (!bm_failed(st)) {
+    for (int64_t i = threadIdx.x; i < n_r; i += 1024) r |= rsplit[i];
+    for (int64_t i = threadIdx.x; i < n_c; i += 1024) c |= csplit[i];
+  }
+  r = __syncthreads_or(r);
+  c = __syncthreads_or(c);
+  if (threadIdx.x == 0) {
+    res[2] = r ? 1 : 0;
+    res[3] = c ? 1 : 0;
+  }
+}
+
 // ------------------------------------------------------------------ host
 struct bm_layout {
-  int64_t nblk, W, nb;
-  size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff, total;
+  int64_t nblk, W, nb, NT, nbt, rb, cbk;
+  size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
+  size_t fb, pwb, ft, tsum, toff, rsplit, csplit, total;  // fused prepare
 };
 
 bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
@@ -753,6 +915,17 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
   L.vals = take(4 * (size_t)std::max<int64_t>(nnz, 1));
   L.bsum = take(16 * (size_t)L.nb);
   L.boff = take(16 * (size_t)L.nb);
+  L.NT = (int64_t)K * cdiv(M, 32);
+  L.nbt = std::max<int64_t>(1, cdiv(L.NT, WT));
+  L.rb = cdiv((int64_t)M + 1, FP_THREADS);
+  L.cbk = cdiv((int64_t)K + 1, FP_THREADS);
+  L.fb = take(4 * (size_t)L.W);
+  L.pwb = take(4 * (size_t)L.W);
+  L.ft = take(4 * (size_t)L.NT);
+  L.tsum = take(16 * (size_t)L.nbt);
+  L.toff = take(16 * (size_t)L.nbt);
+  L.rsplit = take(4 * (size_t)L.rb);
+  L.csplit = take(4 * (size_t)L.cbk);
   L.total = o;
   return L;
 }
@@ -773,10 +946,13 @@ int32_t grid_chunks(int64_t MK, int64_t nnz, int64_t n_drop, int32_t riding) {
   return c;
 }
 
+// One restructuring step; with `fuse` non-NULL the plan arrays of the new
+// COO are built as well and *splits receives the two split flags.
 template <typename T>
 snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int64_t nnz,
                  int64_t n_drop, uint64_t seed, uint64_t step, int64_t* dropped_lin,
-                 int64_t* grown_lin, char* ws, hipStream_t s) {
+                 int64_t* grown_lin, char* ws, hipStream_t s, const fuse_ptrs* fuse,
+                 int32_t* splits) {
   const bm_layout L = make_layout(M, K, nnz);
   bm_state* st = (bm_state*)(ws + L.state);
   int32_t* cnt_eq = (int32_t*)(ws + L.cnt_eq);
@@ -795,7 +971,9 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   int32_t* res_host = host_result_buffer();
   int32_t* res_dev = host_result_device(res_host);
   if (!res_host || !res_dev) return SNACK_E_HIP;
-  res_host[0] = res_host[1] = INT32_MIN;
+  res_host[0] = res_host[1] = res_host[2] = res_host[3] = INT32_MIN;
+  uint32_t* Fb = fuse ? (uint32_t*)(ws + L.fb) : nullptr;
+  int32_t* pwb = fuse ? (int32_t*)(ws + L.pwb) : nullptr;
 
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(4 * HREPL * 256, 256)), dim3(256), 0, s, st);
   const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
@@ -829,8 +1007,28 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
   hipLaunchKernelGGL(k_bi_emit<T>, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
                      bsum, own_base ? nullptr : boff, vals_ws, K,
-                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, row, col, vals,
-                     dropped_lin, grown_lin);
+                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, Fb, pwb, row,
+                     col, vals, dropped_lin, grown_lin);
+  if (fuse) {
+    uint32_t* FT = (uint32_t*)(ws + L.ft);
+    int4* tsum = (int4*)(ws + L.tsum);
+    int4* toff = (int4*)(ws + L.toff);
+    int32_t* rsplit = (int32_t*)(ws + L.rsplit);
+    int32_t* csplit = (int32_t*)(ws + L.csplit);
+    const int64_t tiles = (int64_t)(M / 32) * (K / 32);
+    const int64_t tb = cdiv(tiles * 32, FP_THREADS);
+    hipLaunchKernelGGL(k_fp_rows_transpose, dim3((unsigned)(L.rb + tb)), dim3(FP_THREADS), 0, s,
+                       st, Fb, pwb, M, K, nnz, *fuse, (int32_t)L.rb, rsplit, FT);
+    hipLaunchKernelGGL(k_fp_tsum, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, tsum);
+    const bool own_t = L.nbt <= PREFIX_INBLOCK_MAX;
+    if (!own_t) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, tsum, toff, L.nbt);
+    hipLaunchKernelGGL(k_fp_temit, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, M, K,
+                       tsum, own_t ? nullptr : toff, Fb, pwb, nnz, *fuse);
+    hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
+                       *fuse, csplit);
+    hipLaunchKernelGGL(k_fp_result, dim3(1), dim3(1024), 0, s, st, rsplit, L.rb, csplit, L.cbk,
+                       res_dev);
+  }
   if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
     return SNACK_E_HIP;
   const int32_t err = res_host[0], missing = res_host[1];
@@ -839,6 +1037,11 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (err & 2) return SNACK_E_COO_RANGE;
   if (err & 4) return SNACK_E_COO_ORDER;
   if ((err & 8) || missing > 0) return SNACK_E_COUNT;
+  if (fuse) {
+    if (res_host[2] == INT32_MIN || res_host[3] == INT32_MIN) return SNACK_E_HIP;
+    splits[0] = res_host[2];
+    splits[1] = res_host[3];
+  }
   return SNACK_OK;
 }
 
@@ -860,9 +1063,40 @@ snack_status prune_bitmap(int32_t* row, int32_t* col, void* vals, snack_dtype dt
                           int64_t* dropped_lin, int64_t* grown_lin, void* ws, hipStream_t s) {
   if (dt == SNACK_F32)
     return run<float>(row, col, (float*)vals, M, K, nnz, n_drop, seed, step, dropped_lin,
-                      grown_lin, (char*)ws, s);
+                      grown_lin, (char*)ws, s, nullptr, nullptr);
   return run<bf16>(row, col, (bf16*)vals, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
-                   (char*)ws, s);
+                   (char*)ws, s, nullptr, nullptr);
+}
+
+bool prune_bitmap_fused_ok(int32_t M, int32_t K, int64_t nnz) {
+  return prune_bitmap_ok(M, K, nnz) && M % 32 == 0 && K % 32 == 0;
+}
+
+snack_status prune_bitmap_prepared(snack_plan* plan, int32_t* row, int32_t* col, void* vals,
+                                   snack_dtype dt, int64_t n_drop, uint64_t seed, uint64_t step,
+                                   int64_t* dropped_lin, int64_t* grown_lin, void* ws,
+                                   hipStream_t s) {
+  char* a = (char*)plan->arena;
+  auto arr = [&](int which) { return (int32_t*)(a + plan->off[which]); };
+  fuse_ptrs f{arr(SNACK_ARR_ROW_PTR), arr(SNACK_ARR_RPART_SEG), arr(SNACK_ARR_RPART_NZ),
+              arr(SNACK_ARR_RCUT), arr(SNACK_ARR_COL_PTR), arr(SNACK_ARR_PERM),
+              arr(SNACK_ARR_ROW_T), arr(SNACK_ARR_CPART_SEG), arr(SNACK_ARR_CPART_NZ),
+              arr(SNACK_ARR_CCUT), plan->tile_row, plan->P_row, plan->tile_col, plan->P_col};
+  int32_t splits[2] = {0, 0};
+  plan->prepared = 0;
+  const snack_status st =
+      dt == SNACK_F32
+          ? run<float>(row, col, (float*)vals, plan->M, plan->K, plan->nnz, n_drop, seed, step,
+                       dropped_lin, grown_lin, (char*)ws, s, &f, splits)
+          : run<bf16>(row, col, (bf16*)vals, plan->M, plan->K, plan->nnz, n_drop, seed, step,
+                      dropped_lin, grown_lin, (char*)ws, s, &f, splits);
+  if (st != SNACK_OK) return st;
+  plan->row = row;
+  plan->col = col;
+  plan->has_split_row = splits[0];
+  plan->has_split_col = splits[1];
+  plan->prepared = 1;
+  return SNACK_OK;
 }
 
 }  // namespace snk

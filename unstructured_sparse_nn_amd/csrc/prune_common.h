@@ -41,11 +41,23 @@ __device__ __forceinline__ bool is_nan_mag(uint32_t a) {
   return sizeof(T) == 2 ? (a > 0x7F80u) : (a > 0x7F800000u);
 }
 
+// ---- plan choice (prune.hip) ----------------------------------------------------
+// The bitmap plan when it applies, unless SNACK_PRUNE_PATH=sort.
+bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz);
+
 // ---- bitmap plan (prune_bitmap.hip) -------------------------------------------
 bool prune_bitmap_ok(int32_t M, int32_t K, int64_t nnz);
 size_t prune_bitmap_ws_bytes(int32_t M, int32_t K, int64_t nnz);
 snack_status prune_bitmap(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
                           int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
                           int64_t* dropped_lin, int64_t* grown_lin, void* ws, hipStream_t s);
+// The bitmap plan followed by the plan's derived arrays built from the new
+// support bitmap (needs M, K multiples of 32).  plan: initialised for
+// (M, K, nnz) with its arena; it describes the new COO on success.
+bool prune_bitmap_fused_ok(int32_t M, int32_t K, int64_t nnz);
+snack_status prune_bitmap_prepared(snack_plan* plan, int32_t* row, int32_t* col, void* vals,
+                                   snack_dtype dt, int64_t n_drop, uint64_t seed, uint64_t step,
+                                   int64_t* dropped_lin, int64_t* grown_lin, void* ws,
+                                   hipStream_t s);
 
 }  // namespace snk

@@ -32,6 +32,16 @@ class Topology:
         self.arena = torch.empty(self.plan.arena_bytes, dtype=torch.uint8, device=self.row.device)
         B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
 
+    def restructure(self, vals, n_drop: int, seed: int, step: int, dropped=None, grown=None,
+                    ws=None, stream=None):
+        """One prune/regrow step on (row, col, vals) in place, re-preparing this
+        plan in the same call (snack_prune_regrow_prepared)."""
+        if ws is None:
+            ws = torch.empty(B.snack_prune_regrow_workspace(self.M, self.K, self.nnz, n_drop),
+                             dtype=torch.uint8, device=self.row.device)
+        B.snack_prune_regrow_prepared(self.plan, self.row, self.col, vals, n_drop, seed, step,
+                                      dropped, grown, ws, stream)
+
     def array(self, name: str) -> torch.Tensor:
         """A derived array of the plan as an int32 view into the arena."""
         _, n = B.snack_plan_array(self.plan, name)
@@ -97,11 +107,7 @@ class SparseLinear(torch.nn.Module):
     def prune_regrow(self, frac_ppm: int, step: int):
         t = self.topo
         n_drop = B.snack_drop_count(t.nnz, frac_ppm)
-        ws = torch.empty(B.snack_prune_regrow_workspace(t.M, t.K, t.nnz, n_drop),
-                         dtype=torch.uint8, device=t.row.device)
         dropped = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
         grown = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
-        B.snack_prune_regrow(t.row, t.col, self.vals.data, t.M, t.K, t.nnz, n_drop, self.seed,
-                             step, dropped, grown, ws)
-        t.prepare()
+        t.restructure(self.vals.data, n_drop, self.seed, step, dropped, grown)
         return dropped[:n_drop], grown[:n_drop]
