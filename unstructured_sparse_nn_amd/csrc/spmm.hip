@@ -41,6 +41,7 @@ constexpr int MP_MAX_THREADS = 256;
 constexpr int MP_RC = 8;        // entries a group gathers at once (one round of its run)
 constexpr int MP_MAX_BW = 32;   // batch columns per workgroup (CH * G)
 constexpr int MP_SU = 8;        // staged items per thread per staging round
+constexpr int NUM_XCD = 8;      // accelerator complex dies of an MI355X (workgroups go round-robin)
 
 // Merge-path point of local diagonal d inside a tile: the number x of
 // segment ends consumed (end x' is consumed before entry j iff end[x'] <= j).
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     const int32_t* __restrict__ perm, const T* __restrict__ vals,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
     const T* __restrict__ Xt, T* __restrict__ Y, float* __restrict__ carry, int32_t S,
-    int32_t B, int32_t P, int32_t g_log2, int32_t tile_items) {
+    int32_t B, int32_t P, int32_t g_log2, int32_t tile_items, int32_t xcd_tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int threads = blockDim.x;
   const int G = 1 << g_log2;
@@ -181,7 +182,13 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   const int gl = tid & (G - 1);
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int p = blockIdx.x;
+  // xcd_tiles > 0: workgroup b (dispatched to XCD b % 8) takes tile
+  // (b % 8) * xcd_tiles + b / 8, so each XCD works on one contiguous range
+  // of tiles and its L2 sees a narrower slice of what the tiles gather
+  const int p = xcd_tiles > 0
+                    ? (int)(blockIdx.x % NUM_XCD) * xcd_tiles + (int)(blockIdx.x / NUM_XCD)
+                    : (int)blockIdx.x;
+  if (p >= P) return;
   const int32_t b0 = (int32_t)blockIdx.y * (G * CH) + gl * CH;
   const bool bvalid = b0 < B;
 
@@ -633,14 +640,24 @@ hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_
   return transpose2<bf16>(in0, out0, R0, C0, in1, out1, R1, C1, s);
 }
 
+// The column view reads its values through perm: with XCD-contiguous tile
+// ranges, a line of the value array (consecutive entries of a row, spread
+// over neighbouring columns) is fetched by few XCDs instead of all of them.
+static int32_t xcd_tiles_for(const seg_view& v) {
+  static const bool off = getenv("SNACK_NO_XCD_REMAP") != nullptr;
+  if (off || !v.perm || v.P < 8 * NUM_XCD) return 0;
+  return (int32_t)cdiv(v.P, NUM_XCD);
+}
+
 template <typename T, int CH, bool NODE_OUT, bool PERM>
 static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
                      float* carry, const lane_shape& sh, hipStream_t s) {
-  dim3 grid((unsigned)v.P, (unsigned)cdiv(B, sh.bw));
+  const int32_t xt = xcd_tiles_for(v);
+  dim3 grid((unsigned)(xt ? xt * NUM_XCD : v.P), (unsigned)cdiv(B, sh.bw));
   size_t lds = tile_lds_bytes(v.tile, sh.threads, sh.g_log2, CH);
   hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, PERM>), grid, dim3(sh.threads), lds, s, v.ptr,
                      v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)Xt, (T*)Y,
-                     carry, v.S, B, v.P, sh.g_log2, v.tile);
+                     carry, v.S, B, v.P, sh.g_log2, v.tile, xt);
   if (v.has_split) {
     int64_t n = (int64_t)v.P * B;
     hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
