@@ -207,6 +207,51 @@ def read_traffic(name, launches_bytes):
         return None
 
 
+def dense_baselines(wt, X, batches, rotate=8):
+    """Forward time of the in-repo dense and Dense+Mask kernels (snack_dense_fwd)
+    on the same layer, graph-timed like the sparse products, cold (rotating
+    over `rotate` copies of the dense weight and mask)."""
+    import torch
+    import unstructured_sparse_nn_amd as snk
+    M, K = wt.M, wt.K
+    dense = np.zeros(M * K, dtype=np.uint16)
+    dense[wt.row.astype(np.int64) * K + wt.col] = wt.vals
+    mask = np.zeros(M * K, dtype=np.uint8)
+    mask[wt.row.astype(np.int64) * K + wt.col] = 1
+    Wd = [torch.from_numpy(dense.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(rotate)]
+    Md = [torch.from_numpy(mask).cuda() for _ in range(rotate)]
+    out = {}
+    for B in batches:
+        xb = torch.from_numpy(X.data[:B * K].view(np.int16)).view(torch.bfloat16).cuda()
+        Y = torch.empty(B * M, dtype=torch.bfloat16, device="cuda")
+        for kind, use_mask in (("dense", False), ("dense_mask", True)):
+            def fn(i):
+                snk.snack_dense_fwd(Wd[i % rotate], Md[i % rotate] if use_mask else None, M, K,
+                                    xb, B, Y)
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(16):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 48
+            nbytes = M * K * 2 + (M * K if use_mask else 0) + B * (K + M) * 2
+            out[f"{kind}_B{B}"] = {"us": round(us, 2), "bytes": nbytes,
+                                   "GBps": round(nbytes / us / 1e3, 1)}
+    del Wd, Md
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, X, dY, B, drop_ppm, seconds):
     """The fp64 oracle, serial on one host core, running the same step on the
     same layer, repeated until `seconds` of CPU work."""
@@ -400,6 +445,20 @@ def run_bench(args):
            "products_only_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1)}
     if args.grid:
         rec["grid"] = time_ops_grid(N, (0.95, 0.99), (1, 8, 32), R)
+        log("dense baselines")
+        base = dense_baselines(wt, w.X[0], (1, B))
+        for b in (1, B):  # the sparse forward, graph-timed the same way
+            wb = synth.inference_layer(N=N, sparsity=sp, B=b)
+            ib = [Instance(wb.weights[0], wb.X[0], wb.dY[0], b, True, 0, args.layout)
+                  for _ in range(8)]
+            us = graph_kernel_us(ib, "fwd", launches=16, replays=3)
+            base[f"sparse_fwd_B{b}"] = {"us": round(us, 2)}
+            base[f"dense_mask_B{b}"]["sparse_fwd_speedup"] = round(
+                base[f"dense_mask_B{b}"]["us"] / us, 2)
+            base[f"dense_B{b}"]["sparse_fwd_speedup"] = round(base[f"dense_B{b}"]["us"] / us, 2)
+            del ib
+            torch.cuda.empty_cache()
+        rec["baselines"] = base
     if args.cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(wt, w.X[0], w.dY[0], B, args.drop_ppm,
