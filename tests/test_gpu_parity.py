@@ -482,22 +482,25 @@ def test_gelu_matches_oracle(orc):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("masked", [False, True])
-def test_dense_baseline(orc, dt, masked):
-    w = synth.random_case(6, 300, 1000, 30000, 5, dt)
+@pytest.mark.parametrize("Bsz,K", [(1, 1000), (5, 1000), (32, 1024), (40, 997)])
+def test_dense_baseline(orc, dt, masked, Bsz, K):
+    """Dense and Dense+Mask reference kernels against a numpy product, on
+    every batch-tile path, aligned and ragged K."""
+    w = synth.random_case(6, 300, K, 30000, Bsz, dt)
     wt = w.weights[0]
     rng = np.random.default_rng(1)
-    Wd = (rng.standard_normal(300 * 1000) * 0.02).astype(np.float32)
+    Wd = (rng.standard_normal(300 * K) * 0.02).astype(np.float32)
     if dt == "bf16":
         Wd = synth.f32_to_bf16_bits(Wd)
-    mask = np.zeros(300 * 1000, np.uint8)
-    mask[wt.row.astype(np.int64) * 1000 + wt.col] = 1
-    Y = torch.empty(5 * 300, dtype=torch_dtype(dt), device="cuda")
-    snk.snack_dense_fwd(to_dev(Wd, dt), to_dev(mask) if masked else None, 300, 1000,
-                        to_dev(w.X[0].data, dt), 5, Y)
+    mask = np.zeros(300 * K, np.uint8)
+    mask[wt.row.astype(np.int64) * K + wt.col] = 1
+    Y = torch.empty(Bsz * 300, dtype=torch_dtype(dt), device="cuda")
+    snk.snack_dense_fwd(to_dev(Wd, dt), to_dev(mask) if masked else None, 300, K,
+                        to_dev(w.X[0].data, dt), Bsz, Y)
     Wf = (synth.bf16_bits_to_f32(Wd) if dt == "bf16" else Wd).astype(np.float64)
     Wf = Wf * (mask if masked else 1)
-    Xb = w.X[0].f64().reshape(5, 1000)
-    Wm = Wf.reshape(300, 1000)
+    Xb = w.X[0].f64().reshape(Bsz, K)
+    Wm = Wf.reshape(300, K)
     assert_within(from_dev(Y, dt), Xb @ Wm.T, np.abs(Xb) @ np.abs(Wm).T, dt, "dense")
 
 
