@@ -132,6 +132,12 @@ class Instance:
         t.grad_vals(self.dY, self.X, self.B, self.lay, out=self.dV)
         if ev: ev[3].record()
 
+    def bwd_fused(self, lr=0.0):
+        """dX and dV in one pass (snack_spmm_bwd_fused), no value update."""
+        import unstructured_sparse_nn_amd as snk
+        snk.snack_spmm_bwd_fused(self.topo.plan, self.vals, self.X, self.dY, self.lay, self.B,
+                                 self.dX, self.dV, lr)
+
     def restructure(self, ev=None, fused=True):
         import unstructured_sparse_nn_amd as snk
         self.step_no += 1
@@ -161,7 +167,8 @@ def graph_kernel_us(insts, op, launches=20, replays=5):
                                                               out=insts[i % R].dX),
            "sddmm": lambda i: insts[i % R].topo.grad_vals(insts[i % R].dY, insts[i % R].X,
                                                           insts[i % R].B, insts[i % R].lay,
-                                                          out=insts[i % R].dV)}
+                                                          out=insts[i % R].dV),
+           "bwd_fused": lambda i: insts[i % R].bwd_fused()}
     fn = fns[op]
     for i in range(3):
         fn(i)
@@ -415,6 +422,11 @@ def run_bench(args):
     for op in ("fwd", "bwd_input", "sddmm"):
         ops[op]["us_kernel"] = round(graph_kernel_us(insts, op), 2)
         ops[op]["GBps_kernel"] = round(ops[op]["algo_bytes"] / (ops[op]["us_kernel"] * 1e3), 1)
+    # the alternative backward: dX and dV in one pass (snack_spmm_bwd_fused)
+    fb = ops["bwd_input"]["algo_bytes"] + ops["sddmm"]["algo_bytes"]
+    fus = round(graph_kernel_us(insts, "bwd_fused"), 2)
+    ops["bwd_fused"] = {"us_kernel": fus, "algo_bytes": fb, "GBps_kernel": round(fb / (fus * 1e3), 1),
+                        "note": "dX + dV in one call; not part of the timed step"}
     dom = max(("fwd", "bwd_input", "sddmm"), key=lambda o: ops[o]["us_kernel"])
     kname = {"fwd": "k_seg_spmm (row view)", "bwd_input": "k_seg_spmm (column view)",
              "sddmm": "k_sddmm"}[dom]

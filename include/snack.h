@@ -202,6 +202,27 @@ SNACK_API snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void*
                                    void* dvals, void* stream);
 
 /*
+ * snack_spmm_bwd_fused -- the whole backward of the layer in one pass over
+ * the column view, for batches of at most 32:
+ *   dX = dY W                        (as snack_spmm_bwd_input),
+ *   dvals[k] = sum_b dY[b,row_k] X[b,col_k]   (as snack_sddmm_grad_vals;
+ *                                     dvals may be NULL),
+ *   if lr != 0: vals[k] <- vals[k] - lr * dV_k   (plain SGD, in place; dV_k
+ *                                     is the fp32 sum before rounding, the
+ *                                     result is rounded to the value dtype).
+ * Each entry's dY row is gathered once for both products; its X chunk is
+ * read at its own column.  dX uses the values before the update.  This
+ * follows the SNACK abstract's wish to keep backpropagation in the sparse
+ * paradigm; fusing it with the optimiser is this library's.
+ * X, dY: activations of the forward (B x K / B x M, or node-major); dX as
+ * for snack_spmm_bwd_input.  Errors: as for the products, SNACK_E_SHAPE for
+ * B > 32, SNACK_E_NAN for a NaN or infinite lr.
+ */
+SNACK_API snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, snack_dtype dtype,
+                                  const void* X, const void* dY, snack_layout layout, int32_t B,
+                                  void* dX, void* dvals, float lr, void* stream);
+
+/*
  * snack_drop_count -- number of connections one restructuring step
  * replaces: round half up of nnz * frac_ppm / 10^6 (frac in parts per
  * million).  Returns -1 for negative arguments.

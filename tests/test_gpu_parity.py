@@ -466,6 +466,71 @@ def test_prune_regrow_prepared_rejects_unprepared_plan():
     assert e.value.status == -12
 
 
+FUSED_BWD = [
+    # name, dtype, layout, batch, tile, lr
+    ("single", "f32", "batch", 4, 0, 0.0),
+    ("single", "f32", "batch", 4, 0, 0.05),
+    ("square_0.95_32", "bf16", "batch", 32, 0, 0.0),
+    ("square_0.95_1", "bf16", "batch", 1, 0, 0.01),
+    ("square_0.99_8", "bf16", "batch", 8, 0, 0.01),
+    ("ragged", "f32", "node", 5, 64, 0.1),    # small tiles: split columns and the fix-up
+    ("ragged", "bf16", "batch", 3, 64, 0.1),
+    ("ragged", "bf16", "node", 32, 0, 0.2),
+    ("skewed", "f32", "batch", 16, 64, 0.1),   # one dense column spanning many tiles
+]
+
+
+@pytest.mark.parametrize("name,dt,layout,Bsz,tile,lr", FUSED_BWD)
+def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
+    """One pass gives the input gradient and the value gradient of the
+    separate products, and the SGD step of their definition."""
+    if name == "ragged":
+        w = synth.random_case(15, 300, 200, 9000, Bsz, dt, layout)
+    elif name == "skewed":
+        lin = np.concatenate([np.arange(64) * 40 + 7, np.arange(3000) + 64 * 40])
+        lin = np.unique(lin[lin < 80 * 40])
+        w = synth.random_case(16, 80, 40, lin.size, Bsz, dt, layout, positions=lin)
+    else:
+        w = workload(name)
+    wt, X, dY = w.weights[0], w.X[0], w.dY[0]
+    nm = layout == "node"
+    topo = topology(wt, Bsz, tile)
+    vals = to_dev(wt.vals, dt)
+    dX = torch.empty(Bsz * wt.K, dtype=torch_dtype(dt), device="cuda")
+    dV = torch.empty(wt.nnz, dtype=torch_dtype(dt), device="cuda")
+    snk.snack_spmm_bwd_fused(topo.plan, vals, to_dev(X.data, dt), to_dev(dY.data, dt),
+                             B.NODE_MAJOR if nm else B.BATCH_MAJOR, Bsz, dX, dV, lr)
+    v64 = wt.vals_f64()
+    ref, S = orc.spmm_bwd_input(wt.M, wt.K, wt.row, wt.col, v64, Bsz, dY.f64(), nm)
+    assert_within(from_dev(dX, dt), ref, S, dt, "fused dX")
+    refv, Sv = orc.sddmm(wt.M, wt.K, wt.row, wt.col, Bsz, dY.f64(), X.f64(), nm)
+    assert_within(from_dev(dV, dt), refv, Sv, dt, "fused dV")
+    new = from_dev(vals, dt)
+    if lr == 0.0:
+        assert np.array_equal(new, v64)
+    else:
+        exp = v64 - lr * refv
+        ulp = 2.0 ** (-8 if dt == "bf16" else -23)
+        tol = 1e-2 if dt == "bf16" else 1e-5
+        assert np.all(np.abs(new - exp) <= lr * tol * Sv + ulp * np.abs(exp) + 1e-30)
+
+
+def test_bwd_fused_rejects_wide_batch_and_bad_lr():
+    w = synth.random_case(17, 64, 48, 500, 33, "f32")
+    wt = w.weights[0]
+    topo = topology(wt, 33)
+    vals = to_dev(wt.vals, "f32")
+    X, dY = to_dev(w.X[0].data, "f32"), to_dev(w.dY[0].data, "f32")
+    dX = torch.empty(33 * 48, device="cuda")
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_spmm_bwd_fused(topo.plan, vals, X, dY, B.BATCH_MAJOR, 33, dX, None, 0.1)
+    assert e.value.status == -2
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_spmm_bwd_fused(topo.plan, vals, X, dY, B.BATCH_MAJOR, 8, dX, None,
+                                 float("nan"))
+    assert e.value.status == -7
+
+
 # --------------------------------------------------------------- aux
 def test_gelu_matches_oracle(orc):
     z = torch.linspace(-8, 8, 100003, device="cuda")

@@ -11,5 +11,6 @@ from .binding import (BATCH_MAJOR, BF16, F32, NODE_MAJOR, SnackError, SnackPlan,
                       snack_gelu_fwd, snack_plan_array, snack_plan_init, snack_plan_sizeof,
                       snack_prune_regrow, snack_prune_regrow_prepared,
                       snack_prune_regrow_workspace, snack_sddmm_grad_vals,
-                      snack_spmm_bwd_input, snack_spmm_fwd, snack_version, status_str)
+                      snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd, snack_version,
+                      status_str)
 from .layer import SparseLinear, Topology  # noqa: F401

@@ -67,6 +67,7 @@ def _load():
         "snack_spmm_fwd": ([plan_p, P, i32, P, i32, i32, P, P], i32),
         "snack_spmm_bwd_input": ([plan_p, P, i32, P, i32, i32, P, P], i32),
         "snack_sddmm_grad_vals": ([plan_p, P, P, i32, i32, i32, P, P], i32),
+        "snack_spmm_bwd_fused": ([plan_p, P, i32, P, P, i32, i32, P, P, ctypes.c_float, P], i32),
         "snack_drop_count": ([i64, i32], i64),
         "snack_prune_regrow_workspace": ([i32, i32, i64, i64, ctypes.POINTER(sz)], i32),
         "snack_prune_regrow": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz, P], i32),
@@ -176,6 +177,15 @@ def snack_sddmm_grad_vals(plan, dY, X, layout, B, dvals, stream=None, dtype=None
     dt = _dtype(dvals, dY, X, dtype=dtype)
     _check(_lib.snack_sddmm_grad_vals(ctypes.byref(plan), _ptr(dY), _ptr(X), dt, layout, B,
                                       _ptr(dvals), _stream(stream)), "snack_sddmm_grad_vals")
+
+
+def snack_spmm_bwd_fused(plan, vals, X, dY, layout, B, dX, dvals=None, lr=0.0, stream=None,
+                         dtype=None):
+    """dX = dY W, dvals = (dY^T X) at the nonzeros, and vals -= lr * dV in place, in one pass."""
+    dt = _dtype(vals, X, dY, dX, dtype=dtype)
+    _check(_lib.snack_spmm_bwd_fused(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), _ptr(dY),
+                                     layout, B, _ptr(dX), _ptr(dvals), float(lr),
+                                     _stream(stream)), "snack_spmm_bwd_fused")
 
 
 def snack_drop_count(nnz: int, frac_ppm: int) -> int:

@@ -316,6 +316,20 @@ snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const
                       to_stream(stream));
 }
 
+snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, snack_dtype dtype,
+                                  const void* X, const void* dY, snack_layout layout, int32_t B,
+                                  void* dX, void* dvals, float lr, void* stream) {
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  if (st) return st;
+  if (B > 0 && !X) return SNACK_E_NULL;
+  if (B > 32) return SNACK_E_SHAPE;
+  if (!(lr == lr) || lr - lr != 0.f) return SNACK_E_NAN;  // NaN or infinite step size
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  return launch_bwd_fused(col_view(plan), vals, dtype, X, dY, layout, B, dX,
+                          plan->nnz > 0 ? dvals : nullptr, lr, carry, act_of(plan),
+                          to_stream(stream));
+}
+
 int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {
   if (nnz < 0 || frac_ppm < 0) return -1;
   return (int64_t)(((__int128)nnz * frac_ppm + 500000) / 1000000);

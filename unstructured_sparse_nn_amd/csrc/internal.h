@@ -63,6 +63,11 @@ snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt
                              hipStream_t s);
 snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snack_dtype dt,
                           snack_layout lay, int32_t B, void* dV, void* act_tmp, hipStream_t s);
+// Column view, B <= 32: dX = dY W, dV (nullable) and, if lr != 0, the
+// in-place update vals <- vals - lr * dV, in one pass.
+snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* X,
+                              const void* dY, snack_layout lay, int32_t B, void* dX, void* dV,
+                              float lr, float* carry, void* act_tmp, hipStream_t s);
 hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
                              const void* in1, void* out1, int32_t R1, int32_t C1,
                              hipStream_t s);

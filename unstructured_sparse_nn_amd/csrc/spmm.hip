@@ -98,12 +98,14 @@ struct tile_lds {
   float* pend;     // [threads*CH] partial sum of a run's first, earlier-started segment
   float* wval;     // [4][MP_MAX_BW] per-wave scan totals
   int32_t* wflag;  // [4] per-wave "a segment starts here" flags
+  int32_t* perm;   // [2T] value position of each entry (fused backward only)
 };
 
-__host__ __device__ inline size_t tile_lds_bytes(int tile_items, int threads, int g_log2, int ch) {
+__host__ __device__ inline size_t tile_lds_bytes(int tile_items, int threads, int g_log2, int ch,
+                                                 bool with_perm = false) {
   int NT = threads >> g_log2;
   return 3 * 4 * (size_t)(2 * tile_items) + 8 * (size_t)(NT + 1) + 8 * (size_t)threads * ch +
-         4 * 4 * MP_MAX_BW + 16;
+         4 * 4 * MP_MAX_BW + 16 + (with_perm ? 4 * (size_t)(2 * tile_items) : 0);
 }
 
 __device__ __forceinline__ tile_lds carve(unsigned char* smem, int tile_items, int threads,
@@ -118,6 +120,7 @@ __device__ __forceinline__ tile_lds carve(unsigned char* smem, int tile_items, i
   L.pend = L.scan + threads * ch;
   L.wval = L.pend + threads * ch;
   L.wflag = (int32_t*)(L.wval + 4 * MP_MAX_BW);
+  L.perm = L.wflag + 4;
   return L;
 }
 
@@ -125,12 +128,11 @@ __device__ __forceinline__ tile_lds carve(unsigned char* smem, int tile_items, i
 // round issues all of a thread's MP_SU loads of every array before storing
 // any, so a round costs one memory round trip (two with the value
 // permutation of the column view).
-template <typename T, bool PERM, bool VALS>
+template <typename T, bool PERM, bool VALS, bool KEEP_PERM = false>
 __device__ __forceinline__ void stage_tile(const tile_lds& L, const int32_t* __restrict__ ptr,
                                            const int32_t* __restrict__ idx,
-                                           const int32_t* __restrict__ perm,
-                                           const T* __restrict__ vals, int32_t sb, int32_t zb,
-                                           int nseg, int nz) {
+                                           const int32_t* __restrict__ perm, const T* vals,
+                                           int32_t sb, int32_t zb, int nseg, int nz) {
   const int tid = threadIdx.x, threads = blockDim.x;
   const int nst = max(nseg, nz);
   for (int base = 0; base < nst; base += threads * MP_SU) {
@@ -152,6 +154,13 @@ __device__ __forceinline__ void stage_tile(const tile_lds& L, const int32_t* __r
       }
 #pragma unroll
       for (int j = 0; j < MP_SU; ++j) tv[j] = tk[j] >= 0 ? vals[tk[j]] : (T)0;
+      if constexpr (KEEP_PERM) {
+#pragma unroll
+        for (int j = 0; j < MP_SU; ++j) {
+          const int i = base + j * threads + tid;
+          if (i < nz) L.perm[i] = tk[j];
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < MP_SU; ++j) {
@@ -165,13 +174,19 @@ __device__ __forceinline__ void stage_tile(const tile_lds& L, const int32_t* __r
   }
 }
 
-template <typename T, int CH, bool NODE_OUT, bool PERM>
+// FUSED (column view only): also dV[k] = sum_b in[b, seg] ... for each entry:
+// the dot of its gathered activation chunk with the chunk of Xs at its own
+// segment (column), reduced over the group's lanes, written to dV[perm] and,
+// when lr != 0, vals[perm] <- vals[perm] - lr * dV (the fused backward).
+template <typename T, int CH, bool NODE_OUT, bool PERM, bool FUSED = false>
 __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ perm, const T* __restrict__ vals,
+    const int32_t* __restrict__ perm, const T* vals,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
     const T* __restrict__ Xt, T* __restrict__ Y, float* __restrict__ carry, int32_t S,
-    int32_t B, int32_t P, int32_t g_log2, int32_t tile_items, int32_t xcd_tiles) {
+    int32_t B, int32_t P, int32_t g_log2, int32_t tile_items, int32_t xcd_tiles,
+    const T* __restrict__ Xs = nullptr, T* __restrict__ dV = nullptr, T* vals_upd = nullptr,
+    float lr = 0.f) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int threads = blockDim.x;
   const int G = 1 << g_log2;
@@ -182,6 +197,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   const int gl = tid & (G - 1);
   const int lane = lane_id();
   const int wave = tid >> 6;
+  static_assert(!FUSED || PERM, "the fused backward runs over the column view");
   // xcd_tiles > 0: workgroup b (dispatched to XCD b % 8) takes tile
   // (b % 8) * xcd_tiles + b / 8, so each XCD works on one contiguous range
   // of tiles and its L2 sees a narrower slice of what the tiles gather
@@ -199,7 +215,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
   const int items = nseg + nz;
   const int32_t seg0_start = ptr[sb];
 
-  stage_tile<T, PERM, true>(L, ptr, idx, perm, vals, sb, zb, nseg, nz);
+  stage_tile<T, PERM, true, FUSED>(L, ptr, idx, perm, vals, sb, zb, nseg, nz);
   __syncthreads();
 
   const int R = (items + NT - 1) / NT;
@@ -273,6 +289,30 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
 #pragma unroll
       for (int u = 0; u < MP_RC; ++u) sd[u] += (e <= pos0 + u) ? 1 : 0;
       ++xh;
+    }
+    if constexpr (FUSED) {
+      // value gradient of each entry: its gathered chunk . the chunk of Xs at
+      // its own segment, summed over the group's lanes
+      vec<T, CH> xs[MP_RC];
+#pragma unroll
+      for (int u = 0; u < MP_RC; ++u) {
+        if (u < n && bvalid) {
+          xs[u] = *reinterpret_cast<const vec<T, CH>*>(Xs + (int64_t)(sb + x + sd[u]) * B + b0);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CH; ++c) xs[u].v[c] = (T)0;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MP_RC; ++u) {
+        float d = dot_acc<T, CH>(xv[u], xs[u], 0.f);
+        for (int off = 1; off < G; off <<= 1) d += __shfl_xor(d, off, SNK_WAVE);
+        if (gl == 0 && u < n) {
+          const int32_t pk = L.perm[y + u];
+          if (dV) dV[pk] = elem<T>::from_f(d);
+          if (lr != 0.f) vals_upd[pk] = elem<T>::from_f(L.val[y + u] - lr * d);
+        }
+      }
     }
     int cur = 0;
 #pragma unroll
@@ -703,6 +743,82 @@ snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt
   lane_shape sh = pick_shape(dt, B, v.tile);
   if (dt == SNACK_F32) launch_dt<float>(v, vals, Xt, node_out, B, Y, carry, sh, s);
   else launch_dt<bf16>(v, vals, Xt, node_out, B, Y, carry, sh, s);
+  return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+}
+
+// ---- fused backward (column view): dX, dV and the optional SGD update
+template <typename T, int CH, bool NODE_OUT>
+static void launch_fused_t(const seg_view& v, void* vals, const void* dYt, const void* Xt,
+                           int32_t B, void* dX, void* dV, float lr, float* carry,
+                           const lane_shape& sh, hipStream_t s) {
+  const int32_t xt = xcd_tiles_for(v);
+  dim3 grid((unsigned)(xt ? xt * NUM_XCD : v.P), 1);
+  size_t lds = tile_lds_bytes(v.tile, sh.threads, sh.g_log2, CH, true);
+  hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, true, true>), grid, dim3(sh.threads), lds, s,
+                     v.ptr, v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)dYt,
+                     (T*)dX, carry, v.S, B, v.P, sh.g_log2, v.tile, xt, (const T*)Xt, (T*)dV,
+                     lr != 0.f ? (T*)vals : nullptr, lr);
+  if (v.has_split) {
+    int64_t n = (int64_t)v.P * B;
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                       v.part_seg, v.cut, carry, (T*)dX, v.S, B, v.P);
+  }
+}
+
+template <typename T, int CH>
+static void launch_fused_ch(const seg_view& v, void* vals, const void* dYt, const void* Xt,
+                            bool node_out, int32_t B, void* dX, void* dV, float lr, float* carry,
+                            const lane_shape& sh, hipStream_t s) {
+  if (node_out) launch_fused_t<T, CH, true>(v, vals, dYt, Xt, B, dX, dV, lr, carry, sh, s);
+  else launch_fused_t<T, CH, false>(v, vals, dYt, Xt, B, dX, dV, lr, carry, sh, s);
+}
+
+template <typename T>
+static void launch_fused_dt(const seg_view& v, void* vals, const void* dYt, const void* Xt,
+                            bool node_out, int32_t B, void* dX, void* dV, float lr, float* carry,
+                            const lane_shape& sh, hipStream_t s) {
+  switch (sh.ch) {
+    case 1: launch_fused_ch<T, 1>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s); break;
+    case 2: launch_fused_ch<T, 2>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s); break;
+    case 4: launch_fused_ch<T, 4>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s); break;
+    default:
+      if constexpr (sizeof(T) == 2)
+        launch_fused_ch<T, 8>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
+      break;
+  }
+}
+
+snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* X,
+                              const void* dY, snack_layout lay, int32_t B, void* dX, void* dV,
+                              float lr, float* carry, void* act_tmp, hipStream_t s) {
+  if (B == 0) {  // empty batch: dV = 0, the update is a no-op, dX has no elements
+    if (dV && v.nnz > 0) {
+      dim3 g((unsigned)cdiv(v.nnz, 256));
+      if (dt == SNACK_F32)
+        hipLaunchKernelGGL(k_fill_zero<float>, g, dim3(256), 0, s, (float*)dV, v.nnz);
+      else
+        hipLaunchKernelGGL(k_fill_zero<bf16>, g, dim3(256), 0, s, (bf16*)dV, v.nnz);
+    }
+    return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+  }
+  const lane_shape sh = pick_shape(dt, B, v.tile);
+  if (cdiv(B, sh.bw) != 1) return SNACK_E_SHAPE;  // one workgroup column must see the whole batch
+  const void* dYt = dY;  // gathered by row (F = M)
+  const void* Xt = X;    // read at each entry's column (S = K)
+  if (lay == SNACK_BATCH_MAJOR && B > 1) {
+    if (!act_tmp) return SNACK_E_WORKSPACE;
+    const size_t es = dt == SNACK_F32 ? 4 : 2;
+    char* gt = (char*)act_tmp;
+    char* xt = gt + align_up(es * (size_t)B * v.F, 256);
+    if (launch_transpose2(dt, dY, gt, B, v.F, X, xt, B, v.S, s) != hipSuccess) return SNACK_E_HIP;
+    dYt = gt;
+    Xt = xt;
+  }
+  const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
+  if (dt == SNACK_F32)
+    launch_fused_dt<float>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
+  else
+    launch_fused_dt<bf16>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
   return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
 }
 
