@@ -13,6 +13,10 @@ namespace snk {
 
 typedef uint16_t bf16;  // raw bfloat16 bits
 
+// Accelerator complex dies of an MI355X; workgroup b of a launch runs on die
+// b mod NUM_XCD, and each die has its own L2.
+constexpr int NUM_XCD = 8;
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_to_f32(bf16 h) {
   return __uint_as_float(((uint32_t)h) << 16);

@@ -35,15 +35,12 @@ namespace snk {
 namespace {
 
 constexpr int BT = 256;                   // threads per entry block
-constexpr int RND = 1;                    // rounds of 4 consecutive entries per thread
-constexpr int BE = 4 * BT * RND;          // entries per block: entry r*1024 + 4t + j
+constexpr int BE = 4 * BT;                // entries per block: thread t holds base + 4t .. + 3
 constexpr int HREPL = 64;                 // select-histogram replicas
 constexpr int AREPL = 64;                 // acceptance-count replicas
-constexpr int GAPCAP = 512;               // long zero runs recorded per block
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
 constexpr int WT = 512;                   // threads (= bitmap words) per write block
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
-constexpr int64_t GAP_INLINE = 16;        // zero runs of up to this many words: one thread
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
 // are fat (few blocks) and their counters spread over replicas.
@@ -184,168 +181,165 @@ __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, 
   }
 }
 
-// Zero words [lo, hi) of up to two bitmaps: short runs by the calling
-// thread, longer ones recorded in LDS for the whole block (fill_gaps).
-struct gap_list {
-  int64_t* lo;
-  int64_t* hi;
-  int32_t* n;
-};
-
-__device__ __forceinline__ void zero_words(uint32_t* a, uint32_t* b, int64_t lo, int64_t hi,
-                                           const gap_list& g) {
-  if (hi - lo <= 0) return;
-  if (hi - lo <= GAP_INLINE) {
-    for (int64_t u = lo; u < hi; ++u) {
-      a[u] = 0u;
-      if (b) b[u] = 0u;
-    }
-  } else {
-    const int32_t k = atomicAdd(g.n, 1);
-    if (k < GAPCAP) {
-      g.lo[k] = lo;
-      g.hi[k] = hi;
-    } else {  // list full: this thread fills it
-      for (int64_t u = lo; u < hi; ++u) {
-        a[u] = 0u;
-        if (b) b[u] = 0u;
-      }
-    }
+// The entries a block needs beyond its own, loaded by every thread next to
+// the block's main loads (clamped indices, no branch, one round trip) and
+// kept by a few threads in LDS: the linear index of entry base-1 (-1 for
+// block 0 or an invalid entry) and of the next NEXT entries past the block
+// (-1 past nnz or invalid), with their magnitudes if mag is given.  A
+// bitmap word holds 32 positions, so at most 32 later entries can share the
+// block's last word.  Readers wait for the block's next barrier.
+constexpr int NEXT = 32;
+template <typename T>
+__device__ __forceinline__ void stage_edges(const int32_t* __restrict__ row,
+                                            const int32_t* __restrict__ col,
+                                            const T* __restrict__ vals, int64_t nnz, int32_t M,
+                                            int32_t K, int64_t base, int n, int64_t* edge,
+                                            int64_t* nxt, uint32_t* mag) {
+  const int t = threadIdx.x;
+  const int64_t eb = base > 0 ? base - 1 : 0;
+  const int64_t k = base + n + (t & (NEXT - 1));
+  const int64_t kk = k < nnz ? k : nnz - 1;
+  const int32_t er = row[eb], ec = col[eb], nr = row[kk], nc = col[kk];
+  uint32_t nm = 0;
+  if (mag) nm = magnitude<T>(raw_bits(vals[kk]));
+  if (t == BT - 1) *edge = base > 0 ? lin_of(er, ec, M, K) : -1;
+  if (t < NEXT) {
+    nxt[t] = k < nnz ? lin_of(nr, nc, M, K) : -1;
+    if (mag) mag[t] = nm;
   }
 }
 
-__device__ __forceinline__ void fill_gaps(uint32_t* a, uint32_t* b, const gap_list& g) {
-  __syncthreads();
-  const int32_t n = min(*g.n, GAPCAP);
-  for (int32_t k = 0; k < n; ++k)
-    for (int64_t u = g.lo[k] + threadIdx.x; u < g.hi[k]; u += blockDim.x) {
-      a[u] = 0u;
-      if (b) b[u] = 0u;
+// Bitmap words [w_lo, w_hi] of an entry block, written whole (zeros
+// included) with coalesced stores.  Each chunk of up to CAP words is
+// assembled in LDS -- an LDS atomicOr per flagged entry (l[q] >= 0,
+// f[q]) of the calling thread whose word lies in the chunk, plus `extra`
+// into word w_hi -- and then stored; b, if given, receives zeros over the
+// same words.  An entry whose word lies outside the range (a block's first
+// run, in the previous block's last word) is left to that word's owner.
+// w_lo, w_hi and extra's presence are block-uniform; call from all threads.
+constexpr int CAP = 2048;
+__device__ void write_block_words(uint32_t* buf, int64_t w_lo, int64_t w_hi,
+                                  const int64_t (&l)[4], const bool (&f)[4], uint32_t extra,
+                                  uint32_t* __restrict__ a, uint32_t* __restrict__ b) {
+  for (int64_t cs = w_lo; cs <= w_hi; cs += CAP) {
+    const int32_t len = (int32_t)std::min<int64_t>(CAP, w_hi + 1 - cs);
+    for (int j = threadIdx.x; j < len; j += BT) buf[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t w = l[q] >> 5;
+      if (f[q] && l[q] >= 0 && w >= cs && w < cs + len)
+        atomicOr(&buf[w - cs], 1u << (l[q] & 31));
     }
-}
-
-// Write the owned bitmap words of an entry block.  L[i] = linear index of
-// entry i of the block (-1: invalid), use[i] = its bit belongs in the map;
-// edge0 = word of entry base-1 (-1 for block 0); `more(w)` returns the bits
-// of the entries past the block's end that share word w.  Called by all
-// threads after L/use are complete in LDS.
-template <typename MORE>
-__device__ void write_owned_words(const int64_t* L, const uint8_t* use, int n, int64_t edge0,
-                                  bool last_block, int64_t W, uint32_t* a, uint32_t* b,
-                                  const gap_list& g, MORE more) {
-  for (int q = 0; q < 4 * RND; ++q) {
-    const int i = (q >> 2) * (4 * BT) + 4 * threadIdx.x + (q & 3);
-    if (i >= n || L[i] < 0) continue;
-    const int64_t w = L[i] >> 5;
-    const int64_t pw = i == 0 ? edge0 : (L[i - 1] < 0 ? w - 1 : (L[i - 1] >> 5));
-    if (i > 0 && pw == w) continue;  // not the first entry of its run
-    int e = i;
-    uint32_t bits = 0;
-    while (e < n && L[e] >= 0 && (L[e] >> 5) == w) {
-      if (use[e]) bits |= 1u << (L[e] & 31);
-      ++e;
+    if (threadIdx.x == 0 && extra && w_hi < cs + len) atomicOr(&buf[w_hi - cs], extra);
+    __syncthreads();
+    for (int j = threadIdx.x; j < len; j += BT) {
+      a[cs + j] = buf[j];
+      if (b) b[cs + j] = 0u;
     }
-    if (w != edge0) {  // owned (the only unowned run is a first run in edge0's word)
-      if (e == n && !last_block) bits |= more(w);
-      a[w] = bits;
-      if (b) b[w] = 0u;
-      zero_words(a, b, pw + 1, w, g);
-    }
-    if (last_block && i + (e - i) == n) zero_words(a, b, w + 1, W, g);
+    __syncthreads();
   }
 }
 
-// Support bitmap S (and G cleared), a copy of the values, the NaN / index
-// checks and the first select histogram.
+// Word of a block's last entry (entry n-1, held by thread (n-1)/4), into
+// *whi (-1 if that entry is invalid).
+__device__ __forceinline__ void last_word(const int64_t (&l)[4], int n, int64_t* whi) {
+  const int t = threadIdx.x, i = n - 1;
+  if (t == (i >> 2)) {
+    const int q = i & 3;
+    const int64_t x = q == 0 ? l[0] : q == 1 ? l[1] : q == 2 ? l[2] : l[3];
+    *whi = x < 0 ? -1 : (x >> 5);
+  }
+}
+
+// Support bitmap S (and G cleared), a copy of the values, the NaN / index /
+// order checks and the first select histogram.  Thread t holds entries
+// base + 4t .. base + 4t + 3.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_build(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
     int64_t nnz, int32_t M, int32_t K, int64_t W, int shift, int32_t vec_ok, bm_state* st,
     uint32_t* __restrict__ sup, uint32_t* __restrict__ grown, T* __restrict__ vals_ws) {
   __shared__ int32_t h[256];
-  __shared__ int64_t L[BE];
-  __shared__ uint8_t use[BE];
-  __shared__ int64_t glo[GAPCAP], ghi[GAPCAP];
-  __shared__ int32_t gn;
-  __shared__ int64_t edge0_s;
+  __shared__ uint32_t buf[CAP];
+  __shared__ int64_t lastl[BT];
+  __shared__ int64_t edge_s, whi_s;
+  __shared__ int64_t nxt[NEXT];
   const int t = threadIdx.x;
   h[t] = 0;
-  if (t == 0) gn = 0;
   const int64_t base = (int64_t)blockIdx.x * BE;
   const int n = (int)std::min<int64_t>(BE, nnz - base);
-  if (t == 0) {
-    const int64_t e = base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1;
-    edge0_s = e < 0 ? -1 : (e >> 5);
-  }
-  // all loads first (one round trip)
-  int32_t r4[RND][4], c4[RND][4];
-  T v4[RND][4];
+  const int64_t k0 = base + 4 * t;
+  const bool full = vec_ok && k0 + 3 < nnz;
+  int32_t r4[4], c4[4];
+  T v4[4];
+  if (full) {
+    const int4 rv = *reinterpret_cast<const int4*>(row + k0);
+    const int4 cv = *reinterpret_cast<const int4*>(col + k0);
+    const vec<T, 4> vv = *reinterpret_cast<const vec<T, 4>*>(vals + k0);
+    r4[0] = rv.x; r4[1] = rv.y; r4[2] = rv.z; r4[3] = rv.w;
+    c4[0] = cv.x; c4[1] = cv.y; c4[2] = cv.z; c4[3] = cv.w;
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * t;
-    if (vec_ok && k0 + 3 < nnz) {
-      const int4 rv = *reinterpret_cast<const int4*>(row + k0);
-      const int4 cv = *reinterpret_cast<const int4*>(col + k0);
-      const vec<T, 4> vv = *reinterpret_cast<const vec<T, 4>*>(vals + k0);
-      r4[r][0] = rv.x; r4[r][1] = rv.y; r4[r][2] = rv.z; r4[r][3] = rv.w;
-      c4[r][0] = cv.x; c4[r][1] = cv.y; c4[r][2] = cv.z; c4[r][3] = cv.w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v4[r][j] = vv.v[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = k0 + j < nnz;
-        r4[r][j] = ok ? row[k0 + j] : 0;
-        c4[r][j] = ok ? col[k0 + j] : 0;
-        v4[r][j] = ok ? vals[k0 + j] : (T)0;
-      }
-    }
-  }
-  int err = 0;
-#pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * t;
+    for (int j = 0; j < 4; ++j) v4[j] = vv.v[j];
+  } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t a = magnitude<T>(raw_bits(v4[r][j]));
       const bool ok = k0 + j < nnz;
-      wave_hist_add(h, (a >> shift) & 255u, ok);
-      if (ok) {
-        vals_ws[k0 + j] = v4[r][j];
-        const int64_t l = lin_of(r4[r][j], c4[r][j], M, K);
-        if (is_nan_mag<T>(a)) err |= 1;
-        if (l < 0) err |= 2;
-        const int i = r * (4 * BT) + 4 * t + j;
-        L[i] = l;
-        use[i] = 1;
-      }
+      r4[j] = ok ? row[k0 + j] : 0;
+      c4[j] = ok ? col[k0 + j] : 0;
+      v4[j] = ok ? vals[k0 + j] : (T)0;
     }
   }
+  stage_edges<T>(row, col, vals, nnz, M, K, base, n, &edge_s, nxt, nullptr);
+  __syncthreads();  // h zeroed before any wave adds to it
+  int err = 0;
+  int64_t l[4];
+  bool f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = k0 + j < nnz;
+    const uint32_t a = magnitude<T>(raw_bits(v4[j]));
+    wave_hist_add(h, (a >> shift) & 255u, ok);
+    l[j] = ok ? lin_of(r4[j], c4[j], M, K) : -1;
+    f[j] = ok;
+    if (ok && is_nan_mag<T>(a)) err |= 1;
+    if (ok && l[j] < 0) err |= 2;
+  }
+  if (full) {
+    vec<T, 4> vv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv.v[j] = v4[j];
+    *reinterpret_cast<vec<T, 4>*>(vals_ws + k0) = vv;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + j < nnz) vals_ws[k0 + j] = v4[j];
+  }
+  lastl[t] = l[3];
+  last_word(l, n, &whi_s);
   __syncthreads();
   // strictly increasing: against the previous entry (the block's left edge
-  // from global memory)
-  for (int q = 0; q < 4 * RND; ++q) {
-    const int i = (q >> 2) * (4 * BT) + 4 * t + (q & 3);
-    if (i >= n || L[i] < 0) continue;
-    const int64_t pl = i > 0 ? L[i - 1]
-                             : (base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1);
-    if (pl >= 0 && L[i] <= pl) err |= 4;
+  // staged in LDS)
+  const int64_t edge = edge_s;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (l[q] < 0) continue;
+    const int64_t pl = q > 0 ? l[q - 1] : (t > 0 ? lastl[t - 1] : edge);
+    if (pl >= 0 && l[q] <= pl) err |= 4;
   }
-  const gap_list g{glo, ghi, &gn};
-  const int64_t edge0 = edge0_s;
   const bool last_block = base + n >= nnz;
-  write_owned_words(L, use, n, edge0, last_block, W, sup, grown, g, [&](int64_t w) {
-    uint32_t bits = 0;
-    for (int64_t k = base + n; k < nnz && k < base + n + 32; ++k) {
-      const int64_t l = lin_of(row[k], col[k], M, K);
-      if (l < 0 || (l >> 5) != w) break;
-      bits |= 1u << (l & 31);
+  const int64_t w_lo = edge >= 0 ? (edge >> 5) + 1 : 0;
+  const int64_t w_hi = last_block ? W - 1 : whi_s;
+  uint32_t extra = 0;
+  if (t == 0 && !last_block) {  // next block's entries in this block's last word
+    for (int u = 0; u < NEXT; ++u) {
+      const int64_t x = nxt[u];
+      if (x < 0 || (x >> 5) != w_hi) break;
+      extra |= 1u << (x & 31);
     }
-    return bits;
-  });
-  fill_gaps(sup, grown, g);
+  }
+  write_block_words(buf, w_lo, w_hi, l, f, extra, sup, grown);
   if (err) atomicOr(&st->err, err);
-  __syncthreads();
   if (h[t]) atomicAdd(&st->hist[0][blockIdx.x % HREPL][t], h[t]);
 }
 
@@ -361,24 +355,16 @@ __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64
   __shared__ int32_t h[256];
   const int t = threadIdx.x;
   h[t] = 0;
-  const int64_t base = (int64_t)blockIdx.x * BE;
-  uint32_t a[RND][4];
+  const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * t;
+  uint32_t a[4];
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[r][j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0u;
-  }
+  for (int j = 0; j < 4; ++j) a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0u;
   uint32_t pfx, msk;
   int32_t need;
   pick_digit(st, pass - 1, prev_shift, n_drop, pfx, msk, need);
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wave_hist_add(h, (a[r][j] >> shift) & 255u, k0 + j < nnz && (a[r][j] & msk) == pfx);
-  }
+  for (int j = 0; j < 4; ++j)
+    wave_hist_add(h, (a[j] >> shift) & 255u, k0 + j < nnz && (a[j] & msk) == pfx);
   __syncthreads();
   if (h[t]) atomicAdd(&st->hist[pass][blockIdx.x % HREPL][t], h[t]);
   regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
@@ -394,23 +380,17 @@ __global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int
                                                  const uint32_t* __restrict__ sup,
                                                  uint32_t* __restrict__ grown) {
   __shared__ int32_t lds[BT / SNK_WAVE];
-  const int64_t base = (int64_t)blockIdx.x * BE;
-  uint32_t a[RND][4];
+  const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * threadIdx.x;
+  uint32_t a[4];
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      a[r][j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
-  }
+  for (int j = 0; j < 4; ++j)
+    a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
   uint32_t tau, msk;
   int32_t need;
   pick_digit(st, last_pass, shift, n_drop, tau, msk, need);
   int32_t eq = 0;
 #pragma unroll
-  for (int r = 0; r < RND; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) eq += a[r][j] == tau ? 1 : 0;
+  for (int j = 0; j < 4; ++j) eq += a[j] == tau ? 1 : 0;
   int32_t tot;
   block_excl_scan_i32<BT>(eq, lds, &tot);
   if (threadIdx.x == 0) cnt_eq[blockIdx.x] = tot;
@@ -457,73 +437,61 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
     bm_state* st, uint32_t* __restrict__ dropb, const uint32_t* __restrict__ sup,
     uint32_t* __restrict__ grown) {
   __shared__ int32_t lds[BT / SNK_WAVE];
-  __shared__ int64_t L[BE];
-  __shared__ uint8_t use[BE];
-  __shared__ int64_t glo[GAPCAP], ghi[GAPCAP];
-  __shared__ int32_t gn;
-  __shared__ int64_t edge0_s;
+  __shared__ uint32_t buf[CAP];
+  __shared__ int64_t edge_s, whi_s;
+  __shared__ int64_t nxt[NEXT];
+  __shared__ uint32_t nxt_mag[NEXT];
   const int t = threadIdx.x;
-  if (t == 0) gn = 0;
   const uint32_t tau = st->pfx[last_pass];
   const int32_t need = st->need[last_pass];
   const int64_t base = (int64_t)blockIdx.x * BE;
   const int n = (int)std::min<int64_t>(BE, nnz - base);
-  if (t == 0) {
-    const int64_t e = base > 0 ? lin_of(row[base - 1], col[base - 1], M, K) : -1;
-    edge0_s = e < 0 ? -1 : (e >> 5);
-  }
-  uint32_t a[RND][4];
-  int32_t r4[RND][4], c4[RND][4];
+  const int64_t k0 = base + 4 * t;
+  uint32_t a[4];
+  int64_t l[4];
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    const int64_t k0 = base + r * (4 * BT) + 4 * t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = k0 + j < nnz;
-      a[r][j] = ok ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
-      r4[r][j] = ok ? row[k0 + j] : -1;
-      c4[r][j] = ok ? col[k0 + j] : -1;
-    }
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = k0 + j < nnz;
+    const int64_t kk = ok ? k0 + j : nnz - 1;
+    const uint32_t m = magnitude<T>(raw_bits(vals[kk]));
+    const int32_t r = row[kk], cc = col[kk];
+    a[j] = ok ? m : 0xFFFFFFFFu;
+    l[j] = ok ? lin_of(r, cc, M, K) : -1;
   }
+  stage_edges<T>(row, col, vals, nnz, M, K, base, n, &edge_s, nxt, nxt_mag);
+  last_word(l, n, &whi_s);
   const int32_t E = base_eq ? base_eq[blockIdx.x] : block_sum_prefix(cnt_eq, blockIdx.x);
-  // tie ranks in index order: rounds in turn, a block scan each
-  int32_t run = E;
+  // tie ranks in index order (a block scan; its barriers also publish the
+  // staged edges)
+  int32_t eq = 0;
 #pragma unroll
-  for (int r = 0; r < RND; ++r) {
-    int32_t eq = 0;
+  for (int j = 0; j < 4; ++j) eq += a[j] == tau ? 1 : 0;
+  int32_t tot;
+  int32_t er = E + block_excl_scan_i32<BT>(eq, lds, &tot);
+  const int32_t run = E + tot;
+  bool f[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) eq += a[r][j] == tau ? 1 : 0;
-    int32_t tot;
-    int32_t er = run + block_excl_scan_i32<BT>(eq, lds, &tot);
-    run += tot;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = r * (4 * BT) + 4 * t + j;
-      if (i >= n) continue;
-      const bool is_eq = a[r][j] == tau;
-      use[i] = (a[r][j] < tau || (is_eq && er < need)) ? 1 : 0;
-      er += is_eq ? 1 : 0;
-      L[i] = lin_of(r4[r][j], c4[r][j], M, K);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const bool is_eq = a[j] == tau;
+    f[j] = l[j] >= 0 && (a[j] < tau || (is_eq && er < need));
+    er += is_eq ? 1 : 0;
   }
-  __syncthreads();
-  const gap_list g{glo, ghi, &gn};
-  const int64_t edge0 = edge0_s;
+  const int64_t edge = edge_s;
   const bool last_block = base + n >= nnz;
-  write_owned_words(L, use, n, edge0, last_block, W, dropb, nullptr, g, [&](int64_t w) {
-    // entries of the next block in word w, with their own tie ranks
+  const int64_t w_lo = edge >= 0 ? (edge >> 5) + 1 : 0;
+  const int64_t w_hi = last_block ? W - 1 : whi_s;
+  uint32_t extra = 0;
+  if (t == 0 && !last_block) {  // next block's entries in this word, with their tie ranks
     int32_t ern = run;
-    uint32_t bits = 0;
-    for (int64_t k = base + n; k < nnz && k < base + n + 32; ++k) {
-      const int64_t l = lin_of(row[k], col[k], M, K);
-      if (l < 0 || (l >> 5) != w) break;
-      const uint32_t m = magnitude<T>(raw_bits(vals[k]));
-      if (m < tau || (m == tau && ern < need)) bits |= 1u << (l & 31);
+    for (int u = 0; u < NEXT; ++u) {
+      const int64_t x = nxt[u];
+      if (x < 0 || (x >> 5) != w_hi) break;
+      const uint32_t m = nxt_mag[u];
+      if (m < tau || (m == tau && ern < need)) extra |= 1u << (x & 31);
       ern += m == tau ? 1 : 0;
     }
-    return bits;
-  });
-  fill_gaps(dropb, nullptr, g);
+  }
+  write_block_words(buf, w_lo, w_hi, l, f, extra, dropb, nullptr);
   regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
 }
 
@@ -639,7 +607,7 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
     const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
     int64_t nnz, int64_t n_drop, const bm_state* st, int32_t* __restrict__ result,
-    uint32_t* __restrict__ Fb, int32_t* __restrict__ pwb, int32_t* __restrict__ row,
+    uint2* __restrict__ FP, int32_t* __restrict__ row,
     int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
     int64_t* __restrict__ grown_lin) {
   __shared__ int32_t lds[WT / SNK_WAVE];
@@ -683,10 +651,8 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   int64_t qg = bo.w + (dg >> 16);
   const int64_t pw = w * 32;
   uint32_t F = (S & ~D) | G;
-  if (Fb && w < W) {  // the new support and its per-word prefix, for a fused prepare
-    Fb[w] = F;
-    pwb[w] = (int32_t)qf;
-  }
+  if (FP && w < W)  // the new support and its per-word prefix, for a fused prepare
+    FP[w] = make_uint2(F, (uint32_t)qf);
   if (F) {
     // row and column of the word's first position; the rest step from it
     int32_t r0, c0;
@@ -697,20 +663,34 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       r0 = (int32_t)(pw / K);
       c0 = (int32_t)(pw - (int64_t)r0 * K);
     }
+    // four set bits at a time, their survivor-value loads in flight together
     while (F) {
-      const int b = __ffs(F) - 1;
-      F &= F - 1;
-      if (qf < nnz) {
-        int32_t r = r0, cc = c0 + b;
-        while (cc >= K) {
-          cc -= K;
-          ++r;
-        }
-        row[qf] = r;
-        col[qf] = cc;
-        vals[qf] = ((S >> b) & 1u) ? vals_ws[qs + __popc(S & ((1u << b) - 1u))] : (T)0;
+      int b[4];
+      T v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        b[u] = F ? __ffs(F) - 1 : -1;
+        F &= F - 1;
       }
-      ++qf;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = (b[u] >= 0 && ((S >> b[u]) & 1u)) ? vals_ws[qs + __popc(S & ((1u << b[u]) - 1u))]
+                                                 : (T)0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (b[u] < 0) break;
+        if (qf < nnz) {
+          int32_t r = r0, cc = c0 + b[u];
+          while (cc >= K) {
+            cc -= K;
+            ++r;
+          }
+          row[qf] = r;
+          col[qf] = cc;
+          vals[qf] = v[u];
+        }
+        ++qf;
+      }
     }
   }
   if (dropped_lin) {
@@ -758,7 +738,7 @@ constexpr int FP_THREADS = 256;
 // Blocks [0, rb): row offsets and row tiles, thread per row s in [0, M].
 // Blocks [rb, ..): bit transpose, two 32 x 32 tiles per wave.
 __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
-    const bm_state* st, const uint32_t* __restrict__ Fb, const int32_t* __restrict__ pwb,
+    const bm_state* st, const uint2* __restrict__ FP,
     int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ rsplit,
     uint32_t* __restrict__ FT) {
   if (bm_failed(st)) return;
@@ -767,8 +747,8 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
     const int64_t s = (int64_t)blockIdx.x * FP_THREADS + threadIdx.x;
     bool any = false;
     if (s < M) {
-      const int64_t a = pwb[s * KW];
-      const int64_t b = s + 1 < M ? (int64_t)pwb[(s + 1) * KW] : nnz;
+      const int64_t a = (int32_t)FP[s * KW].y;
+      const int64_t b = s + 1 < M ? (int64_t)(int32_t)FP[(s + 1) * KW].y : nnz;
       f.row_ptr[s] = (int32_t)a;
       any = tile_cuts(s, a, b, nnz, f.T_row, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
     } else if (s == M) {
@@ -783,7 +763,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
   const int l = threadIdx.x & 31;
   const bool ok = tile < WM * KW;
   const int64_t rw = ok ? tile / KW : 0, wc = ok ? tile % KW : 0;
-  const uint32_t word = ok ? Fb[(rw * 32 + l) * KW + wc] : 0u;
+  const uint32_t word = ok ? FP[(rw * 32 + l) * KW + wc].x : 0u;
   uint32_t out = 0;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
@@ -812,21 +792,27 @@ __global__ __launch_bounds__(WT) void k_fp_tsum(const bm_state* st,
 }
 
 // Column view: one thread per FT word (column c, rows 32rw ..); rank of its
-// first entry = block base + block scan.
+// first entry = block base + block scan.  Word block tb holds columns
+// [tb*WT/WM, ...); workgroup b (dispatched to XCD b mod 8) takes word block
+// (b mod 8)*ceil(nbt/8) + b/8, so each XCD gathers the FP lines of one
+// contiguous column range.  A thread takes its entries four at a time, all
+// four FP loads in flight together.
 __global__ __launch_bounds__(WT) void k_fp_temit(
-    const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int32_t M, int32_t K,
-    const int4* __restrict__ tsum, const int4* __restrict__ toff,
-    const uint32_t* __restrict__ Fb, const int32_t* __restrict__ pwb, int64_t nnz, fuse_ptrs f) {
+    const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int64_t nbt, int32_t M,
+    int32_t K, const int4* __restrict__ tsum, const int4* __restrict__ toff,
+    const uint2* __restrict__ FP, int64_t nnz, fuse_ptrs f) {
   __shared__ int32_t lds[WT / SNK_WAVE];
   __shared__ int32_t red[WT / SNK_WAVE];
-  if (bm_failed(st)) return;
+  const int64_t per_xcd = cdiv_dev(nbt, NUM_XCD);
+  const int64_t tb = (int64_t)(blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
+  if (tb >= nbt || bm_failed(st)) return;
   const int t = threadIdx.x;
   int64_t base;
   if (toff) {
-    base = toff[blockIdx.x].x;
+    base = toff[tb].x;
   } else {
     int32_t sacc = 0;
-    for (int64_t i = t; i < (int64_t)blockIdx.x; i += WT) sacc += tsum[i].x;
+    for (int64_t i = t; i < tb; i += WT) sacc += tsum[i].x;
     for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off, SNK_WAVE);
     if (lane_id() == 0) red[t / SNK_WAVE] = sacc;
     __syncthreads();
@@ -834,7 +820,7 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
     for (int k = 0; k < WT / SNK_WAVE; ++k) base += red[k];
   }
   const int64_t KW = K >> 5, WM = M >> 5;
-  const int64_t i = (int64_t)blockIdx.x * WT + t;
+  const int64_t i = tb * WT + t;
   uint32_t word = i < NT ? FT[i] : 0u;
   int32_t tot;
   int64_t q = base + block_excl_scan_i32<WT>(__popc(word), lds, &tot);
@@ -842,16 +828,27 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
   const int64_t c = i / WM, rw = i - c * WM;
   if (rw == 0) f.col_ptr[c] = (int32_t)q;
   if (i == NT - 1) f.col_ptr[K] = (int32_t)nnz;
+  const uint32_t below = (1u << (c & 31)) - 1u;
   while (word) {
-    const int j = __ffs(word) - 1;
-    word &= word - 1;
-    if (q < nnz) {
-      const int64_t r = rw * 32 + j;
-      const int64_t pwi = r * KW + (c >> 5);
-      f.row_t[q] = (int32_t)r;
-      f.perm[q] = pwb[pwi] + __popc(Fb[pwi] & ((1u << (c & 31)) - 1u));
+    int j[4];
+    uint2 fp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      j[u] = word ? __ffs(word) - 1 : -1;
+      word &= word - 1;
     }
-    ++q;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      fp[u] = j[u] >= 0 ? FP[(rw * 32 + j[u]) * KW + (c >> 5)] : make_uint2(0u, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j[u] < 0) break;
+      if (q < nnz) {
+        f.row_t[q] = (int32_t)(rw * 32 + j[u]);
+        f.perm[q] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+      }
+      ++q;
+    }
   }
 }
 
@@ -892,7 +889,7 @@ __global__ __launch_bounds__(1024) void k_fp_result(const bm_state* st,
 struct bm_layout {
   int64_t nblk, W, nb, NT, nbt, rb, cbk;
   size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
-  size_t fb, pwb, ft, tsum, toff, rsplit, csplit, total;  // fused prepare
+  size_t fp, ft, tsum, toff, rsplit, csplit, total;  // fused prepare
 };
 
 bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
@@ -919,8 +916,7 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
   L.nbt = std::max<int64_t>(1, cdiv(L.NT, WT));
   L.rb = cdiv((int64_t)M + 1, FP_THREADS);
   L.cbk = cdiv((int64_t)K + 1, FP_THREADS);
-  L.fb = take(4 * (size_t)L.W);
-  L.pwb = take(4 * (size_t)L.W);
+  L.fp = take(8 * (size_t)L.W);
   L.ft = take(4 * (size_t)L.NT);
   L.tsum = take(16 * (size_t)L.nbt);
   L.toff = take(16 * (size_t)L.nbt);
@@ -972,8 +968,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   int32_t* res_dev = host_result_device(res_host);
   if (!res_host || !res_dev) return SNACK_E_HIP;
   res_host[0] = res_host[1] = res_host[2] = res_host[3] = INT32_MIN;
-  uint32_t* Fb = fuse ? (uint32_t*)(ws + L.fb) : nullptr;
-  int32_t* pwb = fuse ? (int32_t*)(ws + L.pwb) : nullptr;
+  uint2* FP = fuse ? (uint2*)(ws + L.fp) : nullptr;
 
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(4 * HREPL * 256, 256)), dim3(256), 0, s, st);
   const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
@@ -1007,7 +1002,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
   hipLaunchKernelGGL(k_bi_emit<T>, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
                      bsum, own_base ? nullptr : boff, vals_ws, K,
-                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, Fb, pwb, row,
+                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
                      col, vals, dropped_lin, grown_lin);
   if (fuse) {
     uint32_t* FT = (uint32_t*)(ws + L.ft);
@@ -1018,12 +1013,13 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     const int64_t tiles = (int64_t)(M / 32) * (K / 32);
     const int64_t tb = cdiv(tiles * 32, FP_THREADS);
     hipLaunchKernelGGL(k_fp_rows_transpose, dim3((unsigned)(L.rb + tb)), dim3(FP_THREADS), 0, s,
-                       st, Fb, pwb, M, K, nnz, *fuse, (int32_t)L.rb, rsplit, FT);
+                       st, FP, M, K, nnz, *fuse, (int32_t)L.rb, rsplit, FT);
     hipLaunchKernelGGL(k_fp_tsum, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, tsum);
     const bool own_t = L.nbt <= PREFIX_INBLOCK_MAX;
     if (!own_t) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, tsum, toff, L.nbt);
-    hipLaunchKernelGGL(k_fp_temit, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, M, K,
-                       tsum, own_t ? nullptr : toff, Fb, pwb, nnz, *fuse);
+    hipLaunchKernelGGL(k_fp_temit, dim3((unsigned)(NUM_XCD * cdiv(L.nbt, NUM_XCD))), dim3(WT),
+                       0, s, st, FT, L.NT, L.nbt, M, K, tsum, own_t ? nullptr : toff, FP, nnz,
+                       *fuse);
     hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
                        *fuse, csplit);
     hipLaunchKernelGGL(k_fp_result, dim3(1), dim3(1024), 0, s, st, rsplit, L.rb, csplit, L.cbk,
