@@ -24,6 +24,7 @@
 //            survivor's value being the old value at its rank in S.
 // One readback: the last kernel writes (error, positions missing) straight
 // into pinned host memory; row/col/vals are written only on success.
+#include <cmath>
 #include <cstdlib>
 
 #include "common.h"
@@ -144,10 +145,14 @@ __device__ __forceinline__ int32_t take_group(int64_t i0, int64_t stride, int64_
 }
 
 // Regrow chunk c (stream indices [start, start + rem), rem = positions still
-// missing after chunk c-1), spread over the whole grid.  A candidate is
-// taken when it lies outside S and its bit in G was clear.
+// missing after chunk c-1), spread over the rbn workgroups that call it (rbi:
+// this one's index among them).  A candidate is taken when it lies outside S
+// and its bit in G was clear.  The kernels that carry a chunk give it
+// workgroups of its own, so that its atomics (bound by the device's atomic
+// throughput) overlap the kernel's other work.
 __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, int32_t n_drop,
-                             const uint32_t* __restrict__ sup, uint32_t* __restrict__ grown) {
+                             const uint32_t* __restrict__ sup, uint32_t* __restrict__ grown,
+                             int64_t rbi, int64_t rbn) {
   __shared__ int32_t wsum[32];
   int64_t start = 0;
   int32_t rem = n_drop;
@@ -155,19 +160,19 @@ __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, 
     start = st->ch_start[c - 1] + st->ch_rem[c - 1];
     rem = st->ch_rem[c - 1] - chunk_taken(st, c - 1);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (rbi == 0 && threadIdx.x == 0) {
     st->ch_start[c] = start;
     st->ch_rem[c] = rem;
   }
   if (rem <= 0 || st->err) return;  // uniform over the grid
   if (start > STREAM_BOUND) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&st->err, 8);
+    if (rbi == 0 && threadIdx.x == 0) atomicOr(&st->err, 8);
     return;
   }
   int32_t acc = 0;
   const int64_t end = start + rem;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = start + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += 4 * stride)
+  const int64_t stride = rbn * blockDim.x;
+  for (int64_t i = start + rbi * blockDim.x + threadIdx.x; i < end; i += 4 * stride)
     acc += take_group(i, stride, end, stream, MK, sup, grown);
   // one atomic per block, spread over AREPL counters (same-address device
   // atomics serialise)
@@ -177,7 +182,7 @@ __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, 
   if (threadIdx.x == 0) {
     int32_t b = 0;
     for (int i = 0; i < (int)(blockDim.x / SNK_WAVE); ++i) b += wsum[i];
-    if (b) atomicAdd(&st->ch_acc[c][blockIdx.x % AREPL], b);
+    if (b) atomicAdd(&st->ch_acc[c][rbi % AREPL], b);
   }
 }
 
@@ -344,15 +349,20 @@ __global__ __launch_bounds__(BT) void k_bi_build(
 }
 
 // Select pass `pass` >= 1: pick the previous pass's digit, histogram the
-// next digit of the entries matching the prefix; then regrow chunk c.
+// next digit of the entries matching the prefix.  Workgroups from nblk on
+// run regrow chunk c.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64_t nnz,
-                                               int pass, int prev_shift, int shift,
+                                               int64_t nblk, int pass, int prev_shift, int shift,
                                                int32_t n_drop, int32_t c, uint64_t stream,
                                                uint64_t MK, bm_state* st,
                                                const uint32_t* __restrict__ sup,
                                                uint32_t* __restrict__ grown) {
   __shared__ int32_t h[256];
+  if ((int64_t)blockIdx.x >= nblk) {
+    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+    return;
+  }
   const int t = threadIdx.x;
   h[t] = 0;
   const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * t;
@@ -367,19 +377,23 @@ __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64
     wave_hist_add(h, (a[j] >> shift) & 255u, k0 + j < nnz && (a[j] & msk) == pfx);
   __syncthreads();
   if (h[t]) atomicAdd(&st->hist[pass][blockIdx.x % HREPL][t], h[t]);
-  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
 }
 
 // Last pick (the threshold magnitude tau and the ties to drop), entries at
-// tau per block; then regrow chunk c.
+// tau per block.  Workgroups from nblk on run regrow chunk c.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int64_t nnz,
-                                                 int last_pass, int shift, int32_t n_drop,
-                                                 int32_t c, uint64_t stream, uint64_t MK,
-                                                 bm_state* st, int32_t* __restrict__ cnt_eq,
+                                                 int64_t nblk, int last_pass, int shift,
+                                                 int32_t n_drop, int32_t c, uint64_t stream,
+                                                 uint64_t MK, bm_state* st,
+                                                 int32_t* __restrict__ cnt_eq,
                                                  const uint32_t* __restrict__ sup,
                                                  uint32_t* __restrict__ grown) {
   __shared__ int32_t lds[BT / SNK_WAVE];
+  if ((int64_t)blockIdx.x >= nblk) {
+    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+    return;
+  }
   const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * threadIdx.x;
   uint32_t a[4];
 #pragma unroll
@@ -394,7 +408,6 @@ __global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int
   int32_t tot;
   block_excl_scan_i32<BT>(eq, lds, &tot);
   if (threadIdx.x == 0) cnt_eq[blockIdx.x] = tot;
-  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
 }
 
 // One workgroup: base_eq[b] = entries at tau in blocks before b (used when
@@ -428,11 +441,13 @@ __device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ 
 }
 
 // Dropped bitmap D: entry k is dropped if its magnitude is below tau, or at
-// tau with tie rank (index order) below need.  Then regrow chunk c.
+// tau with tie rank (index order) below need.  Workgroups from nblk on run
+// regrow chunk c.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_drop(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
-    int64_t nnz, int32_t M, int32_t K, int64_t W, int last_pass, const int32_t* __restrict__ cnt_eq,
+    int64_t nnz, int64_t nblk, int32_t M, int32_t K, int64_t W, int last_pass,
+    const int32_t* __restrict__ cnt_eq,
     const int32_t* __restrict__ base_eq, int32_t n_drop, int32_t c, uint64_t stream, uint64_t MK,
     bm_state* st, uint32_t* __restrict__ dropb, const uint32_t* __restrict__ sup,
     uint32_t* __restrict__ grown) {
@@ -441,6 +456,10 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
   __shared__ int64_t edge_s, whi_s;
   __shared__ int64_t nxt[NEXT];
   __shared__ uint32_t nxt_mag[NEXT];
+  if ((int64_t)blockIdx.x >= nblk) {
+    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+    return;
+  }
   const int t = threadIdx.x;
   const uint32_t tau = st->pfx[last_pass];
   const int32_t need = st->need[last_pass];
@@ -492,7 +511,6 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
     }
   }
   write_block_words(buf, w_lo, w_hi, l, f, extra, dropb, nullptr);
-  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
 }
 
 // A regrow chunk on its own (only when the acceptance rate is low).
@@ -500,7 +518,7 @@ __global__ __launch_bounds__(BT) void k_bi_chunk(int32_t c, uint64_t stream, uin
                                                  int32_t n_drop, bm_state* st,
                                                  const uint32_t* __restrict__ sup,
                                                  uint32_t* __restrict__ grown) {
-  regrow_chunk(st, c, stream, MK, n_drop, sup, grown);
+  regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, gridDim.x);
 }
 
 // One workgroup: chunks after grid chunk c-1 until nothing is missing (or
@@ -617,6 +635,8 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   if (blockIdx.x == 0 && t == 0) {
     result[0] = err;
     result[1] = missing;
+    result[2] = 0;  // split flags of a fused prepare, set by later kernels
+    result[3] = 0;
   }
   if (err || missing > 0) return;
   // block base: the sum of the sums of earlier blocks
@@ -735,11 +755,12 @@ __device__ __forceinline__ bool bm_failed(const bm_state* st) {
 
 constexpr int FP_THREADS = 256;
 
-// Blocks [0, rb): row offsets and row tiles, thread per row s in [0, M].
-// Blocks [rb, ..): bit transpose, two 32 x 32 tiles per wave.
+// Blocks [0, rb): row offsets and row tiles, thread per row s in [0, M]; a
+// block with a split row sets res[2] (pinned host memory, cleared by the
+// emitter).  Blocks [rb, ..): bit transpose, two 32 x 32 tiles per wave.
 __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
     const bm_state* st, const uint2* __restrict__ FP,
-    int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ rsplit,
+    int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ res,
     uint32_t* __restrict__ FT) {
   if (bm_failed(st)) return;
   const int64_t KW = K >> 5, WM = M >> 5;
@@ -756,7 +777,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
       tile_close(M, nnz, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
     }
     const int any_b = __syncthreads_or(any ? 1 : 0);
-    if (threadIdx.x == 0) rsplit[blockIdx.x] = any_b ? 1 : 0;
+    if (threadIdx.x == 0 && any_b) res[2] = 1;
     return;
   }
   const int64_t tile = ((int64_t)(blockIdx.x - rb) * FP_THREADS + threadIdx.x) >> 5;
@@ -796,16 +817,20 @@ __global__ __launch_bounds__(WT) void k_fp_tsum(const bm_state* st,
 // [tb*WT/WM, ...); workgroup b (dispatched to XCD b mod 8) takes word block
 // (b mod 8)*ceil(nbt/8) + b/8, so each XCD gathers the FP lines of one
 // contiguous column range.  A thread takes its entries four at a time, all
-// four FP loads in flight together.
+// four FP loads in flight together.  With cols_here (WM divides WT, so a
+// block holds whole columns) the block also writes the column tiles of its
+// columns and sets res[3] if one of them is split.
 __global__ __launch_bounds__(WT) void k_fp_temit(
     const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int64_t nbt, int32_t M,
     int32_t K, const int4* __restrict__ tsum, const int4* __restrict__ toff,
-    const uint2* __restrict__ FP, int64_t nnz, fuse_ptrs f) {
+    const uint2* __restrict__ FP, int64_t nnz, fuse_ptrs f, int32_t cols_here,
+    int32_t* __restrict__ res) {
   __shared__ int32_t lds[WT / SNK_WAVE];
   __shared__ int32_t red[WT / SNK_WAVE];
+  __shared__ int32_t cstart[WT];
   const int64_t per_xcd = cdiv_dev(nbt, NUM_XCD);
   const int64_t tb = (int64_t)(blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
-  if (tb >= nbt || bm_failed(st)) return;
+  if (tb >= nbt || bm_failed(st)) return;  // uniform over the block
   const int t = threadIdx.x;
   int64_t base;
   if (toff) {
@@ -821,13 +846,33 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
   }
   const int64_t KW = K >> 5, WM = M >> 5;
   const int64_t i = tb * WT + t;
-  uint32_t word = i < NT ? FT[i] : 0u;
+  const bool valid = i < NT;
+  uint32_t word = valid ? FT[i] : 0u;
   int32_t tot;
   int64_t q = base + block_excl_scan_i32<WT>(__popc(word), lds, &tot);
-  if (i >= NT) return;
   const int64_t c = i / WM, rw = i - c * WM;
-  if (rw == 0) f.col_ptr[c] = (int32_t)q;
-  if (i == NT - 1) f.col_ptr[K] = (int32_t)nnz;
+  const int64_t c0 = tb * WT / WM;  // first column of the block (cols_here)
+  if (valid && rw == 0) {
+    f.col_ptr[c] = (int32_t)q;
+    if (cols_here) cstart[c - c0] = (int32_t)q;
+  }
+  if (valid && i == NT - 1) {
+    f.col_ptr[K] = (int32_t)nnz;
+    if (cols_here) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
+  }
+  if (cols_here) {  // the tiles of the block's columns, before the entries
+    __syncthreads();
+    const int64_t ncol = WT / WM;
+    const int64_t s = c0 + t;
+    bool any = false;
+    if (t < ncol && s < K) {
+      const int64_t a = cstart[t];
+      const int64_t b = (t + 1 < ncol && s + 1 < K) ? (int64_t)cstart[t + 1] : base + tot;
+      any = tile_cuts(s, a, b, nnz, f.T_col, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
+    }
+    if (__ballot(any) != 0 && lane_id() == 0) res[3] = 1;
+  }
+  if (!valid) return;
   const uint32_t below = (1u << (c & 31)) - 1u;
   while (word) {
     int j[4];
@@ -852,10 +897,11 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
   }
 }
 
-// Column tiles, thread per column s in [0, K].
+// Column tiles, thread per column s in [0, K] (shapes whose columns straddle
+// the emitter's word blocks); a block with a split column sets res[3].
 __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int32_t K,
                                                         int64_t nnz, fuse_ptrs f,
-                                                        int32_t* __restrict__ csplit) {
+                                                        int32_t* __restrict__ res) {
   if (bm_failed(st)) return;
   const int64_t s = (int64_t)blockIdx.x * FP_THREADS + threadIdx.x;
   bool any = false;
@@ -863,33 +909,14 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int3
                              f.cpart_seg, f.cpart_nz, f.ccut);
   else if (s == K) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
   const int any_b = __syncthreads_or(any ? 1 : 0);
-  if (threadIdx.x == 0) csplit[blockIdx.x] = any_b ? 1 : 0;
-}
-
-// One workgroup: the split flags of both views into pinned host memory
-// (res[2], res[3]).
-__global__ __launch_bounds__(1024) void k_fp_result(const bm_state* st,
-                                                    const int32_t* __restrict__ rsplit,
-                                                    int64_t n_r, const int32_t* __restrict__ csplit,
-                                                    int64_t n_c, int32_t* __restrict__ res) {
-  int32_t r = 0, c = 0;
-  if (!bm_failed(st)) {
-    for (int64_t i = threadIdx.x; i < n_r; i += 1024) r |= rsplit[i];
-    for (int64_t i = threadIdx.x; i < n_c; i += 1024) c |= csplit[i];
-  }
-  r = __syncthreads_or(r);
-  c = __syncthreads_or(c);
-  if (threadIdx.x == 0) {
-    res[2] = r ? 1 : 0;
-    res[3] = c ? 1 : 0;
-  }
+  if (threadIdx.x == 0 && any_b) res[3] = 1;
 }
 
 // ------------------------------------------------------------------ host
 struct bm_layout {
   int64_t nblk, W, nb, NT, nbt, rb, cbk;
   size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
-  size_t fp, ft, tsum, toff, rsplit, csplit, total;  // fused prepare
+  size_t fp, ft, tsum, toff, total;  // fused prepare
 };
 
 bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
@@ -920,8 +947,6 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
   L.ft = take(4 * (size_t)L.NT);
   L.tsum = take(16 * (size_t)L.nbt);
   L.toff = take(16 * (size_t)L.nbt);
-  L.rsplit = take(4 * (size_t)L.rb);
-  L.csplit = take(4 * (size_t)L.cbk);
   L.total = o;
   return L;
 }
@@ -930,8 +955,12 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
 // kernels, plus stand-alone ones while the expected remainder
 // n_drop * (1 - q)^c stays above what one workgroup finishes quickly (q: a
 // lower bound on the acceptance rate).
+double accept_bound(int64_t MK, int64_t nnz, int64_t n_drop) {
+  return std::max(0.5, 1.0 - (double)(nnz + n_drop) / (double)MK);
+}
+
 int32_t grid_chunks(int64_t MK, int64_t nnz, int64_t n_drop, int32_t riding) {
-  const double q = std::max(0.5, 1.0 - (double)(nnz + n_drop) / (double)MK);
+  const double q = accept_bound(MK, nnz, n_drop);
   int32_t c = riding;
   double rem = (double)n_drop;
   for (int i = 0; i < riding; ++i) rem *= 1.0 - q;
@@ -977,19 +1006,27 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   const int top = 8 * (passes - 1);
   hipLaunchKernelGGL(k_bi_build<T>, eb, et, 0, s, row, col, vals, nnz, M, K, L.W, top, vec_ok, st,
                      sup, grown, vals_ws);
+  // entry workgroups plus the workgroups of regrow chunk c, sized for the
+  // positions expected to be missing at its start
+  const double q = accept_bound((int64_t)MK, nnz, n_drop);
+  auto with_chunk = [&](int32_t c) {
+    const double rem = (double)n_drop * std::pow(1.0 - q, (double)c);
+    const int64_t rb = std::min<int64_t>(1024, std::max<int64_t>(1, (int64_t)(rem / (4 * BT)) + 1));
+    return dim3((unsigned)(L.nblk + rb));
+  };
   int32_t c = 0;
   for (int p = 1; p < passes; ++p, ++c)
-    hipLaunchKernelGGL(k_bi_sel<T>, eb, et, 0, s, vals, nnz, p, top - 8 * (p - 1), top - 8 * p,
-                       nd, c, stream, MK, st, sup, grown);
-  hipLaunchKernelGGL(k_bi_count<T>, eb, et, 0, s, vals, nnz, passes - 1, 0, nd, c, stream, MK, st,
-                     cnt_eq, sup, grown);
+    hipLaunchKernelGGL(k_bi_sel<T>, with_chunk(c), et, 0, s, vals, nnz, L.nblk, p,
+                       top - 8 * (p - 1), top - 8 * p, nd, c, stream, MK, st, sup, grown);
+  hipLaunchKernelGGL(k_bi_count<T>, with_chunk(c), et, 0, s, vals, nnz, L.nblk, passes - 1, 0, nd,
+                     c, stream, MK, st, cnt_eq, sup, grown);
   ++c;
   const bool own_prefix = L.nblk <= PREFIX_INBLOCK_MAX;
   if (!own_prefix)
     hipLaunchKernelGGL(k_bi_eq_scan, dim3(1), dim3(1024), 0, s, cnt_eq, base_eq, L.nblk);
-  hipLaunchKernelGGL(k_bi_drop<T>, eb, et, 0, s, row, col, vals, nnz, M, K, L.W, passes - 1,
-                     cnt_eq, own_prefix ? nullptr : base_eq, nd, c, stream, MK, st, dropb, sup,
-                     grown);
+  hipLaunchKernelGGL(k_bi_drop<T>, with_chunk(c), et, 0, s, row, col, vals, nnz, L.nblk, M, K,
+                     L.W, passes - 1, cnt_eq, own_prefix ? nullptr : base_eq, nd, c, stream, MK,
+                     st, dropb, sup, grown);
   ++c;
   const int32_t total = grid_chunks((int64_t)MK, nnz, n_drop, c);
   const unsigned cb = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(n_drop, BT)));
@@ -1008,22 +1045,20 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     uint32_t* FT = (uint32_t*)(ws + L.ft);
     int4* tsum = (int4*)(ws + L.tsum);
     int4* toff = (int4*)(ws + L.toff);
-    int32_t* rsplit = (int32_t*)(ws + L.rsplit);
-    int32_t* csplit = (int32_t*)(ws + L.csplit);
     const int64_t tiles = (int64_t)(M / 32) * (K / 32);
     const int64_t tb = cdiv(tiles * 32, FP_THREADS);
     hipLaunchKernelGGL(k_fp_rows_transpose, dim3((unsigned)(L.rb + tb)), dim3(FP_THREADS), 0, s,
-                       st, FP, M, K, nnz, *fuse, (int32_t)L.rb, rsplit, FT);
+                       st, FP, M, K, nnz, *fuse, (int32_t)L.rb, res_dev, FT);
     hipLaunchKernelGGL(k_fp_tsum, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, tsum);
     const bool own_t = L.nbt <= PREFIX_INBLOCK_MAX;
     if (!own_t) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, tsum, toff, L.nbt);
+    const int32_t cols_here = (WT % (M / 32)) == 0 ? 1 : 0;
     hipLaunchKernelGGL(k_fp_temit, dim3((unsigned)(NUM_XCD * cdiv(L.nbt, NUM_XCD))), dim3(WT),
                        0, s, st, FT, L.NT, L.nbt, M, K, tsum, own_t ? nullptr : toff, FP, nnz,
-                       *fuse);
-    hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
-                       *fuse, csplit);
-    hipLaunchKernelGGL(k_fp_result, dim3(1), dim3(1024), 0, s, st, rsplit, L.rb, csplit, L.cbk,
-                       res_dev);
+                       *fuse, cols_here, res_dev);
+    if (!cols_here)
+      hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
+                         *fuse, res_dev);
   }
   if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
     return SNACK_E_HIP;
