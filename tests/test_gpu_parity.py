@@ -153,6 +153,9 @@ SMALL = [  # (M, K, nnz, B, dtype, layout, tile)
     (100, 333, 8000, 64, "f32", "node", 0),
     (100, 333, 8000, 5, "bf16", "batch", 1),
     (1000, 3, 2500, 16, "bf16", "node", 128),
+    # tiles of >= 256 items (column view with deferred values), columns split
+    (2000, 2, 3000, 8, "bf16", "node", 256),
+    (2000, 3, 5000, 5, "f32", "batch", 512),
 ]
 
 
