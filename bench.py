@@ -259,6 +259,30 @@ def dense_baselines(wt, X, batches, rotate=8):
     return out
 
 
+def snk_drop(nnz, ppm):
+    import unstructured_sparse_nn_amd as snk
+    return snk.snack_drop_count(nnz, ppm)
+
+
+def footprint(N, nnz, B, n_drop, layout):
+    """Device bytes of the benchmarked layer (sparse, with its plan and
+    restructuring workspace) against the same layer dense and Dense+Mask
+    (snack_memory_footprint), plus the 90%-sparse fp32 point of the same
+    shape without restructuring."""
+    import synth
+    import unstructured_sparse_nn_amd as snk
+    flags = snk.binding.PLAN_NODE_MAJOR_ONLY if layout == "node" else 0
+    out = {}
+    for key, (nz, dt, b, nd, fl) in {
+            "bench_layer": (nnz, snk.BF16, B, n_drop, flags),
+            "fp32_90pct_no_restructure": (synth.nnz_for(N, N, 0.9), snk.F32, 1, 0, 0)}.items():
+        f = snk.snack_memory_footprint(N, N, nz, b, dt, nd, fl)
+        f["sparse_vs_dense"] = round(f["sparse_total"] / f["dense_total"], 4)
+        f["sparse_vs_masked"] = round(f["sparse_total"] / f["masked_total"], 4)
+        out[key] = f
+    return out
+
+
 def cpu_baseline(w, X, dY, B, drop_ppm, seconds):
     """The fp64 oracle, serial on one host core, running the same step on the
     same layer, repeated until `seconds` of CPU work."""
@@ -471,6 +495,8 @@ def run_bench(args):
             del ib
             torch.cuda.empty_cache()
         rec["baselines"] = base
+    rec["footprint"] = footprint(N, wt.nnz, B, 0 if args.products_only else
+                                 snk_drop(wt.nnz, args.drop_ppm), args.layout)
     if args.cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(wt, w.X[0], w.dY[0], B, args.drop_ppm,

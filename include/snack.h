@@ -284,6 +284,43 @@ SNACK_API snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* ro
                                          void* stream);
 
 /*
+ * snack_memory_footprint -- host only: device bytes of one layer, held
+ * against the same layer stored dense and as Dense+Mask (the memory
+ * comparison of the SNACK abstract, which reports a sparse layer at 90%
+ * sparsity using far less memory than a dense one).  For an M x K layer
+ * with nnz connections of element size s (dtype), product calls up to
+ * max_batch, plan flags plan_flags (as snack_plan_init, tile size automatic)
+ * and restructuring steps of n_drop connections (0: no restructuring):
+ *   coo            row, col (int32) and values: nnz * (8 + s)
+ *   value_grad     the value gradient dV: nnz * s
+ *   derived        the arrays a prepared plan keeps (row offsets, column
+ *                  view, tiles and cut flags of both views)
+ *   plan_scratch   the rest of the plan arena (sort buffers of prepare,
+ *                  carry slots, node-major copies of activations)
+ *   restructure_ws snack_prune_regrow_workspace(M, K, nnz, n_drop), or 0
+ *   sparse_total   the sum of the five above
+ *   dense_weight, dense_grad   M * K * s each; dense_total their sum
+ *   mask           a uint8 mask of the Dense+Mask layer: M * K
+ *   masked_total   dense_total + mask
+ *   activations    X, Y and their gradients at max_batch, the same for
+ *                  all three layers: 2 * max_batch * (M + K) * s
+ * No optimiser state is counted (the in-place SGD step of
+ * snack_spmm_bwd_fused keeps none).  Errors: as snack_plan_init and
+ * snack_prune_regrow_workspace, SNACK_E_DTYPE, SNACK_E_COUNT.
+ */
+typedef struct snack_footprint {
+  uint64_t coo, value_grad, derived, plan_scratch, restructure_ws, sparse_total;
+  uint64_t dense_weight, dense_grad, dense_total;
+  uint64_t mask, masked_total;
+  uint64_t activations;
+} snack_footprint;
+
+SNACK_API snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz,
+                                              int32_t max_batch, snack_dtype dtype,
+                                              int64_t n_drop, uint32_t plan_flags,
+                                              snack_footprint* out);
+
+/*
  * GELU with the exact error function, h = z * Phi(z), and its backward
  * dz = dh * (Phi(z) + z * phi(z)), elementwise over n fp32 values (the
  * nonlinearity between the two sparse layers of a GPT-2-shaped MLP block).

@@ -207,3 +207,24 @@ def prune_regrow(M, K, row, col, vals, dtype, n_drop, seed, step):
     ov = ovb.astype(np.uint16) if dtype == "bf16" else ovb.view(np.float32)
     return {"rc": 0, "row": orow, "col": ocol, "vals": ov, "dropped": dl[:n_drop].copy(),
             "grown": gl[:n_drop].copy()}
+
+
+def memory_by_definition(M: int, K: int, nnz: int, elem_bytes: int, max_batch: int) -> dict:
+    """Bytes of the tensors whose size the layer's definition fixes (SNACK
+    abstract: the sparse layer stores only its nonzero connections; the
+    baselines store a dense weight, Dense+Mask adds a mask): element counts
+    times element sizes.  The COO holds two int32 indices and one value per
+    connection; the value gradient one value per connection; the dense layer
+    a weight and a gradient of M*K values; the mask one byte per weight;
+    the activations X (B x K), Y (B x M) and their gradients at B =
+    max_batch.  Plan and workspace sizes belong to the implementation, not
+    to the definition, and are not computed here."""
+    mk = M * K
+    return {
+        "coo": nnz * (4 + 4 + elem_bytes),
+        "value_grad": nnz * elem_bytes,
+        "dense_weight": mk * elem_bytes,
+        "dense_grad": mk * elem_bytes,
+        "mask": mk,
+        "activations": max_batch * (K + M) * elem_bytes * 2,
+    }

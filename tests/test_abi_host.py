@@ -120,3 +120,50 @@ def test_status_strings(snk):
     from unstructured_sparse_nn_amd import binding as b
     for code in b.STATUS:
         assert snk.status_str(code) and snk.status_str(code) != "unknown status"
+
+
+# ---------------------------------------------------------------- footprint
+FOOTPRINT_CASES = [  # (M, K, nnz, max_batch, dtype, n_drop, flags)
+    (4096, 4096, 1677722, 1, "f32", 0, 0),        # 90%: the abstract's single-layer point
+    (4096, 4096, 838861, 32, "bf16", 251658, 1),  # 95%, restructuring 30%
+    (3072, 768, 235930, 1024, "f32", 70779, 0),   # GPT-2 MLP projection at 90%
+    (256, 256, 6554, 4, "f32", 655, 0),
+    (1, 1, 0, 1, "bf16", 0, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,B,dt,n_drop,flags", FOOTPRINT_CASES)
+def test_memory_footprint_matches_definitions_and_allocations(snk, M, K, nnz, B, dt, n_drop,
+                                                              flags):
+    import oracle
+    d = snk.F32 if dt == "f32" else snk.BF16
+    s = 4 if dt == "f32" else 2
+    f = snk.snack_memory_footprint(M, K, nnz, B, d, n_drop, flags)
+    ref = oracle.memory_by_definition(M, K, nnz, s, B)
+    for k, v in ref.items():
+        assert f[k] == v, k
+    # the implementation's parts are exactly what the library asks callers for
+    plan = snk.snack_plan_init(M, K, nnz, B, 0, flags)
+    assert f["derived"] + f["plan_scratch"] == plan.arena_bytes
+    assert f["derived"] == plan.off[10]  # derived arrays precede the scratch
+    ws = snk.snack_prune_regrow_workspace(M, K, nnz, n_drop) if n_drop else 0
+    assert f["restructure_ws"] == ws
+    assert f["sparse_total"] == (f["coo"] + f["value_grad"] + f["derived"] + f["plan_scratch"]
+                                 + f["restructure_ws"])
+    assert f["dense_total"] == f["dense_weight"] + f["dense_grad"]
+    assert f["masked_total"] == f["dense_total"] + f["mask"]
+
+
+def test_memory_footprint_rejects_bad_arguments(snk):
+    from unstructured_sparse_nn_amd import binding as B
+    st = B.raw_status
+    out = B.SnackFootprint()
+    ref = ctypes.byref(out)
+    assert st("snack_memory_footprint", 64, 64, 10, 1, 0, 0, 0, None) == -1
+    assert st("snack_memory_footprint", 64, 64, 10, 1, 7, 0, 0, ref) == -3
+    assert st("snack_memory_footprint", 0, 64, 10, 1, 0, 0, 0, ref) == -2
+    assert st("snack_memory_footprint", 64, 64, 10, 0, 0, 0, 0, ref) == -2
+    assert st("snack_memory_footprint", 64, 64, 10, 1, 0, -1, 0, ref) == -2
+    assert st("snack_memory_footprint", 64, 64, 10, 1, 0, 11, 0, ref) == -8
+    assert st("snack_memory_footprint", 4, 4, 10, 1, 0, 7, 0, ref) == -8
+    assert st("snack_memory_footprint", 64, 64, 10, 1, 0, 0, 8, ref) == -4

@@ -590,3 +590,36 @@ def test_sparse_linear_autograd(orc):
     ref = orc.prune_regrow(256, 256, wt.row, wt.col, wt.vals, "f32", 655, 0, 1)
     assert np.array_equal(grown.cpu().numpy(), ref["grown"])
     assert np.array_equal(layer.topo.row.cpu().numpy(), ref["row"])
+
+
+# ------------------------------------------------------------ memory footprint
+@pytest.mark.parametrize("dt,n_drop_ppm,flags", [("f32", 0, 0), ("bf16", 300000, 1)])
+def test_memory_footprint_matches_device_allocations(dt, n_drop_ppm, flags):
+    """The sparse layer's reported bytes are what its device tensors take:
+    COO, value gradient, plan arena and restructuring workspace, allocated the
+    way the layer allocates them (torch counts each allocation rounded up to
+    512 bytes)."""
+    N, sp, Bsz = 2048, 0.9, 8
+    M = K = N
+    w = synth.inference_layer(N=N, sparsity=sp, B=Bsz, dtype=dt).weights[0]
+    d = snk.F32 if dt == "f32" else snk.BF16
+    n_drop = snk.snack_drop_count(w.nnz, n_drop_ppm)
+    f = snk.snack_memory_footprint(M, K, w.nnz, Bsz, d, n_drop, flags)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    row, col = to_dev(w.row), to_dev(w.col)
+    vals = to_dev(w.vals, dt)
+    dV = torch.empty_like(vals)
+    topo = snk.Topology(row, col, M, K, Bsz, flags=flags)
+    ws = torch.empty(f["restructure_ws"], dtype=torch.uint8, device="cuda") if n_drop else None
+    torch.cuda.synchronize()
+    used = torch.cuda.memory_allocated() - before
+    r512 = lambda n: -(-n // 512) * 512  # noqa: E731
+    expect = (r512(4 * w.nnz) * 2 + r512(vals.element_size() * w.nnz) * 2
+              + r512(f["derived"] + f["plan_scratch"]) + (r512(f["restructure_ws"]) if n_drop else 0))
+    assert used == expect
+    assert f["coo"] + f["value_grad"] == 4 * w.nnz * 2 + vals.element_size() * w.nnz * 2
+    assert topo.arena.numel() == f["derived"] + f["plan_scratch"]
+    if n_drop:  # the workspace suffices for the restructure it was sized for
+        topo.restructure(vals, n_drop, 0, 1, ws=ws)
+    del row, col, vals, dV, topo, ws

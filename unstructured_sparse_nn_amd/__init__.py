@@ -8,7 +8,7 @@ PyTorch only provides device memory and streams.
 """
 from .binding import (BATCH_MAJOR, BF16, F32, NODE_MAJOR, SnackError, SnackPlan,  # noqa: F401
                       snack_coo_prepare, snack_dense_fwd, snack_drop_count, snack_gelu_bwd,
-                      snack_gelu_fwd, snack_plan_array, snack_plan_init, snack_plan_sizeof,
+                      snack_gelu_fwd, snack_memory_footprint, snack_plan_array, snack_plan_init, snack_plan_sizeof,
                       snack_prune_regrow, snack_prune_regrow_prepared,
                       snack_prune_regrow_workspace, snack_sddmm_grad_vals,
                       snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd, snack_version,

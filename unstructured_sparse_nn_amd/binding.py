@@ -37,6 +37,16 @@ class SnackError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)})")
 
 
+FOOTPRINT_FIELDS = ("coo", "value_grad", "derived", "plan_scratch", "restructure_ws",
+                    "sparse_total", "dense_weight", "dense_grad", "dense_total", "mask",
+                    "masked_total", "activations")
+
+
+class SnackFootprint(ctypes.Structure):
+    """Mirror of ``struct snack_footprint``."""
+    _fields_ = [(f, ctypes.c_uint64) for f in FOOTPRINT_FIELDS]
+
+
 class SnackPlan(ctypes.Structure):
     """Mirror of ``struct snack_plan``."""
     _fields_ = [("M", ctypes.c_int32), ("K", ctypes.c_int32), ("nnz", ctypes.c_int64),
@@ -73,6 +83,8 @@ def _load():
         "snack_prune_regrow": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz, P], i32),
         "snack_prune_regrow_prepared": ([plan_p, P, P, P, i32, i64, u64, u64, P, P, P, sz, P],
                                         i32),
+        "snack_memory_footprint": ([i32, i32, i64, i32, i32, i64, ctypes.c_uint32,
+                                    ctypes.POINTER(SnackFootprint)], i32),
         "snack_gelu_fwd": ([P, P, i64, P], i32),
         "snack_gelu_bwd": ([P, P, P, i64, P], i32),
         "snack_dense_fwd": ([P, P, i32, i32, i32, P, i32, P, P], i32),
@@ -222,6 +234,16 @@ def snack_prune_regrow_prepared(plan, row, col, vals, n_drop, seed, step, droppe
                                             _ptr(dropped_lin), _ptr(grown_lin), _ptr(ws),
                                             ws_bytes, _stream(stream)),
            "snack_prune_regrow_prepared")
+
+
+def snack_memory_footprint(M: int, K: int, nnz: int, max_batch: int, dtype: int, n_drop: int = 0,
+                           plan_flags: int = 0) -> dict:
+    """Device bytes of the sparse layer, the dense layer and Dense+Mask (a dict
+    with the fields of ``struct snack_footprint``)."""
+    out = SnackFootprint()
+    _check(_lib.snack_memory_footprint(M, K, nnz, max_batch, dtype, n_drop, plan_flags,
+                                       ctypes.byref(out)), "snack_memory_footprint")
+    return {f: int(getattr(out, f)) for f in FOOTPRINT_FIELDS}
 
 
 def snack_gelu_fwd(z, h, n=None, stream=None):

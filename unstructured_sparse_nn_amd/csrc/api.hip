@@ -345,6 +345,40 @@ snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int
   return SNACK_OK;
 }
 
+snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz, int32_t max_batch,
+                                    snack_dtype dtype, int64_t n_drop, uint32_t plan_flags,
+                                    snack_footprint* out) {
+  if (!out) return SNACK_E_NULL;
+  if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  snack_plan plan;
+  const snack_status st = snack_plan_init(&plan, M, K, nnz, max_batch, 0, plan_flags);
+  if (st != SNACK_OK) return st;
+  if (n_drop < 0) return SNACK_E_SHAPE;
+  if (n_drop > nnz || n_drop > (int64_t)M * K - nnz) return SNACK_E_COUNT;
+  size_t ws = 0;
+  if (n_drop > 0) {
+    const snack_status sw = snack_prune_regrow_workspace(M, K, nnz, n_drop, &ws);
+    if (sw != SNACK_OK) return sw;
+  }
+  const uint64_t s = dtype == SNACK_F32 ? 4 : 2;
+  const uint64_t mk = (uint64_t)M * (uint64_t)K;
+  snack_footprint f;
+  f.coo = (uint64_t)nnz * (8 + s);
+  f.value_grad = (uint64_t)nnz * s;
+  f.derived = plan.off[S_CARRY];  // the derived arrays come first in the arena
+  f.plan_scratch = plan.arena_bytes - f.derived;
+  f.restructure_ws = ws;
+  f.sparse_total = f.coo + f.value_grad + f.derived + f.plan_scratch + f.restructure_ws;
+  f.dense_weight = mk * s;
+  f.dense_grad = mk * s;
+  f.dense_total = f.dense_weight + f.dense_grad;
+  f.mask = mk;
+  f.masked_total = f.dense_total + f.mask;
+  f.activations = 2 * (uint64_t)max_batch * ((uint64_t)M + (uint64_t)K) * s;
+  *out = f;
+  return SNACK_OK;
+}
+
 snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
                                 int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
                                 uint64_t seed, uint64_t step, int64_t* dropped_lin,

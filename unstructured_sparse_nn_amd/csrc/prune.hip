@@ -432,10 +432,10 @@ bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz) {
   return prune_bitmap_ok(M, K, nnz);
 }
 
+// The workspace of the plan that will run (the same choice as the calls).
 size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) {
-  size_t b = make_layout(M, K, nnz, n_drop).total;
-  if (prune_bitmap_ok(M, K, nnz)) b = std::max(b, prune_bitmap_ws_bytes(M, K, nnz));
-  return b;
+  if (use_bitmap_plan(M, K, nnz)) return prune_bitmap_ws_bytes(M, K, nnz);
+  return make_layout(M, K, nnz, n_drop).total;
 }
 
 template <typename T>
