@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--grid", action=argparse.BooleanOptionalAction, default=True,
                     help="also time fwd/dX/dV at 95/99%% x B in {1,8,32}")
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="time multi-layer graph inference (power-law graphs, fused GELU)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--restructure", choices=("fused", "separate"), default="fused",
                     help="prune/regrow + prepare as one call (snack_prune_regrow_prepared) or "
@@ -255,6 +257,115 @@ def dense_baselines(wt, X, batches, rotate=8):
             out[f"{kind}_B{B}"] = {"us": round(us, 2), "bytes": nbytes,
                                    "GBps": round(nbytes / us / 1e3, 1)}
     del Wd, Md
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_calls(fn, reps=10, warm=3):
+    """Mean microseconds of fn() between HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def graph_inference(layers=3):
+    """Multi-layer graph-style inference, H <- GELU(A H) `layers` times with A a
+    synthetic power-law adjacency (random-walk weights) and 128 fp32 node-major
+    features: (1) the 200,000-node, 2,400,000-edge graph, activation fused into
+    the propagation (snack_graph_propagate) against a separate GELU pass;
+    (2) a 16,384-node graph at 99% sparsity against the in-repo Dense+Mask and
+    dense kernels on the same graph (snack_dense_fwd + snack_gelu_fwd per
+    layer, batch-major)."""
+    import torch
+    import synth
+    import unstructured_sparse_nn_amd as snk
+    out = {}
+    NM, F32, GELU = snk.NODE_MAJOR, snk.F32, snk.ACT_GELU
+
+    def sparse_setup(wl):
+        w, X = wl.weights[0], wl.X[0]
+        topo = snk.Topology(to_dev(w.row), to_dev(w.col), w.M, w.K, wl.B,
+                            flags=snk.binding.PLAN_NODE_MAJOR_ONLY)
+        return w, topo, to_dev(w.vals), to_dev(X.data)
+
+    def layer_bytes(w, Bsz):  # index + value per edge, offsets, H in and out (fp32)
+        return w.nnz * 8 + 4 * (w.M + 1) + 2 * w.M * Bsz * 4
+
+    log("graph inference: 200k nodes")
+    wl = synth.graph_layer()
+    w, topo, vals, X = sparse_setup(wl)
+    Y, tmp, Z = torch.empty_like(X), torch.empty_like(X), torch.empty_like(X)
+
+    def fused(act=GELU):
+        snk.snack_graph_propagate(topo.plan, vals, X, NM, wl.B, layers, act, Y, tmp)
+
+    def separate():
+        src = X
+        for l in range(layers):
+            dst = Y if (layers - 1 - l) % 2 == 0 else tmp
+            snk.snack_spmm_fwd(topo.plan, vals, src, NM, wl.B, Z)
+            snk.snack_gelu_fwd(Z, dst)
+            src = dst
+
+    uf, us = time_calls(fused), time_calls(separate)
+    un = time_calls(lambda: fused(snk.ACT_NONE))
+    ur = time_calls(lambda: fused(snk.ACT_RELU))
+    lb = layer_bytes(w, wl.B)
+    out["graph200k"] = {"nodes": w.M, "edges": w.nnz, "features": wl.B, "layers": layers,
+                        "us_gelu": round(uf, 1), "us_relu": round(ur, 1),
+                        "us_no_act": round(un, 1), "us_gelu_two_calls": round(us, 1),
+                        "GBps_relu": round(layers * lb / (ur * 1e3), 1),
+                        "GBps_gelu": round(layers * lb / (uf * 1e3), 1),
+                        "note": "snack_graph_propagate: ReLU applied in the product's store, "
+                                "GELU as an in-place pass after each product; two_calls = "
+                                "snack_spmm_fwd + snack_gelu_fwd per layer"}
+    del topo, vals, X, Y, tmp, Z
+    torch.cuda.empty_cache()
+
+    log("graph inference: 16k nodes at 99% against Dense+Mask")
+    n = 16384
+    wl = synth.graph_layer(n=n, nnz=synth.nnz_for(n, n, 0.99), B=128)
+    w, topo, vals, X = sparse_setup(wl)
+    Y, tmp = torch.empty_like(X), torch.empty_like(X)
+    us_sp = time_calls(lambda: snk.snack_graph_propagate(topo.plan, vals, X, NM, wl.B, layers,
+                                                          GELU, Y, tmp))
+    lin = torch.from_numpy(w.row.astype(np.int64) * n + w.col).cuda()
+    Wd = torch.zeros(n * n, dtype=torch.float32, device="cuda")
+    Wd[lin] = vals
+    mask = torch.zeros(n * n, dtype=torch.uint8, device="cuda")
+    mask[lin] = 1
+    Xb = X.view(n, wl.B).t().contiguous()  # batch-major B x n
+    Zb, Hb, Gb = torch.empty_like(Xb), torch.empty_like(Xb), torch.empty_like(Xb)
+
+    def dense(m):
+        src = Xb
+        for l in range(layers):
+            dst = Hb if (layers - 1 - l) % 2 == 0 else Gb
+            snk.snack_dense_fwd(Wd, m, n, n, src, wl.B, Zb)
+            snk.snack_gelu_fwd(Zb, dst)
+            src = dst
+
+    us_dm = time_calls(lambda: dense(mask), reps=3, warm=1)
+    us_d = time_calls(lambda: dense(None), reps=3, warm=1)
+    # same results: the last layer of both paths (node-major vs batch-major)
+    diff = float((Y.view(n, wl.B).t() - Hb).abs().max())
+    out["graph16k_s0.99"] = {"nodes": n, "edges": w.nnz, "features": wl.B, "layers": layers,
+                             "act": "gelu", "us_sparse": round(us_sp, 1),
+                             "us_dense_mask": round(us_dm, 1), "us_dense": round(us_d, 1),
+                             "speedup_vs_dense_mask": round(us_dm / us_sp, 2),
+                             "speedup_vs_dense": round(us_d / us_sp, 2),
+                             "max_abs_diff_sparse_vs_dense": diff,
+                             "dense_fp32_flop_floor_us": round(
+                                 layers * 2 * n * n * wl.B / 157.3e12 * 1e6, 1)}
+    del topo, vals, X, Y, tmp, Wd, mask, Xb, Zb, Hb, Gb, lin
     torch.cuda.empty_cache()
     return out
 
@@ -495,6 +606,8 @@ def run_bench(args):
             del ib
             torch.cuda.empty_cache()
         rec["baselines"] = base
+    if args.graph:
+        rec["graph_inference"] = graph_inference()
     rec["footprint"] = footprint(N, wt.nnz, B, 0 if args.products_only else
                                  snk_drop(wt.nnz, args.drop_ppm), args.layout)
     if args.cpu_baseline:

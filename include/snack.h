@@ -179,6 +179,42 @@ SNACK_API snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, 
                             const void* X, snack_layout layout, int32_t B, void* Y,
                             void* stream);
 
+/* Nonlinearity applied to each finished output of snack_spmm_fwd_act. */
+typedef enum { SNACK_ACT_NONE = 0, SNACK_ACT_RELU = 1, SNACK_ACT_GELU = 2 } snack_act;
+
+/*
+ * snack_spmm_fwd_act -- snack_spmm_fwd followed by a nonlinearity:
+ * Y[b, r] = act(sum_{k : row[k] = r} v[k] * X[b, col[k]]).
+ * act: SNACK_ACT_NONE (identity), SNACK_ACT_RELU (max(x, 0); NaN gives 0)
+ * or SNACK_ACT_GELU (exact, x * Phi(x) with the error function), the
+ * nonlinearity between propagation steps of the graph-style inference the
+ * SNACK abstract measures.  ReLU is applied in the product's store, to the
+ * fp32 sum before its single rounding; GELU runs as one elementwise pass
+ * over Y on the same stream right after the product (it reads the rounded
+ * sums and rounds again).  Rows without entries give act(0) = 0.  Errors:
+ * as snack_spmm_fwd, and SNACK_E_SHAPE for an unknown act.
+ */
+SNACK_API snack_status snack_spmm_fwd_act(const snack_plan* plan, const void* vals,
+                                          snack_dtype dtype, const void* X, snack_layout layout,
+                                          int32_t B, void* Y, int32_t act, void* stream);
+
+/*
+ * snack_graph_propagate -- multi-layer graph-style inference (the abstract's
+ * "graph-style inference", read here as repeated propagation through one
+ * sparse adjacency): H_0 = X, H_l = act(H_{l-1} W^T) for l = 1 .. layers,
+ * Y = H_layers, each layer one snack_spmm_fwd_act launch on `stream`, each
+ * H_l rounded to dtype.  layers > 1 needs a square plan (M == K) and tmp,
+ * a device buffer of B*M elements used for alternate layers (tmp may be
+ * NULL when layers == 1).  Y must not alias X or tmp.  Asynchronous.
+ * Errors: as snack_spmm_fwd_act; SNACK_E_SHAPE for layers < 1, a
+ * non-square plan with layers > 1, or aliasing; SNACK_E_NULL for a missing
+ * tmp.
+ */
+SNACK_API snack_status snack_graph_propagate(const snack_plan* plan, const void* vals,
+                                             snack_dtype dtype, const void* X,
+                                             snack_layout layout, int32_t B, int32_t layers,
+                                             int32_t act, void* Y, void* tmp, void* stream);
+
 /*
  * snack_spmm_bwd_input -- gradient with respect to the layer input,
  * dX = dY W, kept sparse (only the nonzeros are touched):

@@ -228,3 +228,28 @@ def memory_by_definition(M: int, K: int, nnz: int, elem_bytes: int, max_batch: i
         "mask": mk,
         "activations": max_batch * (K + M) * elem_bytes * 2,
     }
+
+
+def act_f64(x, act: int):
+    """The nonlinearity of a propagation step in fp64: 0 identity, 1 ReLU
+    (max(x, 0)), 2 exact GELU."""
+    x = _f64(x)
+    if act == 1:
+        return np.where(x > 0, x, 0.0)
+    if act == 2:
+        return gelu(x)
+    return x.copy()
+
+
+def graph_propagate(M, K, row, col, v, B, X, layers: int, act: int, node_major=False):
+    """Multi-layer propagation through one sparse adjacency (the SNACK
+    abstract's graph-style inference, read as H_l = act(H_{l-1} W^T)), in fp64
+    with no rounding between layers.  Returns [(H_l, S_l)] for l = 1..layers,
+    S_l the per-output sum of |v| |H_{l-1}| of layer l (its error scale)."""
+    out = []
+    H = _f64(X)
+    for _ in range(layers):
+        Z, S = spmm_fwd(M, K, row, col, v, B, H, node_major)
+        H = act_f64(Z, act)
+        out.append((H, S))
+    return out

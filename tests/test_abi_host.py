@@ -167,3 +167,31 @@ def test_memory_footprint_rejects_bad_arguments(snk):
     assert st("snack_memory_footprint", 64, 64, 10, 1, 0, 11, 0, ref) == -8
     assert st("snack_memory_footprint", 4, 4, 10, 1, 0, 7, 0, ref) == -8
     assert st("snack_memory_footprint", 64, 64, 10, 1, 0, 0, 8, ref) == -4
+
+
+def test_fused_activation_and_propagation_argument_checks(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    q = snk.snack_plan_init(8, 6, 4, 2)
+    cases = [  # (call, status) -- all rejected on the host, nothing launched
+        (lambda: b.snack_spmm_fwd_act(p, 0x1000, 0x2000, 0, 1, 0x3000, 3, stream=0, dtype=0), -2),
+        (lambda: b.snack_spmm_fwd_act(p, 0x1000, 0x2000, 0, 1, 0x3000, -1, stream=0, dtype=0), -2),
+        (lambda: b.snack_spmm_fwd_act(p, 0x1000, 0x2000, 0, 1, 0x3000, 1, stream=0, dtype=0), -12),
+        (lambda: b.snack_graph_propagate(p, 0x1000, 0x2000, 0, 1, 0, 1, 0x3000, 0x4000,
+                                         stream=0, dtype=0), -2),   # no layers
+        (lambda: b.snack_graph_propagate(q, 0x1000, 0x2000, 0, 1, 2, 1, 0x3000, 0x4000,
+                                         stream=0, dtype=0), -2),   # not square
+        (lambda: b.snack_graph_propagate(p, 0x1000, 0x2000, 0, 1, 2, 1, 0x3000, None,
+                                         stream=0, dtype=0), -1),   # tmp missing
+        (lambda: b.snack_graph_propagate(p, 0x1000, 0x2000, 0, 1, 2, 1, 0x2000, 0x4000,
+                                         stream=0, dtype=0), -2),   # Y aliases X
+        (lambda: b.snack_graph_propagate(p, 0x1000, 0x2000, 0, 1, 2, 5, 0x3000, 0x4000,
+                                         stream=0, dtype=0), -2),   # unknown act
+        (lambda: b.snack_graph_propagate(p, 0x1000, 0x2000, 0, 1, 2, 1, 0x3000, 0x4000,
+                                         stream=0, dtype=0), -12),  # unprepared plan
+    ]
+    for call, status in cases:
+        with pytest.raises(snk.SnackError) as e:
+            call()
+        assert e.value.status == status
+    assert b.raw_status("snack_graph_propagate", None, 1, 0, 0, 0, 1, 1, 1, 1, 1, None) == -1

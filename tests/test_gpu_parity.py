@@ -623,3 +623,100 @@ def test_memory_footprint_matches_device_allocations(dt, n_drop_ppm, flags):
     if n_drop:  # the workspace suffices for the restructure it was sized for
         topo.restructure(vals, n_drop, 0, 1, ws=ws)
     del row, col, vals, dV, topo, ws
+
+
+# ------------------------------------- fused activation and multi-layer propagation
+LACT = {0: 1.0, 1: 1.0, 2: 1.13}  # slope bound of each nonlinearity (GELU's is ~1.129)
+UNIT = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8}
+
+
+def propagation_reference(orc, w, Bsz, X64, layers, act, dt, nm):
+    """The oracle's output after `layers` steps and an elementwise bound on the
+    GPU's distance from it: each step adds its accumulation tolerance
+    (tol * S_l), a few roundings of its stored output in dt (8 u |H_l|), and
+    carries the previous bound through |W| and the nonlinearity's slope."""
+    ref = orc.graph_propagate(w.M, w.K, w.row, w.col, w.vals_f64(), Bsz, X64, layers, act, nm)
+    E = np.zeros(Bsz * w.K)
+    absv = np.abs(w.vals_f64())
+    for H, S in ref:
+        prop, _ = orc.spmm_fwd(w.M, w.K, w.row, w.col, absv, Bsz, E, nm)
+        E = LACT[act] * (prop + TOL_DT[dt] * S) + 8 * UNIT[dt] * np.abs(H)
+    return ref[-1][0], E
+
+
+TOL_DT = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def assert_bound(got, ref, E, what):
+    err = np.abs(got - ref)
+    bad = err > E
+    assert np.isfinite(got).all(), what
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {got.size} out of bound; worst "
+                           f"{float(np.max(err - E))}")
+
+
+ACT_CASES = [  # (M, K, nnz, B, dtype, layout, tile)
+    (257, 255, 3000, 8, "bf16", "batch", 64),
+    (1, 64, 64, 4, "f32", "batch", 5),       # one dense row split over many tiles
+    (300, 40, 30, 2, "f32", "batch", 7),     # mostly empty rows: act(0) = 0
+    (511, 129, 9000, 32, "f32", "node", 256),
+    (100, 333, 8000, 5, "bf16", "node", 0),
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt,layout,tile", ACT_CASES)
+def test_spmm_fwd_fused_activation(orc, M, K, nnz, Bsz, dt, layout, tile):
+    wl = synth.random_case(9, M, K, nnz, Bsz, dt, layout)
+    w, X = wl.weights[0], wl.X[0]
+    nm = layout == "node"
+    lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
+    topo = topology(w, Bsz, tile)
+    vals, Xd = to_dev(w.vals, dt), to_dev(X.data, dt)
+    plain = topo.fwd(vals, Xd, Bsz, lay)
+    for act in (B.ACT_NONE, B.ACT_RELU, B.ACT_GELU):
+        Y = torch.empty_like(plain)
+        B.snack_spmm_fwd_act(topo.plan, vals, Xd, lay, Bsz, Y, act)
+        if act == B.ACT_NONE:
+            assert torch.equal(Y, plain)
+        ref, E = propagation_reference(orc, w, Bsz, X.f64(), 1, act, dt, nm)
+        assert_bound(from_dev(Y, dt), ref, E, f"act {act}")
+        Y2 = torch.empty_like(plain)
+        B.snack_spmm_fwd_act(topo.plan, vals, Xd, lay, Bsz, Y2, act)
+        assert torch.equal(Y, Y2)  # bitwise reproducible
+
+
+@pytest.mark.parametrize("dt,layout,Bsz,act", [("f32", "node", 16, 1), ("f32", "node", 16, 2),
+                                               ("bf16", "batch", 5, 1), ("f32", "batch", 3, 2)])
+def test_graph_propagate_small(orc, dt, layout, Bsz, act):
+    nm = layout == "node"
+    lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
+    if dt == "f32" and nm:
+        wl = synth.graph_layer(seed=4, n=3000, nnz=40000, B=Bsz)
+    else:
+        wl = synth.random_case(4, 700, 700, 20000, Bsz, dt, layout)
+    w, X = wl.weights[0], wl.X[0]
+    topo = topology(w, Bsz, 0)
+    vals, Xd = to_dev(w.vals, dt), to_dev(X.data, dt)
+    for layers in (1, 2, 3):
+        Y = torch.empty_like(Xd)
+        tmp = torch.empty_like(Xd)
+        B.snack_graph_propagate(topo.plan, vals, Xd, lay, Bsz, layers, act, Y, tmp)
+        ref, E = propagation_reference(orc, w, Bsz, X.f64(), layers, act, dt, nm)
+        assert_bound(from_dev(Y, dt), ref, E, f"layers {layers}")
+        if layers == 1:
+            Z = torch.empty_like(Xd)
+            B.snack_spmm_fwd_act(topo.plan, vals, Xd, lay, Bsz, Z, act)
+            assert torch.equal(Y, Z)
+
+
+def test_graph_propagate_power_law_graph_full_size(orc):
+    """200,000 nodes, 2,400,000 power-law edges with random-walk weights, 128
+    fp32 node-major features, three ReLU propagation steps, every output."""
+    wl = workload("graph")
+    w, X = wl.weights[0], wl.X[0]
+    topo = topology(w, 128, 0)
+    vals, Xd = to_dev(w.vals, "f32"), to_dev(X.data, "f32")
+    Y, tmp = torch.empty_like(Xd), torch.empty_like(Xd)
+    B.snack_graph_propagate(topo.plan, vals, Xd, B.NODE_MAJOR, 128, 3, B.ACT_RELU, Y, tmp)
+    ref, E = propagation_reference(orc, w, 128, X.f64(), 3, B.ACT_RELU, "f32", True)
+    assert_bound(from_dev(Y, "f32"), ref, E, "graph 3 layers")

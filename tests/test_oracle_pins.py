@@ -384,3 +384,29 @@ def test_generator_counts_and_determinism():
     assert synth.nnz_for(11008, 4096, 0.9) == 4508877
     d = synth.rank_profile(11008, 4096, 4508877, 1.2)
     assert d.sum() == 4508877 and (d == 4096).sum() == 310
+
+
+def test_graph_propagation_composes_dense_steps(orc):
+    """The oracle's multi-layer propagation equals repeated dense products
+    (numpy) with the nonlinearity applied after each, for ReLU and GELU; and
+    with a diagonal identity adjacency and ReLU it is ReLU of the input."""
+    rng = np.random.default_rng(11)
+    N, B, L = 9, 3, 3
+    lin = np.sort(rng.choice(N * N, 30, replace=False))
+    row, col = (lin // N).astype(np.int32), (lin % N).astype(np.int32)
+    v = rng.standard_normal(lin.size)
+    W = np.zeros((N, N))
+    W[row, col] = v
+    X = rng.standard_normal(B * N)
+    for act in (1, 2):
+        got = orc.graph_propagate(N, N, row, col, v, B, X, L, act)
+        H = X.reshape(B, N)
+        for l in range(L):
+            scale = np.abs(H) @ np.abs(W).T  # layer l's error scale, from its input
+            Z = H @ W.T
+            H = np.maximum(Z, 0) if act == 1 else orc.gelu(Z.ravel()).reshape(B, N)
+            assert np.allclose(got[l][0].reshape(B, N), H, rtol=1e-13, atol=1e-15)
+            assert np.allclose(got[l][1].reshape(B, N), scale, rtol=1e-13, atol=1e-15)
+    eye = np.arange(N, dtype=np.int32)
+    out = orc.graph_propagate(N, N, eye, eye, np.ones(N), B, X, 2, 1)
+    assert np.array_equal(out[-1][0], np.maximum(X, 0))

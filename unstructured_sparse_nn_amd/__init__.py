@@ -6,11 +6,13 @@ library ``libsnack.so`` (C ABI in ``include/snack.h``).  ``binding`` mirrors
 that ABI one function per entry point; ``layer`` wraps it as a torch module.
 PyTorch only provides device memory and streams.
 """
-from .binding import (BATCH_MAJOR, BF16, F32, NODE_MAJOR, SnackError, SnackPlan,  # noqa: F401
-                      snack_coo_prepare, snack_dense_fwd, snack_drop_count, snack_gelu_bwd,
+from .binding import (ACT_GELU, ACT_NONE, ACT_RELU, BATCH_MAJOR, BF16, F32,  # noqa: F401
+                      NODE_MAJOR, SnackError, SnackPlan,
+                      snack_coo_prepare, snack_dense_fwd, snack_graph_propagate, snack_drop_count, snack_gelu_bwd,
                       snack_gelu_fwd, snack_memory_footprint, snack_plan_array, snack_plan_init, snack_plan_sizeof,
                       snack_prune_regrow, snack_prune_regrow_prepared,
                       snack_prune_regrow_workspace, snack_sddmm_grad_vals,
-                      snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd, snack_version,
+                      snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd,
+                      snack_spmm_fwd_act, snack_version,
                       status_str)
 from .layer import SparseLinear, Topology  # noqa: F401

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsnack.so")
 
 F32, BF16 = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 PLAN_NODE_MAJOR_ONLY = 1
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
@@ -75,6 +76,8 @@ def _load():
         "snack_coo_prepare": ([plan_p, P, P, P, sz, P], i32),
         "snack_plan_array": ([plan_p, i32, ctypes.POINTER(i64)], P),
         "snack_spmm_fwd": ([plan_p, P, i32, P, i32, i32, P, P], i32),
+        "snack_spmm_fwd_act": ([plan_p, P, i32, P, i32, i32, P, i32, P], i32),
+        "snack_graph_propagate": ([plan_p, P, i32, P, i32, i32, i32, i32, P, P, P], i32),
         "snack_spmm_bwd_input": ([plan_p, P, i32, P, i32, i32, P, P], i32),
         "snack_sddmm_grad_vals": ([plan_p, P, P, i32, i32, i32, P, P], i32),
         "snack_spmm_bwd_fused": ([plan_p, P, i32, P, P, i32, i32, P, P, ctypes.c_float, P], i32),
@@ -177,6 +180,22 @@ def snack_spmm_fwd(plan, vals, X, layout, B, Y, stream=None, dtype=None):
     dt = _dtype(vals, X, Y, dtype=dtype)
     _check(_lib.snack_spmm_fwd(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), layout, B, _ptr(Y),
                                _stream(stream)), "snack_spmm_fwd")
+
+
+def snack_spmm_fwd_act(plan, vals, X, layout, B, Y, act, stream=None, dtype=None):
+    dt = _dtype(vals, X, Y, dtype=dtype)
+    _check(_lib.snack_spmm_fwd_act(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), layout, B,
+                                   _ptr(Y), act, _stream(stream)), "snack_spmm_fwd_act")
+
+
+def snack_graph_propagate(plan, vals, X, layout, B, layers, act, Y, tmp=None, stream=None,
+                          dtype=None):
+    """Y = act(...act(act(X W^T) W^T)... W^T), `layers` propagations (tmp: B*M
+    elements, needed when layers > 1)."""
+    dt = _dtype(vals, X, Y, dtype=dtype)
+    _check(_lib.snack_graph_propagate(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), layout, B,
+                                      layers, act, _ptr(Y), _ptr(tmp), _stream(stream)),
+           "snack_graph_propagate")
 
 
 def snack_spmm_bwd_input(plan, vals, dY, layout, B, dX, stream=None, dtype=None):

@@ -296,6 +296,45 @@ snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtyp
                          to_stream(stream));
 }
 
+snack_status snack_spmm_fwd_act(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                const void* X, snack_layout layout, int32_t B, void* Y,
+                                int32_t act, void* stream) {
+  if (act < SNACK_ACT_NONE || act > SNACK_ACT_GELU) return SNACK_E_SHAPE;
+  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y, dtype, layout, B);
+  if (st) return st;
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  hipStream_t s = to_stream(stream);
+  // ReLU is applied in the product's store; GELU (an erf) runs as one
+  // elementwise pass over Y right after, which measured faster than in the
+  // product's epilogue
+  st = launch_seg_spmm(row_view(plan), vals, dtype, X, layout, B, Y, carry, act_of(plan), s,
+                       act == SNACK_ACT_RELU ? SNACK_ACT_RELU : SNACK_ACT_NONE);
+  if (st || act != SNACK_ACT_GELU) return st;
+  return launch_act_inplace(dtype, Y, (int64_t)B * plan->M, SNACK_ACT_GELU, s) == hipSuccess
+             ? SNACK_OK
+             : SNACK_E_HIP;
+}
+
+snack_status snack_graph_propagate(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                   const void* X, snack_layout layout, int32_t B, int32_t layers,
+                                   int32_t act, void* Y, void* tmp, void* stream) {
+  if (!plan) return SNACK_E_NULL;
+  if (layers < 1 || act < SNACK_ACT_NONE || act > SNACK_ACT_GELU) return SNACK_E_SHAPE;
+  if (layers > 1 && plan->M != plan->K) return SNACK_E_SHAPE;
+  if (layers > 1 && !tmp) return SNACK_E_NULL;
+  if (Y && (Y == X || Y == tmp)) return SNACK_E_SHAPE;
+  // layer l writes Y when layers-1-l is even, else tmp, so the last one
+  // lands in Y; each reads the previous layer's output
+  const void* in = X;
+  for (int32_t l = 0; l < layers; ++l) {
+    void* out = ((layers - 1 - l) % 2 == 0) ? Y : tmp;
+    const snack_status st = snack_spmm_fwd_act(plan, vals, dtype, in, layout, B, out, act, stream);
+    if (st) return st;
+    in = out;
+  }
+  return SNACK_OK;
+}
+
 snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
                                   const void* dY, snack_layout layout, int32_t B, void* dX,
                                   void* stream) {

@@ -10,8 +10,7 @@ __global__ __launch_bounds__(256) void k_gelu_fwd(const float* __restrict__ z,
                                                   float* __restrict__ h, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float x = z[i];
-  h[i] = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  h[i] = gelu_f32(z[i]);
 }
 
 // dz = dh * (Phi(z) + z * phi(z)), phi(z) = exp(-z^2/2) / sqrt(2 pi).
@@ -24,6 +23,31 @@ __global__ __launch_bounds__(256) void k_gelu_bwd(const float* __restrict__ z,
   float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
   float pdf = 0.39894228040143267794f * expf(-0.5f * x * x);
   dz[i] = dh[i] * (cdf + x * pdf);
+}
+
+// y <- act(y) in place, 8 elements per thread (one 16- or 32-byte access
+// when aligned), the GELU step of a propagation after its product.
+template <typename T>
+__global__ __launch_bounds__(256) void k_act_inplace(T* __restrict__ y, int64_t n, int32_t act) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= n) return;
+  if (i0 + 8 <= n && (uintptr_t)(y + i0) % (8 * sizeof(T)) == 0) {
+    vec<T, 8> v = *reinterpret_cast<const vec<T, 8>*>(y + i0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v.v[e] = elem<T>::from_f(apply_act(elem<T>::to_f(v.v[e]), act));
+    *reinterpret_cast<vec<T, 8>*>(y + i0) = v;
+  } else {
+    for (int64_t i = i0; i < n && i < i0 + 8; ++i)
+      y[i] = elem<T>::from_f(apply_act(elem<T>::to_f(y[i]), act));
+  }
+}
+
+hipError_t launch_act_inplace(snack_dtype dt, void* y, int64_t n, int32_t act, hipStream_t s) {
+  if (n <= 0 || act == ACT_NONE) return hipSuccess;
+  const dim3 grid((unsigned)cdiv(cdiv(n, 8), 256));
+  if (dt == SNACK_F32) hipLaunchKernelGGL(k_act_inplace<float>, grid, dim3(256), 0, s, (float*)y, n, act);
+  else hipLaunchKernelGGL(k_act_inplace<bf16>, grid, dim3(256), 0, s, (bf16*)y, n, act);
+  return hipGetLastError();
 }
 
 hipError_t launch_gelu_fwd(const float* z, float* h, int64_t n, hipStream_t s) {

@@ -62,6 +62,22 @@ __device__ __forceinline__ void store_vec(T* __restrict__ p, const float (&in)[N
   *reinterpret_cast<vec<T, N>*>(p) = r;
 }
 
+// ---------------------------------------------------------------- activations
+// Elementwise nonlinearity applied to a finished fp32 output before it is
+// rounded and stored (0 none, 1 ReLU, 2 exact GELU).
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };  // the values of snack_act
+
+// Exact GELU: z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2.
+__device__ __forceinline__ float gelu_f32(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float apply_act(float x, int32_t act) {
+  if (act == ACT_RELU) return x > 0.f ? x : 0.f;
+  if (act == ACT_GELU) return gelu_f32(x);
+  return x;
+}
+
 // ---------------------------------------------------------------- lanes
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -58,9 +58,11 @@ struct seg_view {          // one compressed view of the sparse matrix
 // act_tmp: scratch for the node-major copy of batch-major activations
 // (B > 1); >= elem * B * (F + S) + 256 bytes, or NULL when only node-major
 // activations are used.
+// act: ACT_NONE / ACT_RELU applied to each finished output (ACT_GELU is run
+// as launch_act_inplace after the product).
 snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
                              snack_layout lay, int32_t B, void* Y, float* carry, void* act_tmp,
-                             hipStream_t s);
+                             hipStream_t s, int32_t act = 0);
 snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snack_dtype dt,
                           snack_layout lay, int32_t B, void* dV, void* act_tmp, hipStream_t s);
 // Column view, B <= 32: dX = dY W, dV (nullable) and, if lr != 0, the
@@ -89,6 +91,8 @@ hipError_t launch_prepare_result(const int32_t* errs, int64_t n_errs, const int3
                                  hipStream_t s);
 
 // ---- aux kernels (aux.hip) ------------------------------------------------------
+// y <- act(y) elementwise over n values of dt (in place).
+hipError_t launch_act_inplace(snack_dtype dt, void* y, int64_t n, int32_t act, hipStream_t s);
 hipError_t launch_gelu_fwd(const float* z, float* h, int64_t n, hipStream_t s);
 hipError_t launch_gelu_bwd(const float* z, const float* dh, float* dz, int64_t n,
                            hipStream_t s);

@@ -54,14 +54,17 @@ __device__ __forceinline__ int tile_search(const int32_t* s_end, int d, int nseg
   return lo;
 }
 
-template <typename T, int CH, bool NODE_OUT>
+template <typename T, int CH, bool NODE_OUT, int ACT>
 __device__ __forceinline__ void store_out(T* __restrict__ Y, int32_t s, int32_t b0, int32_t B,
                                           int32_t S, const float (&v)[CH]) {
+  float a[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) a[c] = apply_act(v[c], ACT);
   if constexpr (NODE_OUT) {
-    store_vec<T, CH>(Y + (int64_t)s * B + b0, v);
+    store_vec<T, CH>(Y + (int64_t)s * B + b0, a);
   } else {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) Y[(int64_t)(b0 + c) * S + s] = elem<T>::from_f(v[c]);
+    for (int c = 0; c < CH; ++c) Y[(int64_t)(b0 + c) * S + s] = elem<T>::from_f(a[c]);
   }
 }
 
@@ -198,7 +201,11 @@ __device__ __forceinline__ void stage_tile(const tile_lds& L, const int32_t* __r
 // the dot of its gathered activation chunk with the chunk of Xs at its own
 // segment (column), reduced over the group's lanes, written to dV[perm] and,
 // when lr != 0, vals[perm] <- vals[perm] - lr * dV (the fused backward).
-template <typename T, int CH, bool NODE_OUT, bool PERM, bool FUSED = false, bool DEFER_VALS = false>
+// ACT: nonlinearity applied to each finished output (row view, ReLU only: an
+// erf in this epilogue measured slower than a separate GELU pass), a
+// template argument so that the plain products carry none of its code.
+template <typename T, int CH, bool NODE_OUT, bool PERM, bool FUSED = false, bool DEFER_VALS = false,
+          int ACT = ACT_NONE>
 __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const T* vals,
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
       for (int c = 0; c < CH; ++c) L.pend[tid * CH + c] = v[c];
       has_pend = true;
     } else if (bvalid) {
-      store_out<T, CH, NODE_OUT>(Y, sb + xx, b0, B, S, v);
+      store_out<T, CH, NODE_OUT, ACT>(Y, sb + xx, b0, B, S, v);
     }
     first_emit = false;
   };
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
 #pragma unroll
         for (int c = 0; c < CH; ++c) dst[c] = tot[c];
       } else {
-        store_out<T, CH, NODE_OUT>(Y, sb + x0, b0, B, S, tot);
+        store_out<T, CH, NODE_OUT, ACT>(Y, sb + x0, b0, B, S, tot);
       }
     }
   }
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
 // the same segment.  The pieces start at tile f: walk back over inner cuts of
 // the same segment.  out = sum of the carry-out slots of tiles f..p-1 (in
 // tile order) + the final piece held by tile p.
-template <typename T, bool NODE_OUT>
+template <typename T, bool NODE_OUT, int ACT = ACT_NONE>
 __global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ part_seg,
                                                const int32_t* __restrict__ cut,
                                                const float* __restrict__ carry, T* __restrict__ Y,
@@ -465,6 +472,7 @@ __global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ part_
   float tot = 0.f;
   for (int32_t q = f; q < p; ++q) tot += carry[(int64_t)q * B + b];
   tot += carry[((int64_t)P + p) * B + b];
+  tot = apply_act(tot, ACT);
   if (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
   else Y[(int64_t)b * S + s] = elem<T>::from_f(tot);
 }
@@ -721,9 +729,10 @@ static int32_t xcd_tiles_for(const seg_view& v) {
   return (int32_t)cdiv(v.P, NUM_XCD);
 }
 
-template <typename T, int CH, bool NODE_OUT, bool PERM>
-static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
-                     float* carry, const lane_shape& sh, hipStream_t s) {
+template <typename T, int CH, bool NODE_OUT, bool PERM, int ACT>
+static void launch_t_act(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
+                         float* carry, const lane_shape& sh, hipStream_t s) {
+  static_assert(!PERM || ACT == ACT_NONE, "activations apply to the row view only");
   const int32_t xt = xcd_tiles_for(v);
   dim3 grid((unsigned)(xt ? xt * NUM_XCD : v.P), (unsigned)cdiv(B, sh.bw));
   size_t lds = tile_lds_bytes(v.tile, sh.threads, sh.g_log2, CH);
@@ -734,42 +743,56 @@ static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_
                        lds, s, v.ptr, v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz,
                        (const T*)Xt, (T*)Y, carry, v.S, B, v.P, sh.g_log2, v.tile, xt);
   else
-    hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, PERM>), grid, dim3(sh.threads), lds, s,
-                       v.ptr, v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz,
-                       (const T*)Xt, (T*)Y, carry, v.S, B, v.P, sh.g_log2, v.tile, xt);
+    hipLaunchKernelGGL((k_seg_spmm<T, CH, NODE_OUT, PERM, false, false, ACT>), grid,
+                       dim3(sh.threads), lds, s, v.ptr, v.idx, v.perm, (const T*)vals,
+                       v.part_seg, v.part_nz, (const T*)Xt, (T*)Y, carry, v.S, B, v.P,
+                       sh.g_log2, v.tile, xt);
   if (v.has_split) {
     int64_t n = (int64_t)v.P * B;
-    hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
-                       v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
+                       s, v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
+  }
+}
+
+template <typename T, int CH, bool NODE_OUT, bool PERM>
+static void launch_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
+                     float* carry, const lane_shape& sh, int32_t act, hipStream_t s) {
+  if constexpr (PERM) {
+    launch_t_act<T, CH, NODE_OUT, PERM, ACT_NONE>(v, vals, Xt, B, Y, carry, sh, s);
+  } else {
+    if (act == ACT_RELU) launch_t_act<T, CH, NODE_OUT, PERM, ACT_RELU>(v, vals, Xt, B, Y, carry, sh, s);
+    else launch_t_act<T, CH, NODE_OUT, PERM, ACT_NONE>(v, vals, Xt, B, Y, carry, sh, s);
   }
 }
 
 template <typename T, int CH>
 static void launch_ch(const seg_view& v, const void* vals, const void* Xt, bool node_out,
-                      int32_t B, void* Y, float* carry, const lane_shape& sh, hipStream_t s) {
+                      int32_t B, void* Y, float* carry, const lane_shape& sh, int32_t act,
+                      hipStream_t s) {
   const bool perm = v.perm != nullptr;
-  if (node_out && perm) launch_t<T, CH, true, true>(v, vals, Xt, B, Y, carry, sh, s);
-  else if (node_out) launch_t<T, CH, true, false>(v, vals, Xt, B, Y, carry, sh, s);
-  else if (perm) launch_t<T, CH, false, true>(v, vals, Xt, B, Y, carry, sh, s);
-  else launch_t<T, CH, false, false>(v, vals, Xt, B, Y, carry, sh, s);
+  if (node_out && perm) launch_t<T, CH, true, true>(v, vals, Xt, B, Y, carry, sh, act, s);
+  else if (node_out) launch_t<T, CH, true, false>(v, vals, Xt, B, Y, carry, sh, act, s);
+  else if (perm) launch_t<T, CH, false, true>(v, vals, Xt, B, Y, carry, sh, act, s);
+  else launch_t<T, CH, false, false>(v, vals, Xt, B, Y, carry, sh, act, s);
 }
 
 template <typename T>
 static void launch_dt(const seg_view& v, const void* vals, const void* Xt, bool node_out,
-                      int32_t B, void* Y, float* carry, const lane_shape& sh, hipStream_t s) {
+                      int32_t B, void* Y, float* carry, const lane_shape& sh, int32_t act,
+                      hipStream_t s) {
   switch (sh.ch) {
-    case 1: launch_ch<T, 1>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
-    case 2: launch_ch<T, 2>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
-    case 4: launch_ch<T, 4>(v, vals, Xt, node_out, B, Y, carry, sh, s); break;
+    case 1: launch_ch<T, 1>(v, vals, Xt, node_out, B, Y, carry, sh, act, s); break;
+    case 2: launch_ch<T, 2>(v, vals, Xt, node_out, B, Y, carry, sh, act, s); break;
+    case 4: launch_ch<T, 4>(v, vals, Xt, node_out, B, Y, carry, sh, act, s); break;
     default:
-      if constexpr (sizeof(T) == 2) launch_ch<T, 8>(v, vals, Xt, node_out, B, Y, carry, sh, s);
+      if constexpr (sizeof(T) == 2) launch_ch<T, 8>(v, vals, Xt, node_out, B, Y, carry, sh, act, s);
       break;
   }
 }
 
 snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
                              snack_layout lay, int32_t B, void* Y, float* carry, void* act_tmp,
-                             hipStream_t s) {
+                             hipStream_t s, int32_t act) {
   if (B == 0 || v.S == 0) return SNACK_OK;
   const void* Xt = X;
   if (lay == SNACK_BATCH_MAJOR && B > 1) {  // B x F -> F x B once, then gather chunks
@@ -780,8 +803,8 @@ snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
   lane_shape sh = pick_shape(dt, B, v.tile);
-  if (dt == SNACK_F32) launch_dt<float>(v, vals, Xt, node_out, B, Y, carry, sh, s);
-  else launch_dt<bf16>(v, vals, Xt, node_out, B, Y, carry, sh, s);
+  if (dt == SNACK_F32) launch_dt<float>(v, vals, Xt, node_out, B, Y, carry, sh, act, s);
+  else launch_dt<bf16>(v, vals, Xt, node_out, B, Y, carry, sh, act, s);
   return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
 }
 
