@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--grid", action=argparse.BooleanOptionalAction, default=True,
                     help="also time fwd/dX/dV at 95/99%% x B in {1,8,32}")
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
+    ap.add_argument("--conv", action=argparse.BooleanOptionalAction, default=True,
+                    help="time a sparse 1x1 convolution (generated kernel, generic, dense)")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="time multi-layer graph inference (power-law graphs, fused GELU)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -370,6 +372,49 @@ def graph_inference(layers=3):
     return out
 
 
+def conv1x1_bench(N=8, HW=56 * 56, C=256, sparsity=0.9):
+    """A 1x1 convolution C -> C over N images of HW pixels at `sparsity`: the
+    kernel generated for the fixed weight (NCHW, one launch), the generic
+    products (NCHW: one node-major launch per image; NHWC: one batch-major
+    launch), and the in-repo dense kernel on the same weight (NHWC)."""
+    import torch
+    import synth
+    import unstructured_sparse_nn_amd as snk
+    out = {}
+    for dt in ("bf16", "f32"):
+        wl = synth.random_case(23, C, C, synth.nnz_for(C, C, sparsity), 1, dt, "node")
+        w = wl.weights[0]
+        sd = snk.F32 if dt == "f32" else snk.BF16
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        t0 = time.time()
+        f = snk.snack_fixed_build(w.row, w.col, w.vals, C, C, dtype=sd)
+        build_s = time.time() - t0
+        P = N * HW
+        X = torch.randn(P * C, device="cuda").to(tdt)
+        Y = torch.empty(P * C, dtype=tdt, device="cuda")
+        topo = snk.Topology(to_dev(w.row), to_dev(w.col), C, C, P)
+        vals = to_dev(w.vals, dt == "bf16")
+        Wd = torch.zeros(C * C, dtype=tdt, device="cuda")
+        Wd[torch.from_numpy(w.row.astype(np.int64) * C + w.col).cuda()] = vals
+        t = {"fixed_nchw": time_calls(lambda: snk.snack_fixed_fwd(f, X, HW, N, Y)),
+             "generic_nchw": time_calls(lambda: snk.snack_conv1x1(topo.plan, vals, X, N, HW,
+                                                                  snk.CONV_NCHW, Y)),
+             "generic_nhwc": time_calls(lambda: snk.snack_conv1x1(topo.plan, vals, X, N, HW,
+                                                                  snk.CONV_NHWC, Y)),
+             "dense_nhwc": time_calls(lambda: snk.snack_dense_fwd(Wd, None, C, C, X, P, Y))}
+        act_bytes = 2 * P * C * (4 if dt == "f32" else 2)
+        out[dt] = {"us": {k: round(v, 2) for k, v in t.items()},
+                   "act_GBps_fixed": round(act_bytes / (t["fixed_nchw"] * 1e3), 1),
+                   "fixed_vs_dense": round(t["dense_nhwc"] / t["fixed_nchw"], 2),
+                   "fixed_vs_generic_nchw": round(t["generic_nchw"] / t["fixed_nchw"], 2),
+                   "build_seconds": round(build_s, 2), **f.info()}
+        f.free()
+        del X, Y, topo, vals, Wd
+        torch.cuda.empty_cache()
+    return {"shape": f"{N}x{C}x56x56 -> {N}x{C}x56x56, 1x1, {sparsity:.0%} sparse "
+                     f"({synth.nnz_for(C, C, sparsity)} nnz)", **out}
+
+
 def snk_drop(nnz, ppm):
     import unstructured_sparse_nn_amd as snk
     return snk.snack_drop_count(nnz, ppm)
@@ -608,6 +653,9 @@ def run_bench(args):
         rec["baselines"] = base
     if args.graph:
         rec["graph_inference"] = graph_inference()
+    if args.conv:
+        log("1x1 convolution")
+        rec["conv1x1"] = conv1x1_bench()
     rec["footprint"] = footprint(N, wt.nnz, B, 0 if args.products_only else
                                  snk_drop(wt.nnz, args.drop_ppm), args.layout)
     if args.cpu_baseline:

@@ -357,6 +357,61 @@ SNACK_API snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz,
                                               snack_footprint* out);
 
 /*
+ * Fixed-pattern inference kernels (SparseRT, "Accelerating Unstructured
+ * Sparsity on GPUs for Deep Learning Inference", Abstract: a code generator
+ * that bakes a fixed sparse weight into the kernel, for fully connected
+ * layers and 1x1 convolutions).  snack_fixed_build reads a COO weight and
+ * its values from HOST memory (row, col int32 strictly increasing
+ * row-major, vals float or raw bf16 bits as dtype), writes a kernel for
+ * exactly that weight -- the values become immediate operands, the indices
+ * become the code's structure -- compiles it with hipRTC for gfx950 and
+ * loads it.  Limits: 1 <= K <= 256, nnz <= 65536 (else SNACK_E_SHAPE).
+ * Building takes seconds (compilation); the handle owns the loaded code
+ * object (device memory for code, the one exception to "no allocation")
+ * until snack_fixed_free.  flags: SNACK_FIXED_COMPILE_ONLY generates and
+ * compiles without loading (no GPU needed; the handle cannot run).
+ * Errors: SNACK_E_NULL, SNACK_E_DTYPE, SNACK_E_SHAPE, SNACK_E_COO_RANGE,
+ * SNACK_E_COO_ORDER, SNACK_E_LAYOUT (unknown flag), SNACK_E_HIP (compile or
+ * load failure).
+ *
+ * snack_fixed_fwd: Y = X W^T for `images` independent node-major blocks,
+ * X[i] (K x B) at X + i*K*B and Y[i] (M x B) at Y + i*M*B, in the dtype the
+ * handle was built for; fp32 accumulation, one rounding.  An NCHW 1x1
+ * convolution with C_in = K, C_out = M over images of H*W pixels is this
+ * call with B = H*W.  Asynchronous on `stream`.  Errors: SNACK_E_NULL,
+ * SNACK_E_SHAPE (negative sizes), SNACK_E_NOT_PREPARED (compile-only handle).
+ */
+typedef struct snack_fixed snack_fixed;
+#define SNACK_FIXED_COMPILE_ONLY 1u
+
+SNACK_API snack_status snack_fixed_build(const int32_t* row, const int32_t* col, const void* vals,
+                                         snack_dtype dtype, int32_t M, int32_t K, int64_t nnz,
+                                         uint32_t flags, snack_fixed** out);
+SNACK_API snack_status snack_fixed_fwd(const snack_fixed* f, const void* X, int32_t B,
+                                       int32_t images, void* Y, void* stream);
+/* Waves per workgroup, code-object and source sizes of a built kernel. */
+SNACK_API snack_status snack_fixed_info(const snack_fixed* f, int32_t* groups, size_t* code_bytes,
+                                        size_t* source_bytes);
+/* The compiled gfx950 code object of a handle (host memory owned by it). */
+SNACK_API const void* snack_fixed_code(const snack_fixed* f, size_t* bytes);
+SNACK_API void snack_fixed_free(snack_fixed* f);
+
+/*
+ * snack_conv1x1 -- a 1x1 convolution with the layer's weight (C_out = M,
+ * C_in = K) as products on the prepared plan: NHWC input (N*HW pixels x K
+ * channels) is one batch-major snack_spmm_fwd with B = N*HW; NCHW input
+ * (N images of K x HW) is one node-major snack_spmm_fwd per image with
+ * B = HW.  Output in the same layout.  The plan's max_batch must cover B.
+ * layout: SNACK_CONV_NHWC or SNACK_CONV_NCHW.  Errors: as snack_spmm_fwd,
+ * SNACK_E_LAYOUT for an unknown layout.
+ */
+#define SNACK_CONV_NHWC 0
+#define SNACK_CONV_NCHW 1
+SNACK_API snack_status snack_conv1x1(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                     const void* X, int32_t N, int32_t HW, int32_t layout, void* Y,
+                                     void* stream);
+
+/*
  * GELU with the exact error function, h = z * Phi(z), and its backward
  * dz = dh * (Phi(z) + z * phi(z)), elementwise over n fp32 values (the
  * nonlinearity between the two sparse layers of a GPT-2-shaped MLP block).

@@ -195,3 +195,79 @@ def test_fused_activation_and_propagation_argument_checks(snk):
             call()
         assert e.value.status == status
     assert b.raw_status("snack_graph_propagate", None, 1, 0, 0, 0, 1, 1, 1, 1, 1, None) == -1
+
+
+# ------------------------------------------------ fixed-pattern kernels (hipRTC)
+def _fixed_case(M, K, sp, dt="f32", seed=3):
+    import synth
+    return synth.random_case(seed, M, K, synth.nnz_for(M, K, sp), 4, dt, "node").weights[0]
+
+
+def test_fixed_pattern_kernel_compiles_for_gfx950_without_spills(snk):
+    """The generated kernel compiles for gfx950 on the host.  Its code object
+    has one FMA per entry (the value an operand), no scratch (the staged
+    inputs are read column by column) and no packed fp32 instructions."""
+    import shutil
+    import subprocess
+    import tempfile
+    for M, K, sp, dt in ((48, 40, 0.8, "f32"), (96, 64, 0.6, "bf16")):
+        w = _fixed_case(M, K, sp, dt)
+        f = snk.snack_fixed_build(w.row, w.col, w.vals, M, K,
+                                  dtype=snk.F32 if dt == "f32" else snk.BF16,
+                                  flags=snk.FIXED_COMPILE_ONLY)
+        info = f.info()
+        assert info["groups"] >= 1 and info["code_bytes"] > 0
+        code = f.code()
+        assert len(code) == info["code_bytes"]
+        objdump = "/opt/rocm/llvm/bin/llvm-objdump"
+        readelf = "/opt/rocm/llvm/bin/llvm-readelf"
+        if not (shutil.which(objdump) and shutil.which(readelf)):
+            continue
+        with tempfile.NamedTemporaryFile(suffix=".co") as t:
+            t.write(code)
+            t.flush()
+            asm = subprocess.run([objdump, "-d", "--mcpu=gfx950", t.name], capture_output=True,
+                                 text=True).stdout
+            notes = subprocess.run([readelf, "--notes", t.name], capture_output=True,
+                                   text=True).stdout
+        assert "v_pk_fma_f32" not in asm and "v_pk_mul_f32" not in asm
+        assert "scratch_" not in asm
+        fmas = sum(asm.count(op) for op in ("v_fmamk_f32", "v_fmac_f32", "v_fma_f32",
+                                            "v_mul_f32"))
+        assert fmas >= w.nnz
+        assert ".private_segment_fixed_size: 0" in notes.replace("  ", " ").replace("  ", " ")
+
+
+def test_fixed_pattern_build_rejects_bad_arguments(snk):
+    import numpy as np
+    from unstructured_sparse_nn_amd import binding as b
+    r = np.array([0, 0, 1], np.int32)
+    c = np.array([1, 3, 0], np.int32)
+    v = np.ones(3, np.float32)
+    CO = snk.FIXED_COMPILE_ONLY
+    cases = [
+        (lambda: snk.snack_fixed_build(r, c, v, 2, 300, flags=CO), -2),       # K > 256
+        (lambda: snk.snack_fixed_build(r, c, v, 0, 4, flags=CO), -2),
+        (lambda: snk.snack_fixed_build(r, np.array([3, 1, 0], np.int32), v, 2, 4, flags=CO), -6),
+        (lambda: snk.snack_fixed_build(r, np.array([1, 4, 0], np.int32), v, 2, 4, flags=CO), -5),
+        (lambda: snk.snack_fixed_build(r, c, v, 2, 4, dtype=5, flags=CO), -3),
+        (lambda: snk.snack_fixed_build(r, c, v, 2, 4, flags=8), -4),
+    ]
+    for call, status in cases:
+        with pytest.raises(snk.SnackError) as e:
+            call()
+        assert e.value.status == status
+    big = np.arange(65537, dtype=np.int64)
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_fixed_build((big // 256).astype(np.int32), (big % 256).astype(np.int32),
+                              np.ones(big.size, np.float32), 300, 256, flags=CO)
+    assert e.value.status == -2
+    f = snk.snack_fixed_build(r, c, v, 2, 4, flags=CO)
+    with pytest.raises(snk.SnackError) as e:  # compile-only handles cannot run
+        snk.snack_fixed_fwd(f, 0x1000, 8, 1, 0x2000, stream=0)
+    assert e.value.status == -12
+    assert b.raw_status("snack_fixed_build", None, None, None, 0, 2, 4, 0, 0, None) == -1
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_conv1x1(p, 0x1000, 0x2000, 1, 2, 7, 0x3000, stream=0, dtype=0)
+    assert e.value.status == -4

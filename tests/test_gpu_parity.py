@@ -720,3 +720,72 @@ def test_graph_propagate_power_law_graph_full_size(orc):
     B.snack_graph_propagate(topo.plan, vals, Xd, B.NODE_MAJOR, 128, 3, B.ACT_RELU, Y, tmp)
     ref, E = propagation_reference(orc, w, 128, X.f64(), 3, B.ACT_RELU, "f32", True)
     assert_bound(from_dev(Y, "f32"), ref, E, "graph 3 layers")
+
+
+# ------------------------------------ fixed-pattern kernels and 1x1 convolutions
+FIXED_CASES = [  # (M, K, sparsity, B, images, dtype)
+    (48, 40, 0.8, 100, 1, "f32"),       # ragged batch (not a multiple of 64)
+    (300, 7, 0.5, 64, 3, "f32"),        # several images, narrow input
+    (1, 256, 0.9, 33, 2, "bf16"),       # one output row
+    (256, 256, 0.9, 200, 2, "bf16"),
+    (200, 1, 0.0, 70, 1, "f32"),        # dense single column
+    (64, 64, 1.0, 65, 1, "f32"),        # no entries: Y = 0
+]
+
+
+@pytest.mark.parametrize("M,K,sp,Bsz,images,dt", FIXED_CASES)
+def test_fixed_pattern_kernel(orc, M, K, sp, Bsz, images, dt):
+    nnz = synth.nnz_for(M, K, sp)
+    wl = synth.random_case(13, M, K, nnz, Bsz * images, dt, "node")
+    w = wl.weights[0]
+    f = snk.snack_fixed_build(w.row, w.col, w.vals, M, K,
+                              dtype=snk.F32 if dt == "f32" else snk.BF16)
+    rng = np.random.default_rng(5)
+    X32 = rng.standard_normal(images * K * Bsz).astype(np.float32)
+    Xh = synth.f32_to_bf16_bits(X32) if dt == "bf16" else X32
+    Xd = to_dev(Xh, dt)
+    Y = torch.full((images * M * Bsz,), float("nan"), dtype=Xd.dtype, device="cuda")
+    snk.snack_fixed_fwd(f, Xd, Bsz, images, Y)
+    got = from_dev(Y, dt).reshape(images, M * Bsz)
+    X64 = (synth.bf16_bits_to_f32(Xh) if dt == "bf16" else X32).astype(np.float64)
+    X64 = X64.reshape(images, K * Bsz)
+    for i in range(images):
+        ref, S = orc.spmm_fwd(M, K, w.row, w.col, w.vals_f64(), Bsz, X64[i], True)
+        assert_within(got[i], ref, S, dt, f"image {i}")
+    Y2 = torch.empty_like(Y)
+    snk.snack_fixed_fwd(f, Xd, Bsz, images, Y2)
+    assert torch.equal(Y, Y2)
+    f.free()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_conv1x1_layouts_and_fixed_kernel(orc, dt):
+    """A 1x1 convolution (C_out = 96, C_in = 128, 90% sparse) over 2 images of
+    7 x 9 pixels: NHWC as one batch-major product, NCHW as one node-major
+    product per image and through the generated kernel, all against the
+    oracle on the same pixels."""
+    M, K, N, HW = 96, 128, 2, 63
+    wl = synth.random_case(17, M, K, synth.nnz_for(M, K, 0.9), N * HW, dt, "batch")
+    w = wl.weights[0]
+    pix = wl.X[0]  # N*HW pixels x K channels (batch-major = NHWC)
+    X64 = pix.f64().reshape(N, HW, K)
+    topo = topology(w, N * HW, 0)
+    vals = to_dev(w.vals, dt)
+    Xn = to_dev(pix.data, dt)
+    Yn = torch.empty(N * HW * M, dtype=Xn.dtype, device="cuda")
+    snk.snack_conv1x1(topo.plan, vals, Xn, N, HW, snk.CONV_NHWC, Yn)
+    ref, S = orc.spmm_fwd(M, K, w.row, w.col, w.vals_f64(), N * HW, X64.reshape(-1), False)
+    assert_within(from_dev(Yn, dt), ref, S, dt, "NHWC")
+    # NCHW: the same pixels, channel-major per image
+    raw = pix.data.reshape(N, HW, K).transpose(0, 2, 1).copy().reshape(-1)
+    Xc = to_dev(raw, dt)
+    Yc = torch.empty_like(Yn)
+    snk.snack_conv1x1(topo.plan, vals, Xc, N, HW, snk.CONV_NCHW, Yc)
+    refc = ref.reshape(N, HW, M).transpose(0, 2, 1).reshape(-1)
+    Sc = S.reshape(N, HW, M).transpose(0, 2, 1).reshape(-1)
+    assert_within(from_dev(Yc, dt), refc, Sc, dt, "NCHW")
+    f = snk.snack_fixed_build(w.row, w.col, w.vals, M, K,
+                              dtype=snk.F32 if dt == "f32" else snk.BF16)
+    Yf = torch.empty_like(Yn)
+    snk.snack_fixed_fwd(f, Xc, HW, N, Yf)
+    assert_within(from_dev(Yf, dt), refc, Sc, dt, "NCHW fixed kernel")

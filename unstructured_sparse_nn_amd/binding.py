@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libsnack.so")
 
 F32, BF16 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+CONV_NHWC, CONV_NCHW = 0, 1
+FIXED_COMPILE_ONLY = 1
 PLAN_NODE_MAJOR_ONLY = 1
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
@@ -88,6 +90,13 @@ def _load():
                                         i32),
         "snack_memory_footprint": ([i32, i32, i64, i32, i32, i64, ctypes.c_uint32,
                                     ctypes.POINTER(SnackFootprint)], i32),
+        "snack_fixed_build": ([P, P, P, i32, i32, i32, i64, ctypes.c_uint32, ctypes.POINTER(P)],
+                              i32),
+        "snack_fixed_fwd": ([P, P, i32, i32, P, P], i32),
+        "snack_fixed_info": ([P, ctypes.POINTER(i32), ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
+        "snack_fixed_code": ([P, ctypes.POINTER(sz)], P),
+        "snack_fixed_free": ([P], None),
+        "snack_conv1x1": ([plan_p, P, i32, P, i32, i32, i32, P, P], i32),
         "snack_gelu_fwd": ([P, P, i64, P], i32),
         "snack_gelu_bwd": ([P, P, P, i64, P], i32),
         "snack_dense_fwd": ([P, P, i32, i32, i32, P, i32, P, P], i32),
@@ -263,6 +272,64 @@ def snack_memory_footprint(M: int, K: int, nnz: int, max_batch: int, dtype: int,
     _check(_lib.snack_memory_footprint(M, K, nnz, max_batch, dtype, n_drop, plan_flags,
                                        ctypes.byref(out)), "snack_memory_footprint")
     return {f: int(getattr(out, f)) for f in FOOTPRINT_FIELDS}
+
+
+class SnackFixed:
+    """Handle of a kernel generated for one fixed weight (snack_fixed_build);
+    freed with the object or by ``free()``."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def info(self) -> dict:
+        g, cb, sb = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(_lib.snack_fixed_info(self.handle, ctypes.byref(g), ctypes.byref(cb),
+                                     ctypes.byref(sb)), "snack_fixed_info")
+        return {"groups": g.value, "code_bytes": cb.value, "source_bytes": sb.value}
+
+    def code(self) -> bytes:
+        """The compiled code object."""
+        n = ctypes.c_size_t(0)
+        p = _lib.snack_fixed_code(self.handle, ctypes.byref(n))
+        return ctypes.string_at(p, n.value) if p else b""
+
+    def free(self):
+        if self.handle:
+            _lib.snack_fixed_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+
+def snack_fixed_build(row, col, vals, M: int, K: int, dtype=None, flags: int = 0) -> SnackFixed:
+    """row, col (int32) and vals (float32, or uint16 bf16 bits with dtype=BF16)
+    are HOST numpy arrays."""
+    import numpy as np
+    row = np.ascontiguousarray(row, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    vals = np.ascontiguousarray(vals)
+    if dtype is None:
+        dtype = F32 if vals.dtype == np.float32 else BF16
+    out = ctypes.c_void_p(0)
+    _check(_lib.snack_fixed_build(row.ctypes.data or None, col.ctypes.data or None,
+                                  vals.ctypes.data or None, dtype, M, K, row.size, flags,
+                                  ctypes.byref(out)), "snack_fixed_build")
+    return SnackFixed(out.value)
+
+
+def snack_fixed_fwd(f: SnackFixed, X, B: int, images: int, Y, stream=None):
+    _check(_lib.snack_fixed_fwd(f.handle, _ptr(X), B, images, _ptr(Y), _stream(stream)),
+           "snack_fixed_fwd")
+
+
+def snack_conv1x1(plan, vals, X, N: int, HW: int, layout: int, Y, stream=None, dtype=None):
+    dt = _dtype(vals, X, Y, dtype=dtype)
+    _check(_lib.snack_conv1x1(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), N, HW, layout,
+                              _ptr(Y), _stream(stream)), "snack_conv1x1")
 
 
 def snack_gelu_fwd(z, h, n=None, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsnack.so")
 SOURCES = ["api.hip", "prims.hip", "prepare.hip", "spmm.hip", "prune.hip", "prune_bitmap.hip",
-           "aux.hip"]
+           "aux.hip", "fixed.hip"]
 ARCH = os.environ.get("SNACK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lhiprtc"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

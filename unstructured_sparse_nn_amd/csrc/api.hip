@@ -335,6 +335,27 @@ snack_status snack_graph_propagate(const snack_plan* plan, const void* vals, sna
   return SNACK_OK;
 }
 
+snack_status snack_conv1x1(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                           const void* X, int32_t N, int32_t HW, int32_t layout, void* Y,
+                           void* stream) {
+  if (!plan) return SNACK_E_NULL;
+  if (layout != SNACK_CONV_NHWC && layout != SNACK_CONV_NCHW) return SNACK_E_LAYOUT;
+  if (N < 0 || HW < 0) return SNACK_E_SHAPE;
+  if (layout == SNACK_CONV_NHWC) {
+    const int64_t B = (int64_t)N * HW;
+    if (B > INT32_MAX) return SNACK_E_OVERFLOW;
+    return snack_spmm_fwd(plan, vals, dtype, X, SNACK_BATCH_MAJOR, (int32_t)B, Y, stream);
+  }
+  const size_t es = dtype == SNACK_F32 ? 4 : 2;
+  for (int32_t n = 0; n < N; ++n) {
+    const snack_status st = snack_spmm_fwd(
+        plan, vals, dtype, (const char*)X + (size_t)n * plan->K * HW * es, SNACK_NODE_MAJOR, HW,
+        (char*)Y + (size_t)n * plan->M * HW * es, stream);
+    if (st) return st;
+  }
+  return SNACK_OK;
+}
+
 snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
                                   const void* dY, snack_layout layout, int32_t B, void* dX,
                                   void* stream) {
