@@ -423,6 +423,11 @@ PREPARED_CASES = [
     ("square_0.95_32", "bf16", 300000, 3, 2, 0),  # 4096 x 4096: fused
     ("ragged", "bf16", 250000, 4, 7, 0),         # 300 x 200: not multiples of 32, two calls
     ("single", "f32", 100000, 2, 3, 64),         # small tiles: rows and columns split
+    # density 1/4, every entry dropped: acceptance near 1/2.  bf16 (3 chunks
+    # on the entry kernels) needs stand-alone chunk launches and the finisher;
+    # fp32 (5 chunks) ends in the drop kernel's tail
+    ("quarter_all", "bf16", 1000000, 6, 1, 0),
+    ("quarter_all", "f32", 1000000, 6, 1, 0),
 ]
 
 
@@ -433,6 +438,8 @@ def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile)
     plan match the oracle."""
     if name == "ragged":
         w = synth.random_case(12, 300, 200, 6000, 1, dt).weights[0]
+    elif name == "quarter_all":
+        w = synth.random_case(12, 512, 512, 512 * 512 // 4, 1, dt).weights[0]
     else:
         w = workload(name).weights[0]
     n_drop = orc.drop_count(w.nnz, ppm)

@@ -186,6 +186,45 @@ __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, 
   }
 }
 
+// One workgroup: chunks after grid chunk c-1 until nothing is missing (or
+// the stream bound).  Records the positions still missing.  Any block size
+// up to 1024.
+constexpr int FT = 1024;
+constexpr int FINISH_ROUNDS = 4096;
+__device__ void regrow_tail(int32_t c, uint64_t stream, uint64_t MK, int32_t n_drop,
+                            bm_state* st, const uint32_t* __restrict__ sup,
+                            uint32_t* __restrict__ grown) {
+  __shared__ int32_t red[1024 / SNK_WAVE];
+  const int t = threadIdx.x, nt = blockDim.x;
+  int64_t start = 0;
+  int32_t rem = n_drop;
+  if (c > 0) {
+    start = st->ch_start[c - 1] + st->ch_rem[c - 1];
+    rem = st->ch_rem[c - 1] - chunk_taken(st, c - 1);
+  }
+  const bool ok = st->err == 0;
+  // density <= 1/4 keeps the acceptance rate >= 1/2, so the remainder
+  // roughly halves per round; the round cap only bounds a broken state
+  for (int round = 0; ok && rem > 0; ++round) {
+    if (start > STREAM_BOUND || round >= FINISH_ROUNDS) {
+      if (t == 0) atomicOr(&st->err, 8);
+      break;
+    }
+    int32_t acc = 0;
+    for (int64_t i = start + t; i < start + rem; i += 4 * nt)
+      acc += take_group(i, nt, start + rem, stream, MK, sup, grown);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, SNK_WAVE);
+    if (lane_id() == 0) red[t / SNK_WAVE] = acc;
+    __syncthreads();
+    int32_t taken = 0;
+    for (int i = 0; i < nt / SNK_WAVE; ++i) taken += red[i];
+    __syncthreads();
+    start += rem;
+    rem -= taken;
+  }
+  if (t == 0) st->rem_final = rem;
+}
+
 // The entries a block needs beyond its own, loaded by every thread next to
 // the block's main loads (clamped indices, no branch, one round trip) and
 // kept by a few threads in LDS: the linear index of entry base-1 (-1 for
@@ -442,7 +481,7 @@ __device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ 
 
 // Dropped bitmap D: entry k is dropped if its magnitude is below tau, or at
 // tau with tie rank (index order) below need.  Workgroups from nblk on run
-// regrow chunk c.
+// regrow chunk c; with `tail` a single one runs chunk c and all the rest.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_drop(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
@@ -450,14 +489,17 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
     const int32_t* __restrict__ cnt_eq,
     const int32_t* __restrict__ base_eq, int32_t n_drop, int32_t c, uint64_t stream, uint64_t MK,
     bm_state* st, uint32_t* __restrict__ dropb, const uint32_t* __restrict__ sup,
-    uint32_t* __restrict__ grown) {
+    uint32_t* __restrict__ grown, int32_t tail) {
   __shared__ int32_t lds[BT / SNK_WAVE];
   __shared__ uint32_t buf[CAP];
   __shared__ int64_t edge_s, whi_s;
   __shared__ int64_t nxt[NEXT];
   __shared__ uint32_t nxt_mag[NEXT];
   if ((int64_t)blockIdx.x >= nblk) {
-    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+    if (tail)  // one workgroup: chunk c and every later one (no finisher launch)
+      regrow_tail(c, stream, MK, n_drop, st, sup, grown);
+    else
+      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
     return;
   }
   const int t = threadIdx.x;
@@ -521,43 +563,11 @@ __global__ __launch_bounds__(BT) void k_bi_chunk(int32_t c, uint64_t stream, uin
   regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, gridDim.x);
 }
 
-// One workgroup: chunks after grid chunk c-1 until nothing is missing (or
-// the stream bound).  Records the positions still missing.
-constexpr int FT = 1024;
-constexpr int FINISH_ROUNDS = 4096;
 __global__ __launch_bounds__(FT) void k_bi_finish(int32_t c, uint64_t stream, uint64_t MK,
                                                   int32_t n_drop, bm_state* st,
                                                   const uint32_t* __restrict__ sup,
                                                   uint32_t* __restrict__ grown) {
-  __shared__ int32_t red[FT / SNK_WAVE];
-  const int t = threadIdx.x;
-  int64_t start = 0;
-  int32_t rem = n_drop;
-  if (c > 0) {
-    start = st->ch_start[c - 1] + st->ch_rem[c - 1];
-    rem = st->ch_rem[c - 1] - chunk_taken(st, c - 1);
-  }
-  const bool ok = st->err == 0;
-  // density <= 1/4 keeps the acceptance rate >= 1/2, so the remainder
-  // roughly halves per round; the round cap only bounds a broken state
-  for (int round = 0; ok && rem > 0; ++round) {
-    if (start > STREAM_BOUND || round >= FINISH_ROUNDS) {
-      if (t == 0) atomicOr(&st->err, 8);
-      break;
-    }
-    int32_t acc = 0;
-    for (int64_t i = start + t; i < start + rem; i += 4 * FT)
-      acc += take_group(i, FT, start + rem, stream, MK, sup, grown);
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, SNK_WAVE);
-    if (lane_id() == 0) red[t / SNK_WAVE] = acc;
-    __syncthreads();
-    int32_t taken = 0;
-    for (int i = 0; i < FT / SNK_WAVE; ++i) taken += red[i];
-    __syncthreads();
-    start += rem;
-    rem -= taken;
-  }
-  if (t == 0) st->rem_final = rem;
+  regrow_tail(c, stream, MK, n_drop, st, sup, grown);
 }
 
 __device__ __forceinline__ int4 word_counts(uint32_t S, uint32_t D, uint32_t G) {
@@ -1024,15 +1034,21 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   const bool own_prefix = L.nblk <= PREFIX_INBLOCK_MAX;
   if (!own_prefix)
     hipLaunchKernelGGL(k_bi_eq_scan, dim3(1), dim3(1024), 0, s, cnt_eq, base_eq, L.nblk);
-  hipLaunchKernelGGL(k_bi_drop<T>, with_chunk(c), et, 0, s, row, col, vals, nnz, L.nblk, M, K,
-                     L.W, passes - 1, cnt_eq, own_prefix ? nullptr : base_eq, nd, c, stream, MK,
-                     st, dropb, sup, grown);
+  // when the drop kernel's chunk is the last grid-wide one, a single
+  // workgroup of it also finishes the tail, overlapping the drop work
+  const int32_t total = grid_chunks((int64_t)MK, nnz, n_drop, c + 1);
+  const bool tail = total == c + 1;
+  hipLaunchKernelGGL(k_bi_drop<T>, tail ? dim3((unsigned)(L.nblk + 1)) : with_chunk(c), et, 0, s,
+                     row, col, vals, nnz, L.nblk, M, K, L.W, passes - 1, cnt_eq,
+                     own_prefix ? nullptr : base_eq, nd, c, stream, MK, st, dropb, sup, grown,
+                     tail ? 1 : 0);
   ++c;
-  const int32_t total = grid_chunks((int64_t)MK, nnz, n_drop, c);
-  const unsigned cb = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(n_drop, BT)));
-  for (; c < total; ++c)
-    hipLaunchKernelGGL(k_bi_chunk, dim3(cb), dim3(BT), 0, s, c, stream, MK, nd, st, sup, grown);
-  hipLaunchKernelGGL(k_bi_finish, dim3(1), dim3(FT), 0, s, c, stream, MK, nd, st, sup, grown);
+  if (!tail) {
+    const unsigned cb = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(n_drop, BT)));
+    for (; c < total; ++c)
+      hipLaunchKernelGGL(k_bi_chunk, dim3(cb), dim3(BT), 0, s, c, stream, MK, nd, st, sup, grown);
+    hipLaunchKernelGGL(k_bi_finish, dim3(1), dim3(FT), 0, s, c, stream, MK, nd, st, sup, grown);
+  }
   hipLaunchKernelGGL(k_bi_wsum, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
                      bsum);
   const bool own_base = L.nb <= PREFIX_INBLOCK_MAX;
