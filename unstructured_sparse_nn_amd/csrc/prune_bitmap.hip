@@ -36,11 +36,31 @@ namespace snk {
 namespace {
 
 constexpr int BT = 256;                   // threads per entry block
-constexpr int BE = 4 * BT;                // entries per block: thread t holds base + 4t .. + 3
+constexpr int BE = 4 * BT;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) store of four consecutive values.  The bitmap and
+// value-copy writes of the entry kernels use these: measured, they shorten
+// the drain before the next launch; the emitters' outputs, read soon after,
+// measured slower with them.
+template <typename T>
+__device__ __forceinline__ void stream_store4(T* p, const vec<T, 4>& v) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2 w;
+    __builtin_memcpy(&w, &v, 8);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+  } else {
+    u32x4 w;
+    __builtin_memcpy(&w, &v, 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  }
+}
+                // entries per block: thread t holds base + 4t .. + 3
 constexpr int HREPL = 64;                 // select-histogram replicas
 constexpr int AREPL = 64;                 // acceptance-count replicas
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
 constexpr int WT = 512;                   // threads (= bitmap words) per write block
+constexpr int EMIT_CAP = 2048;            // new entries per write block staged in LDS
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
@@ -278,8 +298,8 @@ __device__ void write_block_words(uint32_t* buf, int64_t w_lo, int64_t w_hi,
     if (threadIdx.x == 0 && extra && w_hi < cs + len) atomicOr(&buf[w_hi - cs], extra);
     __syncthreads();
     for (int j = threadIdx.x; j < len; j += BT) {
-      a[cs + j] = buf[j];
-      if (b) b[cs + j] = 0u;
+      __builtin_nontemporal_store(buf[j], &a[cs + j]);
+      if (b) __builtin_nontemporal_store(0u, &b[cs + j]);
     }
     __syncthreads();
   }
@@ -353,7 +373,7 @@ __global__ __launch_bounds__(BT) void k_bi_build(
     vec<T, 4> vv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) vv.v[j] = v4[j];
-    *reinterpret_cast<vec<T, 4>*>(vals_ws + k0) = vv;
+    stream_store4(vals_ws + k0, vv);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -640,6 +660,8 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     int64_t* __restrict__ grown_lin) {
   __shared__ int32_t lds[WT / SNK_WAVE];
   __shared__ int4 red[WT / SNK_WAVE];
+  __shared__ int32_t srow[EMIT_CAP], scol[EMIT_CAP];
+  __shared__ T sval[EMIT_CAP];
   const int t = threadIdx.x;
   const int32_t err = st->err, missing = st->rem_final;
   if (blockIdx.x == 0 && t == 0) {
@@ -674,6 +696,10 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   // int32 (15 bits each, no overflow) and two block scans serve all four
   int32_t tot;
   const int32_t fs = block_excl_scan_i32<WT>(c.x | (c.y << 16), lds, &tot);
+  // the block's new entries are [bo.x, bo.x + nblk_out): staged in LDS and
+  // written with whole-line streaming stores when they fit (block-uniform)
+  const int32_t nblk_out = tot & 0xFFFF;
+  const bool staged = nblk_out <= EMIT_CAP;
   const int32_t dg = block_excl_scan_i32<WT>(c.z | (c.w << 16), lds, &tot);
   int64_t qf = bo.x + (fs & 0xFFFF);
   const int64_t qs = bo.y + (fs >> 16);
@@ -715,9 +741,16 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
             cc -= K;
             ++r;
           }
-          row[qf] = r;
-          col[qf] = cc;
-          vals[qf] = v[u];
+          if (staged) {
+            const int32_t i = (int32_t)(qf - bo.x);
+            srow[i] = r;
+            scol[i] = cc;
+            sval[i] = v[u];
+          } else {
+            row[qf] = r;
+            col[qf] = cc;
+            vals[qf] = v[u];
+          }
         }
         ++qf;
       }
@@ -739,6 +772,15 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       Gw &= Gw - 1;
       if (qg < n_drop) grown_lin[qg] = pw + b;
       ++qg;
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    const int64_t lim = std::min<int64_t>(nblk_out, nnz - bo.x);
+    for (int64_t j = t; j < lim; j += WT) {
+      __builtin_nontemporal_store(srow[j], &row[bo.x + j]);
+      __builtin_nontemporal_store(scol[j], &col[bo.x + j]);
+      __builtin_nontemporal_store(sval[j], &vals[bo.x + j]);
     }
   }
 }
