@@ -40,7 +40,7 @@ namespace snk {
 constexpr int MP_MAX_THREADS = 256;
 constexpr int MP_RC = 8;        // entries a group gathers at once (one round of its run)
 constexpr int MP_MAX_BW = 32;   // batch columns per workgroup (CH * G)
-constexpr int MP_SU = 8;        // staged items per thread per staging round
+constexpr int MP_SU = 4;        // staged items per thread per staging round
 
 // Merge-path point of local diagonal d inside a tile: the number x of
 // segment ends consumed (end x' is consumed before entry j iff end[x'] <= j).
