@@ -62,6 +62,27 @@ __device__ __forceinline__ void store_vec(T* __restrict__ p, const float (&in)[N
   *reinterpret_cast<vec<T, N>*>(p) = r;
 }
 
+// acc + sum_c a[c] * b[c] in fp32; bf16 pairs go through v_dot2_f32_bf16
+// (exact bf16 products summed into the fp32 accumulator).
+template <typename T, int CH>
+__device__ __forceinline__ float dot_acc(const vec<T, CH>& a, const vec<T, CH>& b, float acc) {
+  if constexpr (sizeof(T) == 2 && CH >= 2) {
+    typedef __bf16 __attribute__((ext_vector_type(2))) bf2;
+#pragma unroll
+    for (int c = 0; c < CH; c += 2) {
+      const uint32_t pa = (uint32_t)a.v[c] | ((uint32_t)a.v[c + 1] << 16);
+      const uint32_t pb = (uint32_t)b.v[c] | ((uint32_t)b.v[c + 1] << 16);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pa),
+                                            __builtin_bit_cast(bf2, pb), acc, false);
+    }
+    return acc;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc = fmaf(elem<T>::to_f(a.v[c]), elem<T>::to_f(b.v[c]), acc);
+    return acc;
+  }
+}
+
 // ---------------------------------------------------------------- activations
 // Elementwise nonlinearity applied to a finished fp32 output before it is
 // rounded and stored (0 none, 1 ReLU, 2 exact GELU).

@@ -70,6 +70,14 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
 snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* X,
                               const void* dY, snack_layout lay, int32_t B, void* dX, void* dV,
                               float lr, float* carry, void* act_tmp, hipStream_t s);
+// Wave-per-segment products (wave.hip), for views with no split segment.
+// Activations already node-major; launch_wave_sddmm returns false (and
+// launches nothing) when one pass of the kernel cannot cover the batch.
+bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B);
+void launch_wave_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* Xt,
+                      int32_t B, void* Y, bool node_out, int32_t act, hipStream_t s);
+bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
+                       int32_t B, void* dV, hipStream_t s);
 hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
                              const void* in1, void* out1, int32_t R1, int32_t C1,
                              hipStream_t s);

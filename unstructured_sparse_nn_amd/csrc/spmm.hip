@@ -68,27 +68,6 @@ __device__ __forceinline__ void store_out(T* __restrict__ Y, int32_t s, int32_t 
   }
 }
 
-// acc + sum_c a[c] * b[c] in fp32; bf16 pairs go through v_dot2_f32_bf16
-// (exact bf16 products summed into the fp32 accumulator).
-template <typename T, int CH>
-__device__ __forceinline__ float dot_acc(const vec<T, CH>& a, const vec<T, CH>& b, float acc) {
-  if constexpr (sizeof(T) == 2 && CH >= 2) {
-    typedef __bf16 __attribute__((ext_vector_type(2))) bf2;
-#pragma unroll
-    for (int c = 0; c < CH; c += 2) {
-      const uint32_t pa = (uint32_t)a.v[c] | ((uint32_t)a.v[c + 1] << 16);
-      const uint32_t pb = (uint32_t)b.v[c] | ((uint32_t)b.v[c + 1] << 16);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pa),
-                                            __builtin_bit_cast(bf2, pb), acc, false);
-    }
-    return acc;
-  } else {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc = fmaf(elem<T>::to_f(a.v[c]), elem<T>::to_f(b.v[c]), acc);
-    return acc;
-  }
-}
-
 // Shared-memory layout of one tile (dynamic LDS).
 struct tile_lds {
   int32_t* end;    // [2T] segment end offsets of the tile's segments
@@ -803,6 +782,10 @@ snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt
     Xt = act_tmp;
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
+  if (wave_eligible(v, dt, B)) {  // no split segment: one wave per segment
+    launch_wave_spmm(v, vals, dt, Xt, B, Y, node_out, act, s);
+    return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+  }
   lane_shape sh = pick_shape(dt, B, v.tile);
   if (dt == SNACK_F32) launch_dt<float>(v, vals, Xt, node_out, B, Y, carry, sh, act, s);
   else launch_dt<bf16>(v, vals, Xt, node_out, B, Y, carry, sh, act, s);
@@ -936,6 +919,8 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
     Xt = xt;
     dYt = gt;
   }
+  if (wave_eligible(v, dt, B) && launch_wave_sddmm(v, dYt, Xt, dt, B, dV, s))
+    return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   lane_shape sh = pick_shape(dt, B, v.tile, true);
   if (dt == SNACK_F32) launch_sddmm_dt<float>(v, dYt, Xt, B, dV, sh, s);
   else launch_sddmm_dt<bf16>(v, dYt, Xt, B, dV, sh, s);
