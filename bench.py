@@ -572,10 +572,16 @@ def run_bench(args):
     log(f"timing {K_} steps")
     t0 = time.perf_counter()
     for i in range(K_):
-        step(args.warmup + i, ev[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / K_ * 1e3
+    # per-op breakdown: the same steps again with events between the calls
+    # (kept out of the headline loop, whose host time they would add to)
+    log(f"per-op events over {K_} more steps")
+    for i in range(K_):
+        step(args.warmup + K_ + i, ev[i])
+    torch.cuda.synchronize()
 
     n_ops = 3 if args.products_only else (4 if fused else 5)
     ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(n_ops)]

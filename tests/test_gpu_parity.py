@@ -796,3 +796,70 @@ def test_conv1x1_layouts_and_fixed_kernel(orc, dt):
     Yf = torch.empty_like(Yn)
     snk.snack_fixed_fwd(f, Xc, HW, N, Yf)
     assert_within(from_dev(Yf, dt), refc, Sc, dt, "NCHW fixed kernel")
+
+
+# ---------------------------------------------------- wave-per-segment path
+# Views with no split segment run one wave per segment (wave.hip); a tile of
+# 2048 items keeps rows of up to 2047 entries whole, so these cases exercise
+# segments spanning several 256-entry load batches, partial gather rounds and
+# the batch passes of wide batches.
+WAVE = [  # (M, K, row degrees lo..hi, Bsz, dt, layout)
+    (40, 1500, (0, 1200), 1, "f32", "node"),
+    (40, 1500, (0, 1200), 3, "bf16", "batch"),
+    (40, 1500, (0, 1200), 8, "bf16", "node"),
+    (40, 1500, (0, 1200), 16, "f32", "batch"),
+    (40, 1500, (0, 1200), 32, "bf16", "node"),
+    (40, 1500, (0, 1200), 32, "f32", "node"),
+    (40, 1500, (0, 1200), 64, "bf16", "node"),
+    (40, 1500, (0, 1200), 64, "f32", "batch"),
+    (40, 1500, (0, 1200), 100, "f32", "node"),
+    (33, 700, (1, 300), 12, "bf16", "batch"),
+    (33, 700, (1, 300), 6, "f32", "node"),
+]
+
+
+@pytest.mark.parametrize("M,K,deg,Bsz,dt,layout", WAVE)
+def test_wave_products_long_segments_and_batches(orc, M, K, deg, Bsz, dt, layout):
+    rng = np.random.default_rng(M * 1000 + Bsz)
+    d = rng.integers(deg[0], deg[1] + 1, size=M)
+    d[:3] = (0, deg[1], 257)  # an empty row, the longest row, one past a load batch
+    lin = np.concatenate([r * K + np.sort(rng.choice(K, n, replace=False))
+                          for r, n in enumerate(d)])
+    w = synth.random_case(11, M, K, lin.size, Bsz, dt, layout, positions=lin)
+    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile=2048,
+                        repeat_check=True)
+    assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_wave_products_match_merge_path(orc, dt):
+    """The same layer through both kernels (default tiles: no split, wave
+    path; 16-item tiles: splits, merge path) agrees with the oracle."""
+    w = synth.random_case(13, 200, 300, 9000, 8, dt, "node")
+    a = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, "node", 8, tile=0)
+    b = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, "node", 8, tile=16)
+    assert a.plan.has_split_row == 0 and b.plan.has_split_row == 1
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_wave_inf_at_segment_end_stays_inf(dt):
+    """Lanes past a segment's end gather at its last entry's index; that row
+    holding Inf must not turn the row's result into NaN (0 * Inf)."""
+    M, K, Bsz = 4, 64, 8
+    lin = np.array([0 * K + 5, 0 * K + 9, 1 * K + 9, 2 * K + 1, 2 * K + 2, 2 * K + 63],
+                   dtype=np.int64)
+    w = synth.random_case(17, M, K, lin.size, Bsz, dt, "node", positions=lin).weights[0]
+    topo = topology(w, Bsz)
+    assert topo.plan.has_split_row == 0
+    vals = torch.ones(lin.size, dtype=torch_dtype(dt), device="cuda")
+    X = torch.ones(K * Bsz, dtype=torch_dtype(dt), device="cuda")
+    X.view(K, Bsz)[9] = float("inf")  # column 9 ends rows 0 and 1
+    Y = topo.fwd(vals, X, Bsz, B.NODE_MAJOR).float().view(M, Bsz).cpu().numpy()
+    assert np.isposinf(Y[0]).all() and np.isposinf(Y[1]).all()
+    assert (Y[2] == 3.0).all() and (Y[3] == 0.0).all()
+    dY = torch.ones(M * Bsz, dtype=torch_dtype(dt), device="cuda")
+    dY.view(M, Bsz)[2] = float("inf")  # row 2 ends column 63 and holds columns 1, 2
+    dX = topo.bwd_input(vals, dY, Bsz, B.NODE_MAJOR).float().view(K, Bsz).cpu().numpy()
+    for c in (1, 2, 63):
+        assert np.isposinf(dX[c]).all()
+    assert (dX[5] == 1.0).all() and (dX[9] == 2.0).all() and (dX[0] == 0.0).all()

@@ -145,9 +145,9 @@ def _dtype(*cands, dtype=None) -> int:
 
 
 def _stream(stream):
-    if stream is None:
+    if stream is None:  # torch's current stream, as a raw handle (no Stream object built)
         import torch
-        return torch.cuda.current_stream().cuda_stream or None
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()) or None
     if isinstance(stream, int):
         return stream or None
     return stream.cuda_stream or None
