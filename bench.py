@@ -194,7 +194,7 @@ def graph_kernel_us(insts, op, launches=20, replays=5):
 
 def src_hash():
     h = hashlib.sha256()
-    for f in ("spmm.hip", "common.h"):
+    for f in ("spmm.hip", "wave.hip", "common.h"):
         h.update(open(os.path.join(ROOT, "unstructured_sparse_nn_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -614,8 +614,13 @@ def run_bench(args):
     ops["bwd_fused"] = {"us_kernel": fus, "algo_bytes": fb, "GBps_kernel": round(fb / (fus * 1e3), 1),
                         "note": "dX + dV in one call; not part of the timed step"}
     dom = max(("fwd", "bwd_input", "sddmm"), key=lambda o: ops[o]["us_kernel"])
-    kname = {"fwd": "k_seg_spmm (row view)", "bwd_input": "k_seg_spmm (column view)",
-             "sddmm": "k_sddmm"}[dom]
+    # views with no split segment run the wave-per-segment kernels
+    plan0 = insts[0].topo.plan
+    split = plan0.has_split_col if dom == "bwd_input" else plan0.has_split_row
+    kname = ({"fwd": "k_wave_spmm (row view)", "bwd_input": "k_wave_spmm (column view)",
+              "sddmm": "k_wave_sddmm"} if not split else
+             {"fwd": "k_seg_spmm (row view)", "bwd_input": "k_seg_spmm (column view)",
+              "sddmm": "k_sddmm"})[dom]
     ach = ops[dom]["algo_bytes"] / (ops[dom]["us_kernel"] * 1e-6) / 1e9
     tag = f"{dom}_square{N}_s{sp}_B{B}_bf16"
     traffic = read_traffic(tag, ops[dom]["algo_bytes"])

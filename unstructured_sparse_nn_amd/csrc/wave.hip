@@ -153,10 +153,39 @@ __device__ __forceinline__ void spmm_rounds(const T* __restrict__ xb, int32_t B,
     xv[i] = *reinterpret_cast<const vec<T, CH>*>(xb + (int64_t)cj * B);
   }
   zero_unless<T, CH>(xv[NR - 1], rb + (NR - 1) * EPI + slot < e);
+  if constexpr (sizeof(T) == 2 && CH >= 2) {
+    // bf16: rounds i and i+1 together, acc[c] += v_i x_i[c] + v_i+1 x_i+1[c]
+    // in one v_dot2_f32_bf16 per column; the pairs (x_i[c], x_i+1[c]) come
+    // from one byte permute of the two gathered words (a bf16 value v is the
+    // high half of its fp32 widening, so (v_i, v_i+1) is a permute too)
+    typedef __bf16 __attribute__((ext_vector_type(2))) bf2;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NR; i += 2) {
+      const bool two = i + 1 < NR;
+      const uint32_t va = __float_as_uint(vj[i]);
+      const uint32_t vb = two ? __float_as_uint(vj[i + 1]) : 0u;
+      const uint32_t vp = __builtin_amdgcn_perm(vb, va, 0x07060302u);
+      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xv[i]);
+      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xv[two ? i + 1 : i]);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = fmaf(vj[i], elem<T>::to_f(xv[i].v[c]), acc[c]);
+      for (int w = 0; w < CH / 2; ++w) {
+        const uint32_t b = two ? wb[w] : 0u;
+        const uint32_t lo = __builtin_amdgcn_perm(b, wa[w], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(b, wa[w], 0x07060302u);
+        acc[2 * w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, vp),
+                                                     __builtin_bit_cast(bf2, lo), acc[2 * w],
+                                                     false);
+        acc[2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, vp),
+                                                         __builtin_bit_cast(bf2, hi),
+                                                         acc[2 * w + 1], false);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[c] = fmaf(vj[i], elem<T>::to_f(xv[i].v[c]), acc[c]);
+    }
   }
 }
 
