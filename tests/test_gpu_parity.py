@@ -487,6 +487,9 @@ FUSED_BWD = [
     ("ragged", "bf16", "batch", 3, 64, 0.1),
     ("ragged", "bf16", "node", 32, 0, 0.2),
     ("skewed", "f32", "batch", 16, 64, 0.1),   # one dense column spanning many tiles
+    # columns of ~750 entries kept whole (wave path over several load batches)
+    ("long", "bf16", "node", 32, 2048, 0.1),
+    ("long", "f32", "batch", 7, 2048, 0.0),
 ]
 
 
@@ -496,6 +499,8 @@ def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
     separate products, and the SGD step of their definition."""
     if name == "ragged":
         w = synth.random_case(15, 300, 200, 9000, Bsz, dt, layout)
+    elif name == "long":
+        w = synth.random_case(18, 1500, 40, 30000, Bsz, dt, layout)
     elif name == "skewed":
         lin = np.concatenate([np.arange(64) * 40 + 7, np.arange(3000) + 64 * 40])
         lin = np.unique(lin[lin < 80 * 40])

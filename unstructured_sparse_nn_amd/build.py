@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsnack.so")
 SOURCES = ["api.hip", "prims.hip", "prepare.hip", "spmm.hip", "prune.hip", "prune_bitmap.hip",
-           "aux.hip", "fixed.hip", "wave.hip"]
+           "aux.hip", "fixed.hip", "wave.hip", "wave_fused.hip"]
 ARCH = os.environ.get("SNACK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -78,6 +78,10 @@ void launch_wave_spmm(const seg_view& v, const void* vals, snack_dtype dt, const
                       int32_t B, void* Y, bool node_out, int32_t act, hipStream_t s);
 bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
                        int32_t B, void* dV, hipStream_t s);
+// Column view: dX, dV (nullable) and the optional update (wave_fused.hip).
+bool launch_wave_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* dYt,
+                           const void* Xt, int32_t B, void* dX, void* dV, float lr,
+                           bool node_out, hipStream_t s);
 hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
                              const void* in1, void* out1, int32_t R1, int32_t C1,
                              hipStream_t s);

@@ -861,6 +861,9 @@ snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, con
     Xt = xt;
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
+  if (wave_eligible(v, dt, B) &&
+      launch_wave_bwd_fused(v, vals, dt, dYt, Xt, B, dX, dV, lr, node_out, s))
+    return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   if (dt == SNACK_F32)
     launch_fused_dt<float>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
   else

@@ -25,169 +25,12 @@
 // instructions per stored entry on that bookkeeping; this one spends
 // about 1.5.
 #include <cstdlib>
-#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
+#include "wave.h"
 
 namespace snk {
-
-constexpr int WV_THREADS = 256;  // four waves per workgroup, one segment each
-constexpr int WV_U = 4;          // index/value loads of 64 entries kept in flight
-
-// Segment handled by this wave; blocks are spread over the dies so that each
-// die covers one contiguous range when xcd_blocks > 0.
-__device__ __forceinline__ int32_t wave_segment(int32_t xcd_blocks) {
-  const int32_t blk = xcd_blocks > 0
-                          ? (int32_t)(blockIdx.x % NUM_XCD) * xcd_blocks +
-                                (int32_t)(blockIdx.x / NUM_XCD)
-                          : (int32_t)blockIdx.x;
-  return __builtin_amdgcn_readfirstlane(blk * (WV_THREADS / SNK_WAVE) +
-                                        (int32_t)(threadIdx.x / SNK_WAVE));
-}
-
-// Butterfly reduce-scatter of acc[CH] over the lanes that share (lane mod
-// LPE): after the call, lane l holds in acc[0] the total of batch column
-// col_of(l) of its LPE group, where that column's bits come from lane bits
-// 5, 4, ... (most significant first).  CH <= 64 / LPE.
-template <int CH, int LPE>
-__device__ __forceinline__ int reduce_scatter(float (&acc)[CH], int lane) {
-  int c = 0;
-  int o = 32;
-#pragma unroll
-  for (int n = CH; n > 1; n >>= 1, o >>= 1) {
-    const bool up = (lane & o) != 0;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float send = up ? acc[i] : acc[i + n / 2];
-      const float keep = up ? acc[i + n / 2] : acc[i];
-      acc[i] = keep + __shfl_xor(send, o, SNK_WAVE);
-    }
-    if (up) c += n / 2;
-  }
-#pragma unroll
-  for (; o >= LPE; o >>= 1) acc[0] += __shfl_xor(acc[0], o, SNK_WAVE);
-  return c;
-}
-
-// x <- 0 where !ok, on the raw words of a gathered chunk (an entry past the
-// segment's end was gathered at a valid, clamped address and must not add
-// even an Inf or NaN of that row).
-template <typename T, int CH>
-__device__ __forceinline__ void zero_unless(vec<T, CH>& x, bool ok) {
-  constexpr int W = (int)(CH * sizeof(T) + 3) / 4;
-  if constexpr (CH * sizeof(T) >= 4) {
-    uint32_t* w = reinterpret_cast<uint32_t*>(&x);
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = ok ? w[i] : 0u;
-  } else {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) x.v[c] = ok ? x.v[c] : (T)0;
-  }
-}
-
-// Loads entries base + q*64 + lane (q < WV_U) with their index clamped to the
-// segment's last entry, so that every load is unconditional and all of them
-// are in flight together.  Values past the end are 0.
-template <typename T, bool PERM, bool VALS>
-__device__ __forceinline__ void load_entries(const int32_t* __restrict__ idx,
-                                             const int32_t* __restrict__ perm,
-                                             const T* __restrict__ vals, int32_t base, int32_t e,
-                                             int lane, int32_t (&ci)[WV_U], float (&cv)[WV_U]) {
-  int32_t kc[WV_U];
-#pragma unroll
-  for (int q = 0; q < WV_U; ++q) kc[q] = min(base + q * SNK_WAVE + lane, e - 1);
-#pragma unroll
-  for (int q = 0; q < WV_U; ++q) ci[q] = idx[kc[q]];
-  if constexpr (VALS) {
-    T raw[WV_U];
-    if constexpr (PERM) {
-      int32_t pk[WV_U];
-#pragma unroll
-      for (int q = 0; q < WV_U; ++q) pk[q] = perm[kc[q]];
-#pragma unroll
-      for (int q = 0; q < WV_U; ++q) raw[q] = vals[pk[q]];
-    } else {
-#pragma unroll
-      for (int q = 0; q < WV_U; ++q) raw[q] = vals[kc[q]];
-    }
-#pragma unroll
-    for (int q = 0; q < WV_U; ++q)
-      cv[q] = (base + q * SNK_WAVE + lane < e) ? elem<T>::to_f(raw[q]) : 0.f;
-  }
-}
-
-// Gather rounds issued together before any is consumed: at most 16 (one
-// gathered chunk each per lane), never more than one loaded batch holds.
-template <int LPE>
-constexpr int wave_rg() {
-  return 4 * LPE < 16 ? 4 * LPE : 16;
-}
-
-// Calls f(integral_constant<N>) for the runtime n in [1, NMAX], so that a
-// round group runs straight-line code with no exit inside (the compiler
-// sinks gathers into conditional blocks and waits for each there).
-template <int NMAX, typename F>
-__device__ __forceinline__ void with_count(int n, F&& f) {
-  if constexpr (NMAX >= 1) {
-    if (n >= NMAX) f(std::integral_constant<int, NMAX>{});
-    else with_count<NMAX - 1>(n, f);
-  }
-}
-
-// NR gather rounds of EPI entries each, from the loaded chunks ci/cv (round i
-// takes chunk i / LPE, lanes (i % LPE) * EPI + slot).  Every gather first,
-// then the FMAs; only the last round can hold entries past the end.
-template <typename T, int CH, int LPE, int NR>
-__device__ __forceinline__ void spmm_rounds(const T* __restrict__ xb, int32_t B,
-                                            const int32_t* ci, const float* cv, int32_t rb,
-                                            int32_t e, int slot, float (&acc)[CH]) {
-  constexpr int EPI = SNK_WAVE / LPE;
-  vec<T, CH> xv[NR];
-  float vj[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int q = i / LPE, src = (i % LPE) * EPI + slot;
-    const int32_t cj = LPE == 1 ? ci[q] : __shfl(ci[q], src, SNK_WAVE);
-    vj[i] = LPE == 1 ? cv[q] : __shfl(cv[q], src, SNK_WAVE);
-    xv[i] = *reinterpret_cast<const vec<T, CH>*>(xb + (int64_t)cj * B);
-  }
-  zero_unless<T, CH>(xv[NR - 1], rb + (NR - 1) * EPI + slot < e);
-  if constexpr (sizeof(T) == 2 && CH >= 2) {
-    // bf16: rounds i and i+1 together, acc[c] += v_i x_i[c] + v_i+1 x_i+1[c]
-    // in one v_dot2_f32_bf16 per column; the pairs (x_i[c], x_i+1[c]) come
-    // from one byte permute of the two gathered words (a bf16 value v is the
-    // high half of its fp32 widening, so (v_i, v_i+1) is a permute too)
-    typedef __bf16 __attribute__((ext_vector_type(2))) bf2;
-#pragma unroll
-    for (int i = 0; i < NR; i += 2) {
-      const bool two = i + 1 < NR;
-      const uint32_t va = __float_as_uint(vj[i]);
-      const uint32_t vb = two ? __float_as_uint(vj[i + 1]) : 0u;
-      const uint32_t vp = __builtin_amdgcn_perm(vb, va, 0x07060302u);
-      const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xv[i]);
-      const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xv[two ? i + 1 : i]);
-#pragma unroll
-      for (int w = 0; w < CH / 2; ++w) {
-        const uint32_t b = two ? wb[w] : 0u;
-        const uint32_t lo = __builtin_amdgcn_perm(b, wa[w], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(b, wa[w], 0x07060302u);
-        acc[2 * w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, vp),
-                                                     __builtin_bit_cast(bf2, lo), acc[2 * w],
-                                                     false);
-        acc[2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, vp),
-                                                         __builtin_bit_cast(bf2, hi),
-                                                         acc[2 * w + 1], false);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) acc[c] = fmaf(vj[i], elem<T>::to_f(xv[i].v[c]), acc[c]);
-    }
-  }
-}
 
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
@@ -212,9 +55,9 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
   for (int c = 0; c < CH; ++c) acc[c] = 0.f;
 
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
-    int32_t ci[WV_U];
+    int32_t ci[WV_U], pk[WV_U];
     float cv[WV_U];
-    load_entries<T, PERM, true>(idx, perm, vals, base, e, lane, ci, cv);
+    load_entries<T, PERM, true>(idx, perm, vals, base, e, lane, ci, cv, pk);
 #pragma unroll
     for (int g = 0; g < WV_U * LPE / RG; ++g) {
       const int q0 = g * RG / LPE;
@@ -239,47 +82,23 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
 }
 
 // The value gradient of NR rounds: every gather first, then the dots and the
-// LPE-lane sums, then per chunk of 64 entries one permute to lane = entry
-// and one coalesced store.
+// LPE-lane sums, then per chunk of 64 entries one coalesced store.
 template <typename T, int CH, int LPE, int NR>
 __device__ __forceinline__ void sddmm_rounds(const T* __restrict__ xb, int32_t B,
                                              const vec<T, CH>& g, const int32_t* ci,
                                              int32_t rb, int32_t e, int lane, int slot,
                                              T* __restrict__ dV) {
-  constexpr int EPI = SNK_WAVE / LPE;
-  constexpr int NQ = (NR + LPE - 1) / LPE;  // chunks touched
+  constexpr int NQ = (NR + LPE - 1) / LPE;
   vec<T, CH> xv[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int q = i / LPE, src = (i % LPE) * EPI + slot;
-    const int32_t cj = LPE == 1 ? ci[q] : __shfl(ci[q], src, SNK_WAVE);
-    xv[i] = *reinterpret_cast<const vec<T, CH>*>(xb + (int64_t)cj * B);
-  }
-  float res[NQ * LPE];
-#pragma unroll
-  for (int i = 0; i < NQ * LPE; ++i) {
-    float d = 0.f;
-    if (i < NR) {
-      d = dot_acc<T, CH>(g, xv[i], 0.f);
-#pragma unroll
-      for (int off = 1; off < LPE; off <<= 1) d += __shfl_xor(d, off, SNK_WAVE);
-    }
-    res[i] = d;
-  }
+  float unused_v[NR];
+  const float zeros[WV_U] = {0.f, 0.f, 0.f, 0.f};
+  gather_rounds<T, CH, LPE, NR>(xb, B, ci, zeros, rb, e, slot, xv, unused_v);
+  float out[NQ];
+  round_dots<T, CH, LPE, NR>(xv, g, lane, out);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    // entry q*64 + lane was dotted in round lane / EPI by slot lane % EPI
-    float out = res[q * LPE];
-    if constexpr (LPE > 1) {
-      const int from = (lane % EPI) * LPE;
-#pragma unroll
-      for (int j = 0; j < LPE; ++j) {
-        const float v = __shfl(res[q * LPE + j], from, SNK_WAVE);
-        if (lane / EPI == j) out = v;
-      }
-    }
     const int32_t k = rb + q * SNK_WAVE + lane;
-    if (k < e) dV[k] = elem<T>::from_f(out);
+    if (k < e) dV[k] = elem<T>::from_f(out[q]);
   }
 }
 
@@ -309,9 +128,10 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
   zero_unless<T, CH>(g, bvalid);
 
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
-    int32_t ci[WV_U];
+    int32_t ci[WV_U], unused_pk[WV_U];
     float unused[WV_U];
-    load_entries<T, false, false>(idx, nullptr, (const T*)nullptr, base, e, lane, ci, unused);
+    load_entries<T, false, false>(idx, nullptr, (const T*)nullptr, base, e, lane, ci, unused,
+                                  unused_pk);
 #pragma unroll
     for (int gi = 0; gi < WV_U * LPE / RG; ++gi) {
       const int q0 = gi * RG / LPE;
@@ -326,22 +146,6 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
 }
 
 // ---------------------------------------------------------------- host side
-struct wave_shape {
-  int ch;   // batch columns per lane
-  int lpe;  // lanes per entry
-};
-
-// Widest lane chunk dividing B (16-byte gathers at most), then the fewest
-// lanes per entry that cover the batch, capped at 64 batch columns per pass.
-static wave_shape wave_pick(snack_dtype dt, int32_t B) {
-  const int chmax = dt == SNACK_BF16 ? 8 : 4;
-  int ch = 1;
-  while (ch < chmax && B % (ch * 2) == 0) ch *= 2;
-  int lpe = 1;
-  while (lpe * ch < B && lpe * ch < 64) lpe *= 2;
-  return {ch, lpe};
-}
-
 // Up to 16 lanes per entry (odd batches above 16 columns take the
 // merge-path kernels, whose lane groups suit them better).
 bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B) {

@@ -1,0 +1,154 @@
+// wave_fused.hip -- the fused backward over the column view, one wave per
+// column, for views with no split segment.
+//
+// For column c (a segment of the column view: entries k' in the column's
+// range, their rows r = row_t[k'] and value positions p = perm[k']):
+//   dX[b, c] = sum_k' v[p] dY[b, r]            (the input gradient)
+//   dV[p]    = sum_b dY[b, r] X[b, c]          (the value gradient)
+//   v[p]    <- RNE(v[p] - lr dV[p])            (optional SGD step, lr != 0)
+// Both gradients ("Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural
+// Networks on GPU", Abstract: backpropagation entirely in the sparse
+// paradigm) share one gather of the dY row per entry: its chunk is added,
+// scaled by the value, into the column's dX sums, and dotted with the
+// column's X chunk (loaded once per wave) for dV.  dV and the updated value
+// are written through perm by the lane that loaded the entry.  Each value is
+// read and written by that one lane only, so the in-place update races with
+// nothing.
+#include "common.h"
+#include "internal.h"
+#include "wave.h"
+
+namespace snk {
+
+template <typename T, int CH, int LPE, int NR>
+__device__ __forceinline__ void fused_rounds(const T* __restrict__ gb, int32_t B,
+                                             const vec<T, CH>& xs, const int32_t* ci,
+                                             const float* cv, const int32_t* pk, int32_t rb,
+                                             int32_t e, int lane, int slot, float (&acc)[CH],
+                                             T* __restrict__ dV, T* vals_upd, float lr) {
+  constexpr int NQ = (NR + LPE - 1) / LPE;
+  vec<T, CH> gv[NR];
+  float vj[NR];
+  gather_rounds<T, CH, LPE, NR>(gb, B, ci, cv, rb, e, slot, gv, vj);
+  accumulate_rounds<T, CH, NR>(gv, vj, acc);
+  float d[NQ];
+  round_dots<T, CH, LPE, NR>(gv, xs, lane, d);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (rb + q * SNK_WAVE + lane < e) {
+      if (dV) dV[pk[q]] = elem<T>::from_f(d[q]);
+      if (lr != 0.f) vals_upd[pk[q]] = elem<T>::from_f(cv[q] - lr * d[q]);
+    }
+  }
+}
+
+// One pass covers the batch: B <= LPE * CH.
+template <typename T, int CH, int LPE, bool NODE_OUT>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_bwd_fused(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, T* vals, const T* __restrict__ dYt,
+    const T* __restrict__ Xt, T* __restrict__ dX, T* __restrict__ dV, float lr, int32_t S,
+    int32_t B, int32_t xcd_blocks) {
+  constexpr int EPI = SNK_WAVE / LPE;
+  constexpr int RG = wave_rg<LPE>();
+  static_assert(CH <= EPI, "reduce-scatter needs CH <= 64 / LPE");
+  const int32_t s = wave_segment(xcd_blocks);
+  if (s >= S) return;
+  const int lane = lane_id();
+  const int slot = lane / LPE;
+  const int sub = lane % LPE;
+  const int32_t b0 = sub * CH;
+  const bool bvalid = b0 < B;
+  const T* __restrict__ gb = dYt + (bvalid ? b0 : 0);
+  vec<T, CH> xs = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)s * B + (bvalid ? b0 : 0));
+  zero_unless<T, CH>(xs, bvalid);
+  const int32_t a = ptr[s], e = ptr[s + 1];
+
+  float acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+
+  for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
+    int32_t ci[WV_U], pk[WV_U];
+    float cv[WV_U];
+    load_entries<T, true, true>(idx, perm, vals, base, e, lane, ci, cv, pk);
+#pragma unroll
+    for (int g = 0; g < WV_U * LPE / RG; ++g) {
+      const int q0 = g * RG / LPE;
+      const int32_t rb = base + g * RG * EPI;
+      if (rb >= e) break;
+      const int nr = (e - rb + EPI - 1) / EPI;
+      with_count<RG>(nr, [&](auto n) {
+        fused_rounds<T, CH, LPE, decltype(n)::value>(gb, B, xs, ci + q0, cv + q0, pk + q0, rb,
+                                                     e, lane, slot, acc, dV, vals, lr);
+      });
+    }
+  }
+
+  const int c = reduce_scatter<CH, LPE>(acc, lane);
+  constexpr int LOW = EPI / CH;
+  if ((slot % LOW) == 0 && bvalid) {
+    const int32_t b = b0 + c;
+    if constexpr (NODE_OUT) dX[(int64_t)s * B + b] = elem<T>::from_f(acc[0]);
+    else dX[(int64_t)b * S + s] = elem<T>::from_f(acc[0]);
+  }
+}
+
+template <typename T, int CH, int LPE>
+static void wave_fused_l(const seg_view& v, void* vals, const void* dYt, const void* Xt,
+                         int32_t B, void* dX, void* dV, float lr, bool node_out,
+                         hipStream_t s) {
+  const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
+  const int32_t xb = nblk >= 8 * NUM_XCD ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+  dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk));
+  if (node_out)
+    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, true>), grid, dim3(WV_THREADS), 0, s, v.ptr,
+                       v.idx, v.perm, (T*)vals, (const T*)dYt, (const T*)Xt, (T*)dX, (T*)dV, lr,
+                       v.S, B, xb);
+  else
+    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, false>), grid, dim3(WV_THREADS), 0, s,
+                       v.ptr, v.idx, v.perm, (T*)vals, (const T*)dYt, (const T*)Xt, (T*)dX,
+                       (T*)dV, lr, v.S, B, xb);
+}
+
+template <typename T, int CH>
+static bool wave_fused_c(const seg_view& v, void* vals, const void* dYt, const void* Xt,
+                         int32_t B, void* dX, void* dV, float lr, bool node_out, int lpe,
+                         hipStream_t s) {
+  switch (lpe) {
+    case 1: wave_fused_l<T, CH, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 2: wave_fused_l<T, CH, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 4: wave_fused_l<T, CH, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 8: wave_fused_l<T, CH, 8>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 16:
+      if constexpr (CH <= 4) {
+        wave_fused_l<T, CH, 16>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s);
+        return true;
+      }
+      return false;
+    default: return false;
+  }
+}
+
+bool launch_wave_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* dYt,
+                           const void* Xt, int32_t B, void* dX, void* dV, float lr,
+                           bool node_out, hipStream_t s) {
+  const wave_shape w = wave_pick(dt, B);
+  if ((int64_t)w.ch * w.lpe < B) return false;  // one pass must cover the batch
+  if (dt == SNACK_F32) {
+    switch (w.ch) {
+      case 1: return wave_fused_c<float, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+      case 2: return wave_fused_c<float, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+      default:
+        return wave_fused_c<float, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    }
+  }
+  switch (w.ch) {
+    case 1: return wave_fused_c<bf16, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    case 2: return wave_fused_c<bf16, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    case 4: return wave_fused_c<bf16, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    default: return wave_fused_c<bf16, 8>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+  }
+}
+
+}  // namespace snk
