@@ -3,6 +3,7 @@
 // groups and the butterfly reduce-scatter.
 #pragma once
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -217,6 +218,12 @@ __device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec
       }
     }
   }
+}
+
+// SNACK_NO_XCD_REMAP set: plain block order (for experiments).
+inline bool no_xcd_remap() {
+  static const bool off = getenv("SNACK_NO_XCD_REMAP") != nullptr;
+  return off;
 }
 
 struct wave_shape {

@@ -157,7 +157,7 @@ template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
                         hipStream_t s) {
   const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
-  const int32_t xb = (PERM && nblk >= 8 * NUM_XCD) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+  const int32_t xb = (PERM && nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
   dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk), (unsigned)cdiv(B, LPE * CH));
   hipLaunchKernelGGL((k_wave_spmm<T, CH, LPE, PERM, NODE_OUT, ACT>), grid, dim3(WV_THREADS), 0,
                      s, v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B, xb);

@@ -99,7 +99,7 @@ static void wave_fused_l(const seg_view& v, void* vals, const void* dYt, const v
                          int32_t B, void* dX, void* dV, float lr, bool node_out,
                          hipStream_t s) {
   const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
-  const int32_t xb = nblk >= 8 * NUM_XCD ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+  const int32_t xb = (nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
   dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk));
   if (node_out)
     hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, true>), grid, dim3(WV_THREADS), 0, s, v.ptr,
