@@ -73,9 +73,16 @@ snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, con
 // Wave-per-segment products (wave.hip), for views with no split segment.
 // Activations already node-major; launch_wave_sddmm returns false (and
 // launches nothing) when one pass of the kernel cannot cover the batch.
-bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B);
+// With split = true, views with split segments qualify too: their tile
+// pieces go through the carry slots (P x B and P x B fp32) and k_fixup.
+bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B, bool split);
 void launch_wave_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* Xt,
-                      int32_t B, void* Y, bool node_out, int32_t act, hipStream_t s);
+                      int32_t B, void* Y, bool node_out, int32_t act, float* carry,
+                      hipStream_t s);
+// out[s] = act(sum of the carry slots of split segment s) for every split
+// segment (k_fixup, spmm.hip).
+void launch_fixup(const seg_view& v, snack_dtype dt, bool node_out, int32_t act,
+                  const float* carry, void* Y, int32_t B, hipStream_t s);
 bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
                        int32_t B, void* dV, hipStream_t s);
 // Column view: dX, dV (nullable) and the optional update (wave_fused.hip).

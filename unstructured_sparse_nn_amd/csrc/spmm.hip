@@ -770,6 +770,30 @@ static void launch_dt(const seg_view& v, const void* vals, const void* Xt, bool 
   }
 }
 
+template <typename T, bool NODE_OUT>
+static void fixup_t(const seg_view& v, int32_t act, const float* carry, void* Y, int32_t B,
+                    hipStream_t s) {
+  const int64_t n = (int64_t)v.P * B;
+  const dim3 g((unsigned)cdiv(n, 256));
+  if (act == ACT_RELU)
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_RELU>), g, dim3(256), 0, s, v.part_seg, v.cut,
+                       carry, (T*)Y, v.S, B, v.P);
+  else
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_NONE>), g, dim3(256), 0, s, v.part_seg, v.cut,
+                       carry, (T*)Y, v.S, B, v.P);
+}
+
+void launch_fixup(const seg_view& v, snack_dtype dt, bool node_out, int32_t act,
+                  const float* carry, void* Y, int32_t B, hipStream_t s) {
+  if (dt == SNACK_F32) {
+    if (node_out) fixup_t<float, true>(v, act, carry, Y, B, s);
+    else fixup_t<float, false>(v, act, carry, Y, B, s);
+  } else {
+    if (node_out) fixup_t<bf16, true>(v, act, carry, Y, B, s);
+    else fixup_t<bf16, false>(v, act, carry, Y, B, s);
+  }
+}
+
 snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* X,
                              snack_layout lay, int32_t B, void* Y, float* carry, void* act_tmp,
                              hipStream_t s, int32_t act) {
@@ -782,8 +806,8 @@ snack_status launch_seg_spmm(const seg_view& v, const void* vals, snack_dtype dt
     Xt = act_tmp;
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
-  if (wave_eligible(v, dt, B)) {  // no split segment: one wave per segment
-    launch_wave_spmm(v, vals, dt, Xt, B, Y, node_out, act, s);
+  if (wave_eligible(v, dt, B, true)) {  // one wave per segment, tile pieces for split ones
+    launch_wave_spmm(v, vals, dt, Xt, B, Y, node_out, act, carry, s);
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   }
   lane_shape sh = pick_shape(dt, B, v.tile);
@@ -861,7 +885,7 @@ snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, con
     Xt = xt;
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
-  if (wave_eligible(v, dt, B) &&
+  if (wave_eligible(v, dt, B, false) &&
       launch_wave_bwd_fused(v, vals, dt, dYt, Xt, B, dX, dV, lr, node_out, s))
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   if (dt == SNACK_F32)
@@ -922,7 +946,7 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
     Xt = xt;
     dYt = gt;
   }
-  if (wave_eligible(v, dt, B) && launch_wave_sddmm(v, dYt, Xt, dt, B, dV, s))
+  if (wave_eligible(v, dt, B, true) && launch_wave_sddmm(v, dYt, Xt, dt, B, dV, s))
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
   lane_shape sh = pick_shape(dt, B, v.tile, true);
   if (dt == SNACK_F32) launch_sddmm_dt<float>(v, dYt, Xt, B, dV, sh, s);

@@ -24,6 +24,7 @@
 // 4096^2, 95%, batch 32 bf16, the merge-path kernel spent about 4.7 wave
 // instructions per stored entry on that bookkeeping; this one spends
 // about 1.5.
+#include <climits>
 #include <cstdlib>
 
 #include "common.h"
@@ -32,28 +33,17 @@
 
 namespace snk {
 
-template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
-    T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks) {
-  constexpr int EPI = SNK_WAVE / LPE;  // entries per gather round
-  constexpr int RG = wave_rg<LPE>();   // rounds per group (a whole number of chunks)
-  static_assert(CH <= EPI, "reduce-scatter needs CH <= 64 / LPE");
-  const int32_t s = wave_segment(xcd_blocks);
-  if (s >= S) return;
-  const int lane = lane_id();
-  const int slot = lane / LPE;
-  const int sub = lane % LPE;
-  const int32_t b0 = (int32_t)blockIdx.y * (LPE * CH) + sub * CH;
-  const bool bvalid = b0 < B;
-  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);  // lanes past the batch read column 0
-  const int32_t a = ptr[s], e = ptr[s + 1];
-
-  float acc[CH];
+// acc[c] = sum over entries [a, e) of v * in[idx, b0 + c]: batches of four
+// 64-entry loads, each split into round groups of straight-line code.
+template <typename T, int CH, int LPE, bool PERM>
+__device__ __forceinline__ void spmm_range(const int32_t* __restrict__ idx,
+                                           const int32_t* __restrict__ perm, const T* vals,
+                                           const T* __restrict__ xb, int32_t B, int32_t a,
+                                           int32_t e, int lane, int slot, float (&acc)[CH]) {
+  constexpr int EPI = SNK_WAVE / LPE;
+  constexpr int RG = wave_rg<LPE>();  // rounds per group (a whole number of chunks)
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.f;
-
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
     int32_t ci[WV_U], pk[WV_U];
     float cv[WV_U];
@@ -69,7 +59,68 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
       });
     }
   }
+}
 
+// The tile pieces of split segments (segments of >= T entries, cut by the
+// load-balanced tiles), one wave per tile p, summed into the carry slots
+// that k_fixup adds in tile order:
+//   carry[p]     the piece of the segment that continues into tile p+1
+//                (cut p+1 is inside it): from the tile's start, or from the
+//                segment's start if it begins in this tile, to cut p+1;
+//   carry[P + p] the last piece of the segment cut at p: from cut p to its end.
+// Pieces are at most 2T entries, so no wave serialises a long segment.
+template <typename T, int CH, int LPE, bool PERM>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_pieces(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const T* __restrict__ vals,
+    const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
+    const int32_t* __restrict__ cut, const T* __restrict__ Xt, float* __restrict__ carry,
+    int32_t P, int32_t B) {
+  constexpr int EPI = SNK_WAVE / LPE;
+  constexpr int LOW = EPI / CH;
+  const int32_t p = wave_segment(0);
+  if (p >= P) return;
+  const int32_t s0 = part_seg[p], s1 = part_seg[p + 1];
+  const bool c0 = cut[p] != 0, c1 = cut[p + 1] != 0;
+  const bool last_piece = c0 && !(c1 && s1 == s0);
+  if (!c1 && !last_piece) return;
+  const int lane = lane_id();
+  const int slot = lane / LPE;
+  const int sub = lane % LPE;
+  const int32_t b0 = (int32_t)blockIdx.y * (LPE * CH) + sub * CH;
+  const bool bvalid = b0 < B;
+  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);
+  auto piece = [&](int32_t a, int32_t e, float* __restrict__ dst) {
+    float acc[CH];
+    spmm_range<T, CH, LPE, PERM>(idx, perm, vals, xb, B, a, e, lane, slot, acc);
+    const int c = reduce_scatter<CH, LPE>(acc, lane);
+    if ((slot % LOW) == 0 && bvalid) dst[b0 + c] = acc[0];
+  };
+  if (last_piece) piece(part_nz[p], ptr[s0 + 1], carry + ((int64_t)P + p) * B);
+  if (c1) piece((c0 && s0 == s1) ? part_nz[p] : ptr[s1], part_nz[p + 1], carry + (int64_t)p * B);
+}
+
+template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
+    T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks, int32_t long_len) {
+  constexpr int EPI = SNK_WAVE / LPE;  // entries per gather round
+  static_assert(CH <= EPI, "reduce-scatter needs CH <= 64 / LPE");
+  const int32_t s = wave_segment(xcd_blocks);
+  if (s >= S) return;
+  const int lane = lane_id();
+  const int slot = lane / LPE;
+  const int sub = lane % LPE;
+  const int32_t b0 = (int32_t)blockIdx.y * (LPE * CH) + sub * CH;
+  const bool bvalid = b0 < B;
+  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);  // lanes past the batch read column 0
+  const int32_t a = ptr[s], e = ptr[s + 1];
+
+  if (e - a >= long_len) return;  // a split segment: its tile pieces are summed elsewhere
+
+  float acc[CH];
+  spmm_range<T, CH, LPE, PERM>(idx, perm, vals, xb, B, a, e, lane, slot, acc);
   const int c = reduce_scatter<CH, LPE>(acc, lane);
   // lanes whose slot bits below the scattered ones are zero write
   constexpr int LOW = EPI / CH;  // slot values sharing one column after the scatter
@@ -102,31 +153,20 @@ __device__ __forceinline__ void sddmm_rounds(const T* __restrict__ xb, int32_t B
   }
 }
 
-// dV[k] for the entries of one row per wave: the row's dY chunk is loaded
-// once, each round gathers EPI entries' X chunks and dots them with it, the
-// LPE lanes of a slot add their partial dots, and every 64 entries the
-// results are permuted to lane = entry and stored coalesced.  B <= LPE * CH.
+// dV[k] for the entries [a, e) of segment s: the segment's dY chunk is
+// loaded once, each round gathers EPI entries' X chunks and dots them with
+// it, the LPE lanes of a slot add their partial dots, and every 64 entries
+// the results are permuted to lane = entry and stored coalesced.
 template <typename T, int CH, int LPE>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
-    int32_t B) {
+__device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
+                                            const T* __restrict__ dYt,
+                                            const T* __restrict__ xb, int32_t B, int32_t s,
+                                            int32_t a, int32_t e, int lane, int slot, int32_t b0,
+                                            bool bvalid, T* __restrict__ dV) {
   constexpr int EPI = SNK_WAVE / LPE;
   constexpr int RG = wave_rg<LPE>();
-  const int32_t s = wave_segment(0);
-  if (s >= S) return;
-  const int lane = lane_id();
-  const int slot = lane / LPE;
-  const int sub = lane % LPE;
-  const int32_t b0 = sub * CH;
-  const bool bvalid = b0 < B;
-  const int32_t a = ptr[s], e = ptr[s + 1];
-  if (a == e) return;
-  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);
-
   vec<T, CH> g = *reinterpret_cast<const vec<T, CH>*>(dYt + (int64_t)s * B + (bvalid ? b0 : 0));
   zero_unless<T, CH>(g, bvalid);
-
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
     int32_t ci[WV_U], unused_pk[WV_U];
     float unused[WV_U];
@@ -145,81 +185,155 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
   }
 }
 
-// ---------------------------------------------------------------- host side
-// Up to 16 lanes per entry (odd batches above 16 columns take the
-// merge-path kernels, whose lane groups suit them better).
-bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B) {
-  static const bool off = getenv("SNACK_NO_WAVE") != nullptr;
-  return !off && !v.has_split && wave_pick(dt, B).lpe <= 16;
+// One row per wave; rows of >= long_len entries (split by the tiles) are
+// left to k_wave_sddmm_pieces.  B <= LPE * CH.
+template <typename T, int CH, int LPE>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
+    int32_t B, int32_t long_len) {
+  const int32_t s = wave_segment(0);
+  if (s >= S) return;
+  const int lane = lane_id();
+  const int slot = lane / LPE;
+  const int32_t b0 = (lane % LPE) * CH;
+  const bool bvalid = b0 < B;
+  const int32_t a = ptr[s], e = ptr[s + 1];
+  if (a == e || e - a >= long_len) return;
+  sddmm_range<T, CH, LPE>(idx, dYt, Xt + (bvalid ? b0 : 0), B, s, a, e, lane, slot, b0, bvalid,
+                          dV);
 }
 
+// The tile pieces of split rows, one wave per tile (the same pieces as
+// k_wave_pieces); each entry's dV is final, so no carry is needed.
+template <typename T, int CH, int LPE>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_pieces(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
+    const int32_t* __restrict__ cut, const T* __restrict__ dYt, const T* __restrict__ Xt,
+    T* __restrict__ dV, int32_t P, int32_t B) {
+  const int32_t p = wave_segment(0);
+  if (p >= P) return;
+  const int32_t s0 = part_seg[p], s1 = part_seg[p + 1];
+  const bool c0 = cut[p] != 0, c1 = cut[p + 1] != 0;
+  const bool last_piece = c0 && !(c1 && s1 == s0);
+  if (!c1 && !last_piece) return;
+  const int lane = lane_id();
+  const int slot = lane / LPE;
+  const int32_t b0 = (lane % LPE) * CH;
+  const bool bvalid = b0 < B;
+  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);
+  if (last_piece)
+    sddmm_range<T, CH, LPE>(idx, dYt, xb, B, s0, part_nz[p], ptr[s0 + 1], lane, slot, b0, bvalid,
+                            dV);
+  if (c1)
+    sddmm_range<T, CH, LPE>(idx, dYt, xb, B, s1, (c0 && s0 == s1) ? part_nz[p] : ptr[s1],
+                            part_nz[p + 1], lane, slot, b0, bvalid, dV);
+}
+
+// ---------------------------------------------------------------- host side
+// Up to 16 lanes per entry (odd batches above 16 columns take the
+// merge-path kernels, whose lane groups suit them better).  Views with split
+// segments qualify when the caller handles their tile pieces (split).
+// SNACK_NO_WAVE / SNACK_NO_WAVE_SPLIT switch the path off (experiments).
+bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B, bool split) {
+  static const bool off = getenv("SNACK_NO_WAVE") != nullptr;
+  static const bool off_split = getenv("SNACK_NO_WAVE_SPLIT") != nullptr;
+  if (off || wave_pick(dt, B).lpe > 16) return false;
+  return !v.has_split || (split && !off_split);
+}
+
+// Segments of >= T entries (split view) are skipped by the per-segment
+// kernel, summed piecewise per tile into the carry slots, and finished by
+// k_fixup.
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
-                        hipStream_t s) {
+                        float* carry, hipStream_t s) {
   const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
-  const int32_t xb = (PERM && nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
-  dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk), (unsigned)cdiv(B, LPE * CH));
+  const int32_t xb =
+      (PERM && nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+  const unsigned passes = (unsigned)cdiv(B, LPE * CH);
+  const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
+  dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk), passes);
   hipLaunchKernelGGL((k_wave_spmm<T, CH, LPE, PERM, NODE_OUT, ACT>), grid, dim3(WV_THREADS), 0,
-                     s, v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B, xb);
+                     s, v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B, xb,
+                     long_len);
+  if (v.has_split) {
+    dim3 pg((unsigned)cdiv(v.P, WV_THREADS / SNK_WAVE), passes);
+    hipLaunchKernelGGL((k_wave_pieces<T, CH, LPE, PERM>), pg, dim3(WV_THREADS), 0, s, v.ptr,
+                       v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, v.cut,
+                       (const T*)Xt, carry, v.P, B);
+    launch_fixup(v, sizeof(T) == 2 ? SNACK_BF16 : SNACK_F32, NODE_OUT, ACT, carry, Y, B, s);
+  }
 }
 
 template <typename T, int CH, int LPE>
 static void wave_spmm_l(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
-                        bool node_out, int32_t act, hipStream_t s) {
+                        bool node_out, int32_t act, float* carry, hipStream_t s) {
   if constexpr (CH * LPE <= 64) {
     const bool perm = v.perm != nullptr;
     if (perm) {
-      if (node_out) wave_spmm_t<T, CH, LPE, true, true, ACT_NONE>(v, vals, Xt, B, Y, s);
-      else wave_spmm_t<T, CH, LPE, true, false, ACT_NONE>(v, vals, Xt, B, Y, s);
+      if (node_out) wave_spmm_t<T, CH, LPE, true, true, ACT_NONE>(v, vals, Xt, B, Y, carry, s);
+      else wave_spmm_t<T, CH, LPE, true, false, ACT_NONE>(v, vals, Xt, B, Y, carry, s);
     } else if (act == ACT_RELU) {
-      if (node_out) wave_spmm_t<T, CH, LPE, false, true, ACT_RELU>(v, vals, Xt, B, Y, s);
-      else wave_spmm_t<T, CH, LPE, false, false, ACT_RELU>(v, vals, Xt, B, Y, s);
+      if (node_out) wave_spmm_t<T, CH, LPE, false, true, ACT_RELU>(v, vals, Xt, B, Y, carry, s);
+      else wave_spmm_t<T, CH, LPE, false, false, ACT_RELU>(v, vals, Xt, B, Y, carry, s);
     } else {
-      if (node_out) wave_spmm_t<T, CH, LPE, false, true, ACT_NONE>(v, vals, Xt, B, Y, s);
-      else wave_spmm_t<T, CH, LPE, false, false, ACT_NONE>(v, vals, Xt, B, Y, s);
+      if (node_out) wave_spmm_t<T, CH, LPE, false, true, ACT_NONE>(v, vals, Xt, B, Y, carry, s);
+      else wave_spmm_t<T, CH, LPE, false, false, ACT_NONE>(v, vals, Xt, B, Y, carry, s);
     }
   }
 }
 
 template <typename T, int CH>
 static void wave_spmm_c(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
-                        bool node_out, int32_t act, int lpe, hipStream_t s) {
+                        bool node_out, int32_t act, int lpe, float* carry, hipStream_t s) {
   switch (lpe) {
-    case 1: wave_spmm_l<T, CH, 1>(v, vals, Xt, B, Y, node_out, act, s); break;
-    case 2: wave_spmm_l<T, CH, 2>(v, vals, Xt, B, Y, node_out, act, s); break;
-    case 4: wave_spmm_l<T, CH, 4>(v, vals, Xt, B, Y, node_out, act, s); break;
-    case 8: wave_spmm_l<T, CH, 8>(v, vals, Xt, B, Y, node_out, act, s); break;
-    default: wave_spmm_l<T, CH, 16>(v, vals, Xt, B, Y, node_out, act, s); break;
+    case 1: wave_spmm_l<T, CH, 1>(v, vals, Xt, B, Y, node_out, act, carry, s); break;
+    case 2: wave_spmm_l<T, CH, 2>(v, vals, Xt, B, Y, node_out, act, carry, s); break;
+    case 4: wave_spmm_l<T, CH, 4>(v, vals, Xt, B, Y, node_out, act, carry, s); break;
+    case 8: wave_spmm_l<T, CH, 8>(v, vals, Xt, B, Y, node_out, act, carry, s); break;
+    default: wave_spmm_l<T, CH, 16>(v, vals, Xt, B, Y, node_out, act, carry, s); break;
   }
 }
 
 template <typename T>
 static void wave_spmm_d(const seg_view& v, const void* vals, const void* Xt, int32_t B, void* Y,
-                        bool node_out, int32_t act, const wave_shape& w, hipStream_t s) {
+                        bool node_out, int32_t act, const wave_shape& w, float* carry,
+                        hipStream_t s) {
   switch (w.ch) {
-    case 1: wave_spmm_c<T, 1>(v, vals, Xt, B, Y, node_out, act, w.lpe, s); break;
-    case 2: wave_spmm_c<T, 2>(v, vals, Xt, B, Y, node_out, act, w.lpe, s); break;
-    case 4: wave_spmm_c<T, 4>(v, vals, Xt, B, Y, node_out, act, w.lpe, s); break;
+    case 1: wave_spmm_c<T, 1>(v, vals, Xt, B, Y, node_out, act, w.lpe, carry, s); break;
+    case 2: wave_spmm_c<T, 2>(v, vals, Xt, B, Y, node_out, act, w.lpe, carry, s); break;
+    case 4: wave_spmm_c<T, 4>(v, vals, Xt, B, Y, node_out, act, w.lpe, carry, s); break;
     default:
-      if constexpr (sizeof(T) == 2) wave_spmm_c<T, 8>(v, vals, Xt, B, Y, node_out, act, w.lpe, s);
+      if constexpr (sizeof(T) == 2) wave_spmm_c<T, 8>(v, vals, Xt, B, Y, node_out, act, w.lpe, carry, s);
       break;
   }
 }
 
 void launch_wave_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* Xt,
-                      int32_t B, void* Y, bool node_out, int32_t act, hipStream_t s) {
+                      int32_t B, void* Y, bool node_out, int32_t act, float* carry,
+                      hipStream_t s) {
   const wave_shape w = wave_pick(dt, B);
-  if (dt == SNACK_F32) wave_spmm_d<float>(v, vals, Xt, B, Y, node_out, act, w, s);
-  else wave_spmm_d<bf16>(v, vals, Xt, B, Y, node_out, act, w, s);
+  if (dt == SNACK_F32) wave_spmm_d<float>(v, vals, Xt, B, Y, node_out, act, w, carry, s);
+  else wave_spmm_d<bf16>(v, vals, Xt, B, Y, node_out, act, w, carry, s);
 }
 
 template <typename T, int CH>
 static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int32_t B, void* dV,
                          int lpe, hipStream_t s) {
   dim3 grid((unsigned)cdiv(v.S, WV_THREADS / SNK_WAVE));
-#define SNK_WSD(L)                                                                             \
-  hipLaunchKernelGGL((k_wave_sddmm<T, CH, L>), grid, dim3(WV_THREADS), 0, s, v.ptr, v.idx,     \
-                     (const T*)dYt, (const T*)Xt, (T*)dV, v.S, B)
+  dim3 pg((unsigned)cdiv(v.P, WV_THREADS / SNK_WAVE));
+  const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
+#define SNK_WSD(L)                                                                              \
+  do {                                                                                          \
+    hipLaunchKernelGGL((k_wave_sddmm<T, CH, L>), grid, dim3(WV_THREADS), 0, s, v.ptr, v.idx,    \
+                       (const T*)dYt, (const T*)Xt, (T*)dV, v.S, B, long_len);                  \
+    if (v.has_split)                                                                            \
+      hipLaunchKernelGGL((k_wave_sddmm_pieces<T, CH, L>), pg, dim3(WV_THREADS), 0, s, v.ptr,    \
+                         v.idx, v.part_seg, v.part_nz, v.cut, (const T*)dYt, (const T*)Xt,      \
+                         (T*)dV, v.P, B);                                                       \
+  } while (0)
   switch (lpe) {
     case 1: SNK_WSD(1); return true;
     case 2: SNK_WSD(2); return true;
