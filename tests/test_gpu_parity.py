@@ -167,13 +167,15 @@ def test_products_small_and_ragged(orc, M, K, nnz, Bsz, dt, layout, tile):
 
 def test_products_skewed_rows_with_splits(orc):
     """Rows of 1 .. 3000 entries, tiles of 64 items: many rows span several
-    tiles and go through the carry fix-up."""
+    tiles; their tile pieces go through the carry slots and the fix-up (wide
+    batches in several passes)."""
     M, K = 400, 3000
     deg = synth.rank_profile(M, K, 60000, 1.3)
     rng = np.random.default_rng(3)
     lin = np.concatenate([r * K + np.sort(rng.choice(K, d, replace=False))
                           for r, d in enumerate(rng.permutation(deg))])
-    for dt, layout, Bsz in (("f32", "batch", 3), ("bf16", "node", 16), ("f32", "node", 32)):
+    for dt, layout, Bsz in (("f32", "batch", 3), ("bf16", "node", 16), ("f32", "node", 32),
+                            ("f32", "node", 100), ("bf16", "batch", 64)):
         w = synth.random_case(7, M, K, lin.size, Bsz, dt, layout, positions=lin)
         topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile=64,
                             repeat_check=True)
