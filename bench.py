@@ -73,6 +73,9 @@ def parse():
                     help="time a sparse 1x1 convolution (generated kernel, generic, dense)")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="time multi-layer graph inference (power-law graphs, fused GELU)")
+    ap.add_argument("--configs", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time fwd/dX/dV on the other layer configurations (one instance "
+                         "each, graph-timed)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--restructure", choices=("fused", "separate"), default="fused",
                     help="prune/regrow + prepare as one call (snack_prune_regrow_prepared) or "
@@ -278,6 +281,77 @@ def time_calls(fn, reps=10, warm=3):
     b.record()
     b.synchronize()
     return a.elapsed_time(b) * 1e3 / reps
+
+
+def time_config(w, B, bf16, layout, ops=("fwd", "bwd_input", "sddmm"), launches=10, replays=3):
+    """Per-launch time of each product on one layer instance (caches warm
+    across launches), from HIP events around replays of a captured graph."""
+    import torch
+    import unstructured_sparse_nn_amd as snk
+    dt = torch.bfloat16 if bf16 else torch.float32
+    lay = snk.NODE_MAJOR if layout == "node" else snk.BATCH_MAJOR
+    topo = snk.Topology(to_dev(w.row), to_dev(w.col), w.M, w.K, B)
+    vals = to_dev(w.vals, bf16)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    X = torch.randn(B * w.K, device="cuda", generator=g).to(dt)
+    dY = torch.randn(B * w.M, device="cuda", generator=g).to(dt)
+    Y = torch.empty(B * w.M, dtype=dt, device="cuda")
+    dX = torch.empty(B * w.K, dtype=dt, device="cuda")
+    dV = torch.empty(w.nnz, dtype=dt, device="cuda")
+    fns = {"fwd": lambda: topo.fwd(vals, X, B, lay, out=Y),
+           "bwd_input": lambda: topo.bwd_input(vals, dY, B, lay, out=dX),
+           "sddmm": lambda: topo.grad_vals(dY, X, B, lay, out=dV)}
+    s_el = 2 if bf16 else 4
+    out = {"split_rows": int(topo.plan.has_split_row), "split_cols": int(topo.plan.has_split_col)}
+    for op in ops:
+        fn = fns[op]
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(launches):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (launches * replays)
+        b = algo_bytes(op, w.M, w.K, w.nnz, B, s_el, s_el)
+        out[op] = {"us": round(us, 2), "GBps": round(b / (us * 1e3), 1),
+                   "GFLOPs": round(2 * w.nnz * B / (us * 1e3), 1)}
+    del topo
+    return out
+
+
+def other_configs():
+    """fwd, dX and dV on the other layer configurations: 256^2 at 90% (fp32,
+    B=4), the GPT-2-small MLP layers at 90% and 99% (fp32, 1024 tokens,
+    batch-major), the LLaMA-7B-shaped projections with skewed rows (bf16,
+    B = 1, 4, 16, node-major) and the 200,000-node graph (fp32, 128 node-major
+    features; forward and input gradient)."""
+    import synth
+    out = {}
+    log("configs: single layer")
+    w = synth.single_layer()
+    out["single_256_s0.9_B4_f32"] = time_config(w.weights[0], 4, False, "batch")
+    for sp in (0.9, 0.99):
+        log(f"configs: gpt2 mlp {sp}")
+        wl = synth.gpt2_mlp(sparsity=sp)
+        for name, wt in (("W1_3072x768", wl.weights[0]), ("W2_768x3072", wl.weights[1])):
+            out[f"gpt2_{name}_s{sp}_B1024_f32"] = time_config(wt, 1024, False, "batch")
+    for which in ("up", "down"):
+        log(f"configs: llama {which}")
+        wt = synth.llama_proj(which=which, B=1).weights[0]
+        for B in (1, 4, 16):
+            out[f"llama_{which}_B{B}_bf16"] = time_config(wt, B, True, "node")
+    log("configs: graph 200k")
+    wt = synth.graph_layer().weights[0]
+    out["graph_200k_B128_f32"] = time_config(wt, 128, False, "node", ops=("fwd", "bwd_input"))
+    return out
 
 
 def graph_inference(layers=3):
@@ -669,6 +743,8 @@ def run_bench(args):
         rec["baselines"] = base
     if args.graph:
         rec["graph_inference"] = graph_inference()
+    if args.configs:
+        rec["configs"] = other_configs()
     if args.conv:
         log("1x1 convolution")
         rec["conv1x1"] = conv1x1_bench()
