@@ -186,12 +186,12 @@ __device__ __forceinline__ void spmm_rounds(const T* __restrict__ xb, int32_t B,
   accumulate_rounds<T, CH, NR>(xv, vj, acc);
 }
 
-// The dot of each round's gathered chunk with g, summed over the LPE lanes
-// of its slot, then permuted so that lane l of chunk q holds the result of
-// entry q*64 + l (rounds past NR give 0).
-template <typename T, int CH, int LPE, int NR>
-__device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec<T, CH>& g,
-                                           int lane, float (&out)[(NR + LPE - 1) / LPE]) {
+// Sums each round's partial dot over the LPE lanes of its slot, then permutes
+// so that lane l of chunk q holds the result of entry q*64 + l (rounds past
+// NR give 0).
+template <int LPE, int NR>
+__device__ __forceinline__ void reduce_permute(const float (&part)[NR], int lane,
+                                               float (&out)[(NR + LPE - 1) / LPE]) {
   constexpr int EPI = SNK_WAVE / LPE;
   constexpr int NQ = (NR + LPE - 1) / LPE;
   float res[NQ * LPE];
@@ -199,7 +199,7 @@ __device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec
   for (int i = 0; i < NQ * LPE; ++i) {
     float d = 0.f;
     if (i < NR) {
-      d = dot_acc<T, CH>(g, xv[i], 0.f);
+      d = part[i];
 #pragma unroll
       for (int off = 1; off < LPE; off <<= 1) d += __shfl_xor(d, off, SNK_WAVE);
     }
@@ -218,6 +218,17 @@ __device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec
       }
     }
   }
+}
+
+// The dot of each round's gathered chunk with g, summed over the LPE lanes
+// of its slot and permuted to lane = entry (reduce_permute).
+template <typename T, int CH, int LPE, int NR>
+__device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec<T, CH>& g,
+                                           int lane, float (&out)[(NR + LPE - 1) / LPE]) {
+  float part[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) part[i] = dot_acc<T, CH>(g, xv[i], 0.f);
+  reduce_permute<LPE, NR>(part, lane, out);
 }
 
 // SNACK_NO_XCD_REMAP set: plain block order (for experiments).

@@ -132,20 +132,43 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
   }
 }
 
-// The value gradient of NR rounds: every gather first, then the dots and the
-// LPE-lane sums, then per chunk of 64 entries one coalesced store.
-template <typename T, int CH, int LPE, int NR>
-__device__ __forceinline__ void sddmm_rounds(const T* __restrict__ xb, int32_t B,
-                                             const vec<T, CH>& g, const int32_t* ci,
+// The value gradient of NR rounds.  One batch pass (B <= LPE * CH): every
+// gather first, then the dots.  Wider batches: per pass of LPE * CH columns,
+// the row's dY chunk and the NR gathered X chunks, their dots accumulated;
+// then the LPE-lane sums and, per chunk of 64 entries, one coalesced store.
+template <typename T, int CH, int LPE, int NR, bool MULTI>
+__device__ __forceinline__ void sddmm_rounds(const T* __restrict__ Xt,
+                                             const T* __restrict__ dYrow, int32_t B,
+                                             int32_t passes, int32_t b0, const int32_t* ci,
                                              int32_t rb, int32_t e, int lane, int slot,
                                              T* __restrict__ dV) {
+  constexpr int EPI = SNK_WAVE / LPE;
   constexpr int NQ = (NR + LPE - 1) / LPE;
-  vec<T, CH> xv[NR];
-  float unused_v[NR];
-  const float zeros[WV_U] = {0.f, 0.f, 0.f, 0.f};
-  gather_rounds<T, CH, LPE, NR>(xb, B, ci, zeros, rb, e, slot, xv, unused_v);
+  int32_t cj[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int q = i / LPE, src = (i % LPE) * EPI + slot;
+    cj[i] = LPE == 1 ? ci[q] : __shfl(ci[q], src, SNK_WAVE);
+  }
+  float part[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) part[i] = 0.f;
+  if (!MULTI) passes = 1;  // one pass: straight-line code
+  for (int32_t bp = 0; bp < passes; ++bp) {
+    const int32_t b = bp * (LPE * CH) + b0;
+    const bool ok = b < B;
+    const int32_t bb = ok ? b : 0;  // lanes past the batch read column 0 and add nothing
+    vec<T, CH> g = *reinterpret_cast<const vec<T, CH>*>(dYrow + bb);
+    zero_unless<T, CH>(g, ok);
+    vec<T, CH> xv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      xv[i] = *reinterpret_cast<const vec<T, CH>*>(Xt + (int64_t)cj[i] * B + bb);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) part[i] = dot_acc<T, CH>(g, xv[i], part[i]);
+  }
   float out[NQ];
-  round_dots<T, CH, LPE, NR>(xv, g, lane, out);
+  reduce_permute<LPE, NR>(part, lane, out);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int32_t k = rb + q * SNK_WAVE + lane;
@@ -153,20 +176,20 @@ __device__ __forceinline__ void sddmm_rounds(const T* __restrict__ xb, int32_t B
   }
 }
 
-// dV[k] for the entries [a, e) of segment s: the segment's dY chunk is
-// loaded once, each round gathers EPI entries' X chunks and dots them with
-// it, the LPE lanes of a slot add their partial dots, and every 64 entries
-// the results are permuted to lane = entry and stored coalesced.
-template <typename T, int CH, int LPE>
+// dV[k] for the entries [a, e) of segment s: each round gathers EPI entries'
+// X chunks and dots them with the segment's dY chunk, the LPE lanes of a
+// slot add their partial dots, and every 64 entries the results are
+// permuted to lane = entry and stored coalesced.
+template <typename T, int CH, int LPE, bool MULTI>
 __device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
                                             const T* __restrict__ dYt,
-                                            const T* __restrict__ xb, int32_t B, int32_t s,
+                                            const T* __restrict__ Xt, int32_t B, int32_t s,
                                             int32_t a, int32_t e, int lane, int slot, int32_t b0,
-                                            bool bvalid, T* __restrict__ dV) {
+                                            T* __restrict__ dV) {
   constexpr int EPI = SNK_WAVE / LPE;
   constexpr int RG = wave_rg<LPE>();
-  vec<T, CH> g = *reinterpret_cast<const vec<T, CH>*>(dYt + (int64_t)s * B + (bvalid ? b0 : 0));
-  zero_unless<T, CH>(g, bvalid);
+  const int32_t passes = (B + LPE * CH - 1) / (LPE * CH);
+  const T* __restrict__ dYrow = dYt + (int64_t)s * B;
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
     int32_t ci[WV_U], unused_pk[WV_U];
     float unused[WV_U];
@@ -179,15 +202,16 @@ __device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
       if (rb >= e) break;
       const int nr = (e - rb + EPI - 1) / EPI;
       with_count<RG>(nr, [&](auto n) {
-        sddmm_rounds<T, CH, LPE, decltype(n)::value>(xb, B, g, ci + q0, rb, e, lane, slot, dV);
+        sddmm_rounds<T, CH, LPE, decltype(n)::value, MULTI>(Xt, dYrow, B, passes, b0, ci + q0,
+                                                            rb, e, lane, slot, dV);
       });
     }
   }
 }
 
 // One row per wave; rows of >= long_len entries (split by the tiles) are
-// left to k_wave_sddmm_pieces.  B <= LPE * CH.
-template <typename T, int CH, int LPE>
+// left to k_wave_sddmm_pieces.  Batches wider than LPE * CH run in passes.
+template <typename T, int CH, int LPE, bool MULTI>
 __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
@@ -197,16 +221,14 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
   const int lane = lane_id();
   const int slot = lane / LPE;
   const int32_t b0 = (lane % LPE) * CH;
-  const bool bvalid = b0 < B;
   const int32_t a = ptr[s], e = ptr[s + 1];
   if (a == e || e - a >= long_len) return;
-  sddmm_range<T, CH, LPE>(idx, dYt, Xt + (bvalid ? b0 : 0), B, s, a, e, lane, slot, b0, bvalid,
-                          dV);
+  sddmm_range<T, CH, LPE, MULTI>(idx, dYt, Xt, B, s, a, e, lane, slot, b0, dV);
 }
 
 // The tile pieces of split rows, one wave per tile (the same pieces as
 // k_wave_pieces); each entry's dV is final, so no carry is needed.
-template <typename T, int CH, int LPE>
+template <typename T, int CH, int LPE, bool MULTI>
 __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_pieces(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
@@ -221,14 +243,12 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_pieces(
   const int lane = lane_id();
   const int slot = lane / LPE;
   const int32_t b0 = (lane % LPE) * CH;
-  const bool bvalid = b0 < B;
-  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);
   if (last_piece)
-    sddmm_range<T, CH, LPE>(idx, dYt, xb, B, s0, part_nz[p], ptr[s0 + 1], lane, slot, b0, bvalid,
-                            dV);
+    sddmm_range<T, CH, LPE, MULTI>(idx, dYt, Xt, B, s0, part_nz[p], ptr[s0 + 1], lane, slot, b0,
+                                   dV);
   if (c1)
-    sddmm_range<T, CH, LPE>(idx, dYt, xb, B, s1, (c0 && s0 == s1) ? part_nz[p] : ptr[s1],
-                            part_nz[p + 1], lane, slot, b0, bvalid, dV);
+    sddmm_range<T, CH, LPE, MULTI>(idx, dYt, Xt, B, s1, (c0 && s0 == s1) ? part_nz[p] : ptr[s1],
+                                   part_nz[p + 1], lane, slot, b0, dV);
 }
 
 // ---------------------------------------------------------------- host side
@@ -325,14 +345,19 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
   dim3 grid((unsigned)cdiv(v.S, WV_THREADS / SNK_WAVE));
   dim3 pg((unsigned)cdiv(v.P, WV_THREADS / SNK_WAVE));
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
-#define SNK_WSD(L)                                                                              \
+#define SNK_WSD1(L, MULTI)                                                                      \
   do {                                                                                          \
-    hipLaunchKernelGGL((k_wave_sddmm<T, CH, L>), grid, dim3(WV_THREADS), 0, s, v.ptr, v.idx,    \
-                       (const T*)dYt, (const T*)Xt, (T*)dV, v.S, B, long_len);                  \
+    hipLaunchKernelGGL((k_wave_sddmm<T, CH, L, MULTI>), grid, dim3(WV_THREADS), 0, s, v.ptr,    \
+                       v.idx, (const T*)dYt, (const T*)Xt, (T*)dV, v.S, B, long_len);           \
     if (v.has_split)                                                                            \
-      hipLaunchKernelGGL((k_wave_sddmm_pieces<T, CH, L>), pg, dim3(WV_THREADS), 0, s, v.ptr,    \
-                         v.idx, v.part_seg, v.part_nz, v.cut, (const T*)dYt, (const T*)Xt,      \
-                         (T*)dV, v.P, B);                                                       \
+      hipLaunchKernelGGL((k_wave_sddmm_pieces<T, CH, L, MULTI>), pg, dim3(WV_THREADS), 0, s,    \
+                         v.ptr, v.idx, v.part_seg, v.part_nz, v.cut, (const T*)dYt,             \
+                         (const T*)Xt, (T*)dV, v.P, B);                                         \
+  } while (0)
+#define SNK_WSD(L)                                             \
+  do {                                                         \
+    if (B > (L) * CH) SNK_WSD1(L, true);                       \
+    else SNK_WSD1(L, false);                                   \
   } while (0)
   switch (lpe) {
     case 1: SNK_WSD(1); return true;
@@ -343,12 +368,12 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
     default: return false;
   }
 #undef SNK_WSD
+#undef SNK_WSD1
 }
 
 bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
                        int32_t B, void* dV, hipStream_t s) {
   const wave_shape w = wave_pick(dt, B);
-  if ((int64_t)w.ch * w.lpe < B) return false;  // one pass must cover the batch
   if (dt == SNACK_F32) {
     switch (w.ch) {
       case 1: return wave_sddmm_c<float, 1>(v, dYt, Xt, B, dV, w.lpe, s);
