@@ -199,7 +199,7 @@ def graph_kernel_us(insts, op, launches=20, replays=5):
 
 def src_hash():
     h = hashlib.sha256()
-    for f in ("spmm.hip", "wave.hip", "wave.h", "common.h"):
+    for f in ("spmm.hip", "wave.hip", "wave.h", "wave_kernels.h", "common.h"):
         h.update(open(os.path.join(ROOT, "unstructured_sparse_nn_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

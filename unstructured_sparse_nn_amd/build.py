@@ -15,8 +15,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsnack.so")
-SOURCES = ["api.hip", "prims.hip", "prepare.hip", "spmm.hip", "prune.hip", "prune_bitmap.hip",
-           "aux.hip", "fixed.hip", "wave.hip", "wave_fused.hip"]
+# longest compiles first (they start first in the worker pool)
+SOURCES = ["wave_spmm_bf16.hip", "wave_spmm_f32.hip", "wave_fused.hip", "wave_sddmm_bf16.hip",
+           "wave_sddmm_f32.hip", "spmm.hip", "prune_bitmap.hip", "api.hip", "prims.hip",
+           "prepare.hip", "prune.hip", "aux.hip", "fixed.hip", "wave.hip"]
 ARCH = os.environ.get("SNACK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
