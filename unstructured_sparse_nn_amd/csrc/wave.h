@@ -70,39 +70,49 @@ __device__ __forceinline__ void zero_unless(vec<T, CH>& x, bool ok) {
 // are in flight together.  Values past the end are 0; with PERM, pk receives
 // each entry's value position.  vals is not restrict-qualified: the fused
 // backward writes the same array after these loads.
-template <typename T, bool PERM, bool VALS>
+template <typename T, bool PERM, bool VALS, int U = WV_U>
 __device__ __forceinline__ void load_entries(const int32_t* __restrict__ idx,
                                              const int32_t* __restrict__ perm, const T* vals,
                                              int32_t base, int32_t e, int lane,
-                                             int32_t (&ci)[WV_U], float (&cv)[WV_U],
-                                             int32_t (&pk)[WV_U]) {
-  int32_t kc[WV_U];
+                                             int32_t (&ci)[U], float (&cv)[U],
+                                             int32_t (&pk)[U]) {
+  int32_t kc[U];
 #pragma unroll
-  for (int q = 0; q < WV_U; ++q) kc[q] = min(base + q * SNK_WAVE + lane, e - 1);
+  for (int q = 0; q < U; ++q) kc[q] = min(base + q * SNK_WAVE + lane, e - 1);
 #pragma unroll
-  for (int q = 0; q < WV_U; ++q) ci[q] = idx[kc[q]];
+  for (int q = 0; q < U; ++q) ci[q] = idx[kc[q]];
   if constexpr (VALS) {
-    T raw[WV_U];
+    T raw[U];
     if constexpr (PERM) {
 #pragma unroll
-      for (int q = 0; q < WV_U; ++q) pk[q] = perm[kc[q]];
+      for (int q = 0; q < U; ++q) pk[q] = perm[kc[q]];
 #pragma unroll
-      for (int q = 0; q < WV_U; ++q) raw[q] = vals[pk[q]];
+      for (int q = 0; q < U; ++q) raw[q] = vals[pk[q]];
     } else {
 #pragma unroll
-      for (int q = 0; q < WV_U; ++q) raw[q] = vals[kc[q]];
+      for (int q = 0; q < U; ++q) raw[q] = vals[kc[q]];
     }
 #pragma unroll
-    for (int q = 0; q < WV_U; ++q)
+    for (int q = 0; q < U; ++q)
       cv[q] = (base + q * SNK_WAVE + lane < e) ? elem<T>::to_f(raw[q]) : 0.f;
   }
 }
 
 // Gather rounds issued together before any is consumed: at most 16 (one
-// gathered chunk each per lane), never more than one loaded batch holds.
-template <int LPE>
+// gathered chunk each per lane), never more than one loaded batch of U
+// 64-entry chunks holds.
+template <int LPE, int U = WV_U>
 constexpr int wave_rg() {
-  return 4 * LPE < 16 ? 4 * LPE : 16;
+  return U * LPE < 16 ? U * LPE : 16;
+}
+
+// 64-entry chunks per loaded batch for segments longer than one batch of
+// WV_U chunks: with few lanes per entry a round covers many entries, so the
+// batch grows to 16 rounds (1,024 entries at one lane per entry) and a long
+// segment takes fewer dependent load/gather round trips.
+template <int LPE>
+constexpr int wave_u_long() {
+  return LPE >= 4 ? WV_U : 16 / LPE;
 }
 
 // Calls f(integral_constant<N>) for the runtime n in [1, NMAX], so that a

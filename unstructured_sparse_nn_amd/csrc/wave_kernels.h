@@ -41,21 +41,19 @@ namespace snk {
 
 // acc[c] = sum over entries [a, e) of v * in[idx, b0 + c]: batches of four
 // 64-entry loads, each split into round groups of straight-line code.
-template <typename T, int CH, int LPE, bool PERM>
-__device__ __forceinline__ void spmm_range(const int32_t* __restrict__ idx,
-                                           const int32_t* __restrict__ perm, const T* vals,
-                                           const T* __restrict__ xb, int32_t B, int32_t a,
-                                           int32_t e, int lane, int slot, float (&acc)[CH]) {
+template <typename T, int CH, int LPE, bool PERM, int U>
+__device__ __forceinline__ void spmm_batches(const int32_t* __restrict__ idx,
+                                             const int32_t* __restrict__ perm, const T* vals,
+                                             const T* __restrict__ xb, int32_t B, int32_t a,
+                                             int32_t e, int lane, int slot, float (&acc)[CH]) {
   constexpr int EPI = SNK_WAVE / LPE;
-  constexpr int RG = wave_rg<LPE>();  // rounds per group (a whole number of chunks)
+  constexpr int RG = wave_rg<LPE, U>();  // rounds per group (a whole number of chunks)
+  for (int32_t base = a; base < e; base += U * SNK_WAVE) {
+    int32_t ci[U], pk[U];
+    float cv[U];
+    load_entries<T, PERM, true, U>(idx, perm, vals, base, e, lane, ci, cv, pk);
 #pragma unroll
-  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
-  for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
-    int32_t ci[WV_U], pk[WV_U];
-    float cv[WV_U];
-    load_entries<T, PERM, true>(idx, perm, vals, base, e, lane, ci, cv, pk);
-#pragma unroll
-    for (int g = 0; g < WV_U * LPE / RG; ++g) {
+    for (int g = 0; g < U * LPE / RG; ++g) {
       const int q0 = g * RG / LPE;
       const int32_t rb = base + g * RG * EPI;  // first entry of the group (wave-uniform)
       if (rb >= e) break;
@@ -65,6 +63,20 @@ __device__ __forceinline__ void spmm_range(const int32_t* __restrict__ idx,
       });
     }
   }
+}
+
+template <typename T, int CH, int LPE, bool PERM>
+__device__ __forceinline__ void spmm_range(const int32_t* __restrict__ idx,
+                                           const int32_t* __restrict__ perm, const T* vals,
+                                           const T* __restrict__ xb, int32_t B, int32_t a,
+                                           int32_t e, int lane, int slot, float (&acc)[CH]) {
+  constexpr int UL = wave_u_long<LPE>();
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+  if (UL > WV_U && e - a > WV_U * SNK_WAVE)  // wave-uniform: a long segment, larger batches
+    spmm_batches<T, CH, LPE, PERM, UL>(idx, perm, vals, xb, B, a, e, lane, slot, acc);
+  else
+    spmm_batches<T, CH, LPE, PERM, WV_U>(idx, perm, vals, xb, B, a, e, lane, slot, acc);
 }
 
 // The tile pieces of split segments (segments of >= T entries, cut by the
@@ -186,23 +198,21 @@ __device__ __forceinline__ void sddmm_rounds(const T* __restrict__ Xt,
 // X chunks and dots them with the segment's dY chunk, the LPE lanes of a
 // slot add their partial dots, and every 64 entries the results are
 // permuted to lane = entry and stored coalesced.
-template <typename T, int CH, int LPE, bool MULTI>
-__device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
-                                            const T* __restrict__ dYt,
-                                            const T* __restrict__ Xt, int32_t B, int32_t s,
-                                            int32_t a, int32_t e, int lane, int slot, int32_t b0,
-                                            T* __restrict__ dV) {
+template <typename T, int CH, int LPE, bool MULTI, int U>
+__device__ __forceinline__ void sddmm_batches(const int32_t* __restrict__ idx,
+                                              const T* __restrict__ dYrow,
+                                              const T* __restrict__ Xt, int32_t B,
+                                              int32_t passes, int32_t a, int32_t e, int lane,
+                                              int slot, int32_t b0, T* __restrict__ dV) {
   constexpr int EPI = SNK_WAVE / LPE;
-  constexpr int RG = wave_rg<LPE>();
-  const int32_t passes = (B + LPE * CH - 1) / (LPE * CH);
-  const T* __restrict__ dYrow = dYt + (int64_t)s * B;
-  for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
-    int32_t ci[WV_U], unused_pk[WV_U];
-    float unused[WV_U];
-    load_entries<T, false, false>(idx, nullptr, (const T*)nullptr, base, e, lane, ci, unused,
-                                  unused_pk);
+  constexpr int RG = wave_rg<LPE, U>();
+  for (int32_t base = a; base < e; base += U * SNK_WAVE) {
+    int32_t ci[U], unused_pk[U];
+    float unused[U];
+    load_entries<T, false, false, U>(idx, nullptr, (const T*)nullptr, base, e, lane, ci, unused,
+                                     unused_pk);
 #pragma unroll
-    for (int gi = 0; gi < WV_U * LPE / RG; ++gi) {
+    for (int gi = 0; gi < U * LPE / RG; ++gi) {
       const int q0 = gi * RG / LPE;
       const int32_t rb = base + gi * RG * EPI;
       if (rb >= e) break;
@@ -213,6 +223,21 @@ __device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
       });
     }
   }
+}
+
+template <typename T, int CH, int LPE, bool MULTI>
+__device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
+                                            const T* __restrict__ dYt,
+                                            const T* __restrict__ Xt, int32_t B, int32_t s,
+                                            int32_t a, int32_t e, int lane, int slot, int32_t b0,
+                                            T* __restrict__ dV) {
+  constexpr int UL = wave_u_long<LPE>();
+  const int32_t passes = (B + LPE * CH - 1) / (LPE * CH);
+  const T* __restrict__ dYrow = dYt + (int64_t)s * B;
+  if (UL > WV_U && e - a > WV_U * SNK_WAVE)  // wave-uniform: a long segment, larger batches
+    sddmm_batches<T, CH, LPE, MULTI, UL>(idx, dYrow, Xt, B, passes, a, e, lane, slot, b0, dV);
+  else
+    sddmm_batches<T, CH, LPE, MULTI, WV_U>(idx, dYrow, Xt, B, passes, a, e, lane, slot, b0, dV);
 }
 
 // One row per wave; rows of >= long_len entries (split by the tiles) are
