@@ -24,8 +24,13 @@
  *     no global device state.  Plans are caller-owned host structs.
  *   - streams: `stream` is a hipStream_t (NULL = the null stream).  All
  *     calls are stream-ordered and asynchronous, except snack_coo_prepare
- *     and snack_prune_regrow, which read a few bytes back and synchronise
- *     the stream before returning.
+ *     and snack_prune_regrow(_prepared), which read a few bytes back and
+ *     wait for the stream before returning.  prepare and the bitmap plan of
+ *     the restructure wait by spinning on a completion word that a last,
+ *     one-thread kernel stores into pinned host memory (falling back to
+ *     hipStreamSynchronize after 20 ms, or always with the environment
+ *     variable SNACK_BLOCKING_SYNC set); the calling thread is busy while it
+ *     waits.
  *   - errors: a negative snack_status.  Argument errors are detected on the
  *     host before anything is launched and leave every output untouched.
  *     Nothing aborts or prints.
@@ -155,7 +160,7 @@ SNACK_API snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, i
  * number of entries + segment ends, whatever the row lengths.
  * Validates the COO first: SNACK_E_COO_RANGE / SNACK_E_COO_ORDER.
  * Runs about a dozen kernels, then reads back 12 bytes (error bits and the
- * two has_split flags) and synchronises `stream`.  Records row, col and
+ * two has_split flags) and waits for `stream` (see streams above).  Records row, col and
  * arena in the plan; they must stay alive and unchanged while the plan is
  * used.  Re-run after every change of the sparsity pattern.
  */

@@ -256,7 +256,7 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
     return SNACK_E_HIP;
   if (launch_prepare_result(errs, seg_bounds_blocks(nnz), rsplit, tiles_blocks(plan->M), csplit,
                             tiles_blocks(plan->K), res_dev, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
+      wait_results(res_host, res_dev, s) != hipSuccess)
     return SNACK_E_HIP;
   if (res_host[0] == INT32_MIN) return SNACK_E_HIP;
   if (res_host[0] & 1) return SNACK_E_COO_RANGE;

@@ -37,6 +37,12 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // straight into it, so a readback costs no copy.  NULL on failure.
 int32_t* host_result_buffer();
 int32_t* host_result_device(int32_t* host);
+// Waits until every kernel queued on s so far has finished and its result
+// words are visible in `host`: a one-thread kernel stores a per-call token
+// into host[RESULT_DONE_SLOT] and the host spins on it (falling back to
+// hipStreamSynchronize after 20 ms, or with SNACK_BLOCKING_SYNC set).
+constexpr int RESULT_DONE_SLOT = 15;
+hipError_t wait_results(int32_t* host, int32_t* dev, hipStream_t s);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- products (spmm.hip) ----------------------------------------------------

@@ -4,6 +4,10 @@
 // stable sort of the entries by column, and the prune/regrow step sorts
 // candidate positions and counts accepted ones with scans.  Deterministic:
 // integer arithmetic only, no order-dependent atomics.
+#include <chrono>
+#include <climits>
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
@@ -374,6 +378,34 @@ int32_t* host_result_buffer() {
       buf = (int32_t*)p;
   }
   return buf;
+}
+
+// Completion word of a call: one thread stores the call's token into the
+// pinned result buffer after every earlier kernel of the stream has finished
+// (stream order); the host spins on it instead of a blocking stream sync.
+__global__ void k_signal(int32_t* __restrict__ flag, int32_t token) {
+  __threadfence_system();
+  *(volatile int32_t*)flag = token;
+}
+
+hipError_t wait_results(int32_t* host, int32_t* dev, hipStream_t s) {
+  static const bool blocking = getenv("SNACK_BLOCKING_SYNC") != nullptr;
+  if (blocking) return hipStreamSynchronize(s);
+  thread_local int32_t token = 0;
+  token = token == INT32_MAX ? 1 : token + 1;
+  volatile int32_t* flag = host + RESULT_DONE_SLOT;
+  *flag = 0;
+  hipLaunchKernelGGL(k_signal, dim3(1), dim3(1), 0, s, dev + RESULT_DONE_SLOT, token);
+  if (hipGetLastError() != hipSuccess) return hipStreamSynchronize(s);
+  // spin for up to 20 ms (a restructure takes ~0.1 ms), then block: a fault
+  // or a slow call still ends in the stream sync and its error
+  const auto t0 = std::chrono::steady_clock::now();
+  while (*flag != token) {
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(20))
+      return hipStreamSynchronize(s);
+    __builtin_ia32_pause();
+  }
+  return hipSuccess;
 }
 
 int32_t* host_result_device(int32_t* host) {

@@ -1118,7 +1118,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
       hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
                          *fuse, res_dev);
   }
-  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+  if (hipGetLastError() != hipSuccess || wait_results(res_host, res_dev, s) != hipSuccess)
     return SNACK_E_HIP;
   const int32_t err = res_host[0], missing = res_host[1];
   if (err == INT32_MIN) return SNACK_E_HIP;
