@@ -589,7 +589,7 @@ def test_dense_baseline(orc, dt, masked, Bsz, K):
 def test_sparse_linear_autograd(orc):
     w = workload("single")
     wt = w.weights[0]
-    layer = snk.SparseLinear(256, 256, to_dev(wt.row), to_dev(wt.col), to_dev(wt.vals), 4)
+    layer = snk.SparseLinear(256, 256, to_dev(wt.row), to_dev(wt.col), to_dev(wt.vals), 40)
     x = to_dev(w.X[0].data).view(4, 256).requires_grad_(True)
     y = layer(x)
     g = to_dev(w.dY[0].data).view(4, 256)
@@ -600,6 +600,12 @@ def test_sparse_linear_autograd(orc):
     assert_within(from_dev(x.grad, "f32"), ref, S, "f32", "SparseLinear dX")
     ref, S = orc.sddmm(256, 256, wt.row, wt.col, 4, w.dY[0].f64(), w.X[0].f64())
     assert_within(from_dev(layer.vals.grad, "f32"), ref, S, "f32", "SparseLinear dV")
+    # a batch above the fused backward's limit takes the two separate calls
+    xw = torch.randn(40, 256, device="cuda", requires_grad=True)
+    layer(xw).backward(torch.ones(40, 256, device="cuda"))
+    ref, S = orc.spmm_bwd_input(256, 256, wt.row, wt.col, wt.vals_f64(), 40,
+                                np.ones(40 * 256))
+    assert_within(from_dev(xw.grad, "f32"), ref, S, "f32", "SparseLinear dX, batch 40")
     dropped, grown = layer.prune_regrow(100000, 1)
     ref = orc.prune_regrow(256, 256, wt.row, wt.col, wt.vals, "f32", 655, 0, 1)
     assert np.array_equal(grown.cpu().numpy(), ref["grown"])

@@ -11,6 +11,9 @@ import torch
 
 from . import binding as B
 
+# Widest batch of snack_spmm_bwd_fused (one workgroup column covers the batch).
+FUSED_MAX_BATCH = 32
+
 
 class Topology:
     """COO pattern (row, col int32 on the GPU) plus its prepared plan."""
@@ -81,6 +84,12 @@ class _SparseLinearFn(torch.autograd.Function):
         topo = ctx.topo
         Bsz = xc.shape[0]
         g = gy.contiguous().view(-1)
+        if ctx.needs_input_grad[0] and ctx.needs_input_grad[1] and 0 < Bsz <= FUSED_MAX_BATCH:
+            # both gradients from one pass over the column view (snack_spmm_bwd_fused)
+            gx = torch.empty(Bsz * topo.K, dtype=g.dtype, device=g.device)
+            gv = torch.empty(topo.nnz, dtype=g.dtype, device=g.device)
+            B.snack_spmm_bwd_fused(topo.plan, vals, xc.view(-1), g, B.BATCH_MAJOR, Bsz, gx, gv)
+            return gx.view(Bsz, topo.K), gv, None
         gx = topo.bwd_input(vals, g, Bsz).view(Bsz, topo.K) if ctx.needs_input_grad[0] else None
         gv = topo.grad_vals(g, xc.view(-1), Bsz) if ctx.needs_input_grad[1] else None
         return gx, gv, None
