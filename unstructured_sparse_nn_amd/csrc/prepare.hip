@@ -16,6 +16,7 @@
 // per-block error flags without any out-of-bounds access.
 #include "common.h"
 #include "internal.h"
+#include "results.h"
 #include "tiles.h"
 
 namespace snk {
@@ -106,9 +107,9 @@ __global__ __launch_bounds__(RES_THREADS) void k_prepare_result(
   r = block_or(r, lds);
   c = block_or(c, lds);
   if (threadIdx.x == 0) {
-    res[0] = e;
-    res[1] = r;
-    res[2] = c;
+    store_result(&res[0], e);
+    store_result(&res[1], r);
+    store_result(&res[2], c);
   }
 }
 

@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "results.h"
 #include "prune_common.h"
 #include "tiles.h"
 
@@ -665,10 +666,10 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   const int t = threadIdx.x;
   const int32_t err = st->err, missing = st->rem_final;
   if (blockIdx.x == 0 && t == 0) {
-    result[0] = err;
-    result[1] = missing;
-    result[2] = 0;  // split flags of a fused prepare, set by later kernels
-    result[3] = 0;
+    store_result(&result[0], err);
+    store_result(&result[1], missing);
+    store_result(&result[2], 0);  // split flags of a fused prepare, set by later kernels
+    store_result(&result[3], 0);
   }
   if (err || missing > 0) return;
   // block base: the sum of the sums of earlier blocks
@@ -829,7 +830,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
       tile_close(M, nnz, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
     }
     const int any_b = __syncthreads_or(any ? 1 : 0);
-    if (threadIdx.x == 0 && any_b) res[2] = 1;
+    if (threadIdx.x == 0 && any_b) store_result(&res[2], 1);
     return;
   }
   const int64_t tile = ((int64_t)(blockIdx.x - rb) * FP_THREADS + threadIdx.x) >> 5;
@@ -922,7 +923,7 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
       const int64_t b = (t + 1 < ncol && s + 1 < K) ? (int64_t)cstart[t + 1] : base + tot;
       any = tile_cuts(s, a, b, nnz, f.T_col, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
     }
-    if (__ballot(any) != 0 && lane_id() == 0) res[3] = 1;
+    if (__ballot(any) != 0 && lane_id() == 0) store_result(&res[3], 1);
   }
   if (!valid) return;
   const uint32_t below = (1u << (c & 31)) - 1u;
@@ -961,7 +962,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int3
                              f.cpart_seg, f.cpart_nz, f.ccut);
   else if (s == K) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
   const int any_b = __syncthreads_or(any ? 1 : 0);
-  if (threadIdx.x == 0 && any_b) res[3] = 1;
+  if (threadIdx.x == 0 && any_b) store_result(&res[3], 1);
 }
 
 // ------------------------------------------------------------------ host
