@@ -2,8 +2,9 @@
 // instantiated per element type by wave_spmm_*.hip and wave_sddmm_*.hip.
 //
 // One 64-lane wave per output segment (row, or column for the transpose);
-// segments of a tile or more are summed as tile pieces (k_wave_pieces,
-// k_wave_sddmm_pieces) and finished by the fix-up of spmm.hip.
+// segments of a tile or more are summed as tile pieces by the first
+// workgroups of the same launch (k_wave_spmm_split, k_wave_sddmm_split); the
+// products' pieces are finished by the fix-up of spmm.hip.
 //
 // The same three products as spmm.hip ("Beyond Masked Sparsity: SNACK
 // Enables Truly Sparse Neural Networks on GPU", Abstract: compute only the
@@ -89,15 +90,14 @@ __device__ __forceinline__ void spmm_range(const int32_t* __restrict__ idx,
 //   carry[P + p] the last piece of the segment cut at p: from cut p to its end.
 // Pieces are at most 2T entries, so no wave serialises a long segment.
 template <typename T, int CH, int LPE, bool PERM>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_pieces(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+__device__ __forceinline__ void wave_pieces_of(
+    int32_t p, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const T* __restrict__ vals,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
     const int32_t* __restrict__ cut, const T* __restrict__ Xt, float* __restrict__ carry,
     int32_t P, int32_t B) {
   constexpr int EPI = SNK_WAVE / LPE;
   constexpr int LOW = EPI / CH;
-  const int32_t p = wave_segment(0);
   if (p >= P) return;
   const int32_t s0 = part_seg[p], s1 = part_seg[p + 1];
   const bool c0 = cut[p] != 0, c1 = cut[p + 1] != 0;
@@ -120,13 +120,12 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_pieces(
 }
 
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+__device__ __forceinline__ void wave_spmm_of(
+    int32_t s, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
-    T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks, int32_t long_len) {
+    T* __restrict__ Y, int32_t S, int32_t B, int32_t long_len) {
   constexpr int EPI = SNK_WAVE / LPE;  // entries per gather round
   static_assert(CH <= EPI, "reduce-scatter needs CH <= 64 / LPE");
-  const int32_t s = wave_segment(xcd_blocks);
   if (s >= S) return;
   const int lane = lane_id();
   const int slot = lane / LPE;
@@ -149,6 +148,41 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
     if constexpr (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(r);
     else Y[(int64_t)b * S + s] = elem<T>::from_f(r);
   }
+}
+
+template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
+    T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks, int32_t long_len) {
+  wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(wave_segment(xcd_blocks), ptr, idx, perm, vals,
+                                                Xt, Y, S, B, long_len);
+}
+
+// Both halves of a view with split segments in one launch, so that they
+// overlap: workgroups below pblk (a multiple of NUM_XCD) run the tile pieces
+// (wave_pieces_of), the rest the segments of < long_len entries (as
+// k_wave_spmm, in the same die-contiguous order, which a multiple of NUM_XCD
+// keeps).
+template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_spmm_split(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
+    T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks, int32_t long_len,
+    const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
+    const int32_t* __restrict__ cut, float* __restrict__ carry, int32_t P, int32_t pblk) {
+  const int32_t w = (int32_t)(threadIdx.x / SNK_WAVE);
+  const int32_t bx = (int32_t)blockIdx.x;
+  if (bx < pblk) {
+    const int32_t p = __builtin_amdgcn_readfirstlane(bx * (WV_THREADS / SNK_WAVE) + w);
+    wave_pieces_of<T, CH, LPE, PERM>(p, ptr, idx, perm, vals, part_seg, part_nz, cut, Xt, carry,
+                                     P, B);
+    return;
+  }
+  const int32_t sb = bx - pblk;
+  const int32_t blk = xcd_blocks > 0 ? (sb % NUM_XCD) * xcd_blocks + sb / NUM_XCD : sb;
+  const int32_t s = __builtin_amdgcn_readfirstlane(blk * (WV_THREADS / SNK_WAVE) + w);
+  wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(s, ptr, idx, perm, vals, Xt, Y, S, B, long_len);
 }
 
 // The value gradient of NR rounds.  One batch pass (B <= LPE * CH): every
@@ -242,13 +276,14 @@ __device__ __forceinline__ void sddmm_range(const int32_t* __restrict__ idx,
 }
 
 // One row per wave; rows of >= long_len entries (split by the tiles) are
-// left to k_wave_sddmm_pieces.  Batches wider than LPE * CH run in passes.
+// left to the tile pieces (wave_sddmm_pieces_of).  Batches wider than
+// LPE * CH run in passes.
 template <typename T, int CH, int LPE, bool MULTI>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
-    int32_t B, int32_t long_len) {
-  const int32_t s = wave_segment(0);
+__device__ __forceinline__ void wave_sddmm_of(int32_t s, const int32_t* __restrict__ ptr,
+                                              const int32_t* __restrict__ idx,
+                                              const T* __restrict__ dYt,
+                                              const T* __restrict__ Xt, T* __restrict__ dV,
+                                              int32_t S, int32_t B, int32_t long_len) {
   if (s >= S) return;
   const int lane = lane_id();
   const int slot = lane / LPE;
@@ -258,15 +293,22 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
   sddmm_range<T, CH, LPE, MULTI>(idx, dYt, Xt, B, s, a, e, lane, slot, b0, dV);
 }
 
-// The tile pieces of split rows, one wave per tile (the same pieces as
-// k_wave_pieces); each entry's dV is final, so no carry is needed.
 template <typename T, int CH, int LPE, bool MULTI>
-__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_pieces(
+__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
+    int32_t B, int32_t long_len) {
+  wave_sddmm_of<T, CH, LPE, MULTI>(wave_segment(0), ptr, idx, dYt, Xt, dV, S, B, long_len);
+}
+
+// The tile pieces of split rows, one wave per tile (the same pieces as
+// wave_pieces_of); each entry's dV is final, so no carry is needed.
+template <typename T, int CH, int LPE, bool MULTI>
+__device__ __forceinline__ void wave_sddmm_pieces_of(
+    int32_t p, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
     const int32_t* __restrict__ cut, const T* __restrict__ dYt, const T* __restrict__ Xt,
     T* __restrict__ dV, int32_t P, int32_t B) {
-  const int32_t p = wave_segment(0);
   if (p >= P) return;
   const int32_t s0 = part_seg[p], s1 = part_seg[p + 1];
   const bool c0 = cut[p] != 0, c1 = cut[p + 1] != 0;
@@ -283,6 +325,27 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_pieces(
                                    part_nz[p + 1], lane, slot, b0, dV);
 }
 
+// Both halves of a view with split rows in one launch, so that they overlap:
+// workgroups below pblk run the tile pieces, the rest the rows of < long_len
+// entries.
+template <typename T, int CH, int LPE, bool MULTI>
+__global__ __launch_bounds__(WV_THREADS) void k_wave_sddmm_split(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ part_seg, const int32_t* __restrict__ part_nz,
+    const int32_t* __restrict__ cut, const T* __restrict__ dYt, const T* __restrict__ Xt,
+    T* __restrict__ dV, int32_t S, int32_t P, int32_t B, int32_t long_len, int32_t pblk) {
+  const int32_t w = (int32_t)(threadIdx.x / SNK_WAVE);
+  const int32_t bx = (int32_t)blockIdx.x;
+  if (bx < pblk) {
+    const int32_t p = __builtin_amdgcn_readfirstlane(bx * (WV_THREADS / SNK_WAVE) + w);
+    wave_sddmm_pieces_of<T, CH, LPE, MULTI>(p, ptr, idx, part_seg, part_nz, cut, dYt, Xt, dV, P,
+                                            B);
+    return;
+  }
+  const int32_t s = __builtin_amdgcn_readfirstlane((bx - pblk) * (WV_THREADS / SNK_WAVE) + w);
+  wave_sddmm_of<T, CH, LPE, MULTI>(s, ptr, idx, dYt, Xt, dV, S, B, long_len);
+}
+
 // ---------------------------------------------------------------- launch templates
 // Segments of >= T entries (split view) are skipped by the per-segment
 // kernel, summed piecewise per tile into the carry slots, and finished by
@@ -295,17 +358,20 @@ static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int
       (PERM && nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
   const unsigned passes = (unsigned)cdiv(B, LPE * CH);
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
-  dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk), passes);
-  hipLaunchKernelGGL((k_wave_spmm<T, CH, LPE, PERM, NODE_OUT, ACT>), grid, dim3(WV_THREADS), 0,
-                     s, v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B, xb,
-                     long_len);
-  if (v.has_split) {
-    dim3 pg((unsigned)cdiv(v.P, WV_THREADS / SNK_WAVE), passes);
-    hipLaunchKernelGGL((k_wave_pieces<T, CH, LPE, PERM>), pg, dim3(WV_THREADS), 0, s, v.ptr,
-                       v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, v.cut,
-                       (const T*)Xt, carry, v.P, B);
-    launch_fixup(v, sizeof(T) == 2 ? SNACK_BF16 : SNACK_F32, NODE_OUT, ACT, carry, Y, B, s);
+  const int32_t sblk = xb ? xb * NUM_XCD : nblk;
+  if (!v.has_split) {
+    hipLaunchKernelGGL((k_wave_spmm<T, CH, LPE, PERM, NODE_OUT, ACT>), dim3((unsigned)sblk, passes),
+                       dim3(WV_THREADS), 0, s, v.ptr, v.idx, v.perm, (const T*)vals,
+                       (const T*)Xt, (T*)Y, v.S, B, xb, long_len);
+    return;
   }
+  const int32_t pblk =
+      (int32_t)(cdiv(cdiv(v.P, WV_THREADS / SNK_WAVE), NUM_XCD) * NUM_XCD);
+  hipLaunchKernelGGL((k_wave_spmm_split<T, CH, LPE, PERM, NODE_OUT, ACT>),
+                     dim3((unsigned)(pblk + sblk), passes), dim3(WV_THREADS), 0, s, v.ptr, v.idx,
+                     v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B, xb, long_len,
+                     v.part_seg, v.part_nz, v.cut, carry, v.P, pblk);
+  launch_fixup(v, sizeof(T) == 2 ? SNACK_BF16 : SNACK_F32, NODE_OUT, ACT, carry, Y, B, s);
 }
 
 template <typename T, int CH, int LPE>
@@ -355,17 +421,19 @@ static void wave_spmm_d(const seg_view& v, const void* vals, const void* Xt, int
 template <typename T, int CH>
 static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int32_t B, void* dV,
                          int lpe, hipStream_t s) {
-  dim3 grid((unsigned)cdiv(v.S, WV_THREADS / SNK_WAVE));
-  dim3 pg((unsigned)cdiv(v.P, WV_THREADS / SNK_WAVE));
+  const int32_t sblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
+  const int32_t pblk = (int32_t)cdiv(v.P, WV_THREADS / SNK_WAVE);
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
 #define SNK_WSD1(L, MULTI)                                                                      \
   do {                                                                                          \
-    hipLaunchKernelGGL((k_wave_sddmm<T, CH, L, MULTI>), grid, dim3(WV_THREADS), 0, s, v.ptr,    \
-                       v.idx, (const T*)dYt, (const T*)Xt, (T*)dV, v.S, B, long_len);           \
-    if (v.has_split)                                                                            \
-      hipLaunchKernelGGL((k_wave_sddmm_pieces<T, CH, L, MULTI>), pg, dim3(WV_THREADS), 0, s,    \
-                         v.ptr, v.idx, v.part_seg, v.part_nz, v.cut, (const T*)dYt,             \
-                         (const T*)Xt, (T*)dV, v.P, B);                                         \
+    if (!v.has_split)                                                                           \
+      hipLaunchKernelGGL((k_wave_sddmm<T, CH, L, MULTI>), dim3((unsigned)sblk),                 \
+                         dim3(WV_THREADS), 0, s, v.ptr, v.idx, (const T*)dYt, (const T*)Xt,     \
+                         (T*)dV, v.S, B, long_len);                                             \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_wave_sddmm_split<T, CH, L, MULTI>), dim3((unsigned)(pblk + sblk)),  \
+                         dim3(WV_THREADS), 0, s, v.ptr, v.idx, v.part_seg, v.part_nz, v.cut,    \
+                         (const T*)dYt, (const T*)Xt, (T*)dV, v.S, v.P, B, long_len, pblk);     \
   } while (0)
 #define SNK_WSD(L)                                             \
   do {                                                         \
