@@ -182,6 +182,24 @@ def test_products_skewed_rows_with_splits(orc):
         assert topo.plan.has_split_row == 1
 
 
+def test_products_skewed_columns_with_splits(orc):
+    """Columns of 1 .. 3000 entries, tiles of 64 items: the input gradient's
+    long columns are summed as tile pieces by the first workgroups of the
+    launch that runs the short ones, in the die-contiguous block order (400
+    columns), with piece workgroups past the last tile."""
+    M, K = 3000, 400
+    deg = synth.rank_profile(K, M, 60000, 1.3)
+    rng = np.random.default_rng(4)
+    lin = np.sort(np.concatenate([np.sort(rng.choice(M, d, replace=False)) * K + c
+                                  for c, d in enumerate(rng.permutation(deg))]))
+    for dt, layout, Bsz in (("f32", "batch", 3), ("bf16", "node", 16), ("f32", "node", 32),
+                            ("bf16", "node", 1), ("f32", "node", 100)):
+        w = synth.random_case(8, M, K, lin.size, Bsz, dt, layout, positions=lin)
+        topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, layout, Bsz, tile=64,
+                            repeat_check=True)
+        assert topo.plan.has_split_col == 1
+
+
 @pytest.mark.parametrize("name,B", [("single", 4)])
 def test_single_layer_config(orc, name, B):
     w = workload(name)
