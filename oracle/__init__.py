@@ -218,7 +218,9 @@ def memory_by_definition(M: int, K: int, nnz: int, elem_bytes: int, max_batch: i
     a weight and a gradient of M*K values; the mask one byte per weight;
     the activations X (B x K), Y (B x M) and their gradients at B =
     max_batch.  Plan and workspace sizes belong to the implementation, not
-    to the definition, and are not computed here."""
+    to the definition, and are not computed here.  Pinned against byte
+    counts written out by hand and against numpy's nbytes of arrays of those
+    shapes and dtypes."""
     mk = M * K
     return {
         "coo": nnz * (4 + 4 + elem_bytes),

@@ -25,6 +25,7 @@
  *
  * Parity pins (see tests/test_oracle_pins.py): a dense masked product through
  * numpy, the identities dX = dY W_dense and dV = (dY^T X)[row, col], the
+ * error scales against the same products taken over |W|, |X| and |dY|, the
  * adjoint identity <dY, Y> = <dX, X> = <v, dV>, exact finite differences of
  * a bilinear map, brute-force recounts of the derived index arrays, a full
  * lexicographic sort for the prune, and published SplitMix64 outputs.

@@ -53,12 +53,20 @@ def test_products_match_dense_masked_gemm(orc, M, K, nnz, B, layout):
     Xb, dYb = as_bf(X, layout, B, K), as_bf(dY, layout, B, M)
     Y, S = orc.spmm_fwd(M, K, wt.row, wt.col, wt.vals_f64(), B, X, nm)
     np.testing.assert_allclose(as_bf(Y, layout, B, M), Xb @ W.T, rtol=0, atol=1e-13)
-    dX, _ = orc.spmm_bwd_input(M, K, wt.row, wt.col, wt.vals_f64(), B, dY, nm)
+    dX, S_dx = orc.spmm_bwd_input(M, K, wt.row, wt.col, wt.vals_f64(), B, dY, nm)
     np.testing.assert_allclose(as_bf(dX, layout, B, K), dYb @ W, rtol=0, atol=1e-13)
-    dV, _ = orc.sddmm(M, K, wt.row, wt.col, B, dY, X, nm)
+    dV, S_dw = orc.sddmm(M, K, wt.row, wt.col, B, dY, X, nm)
     np.testing.assert_allclose(dV, (dYb.T @ Xb)[wt.row, wt.col], rtol=0, atol=1e-13)
-    # scale is the sum of term magnitudes: |Y| <= S, and S = |X| |W|^T
+    # each error scale is the sum of its output's term magnitudes, i.e. the
+    # same product taken over |W|, |X| and |dY|: S_y = |X| |W|^T,
+    # S_dx = |dY| |W| and S_dw = (|dY|^T |X|) at the nonzeros.  These scales
+    # gate every GPU tolerance, so a wrong one would silently loosen them.
     np.testing.assert_allclose(as_bf(S, layout, B, M), np.abs(Xb) @ np.abs(W).T, atol=1e-13)
+    np.testing.assert_allclose(as_bf(S_dx, layout, B, K), np.abs(dYb) @ np.abs(W), atol=1e-13)
+    np.testing.assert_allclose(S_dw, (np.abs(dYb).T @ np.abs(Xb))[wt.row, wt.col], atol=1e-13)
+    # a scale bounds its output and is never negative
+    for out, sc in ((Y, S), (dX, S_dx), (dV, S_dw)):
+        assert (sc >= 0).all() and (np.abs(out) <= sc + 1e-13).all()
 
 
 def test_diagonal_identity_is_exact(orc):
@@ -410,3 +418,54 @@ def test_graph_propagation_composes_dense_steps(orc):
     eye = np.arange(N, dtype=np.int32)
     out = orc.graph_propagate(N, N, eye, eye, np.ones(N), B, X, 2, 1)
     assert np.array_equal(out[-1][0], np.maximum(X, 0))
+
+
+# ------------------------------------------------------------ memory by definition
+# Byte counts of the definition-fixed tensors, written out by hand (not by
+# the oracle's formula): int32 row and col plus one value per connection for
+# the COO, one value per connection for the value gradient, M*K values for
+# the dense weight and again for its gradient, one byte per weight for the
+# Dense+Mask mask, and X, Y, dX, dY at the largest batch.  The SNACK
+# abstract compares a 90%-sparse single layer's memory against dense; the
+# second case is that point at 4096 x 4096 in fp32.
+MEMORY_BY_HAND = [
+    # 256 x 256 at 90%: 6,554 nnz, fp32, batch 4
+    ((256, 256, 6554, 4, 4),
+     {"coo": 78_648, "value_grad": 26_216, "dense_weight": 262_144, "dense_grad": 262_144,
+      "mask": 65_536, "activations": 16_384}),
+    # 4096 x 4096 at 90%: 1,677,722 nnz, fp32, batch 1
+    ((4096, 4096, 1_677_722, 4, 1),
+     {"coo": 20_132_664, "value_grad": 6_710_888, "dense_weight": 67_108_864,
+      "dense_grad": 67_108_864, "mask": 16_777_216, "activations": 65_536}),
+    # 4096 x 4096 at 95%: 838,861 nnz, bf16, batch 32
+    ((4096, 4096, 838_861, 2, 32),
+     {"coo": 8_388_610, "value_grad": 1_677_722, "dense_weight": 33_554_432,
+      "dense_grad": 33_554_432, "mask": 16_777_216, "activations": 1_048_576}),
+]
+
+
+@pytest.mark.parametrize("args,expect", MEMORY_BY_HAND)
+def test_memory_by_definition_hand_counts(orc, args, expect):
+    assert orc.memory_by_definition(*args) == expect
+
+
+@pytest.mark.parametrize("args,_", MEMORY_BY_HAND[:2])
+def test_memory_by_definition_matches_allocated_arrays(orc, args, _):
+    """The same counts as the nbytes of arrays of those shapes and dtypes
+    (numpy's own bookkeeping; np.empty touches no memory)."""
+    M, K, nnz, s, B = args
+    ft = {4: np.float32, 2: np.uint16}[s]
+    arrays = {"coo": [np.empty(nnz, np.int32), np.empty(nnz, np.int32), np.empty(nnz, ft)],
+              "value_grad": [np.empty(nnz, ft)],
+              "dense_weight": [np.empty((M, K), ft)], "dense_grad": [np.empty((M, K), ft)],
+              "mask": [np.empty((M, K), np.uint8)],
+              "activations": [np.empty((B, K), ft), np.empty((B, M), ft),
+                              np.empty((B, K), ft), np.empty((B, M), ft)]}
+    got = orc.memory_by_definition(M, K, nnz, s, B)
+    assert got == {k: sum(a.nbytes for a in v) for k, v in arrays.items()}
+    # by definition the sparse layer (COO + value gradient) at 10% density
+    # with int32 indices and fp32 values holds 16 B per connection against 8 B
+    # per dense weight: one fifth of the dense layer
+    if (M, K, s) == (4096, 4096, 4):
+        assert (got["coo"] + got["value_grad"]) * 5 == pytest.approx(
+            got["dense_weight"] + got["dense_grad"], rel=1e-6)
