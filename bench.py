@@ -126,6 +126,9 @@ class Instance:
         self.dV = torch.empty(wt.nnz, dtype=dt, device="cuda")
         self.topo = snk.Topology(self.row, self.col, wt.M, wt.K, B,
                                  flags=snk.binding.PLAN_NODE_MAJOR_ONLY if layout == "node" else 0)
+        # the values in column order, read coalesced by the input gradient;
+        # kept in step by the restructure, which writes them
+        self.vals_t = self.topo.gather_vals_t(self.vals)
         self.n_drop = snk.snack_drop_count(wt.nnz, drop_ppm)
         self.ws = torch.empty(snk.snack_prune_regrow_workspace(wt.M, wt.K, wt.nnz, self.n_drop),
                               dtype=torch.uint8, device="cuda")
@@ -136,7 +139,7 @@ class Instance:
         if ev: ev[0].record()
         t.fwd(self.vals, self.X, self.B, self.lay, out=self.Y)
         if ev: ev[1].record()
-        t.bwd_input(self.vals, self.dY, self.B, self.lay, out=self.dX)
+        t.bwd_input_t(self.vals_t, self.dY, self.B, self.lay, out=self.dX)
         if ev: ev[2].record()
         t.grad_vals(self.dY, self.X, self.B, self.lay, out=self.dV)
         if ev: ev[3].record()
@@ -145,20 +148,22 @@ class Instance:
         """dX and dV in one pass (snack_spmm_bwd_fused), no value update."""
         import unstructured_sparse_nn_amd as snk
         snk.snack_spmm_bwd_fused(self.topo.plan, self.vals, self.X, self.dY, self.lay, self.B,
-                                 self.dX, self.dV, lr)
+                                 self.dX, self.dV, lr, vals_t=self.vals_t)
 
     def restructure(self, ev=None, fused=True):
         import unstructured_sparse_nn_amd as snk
         self.step_no += 1
         if fused:  # prune/regrow and re-prepare in one call
             snk.snack_prune_regrow_prepared(self.topo.plan, self.row, self.col, self.vals,
-                                            self.n_drop, 0, self.step_no, None, None, self.ws)
+                                            self.n_drop, 0, self.step_no, None, None, self.ws,
+                                            vals_t=self.vals_t)
             if ev: ev[4].record()
             return
         snk.snack_prune_regrow(self.row, self.col, self.vals, self.M, self.K, self.topo.nnz,
                                self.n_drop, 0, self.step_no, None, None, self.ws)
         if ev: ev[4].record()
         snk.snack_coo_prepare(self.topo.plan, self.row, self.col, self.topo.arena)
+        snk.snack_gather_vals_t(self.topo.plan, self.vals, self.vals_t)
         if ev: ev[5].record()
 
 
@@ -171,9 +176,15 @@ def graph_kernel_us(insts, op, launches=20, replays=5):
     fns = {"fwd": lambda i: insts[i % R].topo.fwd(insts[i % R].vals, insts[i % R].X,
                                                    insts[i % R].B, insts[i % R].lay,
                                                    out=insts[i % R].Y),
-           "bwd_input": lambda i: insts[i % R].topo.bwd_input(insts[i % R].vals, insts[i % R].dY,
-                                                              insts[i % R].B, insts[i % R].lay,
-                                                              out=insts[i % R].dX),
+           "bwd_input": lambda i: insts[i % R].topo.bwd_input_t(insts[i % R].vals_t,
+                                                                insts[i % R].dY, insts[i % R].B,
+                                                                insts[i % R].lay,
+                                                                out=insts[i % R].dX),
+           "bwd_input_perm": lambda i: insts[i % R].topo.bwd_input(insts[i % R].vals,
+                                                                   insts[i % R].dY,
+                                                                   insts[i % R].B,
+                                                                   insts[i % R].lay,
+                                                                   out=insts[i % R].dX),
            "sddmm": lambda i: insts[i % R].topo.grad_vals(insts[i % R].dY, insts[i % R].X,
                                                           insts[i % R].B, insts[i % R].lay,
                                                           out=insts[i % R].dV),

@@ -20,17 +20,19 @@
  *     (B x F, element [b*F + f]) or node-major (F x B, element [f*B + b]).
  *     Outputs use the same layout as the inputs.
  *   - memory: every array argument is caller-owned device memory unless
- *     stated otherwise; the library never allocates device memory and keeps
- *     no global device state.  Plans are caller-owned host structs.
+ *     stated otherwise.  The library allocates no memory (device or pinned
+ *     host) and keeps no global state; its one exception is the code object
+ *     of a generated fixed-pattern kernel (snack_fixed_build), owned by its
+ *     handle.  Plans are caller-owned host structs.
  *   - streams: `stream` is a hipStream_t (NULL = the null stream).  All
  *     calls are stream-ordered and asynchronous, except snack_coo_prepare
- *     and snack_prune_regrow(_prepared), which read a few bytes back and
- *     wait for the stream before returning.  prepare and the bitmap plan of
- *     the restructure wait by spinning on a completion word that a last,
- *     one-thread kernel stores into pinned host memory (falling back to
- *     hipStreamSynchronize after 20 ms, or always with the environment
- *     variable SNACK_BLOCKING_SYNC set); the calling thread is busy while it
- *     waits.
+ *     and snack_prune_regrow(_prepared), which read a few words back and
+ *     wait for the stream before returning.  With a plan whose host_words
+ *     point to caller-owned pinned host memory, the kernels store those
+ *     words straight into it and the host spins on a completion word that a
+ *     last, one-thread kernel stores (falling back to hipStreamSynchronize
+ *     after 20 ms); the calling thread is busy while it waits.  Otherwise the
+ *     words are copied back and the stream synchronised.
  *   - errors: a negative snack_status.  Argument errors are detected on the
  *     host before anything is launched and leave every output untouched.
  *     Nothing aborts or prints.
@@ -89,6 +91,9 @@ typedef enum {
 
 #define SNACK_PLAN_SLOTS 16
 
+/* Bytes of caller-owned pinned host memory a plan's host_words must hold. */
+#define SNACK_HOST_WORDS_BYTES 64
+
 /*
  * Plan: the prepared topology of one COO weight.  Filled by snack_plan_init
  * (sizes) and snack_coo_prepare (derived arrays in the caller's arena).
@@ -109,6 +114,15 @@ typedef struct snack_plan {
   void* arena;               /* device arena recorded by prepare (not owned) */
   size_t arena_bytes;        /* bytes the arena must provide (set by init) */
   size_t off[SNACK_PLAN_SLOTS]; /* byte offsets of the arrays in the arena */
+  /* Optional, set by the caller after snack_plan_init: pinned, device-mapped
+   * host memory of SNACK_HOST_WORDS_BYTES bytes (hipHostMalloc, or a pinned
+   * torch tensor), owned by the caller and used by one call at a time.  The
+   * calls that read words back (prepare, the prepared restructure) have the
+   * kernels store them straight into it, with no copy; NULL: the words come
+   * back by a copy and a stream sync (a few microseconds more). */
+  int32_t* host_words;
+  int32_t* host_words_dev;   /* device address of host_words (set by the library) */
+  const int32_t* host_words_key; /* host_words that host_words_dev belongs to */
 } snack_plan;
 
 /* Library version (major*10000 + minor*100 + patch) and sizeof(snack_plan),
@@ -162,7 +176,8 @@ SNACK_API snack_status snack_plan_init(snack_plan* plan, int32_t M, int32_t K, i
  * Runs about a dozen kernels, then reads back 12 bytes (error bits and the
  * two has_split flags) and waits for `stream` (see streams above).  Records row, col and
  * arena in the plan; they must stay alive and unchanged while the plan is
- * used.  Re-run after every change of the sparsity pattern.
+ * used.  Re-run after every change of the sparsity pattern.  SNACK_E_WORKSPACE
+ * if plan->host_words is set but is not pinned, device-mapped host memory.
  */
 SNACK_API snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32_t* col,
                                void* arena, size_t arena_bytes, void* stream);
@@ -232,6 +247,34 @@ SNACK_API snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* 
                                   void* stream);
 
 /*
+ * Values in column order.  The input gradient walks the column view, whose
+ * i-th entry is stored value perm[i]; reading vals[perm[i]] is a scattered
+ * load per entry.  A caller-owned copy vals_t[i] = vals[perm[i]] (nnz
+ * elements of the value dtype) lets it read the values coalesced, as the
+ * forward product does.  The copy is the caller's to keep in step with the
+ * values: snack_gather_vals_t writes it from vals, and the two calls that
+ * write the values themselves (snack_spmm_bwd_fused's update,
+ * snack_prune_regrow_prepared) can keep it as well.
+ *
+ * snack_gather_vals_t: vals_t[i] = vals[perm[i]] for i < nnz.  Asynchronous.
+ * Errors: SNACK_E_NULL, SNACK_E_NOT_PREPARED, SNACK_E_DTYPE.
+ */
+SNACK_API snack_status snack_gather_vals_t(const snack_plan* plan, const void* vals,
+                                           snack_dtype dtype, void* vals_t, void* stream);
+
+/*
+ * snack_spmm_bwd_input_t -- snack_spmm_bwd_input with the values given in
+ * column order (vals_t as above):
+ *     dX[b, c] = sum_{i : col_ptr[c] <= i < col_ptr[c+1]} vals_t[i] * dY[b, row_t[i]]
+ * which equals dY W when vals_t[i] = vals[perm[i]].  Same arguments, layouts
+ * and errors as snack_spmm_bwd_input.
+ */
+SNACK_API snack_status snack_spmm_bwd_input_t(const snack_plan* plan, const void* vals_t,
+                                              snack_dtype dtype, const void* dY,
+                                              snack_layout layout, int32_t B, void* dX,
+                                              void* stream);
+
+/*
  * snack_sddmm_grad_vals -- gradient with respect to the stored values
  * only, (dY^T X) sampled at the nonzeros:
  *     dV[k] = sum_{b < B} dY[b, row[k]] * X[b, col[k]]
@@ -256,12 +299,16 @@ SNACK_API snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void*
  * follows the SNACK abstract's wish to keep backpropagation in the sparse
  * paradigm; fusing it with the optimiser is this library's.
  * X, dY: activations of the forward (B x K / B x M, or node-major); dX as
- * for snack_spmm_bwd_input.  Errors: as for the products, SNACK_E_SHAPE for
- * B > 32, SNACK_E_NAN for a NaN or infinite lr.
+ * for snack_spmm_bwd_input.  vals_t (nullable): the values in column order
+ * (vals_t[i] == vals[perm[i]], see snack_gather_vals_t); when given, the
+ * values are read from it coalesced, and with lr != 0 it is updated as well,
+ * so it stays in step with vals.  Errors: as for the products, SNACK_E_SHAPE
+ * for B > 32, SNACK_E_NAN for a NaN or infinite lr.
  */
-SNACK_API snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, snack_dtype dtype,
-                                  const void* X, const void* dY, snack_layout layout, int32_t B,
-                                  void* dX, void* dvals, float lr, void* stream);
+SNACK_API snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, void* vals_t,
+                                  snack_dtype dtype, const void* X, const void* dY,
+                                  snack_layout layout, int32_t B, void* dX, void* dvals,
+                                  float lr, void* stream);
 
 /*
  * snack_drop_count -- number of connections one restructuring step
@@ -273,6 +320,16 @@ SNACK_API int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm);
 /* Workspace bytes snack_prune_regrow needs for these sizes. */
 SNACK_API snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
                                           size_t* bytes);
+
+/* Restructure flags (the _ex calls and snack_prune_regrow_prepared).  The
+ * library runs the bitmap plan (support bitmaps over the M x K grid) when the
+ * density is at most 1/4 and the bitmaps are small, else the sort plan
+ * (candidates sorted by position).  SNACK_PRUNE_SORT_PLAN forces the sort
+ * plan; both give identical results. */
+#define SNACK_PRUNE_SORT_PLAN 1u
+SNACK_API snack_status snack_prune_regrow_workspace_ex(int32_t M, int32_t K, int64_t nnz,
+                                                       int64_t n_drop, uint32_t flags,
+                                                       size_t* bytes);
 
 /*
  * snack_prune_regrow -- one restructuring step of dynamic sparse training
@@ -294,12 +351,20 @@ SNACK_API snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_
  * grown linear indices in increasing order.  ws must hold
  * snack_prune_regrow_workspace bytes.  Re-run snack_coo_prepare afterwards.
  * Errors: SNACK_E_COUNT, SNACK_E_NAN (COO left unchanged), SNACK_E_WORKSPACE.
- * Synchronises `stream`.
+ * Synchronises `stream` (its few result words come back by a copy).
  */
 SNACK_API snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
                                 int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
                                 uint64_t seed, uint64_t step, int64_t* dropped_lin,
                                 int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream);
+/* The same with restructure flags (ws sized by snack_prune_regrow_workspace_ex
+ * with the same flags); SNACK_E_LAYOUT for an unknown flag. */
+SNACK_API snack_status snack_prune_regrow_ex(int32_t* row, int32_t* col, void* vals,
+                                             snack_dtype dtype, int32_t M, int32_t K,
+                                             int64_t nnz, int64_t n_drop, uint64_t seed,
+                                             uint64_t step, int64_t* dropped_lin,
+                                             int64_t* grown_lin, void* ws, size_t ws_bytes,
+                                             uint32_t flags, void* stream);
 
 /*
  * snack_prune_regrow_prepared -- snack_prune_regrow followed by
@@ -312,17 +377,19 @@ SNACK_API snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals
  * from a 32 x 32 bit-tile transpose), with no sort and no re-validation;
  * otherwise the two calls run one after the other.  Results (COO, lists,
  * derived arrays) are identical either way.  dtype, n_drop, seed, step,
- * dropped_lin, grown_lin, ws, ws_bytes: as for snack_prune_regrow (ws sized
- * by snack_prune_regrow_workspace).  Errors: as for snack_prune_regrow, plus
- * SNACK_E_NOT_PREPARED (plan never prepared) and SNACK_E_SHAPE (plan of
- * another shape).  On error the plan must be prepared again before use.
+ * dropped_lin, grown_lin, ws, ws_bytes, flags: as for snack_prune_regrow_ex
+ * (ws sized by snack_prune_regrow_workspace_ex with the same flags).
+ * vals_t (nullable, nnz elements): receives the new values in the new
+ * column order (vals_t[i] = vals[perm[i]], see snack_gather_vals_t).
+ * Errors: as for snack_prune_regrow_ex, plus SNACK_E_NOT_PREPARED (plan
+ * never prepared).  On error the plan must be prepared again before use.
  * Synchronises `stream`.
  */
 SNACK_API snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* row, int32_t* col,
-                                         void* vals, snack_dtype dtype, int64_t n_drop,
-                                         uint64_t seed, uint64_t step, int64_t* dropped_lin,
-                                         int64_t* grown_lin, void* ws, size_t ws_bytes,
-                                         void* stream);
+                                         void* vals, void* vals_t, snack_dtype dtype,
+                                         int64_t n_drop, uint64_t seed, uint64_t step,
+                                         int64_t* dropped_lin, int64_t* grown_lin, void* ws,
+                                         size_t ws_bytes, uint32_t flags, void* stream);
 
 /*
  * snack_memory_footprint -- host only: device bytes of one layer, held
@@ -334,12 +401,14 @@ SNACK_API snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* ro
  * and restructuring steps of n_drop connections (0: no restructuring):
  *   coo            row, col (int32) and values: nnz * (8 + s)
  *   value_grad     the value gradient dV: nnz * s
+ *   col_values     the values in column order that the input gradient reads
+ *                  (snack_gather_vals_t): nnz * s
  *   derived        the arrays a prepared plan keeps (row offsets, column
  *                  view, tiles and cut flags of both views)
  *   plan_scratch   the rest of the plan arena (sort buffers of prepare,
  *                  carry slots, node-major copies of activations)
  *   restructure_ws snack_prune_regrow_workspace(M, K, nnz, n_drop), or 0
- *   sparse_total   the sum of the five above
+ *   sparse_total   the sum of the six above
  *   dense_weight, dense_grad   M * K * s each; dense_total their sum
  *   mask           a uint8 mask of the Dense+Mask layer: M * K
  *   masked_total   dense_total + mask
@@ -350,7 +419,7 @@ SNACK_API snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* ro
  * snack_prune_regrow_workspace, SNACK_E_DTYPE, SNACK_E_COUNT.
  */
 typedef struct snack_footprint {
-  uint64_t coo, value_grad, derived, plan_scratch, restructure_ws, sparse_total;
+  uint64_t coo, value_grad, col_values, derived, plan_scratch, restructure_ws, sparse_total;
   uint64_t dense_weight, dense_grad, dense_total;
   uint64_t mask, masked_total;
   uint64_t activations;

@@ -80,6 +80,51 @@ def test_products_reject_unprepared_plan(snk):
     assert b.raw_status("snack_spmm_fwd", None, 1, 0, 1, 0, 1, 1, None) == -1
 
 
+def test_column_order_value_calls_reject_bad_arguments(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_gather_vals_t(p, 0x1000, 0x2000, stream=0, dtype=b.F32)
+    assert e.value.status == -12
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_spmm_bwd_input_t(p, 0x1000, 0x2000, 0, 1, 0x3000, stream=0, dtype=b.F32)
+    assert e.value.status == -12
+    assert b.raw_status("snack_gather_vals_t", None, 1, 0, 1, None) == -1
+    assert b.raw_status("snack_spmm_bwd_input_t", None, 1, 0, 1, 0, 1, 1, None) == -1
+
+
+def test_restructure_flags_and_workspaces(snk):
+    from unstructured_sparse_nn_amd import binding as b
+    auto = b.snack_prune_regrow_workspace(256, 256, 6554, 655)
+    assert b.snack_prune_regrow_workspace(256, 256, 6554, 655, flags=b.PRUNE_SORT_PLAN) > 0
+    assert auto == b.snack_prune_regrow_workspace(256, 256, 6554, 655, flags=0)
+    sz = ctypes.c_size_t(0)
+    assert b.raw_status("snack_prune_regrow_workspace_ex", 256, 256, 6554, 655, 2,
+                        ctypes.byref(sz)) == -4
+    with pytest.raises(snk.SnackError) as e:
+        b.snack_prune_regrow(0x10, 0x20, 0x30, 4, 4, 3, 1, 0, 0, None, None, 0x40, stream=0,
+                             ws_bytes=1 << 20, dtype=b.F32, flags=6)
+    assert e.value.status == -4
+    p = snk.snack_plan_init(8, 8, 4, 2)
+    with pytest.raises(snk.SnackError) as e:  # never prepared: no arena
+        b.snack_prune_regrow_prepared(p, 0x10, 0x20, 0x30, 1, 0, 0, None, None, 0x40, stream=0,
+                                      ws_bytes=1 << 20, dtype=b.F32)
+    assert e.value.status == -12
+
+
+def test_library_allocates_nothing_and_reads_no_environment():
+    """The boundary's promise, checked in the sources: no device or pinned
+    allocation outside the fixed-pattern generator's code object, no
+    environment switches, no thread-local or function-static state."""
+    csrc = os.path.join(ROOT, "unstructured_sparse_nn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        text = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, name)).read())
+        for bad in ("getenv", "hipMalloc", "hipHostMalloc", "hipFree", "thread_local"):
+            assert bad not in text, (name, bad)
+        assert not re.search(r"\bstatic\s+(const\s+)?(bool|int|int32_t|int64_t|size_t|char)\b"
+                             r"[^(;]*=", text), name
+
+
 def test_prepare_rejects_small_arena_before_any_launch(snk):
     from unstructured_sparse_nn_amd import binding as b
     p = snk.snack_plan_init(8, 8, 4, 2)
@@ -148,8 +193,9 @@ def test_memory_footprint_matches_definitions_and_allocations(snk, M, K, nnz, B,
     assert f["derived"] == plan.off[10]  # derived arrays precede the scratch
     ws = snk.snack_prune_regrow_workspace(M, K, nnz, n_drop) if n_drop else 0
     assert f["restructure_ws"] == ws
-    assert f["sparse_total"] == (f["coo"] + f["value_grad"] + f["derived"] + f["plan_scratch"]
-                                 + f["restructure_ws"])
+    assert f["col_values"] == f["value_grad"]  # one value per connection, column order
+    assert f["sparse_total"] == (f["coo"] + f["value_grad"] + f["col_values"] + f["derived"]
+                                 + f["plan_scratch"] + f["restructure_ws"])
     assert f["dense_total"] == f["dense_weight"] + f["dense_grad"]
     assert f["masked_total"] == f["dense_total"] + f["mask"]
 

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpuhelp import assert_within, from_dev, to_dev, topology, torch_dtype
+from gpuhelp import assert_within, from_dev, node_major, to_dev, topology, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -65,10 +65,11 @@ def check_prepare(orc, w, topo):
         assert has == int(len(ref["split_seg"]) > 0)
 
 
-def run_products(orc, w, X, dY, dt, layout, Bsz, tile=0, sddmm=True, repeat_check=False):
+def run_products(orc, w, X, dY, dt, layout, Bsz, tile=0, sddmm=True, repeat_check=False,
+                 flags=0):
     nm = layout == "node"
     lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
-    topo = topology(w, max(Bsz, 1), tile)
+    topo = topology(w, max(Bsz, 1), tile, flags)
     vals = to_dev(w.vals, dt)
     Xd, dYd = to_dev(X.data, dt), to_dev(dY.data, dt)
     v64 = w.vals_f64()
@@ -213,12 +214,35 @@ def test_square_inference_configs(orc, sp, Bsz):
     run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz, repeat_check=True)
 
 
+@pytest.mark.parametrize("sp", ["0.95", "0.99"])
+@pytest.mark.parametrize("Bsz", [1, 8, 32])
+def test_square_node_major_benchmarked_path(orc, sp, Bsz):
+    """The layer and launch configuration the benchmark times: 4096^2,
+    node-major activations, a plan without batch-major scratch."""
+    w = workload(f"square_{sp}_{Bsz}")
+    topo = run_products(orc, w.weights[0], node_major(w.X[0]), node_major(w.dY[0]), "bf16",
+                        "node", Bsz, repeat_check=True, flags=B.PLAN_NODE_MAJOR_ONLY)
+    assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
+
+
 @pytest.mark.parametrize("which", ["up", "down"])
 @pytest.mark.parametrize("Bsz", [1, 4, 16])
 def test_llama_projection_configs(orc, which, Bsz):
     w = workload(f"llama_{which}_{Bsz}")
-    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz)
+    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], "bf16", "batch", Bsz,
+                        repeat_check=True)
     assert topo.plan.has_split_row == 1  # dense rows longer than a tile
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+@pytest.mark.parametrize("Bsz", [1, 4, 16])
+def test_llama_projection_node_major(orc, which, Bsz):
+    """The LLaMA-shaped layers as the benchmark runs them: node-major, no
+    batch-major scratch, split rows through the tile pieces and the fix-up."""
+    w = workload(f"llama_{which}_{Bsz}")
+    topo = run_products(orc, w.weights[0], node_major(w.X[0]), node_major(w.dY[0]), "bf16",
+                        "node", Bsz, repeat_check=True, flags=B.PLAN_NODE_MAJOR_ONLY)
+    assert topo.plan.has_split_row == 1
 
 
 def test_graph_config(orc):
@@ -303,35 +327,112 @@ def test_zero_batch_and_empty_weight(orc):
     assert ex.value.status == -2
 
 
+# ------------------------------------------------- values in column order
+def bits_of(t, dt):
+    """Raw bits of a float tensor (bitwise comparisons)."""
+    return (t.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16"
+            else t.view(torch.int32).cpu().numpy().view(np.uint32))
+
+
+VALS_T_CASES = [
+    # name, dtype, layout, batch, tile, flags
+    ("square_0.95_32", "bf16", "node", 32, 0, B.PLAN_NODE_MAJOR_ONLY),
+    ("square_0.99_1", "bf16", "node", 1, 0, B.PLAN_NODE_MAJOR_ONLY),
+    ("llama_up_1", "bf16", "node", 1, 0, B.PLAN_NODE_MAJOR_ONLY),
+    ("llama_down_4", "bf16", "node", 4, 0, B.PLAN_NODE_MAJOR_ONLY),
+    ("single", "f32", "batch", 4, 0, 0),
+    ("ragged", "f32", "node", 5, 64, 0),      # split columns: tile pieces and the fix-up
+    ("ragged", "bf16", "batch", 33, 0, 0),    # odd batch above 16: the merge-path kernel
+    ("ragged", "f32", "node", 100, 64, 0),    # wide batch in passes, split columns
+]
+
+
+@pytest.mark.parametrize("name,dt,layout,Bsz,tile,flags", VALS_T_CASES)
+def test_bwd_input_from_column_ordered_values(orc, name, dt, layout, Bsz, tile, flags):
+    """snack_gather_vals_t is vals[perm] bit for bit, and the input gradient
+    from it matches the oracle and equals, bit for bit, the one that reads the
+    values through perm (same entries, same order, same reduction tree)."""
+    if name == "ragged":
+        w = synth.random_case(19, 300, 200, 9000, Bsz, dt, layout)
+        wt, dY = w.weights[0], w.dY[0]
+    else:
+        w = workload(name)
+        wt = w.weights[0]
+        dY = node_major(w.dY[0]) if layout == "node" else w.dY[0]
+    nm = layout == "node"
+    lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
+    topo = topology(wt, Bsz, tile, flags)
+    vals = to_dev(wt.vals, dt)
+    vt = topo.gather_vals_t(vals)
+    _, perm, _ = orc.csc(wt.K, wt.row, wt.col)
+    assert np.array_equal(bits_of(vt, dt), bits_of(vals, dt)[perm])
+    dYd = to_dev(dY.data, dt)
+    dX = topo.bwd_input_t(vt, dYd, Bsz, lay)
+    ref, S = orc.spmm_bwd_input(wt.M, wt.K, wt.row, wt.col, wt.vals_f64(), Bsz, dY.f64(), nm)
+    assert_within(from_dev(dX, dt), ref, S, dt, "bwd_input_t")
+    assert torch.equal(topo.bwd_input(vals, dYd, Bsz, lay), dX)
+    assert torch.equal(topo.bwd_input_t(vt, dYd, Bsz, lay), dX)
+
+
+@pytest.mark.parametrize("dt,layout,Bsz,tile,lr", [
+    ("bf16", "node", 32, 0, 0.05), ("f32", "batch", 4, 0, 0.1), ("bf16", "batch", 8, 0, 0.0),
+    ("f32", "node", 5, 64, 0.1),   # split columns: merge-path form, copy refreshed by a gather
+])
+def test_bwd_fused_keeps_column_ordered_values(orc, dt, layout, Bsz, tile, lr):
+    """With vals_t, the fused backward reads the column-ordered values and its
+    SGD step updates both copies; results equal those of the call without it,
+    bit for bit, over two steps."""
+    w = synth.random_case(20, 512, 384, 20000, Bsz, dt, layout)
+    wt = w.weights[0]
+    lay = B.NODE_MAJOR if layout == "node" else B.BATCH_MAJOR
+    topo = topology(wt, Bsz, tile)
+    X, dY = to_dev(w.X[0].data, dt), to_dev(w.dY[0].data, dt)
+    v1, v2 = to_dev(wt.vals, dt), to_dev(wt.vals, dt)
+    vt = topo.gather_vals_t(v2)
+    _, perm, _ = orc.csc(wt.K, wt.row, wt.col)
+    for _ in range(2):
+        outs = []
+        for v, t in ((v1, None), (v2, vt)):
+            dX = torch.empty(Bsz * wt.K, dtype=torch_dtype(dt), device="cuda")
+            dV = torch.empty(wt.nnz, dtype=torch_dtype(dt), device="cuda")
+            snk.snack_spmm_bwd_fused(topo.plan, v, X, dY, lay, Bsz, dX, dV, lr, vals_t=t)
+            outs.append((dX, dV))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+        assert torch.equal(v1, v2)
+        assert np.array_equal(bits_of(vt, dt), bits_of(v2, dt)[perm])
+    ref, S = orc.spmm_bwd_input(wt.M, wt.K, wt.row, wt.col, wt.vals_f64(), Bsz, w.dY[0].f64(),
+                                layout == "node")
+    if lr == 0.0:
+        assert_within(from_dev(outs[1][0], dt), ref, S, dt, "fused dX with vals_t")
+
+
 # --------------------------------------------------------------- prune / regrow
 @pytest.fixture(params=["auto", "sort"])
-def prune_plan(request, monkeypatch):
-    """Run a prune test with the library's own plan choice (the bitmap plan
-    for every layer density <= 1/4 here) and again forced onto the sort plan."""
-    if request.param == "sort":
-        monkeypatch.setenv("SNACK_PRUNE_PATH", "sort")
-    else:
-        monkeypatch.delenv("SNACK_PRUNE_PATH", raising=False)
-    return request.param
+def prune_plan(request):
+    """Restructure flags of a prune test: the library's own plan choice (the
+    bitmap plan for every layer density <= 1/4 here), and again forced onto
+    the sort plan."""
+    return B.PRUNE_SORT_PLAN if request.param == "sort" else 0
 
 
-def gpu_prune(w, dt, n_drop, seed, step, vals=None):
+def gpu_prune(w, dt, n_drop, seed, step, vals=None, flags=0):
     row, col = to_dev(w.row), to_dev(w.col)
     v = to_dev(w.vals if vals is None else vals, dt)
-    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop, flags),
                      dtype=torch.uint8, device="cuda")
     dl = torch.empty(max(n_drop, 1), dtype=torch.int64, device="cuda")
     gl = torch.empty(max(n_drop, 1), dtype=torch.int64, device="cuda")
-    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, seed, step, dl, gl, ws)
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, seed, step, dl, gl, ws,
+                           flags=flags)
     return row, col, v, dl[:n_drop], gl[:n_drop]
 
 
-def check_prune(orc, w, dt, ppm, seed, step, vals=None):
+def check_prune(orc, w, dt, ppm, seed, step, vals=None, flags=0):
     n_drop = orc.drop_count(w.nnz, ppm)
     vals = w.vals if vals is None else vals
     ref = orc.prune_regrow(w.M, w.K, w.row, w.col, vals, dt, n_drop, seed, step)
     assert ref["rc"] == 0
-    row, col, v, dl, gl = gpu_prune(w, dt, n_drop, seed, step, vals)
+    row, col, v, dl, gl = gpu_prune(w, dt, n_drop, seed, step, vals, flags)
     assert np.array_equal(row.cpu().numpy(), ref["row"])
     assert np.array_equal(col.cpu().numpy(), ref["col"])
     if dt == "bf16":
@@ -347,13 +448,13 @@ def check_prune(orc, w, dt, ppm, seed, step, vals=None):
 
 def test_prune_regrow_single_layer(orc, prune_plan):
     w = workload("single").weights[0]
-    check_prune(orc, w, "f32", 100000, 0, 1)
+    check_prune(orc, w, "f32", 100000, 0, 1, flags=prune_plan)
 
 
 @pytest.mark.parametrize("sp", ["0.9", "0.99"])
 def test_prune_regrow_gpt2(orc, sp, prune_plan):
     for W in workload(f"gpt2_{sp}").weights:
-        row, col = check_prune(orc, W, "f32", 300000, 0, 5)
+        row, col = check_prune(orc, W, "f32", 300000, 0, 5, flags=prune_plan)
         # the restructured COO prepares exactly as the oracle says
         w2 = synth.SparseWeight(W.M, W.K, row.cpu().numpy(), col.cpu().numpy(), W.vals, "f32")
         check_prepare(orc, w2, topology(w2, 1))
@@ -365,12 +466,12 @@ def test_prune_regrow_bf16_ties_and_signed_zero(orc, prune_plan):
     vals[::7] = vals[3]                    # many exact ties
     vals[1::11] = np.uint16(0x8000)        # -0
     vals[2::13] = np.uint16(0)             # +0
-    check_prune(orc, w, "bf16", 250000, 42, 9, vals)
+    check_prune(orc, w, "bf16", 250000, 42, 9, vals, flags=prune_plan)
 
 
 def test_prune_regrow_square_bf16(orc, prune_plan):
     w = workload("square_0.95_1").weights[0]
-    check_prune(orc, w, "bf16", 300000, 3, 1)
+    check_prune(orc, w, "bf16", 300000, 3, 1, flags=prune_plan)
 
 
 def test_prune_regrow_nearly_full_needs_several_chunks(orc, prune_plan):
@@ -378,7 +479,7 @@ def test_prune_regrow_nearly_full_needs_several_chunks(orc, prune_plan):
     M, K = 40, 60
     nnz = M * K - 30
     w = synth.random_case(9, M, K, nnz, 1).weights[0]
-    check_prune(orc, w, "f32", 10000, 5, 2)
+    check_prune(orc, w, "f32", 10000, 5, 2, flags=prune_plan)
 
 
 def test_prune_regrow_rejects_nan_and_keeps_coo(prune_plan):
@@ -387,10 +488,11 @@ def test_prune_regrow_rejects_nan_and_keeps_coo(prune_plan):
     vals[17] = np.nan
     row, col = to_dev(w.row), to_dev(w.col)
     v = to_dev(vals)
-    ws = torch.empty(snk.snack_prune_regrow_workspace(64, 64, 400, 40), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(snk.snack_prune_regrow_workspace(64, 64, 400, 40, prune_plan),
+                     dtype=torch.uint8, device="cuda")
     with pytest.raises(snk.SnackError) as e:
-        snk.snack_prune_regrow(row, col, v, 64, 64, 400, 40, 1, 1, None, None, ws)
+        snk.snack_prune_regrow(row, col, v, 64, 64, 400, 40, 1, 1, None, None, ws,
+                               flags=prune_plan)
     assert e.value.status == -7
     assert np.array_equal(row.cpu().numpy(), w.row) and np.array_equal(col.cpu().numpy(), w.col)
 
@@ -407,13 +509,15 @@ def test_prune_regrow_without_lists_and_second_step(orc, prune_plan):
     w = workload("single").weights[0]
     n_drop = orc.drop_count(w.nnz, 100000)
     row, col, v = to_dev(w.row), to_dev(w.col), to_dev(w.vals)
-    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop, prune_plan),
                      dtype=torch.uint8, device="cuda")
-    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 1, None, None, ws)
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 1, None, None, ws,
+                           flags=prune_plan)
     ref = orc.prune_regrow(w.M, w.K, w.row, w.col, w.vals, "f32", n_drop, 0, 1)
     assert np.array_equal(row.cpu().numpy(), ref["row"])
     assert np.array_equal(col.cpu().numpy(), ref["col"])
-    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 2, None, None, ws)
+    snk.snack_prune_regrow(row, col, v, w.M, w.K, w.nnz, n_drop, 0, 2, None, None, ws,
+                           flags=prune_plan)
     ref2 = orc.prune_regrow(w.M, w.K, ref["row"], ref["col"],
                             np.asarray(ref["vals"], np.float32), "f32", n_drop, 0, 2)
     assert np.array_equal(row.cpu().numpy(), ref2["row"])
@@ -467,18 +571,21 @@ def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile)
     assert ref["rc"] == 0
     topo = topology(w, 4, tile)
     v = to_dev(w.vals, dt)
-    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop),
+    ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop, prune_plan),
                      dtype=torch.uint8, device="cuda")
     dl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
     gl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
+    vt = torch.full_like(v, 3.0)  # receives the new values in the new column order
     snk.snack_prune_regrow_prepared(topo.plan, topo.row, topo.col, v, n_drop, seed, step, dl, gl,
-                                    ws)
+                                    ws, vals_t=vt, flags=prune_plan)
     assert np.array_equal(topo.row.cpu().numpy(), ref["row"])
     assert np.array_equal(topo.col.cpu().numpy(), ref["col"])
     assert np.array_equal(dl.cpu().numpy(), ref["dropped"])
     assert np.array_equal(gl.cpu().numpy(), ref["grown"])
     w2 = synth.SparseWeight(w.M, w.K, ref["row"], ref["col"], ref["vals"], dt)
     check_prepare(orc, w2, topo)
+    _, perm, _ = orc.csc(w.K, ref["row"], ref["col"])
+    assert np.array_equal(bits_of(vt, dt), bits_of(v, dt)[perm])
     xf = np.random.default_rng(14).standard_normal(4 * w.K).astype(np.float32)
     Xa = synth.Activation(xf if dt == "f32" else synth.f32_to_bf16_bits(xf), dt, 4, w.K,
                           "batch")
@@ -604,6 +711,37 @@ def test_dense_baseline(orc, dt, masked, Bsz, K):
     assert_within(from_dev(Y, dt), Xb @ Wm.T, np.abs(Xb) @ np.abs(Wm).T, dt, "dense")
 
 
+def test_sparse_linear_column_values_follow_updates(orc):
+    """The layer's column-ordered values follow a restructure (written by it)
+    and a torch optimiser step (the version counter moves: gathered again);
+    the input gradient read from them matches the oracle each time."""
+    w = synth.random_case(22, 256, 320, 8000, 8, "f32")
+    wt = w.weights[0]
+    layer = snk.SparseLinear(320, 256, to_dev(wt.row), to_dev(wt.col), to_dev(wt.vals), 8)
+    x = to_dev(w.X[0].data).view(8, 320)
+    g = to_dev(w.dY[0].data).view(8, 256)
+    opt = torch.optim.SGD([layer.vals], lr=0.5)
+
+    def check(what):
+        xr = x.clone().requires_grad_(True)
+        layer.zero_grad()
+        layer(xr).backward(g)
+        row, col = layer.topo.row.cpu().numpy(), layer.topo.col.cpu().numpy()
+        v = layer.vals.detach().cpu().numpy().astype(np.float64)
+        ref, S = orc.spmm_bwd_input(256, 320, row, col, v, 8, w.dY[0].f64())
+        assert_within(from_dev(xr.grad, "f32"), ref, S, "f32", what)
+        _, perm, _ = orc.csc(320, row, col)
+        assert np.array_equal(bits_of(layer.vals_t(), "f32"), bits_of(layer.vals.data, "f32")[perm])
+
+    check("dX, first step")
+    opt.step()                      # torch changes the values: the copy is gathered again
+    check("dX after an optimiser step")
+    layer.prune_regrow(200000, 1)   # the restructure writes the copy itself
+    check("dX after a restructure")
+    opt.step()
+    check("dX after a restructure and an optimiser step")
+
+
 def test_sparse_linear_autograd(orc):
     w = workload("single")
     wt = w.weights[0]
@@ -649,18 +787,20 @@ def test_memory_footprint_matches_device_allocations(dt, n_drop_ppm, flags):
     vals = to_dev(w.vals, dt)
     dV = torch.empty_like(vals)
     topo = snk.Topology(row, col, M, K, Bsz, flags=flags)
+    vt = topo.gather_vals_t(vals)
     ws = torch.empty(f["restructure_ws"], dtype=torch.uint8, device="cuda") if n_drop else None
     torch.cuda.synchronize()
     used = torch.cuda.memory_allocated() - before
     r512 = lambda n: -(-n // 512) * 512  # noqa: E731
-    expect = (r512(4 * w.nnz) * 2 + r512(vals.element_size() * w.nnz) * 2
+    expect = (r512(4 * w.nnz) * 2 + r512(vals.element_size() * w.nnz) * 3
               + r512(f["derived"] + f["plan_scratch"]) + (r512(f["restructure_ws"]) if n_drop else 0))
     assert used == expect
-    assert f["coo"] + f["value_grad"] == 4 * w.nnz * 2 + vals.element_size() * w.nnz * 2
+    assert (f["coo"] + f["value_grad"] + f["col_values"]
+            == 4 * w.nnz * 2 + vals.element_size() * w.nnz * 3)
     assert topo.arena.numel() == f["derived"] + f["plan_scratch"]
     if n_drop:  # the workspace suffices for the restructure it was sized for
-        topo.restructure(vals, n_drop, 0, 1, ws=ws)
-    del row, col, vals, dV, topo, ws
+        topo.restructure(vals, n_drop, 0, 1, ws=ws, vals_t=vt)
+    del row, col, vals, dV, topo, ws, vt
 
 
 # ------------------------------------- fused activation and multi-layer propagation

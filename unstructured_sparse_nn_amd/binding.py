@@ -22,6 +22,8 @@ ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 CONV_NHWC, CONV_NCHW = 0, 1
 FIXED_COMPILE_ONLY = 1
 PLAN_NODE_MAJOR_ONLY = 1
+PRUNE_SORT_PLAN = 1
+HOST_WORDS_BYTES = 64
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
 
@@ -40,7 +42,8 @@ class SnackError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)})")
 
 
-FOOTPRINT_FIELDS = ("coo", "value_grad", "derived", "plan_scratch", "restructure_ws",
+FOOTPRINT_FIELDS = ("coo", "value_grad", "col_values", "derived", "plan_scratch",
+                    "restructure_ws",
                     "sparse_total", "dense_weight", "dense_grad", "dense_total", "mask",
                     "masked_total", "activations")
 
@@ -59,7 +62,8 @@ class SnackPlan(ctypes.Structure):
                 ("has_split_col", ctypes.c_int32), ("prepared", ctypes.c_int32),
                 ("row", ctypes.c_void_p), ("col", ctypes.c_void_p),
                 ("arena", ctypes.c_void_p), ("arena_bytes", ctypes.c_size_t),
-                ("off", ctypes.c_size_t * PLAN_SLOTS)]
+                ("off", ctypes.c_size_t * PLAN_SLOTS), ("host_words", ctypes.c_void_p),
+                ("host_words_dev", ctypes.c_void_p), ("host_words_key", ctypes.c_void_p)]
 
 
 def _load():
@@ -81,13 +85,20 @@ def _load():
         "snack_spmm_fwd_act": ([plan_p, P, i32, P, i32, i32, P, i32, P], i32),
         "snack_graph_propagate": ([plan_p, P, i32, P, i32, i32, i32, i32, P, P, P], i32),
         "snack_spmm_bwd_input": ([plan_p, P, i32, P, i32, i32, P, P], i32),
+        "snack_gather_vals_t": ([plan_p, P, i32, P, P], i32),
+        "snack_spmm_bwd_input_t": ([plan_p, P, i32, P, i32, i32, P, P], i32),
         "snack_sddmm_grad_vals": ([plan_p, P, P, i32, i32, i32, P, P], i32),
-        "snack_spmm_bwd_fused": ([plan_p, P, i32, P, P, i32, i32, P, P, ctypes.c_float, P], i32),
+        "snack_spmm_bwd_fused": ([plan_p, P, P, i32, P, P, i32, i32, P, P, ctypes.c_float, P],
+                                 i32),
         "snack_drop_count": ([i64, i32], i64),
         "snack_prune_regrow_workspace": ([i32, i32, i64, i64, ctypes.POINTER(sz)], i32),
+        "snack_prune_regrow_workspace_ex": ([i32, i32, i64, i64, ctypes.c_uint32,
+                                             ctypes.POINTER(sz)], i32),
         "snack_prune_regrow": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz, P], i32),
-        "snack_prune_regrow_prepared": ([plan_p, P, P, P, i32, i64, u64, u64, P, P, P, sz, P],
-                                        i32),
+        "snack_prune_regrow_ex": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P, sz,
+                                   ctypes.c_uint32, P], i32),
+        "snack_prune_regrow_prepared": ([plan_p, P, P, P, P, i32, i64, u64, u64, P, P, P, sz,
+                                         ctypes.c_uint32, P], i32),
         "snack_memory_footprint": ([i32, i32, i64, i32, i32, i64, ctypes.c_uint32,
                                     ctypes.POINTER(SnackFootprint)], i32),
         "snack_fixed_build": ([P, P, P, i32, i32, i32, i64, ctypes.c_uint32, ctypes.POINTER(P)],
@@ -213,6 +224,20 @@ def snack_spmm_bwd_input(plan, vals, dY, layout, B, dX, stream=None, dtype=None)
                                      _ptr(dX), _stream(stream)), "snack_spmm_bwd_input")
 
 
+def snack_gather_vals_t(plan, vals, vals_t, stream=None, dtype=None):
+    """vals_t[i] = vals[perm[i]]: the values in the plan's column order."""
+    dt = _dtype(vals, vals_t, dtype=dtype)
+    _check(_lib.snack_gather_vals_t(ctypes.byref(plan), _ptr(vals), dt, _ptr(vals_t),
+                                    _stream(stream)), "snack_gather_vals_t")
+
+
+def snack_spmm_bwd_input_t(plan, vals_t, dY, layout, B, dX, stream=None, dtype=None):
+    """dX = dY W with the values given in column order (vals_t)."""
+    dt = _dtype(vals_t, dY, dX, dtype=dtype)
+    _check(_lib.snack_spmm_bwd_input_t(ctypes.byref(plan), _ptr(vals_t), dt, _ptr(dY), layout,
+                                       B, _ptr(dX), _stream(stream)), "snack_spmm_bwd_input_t")
+
+
 def snack_sddmm_grad_vals(plan, dY, X, layout, B, dvals, stream=None, dtype=None):
     dt = _dtype(dvals, dY, X, dtype=dtype)
     _check(_lib.snack_sddmm_grad_vals(ctypes.byref(plan), _ptr(dY), _ptr(X), dt, layout, B,
@@ -220,11 +245,12 @@ def snack_sddmm_grad_vals(plan, dY, X, layout, B, dvals, stream=None, dtype=None
 
 
 def snack_spmm_bwd_fused(plan, vals, X, dY, layout, B, dX, dvals=None, lr=0.0, stream=None,
-                         dtype=None):
-    """dX = dY W, dvals = (dY^T X) at the nonzeros, and vals -= lr * dV in place, in one pass."""
+                         dtype=None, vals_t=None):
+    """dX = dY W, dvals = (dY^T X) at the nonzeros, and vals -= lr * dV in place, in one pass
+    (vals_t: the values in column order, read instead of vals and updated with them)."""
     dt = _dtype(vals, X, dY, dX, dtype=dtype)
-    _check(_lib.snack_spmm_bwd_fused(ctypes.byref(plan), _ptr(vals), dt, _ptr(X), _ptr(dY),
-                                     layout, B, _ptr(dX), _ptr(dvals), float(lr),
+    _check(_lib.snack_spmm_bwd_fused(ctypes.byref(plan), _ptr(vals), _ptr(vals_t), dt, _ptr(X),
+                                     _ptr(dY), layout, B, _ptr(dX), _ptr(dvals), float(lr),
                                      _stream(stream)), "snack_spmm_bwd_fused")
 
 
@@ -232,35 +258,48 @@ def snack_drop_count(nnz: int, frac_ppm: int) -> int:
     return _lib.snack_drop_count(nnz, frac_ppm)
 
 
-def snack_prune_regrow_workspace(M: int, K: int, nnz: int, n_drop: int) -> int:
+def snack_prune_regrow_workspace(M: int, K: int, nnz: int, n_drop: int, flags: int = 0) -> int:
+    """Workspace bytes of a restructure (flags: PRUNE_SORT_PLAN forces the sort plan;
+    the plain entry point when flags == 0)."""
     out = ctypes.c_size_t(0)
-    _check(_lib.snack_prune_regrow_workspace(M, K, nnz, n_drop, ctypes.byref(out)),
-           "snack_prune_regrow_workspace")
+    if flags:
+        _check(_lib.snack_prune_regrow_workspace_ex(M, K, nnz, n_drop, flags, ctypes.byref(out)),
+               "snack_prune_regrow_workspace_ex")
+    else:
+        _check(_lib.snack_prune_regrow_workspace(M, K, nnz, n_drop, ctypes.byref(out)),
+               "snack_prune_regrow_workspace")
     return out.value
 
 
+def _nbytes(buf, given):
+    if given is not None:
+        return given
+    return buf.numel() * buf.element_size() if buf is not None and not isinstance(buf, int) else 0
+
+
 def snack_prune_regrow(row, col, vals, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
-                       ws, stream=None, ws_bytes=None, dtype=None):
+                       ws, stream=None, ws_bytes=None, dtype=None, flags: int = 0):
     dt = _dtype(vals, dtype=dtype)
-    if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size() if ws is not None and \
-            not isinstance(ws, int) else 0
-    _check(_lib.snack_prune_regrow(_ptr(row), _ptr(col), _ptr(vals), dt, M, K, nnz, n_drop,
-                                   seed & (2**64 - 1), step & (2**64 - 1), _ptr(dropped_lin),
-                                   _ptr(grown_lin), _ptr(ws), ws_bytes, _stream(stream)),
-           "snack_prune_regrow")
+    ws_bytes = _nbytes(ws, ws_bytes)
+    args = (_ptr(row), _ptr(col), _ptr(vals), dt, M, K, nnz, n_drop, seed & (2**64 - 1),
+            step & (2**64 - 1), _ptr(dropped_lin), _ptr(grown_lin), _ptr(ws), ws_bytes)
+    if flags:
+        _check(_lib.snack_prune_regrow_ex(*args, flags, _stream(stream)), "snack_prune_regrow_ex")
+    else:
+        _check(_lib.snack_prune_regrow(*args, _stream(stream)), "snack_prune_regrow")
 
 
 def snack_prune_regrow_prepared(plan, row, col, vals, n_drop, seed, step, dropped_lin, grown_lin,
-                                ws, stream=None, ws_bytes=None, dtype=None):
+                                ws, stream=None, ws_bytes=None, dtype=None, vals_t=None,
+                                flags: int = 0):
+    """Restructure and re-prepare in one call; vals_t (optional) receives the new
+    values in the new column order."""
     dt = _dtype(vals, dtype=dtype)
-    if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size() if ws is not None and \
-            not isinstance(ws, int) else 0
     _check(_lib.snack_prune_regrow_prepared(ctypes.byref(plan), _ptr(row), _ptr(col), _ptr(vals),
-                                            dt, n_drop, seed & (2**64 - 1), step & (2**64 - 1),
-                                            _ptr(dropped_lin), _ptr(grown_lin), _ptr(ws),
-                                            ws_bytes, _stream(stream)),
+                                            _ptr(vals_t), dt, n_drop, seed & (2**64 - 1),
+                                            step & (2**64 - 1), _ptr(dropped_lin),
+                                            _ptr(grown_lin), _ptr(ws), _nbytes(ws, ws_bytes),
+                                            flags, _stream(stream)),
            "snack_prune_regrow_prepared")
 
 

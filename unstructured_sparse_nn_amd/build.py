@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libsnack.so")
 SOURCES = ["wave_spmm_bf16.hip", "wave_spmm_f32.hip", "wave_fused.hip", "wave_sddmm_bf16.hip",
            "wave_sddmm_f32.hip", "spmm.hip", "prune_bitmap.hip", "api.hip", "prims.hip",
            "prepare.hip", "prune.hip", "aux.hip", "fixed.hip", "wave.hip"]
-ARCH = os.environ.get("SNACK_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"  # the MI355X (CDNA4); no other target is built
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -39,7 +39,7 @@ __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict_
 constexpr int SLOT_PRIV = 15;
 
 struct priv_layout {
-  size_t errs, rsplit, csplit, tmp, total;
+  size_t res, errs, rsplit, csplit, tmp, total;
 };
 
 priv_layout priv_of(const snack_plan* p) {
@@ -52,6 +52,7 @@ priv_layout priv_of(const snack_plan* p) {
     o = align_up(o + b, 256);
     return at;
   };
+  L.res = take(4 * RESULT_WORDS);
   L.errs = take(4 * (size_t)seg_bounds_blocks(p->nnz));
   L.rsplit = take(4 * (size_t)tiles_blocks(p->M));
   L.csplit = take(4 * (size_t)tiles_blocks(p->K));
@@ -109,6 +110,25 @@ void* act_of(const snack_plan* p) {
   return (char*)p->arena + p->off[S_ACT];
 }
 
+// The result words of a call on this plan: the caller's pinned host words
+// when the plan has them (their device address resolved once per buffer),
+// else the plan's private device words.
+snack_status plan_results(snack_plan* p, result_words& r) {
+  if (p->host_words) {
+    if (p->host_words_key != p->host_words || !p->host_words_dev) {
+      p->host_words_dev = host_words_device(p->host_words);
+      p->host_words_key = p->host_words_dev ? p->host_words : nullptr;
+      if (!p->host_words_dev) return SNACK_E_WORKSPACE;
+    }
+    r.host = p->host_words;
+    r.dev = p->host_words_dev;
+    return SNACK_OK;
+  }
+  r.host = nullptr;
+  r.dev = (int32_t*)((char*)p->arena + p->off[SLOT_PRIV] + priv_of(p).res);
+  return SNACK_OK;
+}
+
 snack_status check_product(const snack_plan* p, const void* a, const void* b, const void* c,
                            snack_dtype dt, snack_layout lay, int32_t B) {
   if (!p) return SNACK_E_NULL;
@@ -124,7 +144,7 @@ snack_status check_product(const snack_plan* p, const void* a, const void* b, co
 
 extern "C" {
 
-int32_t snack_version(void) { return 100; }
+int32_t snack_version(void) { return 200; }
 size_t snack_plan_sizeof(void) { return sizeof(snack_plan); }
 
 const char* snack_status_str(snack_status s) {
@@ -216,10 +236,9 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
   int32_t* perm = (int32_t*)(a + plan->off[SNACK_ARR_PERM]);
   int32_t* row_t = (int32_t*)(a + plan->off[SNACK_ARR_ROW_T]);
 
-  int32_t* res_host = host_result_buffer();
-  int32_t* res_dev = host_result_device(res_host);
-  if (!res_host || !res_dev) return SNACK_E_HIP;
-  res_host[0] = res_host[1] = res_host[2] = INT32_MIN;
+  result_words rw;
+  if (snack_status st = plan_results(plan, rw)) return st;
+  if (results_begin(rw, 3, s) != hipSuccess) return SNACK_E_HIP;
 
   // Every kernel below is safe on an invalid COO (all writes are clamped);
   // the error bits come back once at the end, with the split flags.
@@ -255,14 +274,15 @@ snack_status snack_coo_prepare(snack_plan* plan, const int32_t* row, const int32
                    (int32_t*)(a + plan->off[SNACK_ARR_CCUT]), csplit, s) != hipSuccess)
     return SNACK_E_HIP;
   if (launch_prepare_result(errs, seg_bounds_blocks(nnz), rsplit, tiles_blocks(plan->M), csplit,
-                            tiles_blocks(plan->K), res_dev, s) != hipSuccess ||
-      wait_results(res_host, res_dev, s) != hipSuccess)
+                            tiles_blocks(plan->K), rw.dev, s) != hipSuccess ||
+      results_wait(rw, 3, s) != hipSuccess)
     return SNACK_E_HIP;
-  if (res_host[0] == INT32_MIN) return SNACK_E_HIP;
-  if (res_host[0] & 1) return SNACK_E_COO_RANGE;
-  if (res_host[0] & 2) return SNACK_E_COO_ORDER;
-  plan->has_split_row = res_host[1] ? 1 : 0;
-  plan->has_split_col = res_host[2] ? 1 : 0;
+  const int32_t* res = rw.words();
+  if (res[0] == INT32_MIN) return SNACK_E_HIP;
+  if (res[0] & 1) return SNACK_E_COO_RANGE;
+  if (res[0] & 2) return SNACK_E_COO_ORDER;
+  plan->has_split_row = res[1] ? 1 : 0;
+  plan->has_split_col = res[2] ? 1 : 0;
   plan->prepared = 1;
   return SNACK_OK;
 }
@@ -366,6 +386,32 @@ snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snac
                          to_stream(stream));
 }
 
+snack_status snack_gather_vals_t(const snack_plan* plan, const void* vals, snack_dtype dtype,
+                                 void* vals_t, void* stream) {
+  if (!plan) return SNACK_E_NULL;
+  if (!plan->prepared || !plan->arena) return SNACK_E_NOT_PREPARED;
+  if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  if (plan->nnz == 0) return SNACK_OK;
+  if (!vals || !vals_t) return SNACK_E_NULL;
+  return launch_gather_vals_t(col_view(plan).perm, vals, dtype, vals_t, plan->nnz,
+                              to_stream(stream)) == hipSuccess
+             ? SNACK_OK
+             : SNACK_E_HIP;
+}
+
+snack_status snack_spmm_bwd_input_t(const snack_plan* plan, const void* vals_t,
+                                    snack_dtype dtype, const void* dY, snack_layout layout,
+                                    int32_t B, void* dX, void* stream) {
+  snack_status st =
+      check_product(plan, dY, dX, plan && plan->nnz ? vals_t : dX, dtype, layout, B);
+  if (st) return st;
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  seg_view v = col_view(plan);
+  v.perm = nullptr;  // the values arrive in column order
+  return launch_seg_spmm(v, vals_t, dtype, dY, layout, B, dX, carry, act_of(plan),
+                         to_stream(stream));
+}
+
 snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const void* X,
                                    snack_dtype dtype, snack_layout layout, int32_t B,
                                    void* dvals, void* stream) {
@@ -376,18 +422,19 @@ snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const
                       to_stream(stream));
 }
 
-snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, snack_dtype dtype,
-                                  const void* X, const void* dY, snack_layout layout, int32_t B,
-                                  void* dX, void* dvals, float lr, void* stream) {
+snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, void* vals_t,
+                                  snack_dtype dtype, const void* X, const void* dY,
+                                  snack_layout layout, int32_t B, void* dX, void* dvals,
+                                  float lr, void* stream) {
   snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
   if (st) return st;
   if (B > 0 && !X) return SNACK_E_NULL;
   if (B > 32) return SNACK_E_SHAPE;
   if (!(lr == lr) || lr - lr != 0.f) return SNACK_E_NAN;  // NaN or infinite step size
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
-  return launch_bwd_fused(col_view(plan), vals, dtype, X, dY, layout, B, dX,
-                          plan->nnz > 0 ? dvals : nullptr, lr, carry, act_of(plan),
-                          to_stream(stream));
+  return launch_bwd_fused(col_view(plan), vals, plan->nnz > 0 ? vals_t : nullptr, dtype, X, dY,
+                          layout, B, dX, plan->nnz > 0 ? dvals : nullptr, lr, carry,
+                          act_of(plan), to_stream(stream));
 }
 
 int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {
@@ -395,14 +442,20 @@ int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {
   return (int64_t)(((__int128)nnz * frac_ppm + 500000) / 1000000);
 }
 
-snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
-                                          size_t* bytes) {
+snack_status snack_prune_regrow_workspace_ex(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                             uint32_t flags, size_t* bytes) {
   if (!bytes) return SNACK_E_NULL;
+  if (flags & ~(uint32_t)SNACK_PRUNE_SORT_PLAN) return SNACK_E_LAYOUT;
   if (M < 1 || K < 1 || nnz < 0 || (double)nnz > (double)M * K || n_drop < 0)
     return SNACK_E_SHAPE;
   if (nnz >= (int64_t)INT32_MAX) return SNACK_E_OVERFLOW;
-  *bytes = prune_regrow_ws_bytes(M, K, nnz, n_drop);
+  *bytes = prune_regrow_ws_bytes(M, K, nnz, n_drop, flags);
   return SNACK_OK;
+}
+
+snack_status snack_prune_regrow_workspace(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                          size_t* bytes) {
+  return snack_prune_regrow_workspace_ex(M, K, nnz, n_drop, 0, bytes);
 }
 
 snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz, int32_t max_batch,
@@ -425,10 +478,12 @@ snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz, int32_t m
   snack_footprint f;
   f.coo = (uint64_t)nnz * (8 + s);
   f.value_grad = (uint64_t)nnz * s;
+  f.col_values = (uint64_t)nnz * s;
   f.derived = plan.off[S_CARRY];  // the derived arrays come first in the arena
   f.plan_scratch = plan.arena_bytes - f.derived;
   f.restructure_ws = ws;
-  f.sparse_total = f.coo + f.value_grad + f.derived + f.plan_scratch + f.restructure_ws;
+  f.sparse_total =
+      f.coo + f.value_grad + f.col_values + f.derived + f.plan_scratch + f.restructure_ws;
   f.dense_weight = mk * s;
   f.dense_grad = mk * s;
   f.dense_total = f.dense_weight + f.dense_grad;
@@ -439,11 +494,13 @@ snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz, int32_t m
   return SNACK_OK;
 }
 
-snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
-                                int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
-                                uint64_t seed, uint64_t step, int64_t* dropped_lin,
-                                int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream) {
+snack_status snack_prune_regrow_ex(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
+                                   int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                   uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                   int64_t* grown_lin, void* ws, size_t ws_bytes, uint32_t flags,
+                                   void* stream) {
   if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  if (flags & ~(uint32_t)SNACK_PRUNE_SORT_PLAN) return SNACK_E_LAYOUT;
   if (M < 1 || K < 1 || nnz < 0 || (double)nnz > (double)M * K || n_drop < 0)
     return SNACK_E_SHAPE;
   if (nnz >= (int64_t)INT32_MAX) return SNACK_E_OVERFLOW;
@@ -451,35 +508,56 @@ snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dt
   if (n_drop == 0) return SNACK_OK;
   if (!row || !col || !vals || !ws) return SNACK_E_NULL;
   return prune_regrow(row, col, vals, dtype, M, K, nnz, n_drop, seed, step, dropped_lin,
-                      grown_lin, ws, ws_bytes, to_stream(stream));
+                      grown_lin, ws, ws_bytes, flags, to_stream(stream));
+}
+
+snack_status snack_prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dtype,
+                                int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                                uint64_t seed, uint64_t step, int64_t* dropped_lin,
+                                int64_t* grown_lin, void* ws, size_t ws_bytes, void* stream) {
+  return snack_prune_regrow_ex(row, col, vals, dtype, M, K, nnz, n_drop, seed, step,
+                               dropped_lin, grown_lin, ws, ws_bytes, 0, stream);
 }
 
 snack_status snack_prune_regrow_prepared(snack_plan* plan, int32_t* row, int32_t* col,
-                                         void* vals, snack_dtype dtype, int64_t n_drop,
-                                         uint64_t seed, uint64_t step, int64_t* dropped_lin,
-                                         int64_t* grown_lin, void* ws, size_t ws_bytes,
-                                         void* stream) {
+                                         void* vals, void* vals_t, snack_dtype dtype,
+                                         int64_t n_drop, uint64_t seed, uint64_t step,
+                                         int64_t* dropped_lin, int64_t* grown_lin, void* ws,
+                                         size_t ws_bytes, uint32_t flags, void* stream) {
   if (!plan) return SNACK_E_NULL;
   if (!plan->arena || plan->arena_bytes == 0) return SNACK_E_NOT_PREPARED;
   if (dtype != SNACK_F32 && dtype != SNACK_BF16) return SNACK_E_DTYPE;
+  if (flags & ~(uint32_t)SNACK_PRUNE_SORT_PLAN) return SNACK_E_LAYOUT;
   const int32_t M = plan->M, K = plan->K;
   const int64_t nnz = plan->nnz;
   if (n_drop < 0) return SNACK_E_SHAPE;
   if (n_drop > nnz || n_drop > (int64_t)M * K - nnz) return SNACK_E_COUNT;
   if (nnz > 0 && (!row || !col || !vals)) return SNACK_E_NULL;
   hipStream_t s = to_stream(stream);
+  // the values in the new column order, after a restructure that did not
+  // write them itself
+  auto finish_vals_t = [&](snack_status st) {
+    if (st != SNACK_OK || !vals_t || nnz == 0) return st;
+    return launch_gather_vals_t(col_view(plan).perm, vals, dtype, vals_t, nnz, s) == hipSuccess
+               ? SNACK_OK
+               : SNACK_E_HIP;
+  };
   if (n_drop == 0)
-    return snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream);
+    return finish_vals_t(
+        snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream));
   if (!ws) return SNACK_E_NULL;
-  if (ws_bytes < prune_regrow_ws_bytes(M, K, nnz, n_drop)) return SNACK_E_WORKSPACE;
-  if (use_bitmap_plan(M, K, nnz) && prune_bitmap_fused_ok(M, K, nnz))
-    return prune_bitmap_prepared(plan, row, col, vals, dtype, n_drop, seed, step, dropped_lin,
-                                 grown_lin, ws, s);
+  if (ws_bytes < prune_regrow_ws_bytes(M, K, nnz, n_drop, flags)) return SNACK_E_WORKSPACE;
+  if (use_bitmap_plan(M, K, nnz, flags) && prune_bitmap_fused_ok(M, K, nnz)) {
+    result_words rw;
+    if (snack_status st = plan_results(plan, rw)) return st;
+    return prune_bitmap_prepared(plan, row, col, vals, vals_t, dtype, n_drop, seed, step,
+                                 dropped_lin, grown_lin, ws, rw, s);
+  }
   plan->prepared = 0;
   const snack_status st = prune_regrow(row, col, vals, dtype, M, K, nnz, n_drop, seed, step,
-                                       dropped_lin, grown_lin, ws, ws_bytes, s);
+                                       dropped_lin, grown_lin, ws, ws_bytes, flags, s);
   if (st != SNACK_OK) return st;
-  return snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream);
+  return finish_vals_t(snack_coo_prepare(plan, row, col, plan->arena, plan->arena_bytes, stream));
 }
 
 snack_status snack_gelu_fwd(const float* z, float* h, int64_t n, void* stream) {

@@ -155,10 +155,8 @@ std::string generate(const int32_t* row, const int32_t* col, const void* vals, s
   return s;
 }
 
-const char* offload_arch() {
-  const char* e = std::getenv("SNACK_OFFLOAD_ARCH");
-  return e ? e : "gfx950";
-}
+// The generated kernels target the MI355X only.
+const char* offload_arch() { return "gfx950"; }
 
 }  // namespace
 

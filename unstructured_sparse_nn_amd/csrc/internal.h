@@ -32,17 +32,28 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint6
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// A small pinned, device-mapped host buffer per calling thread (256 bytes,
-// kept until the process ends): kernels write a call's few result words
-// straight into it, so a readback costs no copy.  NULL on failure.
-int32_t* host_result_buffer();
-int32_t* host_result_device(int32_t* host);
-// Waits until every kernel queued on s so far has finished and its result
-// words are visible in `host`: a one-thread kernel stores a per-call token
-// into host[RESULT_DONE_SLOT] and the host spins on it (falling back to
-// hipStreamSynchronize after 20 ms, or with SNACK_BLOCKING_SYNC set).
+// Result words of a call that reads a few words back (prepare, the
+// restructure).  Kernels store them at `dev`.  With caller-owned pinned,
+// device-mapped host memory (snack_plan.host_words) `dev` maps to `host` and
+// the host spins on a completion word that a last one-thread kernel stores;
+// otherwise `dev` is device scratch and the words come back by one copy and a
+// stream sync into `local`.  Nothing here allocates.
+constexpr int RESULT_WORDS = 16;
 constexpr int RESULT_DONE_SLOT = 15;
-hipError_t wait_results(int32_t* host, int32_t* dev, hipStream_t s);
+struct result_words {
+  int32_t* dev = nullptr;    // device address the kernels store to
+  int32_t* host = nullptr;   // caller's pinned words, or NULL
+  int32_t local[RESULT_WORDS] = {};
+  const int32_t* words() const { return host ? host : local; }
+};
+// Marks words [0, n) as not written (INT32_MIN) before the kernels run.
+hipError_t results_begin(result_words& r, int n, hipStream_t s);
+// Waits for every kernel queued on s so far; afterwards words() holds the
+// values they stored.  Pinned words: spins on a completion token (falling
+// back to hipStreamSynchronize after 20 ms).
+hipError_t results_wait(result_words& r, int n, hipStream_t s);
+// Device address of caller-owned pinned host memory (NULL if it is not).
+int32_t* host_words_device(int32_t* host);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- products (spmm.hip) ----------------------------------------------------
@@ -73,9 +84,15 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
                           snack_layout lay, int32_t B, void* dV, void* act_tmp, hipStream_t s);
 // Column view, B <= 32: dX = dY W, dV (nullable) and, if lr != 0, the
 // in-place update vals <- vals - lr * dV, in one pass.
-snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* X,
-                              const void* dY, snack_layout lay, int32_t B, void* dX, void* dV,
-                              float lr, float* carry, void* act_tmp, hipStream_t s);
+// vals_t (nullable): the values in column order, read coalesced instead of
+// through perm, and updated with them when lr != 0.
+snack_status launch_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
+                              const void* X, const void* dY, snack_layout lay, int32_t B,
+                              void* dX, void* dV, float lr, float* carry, void* act_tmp,
+                              hipStream_t s);
+// vals_t[i] = vals[perm[i]] for i < nnz.
+hipError_t launch_gather_vals_t(const int32_t* perm, const void* vals, snack_dtype dt,
+                                void* vals_t, int64_t nnz, hipStream_t s);
 // Wave-per-segment products (wave.hip), for views with no split segment.
 // Activations already node-major; launch_wave_sddmm returns false (and
 // launches nothing) when one pass of the kernel cannot cover the batch.
@@ -92,9 +109,9 @@ void launch_fixup(const seg_view& v, snack_dtype dt, bool node_out, int32_t act,
 bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
                        int32_t B, void* dV, hipStream_t s);
 // Column view: dX, dV (nullable) and the optional update (wave_fused.hip).
-bool launch_wave_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* dYt,
-                           const void* Xt, int32_t B, void* dX, void* dV, float lr,
-                           bool node_out, hipStream_t s);
+bool launch_wave_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
+                           const void* dYt, const void* Xt, int32_t B, void* dX, void* dV,
+                           float lr, bool node_out, hipStream_t s);
 hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
                              const void* in1, void* out1, int32_t R1, int32_t C1,
                              hipStream_t s);
@@ -125,10 +142,11 @@ hipError_t launch_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dt, 
                             int32_t K, const void* X, int32_t B, void* Y, hipStream_t s);
 
 // ---- prune / regrow (prune.hip) ---------------------------------------------------
-size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop);
+size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                             uint32_t flags);
 snack_status prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
                           int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
                           int64_t* dropped_lin, int64_t* grown_lin, void* ws, size_t ws_bytes,
-                          hipStream_t s);
+                          uint32_t flags, hipStream_t s);
 
 }  // namespace snk

@@ -370,32 +370,42 @@ hipError_t radix_sort_u64(const uint64_t* keys_in, const int32_t* vals_in, uint6
 }
 
 // ============================================================== host results
-int32_t* host_result_buffer() {
-  thread_local int32_t* buf = nullptr;
-  if (!buf) {
-    void* p = nullptr;
-    if (hipHostMalloc(&p, 256, hipHostMallocMapped | hipHostMallocPortable) == hipSuccess)
-      buf = (int32_t*)p;
-  }
-  return buf;
+__global__ void k_fill_words(int32_t* __restrict__ w, int32_t n, int32_t v) {
+  if ((int32_t)threadIdx.x < n) w[threadIdx.x] = v;
 }
 
 // Completion word of a call: one thread stores the call's token into the
-// pinned result buffer after every earlier kernel of the stream has finished
+// pinned result words after every earlier kernel of the stream has finished
 // (stream order); the host spins on it instead of a blocking stream sync.
 __global__ void k_signal(int32_t* __restrict__ flag, int32_t token) {
   __threadfence_system();
   *(volatile int32_t*)flag = token;
 }
 
-hipError_t wait_results(int32_t* host, int32_t* dev, hipStream_t s) {
-  static const bool blocking = getenv("SNACK_BLOCKING_SYNC") != nullptr;
-  if (blocking) return hipStreamSynchronize(s);
-  thread_local int32_t token = 0;
-  token = token == INT32_MAX ? 1 : token + 1;
-  volatile int32_t* flag = host + RESULT_DONE_SLOT;
-  *flag = 0;
-  hipLaunchKernelGGL(k_signal, dim3(1), dim3(1), 0, s, dev + RESULT_DONE_SLOT, token);
+hipError_t results_begin(result_words& r, int n, hipStream_t s) {
+  if (r.host) {
+    for (int i = 0; i < n; ++i) r.host[i] = INT32_MIN;
+    return hipSuccess;
+  }
+  for (int i = 0; i < n; ++i) r.local[i] = INT32_MIN;
+  hipLaunchKernelGGL(k_fill_words, dim3(1), dim3(64), 0, s, r.dev, (int32_t)n, INT32_MIN);
+  return hipGetLastError();
+}
+
+hipError_t results_wait(result_words& r, int n, hipStream_t s) {
+  if (!r.host) {
+    if (hipMemcpyAsync(r.local, r.dev, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+      return hipErrorUnknown;
+    return hipStreamSynchronize(s);
+  }
+  // the token follows the one the previous call left in these words (that
+  // call has finished: every call waits for its own token), so no state is
+  // kept between calls
+  volatile int32_t* flag = r.host + RESULT_DONE_SLOT;
+  int32_t token = *flag + 1;
+  if (token <= 0) token = 1;
+  hipLaunchKernelGGL(k_signal, dim3(1), dim3(1), 0, s, r.dev + RESULT_DONE_SLOT, token);
   if (hipGetLastError() != hipSuccess) return hipStreamSynchronize(s);
   // spin for up to 20 ms (a restructure takes ~0.1 ms), then block: a fault
   // or a slow call still ends in the stream sync and its error
@@ -408,17 +418,14 @@ hipError_t wait_results(int32_t* host, int32_t* dev, hipStream_t s) {
   return hipSuccess;
 }
 
-int32_t* host_result_device(int32_t* host) {
-  thread_local int32_t* h = nullptr;
-  thread_local int32_t* d = nullptr;
+int32_t* host_words_device(int32_t* host) {
   if (!host) return nullptr;
-  if (host != h) {
-    void* p = nullptr;
-    if (hipHostGetDevicePointer(&p, host, 0) != hipSuccess) return nullptr;
-    h = host;
-    d = (int32_t*)p;
+  void* p = nullptr;
+  if (hipHostGetDevicePointer(&p, host, 0) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of a failed lookup
+    return nullptr;
   }
-  return d;
+  return (int32_t*)p;
 }
 
 }  // namespace snk

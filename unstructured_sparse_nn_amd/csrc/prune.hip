@@ -424,17 +424,17 @@ static pr_layout make_layout(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) 
   return L;
 }
 
-// SNACK_PRUNE_PATH=sort forces the sort plan (tests run both plans on the
+// SNACK_PRUNE_SORT_PLAN forces the sort plan (tests run both plans on the
 // same inputs).
-bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz) {
-  const char* e = getenv("SNACK_PRUNE_PATH");
-  if (e && e[0] == 's') return false;
+bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz, uint32_t flags) {
+  if (flags & SNACK_PRUNE_SORT_PLAN) return false;
   return prune_bitmap_ok(M, K, nnz);
 }
 
 // The workspace of the plan that will run (the same choice as the calls).
-size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop) {
-  if (use_bitmap_plan(M, K, nnz)) return prune_bitmap_ws_bytes(M, K, nnz);
+size_t prune_regrow_ws_bytes(int32_t M, int32_t K, int64_t nnz, int64_t n_drop,
+                             uint32_t flags) {
+  if (use_bitmap_plan(M, K, nnz, flags)) return prune_bitmap_ws_bytes(M, K, nnz);
   return make_layout(M, K, nnz, n_drop).total;
 }
 
@@ -528,9 +528,9 @@ static snack_status run_sort(int32_t* row, int32_t* col, T* vals, int32_t M, int
 snack_status prune_regrow(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
                           int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
                           int64_t* dropped_lin, int64_t* grown_lin, void* ws, size_t ws_bytes,
-                          hipStream_t s) {
-  if (ws_bytes < prune_regrow_ws_bytes(M, K, nnz, n_drop)) return SNACK_E_WORKSPACE;
-  if (use_bitmap_plan(M, K, nnz))
+                          uint32_t flags, hipStream_t s) {
+  if (ws_bytes < prune_regrow_ws_bytes(M, K, nnz, n_drop, flags)) return SNACK_E_WORKSPACE;
+  if (use_bitmap_plan(M, K, nnz, flags))
     return prune_bitmap(row, col, vals, dt, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
                         ws, s);
   if (dt == SNACK_F32)

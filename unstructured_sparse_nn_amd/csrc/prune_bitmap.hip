@@ -22,8 +22,9 @@
 //            on the select kernels; one workgroup finishes the tail;
 //   write    new COO = the set bits of (S & ~D) | G in position order, a
 //            survivor's value being the old value at its rank in S.
-// One readback: the last kernel writes (error, positions missing) straight
-// into pinned host memory; row/col/vals are written only on success.
+// One readback: the last kernel writes (error, positions missing) into the
+// call's result words (the caller's pinned host words, or device words
+// copied back); row/col/vals are written only on success.
 #include <cmath>
 #include <cstdlib>
 
@@ -873,11 +874,12 @@ __global__ __launch_bounds__(WT) void k_fp_tsum(const bm_state* st,
 // four FP loads in flight together.  With cols_here (WM divides WT, so a
 // block holds whole columns) the block also writes the column tiles of its
 // columns and sets res[3] if one of them is split.
+template <typename T>
 __global__ __launch_bounds__(WT) void k_fp_temit(
     const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int64_t nbt, int32_t M,
     int32_t K, const int4* __restrict__ tsum, const int4* __restrict__ toff,
     const uint2* __restrict__ FP, int64_t nnz, fuse_ptrs f, int32_t cols_here,
-    int32_t* __restrict__ res) {
+    int32_t* __restrict__ res, const T* __restrict__ vals, T* __restrict__ vals_t) {
   __shared__ int32_t lds[WT / SNK_WAVE];
   __shared__ int32_t red[WT / SNK_WAVE];
   __shared__ int32_t cstart[WT];
@@ -938,12 +940,24 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       fp[u] = j[u] >= 0 ? FP[(rw * 32 + j[u]) * KW + (c >> 5)] : make_uint2(0u, 0u);
+    int32_t pos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+    // the value of each entry in column order: one gather of the new values,
+    // the four of this batch in flight together
+    T v[4];
+    if (vals_t) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = (j[u] >= 0 && q + u < nnz) ? vals[pos[u]] : (T)0;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (j[u] < 0) break;
       if (q < nnz) {
         f.row_t[q] = (int32_t)(rw * 32 + j[u]);
-        f.perm[q] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+        f.perm[q] = pos[u];
+        if (vals_t) vals_t[q] = v[u];
       }
       ++q;
     }
@@ -968,7 +982,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int3
 // ------------------------------------------------------------------ host
 struct bm_layout {
   int64_t nblk, W, nb, NT, nbt, rb, cbk;
-  size_t state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
+  size_t res, state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
   size_t fp, ft, tsum, toff, total;  // fused prepare
 };
 
@@ -983,6 +997,7 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
     o = align_up(o + bytes, 256);
     return at;
   };
+  L.res = take(4 * RESULT_WORDS);  // result words when no pinned host words are given
   L.state = take(sizeof(bm_state));
   L.cnt_eq = take(4 * (size_t)L.nblk);
   L.base_eq = take(4 * (size_t)L.nblk);
@@ -1029,8 +1044,8 @@ int32_t grid_chunks(int64_t MK, int64_t nnz, int64_t n_drop, int32_t riding) {
 template <typename T>
 snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int64_t nnz,
                  int64_t n_drop, uint64_t seed, uint64_t step, int64_t* dropped_lin,
-                 int64_t* grown_lin, char* ws, hipStream_t s, const fuse_ptrs* fuse,
-                 int32_t* splits) {
+                 int64_t* grown_lin, char* ws, result_words& rw, hipStream_t s,
+                 const fuse_ptrs* fuse, int32_t* splits, T* vals_t) {
   const bm_layout L = make_layout(M, K, nnz);
   bm_state* st = (bm_state*)(ws + L.state);
   int32_t* cnt_eq = (int32_t*)(ws + L.cnt_eq);
@@ -1046,10 +1061,9 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   const int32_t nd = (int32_t)n_drop;
   const dim3 eb((unsigned)L.nblk), et(BT);
 
-  int32_t* res_host = host_result_buffer();
-  int32_t* res_dev = host_result_device(res_host);
-  if (!res_host || !res_dev) return SNACK_E_HIP;
-  res_host[0] = res_host[1] = res_host[2] = res_host[3] = INT32_MIN;
+  if (!rw.dev) rw.dev = (int32_t*)(ws + L.res);
+  int32_t* res_dev = rw.dev;
+  if (results_begin(rw, 4, s) != hipSuccess) return SNACK_E_HIP;
   uint2* FP = fuse ? (uint2*)(ws + L.fp) : nullptr;
 
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(4 * HREPL * 256, 256)), dim3(256), 0, s, st);
@@ -1112,15 +1126,16 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     const bool own_t = L.nbt <= PREFIX_INBLOCK_MAX;
     if (!own_t) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, tsum, toff, L.nbt);
     const int32_t cols_here = (WT % (M / 32)) == 0 ? 1 : 0;
-    hipLaunchKernelGGL(k_fp_temit, dim3((unsigned)(NUM_XCD * cdiv(L.nbt, NUM_XCD))), dim3(WT),
-                       0, s, st, FT, L.NT, L.nbt, M, K, tsum, own_t ? nullptr : toff, FP, nnz,
-                       *fuse, cols_here, res_dev);
+    hipLaunchKernelGGL(k_fp_temit<T>, dim3((unsigned)(NUM_XCD * cdiv(L.nbt, NUM_XCD))),
+                       dim3(WT), 0, s, st, FT, L.NT, L.nbt, M, K, tsum, own_t ? nullptr : toff,
+                       FP, nnz, *fuse, cols_here, res_dev, (const T*)vals, vals_t);
     if (!cols_here)
       hipLaunchKernelGGL(k_fp_cols, dim3((unsigned)L.cbk), dim3(FP_THREADS), 0, s, st, K, nnz,
                          *fuse, res_dev);
   }
-  if (hipGetLastError() != hipSuccess || wait_results(res_host, res_dev, s) != hipSuccess)
+  if (hipGetLastError() != hipSuccess || results_wait(rw, 4, s) != hipSuccess)
     return SNACK_E_HIP;
+  const int32_t* res_host = rw.words();
   const int32_t err = res_host[0], missing = res_host[1];
   if (err == INT32_MIN) return SNACK_E_HIP;
   if (err & 1) return SNACK_E_NAN;
@@ -1151,11 +1166,12 @@ size_t prune_bitmap_ws_bytes(int32_t M, int32_t K, int64_t nnz) {
 snack_status prune_bitmap(int32_t* row, int32_t* col, void* vals, snack_dtype dt, int32_t M,
                           int32_t K, int64_t nnz, int64_t n_drop, uint64_t seed, uint64_t step,
                           int64_t* dropped_lin, int64_t* grown_lin, void* ws, hipStream_t s) {
+  result_words rw;  // device words in the workspace, read back by a copy
   if (dt == SNACK_F32)
     return run<float>(row, col, (float*)vals, M, K, nnz, n_drop, seed, step, dropped_lin,
-                      grown_lin, (char*)ws, s, nullptr, nullptr);
+                      grown_lin, (char*)ws, rw, s, nullptr, nullptr, nullptr);
   return run<bf16>(row, col, (bf16*)vals, M, K, nnz, n_drop, seed, step, dropped_lin, grown_lin,
-                   (char*)ws, s, nullptr, nullptr);
+                   (char*)ws, rw, s, nullptr, nullptr, nullptr);
 }
 
 bool prune_bitmap_fused_ok(int32_t M, int32_t K, int64_t nnz) {
@@ -1163,9 +1179,9 @@ bool prune_bitmap_fused_ok(int32_t M, int32_t K, int64_t nnz) {
 }
 
 snack_status prune_bitmap_prepared(snack_plan* plan, int32_t* row, int32_t* col, void* vals,
-                                   snack_dtype dt, int64_t n_drop, uint64_t seed, uint64_t step,
-                                   int64_t* dropped_lin, int64_t* grown_lin, void* ws,
-                                   hipStream_t s) {
+                                   void* vals_t, snack_dtype dt, int64_t n_drop, uint64_t seed,
+                                   uint64_t step, int64_t* dropped_lin, int64_t* grown_lin,
+                                   void* ws, result_words& rw, hipStream_t s) {
   char* a = (char*)plan->arena;
   auto arr = [&](int which) { return (int32_t*)(a + plan->off[which]); };
   fuse_ptrs f{arr(SNACK_ARR_ROW_PTR), arr(SNACK_ARR_RPART_SEG), arr(SNACK_ARR_RPART_NZ),
@@ -1177,9 +1193,9 @@ snack_status prune_bitmap_prepared(snack_plan* plan, int32_t* row, int32_t* col,
   const snack_status st =
       dt == SNACK_F32
           ? run<float>(row, col, (float*)vals, plan->M, plan->K, plan->nnz, n_drop, seed, step,
-                       dropped_lin, grown_lin, (char*)ws, s, &f, splits)
+                       dropped_lin, grown_lin, (char*)ws, rw, s, &f, splits, (float*)vals_t)
           : run<bf16>(row, col, (bf16*)vals, plan->M, plan->K, plan->nnz, n_drop, seed, step,
-                      dropped_lin, grown_lin, (char*)ws, s, &f, splits);
+                      dropped_lin, grown_lin, (char*)ws, rw, s, &f, splits, (bf16*)vals_t);
   if (st != SNACK_OK) return st;
   plan->row = row;
   plan->col = col;

@@ -42,8 +42,8 @@ __device__ __forceinline__ bool is_nan_mag(uint32_t a) {
 }
 
 // ---- plan choice (prune.hip) ----------------------------------------------------
-// The bitmap plan when it applies, unless SNACK_PRUNE_PATH=sort.
-bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz);
+// The bitmap plan when it applies, unless flags has SNACK_PRUNE_SORT_PLAN.
+bool use_bitmap_plan(int32_t M, int32_t K, int64_t nnz, uint32_t flags);
 
 // ---- bitmap plan (prune_bitmap.hip) -------------------------------------------
 bool prune_bitmap_ok(int32_t M, int32_t K, int64_t nnz);
@@ -55,9 +55,12 @@ snack_status prune_bitmap(int32_t* row, int32_t* col, void* vals, snack_dtype dt
 // support bitmap (needs M, K multiples of 32).  plan: initialised for
 // (M, K, nnz) with its arena; it describes the new COO on success.
 bool prune_bitmap_fused_ok(int32_t M, int32_t K, int64_t nnz);
+// vals_t (nullable) receives the new values in the new column order; rw:
+// the plan's result words (internal.h).
+struct result_words;
 snack_status prune_bitmap_prepared(snack_plan* plan, int32_t* row, int32_t* col, void* vals,
-                                   snack_dtype dt, int64_t n_drop, uint64_t seed, uint64_t step,
-                                   int64_t* dropped_lin, int64_t* grown_lin, void* ws,
-                                   hipStream_t s);
+                                   void* vals_t, snack_dtype dt, int64_t n_drop, uint64_t seed,
+                                   uint64_t step, int64_t* dropped_lin, int64_t* grown_lin,
+                                   void* ws, result_words& rw, hipStream_t s);
 
 }  // namespace snk

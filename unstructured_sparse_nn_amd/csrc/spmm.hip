@@ -645,22 +645,14 @@ struct lane_shape {
 // (8-byte gathers): with 8 the product kernel needs ~114 VGPRs and runs at
 // 4 waves per SIMD, which costs more at batch 32 on gfx950 than the wider
 // loads gain.  The bf16 value gradient takes 8 (16-byte gathers), consumed
-// pairwise by v_dot2_f32_bf16.  SNACK_BF16_CHMAX (1, 2, 4 or 8) overrides the
-// product width for experiments.
-static int bf16_chmax_products() {
-  static int v = [] {
-    const char* e = getenv("SNACK_BF16_CHMAX");
-    int c = e ? atoi(e) : 4;
-    return (c == 1 || c == 2 || c == 4 || c == 8) ? c : 4;
-  }();
-  return v;
-}
+// pairwise by v_dot2_f32_bf16.
+constexpr int BF16_CHMAX_PRODUCTS = 4;
 
 // Lanes per item group and workgroup size: enough groups that a run of the
 // tile's < 2T merge-path items holds at most MP_RC entries, so each group
 // gathers its whole run in one round (capped at MP_MAX_THREADS threads).
 static lane_shape pick_shape(snack_dtype dt, int32_t B, int32_t tile_items, bool sddmm = false) {
-  const int chmax = dt == SNACK_BF16 ? (sddmm ? 8 : bf16_chmax_products()) : 4;
+  const int chmax = dt == SNACK_BF16 ? (sddmm ? 8 : BF16_CHMAX_PRODUCTS) : 4;
   int ch = 1;
   while (ch < chmax && B % (ch * 2) == 0) ch *= 2;
   int want = (int)std::min<int64_t>(cdiv(B, ch), MP_MAX_BW / ch);
@@ -704,8 +696,7 @@ hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_
 // ranges, a line of the value array (consecutive entries of a row, spread
 // over neighbouring columns) is fetched by few XCDs instead of all of them.
 static int32_t xcd_tiles_for(const seg_view& v) {
-  static const bool off = getenv("SNACK_NO_XCD_REMAP") != nullptr;
-  if (off || !v.perm || v.P < 8 * NUM_XCD) return 0;
+  if (!v.perm || v.P < 8 * NUM_XCD) return 0;
   return (int32_t)cdiv(v.P, NUM_XCD);
 }
 
@@ -858,9 +849,43 @@ static void launch_fused_dt(const seg_view& v, void* vals, const void* dYt, cons
   }
 }
 
-snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* X,
-                              const void* dY, snack_layout lay, int32_t B, void* dX, void* dV,
-                              float lr, float* carry, void* act_tmp, hipStream_t s) {
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_vals_t(const int32_t* __restrict__ perm,
+                                                       const T* __restrict__ vals,
+                                                       T* __restrict__ vals_t, int64_t nnz) {
+  // four entries per thread, their perm and value loads in flight together
+  const int64_t i0 = ((int64_t)blockIdx.x * 256) * 4 + threadIdx.x;
+  int32_t p[4];
+  T v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + u * 256;
+    p[u] = i < nnz ? perm[i] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = i0 + u * 256 < nnz ? vals[p[u]] : (T)0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (i0 + u * 256 < nnz) vals_t[i0 + u * 256] = v[u];
+}
+
+hipError_t launch_gather_vals_t(const int32_t* perm, const void* vals, snack_dtype dt,
+                                void* vals_t, int64_t nnz, hipStream_t s) {
+  if (nnz <= 0) return hipSuccess;
+  const dim3 g((unsigned)cdiv(nnz, 1024));
+  if (dt == SNACK_F32)
+    hipLaunchKernelGGL(k_gather_vals_t<float>, g, dim3(256), 0, s, perm, (const float*)vals,
+                       (float*)vals_t, nnz);
+  else
+    hipLaunchKernelGGL(k_gather_vals_t<bf16>, g, dim3(256), 0, s, perm, (const bf16*)vals,
+                       (bf16*)vals_t, nnz);
+  return hipGetLastError();
+}
+
+snack_status launch_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
+                              const void* X, const void* dY, snack_layout lay, int32_t B,
+                              void* dX, void* dV, float lr, float* carry, void* act_tmp,
+                              hipStream_t s) {
   if (B == 0) {  // empty batch: dV = 0, the update is a no-op, dX has no elements
     if (dV && v.nnz > 0) {
       dim3 g((unsigned)cdiv(v.nnz, 256));
@@ -886,12 +911,17 @@ snack_status launch_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, con
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
   if (wave_eligible(v, dt, B, false) &&
-      launch_wave_bwd_fused(v, vals, dt, dYt, Xt, B, dX, dV, lr, node_out, s))
+      launch_wave_bwd_fused(v, vals, vals_t, dt, dYt, Xt, B, dX, dV, lr, node_out, s))
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+  // the merge-path form reads the values through perm; an update is then
+  // carried into the column-ordered copy by one gather
   if (dt == SNACK_F32)
     launch_fused_dt<float>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
   else
     launch_fused_dt<bf16>(v, vals, dYt, Xt, node_out, B, dX, dV, lr, carry, sh, s);
+  if (vals_t && lr != 0.f && launch_gather_vals_t(v.perm, vals, dt, vals_t, v.nnz, s) !=
+                                 hipSuccess)
+    return SNACK_E_HIP;
   return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
 }
 

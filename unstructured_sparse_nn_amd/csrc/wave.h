@@ -3,7 +3,6 @@
 // groups and the butterfly reduce-scatter.
 #pragma once
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -239,12 +238,6 @@ __device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec
 #pragma unroll
   for (int i = 0; i < NR; ++i) part[i] = dot_acc<T, CH>(g, xv[i], 0.f);
   reduce_permute<LPE, NR>(part, lane, out);
-}
-
-// SNACK_NO_XCD_REMAP set: plain block order (for experiments).
-inline bool no_xcd_remap() {
-  static const bool off = getenv("SNACK_NO_XCD_REMAP") != nullptr;
-  return off;
 }
 
 struct wave_shape {

@@ -1,8 +1,6 @@
 // wave.hip -- which products take the wave-per-segment kernels, and the
 // dispatch to their per-element-type instances (the kernels themselves are
 // in wave_kernels.h).
-#include <cstdlib>
-
 #include "common.h"
 #include "internal.h"
 #include "wave.h"
@@ -22,12 +20,9 @@ bool wave_sddmm_bf16(const seg_view&, const void*, const void*, int32_t, void*, 
 // Up to 16 lanes per entry (odd batches above 16 columns take the
 // merge-path kernels, whose lane groups suit them better).  Views with split
 // segments qualify when the caller handles their tile pieces (split).
-// SNACK_NO_WAVE / SNACK_NO_WAVE_SPLIT switch the path off (experiments).
 bool wave_eligible(const seg_view& v, snack_dtype dt, int32_t B, bool split) {
-  static const bool off = getenv("SNACK_NO_WAVE") != nullptr;
-  static const bool off_split = getenv("SNACK_NO_WAVE_SPLIT") != nullptr;
-  if (off || wave_pick(dt, B).lpe > 16) return false;
-  return !v.has_split || (split && !off_split);
+  if (wave_pick(dt, B).lpe > 16) return false;
+  return !v.has_split || split;
 }
 
 void launch_wave_spmm(const seg_view& v, const void* vals, snack_dtype dt, const void* Xt,

@@ -13,19 +13,22 @@
 // column's X chunk (loaded once per wave) for dV.  dV and the updated value
 // are written through perm by the lane that loaded the entry.  Each value is
 // read and written by that one lane only, so the in-place update races with
-// nothing.
+// nothing.  With the values also kept in column order (vals_t, VT), they are
+// read from there coalesced instead of through perm, and the update writes
+// both copies.
 #include "common.h"
 #include "internal.h"
 #include "wave.h"
 
 namespace snk {
 
-template <typename T, int CH, int LPE, int NR>
+template <typename T, int CH, int LPE, int NR, bool VT>
 __device__ __forceinline__ void fused_rounds(const T* __restrict__ gb, int32_t B,
                                              const vec<T, CH>& xs, const int32_t* ci,
                                              const float* cv, const int32_t* pk, int32_t rb,
                                              int32_t e, int lane, int slot, float (&acc)[CH],
-                                             T* __restrict__ dV, T* vals_upd, float lr) {
+                                             T* __restrict__ dV, T* vals_upd, T* vals_t,
+                                             float lr) {
   constexpr int NQ = (NR + LPE - 1) / LPE;
   vec<T, CH> gv[NR];
   float vj[NR];
@@ -35,18 +38,46 @@ __device__ __forceinline__ void fused_rounds(const T* __restrict__ gb, int32_t B
   round_dots<T, CH, LPE, NR>(gv, xs, lane, d);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    if (rb + q * SNK_WAVE + lane < e) {
+    const int32_t k = rb + q * SNK_WAVE + lane;
+    if (k < e) {
       if (dV) dV[pk[q]] = elem<T>::from_f(d[q]);
-      if (lr != 0.f) vals_upd[pk[q]] = elem<T>::from_f(cv[q] - lr * d[q]);
+      if (lr != 0.f) {
+        const T u = elem<T>::from_f(cv[q] - lr * d[q]);
+        vals_upd[pk[q]] = u;
+        if constexpr (VT) vals_t[k] = u;
+      }
     }
   }
 }
 
+// The fused kernel's entry loads with the values in column order: index,
+// value position and value, all at the entry's own (coalesced) position.
+template <typename T>
+__device__ __forceinline__ void load_entries_vt(const int32_t* __restrict__ idx,
+                                                const int32_t* __restrict__ perm,
+                                                const T* vals_t, int32_t base, int32_t e,
+                                                int lane, int32_t (&ci)[WV_U],
+                                                float (&cv)[WV_U], int32_t (&pk)[WV_U]) {
+  int32_t kc[WV_U];
+  T raw[WV_U];
+#pragma unroll
+  for (int q = 0; q < WV_U; ++q) kc[q] = min(base + q * SNK_WAVE + lane, e - 1);
+#pragma unroll
+  for (int q = 0; q < WV_U; ++q) ci[q] = idx[kc[q]];
+#pragma unroll
+  for (int q = 0; q < WV_U; ++q) pk[q] = perm[kc[q]];
+#pragma unroll
+  for (int q = 0; q < WV_U; ++q) raw[q] = vals_t[kc[q]];
+#pragma unroll
+  for (int q = 0; q < WV_U; ++q)
+    cv[q] = (base + q * SNK_WAVE + lane < e) ? elem<T>::to_f(raw[q]) : 0.f;
+}
+
 // One pass covers the batch: B <= LPE * CH.
-template <typename T, int CH, int LPE, bool NODE_OUT>
+template <typename T, int CH, int LPE, bool NODE_OUT, bool VT>
 __global__ __launch_bounds__(WV_THREADS) void k_wave_bwd_fused(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ perm, T* vals, const T* __restrict__ dYt,
+    const int32_t* __restrict__ perm, T* vals, T* vals_t, const T* __restrict__ dYt,
     const T* __restrict__ Xt, T* __restrict__ dX, T* __restrict__ dV, float lr, int32_t S,
     int32_t B, int32_t xcd_blocks) {
   constexpr int EPI = SNK_WAVE / LPE;
@@ -71,7 +102,8 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_bwd_fused(
   for (int32_t base = a; base < e; base += WV_U * SNK_WAVE) {
     int32_t ci[WV_U], pk[WV_U];
     float cv[WV_U];
-    load_entries<T, true, true>(idx, perm, vals, base, e, lane, ci, cv, pk);
+    if constexpr (VT) load_entries_vt<T>(idx, perm, vals_t, base, e, lane, ci, cv, pk);
+    else load_entries<T, true, true>(idx, perm, vals, base, e, lane, ci, cv, pk);
 #pragma unroll
     for (int g = 0; g < WV_U * LPE / RG; ++g) {
       const int q0 = g * RG / LPE;
@@ -79,8 +111,9 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_bwd_fused(
       if (rb >= e) break;
       const int nr = (e - rb + EPI - 1) / EPI;
       with_count<RG>(nr, [&](auto n) {
-        fused_rounds<T, CH, LPE, decltype(n)::value>(gb, B, xs, ci + q0, cv + q0, pk + q0, rb,
-                                                     e, lane, slot, acc, dV, vals, lr);
+        fused_rounds<T, CH, LPE, decltype(n)::value, VT>(gb, B, xs, ci + q0, cv + q0, pk + q0,
+                                                         rb, e, lane, slot, acc, dV, vals,
+                                                         vals_t, lr);
       });
     }
   }
@@ -94,35 +127,48 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_bwd_fused(
   }
 }
 
+template <typename T, int CH, int LPE, bool NODE_OUT>
+static void wave_fused_n(const seg_view& v, void* vals, void* vals_t, const void* dYt,
+                         const void* Xt, int32_t B, void* dX, void* dV, float lr, dim3 grid,
+                         int32_t xb, hipStream_t s) {
+  if (vals_t)
+    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, NODE_OUT, true>), grid, dim3(WV_THREADS), 0,
+                       s, v.ptr, v.idx, v.perm, (T*)vals, (T*)vals_t, (const T*)dYt,
+                       (const T*)Xt, (T*)dX, (T*)dV, lr, v.S, B, xb);
+  else
+    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, NODE_OUT, false>), grid, dim3(WV_THREADS),
+                       0, s, v.ptr, v.idx, v.perm, (T*)vals, (T*)nullptr, (const T*)dYt,
+                       (const T*)Xt, (T*)dX, (T*)dV, lr, v.S, B, xb);
+}
+
 template <typename T, int CH, int LPE>
-static void wave_fused_l(const seg_view& v, void* vals, const void* dYt, const void* Xt,
-                         int32_t B, void* dX, void* dV, float lr, bool node_out,
+static void wave_fused_l(const seg_view& v, void* vals, void* vals_t, const void* dYt,
+                         const void* Xt, int32_t B, void* dX, void* dV, float lr, bool node_out,
                          hipStream_t s) {
   const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
-  const int32_t xb = (nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+  // die-contiguous column ranges: a line of the row-ordered arrays accessed
+  // through perm (values read, dV and updated values written) is touched by
+  // few dies instead of all eight
+  const int32_t xb = nblk >= 8 * NUM_XCD ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
   dim3 grid((unsigned)(xb ? xb * NUM_XCD : nblk));
   if (node_out)
-    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, true>), grid, dim3(WV_THREADS), 0, s, v.ptr,
-                       v.idx, v.perm, (T*)vals, (const T*)dYt, (const T*)Xt, (T*)dX, (T*)dV, lr,
-                       v.S, B, xb);
+    wave_fused_n<T, CH, LPE, true>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, grid, xb, s);
   else
-    hipLaunchKernelGGL((k_wave_bwd_fused<T, CH, LPE, false>), grid, dim3(WV_THREADS), 0, s,
-                       v.ptr, v.idx, v.perm, (T*)vals, (const T*)dYt, (const T*)Xt, (T*)dX,
-                       (T*)dV, lr, v.S, B, xb);
+    wave_fused_n<T, CH, LPE, false>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, grid, xb, s);
 }
 
 template <typename T, int CH>
-static bool wave_fused_c(const seg_view& v, void* vals, const void* dYt, const void* Xt,
-                         int32_t B, void* dX, void* dV, float lr, bool node_out, int lpe,
-                         hipStream_t s) {
+static bool wave_fused_c(const seg_view& v, void* vals, void* vals_t, const void* dYt,
+                         const void* Xt, int32_t B, void* dX, void* dV, float lr, bool node_out,
+                         int lpe, hipStream_t s) {
   switch (lpe) {
-    case 1: wave_fused_l<T, CH, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
-    case 2: wave_fused_l<T, CH, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
-    case 4: wave_fused_l<T, CH, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
-    case 8: wave_fused_l<T, CH, 8>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 1: wave_fused_l<T, CH, 1>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 2: wave_fused_l<T, CH, 2>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 4: wave_fused_l<T, CH, 4>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
+    case 8: wave_fused_l<T, CH, 8>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, s); return true;
     case 16:
       if constexpr (CH <= 4) {
-        wave_fused_l<T, CH, 16>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, s);
+        wave_fused_l<T, CH, 16>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, s);
         return true;
       }
       return false;
@@ -130,24 +176,27 @@ static bool wave_fused_c(const seg_view& v, void* vals, const void* dYt, const v
   }
 }
 
-bool launch_wave_bwd_fused(const seg_view& v, void* vals, snack_dtype dt, const void* dYt,
-                           const void* Xt, int32_t B, void* dX, void* dV, float lr,
-                           bool node_out, hipStream_t s) {
+bool launch_wave_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
+                           const void* dYt, const void* Xt, int32_t B, void* dX, void* dV,
+                           float lr, bool node_out, hipStream_t s) {
   const wave_shape w = wave_pick(dt, B);
   if ((int64_t)w.ch * w.lpe < B) return false;  // one pass must cover the batch
   if (dt == SNACK_F32) {
     switch (w.ch) {
-      case 1: return wave_fused_c<float, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
-      case 2: return wave_fused_c<float, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+      case 1:
+        return wave_fused_c<float, 1>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+      case 2:
+        return wave_fused_c<float, 2>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
       default:
-        return wave_fused_c<float, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+        return wave_fused_c<float, 4>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
     }
   }
   switch (w.ch) {
-    case 1: return wave_fused_c<bf16, 1>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
-    case 2: return wave_fused_c<bf16, 2>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
-    case 4: return wave_fused_c<bf16, 4>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
-    default: return wave_fused_c<bf16, 8>(v, vals, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    case 1: return wave_fused_c<bf16, 1>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    case 2: return wave_fused_c<bf16, 2>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    case 4: return wave_fused_c<bf16, 4>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
+    default:
+      return wave_fused_c<bf16, 8>(v, vals, vals_t, dYt, Xt, B, dX, dV, lr, node_out, w.lpe, s);
   }
 }
 

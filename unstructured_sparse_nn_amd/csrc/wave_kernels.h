@@ -355,7 +355,7 @@ static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int
                         float* carry, hipStream_t s) {
   const int32_t nblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
   const int32_t xb =
-      (PERM && nblk >= 8 * NUM_XCD && !no_xcd_remap()) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
+      (PERM && nblk >= 8 * NUM_XCD) ? (int32_t)cdiv(nblk, NUM_XCD) : 0;
   const unsigned passes = (unsigned)cdiv(B, LPE * CH);
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
   const int32_t sblk = xb ? xb * NUM_XCD : nblk;

@@ -1,9 +1,11 @@
 """Torch-facing wrappers: a prepared sparse topology and the SparseLinear
-module ("a simple PyTorch API for restructuring connections and
-backpropagating gradients entirely in the sparse paradigm", SNACK abstract).
+module, the torch API for sparse training and restructuring ("Beyond Masked
+Sparsity: SNACK Enables Truly Sparse Neural Networks on GPU", Abstract).
 
-Torch allocates the device buffers and supplies the stream; every product,
-gradient and restructuring step is a call into the HIP library.
+Torch allocates the device buffers (and the small pinned host buffer through
+which prepare and the restructure read their result words) and supplies the
+stream; every product, gradient and restructuring step is a call into the
+HIP library.
 """
 from __future__ import annotations
 
@@ -33,17 +35,30 @@ class Topology:
         self.plan = B.snack_plan_init(self.M, self.K, self.nnz, self.max_batch, self.tile_items,
                                       self.flags)
         self.arena = torch.empty(self.plan.arena_bytes, dtype=torch.uint8, device=self.row.device)
-        B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
+        # pinned host words: prepare and the restructure read their few result
+        # words from here with no copy (without them: a copy and a sync)
+        self.host_words = torch.zeros(B.HOST_WORDS_BYTES // 4, dtype=torch.int32,
+                                      pin_memory=True)
+        self.plan.host_words = self.host_words.data_ptr()
+        try:
+            B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
+        except B.SnackError as e:
+            if e.status != -9:  # SNACK_E_WORKSPACE: the pinned words are not device-mapped
+                raise
+            self.plan.host_words = None
+            B.snack_coo_prepare(self.plan, self.row, self.col, self.arena, stream)
 
     def restructure(self, vals, n_drop: int, seed: int, step: int, dropped=None, grown=None,
-                    ws=None, stream=None):
+                    ws=None, stream=None, vals_t=None, flags: int = 0):
         """One prune/regrow step on (row, col, vals) in place, re-preparing this
-        plan in the same call (snack_prune_regrow_prepared)."""
+        plan in the same call (snack_prune_regrow_prepared); vals_t, if given,
+        receives the new values in the new column order."""
         if ws is None:
-            ws = torch.empty(B.snack_prune_regrow_workspace(self.M, self.K, self.nnz, n_drop),
+            ws = torch.empty(B.snack_prune_regrow_workspace(self.M, self.K, self.nnz, n_drop,
+                                                            flags),
                              dtype=torch.uint8, device=self.row.device)
         B.snack_prune_regrow_prepared(self.plan, self.row, self.col, vals, n_drop, seed, step,
-                                      dropped, grown, ws, stream)
+                                      dropped, grown, ws, stream, vals_t=vals_t, flags=flags)
 
     def array(self, name: str) -> torch.Tensor:
         """A derived array of the plan as an int32 view into the arena."""
@@ -63,6 +78,19 @@ class Topology:
         B.snack_spmm_bwd_input(self.plan, vals, dY, layout, Bsz, dX)
         return dX
 
+    def gather_vals_t(self, vals, out=None):
+        """The values in this plan's column order (vals_t[i] = vals[perm[i]])."""
+        vt = out if out is not None else torch.empty_like(vals)
+        B.snack_gather_vals_t(self.plan, vals, vt)
+        return vt
+
+    def bwd_input_t(self, vals_t, dY, Bsz, layout=B.BATCH_MAJOR, out=None):
+        """dX = dY W from the values in column order."""
+        dX = out if out is not None else torch.empty(Bsz * self.K, dtype=dY.dtype,
+                                                     device=dY.device)
+        B.snack_spmm_bwd_input_t(self.plan, vals_t, dY, layout, Bsz, dX)
+        return dX
+
     def grad_vals(self, dY, X, Bsz, layout=B.BATCH_MAJOR, out=None):
         dV = out if out is not None else torch.empty(self.nnz, dtype=X.dtype, device=X.device)
         B.snack_sddmm_grad_vals(self.plan, dY, X, layout, Bsz, dV)
@@ -71,26 +99,30 @@ class Topology:
 
 class _SparseLinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, vals, topo):
+    def forward(ctx, x, vals, layer):
+        topo = layer.topo
         Bsz = x.shape[0]
         xc = x.contiguous()
-        ctx.topo = topo
+        ctx.layer = layer
         ctx.save_for_backward(xc, vals)
         return topo.fwd(vals, xc.view(-1), Bsz).view(Bsz, topo.M)
 
     @staticmethod
     def backward(ctx, gy):
         xc, vals = ctx.saved_tensors
-        topo = ctx.topo
+        layer = ctx.layer
+        topo = layer.topo
         Bsz = xc.shape[0]
         g = gy.contiguous().view(-1)
+        vt = layer.vals_t()  # the values in column order: read coalesced by the input gradient
         if ctx.needs_input_grad[0] and ctx.needs_input_grad[1] and 0 < Bsz <= FUSED_MAX_BATCH:
             # both gradients from one pass over the column view (snack_spmm_bwd_fused)
             gx = torch.empty(Bsz * topo.K, dtype=g.dtype, device=g.device)
             gv = torch.empty(topo.nnz, dtype=g.dtype, device=g.device)
-            B.snack_spmm_bwd_fused(topo.plan, vals, xc.view(-1), g, B.BATCH_MAJOR, Bsz, gx, gv)
+            B.snack_spmm_bwd_fused(topo.plan, vals, xc.view(-1), g, B.BATCH_MAJOR, Bsz, gx, gv,
+                                   vals_t=vt)
             return gx.view(Bsz, topo.K), gv, None
-        gx = topo.bwd_input(vals, g, Bsz).view(Bsz, topo.K) if ctx.needs_input_grad[0] else None
+        gx = topo.bwd_input_t(vt, g, Bsz).view(Bsz, topo.K) if ctx.needs_input_grad[0] else None
         gv = topo.grad_vals(g, xc.view(-1), Bsz) if ctx.needs_input_grad[1] else None
         return gx, gv, None
 
@@ -100,7 +132,13 @@ class SparseLinear(torch.nn.Module):
 
     ``prune_regrow(frac_ppm, step)`` drops the smallest-magnitude fraction of
     the connections and regrows as many at seeded random free positions
-    (value 0), then re-prepares the topology."""
+    (value 0), then re-prepares the topology.
+
+    The layer keeps a second copy of the values in the topology's column
+    order, which the input gradient reads coalesced.  It is refreshed by one
+    gather whenever the values tensor is replaced or changed by torch (its
+    version counter moves, as with an optimiser step), and written directly by
+    the restructure."""
 
     def __init__(self, in_features: int, out_features: int, row, col, vals, max_batch: int,
                  seed: int = 0, tile_items: int = 0):
@@ -108,9 +146,26 @@ class SparseLinear(torch.nn.Module):
         self.in_features, self.out_features, self.seed = in_features, out_features, seed
         self.topo = Topology(row, col, out_features, in_features, max_batch, tile_items)
         self.vals = torch.nn.Parameter(vals)
+        self._vals_t = None
+        self._vals_t_key = None
+
+    def _key(self):
+        v = self.vals
+        return (v.data_ptr(), v._version, v.dtype, v.numel())
+
+    def vals_t(self) -> torch.Tensor:
+        """The values in column order, gathered again only if they changed."""
+        key = self._key()
+        if self._vals_t is None or self._vals_t_key != key:
+            if self._vals_t is None or self._vals_t.dtype != self.vals.dtype or \
+                    self._vals_t.numel() != self.vals.numel():
+                self._vals_t = torch.empty_like(self.vals.data)
+            self.topo.gather_vals_t(self.vals.data, out=self._vals_t)
+            self._vals_t_key = key
+        return self._vals_t
 
     def forward(self, x):
-        return _SparseLinearFn.apply(x, self.vals, self.topo)
+        return _SparseLinearFn.apply(x, self.vals, self)
 
     @torch.no_grad()
     def prune_regrow(self, frac_ppm: int, step: int):
@@ -118,5 +173,9 @@ class SparseLinear(torch.nn.Module):
         n_drop = B.snack_drop_count(t.nnz, frac_ppm)
         dropped = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
         grown = torch.empty(max(n_drop, 1), dtype=torch.int64, device=t.row.device)
-        t.restructure(self.vals.data, n_drop, self.seed, step, dropped, grown)
+        if self._vals_t is None or self._vals_t.dtype != self.vals.dtype:
+            self._vals_t = torch.empty_like(self.vals.data)
+        t.restructure(self.vals.data, n_drop, self.seed, step, dropped, grown,
+                      vals_t=self._vals_t)
+        self._vals_t_key = self._key()  # written by the restructure itself
         return dropped[:n_drop], grown[:n_drop]
