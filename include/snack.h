@@ -21,9 +21,10 @@
  *     Outputs use the same layout as the inputs.
  *   - memory: every array argument is caller-owned device memory unless
  *     stated otherwise.  The library allocates no memory (device or pinned
- *     host) and keeps no global state; its one exception is the code object
+ *     host) and keeps no global state, with two exceptions: the code object
  *     of a generated fixed-pattern kernel (snack_fixed_build), owned by its
- *     handle.  Plans are caller-owned host structs.
+ *     handle, and the per-GPU workspace array of snack_prune_regrow_static.
+ *     Plans are caller-owned host structs.
  *   - streams: `stream` is a hipStream_t (NULL = the null stream).  All
  *     calls are stream-ordered and asynchronous, except snack_coo_prepare
  *     and snack_prune_regrow(_prepared), which read a few words back and
@@ -365,6 +366,25 @@ SNACK_API snack_status snack_prune_regrow_ex(int32_t* row, int32_t* col, void* v
                                              uint64_t step, int64_t* dropped_lin,
                                              int64_t* grown_lin, void* ws, size_t ws_bytes,
                                              uint32_t flags, void* stream);
+
+/*
+ * snack_prune_regrow_static -- snack_prune_regrow for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same step, arguments and results, with the
+ * workspace taken from a device array the library holds, one per GPU,
+ * SNACK_STATIC_WS_MAX bytes (32 MiB: enough for 4096 x 4096 layers at 90-99%
+ * sparsity and the GPT-2-sized projections; kept until the process ends).
+ * The call allocates nothing.  Layers whose snack_prune_regrow_workspace
+ * exceeds the limit get SNACK_E_WORKSPACE.  Every call on one GPU shares its
+ * array: calls that overlap on one GPU (several streams or host threads)
+ * race and must be serialised by the caller.  Synchronises `stream`.
+ */
+#define SNACK_STATIC_WS_MAX (32u << 20)
+SNACK_API snack_status snack_prune_regrow_static(int32_t* row, int32_t* col, void* vals,
+                                                 snack_dtype dtype, int32_t M, int32_t K,
+                                                 int64_t nnz, int64_t n_drop, uint64_t seed,
+                                                 uint64_t step, int64_t* dropped_lin,
+                                                 int64_t* grown_lin, void* stream);
 
 /*
  * snack_prune_regrow_prepared -- snack_prune_regrow followed by

@@ -11,7 +11,7 @@ from .binding import (ACT_GELU, ACT_NONE, ACT_RELU, BATCH_MAJOR, BF16, CONV_NCHW
                       SnackPlan, snack_conv1x1, snack_fixed_build, snack_fixed_fwd,
                       snack_coo_prepare, snack_dense_fwd, snack_graph_propagate, snack_drop_count, snack_gelu_bwd,
                       snack_gelu_fwd, snack_memory_footprint, snack_plan_array, snack_plan_init, snack_plan_sizeof,
-                      snack_prune_regrow, snack_prune_regrow_prepared,
+                      snack_prune_regrow, snack_prune_regrow_prepared, snack_prune_regrow_static,
                       snack_prune_regrow_workspace, snack_sddmm_grad_vals, snack_gather_vals_t,
                       snack_spmm_bwd_input_t,
                       snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd,

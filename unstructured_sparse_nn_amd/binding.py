@@ -24,6 +24,7 @@ FIXED_COMPILE_ONLY = 1
 PLAN_NODE_MAJOR_ONLY = 1
 PRUNE_SORT_PLAN = 1
 HOST_WORDS_BYTES = 64
+STATIC_WS_MAX = 32 << 20
 BATCH_MAJOR, NODE_MAJOR = 0, 1
 PLAN_SLOTS = 16
 
@@ -99,6 +100,8 @@ def _load():
                                    ctypes.c_uint32, P], i32),
         "snack_prune_regrow_prepared": ([plan_p, P, P, P, P, i32, i64, u64, u64, P, P, P, sz,
                                          ctypes.c_uint32, P], i32),
+        "snack_prune_regrow_static": ([P, P, P, i32, i32, i32, i64, i64, u64, u64, P, P, P],
+                                      i32),
         "snack_memory_footprint": ([i32, i32, i64, i32, i32, i64, ctypes.c_uint32,
                                     ctypes.POINTER(SnackFootprint)], i32),
         "snack_fixed_build": ([P, P, P, i32, i32, i32, i64, ctypes.c_uint32, ctypes.POINTER(P)],
@@ -287,6 +290,17 @@ def snack_prune_regrow(row, col, vals, M, K, nnz, n_drop, seed, step, dropped_li
         _check(_lib.snack_prune_regrow_ex(*args, flags, _stream(stream)), "snack_prune_regrow_ex")
     else:
         _check(_lib.snack_prune_regrow(*args, _stream(stream)), "snack_prune_regrow")
+
+
+def snack_prune_regrow_static(row, col, vals, M, K, nnz, n_drop, seed, step, dropped_lin,
+                              grown_lin, stream=None, dtype=None):
+    """snack_prune_regrow with the library's per-GPU workspace array (no allocation)."""
+    dt = _dtype(vals, dtype=dtype)
+    _check(_lib.snack_prune_regrow_static(_ptr(row), _ptr(col), _ptr(vals), dt, M, K, nnz,
+                                          n_drop, seed & (2**64 - 1), step & (2**64 - 1),
+                                          _ptr(dropped_lin), _ptr(grown_lin),
+                                          _stream(stream)),
+           "snack_prune_regrow_static")
 
 
 def snack_prune_regrow_prepared(plan, row, col, vals, n_drop, seed, step, dropped_lin, grown_lin,
