@@ -3,16 +3,24 @@
 One step = one dynamic-sparse-training step of a 4096 x 4096 layer at 95%
 sparsity (838,861 nnz, bf16 values and activations, fp32 accumulation) on a
 batch of 32:
-    forward Y = X W^T  ->  input gradient dX = dY W  ->  value gradient
-    dV = (dY^T X) at the nonzeros  ->  prune/regrow of 30% of the
-    connections  ->  re-prepare the topology (offsets, tiles, column view);
-    the last two are one call (snack_prune_regrow_prepared) unless
-    --restructure separate.
+    forward Y = X W^T  ->  input gradient dX = dY W (values read in column
+    order)  ->  value gradient dV = (dY^T X) at the nonzeros  ->  prune/regrow
+    of 30% of the connections  ->  re-prepare the topology (offsets, tiles,
+    column view, column-ordered values); the last two are one call
+    (snack_prune_regrow_prepared) unless --restructure separate.
 The metric is the fwd+bwd SpMM bandwidth: algorithmic bytes of the three
 products (values + indices + offsets + activations read + outputs written)
 per second of whole-step time.  Inputs are resident in HBM before timing;
-by default the step rotates over 20 independent layer instances (~580 MB) so
-that each step reads from HBM rather than the 256 MB Infinity Cache.
+the step rotates over 20 independent layer instances (~1.2 GB touched per
+rotation) so that each step reads from HBM rather than the 256 MB Infinity
+Cache.
+
+Per-op kernel times (``ops``, ``grid``, ``sweep``, ``baselines``) are cold:
+each op rotates over enough distinct instances that at least 512 MB of the
+data it touches lies between two uses of one instance.  ``ops_warm`` repeats
+one instance (cache-resident) for comparison.  ``calibration`` holds the
+machine floors measured in the same run (empty kernel, streaming read and
+write, dependent-load latency).
 
 Prints one JSON line (see --help).  --gpus > 1 is not supported: the layer
 runs on one GPU.
@@ -52,6 +60,26 @@ def algo_bytes(op: str, M: int, K: int, nnz: int, B: int, s_w: int, s_a: int,
     raise KeyError(op)
 
 
+def restructure_bytes(M: int, K: int, nnz: int, s_w: int, P_row: int, P_col: int) -> int:
+    """Minimum bytes of one restructure with the re-prepared plan: the COO
+    read and written back (two int32 indices and a value per connection,
+    each way), the plan's derived arrays written (row and column offsets,
+    perm and row_t, the tiles and cut flags of both views) and the
+    column-ordered values written."""
+    coo = nnz * (8 + s_w)
+    plan = 4 * (M + 1) + 4 * (K + 1) + 8 * nnz + 12 * (P_row + 1) + 12 * (P_col + 1)
+    return 2 * coo + plan + nnz * s_w
+
+
+COLD_BYTES = 512e6  # data an op touches between two uses of one instance (> 256 MB MALL)
+
+
+def rotation_for(op_bytes: int, cap: int = 600) -> int:
+    """Instances to rotate so that >= COLD_BYTES of an op's data lies between
+    two uses of one instance."""
+    return max(2, min(cap, int(-(-COLD_BYTES // op_bytes)) + 1))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,7 +95,12 @@ def parse():
     ap.add_argument("--rotate", type=int, default=20,
                     help="layer instances cycled through (1 = cache-warm)")
     ap.add_argument("--grid", action=argparse.BooleanOptionalAction, default=True,
-                    help="also time fwd/dX/dV at 95/99%% x B in {1,8,32}")
+                    help="also time fwd/dX/dV at 95/99%% x B in {1,8,32} (cold)")
+    ap.add_argument("--sizes", default="8192,16384,32768",
+                    help="square sizes of the cold size sweep of fwd/dX/dV at 95/99%% x B in "
+                         "{1,8,32} ('' = none)")
+    ap.add_argument("--calibrate", action=argparse.BooleanOptionalAction, default=True,
+                    help="measure the machine floors (empty kernel, stream read/write, latency)")
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--conv", action=argparse.BooleanOptionalAction, default=True,
                     help="time a sparse 1x1 convolution (generated kernel, generic, dense)")
@@ -108,18 +141,25 @@ def layout_data(act, layout):
 
 
 class Instance:
-    """One layer: COO + values + activations + prepared topology + scratch."""
+    """One layer: COO + values (+ column-ordered copy) + activations + prepared
+    topology + outputs; with ``restructure`` also a restructuring workspace.
+    ``like`` clones another instance's host-side inputs on the device (distinct
+    buffers, same contents) instead of copying them from the host again."""
 
-    def __init__(self, w, X, dY, B, bf16, drop_ppm, layout="node"):
+    def __init__(self, w, X, dY, B, bf16, drop_ppm, layout="node", restructure=True, like=None):
         import torch
         import unstructured_sparse_nn_amd as snk
         wt = w
-        self.M, self.K, self.B = wt.M, wt.K, B
+        self.M, self.K, self.B, self.nnz = wt.M, wt.K, B, wt.nnz
         self.lay = snk.NODE_MAJOR if layout == "node" else snk.BATCH_MAJOR
-        self.row, self.col = to_dev(wt.row), to_dev(wt.col)
-        self.vals = to_dev(wt.vals, bf16)
-        self.X = to_dev(layout_data(X, layout), bf16)
-        self.dY = to_dev(layout_data(dY, layout), bf16)
+        if like is None:
+            self.row, self.col = to_dev(wt.row), to_dev(wt.col)
+            self.vals = to_dev(wt.vals, bf16)
+            self.X = to_dev(layout_data(X, layout), bf16)
+            self.dY = to_dev(layout_data(dY, layout), bf16)
+        else:
+            self.row, self.col, self.vals = like.row.clone(), like.col.clone(), like.vals.clone()
+            self.X, self.dY = like.X.clone(), like.dY.clone()
         dt = self.vals.dtype
         self.Y = torch.empty(B * wt.M, dtype=dt, device="cuda")
         self.dX = torch.empty(B * wt.K, dtype=dt, device="cuda")
@@ -130,8 +170,11 @@ class Instance:
         # kept in step by the restructure, which writes them
         self.vals_t = self.topo.gather_vals_t(self.vals)
         self.n_drop = snk.snack_drop_count(wt.nnz, drop_ppm)
-        self.ws = torch.empty(snk.snack_prune_regrow_workspace(wt.M, wt.K, wt.nnz, self.n_drop),
-                              dtype=torch.uint8, device="cuda")
+        self.ws = None
+        if restructure:
+            self.ws = torch.empty(snk.snack_prune_regrow_workspace(wt.M, wt.K, wt.nnz,
+                                                                   self.n_drop),
+                                  dtype=torch.uint8, device="cuda")
         self.step_no = 0
 
     def products(self, ev=None):
@@ -145,7 +188,8 @@ class Instance:
         if ev: ev[3].record()
 
     def bwd_fused(self, lr=0.0):
-        """dX and dV in one pass (snack_spmm_bwd_fused), no value update."""
+        """dX and dV in one pass (snack_spmm_bwd_fused); with lr != 0 the SGD
+        step on both copies of the values."""
         import unstructured_sparse_nn_amd as snk
         snk.snack_spmm_bwd_fused(self.topo.plan, self.vals, self.X, self.dY, self.lay, self.B,
                                  self.dX, self.dV, lr, vals_t=self.vals_t)
@@ -167,36 +211,48 @@ class Instance:
         if ev: ev[5].record()
 
 
-def graph_kernel_us(insts, op, launches=20, replays=5):
-    """Mean duration of one launch of a product op, from HIP events around
-    replays of a captured graph of `launches` back-to-back launches (rotating
-    over the instances), so that no host work sits between the kernels."""
+def make_instances(w, X, dY, B, R, layout="node", restructure=False, drop_ppm=0):
+    """R product instances of one layer (bf16), the first from the host, the
+    rest cloned on the device."""
+    first = Instance(w, X, dY, B, True, drop_ppm, layout, restructure)
+    out = [first]
+    for _ in range(R - 1):
+        out.append(Instance(w, X, dY, B, True, drop_ppm, layout, restructure, like=first))
+    return out
+
+
+def op_fn(inst, op):
+    """The call of one product op on one instance."""
+    t = inst.topo
+    if op == "fwd":
+        return lambda: t.fwd(inst.vals, inst.X, inst.B, inst.lay, out=inst.Y)
+    if op == "bwd_input":
+        return lambda: t.bwd_input_t(inst.vals_t, inst.dY, inst.B, inst.lay, out=inst.dX)
+    if op == "bwd_input_perm":
+        return lambda: t.bwd_input(inst.vals, inst.dY, inst.B, inst.lay, out=inst.dX)
+    if op == "sddmm":
+        return lambda: t.grad_vals(inst.dY, inst.X, inst.B, inst.lay, out=inst.dV)
+    if op == "bwd_fused":
+        return lambda: inst.bwd_fused()
+    raise KeyError(op)
+
+
+def graph_us(fns, launches=None, replays=3):
+    """Mean duration of one launch, from HIP events around replays of a
+    captured graph of back-to-back launches cycling through ``fns`` (so no
+    host work sits between the kernels).  With len(fns) instances of ``B``
+    bytes each, consecutive uses of one instance are len(fns) - 1 instances'
+    data apart."""
     import torch
-    R = len(insts)
-    fns = {"fwd": lambda i: insts[i % R].topo.fwd(insts[i % R].vals, insts[i % R].X,
-                                                   insts[i % R].B, insts[i % R].lay,
-                                                   out=insts[i % R].Y),
-           "bwd_input": lambda i: insts[i % R].topo.bwd_input_t(insts[i % R].vals_t,
-                                                                insts[i % R].dY, insts[i % R].B,
-                                                                insts[i % R].lay,
-                                                                out=insts[i % R].dX),
-           "bwd_input_perm": lambda i: insts[i % R].topo.bwd_input(insts[i % R].vals,
-                                                                   insts[i % R].dY,
-                                                                   insts[i % R].B,
-                                                                   insts[i % R].lay,
-                                                                   out=insts[i % R].dX),
-           "sddmm": lambda i: insts[i % R].topo.grad_vals(insts[i % R].dY, insts[i % R].X,
-                                                          insts[i % R].B, insts[i % R].lay,
-                                                          out=insts[i % R].dV),
-           "bwd_fused": lambda i: insts[i % R].bwd_fused()}
-    fn = fns[op]
-    for i in range(3):
-        fn(i)
+    n = len(fns)
+    launches = launches or max(n, 20)
+    for i in range(min(n, 3)):
+        fns[i]()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(launches):
-            fn(i)
+            fns[i % n]()
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -205,7 +261,13 @@ def graph_kernel_us(insts, op, launches=20, replays=5):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (launches * replays)
+    us = e0.elapsed_time(e1) * 1e3 / (launches * replays)
+    del g
+    return us
+
+
+def graph_kernel_us(insts, op, launches=None, replays=3):
+    return graph_us([op_fn(i, op) for i in insts], launches, replays)
 
 
 def src_hash():
@@ -234,10 +296,11 @@ def read_traffic(name, launches_bytes):
         return None
 
 
-def dense_baselines(wt, X, batches, rotate=8):
-    """Forward time of the in-repo dense and Dense+Mask kernels (snack_dense_fwd)
-    on the same layer, graph-timed like the sparse products, cold (rotating
-    over `rotate` copies of the dense weight and mask)."""
+def dense_baselines(wt, X, batches, sparse_us):
+    """Forward time of the in-repo dense and Dense+Mask kernels
+    (snack_dense_fwd) on the same layer, graph-timed like the sparse products
+    and cold the same way (>= 512 MB of weights, masks and activations between
+    two uses of one copy).  sparse_us: the cold sparse forward per batch."""
     import torch
     import unstructured_sparse_nn_amd as snk
     M, K = wt.M, wt.K
@@ -245,36 +308,71 @@ def dense_baselines(wt, X, batches, rotate=8):
     dense[wt.row.astype(np.int64) * K + wt.col] = wt.vals
     mask = np.zeros(M * K, dtype=np.uint8)
     mask[wt.row.astype(np.int64) * K + wt.col] = 1
-    Wd = [torch.from_numpy(dense.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(rotate)]
-    Md = [torch.from_numpy(mask).cuda() for _ in range(rotate)]
+    w0 = torch.from_numpy(dense.view(np.int16)).view(torch.bfloat16).cuda()
+    m0 = torch.from_numpy(mask).cuda()
     out = {}
-    for B in batches:
-        xb = torch.from_numpy(X.data[:B * K].view(np.int16)).view(torch.bfloat16).cuda()
-        Y = torch.empty(B * M, dtype=torch.bfloat16, device="cuda")
-        for kind, use_mask in (("dense", False), ("dense_mask", True)):
-            def fn(i):
-                snk.snack_dense_fwd(Wd[i % rotate], Md[i % rotate] if use_mask else None, M, K,
-                                    xb, B, Y)
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(16):
-                    fn(i)
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(3):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / 48
-            nbytes = M * K * 2 + (M * K if use_mask else 0) + B * (K + M) * 2
-            out[f"{kind}_B{B}"] = {"us": round(us, 2), "bytes": nbytes,
-                                   "GBps": round(nbytes / us / 1e3, 1)}
-    del Wd, Md
+    for kind, use_mask in (("dense", False), ("dense_mask", True)):
+        per = M * K * 2 + (M * K if use_mask else 0)
+        R = rotation_for(per)
+        Wd = [w0] + [w0.clone() for _ in range(R - 1)]
+        Md = ([m0] + [m0.clone() for _ in range(R - 1)]) if use_mask else [None] * R
+        for B in batches:
+            xb = torch.from_numpy(X.data[:B * K].view(np.int16)).view(torch.bfloat16).cuda()
+            Y = torch.empty(B * M, dtype=torch.bfloat16, device="cuda")
+            fns = [(lambda i=i: snk.snack_dense_fwd(Wd[i], Md[i], M, K, xb, B, Y))
+                   for i in range(R)]
+            us = graph_us(fns)
+            nbytes = per + B * (K + M) * 2
+            rec = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                   "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "rotate": R,
+                   "floor_us_at_8TBps": round(nbytes / HBM_PEAK_GBPS / 1e3, 2)}
+            if B in sparse_us:
+                rec["sparse_fwd_us"] = sparse_us[B]
+                rec["sparse_fwd_speedup"] = round(us / sparse_us[B], 2)
+                # against the dense layer's own byte floor: what a perfect dense
+                # kernel would give
+                rec["sparse_fwd_speedup_vs_floor"] = round(rec["floor_us_at_8TBps"]
+                                                           / sparse_us[B], 2)
+            out[f"{kind}_B{B}"] = rec
+        del Wd, Md
+        torch.cuda.empty_cache()
+    return out
+
+
+def calibrate():
+    """Machine floors on this machine, same process: an empty kernel (graph-timed
+    back-to-back launches), a 1 GiB streaming read and write, and the latency
+    of dependent loads over 1 GiB (HBM) and over 2 MiB (L2)."""
+    import torch
+    import unstructured_sparse_nn_amd as snk
+    B_ = snk.binding
+    out = {}
+    out["empty_kernel_us"] = round(graph_us([lambda: snk.snack_calibrate(B_.CALIB_EMPTY, n=1)],
+                                            launches=50, replays=5), 2)
+    nbytes = 1 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for name, kind in (("read", B_.CALIB_READ), ("write", B_.CALIB_WRITE)):
+        us = graph_us([lambda k=kind: snk.snack_calibrate(k, buf, nbytes, 4096)], launches=4,
+                      replays=3)
+        out[f"stream_{name}_GBps"] = round(nbytes / us / 1e3, 1)
+    # HBM: one pass right after the 1 GiB chain is written (the chain from
+    # slot 0 was written first, so it has left the caches); L2: a 2 MiB chain,
+    # warmed first
+    for name, size, hops, warm in (("hbm", nbytes, 20000, 0), ("l2", 2 << 20, 100000, 1)):
+        snk.snack_calibrate(B_.CALIB_CHAIN, buf, size)
+        us = time_calls(lambda s=size, h=hops: snk.snack_calibrate(B_.CALIB_CHASE, buf, s, h),
+                        reps=1, warm=warm)
+        out[f"dependent_load_{name}_ns"] = round(us * 1e3 / hops, 1)
+    # reads of 5.6 MB (one 4096^2 product launch's bytes) and 1.0 MB (at 99%),
+    # each over distinct regions of the buffer (cold): the best a launch that
+    # size can do, launch, ramp and drain included
+    for tag, small in (("5.6MB", 5_573_888), ("1.0MB", 1_039_616)):
+        regions = min(64, nbytes // small)
+        base = buf.data_ptr()
+        fns = [(lambda a=base + k * small: snk.snack_calibrate(B_.CALIB_READ, a, small, 2048))
+               for k in range(regions)]
+        out[f"stream_read_{tag}_us"] = round(graph_us(fns, launches=regions, replays=3), 2)
+    del buf
     torch.cuda.empty_cache()
     return out
 
@@ -294,61 +392,67 @@ def time_calls(fn, reps=10, warm=3):
     return a.elapsed_time(b) * 1e3 / reps
 
 
-def time_config(w, B, bf16, layout, ops=("fwd", "bwd_input", "sddmm"), launches=10, replays=3):
-    """Per-launch time of each product on one layer instance (caches warm
-    across launches), from HIP events around replays of a captured graph."""
+def time_config(w, B, bf16, layout, ops=("fwd", "bwd_input", "sddmm"), cold=True):
+    """Per-launch time of each product on one layer configuration, from HIP
+    events around graph replays.  cold: rotate over enough device copies of
+    the layer (COO, plan, column-ordered values, activations, outputs) that
+    >= 512 MB of an op's data lies between two uses of one copy; else one
+    instance, caches warm."""
     import torch
     import unstructured_sparse_nn_amd as snk
     dt = torch.bfloat16 if bf16 else torch.float32
     lay = snk.NODE_MAJOR if layout == "node" else snk.BATCH_MAJOR
-    topo = snk.Topology(to_dev(w.row), to_dev(w.col), w.M, w.K, B)
-    vals = to_dev(w.vals, bf16)
-    g = torch.Generator(device="cuda").manual_seed(0)
-    X = torch.randn(B * w.K, device="cuda", generator=g).to(dt)
-    dY = torch.randn(B * w.M, device="cuda", generator=g).to(dt)
-    Y = torch.empty(B * w.M, dtype=dt, device="cuda")
-    dX = torch.empty(B * w.K, dtype=dt, device="cuda")
-    dV = torch.empty(w.nnz, dtype=dt, device="cuda")
-    fns = {"fwd": lambda: topo.fwd(vals, X, B, lay, out=Y),
-           "bwd_input": lambda: topo.bwd_input(vals, dY, B, lay, out=dX),
-           "sddmm": lambda: topo.grad_vals(dY, X, B, lay, out=dV)}
     s_el = 2 if bf16 else 4
-    out = {"split_rows": int(topo.plan.has_split_row), "split_cols": int(topo.plan.has_split_col)}
+    op_bytes = min(algo_bytes(op, w.M, w.K, w.nnz, B, s_el, s_el) for op in ops)
+    R = rotation_for(op_bytes, cap=64) if cold else 1
+    g = torch.Generator(device="cuda").manual_seed(0)
+    row, col, vals = to_dev(w.row), to_dev(w.col), to_dev(w.vals, bf16)
+    X0 = torch.randn(B * w.K, device="cuda", generator=g).to(dt)
+    dY0 = torch.randn(B * w.M, device="cuda", generator=g).to(dt)
+    insts = []
+    for r in range(R):
+        rr, cc, vv = (row, col, vals) if r == 0 else (row.clone(), col.clone(), vals.clone())
+        topo = snk.Topology(rr, cc, w.M, w.K, B)
+        insts.append({"topo": topo, "vals": vv, "vt": topo.gather_vals_t(vv),
+                      "X": X0 if r == 0 else X0.clone(), "dY": dY0 if r == 0 else dY0.clone(),
+                      "Y": torch.empty(B * w.M, dtype=dt, device="cuda"),
+                      "dX": torch.empty(B * w.K, dtype=dt, device="cuda"),
+                      "dV": torch.empty(w.nnz, dtype=dt, device="cuda")})
+
+    def fn(d, op):
+        t = d["topo"]
+        if op == "fwd":
+            return lambda: t.fwd(d["vals"], d["X"], B, lay, out=d["Y"])
+        if op == "bwd_input":
+            return lambda: t.bwd_input_t(d["vt"], d["dY"], B, lay, out=d["dX"])
+        return lambda: t.grad_vals(d["dY"], d["X"], B, lay, out=d["dV"])
+
+    plan = insts[0]["topo"].plan
+    out = {"split_rows": int(plan.has_split_row), "split_cols": int(plan.has_split_col),
+           "rotate": R, "cache": "cold (HBM)" if cold else "warm"}
     for op in ops:
-        fn = fns[op]
-        fn()
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for _ in range(launches):
-                fn()
-        gr.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(replays):
-            gr.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (launches * replays)
+        us = graph_us([fn(d, op) for d in insts], launches=max(R, 10))
         b = algo_bytes(op, w.M, w.K, w.nnz, B, s_el, s_el)
         out[op] = {"us": round(us, 2), "GBps": round(b / (us * 1e3), 1),
+                   "frac": round(b / (us * 1e3) / HBM_PEAK_GBPS, 4),
                    "GFLOPs": round(2 * w.nnz * B / (us * 1e3), 1)}
-    del topo
+    del insts
+    torch.cuda.empty_cache()
     return out
 
 
 def other_configs():
     """fwd, dX and dV on the other layer configurations: 256^2 at 90% (fp32,
-    B=4), the GPT-2-small MLP layers at 90% and 99% (fp32, 1024 tokens,
-    batch-major), the LLaMA-7B-shaped projections with skewed rows (bf16,
-    B = 1, 4, 16, node-major) and the 200,000-node graph (fp32, 128 node-major
-    features; forward and input gradient)."""
+    B=4, warm: it is launch-bound), the GPT-2-small MLP layers at 90% and 99%
+    (fp32, 1024 tokens, batch-major), the LLaMA-7B-shaped projections with
+    skewed rows (bf16, B = 1, 4, 16, node-major) and the 200,000-node graph
+    (fp32, 128 node-major features; forward and input gradient), all cold
+    but the first."""
     import synth
     out = {}
     log("configs: single layer")
     w = synth.single_layer()
-    out["single_256_s0.9_B4_f32"] = time_config(w.weights[0], 4, False, "batch")
+    out["single_256_s0.9_B4_f32"] = time_config(w.weights[0], 4, False, "batch", cold=False)
     for sp in (0.9, 0.99):
         log(f"configs: gpt2 mlp {sp}")
         wl = synth.gpt2_mlp(sparsity=sp)
@@ -527,74 +631,91 @@ def footprint(N, nnz, B, n_drop, layout):
 
 
 def cpu_baseline(w, X, dY, B, drop_ppm, seconds):
-    """The fp64 oracle, serial on one host core, running the same step on the
-    same layer, repeated until `seconds` of CPU work."""
+    """The fp64 oracle, serial, pinned to one host core (sched_setaffinity),
+    running the same step on the same layer: three runs of whole steps
+    (~seconds / 3 each), the median step time."""
     import oracle
     import synth
     M, K = w.M, w.K
-    v = w.vals_f64()
     x64, g64 = X.f64(), dY.f64()
-    row, col = w.row.copy(), w.col.copy()
-    vals = w.vals.copy()
     n_drop = oracle.drop_count(w.nnz, drop_ppm)
     bytes_step = sum(algo_bytes(op, M, K, w.nnz, B, 2, 2) for op in ("fwd", "bwd_input", "sddmm"))
-    steps, t_total = 0, 0.0
     T = 512
-    while t_total < seconds and steps < 50:
-        t0 = time.perf_counter()
-        oracle.spmm_fwd(M, K, row, col, v, B, x64)
-        oracle.spmm_bwd_input(M, K, row, col, v, B, g64)
-        oracle.sddmm(M, K, row, col, B, g64, x64)
-        out = oracle.prune_regrow(M, K, row, col, vals, "bf16", n_drop, 0, steps + 1)
-        rp = oracle.row_ptr(M, out["row"])
-        cp, _, _ = oracle.csc(K, out["row"], out["col"])
-        oracle.partition(rp, T)
-        oracle.partition(cp, T)
-        t_total += time.perf_counter() - t0
-        row, col, vals = out["row"], out["col"], out["vals"]
-        v = synth.bf16_bits_to_f32(vals).astype(np.float64)
-        steps += 1
-    return {"value": round(bytes_step * steps / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        row, col, vals = w.row.copy(), w.col.copy(), w.vals.copy()
+        step_no, runs = 0, []
+        for _ in range(3):
+            n, t_run = 0, 0.0
+            while t_run < seconds / 3 and n < 20:
+                v = synth.bf16_bits_to_f32(vals).astype(np.float64)
+                t0 = time.perf_counter()
+                oracle.spmm_fwd(M, K, row, col, v, B, x64)
+                oracle.spmm_bwd_input(M, K, row, col, v, B, g64)
+                oracle.sddmm(M, K, row, col, B, g64, x64)
+                step_no += 1
+                out = oracle.prune_regrow(M, K, row, col, vals, "bf16", n_drop, 0, step_no)
+                rp = oracle.row_ptr(M, out["row"])
+                cp, _, _ = oracle.csc(K, out["row"], out["col"])
+                oracle.partition(rp, T)
+                oracle.partition(cp, T)
+                t_run += time.perf_counter() - t0
+                row, col, vals = out["row"], out["col"], out["vals"]
+                n += 1
+            runs.append(t_run / n)
+    finally:
+        os.sched_setaffinity(0, old_aff)
+    t_step = float(np.median(runs))
+    return {"value": round(bytes_step / t_step / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{steps} full steps (fwd, dX, dV, prune/regrow, row/column views and "
-                      f"partitions) of the same {M}x{K} layer, B={B}, fp64 serial C, "
-                      f"{t_total:.1f} s on 1 of {os.cpu_count()} host threads "
-                      f"({platform.processor() or platform.machine()})"}
+            "sample": f"median of 3 runs of whole steps (fwd, dX, dV, prune/regrow, row/column "
+                      f"views and partitions; {step_no} steps, {sum(runs) / 3 * step_no:.1f} s) "
+                      f"of the same {M}x{K} layer, B={B}, fp64 serial C pinned to host core "
+                      f"{core} of {os.cpu_count()} ({platform.processor() or platform.machine()}); "
+                      f"s/step per run " + ", ".join(f"{r:.3f}" for r in runs)}
 
 
-def time_ops_grid(sizes, sparsities, batches, rotate, layouts=("node", "batch")):
-    """Per-op time (HIP events on the launch stream, median over launches)
-    over a grid of sparsity x batch x activation layout."""
-    import synth
+def cold_products(w, X, dY, B, ops=("fwd", "bwd_input", "sddmm"), layout="node"):
+    """Per-launch time of the products on one bf16 layer, cold: rotate over
+    enough device copies that >= 512 MB of each op's data lies between two
+    uses of one copy."""
     import torch
+    op_bytes = {op: algo_bytes(op.replace("_perm", ""), w.M, w.K, w.nnz, B, 2, 2)
+                for op in ops}
+    R = rotation_for(min(op_bytes.values()))
+    insts = make_instances(w, X, dY, B, R, layout)
+    out = {"rotate": R}
+    for op in ops:
+        us = graph_kernel_us(insts, op)
+        b = op_bytes[op]
+        out[op] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                   "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    del insts
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_ops_grid(sizes, sparsities, batches, tag="sweep"):
+    """Cold per-op time (fwd, dX from column-ordered values, dV) of square
+    bf16 layers over size x sparsity x batch, node-major."""
+    import synth
     out = {}
-    for sp in sparsities:
-        for B in batches:
-          w = synth.inference_layer(N=sizes, sparsity=sp, B=B)
-          for layout in (layouts if B > 1 else ("node",)):
-            log(f"grid s={sp} B={B} {layout}")
-            insts = [Instance(w.weights[0], w.X[0], w.dY[0], B, True, 0, layout)
-                     for _ in range(rotate)]
-            n = 30
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
-            for i in range(5):
-                insts[i % rotate].products()
-            torch.cuda.synchronize()
-            for i in range(n):
-                insts[i % rotate].products(ev[i])
-            torch.cuda.synchronize()
-            ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)]
-                           for i in range(n)])
-            wt = w.weights[0]
-            rec = {}
-            for j, op in enumerate(("fwd", "bwd_input", "sddmm")):
-                b = algo_bytes(op, wt.M, wt.K, wt.nnz, B, 2, 2)
-                us = float(np.median(ms[:, j])) * 1e3
-                rec[op] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
-                           "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
-            out[f"s{sp}_B{B}_{layout}"] = rec
-            del insts
-            torch.cuda.empty_cache()
+    for N in sizes:
+        for sp in sparsities:
+            log(f"{tag} N={N} s={sp}: inputs")
+            wl = synth.inference_layer(N=N, sparsity=sp, B=max(batches))
+            w = wl.weights[0]
+            rng = np.random.default_rng(7)
+            for B in batches:
+                log(f"{tag} N={N} s={sp} B={B}")
+                X = synth.activation(rng, B, N, "bf16")
+                dY = synth.activation(rng, B, N, "bf16")
+                rec = cold_products(w, X, dY, B)
+                rec["algo_bytes"] = algo_bytes("fwd", N, N, w.nnz, B, 2, 2)
+                out[f"N{N}_s{sp}_B{B}"] = rec
+            del wl, w
     return out
 
 
@@ -629,6 +750,11 @@ def run_bench(args):
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": n * 4}), flush=True)
         return
+
+    calib = None
+    if args.calibrate:
+        log("calibration floors")
+        calib = calibrate()
 
     N, B, sp = args.size, args.batch, args.sparsity
     log(f"inputs {N}x{N} s={sp} B={B}")
@@ -686,36 +812,88 @@ def run_bench(args):
             rec["algo_bytes"] = b
             rec["GBps"] = round(b / (rec["us_mean"] * 1e3), 1)
         ops[op] = rec
-    prod_us = sum(ops[o]["us_mean"] for o in ("fwd", "bwd_input", "sddmm"))
     value = prod_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # per-launch kernel durations from graph replays (no host gaps), then
-    # the dominant product kernel: the one with the largest duration
-    log("graph-timed product kernels")
-    for op in ("fwd", "bwd_input", "sddmm"):
-        ops[op]["us_kernel"] = round(graph_kernel_us(insts, op), 2)
-        ops[op]["GBps_kernel"] = round(ops[op]["algo_bytes"] / (ops[op]["us_kernel"] * 1e3), 1)
-    # the alternative backward: dX and dV in one pass (snack_spmm_bwd_fused)
-    fb = algo_bytes("bwd_fused", wt.M, wt.K, wt.nnz, B, 2, 2)
-    fus = round(graph_kernel_us(insts, "bwd_fused"), 2)
-    ops["bwd_fused"] = {"us_kernel": fus, "algo_bytes": fb, "GBps_kernel": round(fb / (fus * 1e3), 1),
-                        "us_separate": round(ops["bwd_input"]["us_kernel"]
-                                             + ops["sddmm"]["us_kernel"], 2),
-                        "note": "dX + dV in one call over one index stream (its own minimum "
-                                "bytes); not part of the timed step"}
-    dom = max(("fwd", "bwd_input", "sddmm"), key=lambda o: ops[o]["us_kernel"])
-    # views with no split segment run the wave-per-segment kernels
     plan0 = insts[0].topo.plan
+    if fused and not args.products_only:
+        rb = restructure_bytes(wt.M, wt.K, wt.nnz, 2, plan0.P_row, plan0.P_col)
+        us_r = ops["restructure"]["us_median"]
+        ops["restructure"].update({
+            "algo_bytes": rb, "GBps": round(rb / us_r / 1e3, 1),
+            "frac": round(rb / us_r / 1e3 / HBM_PEAK_GBPS, 4),
+            "model": "COO read and written back (8 + 2 B per connection each way), plan "
+                     "arrays written (offsets, perm, row_t, tiles of both views), "
+                     "column-ordered values written; event-timed call, host spin included"})
+
+    # the layer's own training step: forward, fused backward with the SGD
+    # update of both copies of the values, restructure (snack_prune_regrow_
+    # prepared), over the same rotated instances
+    train = None
+    if fused and not args.products_only:
+        log("training step (fwd, fused backward + SGD, restructure)")
+
+        def tstep(i):
+            inst = insts[i % R]
+            inst.topo.fwd(inst.vals, inst.X, inst.B, inst.lay, out=inst.Y)
+            inst.bwd_fused(lr=1e-3)
+            inst.restructure(None, True)
+
+        for i in range(args.warmup):
+            tstep(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K_):
+            tstep(args.warmup + i)
+        torch.cuda.synchronize()
+        ms_t = (time.perf_counter() - t0) / K_ * 1e3
+        tb = (algo_bytes("fwd", wt.M, wt.K, wt.nnz, B, 2, 2)
+              + algo_bytes("bwd_fused", wt.M, wt.K, wt.nnz, B, 2, 2))
+        train = {"ms_per_step": round(ms_t, 4), "GBps": round(tb / (ms_t * 1e-3) / 1e9, 2),
+                 "algo_bytes": tb,
+                 "note": "fwd + snack_spmm_bwd_fused (dX, dV, SGD on vals and vals_t) + "
+                         "restructure; bytes of the forward and the fused backward"}
+    del insts
+    torch.cuda.empty_cache()
+
+    # cold per-launch kernel durations of the products (>= 512 MB rotated),
+    # then the same with one instance (warm); the dominant product kernel is
+    # the one with the largest cold duration
+    log("cold product kernels")
+    cold = cold_products(wt, w.X[0], w.dY[0], B,
+                         ops=("fwd", "bwd_input", "sddmm", "bwd_input_perm", "bwd_fused"),
+                         layout=args.layout)
+    for op in ("fwd", "bwd_input", "sddmm"):
+        ops[op]["us_kernel"] = cold[op]["us"]
+        ops[op]["GBps_kernel"] = cold[op]["GBps"]
+        ops[op]["frac_kernel"] = cold[op]["frac"]
+    fb = algo_bytes("bwd_fused", wt.M, wt.K, wt.nnz, B, 2, 2)
+    ops["bwd_fused"] = {"us_kernel": cold["bwd_fused"]["us"], "algo_bytes": fb,
+                        "GBps_kernel": round(fb / (cold["bwd_fused"]["us"] * 1e3), 1),
+                        "us_separate": round(cold["bwd_input"]["us"] + cold["sddmm"]["us"], 2),
+                        "note": "dX + dV in one call over one index stream (its own minimum "
+                                "bytes), column-ordered values; not part of the timed step"}
+    ops["bwd_input_perm"] = {"us_kernel": cold["bwd_input_perm"]["us"],
+                             "note": "dX reading the values through perm (snack_spmm_bwd_input)"}
+    log("warm product kernels")
+    warm_inst = make_instances(wt, w.X[0], w.dY[0], B, 1, args.layout)
+    ops_warm = {"cache": "warm (one instance repeated)"}
+    for op in ("fwd", "bwd_input", "sddmm", "bwd_fused"):
+        ops_warm[op] = {"us": round(graph_kernel_us(warm_inst, op), 2)}
+    del warm_inst
+    torch.cuda.empty_cache()
+
+    dom = max(("fwd", "bwd_input", "sddmm"), key=lambda o: ops[o]["us_kernel"])
     split = plan0.has_split_col if dom == "bwd_input" else plan0.has_split_row
-    kname = ({"fwd": "k_wave_spmm (row view)", "bwd_input": "k_wave_spmm (column view)",
-              "sddmm": "k_wave_sddmm"} if not split else
-             {"fwd": "k_seg_spmm (row view)", "bwd_input": "k_seg_spmm (column view)",
-              "sddmm": "k_sddmm"})[dom]
+    kname = ({"fwd": "k_wave_spmm (row view)", "bwd_input": "k_wave_spmm (column view, "
+              "column-ordered values)", "sddmm": "k_wave_sddmm"} if not split else
+             {"fwd": "k_wave_spmm_split (row view)", "bwd_input": "k_wave_spmm_split (column "
+              "view)", "sddmm": "k_wave_sddmm_split"})[dom]
     ach = ops[dom]["algo_bytes"] / (ops[dom]["us_kernel"] * 1e-6) / 1e9
     tag = f"{dom}_square{N}_s{sp}_B{B}_bf16"
     traffic = read_traffic(tag, ops[dom]["algo_bytes"])
     roof = {"bound": "hbm", "kernel": kname, "op": dom, "achieved": round(ach, 1),
-            "us_per_launch": ops[dom]["us_kernel"], "timing": "HIP events around graph replays",
+            "us_per_launch": ops[dom]["us_kernel"],
+            "timing": f"HIP events around graph replays, cold ({cold['rotate']} instances "
+                      f"rotated, >= 512 MB between reuses)",
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
             "traffic": traffic, "algo_bytes_per_launch": ops[dom]["algo_bytes"]}
 
@@ -732,26 +910,28 @@ def run_bench(args):
                       "M": N, "K": N, "nnz": wt.nnz, "batch": B,
                       "layout": "node-major (K x B)" if args.layout == "node" else "batch-major (B x K)",
                       "rotate_instances": R,
-                      "cache": "cold (HBM)" if R > 1 else "warm (Infinity Cache)"},
+                      "cache": "cold (HBM): the step's 20 instances touch ~1.2 GB per rotation"},
            "roofline": roof,
            "ops": ops,
-           "products_only_GBps": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1)}
+           "ops_warm": ops_warm,
+           "products_only_GBps": round(prod_bytes / (sum(ops[o]["us_kernel"] for o in
+                                                         ("fwd", "bwd_input", "sddmm"))
+                                                     * 1e-6) / 1e9, 1)}
+    if train:
+        rec["train_step"] = train
+    if calib:
+        rec["calibration"] = calib
     if args.grid:
-        rec["grid"] = time_ops_grid(N, (0.95, 0.99), (1, 8, 32), R)
-        log("dense baselines")
-        base = dense_baselines(wt, w.X[0], (1, B))
-        for b in (1, B):  # the sparse forward, graph-timed the same way
-            wb = synth.inference_layer(N=N, sparsity=sp, B=b)
-            ib = [Instance(wb.weights[0], wb.X[0], wb.dY[0], b, True, 0, args.layout)
-                  for _ in range(8)]
-            us = graph_kernel_us(ib, "fwd", launches=16, replays=3)
-            base[f"sparse_fwd_B{b}"] = {"us": round(us, 2)}
-            base[f"dense_mask_B{b}"]["sparse_fwd_speedup"] = round(
-                base[f"dense_mask_B{b}"]["us"] / us, 2)
-            base[f"dense_B{b}"]["sparse_fwd_speedup"] = round(base[f"dense_B{b}"]["us"] / us, 2)
-            del ib
-            torch.cuda.empty_cache()
-        rec["baselines"] = base
+        log("grid (cold)")
+        grid = time_ops_grid([N], (0.95, 0.99), (1, 8, 32), tag="grid")
+        rec["grid"] = grid
+        log("dense baselines (cold)")
+        sparse_us = {b: grid[f"N{N}_s{sp}_B{b}"]["fwd"]["us"] for b in (1, B)
+                     if f"N{N}_s{sp}_B{b}" in grid}
+        rec["baselines"] = dense_baselines(wt, w.X[0], (1, B), sparse_us)
+    sizes = [int(x) for x in args.sizes.split(",") if x.strip()]
+    if sizes:
+        rec["sweep"] = time_ops_grid(sizes, (0.95, 0.99), (1, 8, 32))
     if args.graph:
         rec["graph_inference"] = graph_inference()
     if args.configs:
@@ -762,7 +942,7 @@ def run_bench(args):
     rec["footprint"] = footprint(N, wt.nnz, B, 0 if args.products_only else
                                  snk_drop(wt.nnz, args.drop_ppm), args.layout)
     if args.cpu_baseline:
-        log("cpu baseline (oracle)")
+        log("cpu baseline (oracle, one pinned core)")
         rec["cpu_baseline"] = cpu_baseline(wt, w.X[0], w.dY[0], B, args.drop_ppm,
                                            args.cpu_seconds)
     print(json.dumps(rec), flush=True)

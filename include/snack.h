@@ -523,6 +523,30 @@ SNACK_API snack_status snack_gelu_bwd(const float* z, const float* dh, float* dz
 SNACK_API snack_status snack_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dtype, int32_t M,
                              int32_t K, const void* X, int32_t B, void* Y, void* stream);
 
+/*
+ * snack_calibrate -- the benchmark's machine floors, not part of the layer:
+ *   SNACK_CALIB_EMPTY  an empty kernel of n workgroups (launch and drain);
+ *   SNACK_CALIB_READ   read every 16-byte word of buf[0, bytes) once, n
+ *                      workgroups (the last word is a sink that is written
+ *                      only in the improbable case that the words' xor is
+ *                      0x9E3779B9);
+ *   SNACK_CALIB_WRITE  write zeros over buf[0, bytes), n workgroups;
+ *   SNACK_CALIB_CHAIN  write a cycle of 128-byte slots into buf (a
+ *                      full-period linear congruential order over the
+ *                      largest power-of-two count of slots that fits);
+ *   SNACK_CALIB_CHASE  one thread follows n links of that cycle, each load
+ *                      depending on the last (memory latency).
+ * bytes: a multiple of 16 for READ / WRITE.  Asynchronous on `stream`.
+ * Errors: SNACK_E_NULL, SNACK_E_SHAPE (bad kind, size or count).
+ */
+#define SNACK_CALIB_EMPTY 0
+#define SNACK_CALIB_READ 1
+#define SNACK_CALIB_WRITE 2
+#define SNACK_CALIB_CHAIN 3
+#define SNACK_CALIB_CHASE 4
+SNACK_API snack_status snack_calibrate(int32_t kind, void* buf, size_t bytes, int64_t n,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

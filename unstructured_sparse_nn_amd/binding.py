@@ -114,6 +114,7 @@ def _load():
         "snack_gelu_fwd": ([P, P, i64, P], i32),
         "snack_gelu_bwd": ([P, P, P, i64, P], i32),
         "snack_dense_fwd": ([P, P, i32, i32, i32, P, i32, P, P], i32),
+        "snack_calibrate": ([i32, P, sz, i64, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -400,6 +401,14 @@ def snack_dense_fwd(W, mask, M, K, X, B, Y, stream=None, dtype=None):
     dt = _dtype(W, X, Y, dtype=dtype)
     _check(_lib.snack_dense_fwd(_ptr(W), _ptr(mask), dt, M, K, _ptr(X), B, _ptr(Y),
                                 _stream(stream)), "snack_dense_fwd")
+
+
+CALIB_EMPTY, CALIB_READ, CALIB_WRITE, CALIB_CHAIN, CALIB_CHASE = 0, 1, 2, 3, 4
+
+
+def snack_calibrate(kind: int, buf=None, nbytes: int = 0, n: int = 1, stream=None):
+    """Launch one calibration kernel (empty, read, write, chain, chase)."""
+    _check(_lib.snack_calibrate(kind, _ptr(buf), nbytes, n, _stream(stream)), "snack_calibrate")
 
 
 def raw_status(name: str, *args) -> int:

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libsnack.so")
 # longest compiles first (they start first in the worker pool)
 SOURCES = ["wave_spmm_bf16.hip", "wave_spmm_f32.hip", "wave_fused.hip", "wave_sddmm_bf16.hip",
            "wave_sddmm_f32.hip", "spmm.hip", "prune_bitmap.hip", "api.hip", "prims.hip",
-           "prepare.hip", "prune.hip", "aux.hip", "fixed.hip", "wave.hip", "noalloc.hip"]
+           "prepare.hip", "prune.hip", "aux.hip", "fixed.hip", "wave.hip", "noalloc.hip", "calib.hip"]
 ARCH = "gfx950"  # the MI355X (CDNA4); no other target is built
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

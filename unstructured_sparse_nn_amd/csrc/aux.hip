@@ -273,18 +273,129 @@ __global__ __launch_bounds__(64 * DM_WAVES) void k_dense_mfma(const bf16* __rest
   }
 }
 
-// Rows per workgroup grow with the batch tile, so that the staged chunk of X
-// is shared by enough rows (16 rows for 32 batch columns).
+// Small batches (B <= 8) as a weight stream: each wave owns RW rows and the
+// whole batch; per 512-wide step each lane takes 8 consecutive k (16 bytes
+// of bf16 W, 32 of fp32), and U steps' loads of W, of the mask and of X (read
+// from the caches: every wave reads the same X) are all issued before any of
+// them is used (at batch 1 a 4096-wide bf16 row, 8 KB, per wave at once:
+// the whole weight in flight over the GPU).  No LDS, no barrier; the lane
+// partial sums are reduced across the wave at the end.
+template <typename T, bool MASK, int RW, int BT, int U>
+__global__ __launch_bounds__(256) void k_dense_stream(const T* __restrict__ W,
+                                                      const uint8_t* __restrict__ mask, int32_t M,
+                                                      int32_t K, const T* __restrict__ X,
+                                                      int32_t B, T* __restrict__ Y,
+                                                      int32_t vec_ok) {
+  const int wv = threadIdx.x / SNK_WAVE, l = lane_id();
+  const int32_t r0 = (int32_t)(blockIdx.x * 4 + wv) * RW;
+  if (r0 >= M) return;
+  const bool aligned = vec_ok && (K % 8) == 0;
+  float acc[RW][BT];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < BT; ++j) acc[i][j] = 0.f;
+  for (int32_t kc = 0; kc < K; kc += U * DN_KC) {
+    vec<T, 8> w[U][RW], x[U][BT];
+    uint2 m[U][RW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (int64_t)kc + u * DN_KC + l * 8;
+      const bool full = aligned && k + 8 <= K;
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const int32_t r = min(r0 + i, M - 1);  // rows past M add into acc rows never stored
+        const T* p = W + (int64_t)r * K;
+        if (full) {
+          w[u][i] = *reinterpret_cast<const vec<T, 8>*>(p + k);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[u][i].v[e] = k + e < K ? p[k + e] : (T)0;
+        }
+        if (MASK) {
+          const uint8_t* mp = mask + (int64_t)r * K;
+          if (full) {
+            m[u][i] = *reinterpret_cast<const uint2*>(mp + k);
+          } else {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t b = k + e < K ? mp[k + e] : 0u;
+              if (e < 4) lo |= b << (8 * e);
+              else hi |= b << (8 * (e - 4));
+            }
+            m[u][i] = make_uint2(lo, hi);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BT; ++j) {
+        const int32_t b = min(j, B - 1);  // batch columns past B are never stored
+        const T* p = X + (int64_t)b * K;
+        if (full) {
+          x[u][j] = *reinterpret_cast<const vec<T, 8>*>(p + k);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[u][j].v[e] = k + e < K ? p[k + e] : (T)0;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        float wf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wf[e] = elem<T>::to_f(w[u][i].v[e]);
+          if (MASK && (((e < 4 ? m[u][i].x : m[u][i].y) >> (8 * (e & 3))) & 0xFFu) == 0)
+            wf[e] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < BT; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[i][j] = fmaf(wf[e], elem<T>::to_f(x[u][j].v[e]), acc[i][j]);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < BT; ++j)
+      for (int off = 32; off > 0; off >>= 1) acc[i][j] += __shfl_xor(acc[i][j], off, SNK_WAVE);
+  if (l == 0) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int j = 0; j < BT; ++j)
+        if (r0 + i < M && j < B) Y[(int64_t)j * M + r0 + i] = elem<T>::from_f(acc[i][j]);
+  }
+}
+
+// Batches up to 8 take the weight stream; wider ones stage chunks of X in
+// LDS, with rows per workgroup growing with the batch tile, so that the
+// staged chunk is shared by enough rows (16 rows for 32 batch columns).
 template <typename T, bool MASK>
 static void launch_dense(const T* W, const uint8_t* mask, int32_t M, int32_t K, const T* X,
                          int32_t B, T* Y, hipStream_t s) {
-  constexpr int w4 = 4, w16 = 16;  // waves per workgroup
+  constexpr int w16 = 16;  // waves per workgroup
+  const int32_t vec_ok = ((uintptr_t)W % 32 == 0 && (uintptr_t)X % 32 == 0 &&
+                          (uintptr_t)mask % 8 == 0) ? 1 : 0;
+  // one row per wave, four waves per workgroup; the steps in flight shrink
+  // as the batch (and so the X chunks held per step) grows
+  const dim3 g1((unsigned)cdiv(M, 4));
   if (B <= 1) {
-    hipLaunchKernelGGL((k_dense_fwd<T, MASK, 2, 1, 64 * w4>), dim3((unsigned)cdiv(M, 2 * w4), 1),
-                       dim3(64 * w4), 0, s, W, mask, M, K, X, B, Y);
+    hipLaunchKernelGGL((k_dense_stream<T, MASK, 1, 1, 8>), g1, dim3(256), 0, s, W, mask, M, K, X,
+                       B, Y, vec_ok);
+  } else if (B <= 2) {
+    hipLaunchKernelGGL((k_dense_stream<T, MASK, 1, 2, 8>), g1, dim3(256), 0, s, W, mask, M, K, X,
+                       B, Y, vec_ok);
+  } else if (B <= 4) {
+    hipLaunchKernelGGL((k_dense_stream<T, MASK, 1, 4, 4>), g1, dim3(256), 0, s, W, mask, M, K, X,
+                       B, Y, vec_ok);
   } else if (B <= 8) {
-    hipLaunchKernelGGL((k_dense_fwd<T, MASK, 2, 8, 64 * w4>), dim3((unsigned)cdiv(M, 2 * w4), 1),
-                       dim3(64 * w4), 0, s, W, mask, M, K, X, B, Y);
+    hipLaunchKernelGGL((k_dense_stream<T, MASK, 1, 8, 2>), g1, dim3(256), 0, s, W, mask, M, K, X,
+                       B, Y, vec_ok);
   } else {
     hipLaunchKernelGGL((k_dense_fwd<T, MASK, 1, 32, 64 * w16>),
                        dim3((unsigned)cdiv(M, w16), (unsigned)cdiv(B, 32)), dim3(64 * w16), 0, s,

@@ -779,10 +779,12 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   if (staged) {
     __syncthreads();
     const int64_t lim = std::min<int64_t>(nblk_out, nnz - bo.x);
+    // the values with plain stores: the column emitter of a fused prepare
+    // gathers them again right after
     for (int64_t j = t; j < lim; j += WT) {
       __builtin_nontemporal_store(srow[j], &row[bo.x + j]);
       __builtin_nontemporal_store(scol[j], &col[bo.x + j]);
-      __builtin_nontemporal_store(sval[j], &vals[bo.x + j]);
+      vals[bo.x + j] = sval[j];
     }
   }
 }
