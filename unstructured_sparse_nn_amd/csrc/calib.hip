@@ -16,15 +16,18 @@ __global__ void k_calib_empty() {}
 // non-temporal loads in flight per thread); a word is stored only if the
 // running xor hits an improbable value, so no load can be dropped and nothing
 // is written in practice.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void k_calib_read(const uint4* __restrict__ p, int64_t n,
                                                     uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * 256;
+  const u32x4* __restrict__ q = reinterpret_cast<const u32x4*>(p);
   uint32_t acc = 0;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   for (; i + 7 * stride < n; i += 8 * stride) {
-    uint4 a[8];
+    u32x4 a[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = __builtin_nontemporal_load(&p[i + u * stride]);
+    for (int u = 0; u < 8; ++u) a[u] = __builtin_nontemporal_load(&q[i + u * stride]);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
   }
