@@ -225,6 +225,24 @@ def test_square_node_major_benchmarked_path(orc, sp, Bsz):
     assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
 
 
+LDS_CASES = [
+    # M, K, nnz, B, dtype: layers with >= 16,384 segments whose whole
+    # node-major input fits in 64 KB of LDS take the LDS-staged wave kernel
+    (16384, 3001, 200000, 1, "bf16"),    # forward staged; 6,002-byte input (ragged tail)
+    (3001, 20000, 300000, 4, "f32"),     # input gradient staged (dY: 3,001 x 4 fp32, 48 KB)
+    (32768, 2048, 1000000, 16, "bf16"),  # forward staged, exactly 64 KB, two lanes per entry
+    (32768, 32768, 10737418, 1, "bf16"),  # 32768^2 at 99%: the size sweep's largest layer
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt", LDS_CASES)
+def test_wave_lds_staged_inputs(orc, M, K, nnz, Bsz, dt):
+    w = synth.random_case(24, M, K, nnz, Bsz, dt, "node")
+    topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, "node", Bsz, repeat_check=True,
+                        flags=B.PLAN_NODE_MAJOR_ONLY)
+    assert topo.plan.has_split_row == 0
+
+
 @pytest.mark.parametrize("which", ["up", "down"])
 @pytest.mark.parametrize("Bsz", [1, 4, 16])
 def test_llama_projection_configs(orc, which, Bsz):

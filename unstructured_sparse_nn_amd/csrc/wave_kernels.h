@@ -159,6 +159,40 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
                                                 Xt, Y, S, B, long_len);
 }
 
+// Layers whose whole node-major input fits in LDS (F * B elements of at most
+// WL_LDS bytes: batch 1 up to 32,768 bf16 features) and has many segments:
+// each 16-wave workgroup copies the input into LDS once (16-byte copies, one
+// barrier), then its waves take segments in a grid-stride loop and gather
+// from LDS.  On large layers the gathers are otherwise scattered L2 requests
+// (one per entry at batch 1), which bound the launch well below the entry
+// stream; from LDS they cost a few LDS cycles per 64 entries.  One batch pass
+// (B <= LPE * CH); no split segments.
+constexpr int WL_THREADS = 1024;
+constexpr int WL_LDS = 64 * 1024;
+constexpr int WL_MIN_SEGMENTS = 16384;
+
+template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
+__global__ __launch_bounds__(WL_THREADS) void k_wave_spmm_lds(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
+    T* __restrict__ Y, int32_t S, int32_t B, int64_t x_elems) {
+  extern __shared__ uint4 xs_raw[];
+  const int64_t nbytes = x_elems * (int64_t)sizeof(T);
+  const int64_t n16 = nbytes / 16;  // whole 16-byte words (Xt is 16-byte aligned)
+  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(Xt);
+  for (int64_t i = threadIdx.x; i < n16; i += WL_THREADS) xs_raw[i] = src[i];
+  T* xs = reinterpret_cast<T*>(xs_raw);
+  for (int64_t i = n16 * (16 / (int64_t)sizeof(T)) + threadIdx.x; i < x_elems; i += WL_THREADS)
+    xs[i] = Xt[i];  // the tail past the last whole word
+  __syncthreads();
+  const int32_t waves = (int32_t)gridDim.x * (WL_THREADS / SNK_WAVE);
+  for (int32_t s = __builtin_amdgcn_readfirstlane((int32_t)blockIdx.x * (WL_THREADS / SNK_WAVE) +
+                                                  (int32_t)(threadIdx.x / SNK_WAVE));
+       s < S; s += waves)
+    wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(s, ptr, idx, perm, vals, xs, Y, S, B,
+                                                  INT32_MAX);
+}
+
 // Both halves of a view with split segments in one launch, so that they
 // overlap: workgroups below pblk (a multiple of NUM_XCD) run the tile pieces
 // (wave_pieces_of), the rest the segments of < long_len entries (as
@@ -325,6 +359,30 @@ __device__ __forceinline__ void wave_sddmm_pieces_of(
                                    part_nz[p + 1], lane, slot, b0, dV);
 }
 
+// The value gradient with the whole node-major X in LDS (the conditions of
+// k_wave_spmm_lds): X staged once per 16-wave workgroup, rows taken in a
+// grid-stride loop, each entry's X chunk read from LDS; the row's dY chunk
+// is read from memory as in k_wave_sddmm.
+template <typename T, int CH, int LPE>
+__global__ __launch_bounds__(WL_THREADS) void k_wave_sddmm_lds(
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
+    const T* __restrict__ dYt, const T* __restrict__ Xt, T* __restrict__ dV, int32_t S,
+    int32_t B, int64_t x_elems) {
+  extern __shared__ uint4 xs_raw[];
+  const int64_t n16 = x_elems * (int64_t)sizeof(T) / 16;
+  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(Xt);
+  for (int64_t i = threadIdx.x; i < n16; i += WL_THREADS) xs_raw[i] = src[i];
+  T* xs = reinterpret_cast<T*>(xs_raw);
+  for (int64_t i = n16 * (16 / (int64_t)sizeof(T)) + threadIdx.x; i < x_elems; i += WL_THREADS)
+    xs[i] = Xt[i];
+  __syncthreads();
+  const int32_t waves = (int32_t)gridDim.x * (WL_THREADS / SNK_WAVE);
+  for (int32_t s = __builtin_amdgcn_readfirstlane((int32_t)blockIdx.x * (WL_THREADS / SNK_WAVE) +
+                                                  (int32_t)(threadIdx.x / SNK_WAVE));
+       s < S; s += waves)
+    wave_sddmm_of<T, CH, LPE, false>(s, ptr, idx, dYt, xs, dV, S, B, INT32_MAX);
+}
+
 // Both halves of a view with split rows in one launch, so that they overlap:
 // workgroups below pblk run the tile pieces, the rest the rows of < long_len
 // entries.
@@ -359,6 +417,17 @@ static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int
   const unsigned passes = (unsigned)cdiv(B, LPE * CH);
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
   const int32_t sblk = xb ? xb * NUM_XCD : nblk;
+  const int64_t x_elems = (int64_t)v.F * B;
+  if (!v.has_split && passes == 1 && v.S >= WL_MIN_SEGMENTS &&
+      x_elems * (int64_t)sizeof(T) <= WL_LDS && (uintptr_t)Xt % 16 == 0) {
+    // two workgroups per CU (their LDS), or one per 16 segments if fewer
+    const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
+    hipLaunchKernelGGL((k_wave_spmm_lds<T, CH, LPE, PERM, NODE_OUT, ACT>), dim3((unsigned)wl_blk),
+                       dim3(WL_THREADS), (size_t)align_up((size_t)(x_elems * sizeof(T)), 16), s,
+                       v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B,
+                       x_elems);
+    return;
+  }
   if (!v.has_split) {
     hipLaunchKernelGGL((k_wave_spmm<T, CH, LPE, PERM, NODE_OUT, ACT>), dim3((unsigned)sblk, passes),
                        dim3(WV_THREADS), 0, s, v.ptr, v.idx, v.perm, (const T*)vals,
@@ -424,6 +493,12 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
   const int32_t sblk = (int32_t)cdiv(v.S, WV_THREADS / SNK_WAVE);
   const int32_t pblk = (int32_t)cdiv(v.P, WV_THREADS / SNK_WAVE);
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
+  // X in LDS (see k_wave_spmm_lds): one batch pass, many rows, no split row
+  const int64_t x_elems = (int64_t)v.F * B;
+  const bool lds_ok = !v.has_split && v.S >= WL_MIN_SEGMENTS &&
+                      x_elems * (int64_t)sizeof(T) <= WL_LDS && (uintptr_t)Xt % 16 == 0;
+  const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
+  const size_t lds_bytes = align_up((size_t)(x_elems * sizeof(T)), 16);
 #define SNK_WSD1(L, MULTI)                                                                      \
   do {                                                                                          \
     if (!v.has_split)                                                                           \
@@ -435,10 +510,17 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
                          dim3(WV_THREADS), 0, s, v.ptr, v.idx, v.part_seg, v.part_nz, v.cut,    \
                          (const T*)dYt, (const T*)Xt, (T*)dV, v.S, v.P, B, long_len, pblk);     \
   } while (0)
-#define SNK_WSD(L)                                             \
-  do {                                                         \
-    if (B > (L) * CH) SNK_WSD1(L, true);                       \
-    else SNK_WSD1(L, false);                                   \
+#define SNK_WSD(L)                                                                       \
+  do {                                                                                   \
+    if (B > (L) * CH) {                                                                  \
+      SNK_WSD1(L, true);                                                                 \
+    } else if (lds_ok) {                                                                 \
+      hipLaunchKernelGGL((k_wave_sddmm_lds<T, CH, L>), dim3((unsigned)wl_blk),           \
+                         dim3(WL_THREADS), lds_bytes, s, v.ptr, v.idx, (const T*)dYt,    \
+                         (const T*)Xt, (T*)dV, v.S, B, x_elems);                        \
+    } else {                                                                             \
+      SNK_WSD1(L, false);                                                                \
+    }                                                                                    \
   } while (0)
   switch (lpe) {
     case 1: SNK_WSD(1); return true;
