@@ -435,25 +435,61 @@ __global__ __launch_bounds__(MP_MAX_THREADS) void k_seg_spmm(
 // the same segment.  The pieces start at tile f: walk back over inner cuts of
 // the same segment.  out = sum of the carry-out slots of tiles f..p-1 (in
 // tile order) + the final piece held by tile p.
+// One wave per tile (four per workgroup) and per 64 batch columns
+// (blockIdx.y): a tile that finishes nothing exits after one load.  A
+// finishing tile finds f with one 64-tile window of cut flags and segments
+// per round (a ballot), not one dependent load per piece; then its lanes take
+// batch columns and add the pieces, eight loads in flight.
+constexpr int FX_WAVES = 4;
 template <typename T, bool NODE_OUT, int ACT = ACT_NONE>
-__global__ __launch_bounds__(256) void k_fixup(const int32_t* __restrict__ part_seg,
-                                               const int32_t* __restrict__ cut,
-                                               const float* __restrict__ carry, T* __restrict__ Y,
-                                               int32_t S, int32_t B, int32_t P) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)P * B) return;
-  const int32_t p = (int32_t)(i / B), b = (int32_t)(i % B);
-  if (!cut[p]) return;
+__global__ __launch_bounds__(64 * FX_WAVES) void k_fixup(const int32_t* __restrict__ part_seg,
+                                                         const int32_t* __restrict__ cut,
+                                                         const float* __restrict__ carry,
+                                                         T* __restrict__ Y, int32_t S, int32_t B,
+                                                         int32_t P) {
+  const int32_t p = __builtin_amdgcn_readfirstlane(
+      (int32_t)blockIdx.x * FX_WAVES + (int32_t)(threadIdx.x / SNK_WAVE));
+  if (p >= P || !cut[p]) return;
   const int32_t s = part_seg[p];
   if (p + 1 < P && cut[p + 1] && part_seg[p + 1] == s) return;
-  int32_t f = p - 1;
-  while (f >= 1 && cut[f] && part_seg[f] == s) --f;
-  float tot = 0.f;
-  for (int32_t q = f; q < p; ++q) tot += carry[(int64_t)q * B + b];
-  tot += carry[((int64_t)P + p) * B + b];
-  tot = apply_act(tot, ACT);
-  if (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
-  else Y[(int64_t)b * S + s] = elem<T>::from_f(tot);
+  const int lane = lane_id();
+  // f = the last q < p (walking back) at which the run of inner cuts of
+  // segment s stops: q < 1, or cut[q] == 0, or part_seg[q] != s
+  int32_t f = 0;
+  for (int32_t top = p - 1;; top -= SNK_WAVE) {
+    const int32_t q = top - lane;
+    const int32_t qc = q < 0 ? 0 : q;  // loads stay in bounds; q < 1 stops the run anyway
+    const bool cont = q >= 1 && cut[qc] != 0 && part_seg[qc] == s;
+    const uint64_t stop = __ballot(!cont);
+    if (stop) {
+      f = top - (int32_t)__builtin_ctzll(stop);
+      break;
+    }
+  }
+  f = __builtin_amdgcn_readfirstlane(f < 0 ? 0 : f);
+  constexpr int U = 8;
+  for (int32_t b = (int32_t)blockIdx.y * SNK_WAVE + lane; b < B;
+       b += (int32_t)gridDim.y * SNK_WAVE) {
+    float tot = 0.f;
+    int32_t q = f;
+    for (; q + U <= p; q += U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = carry[(int64_t)(q + u) * B + b];
+#pragma unroll
+      for (int u = 0; u < U; ++u) tot += v[u];
+    }
+    for (; q < p; ++q) tot += carry[(int64_t)q * B + b];
+    tot += carry[((int64_t)P + p) * B + b];
+    tot = apply_act(tot, ACT);
+    if (NODE_OUT) Y[(int64_t)s * B + b] = elem<T>::from_f(tot);
+    else Y[(int64_t)b * S + s] = elem<T>::from_f(tot);
+  }
+}
+
+// Grid of the fix-up: tiles over x, 64-column batch chunks over y.
+static dim3 fixup_grid(const seg_view& v, int32_t B) {
+  return dim3((unsigned)cdiv(v.P, FX_WAVES), (unsigned)std::min<int64_t>(cdiv(B, SNK_WAVE), 64));
 }
 
 // RC: entries a group gathers per round.
@@ -718,11 +754,9 @@ static void launch_t_act(const seg_view& v, const void* vals, const void* Xt, in
                        dim3(sh.threads), lds, s, v.ptr, v.idx, v.perm, (const T*)vals,
                        v.part_seg, v.part_nz, (const T*)Xt, (T*)Y, carry, v.S, B, v.P,
                        sh.g_log2, v.tile, xt);
-  if (v.has_split) {
-    int64_t n = (int64_t)v.P * B;
-    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
-                       s, v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
-  }
+  if (v.has_split)
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT>), fixup_grid(v, B), dim3(64 * FX_WAVES), 0, s,
+                       v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
 }
 
 template <typename T, int CH, bool NODE_OUT, bool PERM>
@@ -764,14 +798,13 @@ static void launch_dt(const seg_view& v, const void* vals, const void* Xt, bool 
 template <typename T, bool NODE_OUT>
 static void fixup_t(const seg_view& v, int32_t act, const float* carry, void* Y, int32_t B,
                     hipStream_t s) {
-  const int64_t n = (int64_t)v.P * B;
-  const dim3 g((unsigned)cdiv(n, 256));
+  const dim3 g = fixup_grid(v, B);
   if (act == ACT_RELU)
-    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_RELU>), g, dim3(256), 0, s, v.part_seg, v.cut,
-                       carry, (T*)Y, v.S, B, v.P);
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_RELU>), g, dim3(64 * FX_WAVES), 0, s,
+                       v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
   else
-    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_NONE>), g, dim3(256), 0, s, v.part_seg, v.cut,
-                       carry, (T*)Y, v.S, B, v.P);
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT, ACT_NONE>), g, dim3(64 * FX_WAVES), 0, s,
+                       v.part_seg, v.cut, carry, (T*)Y, v.S, B, v.P);
 }
 
 void launch_fixup(const seg_view& v, snack_dtype dt, bool node_out, int32_t act,
@@ -819,11 +852,9 @@ static void launch_fused_t(const seg_view& v, void* vals, const void* dYt, const
                      v.ptr, v.idx, v.perm, (const T*)vals, v.part_seg, v.part_nz, (const T*)dYt,
                      (T*)dX, carry, v.S, B, v.P, sh.g_log2, v.tile, xt, (const T*)Xt, (T*)dV,
                      lr != 0.f ? (T*)vals : nullptr, lr);
-  if (v.has_split) {
-    int64_t n = (int64_t)v.P * B;
-    hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+  if (v.has_split)
+    hipLaunchKernelGGL((k_fixup<T, NODE_OUT>), fixup_grid(v, B), dim3(64 * FX_WAVES), 0, s,
                        v.part_seg, v.cut, carry, (T*)dX, v.S, B, v.P);
-  }
 }
 
 template <typename T, int CH>

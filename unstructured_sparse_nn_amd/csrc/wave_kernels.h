@@ -119,11 +119,16 @@ __device__ __forceinline__ void wave_pieces_of(
   if (c1) piece((c0 && s0 == s1) ? part_nz[p] : ptr[s1], part_nz[p + 1], carry + (int64_t)p * B);
 }
 
+// Segment s of the pass blockIdx.y (batch columns b0 = blockIdx.y * LPE * CH
+// + ...).  The gathered rows are read from Xs with row stride xstride, Xs
+// holding the batch columns from xcol0 on: the node-major input itself
+// (xstride = B, xcol0 = 0) or a copy of it, or of the pass's columns, in LDS.
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 __device__ __forceinline__ void wave_spmm_of(
     int32_t s, const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
-    T* __restrict__ Y, int32_t S, int32_t B, int32_t long_len) {
+    const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xs,
+    T* __restrict__ Y, int32_t S, int32_t B, int32_t long_len, int32_t xstride,
+    int32_t xcol0 = 0) {
   constexpr int EPI = SNK_WAVE / LPE;  // entries per gather round
   static_assert(CH <= EPI, "reduce-scatter needs CH <= 64 / LPE");
   if (s >= S) return;
@@ -132,13 +137,14 @@ __device__ __forceinline__ void wave_spmm_of(
   const int sub = lane % LPE;
   const int32_t b0 = (int32_t)blockIdx.y * (LPE * CH) + sub * CH;
   const bool bvalid = b0 < B;
-  const T* __restrict__ xb = Xt + (bvalid ? b0 : 0);  // lanes past the batch read column 0
+  // lanes past the batch read the first column
+  const T* __restrict__ xb = Xs + (bvalid ? b0 - xcol0 : 0);
   const int32_t a = ptr[s], e = ptr[s + 1];
 
   if (e - a >= long_len) return;  // a split segment: its tile pieces are summed elsewhere
 
   float acc[CH];
-  spmm_range<T, CH, LPE, PERM>(idx, perm, vals, xb, B, a, e, lane, slot, acc);
+  spmm_range<T, CH, LPE, PERM>(idx, perm, vals, xb, xstride, a, e, lane, slot, acc);
   const int c = reduce_scatter<CH, LPE>(acc, lane);
   // lanes whose slot bits below the scattered ones are zero write
   constexpr int LOW = EPI / CH;  // slot values sharing one column after the scatter
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
     const int32_t* __restrict__ perm, const T* __restrict__ vals, const T* __restrict__ Xt,
     T* __restrict__ Y, int32_t S, int32_t B, int32_t xcd_blocks, int32_t long_len) {
   wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(wave_segment(xcd_blocks), ptr, idx, perm, vals,
-                                                Xt, Y, S, B, long_len);
+                                                Xt, Y, S, B, long_len, B);
 }
 
 // Layers whose whole node-major input fits in LDS (F * B elements of at most
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(WL_THREADS) void k_wave_spmm_lds(
                                                   (int32_t)(threadIdx.x / SNK_WAVE));
        s < S; s += waves)
     wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(s, ptr, idx, perm, vals, xs, Y, S, B,
-                                                  INT32_MAX);
+                                                  INT32_MAX, B);
 }
 
 // Both halves of a view with split segments in one launch, so that they
@@ -216,7 +222,8 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm_split(
   const int32_t sb = bx - pblk;
   const int32_t blk = xcd_blocks > 0 ? (sb % NUM_XCD) * xcd_blocks + sb / NUM_XCD : sb;
   const int32_t s = __builtin_amdgcn_readfirstlane(blk * (WV_THREADS / SNK_WAVE) + w);
-  wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(s, ptr, idx, perm, vals, Xt, Y, S, B, long_len);
+  wave_spmm_of<T, CH, LPE, PERM, NODE_OUT, ACT>(s, ptr, idx, perm, vals, Xt, Y, S, B, long_len,
+                                                B);
 }
 
 // The value gradient of NR rounds.  One batch pass (B <= LPE * CH): every
