@@ -72,8 +72,12 @@ typedef int32_t snack_status;
 #define SNACK_E_HIP (-11)          /* a HIP launch or runtime call failed */
 #define SNACK_E_NOT_PREPARED (-12) /* the plan has not been prepared */
 
-typedef enum { SNACK_F32 = 0, SNACK_BF16 = 1 } snack_dtype;
-typedef enum { SNACK_BATCH_MAJOR = 0, SNACK_NODE_MAJOR = 1 } snack_layout;
+/* Element type and activation layout are plain int32 arguments (any value
+ * may be passed and is checked: SNACK_E_DTYPE / SNACK_E_LAYOUT). */
+typedef int32_t snack_dtype;
+enum { SNACK_F32 = 0, SNACK_BF16 = 1 };
+typedef int32_t snack_layout;
+enum { SNACK_BATCH_MAJOR = 0, SNACK_NODE_MAJOR = 1 };
 
 /* Derived arrays of a prepared plan (see snack_plan_array). */
 typedef enum {

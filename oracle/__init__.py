@@ -20,20 +20,28 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
+# SNACK_ORACLE_SANITIZE=1 (set by the sanitizer test for its child process):
+# load the AddressSanitizer + UndefinedBehaviorSanitizer build instead
+_SANITIZE = os.environ.get("SNACK_ORACLE_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "liboracle_asan.so" if _SANITIZE else "liboracle.so")
 
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into liboracle.so (serial, no fast-math)."""
-    if force or not os.path.exists(_SO):
-        tmp = _SO + ".tmp"
+def build(force: bool = True, sanitize: bool = _SANITIZE) -> str:
+    """Compile oracle.c with gcc into liboracle.so (serial, no fast-math); with
+    sanitize, into liboracle_asan.so with -fsanitize=address,undefined (no
+    recovery: the first report aborts)."""
+    so = os.path.join(_HERE, "liboracle_asan.so" if sanitize else "liboracle.so")
+    if force or not os.path.exists(so):
+        tmp = so + ".tmp"
+        extra = (["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer"] if sanitize else [])
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                        "-fno-fast-math", "-o", tmp, _SRC, "-lm"], check=True)
-        os.replace(tmp, _SO)
-    return _SO
+                        "-fno-fast-math", *extra, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, so)
+    return so
 
 
 def _load():

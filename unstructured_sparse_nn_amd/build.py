@@ -53,5 +53,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Sources whose host code is more than kernel launches: argument checks and
+# plan layout, the fixed-pattern code generator, the static workspace, the
+# calibration entry point.
+HOST_HEAVY = ["api.hip", "fixed.hip", "noalloc.hip", "calib.hip"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libsnack.so in out_dir with the host code of HOST_HEAVY built with
+    AddressSanitizer and UndefinedBehaviorSanitizer (-Xarch_host: device code
+    unchanged) and the other objects taken from the regular build in _build,
+    for running the host-side ABI tests under the sanitizers.  Needs a
+    regular build first."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = []
+    for f in ("-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fno-omit-frame-pointer", "-g"):
+        san += ["-Xarch_host", f]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        r = subprocess.run([HIPCC, *CFLAGS, *san, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized host) failed for {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(len(HOST_HEAVY)) as ex:
+        objs = list(ex.map(one, HOST_HEAVY))
+    for src in SOURCES:
+        if src not in HOST_HEAVY:
+            obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+            if not os.path.exists(obj):
+                raise FileNotFoundError(obj)
+            objs.append(obj)
+    lib = os.path.join(out_dir, "libsnack.so")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+                        "-fsanitize=address,undefined", "-o", lib, *objs, "-lhiprtc"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized host) failed:\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
