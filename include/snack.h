@@ -316,6 +316,35 @@ SNACK_API snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, 
                                   float lr, void* stream);
 
 /*
+ * snack_spmm_bwd_fused_adam -- snack_spmm_bwd_fused with an Adam step
+ * (Kingma & Ba, "Adam: A Method for Stochastic Optimization", ICLR 2015,
+ * Algorithm 1) in place of SGD: with g_k the fp32 sum dV_k before rounding,
+ *   m_k <- beta1 m_k + (1 - beta1) g_k,   v_k <- beta2 v_k + (1 - beta2) g_k^2,
+ *   vals[k] <- RNE(vals[k] - lr (m_k c1) / (sqrt(v_k c2) + eps)),
+ * c1 = 1 / (1 - beta1^step), c2 = 1 / (1 - beta2^step) (in double on the
+ * host).  m_t and v_t (fp32, nnz each) hold the moments in the plan's column
+ * order (entry i of the column view, as vals_t), caller-owned, zero before
+ * step 1, read and written coalesced; they follow the column order of the
+ * plan, so a restructure (which reorders and replaces entries) leaves them
+ * to the caller to reset.  vals_t (nullable), dX, dvals (nullable): as for
+ * snack_spmm_bwd_fused.  Runs in the one-wave-per-column form only: a column
+ * view with columns split over tiles, or a batch that one pass does not
+ * cover (odd batches above 16), gives SNACK_E_SHAPE before anything is
+ * launched.  Errors: as snack_spmm_bwd_fused; SNACK_E_NULL (adam, X, or the
+ * moments missing), SNACK_E_SHAPE (B < 1 or B > 32, step < 1, a beta outside
+ * [0, 1), eps < 0), SNACK_E_NAN (a hyperparameter NaN or infinite).
+ */
+typedef struct snack_adam {
+  float lr, beta1, beta2, eps;
+  int32_t step;  /* t >= 1 */
+} snack_adam;
+SNACK_API snack_status snack_spmm_bwd_fused_adam(const snack_plan* plan, void* vals, void* vals_t,
+                                                 snack_dtype dtype, const void* X, const void* dY,
+                                                 snack_layout layout, int32_t B, void* dX,
+                                                 void* dvals, float* m_t, float* v_t,
+                                                 const snack_adam* adam, void* stream);
+
+/*
  * snack_drop_count -- number of connections one restructuring step
  * replaces: round half up of nnz * frac_ppm / 10^6 (frac in parts per
  * million).  Returns -1 for negative arguments.

@@ -217,6 +217,20 @@ def prune_regrow(M, K, row, col, vals, dtype, n_drop, seed, step):
             "grown": gl[:n_drop].copy()}
 
 
+def adam_step(w, g, m, v, lr, beta1, beta2, eps, step):
+    """One Adam step (Kingma & Ba, "Adam: A Method for Stochastic
+    Optimization", ICLR 2015, Algorithm 1) in fp64 on flat arrays:
+        m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2,
+        w <- w - lr * (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps).
+    Returns (w, m, v); nothing is rounded."""
+    w, g, m, v = (np.asarray(a, dtype=np.float64) for a in (w, g, m, v))
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    mh = m / (1.0 - beta1 ** step)
+    vh = v / (1.0 - beta2 ** step)
+    return w - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
 def memory_by_definition(M: int, K: int, nnz: int, elem_bytes: int, max_batch: int) -> dict:
     """Bytes of the tensors whose size the layer's definition fixes (SNACK
     abstract: the sparse layer stores only its nonzero connections; the

@@ -675,6 +675,79 @@ def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
         assert np.all(np.abs(new - exp) <= lr * tol * Sv + ulp * np.abs(exp) + 1e-30)
 
 
+@pytest.mark.parametrize("dt,layout,Bsz,use_vt", [("f32", "node", 8, True),
+                                                   ("f32", "batch", 5, False),
+                                                   ("bf16", "node", 32, True)])
+def test_bwd_fused_adam(orc, dt, layout, Bsz, use_vt):
+    """Three Adam steps through the fused backward against the oracle's step
+    (Kingma & Ba, Algorithm 1).  fp32: the returned dV is the fp32 gradient
+    sum itself, so the oracle steps from it and the moments and values must
+    agree to fp32 rounding; bf16: the moments against the oracle's exact
+    gradient within the products' tolerance carried through the step."""
+    w = synth.random_case(25, 512, 384, 20000, Bsz, dt, layout)
+    wt = w.weights[0]
+    lay = B.NODE_MAJOR if layout == "node" else B.BATCH_MAJOR
+    topo = topology(wt, Bsz)
+    assert topo.plan.has_split_col == 0
+    X, dY = to_dev(w.X[0].data, dt), to_dev(w.dY[0].data, dt)
+    vals = to_dev(wt.vals, dt)
+    vt = topo.gather_vals_t(vals) if use_vt else None
+    m_t = torch.zeros(wt.nnz, device="cuda")
+    v_t = torch.zeros(wt.nnz, device="cuda")
+    _, perm, _ = orc.csc(wt.K, wt.row, wt.col)
+    # the ABI takes the hyperparameters as fp32: the oracle steps with those values
+    lr, b1, b2, eps = (float(np.float32(x)) for x in (1e-3, 0.9, 0.999, 1e-8))
+    m64, v64 = np.zeros(wt.nnz), np.zeros(wt.nnz)
+    gref, Sg = orc.sddmm(wt.M, wt.K, wt.row, wt.col, Bsz, w.dY[0].f64(), w.X[0].f64(),
+                         layout == "node")
+    for t in (1, 2, 3):
+        dX = torch.empty(Bsz * wt.K, dtype=torch_dtype(dt), device="cuda")
+        dV = torch.empty(wt.nnz, dtype=torch_dtype(dt), device="cuda")
+        prev = from_dev(vals, dt)
+        snk.snack_spmm_bwd_fused_adam(topo.plan, vals, X, dY, lay, Bsz, dX, dV, m_t, v_t, lr, t,
+                                      b1, b2, eps, vals_t=vt)
+        got_v, got_m = from_dev(vals, dt), m_t.cpu().numpy().astype(np.float64)[np.argsort(perm)]
+        got_s = v_t.cpu().numpy().astype(np.float64)[np.argsort(perm)]
+        assert_within(from_dev(dV, dt), gref, Sg, dt, f"adam step {t} dV")
+        if use_vt:
+            assert np.array_equal(bits_of(vt, dt), bits_of(vals, dt)[perm])
+        if dt == "f32":  # step the oracle from the GPU's own fp32 gradient
+            w_ref, m64, v64 = orc.adam_step(prev, from_dev(dV, dt), m64, v64, lr, b1, b2, eps, t)
+            np.testing.assert_allclose(got_m, m64, rtol=4e-6, atol=1e-12)
+            np.testing.assert_allclose(got_s, v64, rtol=4e-6, atol=1e-15)
+            assert np.all(np.abs(got_v - w_ref) <= 4 * 2.0 ** -24 * np.abs(w_ref) + lr * 1e-4)
+        else:  # the moments against the exact gradient, errors carried through the step
+            w_ref, m64, v64 = orc.adam_step(prev, gref, m64, v64, lr, b1, b2, eps, t)
+            tol_g = 1e-2 * Sg
+            assert np.all(np.abs(got_m - m64) <= tol_g + 1e-6 * np.abs(m64) + 1e-30)
+            assert np.all(np.abs(got_s - v64) <= 2 * np.abs(gref) * tol_g + tol_g ** 2
+                          + 1e-6 * v64 + 1e-30)
+            assert np.all(np.abs(got_v - w_ref) <= 2.0 ** -7 * np.abs(w_ref) + 3 * lr)
+            m64, v64 = got_m, got_s  # continue from the GPU's moments
+
+
+def test_bwd_fused_adam_rejections():
+    w = synth.random_case(26, 80, 40, 900, 4, "f32")
+    wt = w.weights[0]
+    X, dY = to_dev(w.X[0].data, "f32"), to_dev(w.dY[0].data, "f32")
+    dX = torch.empty(4 * 40, device="cuda")
+    m = torch.zeros(wt.nnz, device="cuda")
+    vals = to_dev(wt.vals, "f32")
+    split = topology(wt, 4, tile=8)  # columns of ~22 entries over 8-item tiles
+    assert split.plan.has_split_col == 1
+    for topo, kw, status in ((split, {}, -2),
+                             (topology(wt, 4), {"step": 0}, -2),
+                             (topology(wt, 4), {"lr": float("nan")}, -7)):
+        args = dict(lr=1e-3, step=1)
+        args.update(kw)
+        before = vals.clone()
+        with pytest.raises(snk.SnackError) as e:
+            snk.snack_spmm_bwd_fused_adam(topo.plan, vals, X, dY, B.BATCH_MAJOR, 4, dX, None, m,
+                                          m.clone(), args["lr"], args["step"])
+        assert e.value.status == status
+        assert torch.equal(vals, before)
+
+
 def test_bwd_fused_rejects_wide_batch_and_bad_lr():
     w = synth.random_case(17, 64, 48, 500, 33, "f32")
     wt = w.weights[0]

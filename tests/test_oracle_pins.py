@@ -469,3 +469,30 @@ def test_memory_by_definition_matches_allocated_arrays(orc, args, _):
     if (M, K, s) == (4096, 4096, 4):
         assert (got["coo"] + got["value_grad"]) * 5 == pytest.approx(
             got["dense_weight"] + got["dense_grad"], rel=1e-6)
+
+
+# ------------------------------------------------------------ Adam
+def test_adam_first_step_is_lr_times_sign(orc):
+    """From zero moments the bias-corrected first step is g / (|g| + eps):
+    lr * sign(g) when |g| >> eps (Kingma & Ba, Algorithm 1, at t = 1)."""
+    rng = np.random.default_rng(3)
+    g = rng.standard_normal(1000)
+    w = rng.standard_normal(1000)
+    z = np.zeros(1000)
+    w1, m1, v1 = orc.adam_step(w, g, z, z, 1e-3, 0.9, 0.999, 1e-8, 1)
+    np.testing.assert_allclose(m1, 0.1 * g, rtol=1e-13)
+    np.testing.assert_allclose(v1, 0.001 * g * g, rtol=1e-13)
+    np.testing.assert_allclose(w - w1, 1e-3 * g / (np.abs(g) + 1e-8), rtol=1e-12)
+
+
+def test_adam_constant_gradient_keeps_unit_steps(orc):
+    """With a constant gradient the bias corrections make every step
+    lr * g / (|g| + eps) (m_hat = g, v_hat = g^2 at every t)."""
+    g = np.array([0.5, -2.0, 3e-3])
+    w = np.zeros(3)
+    m = np.zeros(3)
+    v = np.zeros(3)
+    for t in range(1, 8):
+        w_new, m, v = orc.adam_step(w, g, m, v, 0.01, 0.9, 0.99, 1e-12, t)
+        np.testing.assert_allclose(w - w_new, 0.01 * np.sign(g), rtol=1e-9)
+        w = w_new

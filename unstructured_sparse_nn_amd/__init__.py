@@ -14,7 +14,8 @@ from .binding import (ACT_GELU, ACT_NONE, ACT_RELU, BATCH_MAJOR, BF16, CONV_NCHW
                       snack_prune_regrow, snack_prune_regrow_prepared, snack_prune_regrow_static,
                       snack_prune_regrow_workspace, snack_sddmm_grad_vals, snack_gather_vals_t,
                       snack_spmm_bwd_input_t,
-                      snack_spmm_bwd_fused, snack_spmm_bwd_input, snack_spmm_fwd,
+                      snack_spmm_bwd_fused, snack_spmm_bwd_fused_adam, snack_spmm_bwd_input,
+                      snack_spmm_fwd,
                       snack_spmm_fwd_act, snack_version, snack_calibrate,
                       status_str)
 from .layer import SparseLinear, Topology  # noqa: F401

@@ -54,6 +54,12 @@ class SnackFootprint(ctypes.Structure):
     _fields_ = [(f, ctypes.c_uint64) for f in FOOTPRINT_FIELDS]
 
 
+class SnackAdam(ctypes.Structure):
+    """Mirror of ``struct snack_adam``."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
 class SnackPlan(ctypes.Structure):
     """Mirror of ``struct snack_plan``."""
     _fields_ = [("M", ctypes.c_int32), ("K", ctypes.c_int32), ("nnz", ctypes.c_int64),
@@ -91,6 +97,8 @@ def _load():
         "snack_sddmm_grad_vals": ([plan_p, P, P, i32, i32, i32, P, P], i32),
         "snack_spmm_bwd_fused": ([plan_p, P, P, i32, P, P, i32, i32, P, P, ctypes.c_float, P],
                                  i32),
+        "snack_spmm_bwd_fused_adam": ([plan_p, P, P, i32, P, P, i32, i32, P, P, P, P,
+                                       ctypes.POINTER(SnackAdam), P], i32),
         "snack_drop_count": ([i64, i32], i64),
         "snack_prune_regrow_workspace": ([i32, i32, i64, i64, ctypes.POINTER(sz)], i32),
         "snack_prune_regrow_workspace_ex": ([i32, i32, i64, i64, ctypes.c_uint32,
@@ -256,6 +264,19 @@ def snack_spmm_bwd_fused(plan, vals, X, dY, layout, B, dX, dvals=None, lr=0.0, s
     _check(_lib.snack_spmm_bwd_fused(ctypes.byref(plan), _ptr(vals), _ptr(vals_t), dt, _ptr(X),
                                      _ptr(dY), layout, B, _ptr(dX), _ptr(dvals), float(lr),
                                      _stream(stream)), "snack_spmm_bwd_fused")
+
+
+def snack_spmm_bwd_fused_adam(plan, vals, X, dY, layout, B, dX, dvals, m_t, v_t, lr, step,
+                              beta1=0.9, beta2=0.999, eps=1e-8, stream=None, dtype=None,
+                              vals_t=None):
+    """dX, dV and an Adam step on the values in one pass (moments m_t, v_t: fp32,
+    column order)."""
+    dt = _dtype(vals, X, dY, dX, dtype=dtype)
+    hp = SnackAdam(float(lr), float(beta1), float(beta2), float(eps), int(step))
+    _check(_lib.snack_spmm_bwd_fused_adam(ctypes.byref(plan), _ptr(vals), _ptr(vals_t), dt,
+                                          _ptr(X), _ptr(dY), layout, B, _ptr(dX), _ptr(dvals),
+                                          _ptr(m_t), _ptr(v_t), ctypes.byref(hp),
+                                          _stream(stream)), "snack_spmm_bwd_fused_adam")
 
 
 def snack_drop_count(nnz: int, frac_ppm: int) -> int:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/snack.h"
@@ -435,6 +436,32 @@ snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, void* vals
   return launch_bwd_fused(col_view(plan), vals, plan->nnz > 0 ? vals_t : nullptr, dtype, X, dY,
                           layout, B, dX, plan->nnz > 0 ? dvals : nullptr, lr, carry,
                           act_of(plan), to_stream(stream));
+}
+
+snack_status snack_spmm_bwd_fused_adam(const snack_plan* plan, void* vals, void* vals_t,
+                                       snack_dtype dtype, const void* X, const void* dY,
+                                       snack_layout layout, int32_t B, void* dX, void* dvals,
+                                       float* m_t, float* v_t, const snack_adam* adam,
+                                       void* stream) {
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  if (st) return st;
+  if (!adam || !X) return SNACK_E_NULL;
+  if (plan->nnz > 0 && (!m_t || !v_t)) return SNACK_E_NULL;
+  if (B < 1 || B > 32 || adam->step < 1) return SNACK_E_SHAPE;
+  const float hp[4] = {adam->lr, adam->beta1, adam->beta2, adam->eps};
+  for (float x : hp)
+    if (!(x == x) || x - x != 0.f) return SNACK_E_NAN;
+  if (!(adam->beta1 >= 0.f && adam->beta1 < 1.f && adam->beta2 >= 0.f && adam->beta2 < 1.f &&
+        adam->eps >= 0.f))
+    return SNACK_E_SHAPE;
+  if (plan->nnz == 0) return SNACK_OK;
+  // bias corrections in double on the host
+  const double c1 = 1.0 / (1.0 - std::pow((double)adam->beta1, (double)adam->step));
+  const double c2 = 1.0 / (1.0 - std::pow((double)adam->beta2, (double)adam->step));
+  const float h[6] = {adam->lr, adam->beta1, adam->beta2, adam->eps, (float)c1, (float)c2};
+  float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
+  return launch_bwd_fused(col_view(plan), vals, vals_t, dtype, X, dY, layout, B, dX, dvals, 0.f,
+                          carry, act_of(plan), to_stream(stream), m_t, v_t, h);
 }
 
 int64_t snack_drop_count(int64_t nnz, int32_t frac_ppm) {

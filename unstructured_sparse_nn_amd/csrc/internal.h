@@ -89,7 +89,8 @@ snack_status launch_sddmm(const seg_view& v, const void* dY, const void* X, snac
 snack_status launch_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
                               const void* X, const void* dY, snack_layout lay, int32_t B,
                               void* dX, void* dV, float lr, float* carry, void* act_tmp,
-                              hipStream_t s);
+                              hipStream_t s, float* m_t = nullptr, float* v_t = nullptr,
+                              const float* adam = nullptr);
 // vals_t[i] = vals[perm[i]] for i < nnz.
 hipError_t launch_gather_vals_t(const int32_t* perm, const void* vals, snack_dtype dt,
                                 void* vals_t, int64_t nnz, hipStream_t s);
@@ -109,9 +110,13 @@ void launch_fixup(const seg_view& v, snack_dtype dt, bool node_out, int32_t act,
 bool launch_wave_sddmm(const seg_view& v, const void* dYt, const void* Xt, snack_dtype dt,
                        int32_t B, void* dV, hipStream_t s);
 // Column view: dX, dV (nullable) and the optional update (wave_fused.hip).
+// With adam (NULL for SGD): the Adam step instead, hyperparameters
+// {lr, beta1, beta2, eps, 1/(1-beta1^t), 1/(1-beta2^t)}, moments m_t, v_t
+// (fp32, column order).
 bool launch_wave_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
                            const void* dYt, const void* Xt, int32_t B, void* dX, void* dV,
-                           float lr, bool node_out, hipStream_t s);
+                           float lr, bool node_out, hipStream_t s, float* m_t = nullptr,
+                           float* v_t = nullptr, const float* adam = nullptr);
 hipError_t launch_transpose2(snack_dtype dt, const void* in0, void* out0, int32_t R0, int32_t C0,
                              const void* in1, void* out1, int32_t R1, int32_t C1,
                              hipStream_t s);

@@ -34,6 +34,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "wave.h"
 
 namespace snk {
 
@@ -916,7 +917,12 @@ hipError_t launch_gather_vals_t(const int32_t* perm, const void* vals, snack_dty
 snack_status launch_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack_dtype dt,
                               const void* X, const void* dY, snack_layout lay, int32_t B,
                               void* dX, void* dV, float lr, float* carry, void* act_tmp,
-                              hipStream_t s) {
+                              hipStream_t s, float* m_t, float* v_t, const float* adam) {
+  if (adam) {  // the Adam step runs in the wave form only: check before any launch
+    const wave_shape w = wave_pick(dt, B);
+    if (B < 1 || !wave_eligible(v, dt, B, false) || (int64_t)w.ch * w.lpe < B)
+      return SNACK_E_SHAPE;
+  }
   if (B == 0) {  // empty batch: dV = 0, the update is a no-op, dX has no elements
     if (dV && v.nnz > 0) {
       dim3 g((unsigned)cdiv(v.nnz, 256));
@@ -942,8 +948,10 @@ snack_status launch_bwd_fused(const seg_view& v, void* vals, void* vals_t, snack
   }
   const bool node_out = lay == SNACK_NODE_MAJOR || B == 1;
   if (wave_eligible(v, dt, B, false) &&
-      launch_wave_bwd_fused(v, vals, vals_t, dt, dYt, Xt, B, dX, dV, lr, node_out, s))
+      launch_wave_bwd_fused(v, vals, vals_t, dt, dYt, Xt, B, dX, dV, lr, node_out, s, m_t, v_t,
+                            adam))
     return hipGetLastError() == hipSuccess ? SNACK_OK : SNACK_E_HIP;
+  if (adam) return SNACK_E_SHAPE;  // not reached: eligibility checked above
   // the merge-path form reads the values through perm; an update is then
   // carried into the column-ordered copy by one gather
   if (dt == SNACK_F32)
