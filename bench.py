@@ -104,6 +104,10 @@ def parse():
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--conv", action=argparse.BooleanOptionalAction, default=True,
                     help="time a sparse 1x1 convolution (generated kernel, generic, dense)")
+    ap.add_argument("--fixed-full", action="store_true",
+                    help="also generate fixed-pattern kernels for full-size layers (GPT-2 "
+                         "W1/W2 at 90%%, 4096^2 at 99%%; minutes of compilation) and time them "
+                         "against the generic forward")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="time multi-layer graph inference (power-law graphs, fused GELU)")
     ap.add_argument("--configs", action=argparse.BooleanOptionalAction, default=True,
@@ -606,6 +610,50 @@ def conv1x1_bench(N=8, HW=56 * 56, C=256, sparsity=0.9):
                      f"({synth.nnz_for(C, C, sparsity)} nnz)", **out}
 
 
+def fixed_full_bench():
+    """Fixed-pattern kernels generated for full-size fully connected layers
+    (node-major, one launch each) against the generic forward on the same
+    weight and inputs; the generated code and its compile time grow with nnz
+    (about a minute per 200K entries)."""
+    import torch
+    import synth
+    import unstructured_sparse_nn_amd as snk
+    out = {}
+    for name, M, K, sp, B, dt in (("gpt2_W1_s0.9_B1024_f32", 3072, 768, 0.9, 1024, "f32"),
+                                  ("gpt2_W2_s0.9_B1024_f32", 768, 3072, 0.9, 1024, "f32"),
+                                  ("square4096_s0.99_B32_bf16", 4096, 4096, 0.99, 32, "bf16"),
+                                  ("square4096_s0.99_B1024_bf16", 4096, 4096, 0.99, 1024, "bf16")):
+        wl = synth.random_case(29, M, K, synth.nnz_for(M, K, sp), 1, dt, "node")
+        w = wl.weights[0]
+        sd = snk.F32 if dt == "f32" else snk.BF16
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        log(f"fixed-pattern build {name} ({w.nnz} nnz)")
+        t0 = time.time()
+        f = snk.snack_fixed_build(w.row, w.col, w.vals, M, K, dtype=sd)
+        build_s = time.time() - t0
+        X = torch.randn(K * B, device="cuda").to(tdt)
+        Y = torch.empty(M * B, dtype=tdt, device="cuda")
+        Y2 = torch.empty_like(Y)
+        topo = snk.Topology(to_dev(w.row), to_dev(w.col), M, K, B,
+                            flags=snk.binding.PLAN_NODE_MAJOR_ONLY)
+        vals = to_dev(w.vals, dt == "bf16")
+        t = {"fixed": time_calls(lambda: snk.snack_fixed_fwd(f, X, B, 1, Y)),
+             "generic": time_calls(lambda: topo.fwd(vals, X, B, snk.NODE_MAJOR, out=Y2))}
+        # same products up to the order of the fp32 sums
+        err = (Y.float() - Y2.float()).abs().max().item()
+        scale = Y2.float().abs().max().item()
+        flops = 2 * w.nnz * B
+        out[name] = {"nnz": w.nnz, "us": {k: round(v, 2) for k, v in t.items()},
+                     "fixed_vs_generic": round(t["generic"] / t["fixed"], 2),
+                     "fixed_TFLOPs": round(flops / (t["fixed"] * 1e6), 2),
+                     "max_abs_diff_vs_generic": err, "max_abs_generic": scale,
+                     "build_seconds": round(build_s, 1), **f.info()}
+        f.free()
+        del X, Y, Y2, topo, vals
+        torch.cuda.empty_cache()
+    return out
+
+
 def snk_drop(nnz, ppm):
     import unstructured_sparse_nn_amd as snk
     return snk.snack_drop_count(nnz, ppm)
@@ -939,6 +987,8 @@ def run_bench(args):
     if args.conv:
         log("1x1 convolution")
         rec["conv1x1"] = conv1x1_bench()
+    if args.fixed_full:
+        rec["fixed_full"] = fixed_full_bench()
     rec["footprint"] = footprint(N, wt.nnz, B, 0 if args.products_only else
                                  snk_drop(wt.nnz, args.drop_ppm), args.layout)
     if args.cpu_baseline:

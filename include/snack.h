@@ -492,21 +492,26 @@ SNACK_API snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz,
  * row-major, vals float or raw bf16 bits as dtype), writes a kernel for
  * exactly that weight -- the values become immediate operands, the indices
  * become the code's structure -- compiles it with hipRTC for gfx950 and
- * loads it.  Limits: 1 <= K <= 256, nnz <= 65536 (else SNACK_E_SHAPE).
- * Building takes seconds (compilation); the handle owns the loaded code
- * object (device memory for code, the one exception to "no allocation")
- * until snack_fixed_free.  flags: SNACK_FIXED_COMPILE_ONLY generates and
- * compiles without loading (no GPU needed; the handle cannot run).
- * Errors: SNACK_E_NULL, SNACK_E_DTYPE, SNACK_E_SHAPE, SNACK_E_COO_RANGE,
- * SNACK_E_COO_ORDER, SNACK_E_LAYOUT (unknown flag), SNACK_E_HIP (compile or
- * load failure).
+ * loads it.  The rows are cut into bands of about 4K entries (one
+ * workgroup each per 64 batch columns) and the inputs are staged in tiles
+ * of 256, so any M and K work.  Limits: M, K >= 1, nnz <= 2^23, at most
+ * 65535 bands (else SNACK_E_SHAPE).  Code size and build time grow linearly
+ * with nnz: about 8 bytes of code and 0.2 ms of compilation per entry (a
+ * 4096 x 4096 layer at 95% sparsity takes minutes).  The handle owns the
+ * loaded code object (device memory for code, the one exception to "no
+ * allocation") until snack_fixed_free.  flags: SNACK_FIXED_COMPILE_ONLY
+ * generates and compiles without loading (no GPU needed; the handle cannot
+ * run).  Errors: SNACK_E_NULL, SNACK_E_DTYPE, SNACK_E_SHAPE,
+ * SNACK_E_COO_RANGE, SNACK_E_COO_ORDER, SNACK_E_LAYOUT (unknown flag),
+ * SNACK_E_HIP (compile or load failure).
  *
  * snack_fixed_fwd: Y = X W^T for `images` independent node-major blocks,
  * X[i] (K x B) at X + i*K*B and Y[i] (M x B) at Y + i*M*B, in the dtype the
  * handle was built for; fp32 accumulation, one rounding.  An NCHW 1x1
  * convolution with C_in = K, C_out = M over images of H*W pixels is this
- * call with B = H*W.  Asynchronous on `stream`.  Errors: SNACK_E_NULL,
- * SNACK_E_SHAPE (negative sizes), SNACK_E_NOT_PREPARED (compile-only handle).
+ * call with B = H*W.  One launch, asynchronous on `stream`.  Errors:
+ * SNACK_E_NULL, SNACK_E_SHAPE (negative sizes, more than 65535 images),
+ * SNACK_E_NOT_PREPARED (compile-only handle).
  */
 typedef struct snack_fixed snack_fixed;
 #define SNACK_FIXED_COMPILE_ONLY 1u
@@ -516,9 +521,10 @@ SNACK_API snack_status snack_fixed_build(const int32_t* row, const int32_t* col,
                                          uint32_t flags, snack_fixed** out);
 SNACK_API snack_status snack_fixed_fwd(const snack_fixed* f, const void* X, int32_t B,
                                        int32_t images, void* Y, void* stream);
-/* Waves per workgroup, code-object and source sizes of a built kernel. */
-SNACK_API snack_status snack_fixed_info(const snack_fixed* f, int32_t* groups, size_t* code_bytes,
-                                        size_t* source_bytes);
+/* Waves per workgroup, bands (workgroups per batch tile and image),
+ * code-object and source sizes of a built kernel; any pointer may be NULL. */
+SNACK_API snack_status snack_fixed_info(const snack_fixed* f, int32_t* waves, int32_t* bands,
+                                        size_t* code_bytes, size_t* source_bytes);
 /* The compiled gfx950 code object of a handle (host memory owned by it). */
 SNACK_API const void* snack_fixed_code(const snack_fixed* f, size_t* bytes);
 SNACK_API void snack_fixed_free(snack_fixed* f);

@@ -250,19 +250,23 @@ def _fixed_case(M, K, sp, dt="f32", seed=3):
 
 
 def test_fixed_pattern_kernel_compiles_for_gfx950_without_spills(snk):
-    """The generated kernel compiles for gfx950 on the host.  Its code object
-    has one FMA per entry (the value an operand), no scratch (the staged
-    inputs are read column by column) and no packed fp32 instructions."""
+    """The generated kernel compiles for gfx950 on the host, also with K over
+    one staged tile of 256 inputs.  Its code object has one FMA per entry
+    (the value an operand), no scratch and no packed fp32 instructions, and
+    reads the staged inputs from LDS (ds_ instructions, no flat loads of
+    them)."""
     import shutil
     import subprocess
     import tempfile
-    for M, K, sp, dt in ((48, 40, 0.8, "f32"), (96, 64, 0.6, "bf16")):
+    for M, K, sp, dt in ((48, 40, 0.8, "f32"), (96, 64, 0.6, "bf16"), (40, 700, 0.9, "bf16")):
         w = _fixed_case(M, K, sp, dt)
         f = snk.snack_fixed_build(w.row, w.col, w.vals, M, K,
                                   dtype=snk.F32 if dt == "f32" else snk.BF16,
                                   flags=snk.FIXED_COMPILE_ONLY)
         info = f.info()
-        assert info["groups"] >= 1 and info["code_bytes"] > 0
+        assert 1 <= info["waves"] <= 8 and info["code_bytes"] > 0
+        # bands: waves of at most 32 rows each, at most 8 waves per band
+        assert info["bands"] >= -(-M // (32 * 8))
         code = f.code()
         assert len(code) == info["code_bytes"]
         objdump = "/opt/rocm/llvm/bin/llvm-objdump"
@@ -282,6 +286,7 @@ def test_fixed_pattern_kernel_compiles_for_gfx950_without_spills(snk):
                                             "v_mul_f32"))
         assert fmas >= w.nnz
         assert ".private_segment_fixed_size: 0" in notes.replace("  ", " ").replace("  ", " ")
+        assert asm.count("ds_read") + asm.count("ds_load") > 0
 
 
 def test_fixed_pattern_build_rejects_bad_arguments(snk):
@@ -292,8 +297,8 @@ def test_fixed_pattern_build_rejects_bad_arguments(snk):
     v = np.ones(3, np.float32)
     CO = snk.FIXED_COMPILE_ONLY
     cases = [
-        (lambda: snk.snack_fixed_build(r, c, v, 2, 300, flags=CO), -2),       # K > 256
         (lambda: snk.snack_fixed_build(r, c, v, 0, 4, flags=CO), -2),
+        (lambda: snk.snack_fixed_build(r, c, v, 2, 0, flags=CO), -2),
         (lambda: snk.snack_fixed_build(r, np.array([3, 1, 0], np.int32), v, 2, 4, flags=CO), -6),
         (lambda: snk.snack_fixed_build(r, np.array([1, 4, 0], np.int32), v, 2, 4, flags=CO), -5),
         (lambda: snk.snack_fixed_build(r, c, v, 2, 4, dtype=5, flags=CO), -3),
@@ -303,11 +308,12 @@ def test_fixed_pattern_build_rejects_bad_arguments(snk):
         with pytest.raises(snk.SnackError) as e:
             call()
         assert e.value.status == status
-    big = np.arange(65537, dtype=np.int64)
-    with pytest.raises(snk.SnackError) as e:
-        snk.snack_fixed_build((big // 256).astype(np.int32), (big % 256).astype(np.int32),
-                              np.ones(big.size, np.float32), 300, 256, flags=CO)
-    assert e.value.status == -2
+    import ctypes
+    out = ctypes.c_void_p(0)
+    # more than 2^23 entries: refused before the arrays are read
+    assert b.raw_status("snack_fixed_build", r.ctypes.data, c.ctypes.data, v.ctypes.data, 0,
+                        4096, 4096, (1 << 23) + 1, CO, ctypes.byref(out)) == -2
+    assert out.value is None
     f = snk.snack_fixed_build(r, c, v, 2, 4, flags=CO)
     with pytest.raises(snk.SnackError) as e:  # compile-only handles cannot run
         snk.snack_fixed_fwd(f, 0x1000, 8, 1, 0x2000, stream=0)

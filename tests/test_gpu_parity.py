@@ -999,6 +999,9 @@ FIXED_CASES = [  # (M, K, sparsity, B, images, dtype)
     (256, 256, 0.9, 200, 2, "bf16"),
     (200, 1, 0.0, 70, 1, "f32"),        # dense single column
     (64, 64, 1.0, 65, 1, "f32"),        # no entries: Y = 0
+    (96, 1000, 0.95, 40, 2, "bf16"),    # four staged tiles, two bands
+    (768, 3072, 0.99, 64, 1, "f32"),    # GPT-2 W2 shape at 99%: twelve tiles
+    (3072, 768, 0.99, 100, 1, "bf16"),  # GPT-2 W1 shape at 99%: many bands
 ]
 
 

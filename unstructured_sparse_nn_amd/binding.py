@@ -115,7 +115,8 @@ def _load():
         "snack_fixed_build": ([P, P, P, i32, i32, i32, i64, ctypes.c_uint32, ctypes.POINTER(P)],
                               i32),
         "snack_fixed_fwd": ([P, P, i32, i32, P, P], i32),
-        "snack_fixed_info": ([P, ctypes.POINTER(i32), ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
+        "snack_fixed_info": ([P, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(sz),
+                              ctypes.POINTER(sz)], i32),
         "snack_fixed_code": ([P, ctypes.POINTER(sz)], P),
         "snack_fixed_free": ([P], None),
         "snack_conv1x1": ([plan_p, P, i32, P, i32, i32, i32, P, P], i32),
@@ -357,10 +358,12 @@ class SnackFixed:
         self.handle = handle
 
     def info(self) -> dict:
-        g, cb, sb = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
-        _check(_lib.snack_fixed_info(self.handle, ctypes.byref(g), ctypes.byref(cb),
-                                     ctypes.byref(sb)), "snack_fixed_info")
-        return {"groups": g.value, "code_bytes": cb.value, "source_bytes": sb.value}
+        g, nb = ctypes.c_int32(0), ctypes.c_int32(0)
+        cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(_lib.snack_fixed_info(self.handle, ctypes.byref(g), ctypes.byref(nb),
+                                     ctypes.byref(cb), ctypes.byref(sb)), "snack_fixed_info")
+        return {"waves": g.value, "bands": nb.value, "code_bytes": cb.value,
+                "source_bytes": sb.value}
 
     def code(self) -> bytes:
         """The compiled code object."""
