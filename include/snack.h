@@ -145,9 +145,12 @@ SNACK_API const char* snack_status_str(snack_status s);
  * snack_plan_init -- host only, no device work.
  * Computes tile sizes, tile counts and the arena layout for a weight of
  * shape M x K with nnz nonzeros, for product calls with B <= max_batch.
- * tile_items = 0 picks the tile size automatically (a power of two in
- * [128, 2048] giving at most ~2048 tiles); otherwise it must lie in
- * [1, 2048] and is used for both views.  Unless flags has
+ * tile_items = 0 picks each view's tile size automatically: the smallest
+ * power of two in [128, 2048] giving at most ~2048 tiles, and for
+ * max_batch > 32 also at least twice the view's mean segment length (so
+ * that only segments well above the mean are cut into tile pieces, whose
+ * partial sums travel through fp32 carry slots); otherwise tile_items must
+ * lie in [1, 2048] and is used for both views.  Unless flags has
  * SNACK_PLAN_NODE_MAJOR_ONLY, the arena also holds 4*max_batch*(M+K) bytes
  * into which product calls copy batch-major activations (B > 1) in
  * node-major order before gathering from them.

@@ -46,6 +46,12 @@ def test_plan_init_sizes(snk):
     assert p.P_row <= 2048 and p.arena_bytes > 0
     p = snk.snack_plan_init(200000, 200000, 2400000, 128)
     assert p.tile_row == 2048
+    # batches wider than 32: tiles of at least twice the mean segment length
+    # (GPT-2 W1 3072 x 768 at 90%: rows of ~77, columns of ~307 entries)
+    p = snk.snack_plan_init(3072, 768, 235930, 1024)
+    assert (p.tile_row, p.tile_col) == (256, 1024)
+    p = snk.snack_plan_init(3072, 768, 235930, 32)
+    assert (p.tile_row, p.tile_col) == (128, 128)
     p = snk.snack_plan_init(7, 5, 0, 1, tile_items=3)
     assert p.tile_row == 3 and p.P_row == 3 and p.P_col == 2
     offs = list(p.off)[:10]
