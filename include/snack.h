@@ -71,6 +71,8 @@ typedef int32_t snack_status;
 #define SNACK_E_OVERFLOW (-10)     /* a size exceeds the int32 index range */
 #define SNACK_E_HIP (-11)          /* a HIP launch or runtime call failed */
 #define SNACK_E_NOT_PREPARED (-12) /* the plan has not been prepared */
+#define SNACK_E_PLAN_CORRUPT (-13) /* debug build only: a plan array or COO index failed
+                                      the device check run before a product */
 
 /* Element type and activation layout are plain int32 arguments (any value
  * may be passed and is checked: SNACK_E_DTYPE / SNACK_E_LAYOUT). */

@@ -15,7 +15,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsnack.so")
+# SNACK_LIBRARY selects another build of the same ABI, e.g. the debug build
+# libsnack_debug.so (device checks of plan arrays before every product).
+LIB_PATH = os.environ.get("SNACK_LIBRARY") or os.path.join(HERE, "libsnack.so")
 
 F32, BF16 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
@@ -34,7 +36,8 @@ ARRAYS = {"row_ptr": 0, "rpart_seg": 1, "rpart_nz": 2, "rcut": 3, "col_ptr": 4, 
 STATUS = {0: "SNACK_OK", -1: "SNACK_E_NULL", -2: "SNACK_E_SHAPE", -3: "SNACK_E_DTYPE",
           -4: "SNACK_E_LAYOUT", -5: "SNACK_E_COO_RANGE", -6: "SNACK_E_COO_ORDER",
           -7: "SNACK_E_NAN", -8: "SNACK_E_COUNT", -9: "SNACK_E_WORKSPACE",
-          -10: "SNACK_E_OVERFLOW", -11: "SNACK_E_HIP", -12: "SNACK_E_NOT_PREPARED"}
+          -10: "SNACK_E_OVERFLOW", -11: "SNACK_E_HIP", -12: "SNACK_E_NOT_PREPARED",
+          -13: "SNACK_E_PLAN_CORRUPT"}
 
 
 class SnackError(RuntimeError):

@@ -37,19 +37,44 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lhiprtc"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+# The debug build: the same library with SNACK_DEBUG_CHECKS defined in
+# api.hip, whose product entry points then check every plan array and COO
+# index on the device (within the arrays' sizes) before launching, and
+# return SNACK_E_PLAN_CORRUPT instead of reading out of bounds.  Selected
+# at import time with SNACK_LIBRARY=<path of libsnack_debug.so>.
+DEBUG_LIB = os.path.join(HERE, "libsnack_debug.so")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES) + 1, int(os.environ.get("MAX_JOBS", "8")))
+
+    def debug_api():
+        obj = os.path.join(BUILD, "api_debug.o")
+        cmd = [HIPCC, *CFLAGS, "-DSNACK_DEBUG_CHECKS", "-c", os.path.join(CSRC, "api.hip"),
+               "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for api.hip (debug checks):\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(jobs) as ex:
+        dbg = ex.submit(debug_api)
+        objs = list(ex.map(_compile, SOURCES))
+        dbg_obj = dbg.result()
+    _link(objs, LIB)
+    _link([dbg_obj if os.path.basename(o) == "api.o" else o for o in objs], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {DEBUG_LIB}", file=sys.stderr)
     return LIB
 
 

@@ -139,14 +139,101 @@ snack_status plan_results(snack_plan* p, result_words& r) {
   return SNACK_OK;
 }
 
+#ifdef SNACK_DEBUG_CHECKS
+// Debug build: before a product runs, every array its kernels take indices
+// from is checked on the device, reading each array only within the size the
+// plan gives it: offsets start at 0, never decrease and end at nnz; entry
+// indices (the COO columns, row_t) and perm lie in range; tile starts lie in
+// range and never decrease; cut flags are 0 or 1.  A violation sets a bit of
+// *err (one atomic per wave that found one); the product is then not
+// launched.  Bits: 1 row offsets, 2 COO column, 4 row tiles, 8 column
+// offsets, 16 row_t, 32 perm, 64 column tiles.
+struct dbg_arrays {
+  const int32_t *rptr, *col, *rseg, *rnz, *rcut, *cptr, *rowt, *perm, *cseg, *cnz, *ccut;
+  int64_t M, K, nnz, Pr, Pc;
+};
+
+__device__ __forceinline__ int32_t dbg_offsets(const int32_t* ptr, int64_t S, int64_t nnz,
+                                               int64_t i) {
+  const int32_t v = ptr[i];
+  if (v < 0 || v > nnz) return 1;
+  if (i == 0 && v != 0) return 1;
+  if (i == S && v != nnz) return 1;
+  return (i < S && ptr[i + 1] < v) ? 1 : 0;
+}
+
+__device__ __forceinline__ int32_t dbg_tiles(const int32_t* seg, const int32_t* nz,
+                                             const int32_t* cut, int64_t P, int64_t S,
+                                             int64_t nnz, int64_t p) {
+  const int32_t a = seg[p], b = nz[p], c = cut[p];
+  if (a < 0 || a > S || b < 0 || b > nnz || (c != 0 && c != 1)) return 1;
+  return (p < P && (seg[p + 1] < a || nz[p + 1] < b)) ? 1 : 0;
+}
+
+__global__ __launch_bounds__(256) void k_debug_check(dbg_arrays d, int32_t* __restrict__ err) {
+  const int64_t n_rp = d.M + 1, n_cp = d.K + 1, n_rt = d.Pr + 1, n_ct = d.Pc + 1;
+  const int64_t total = n_rp + n_cp + n_rt + n_ct + 3 * d.nnz;
+  int32_t bits = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    int64_t j = i;
+    if (j < n_rp) { bits |= dbg_offsets(d.rptr, d.M, d.nnz, j); continue; }
+    j -= n_rp;
+    if (j < n_cp) { bits |= dbg_offsets(d.cptr, d.K, d.nnz, j) << 3; continue; }
+    j -= n_cp;
+    if (j < n_rt) { bits |= dbg_tiles(d.rseg, d.rnz, d.rcut, d.Pr, d.M, d.nnz, j) << 2; continue; }
+    j -= n_rt;
+    if (j < n_ct) { bits |= dbg_tiles(d.cseg, d.cnz, d.ccut, d.Pc, d.K, d.nnz, j) << 6; continue; }
+    j -= n_ct;
+    if (j < d.nnz) { const int32_t c = d.col[j]; bits |= (c < 0 || c >= d.K) ? 2 : 0; continue; }
+    j -= d.nnz;
+    if (j < d.nnz) { const int32_t r = d.rowt[j]; bits |= (r < 0 || r >= d.M) ? 16 : 0; continue; }
+    j -= d.nnz;
+    const int32_t q = d.perm[j];
+    bits |= (q < 0 || q >= d.nnz) ? 32 : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) bits |= __shfl_xor(bits, off, 64);
+  if (bits && __lane_id() == 0) atomicOr(err, bits);
+}
+
+__global__ void k_debug_clear(int32_t* err) { *err = 0; }
+
+snack_status debug_check_plan(const snack_plan* p, hipStream_t s) {
+  char* a = (char*)p->arena;
+  auto arr = [&](int which) { return (const int32_t*)(a + p->off[which]); };
+  dbg_arrays d{arr(SNACK_ARR_ROW_PTR), p->col, arr(SNACK_ARR_RPART_SEG),
+               arr(SNACK_ARR_RPART_NZ), arr(SNACK_ARR_RCUT), arr(SNACK_ARR_COL_PTR),
+               arr(SNACK_ARR_ROW_T), arr(SNACK_ARR_PERM), arr(SNACK_ARR_CPART_SEG),
+               arr(SNACK_ARR_CPART_NZ), arr(SNACK_ARR_CCUT), p->M, p->K, p->nnz, p->P_row,
+               p->P_col};
+  if (p->nnz > 0 && !p->col) return SNACK_E_NOT_PREPARED;
+  int32_t* err = (int32_t*)(a + p->off[SLOT_PRIV] + priv_of(p).res);
+  int32_t h = 0;
+  // on the caller's stream, after its earlier work; the debug build waits
+  // for the verdict (one stream synchronisation per product call)
+  hipLaunchKernelGGL(k_debug_clear, dim3(1), dim3(1), 0, s, err);
+  hipLaunchKernelGGL(k_debug_check, dim3(1024), dim3(256), 0, s, d, err);
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyAsync(&h, err, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SNACK_E_HIP;
+  return h ? SNACK_E_PLAN_CORRUPT : SNACK_OK;
+}
+#endif
+
 snack_status check_product(const snack_plan* p, const void* a, const void* b, const void* c,
-                           snack_dtype dt, snack_layout lay, int32_t B) {
+                           snack_dtype dt, snack_layout lay, int32_t B, void* stream) {
   if (!p) return SNACK_E_NULL;
   if (!p->prepared || !p->arena) return SNACK_E_NOT_PREPARED;
   snack_status st = check_dtype_layout(dt, lay);
   if (st) return st;
   if (B < 0 || B > p->max_batch) return SNACK_E_SHAPE;
   if (B > 0 && (!a || !b || !c)) return SNACK_E_NULL;
+#ifdef SNACK_DEBUG_CHECKS
+  if (B > 0) return debug_check_plan(p, to_stream(stream));
+#else
+  (void)stream;
+#endif
   return SNACK_OK;
 }
 
@@ -172,6 +259,7 @@ const char* snack_status_str(snack_status s) {
     case SNACK_E_OVERFLOW: return "size exceeds int32 index range";
     case SNACK_E_HIP: return "HIP launch or runtime error";
     case SNACK_E_NOT_PREPARED: return "plan not prepared";
+    case SNACK_E_PLAN_CORRUPT: return "plan array or COO index out of range (debug build check)";
     default: return "unknown status";
   }
 }
@@ -319,7 +407,8 @@ const void* snack_plan_array(const snack_plan* plan, int32_t which, int64_t* cou
 snack_status snack_spmm_fwd(const snack_plan* plan, const void* vals, snack_dtype dtype,
                             const void* X, snack_layout layout, int32_t B, void* Y,
                             void* stream) {
-  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y, dtype, layout, B);
+  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y,
+                                  dtype, layout, B, stream);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
   return launch_seg_spmm(row_view(plan), vals, dtype, X, layout, B, Y, carry, act_of(plan),
@@ -330,7 +419,8 @@ snack_status snack_spmm_fwd_act(const snack_plan* plan, const void* vals, snack_
                                 const void* X, snack_layout layout, int32_t B, void* Y,
                                 int32_t act, void* stream) {
   if (act < SNACK_ACT_NONE || act > SNACK_ACT_GELU) return SNACK_E_SHAPE;
-  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y, dtype, layout, B);
+  snack_status st = check_product(plan, X, Y, plan && plan->nnz ? vals : Y,
+                                  dtype, layout, B, stream);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
   hipStream_t s = to_stream(stream);
@@ -389,7 +479,8 @@ snack_status snack_conv1x1(const snack_plan* plan, const void* vals, snack_dtype
 snack_status snack_spmm_bwd_input(const snack_plan* plan, const void* vals, snack_dtype dtype,
                                   const void* dY, snack_layout layout, int32_t B, void* dX,
                                   void* stream) {
-  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX,
+                                  dtype, layout, B, stream);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
   return launch_seg_spmm(col_view(plan), vals, dtype, dY, layout, B, dX, carry, act_of(plan),
@@ -413,7 +504,7 @@ snack_status snack_spmm_bwd_input_t(const snack_plan* plan, const void* vals_t,
                                     snack_dtype dtype, const void* dY, snack_layout layout,
                                     int32_t B, void* dX, void* stream) {
   snack_status st =
-      check_product(plan, dY, dX, plan && plan->nnz ? vals_t : dX, dtype, layout, B);
+      check_product(plan, dY, dX, plan && plan->nnz ? vals_t : dX, dtype, layout, B, stream);
   if (st) return st;
   float* carry = (float*)((char*)plan->arena + plan->off[S_CARRY]);
   seg_view v = col_view(plan);
@@ -425,7 +516,8 @@ snack_status snack_spmm_bwd_input_t(const snack_plan* plan, const void* vals_t,
 snack_status snack_sddmm_grad_vals(const snack_plan* plan, const void* dY, const void* X,
                                    snack_dtype dtype, snack_layout layout, int32_t B,
                                    void* dvals, void* stream) {
-  snack_status st = check_product(plan, dY, X, plan && plan->nnz ? dvals : X, dtype, layout, B);
+  snack_status st = check_product(plan, dY, X, plan && plan->nnz ? dvals : X,
+                                  dtype, layout, B, stream);
   if (st) return st;
   if (plan->nnz > 0 && !dvals) return SNACK_E_NULL;
   return launch_sddmm(row_view(plan), dY, X, dtype, layout, B, dvals, act_of(plan),
@@ -436,7 +528,8 @@ snack_status snack_spmm_bwd_fused(const snack_plan* plan, void* vals, void* vals
                                   snack_dtype dtype, const void* X, const void* dY,
                                   snack_layout layout, int32_t B, void* dX, void* dvals,
                                   float lr, void* stream) {
-  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX,
+                                  dtype, layout, B, stream);
   if (st) return st;
   if (B > 0 && !X) return SNACK_E_NULL;
   if (B > 32) return SNACK_E_SHAPE;
@@ -452,7 +545,8 @@ snack_status snack_spmm_bwd_fused_adam(const snack_plan* plan, void* vals, void*
                                        snack_layout layout, int32_t B, void* dX, void* dvals,
                                        float* m_t, float* v_t, const snack_adam* adam,
                                        void* stream) {
-  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX, dtype, layout, B);
+  snack_status st = check_product(plan, dY, dX, plan && plan->nnz ? vals : dX,
+                                  dtype, layout, B, stream);
   if (st) return st;
   if (!adam || !X) return SNACK_E_NULL;
   if (plan->nnz > 0 && (!m_t || !v_t)) return SNACK_E_NULL;
