@@ -243,6 +243,33 @@ def test_wave_lds_staged_inputs(orc, M, K, nnz, Bsz, dt):
     assert topo.plan.has_split_row == 0
 
 
+WIDE_CASES = [  # (M, K, nnz, B, dtype, layout): batches of several 64-column passes
+    (300, 700, 21000, 128, "f32", "node"),
+    (300, 700, 21000, 192, "f32", "batch"),    # batch-major through the node-major copy
+    (96, 3000, 28800, 256, "bf16", "node"),    # rows of ~300 entries kept whole (wide tiles)
+    (2000, 1500, 30000, 128, "bf16", "node"),
+    (5000, 40, 20000, 256, "bf16", "node"),    # columns of ~500 entries kept whole
+    (64, 64, 0, 128, "f32", "node"),           # no entries: zeros
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt,layout", WIDE_CASES)
+def test_wide_batches(orc, M, K, nnz, Bsz, dt, layout):
+    """Batches of 128 or more run in 64-column passes on plans whose wide
+    tiles keep uniform segments whole (no split, no fix-up); also the input
+    gradient from column-ordered values."""
+    w = synth.random_case(27, M, K, nnz, Bsz, dt, layout)
+    wt = w.weights[0]
+    topo = run_products(orc, wt, w.X[0], w.dY[0], dt, layout, Bsz, repeat_check=True)
+    assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
+    lay = B.NODE_MAJOR if layout == "node" else B.BATCH_MAJOR
+    vals = to_dev(wt.vals, dt)
+    dX = topo.bwd_input_t(topo.gather_vals_t(vals), to_dev(w.dY[0].data, dt), Bsz, lay)
+    ref, S = orc.spmm_bwd_input(M, K, wt.row, wt.col, wt.vals_f64(), Bsz, w.dY[0].f64(),
+                                layout == "node")
+    assert_within(from_dev(dX, dt), ref, S, dt, "bwd_input_t")
+
+
 @pytest.mark.parametrize("which", ["up", "down"])
 @pytest.mark.parametrize("Bsz", [1, 4, 16])
 def test_llama_projection_configs(orc, which, Bsz):
