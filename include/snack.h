@@ -497,7 +497,7 @@ SNACK_API snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz,
  * row-major, vals float or raw bf16 bits as dtype), writes a kernel for
  * exactly that weight -- the values become immediate operands, the indices
  * become the code's structure -- compiles it with hipRTC for gfx950 and
- * loads it.  The rows are cut into bands of about 4K entries (one
+ * loads it.  The rows are cut into bands of about 8K entries (one
  * workgroup each per 64 batch columns) and the inputs are staged in tiles
  * of 256, so any M and K work.  Limits: M, K >= 1, nnz <= 2^23, at most
  * 65535 bands (else SNACK_E_SHAPE).  Code size and build time grow linearly

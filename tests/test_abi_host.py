@@ -270,9 +270,9 @@ def test_fixed_pattern_kernel_compiles_for_gfx950_without_spills(snk):
                                   dtype=snk.F32 if dt == "f32" else snk.BF16,
                                   flags=snk.FIXED_COMPILE_ONLY)
         info = f.info()
-        assert 1 <= info["waves"] <= 8 and info["code_bytes"] > 0
-        # bands: waves of at most 32 rows each, at most 8 waves per band
-        assert info["bands"] >= -(-M // (32 * 8))
+        assert 1 <= info["waves"] <= 16 and info["code_bytes"] > 0
+        # bands: waves of at most 32 rows each, at most 16 waves per band
+        assert info["bands"] >= -(-M // (32 * 16))
         code = f.code()
         assert len(code) == info["code_bytes"]
         objdump = "/opt/rocm/llvm/bin/llvm-objdump"

@@ -9,12 +9,13 @@
 // library's, for CDNA4:
 //   * node-major activations, X: K x B per image, Y: M x B per image (a 1x1
 //     convolution over an NCHW image is exactly this, B = H*W);
-//   * the rows are cut into bands of about BAND_NNZ entries; workgroup
-//     (x, y, z) computes band y for the 64 batch columns 64x.. (one per lane)
-//     of image z, so a fully connected layer of any size fills the GPU even
-//     at one batch tile.  Inside a band, each wave owns a run of at most
-//     RMAX consecutive rows (about WAVE_NNZ entries) whose accumulators live
-//     in registers for the whole band;
+//   * the rows are cut into waves -- runs of at most RMAX consecutive rows,
+//     about WAVE_NNZ entries -- whose accumulators live in registers, and
+//     the waves into bands of up to MAX_WAVES; workgroup (x, y, z) computes
+//     band y for the 64 batch columns 64x.. (one per lane) of image z, so a
+//     fully connected layer of any size fills the GPU even at one batch
+//     tile, and a small one (a 1x1 convolution) stages its inputs once per
+//     batch tile;
 //   * the inputs are staged in LDS as fp32 in tiles of KT columns x 64 batch
 //     columns (coalesced loads); a band stages only the tiles holding one of
 //     its entries.  Per tile, a wave walks the columns of its entries in
@@ -53,7 +54,7 @@ namespace {
 constexpr int KT = 256;               // staged inputs per tile: KT x 64 fp32 = 64 KB of LDS
 constexpr int RMAX = 32;              // rows (accumulators) per wave
 constexpr int64_t WAVE_NNZ = 512;     // entries per wave, about
-constexpr int MAX_WAVES = 8;          // waves per workgroup
+constexpr int MAX_WAVES = 16;         // waves per workgroup
 constexpr int64_t MAX_NNZ = 1 << 23;  // entries baked into one handle
 constexpr int32_t MAX_BANDS = 65535;  // workgroups along grid y
 
