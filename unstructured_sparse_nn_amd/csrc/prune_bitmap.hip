@@ -58,7 +58,7 @@ __device__ __forceinline__ void stream_store4(T* p, const vec<T, 4>& v) {
   }
 }
                 // entries per block: thread t holds base + 4t .. + 3
-constexpr int HREPL = 64;                 // select-histogram replicas
+constexpr int HREPL = 16;                 // select-histogram replicas
 constexpr int AREPL = 64;                 // acceptance-count replicas
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
 constexpr int WT = 512;                   // threads (= bitmap words) per write block
