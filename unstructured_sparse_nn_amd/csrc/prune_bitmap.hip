@@ -91,8 +91,12 @@ __device__ __forceinline__ int64_t lin_of(int32_t r, int32_t c, int32_t M, int32
   return (r < 0 || r >= M || c < 0 || c >= K) ? -1 : (int64_t)r * K + c;
 }
 
-__global__ __launch_bounds__(256) void k_bi_init(bm_state* st) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+// Also zeroes zero[0 .. nzero) (the transposed bitmap's block sums of a fused
+// prepare, which the transposer adds into).
+__global__ __launch_bounds__(256) void k_bi_init(bm_state* st, int32_t* __restrict__ zero,
+                                                 int64_t nzero) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nzero) zero[i] = 0;
   if (i < 4 * HREPL * 256) (&st->hist[0][0][0])[i] = 0;
   if (i < SLOTS * AREPL) (&st->ch_acc[0][0])[i] = 0;
   if (i == 0) {
@@ -813,11 +817,18 @@ constexpr int FP_THREADS = 256;
 
 // Blocks [0, rb): row offsets and row tiles, thread per row s in [0, M]; a
 // block with a split row sets res[2] (pinned host memory, cleared by the
-// emitter).  Blocks [rb, ..): bit transpose, two 32 x 32 tiles per wave.
+// emitter).  Blocks [rb, ..): the bit transpose FT of F and its popcount
+// sums per block of WT words of FT (k_fp_temit's blocks), which tsum must
+// hold zeroed.  Block j covers column word wc and row words rw0 .. rw0+7
+// (two 32 x 32 tiles per wave: 32 ballots give the column words of both),
+// so that neighbouring lanes of the block write neighbouring FT words and
+// the block's counts fall into a few FT blocks, summed in LDS first.
+constexpr int TS_SPAN = 256;  // FT blocks one transpose block can touch, summed in LDS
 __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
     const bm_state* st, const uint2* __restrict__ FP,
     int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ res,
-    uint32_t* __restrict__ FT) {
+    uint32_t* __restrict__ FT, int32_t* __restrict__ tsum) {
+  __shared__ int32_t tsl[TS_SPAN];
   if (bm_failed(st)) return;
   const int64_t KW = K >> 5, WM = M >> 5;
   if ((int)blockIdx.x < rb) {
@@ -836,35 +847,39 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
     if (threadIdx.x == 0 && any_b) store_result(&res[2], 1);
     return;
   }
-  const int64_t tile = ((int64_t)(blockIdx.x - rb) * FP_THREADS + threadIdx.x) >> 5;
-  const int l = threadIdx.x & 31;
-  const bool ok = tile < WM * KW;
-  const int64_t rw = ok ? tile / KW : 0, wc = ok ? tile % KW : 0;
+  const int64_t RWG = cdiv_dev(WM, 8);  // groups of 8 row words per column word
+  const int64_t j = (int64_t)blockIdx.x - rb;
+  const int64_t wc = j / RWG, rw0 = (j - wc * RWG) * 8;
+  const int lane = threadIdx.x & 63, l = lane & 31;
+  const int64_t rw = rw0 + 2 * (threadIdx.x >> 6) + (lane >> 5);
+  const bool ok = wc < KW && rw < WM;
   const uint32_t word = ok ? FP[(rw * 32 + l) * KW + wc].x : 0u;
   uint32_t out = 0;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint64_t m = __ballot((word >> j) & 1u);  // bit i: row i of the lane's tile
-    if (l == j) out = (threadIdx.x & 32) ? (uint32_t)(m >> 32) : (uint32_t)m;
+  for (int b = 0; b < 32; ++b) {
+    const uint64_t m = __ballot((word >> b) & 1u);  // bit i: row i of the lane's tile
+    if (l == b) out = (lane & 32) ? (uint32_t)(m >> 32) : (uint32_t)m;
   }
-  if (ok) FT[(wc * 32 + l) * WM + rw] = out;
-}
-
-// Per block of WT words of FT: popcount sums.
-__global__ __launch_bounds__(WT) void k_fp_tsum(const bm_state* st,
-                                                const uint32_t* __restrict__ FT, int64_t NT,
-                                                int4* __restrict__ tsum) {
-  __shared__ int32_t lds[WT / SNK_WAVE];
-  if (bm_failed(st)) return;
-  const int64_t i = (int64_t)blockIdx.x * WT + threadIdx.x;
-  int32_t c = i < NT ? __popc(FT[i]) : 0;
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, SNK_WAVE);
-  if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = c;
+  const int64_t c = wc * 32 + l;
+  if (ok) FT[c * WM + rw] = out;
+  // the FT blocks this block's words fall in: [tb_lo, tb_hi] (block-uniform)
+  const int64_t rw_last = std::min<int64_t>(rw0 + 7, WM - 1);
+  const int64_t tb_lo = (wc * 32 * WM + rw0) / WT;
+  const int64_t tb_hi = ((wc * 32 + 31) * WM + rw_last) / WT;
+  const bool in_lds = tb_hi - tb_lo < TS_SPAN;
+  if (in_lds)
+    for (int i = threadIdx.x; i < TS_SPAN; i += FP_THREADS) tsl[i] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t tot = 0;
-    for (int k = 0; k < WT / SNK_WAVE; ++k) tot += lds[k];
-    tsum[blockIdx.x] = make_int4(tot, 0, 0, 0);
+  const int32_t pc = ok ? __popc(out) : 0;
+  if (pc) {
+    const int64_t tb = (c * WM + rw) / WT;
+    if (in_lds) atomicAdd(&tsl[tb - tb_lo], pc);
+    else atomicAdd(&tsum[4 * tb], pc);  // .x of the block's int4
+  }
+  if (in_lds) {
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i <= tb_hi - tb_lo; i += FP_THREADS)
+      if (tsl[i]) atomicAdd(&tsum[4 * (tb_lo + i)], tsl[i]);
   }
 }
 
@@ -1068,7 +1083,10 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (results_begin(rw, 4, s) != hipSuccess) return SNACK_E_HIP;
   uint2* FP = fuse ? (uint2*)(ws + L.fp) : nullptr;
 
-  hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(4 * HREPL * 256, 256)), dim3(256), 0, s, st);
+  int32_t* tsum_zero = fuse ? (int32_t*)(ws + L.tsum) : nullptr;
+  const int64_t nzero = fuse ? 4 * L.nbt : 0;
+  hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(std::max<int64_t>(4 * HREPL * 256, nzero), 256)),
+                     dim3(256), 0, s, st, tsum_zero, nzero);
   const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
                           (uintptr_t)vals % (4 * sizeof(T)) == 0) ? 1 : 0;
   const int passes = sizeof(T) == 2 ? 2 : 4;
@@ -1120,11 +1138,9 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     uint32_t* FT = (uint32_t*)(ws + L.ft);
     int4* tsum = (int4*)(ws + L.tsum);
     int4* toff = (int4*)(ws + L.toff);
-    const int64_t tiles = (int64_t)(M / 32) * (K / 32);
-    const int64_t tb = cdiv(tiles * 32, FP_THREADS);
-    hipLaunchKernelGGL(k_fp_rows_transpose, dim3((unsigned)(L.rb + tb)), dim3(FP_THREADS), 0, s,
-                       st, FP, M, K, nnz, *fuse, (int32_t)L.rb, res_dev, FT);
-    hipLaunchKernelGGL(k_fp_tsum, dim3((unsigned)L.nbt), dim3(WT), 0, s, st, FT, L.NT, tsum);
+    const int64_t tblk = (int64_t)(K / 32) * cdiv((int64_t)(M / 32), 8);
+    hipLaunchKernelGGL(k_fp_rows_transpose, dim3((unsigned)(L.rb + tblk)), dim3(FP_THREADS), 0,
+                       s, st, FP, M, K, nnz, *fuse, (int32_t)L.rb, res_dev, FT, (int32_t*)tsum);
     const bool own_t = L.nbt <= PREFIX_INBLOCK_MAX;
     if (!own_t) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, tsum, toff, L.nbt);
     const int32_t cols_here = (WT % (M / 32)) == 0 ? 1 : 0;
