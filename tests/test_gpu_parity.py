@@ -243,6 +243,37 @@ def test_wave_lds_staged_inputs(orc, M, K, nnz, Bsz, dt):
     assert topo.plan.has_split_row == 0
 
 
+LARGE_CASES = [  # (M, K, nnz, B, dtype, layout): >= 16,384 segments, inputs over 64 KB
+    (16500, 20000, 1_300_000, 8, "bf16", "node"),
+    (16384, 16384, 1_000_000, 32, "bf16", "node"),
+    (16384, 16384, 800_000, 4, "f32", "node"),
+    (16390, 16500, 500_000, 16, "bf16", "batch"),   # batch-major in and out
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt,layout", LARGE_CASES)
+def test_large_layers_small_batches(orc, M, K, nnz, Bsz, dt, layout):
+    """Large layers at batches 4 to 32, whose node-major input does not fit
+    LDS: the gather kernels (forward, input gradient through perm and from
+    column-ordered values, forward with ReLU)."""
+    w = synth.random_case(28, M, K, nnz, Bsz, dt, layout)
+    wt = w.weights[0]
+    topo = run_products(orc, wt, w.X[0], w.dY[0], dt, layout, Bsz, sddmm=False,
+                        repeat_check=True)
+    assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
+    nm = layout == "node"
+    lay = B.NODE_MAJOR if nm else B.BATCH_MAJOR
+    vals = to_dev(wt.vals, dt)
+    dYd, Xd = to_dev(w.dY[0].data, dt), to_dev(w.X[0].data, dt)
+    dX = topo.bwd_input_t(topo.gather_vals_t(vals), dYd, Bsz, lay)
+    ref, S = orc.spmm_bwd_input(M, K, wt.row, wt.col, wt.vals_f64(), Bsz, w.dY[0].f64(), nm)
+    assert_within(from_dev(dX, dt), ref, S, dt, "bwd_input_t")
+    Y = torch.empty(Bsz * M, dtype=Xd.dtype, device="cuda")
+    snk.snack_spmm_fwd_act(topo.plan, vals, Xd, lay, Bsz, Y, snk.ACT_RELU)
+    ref, S = orc.spmm_fwd(M, K, wt.row, wt.col, wt.vals_f64(), Bsz, w.X[0].f64(), nm)
+    assert_within(from_dev(Y, dt), np.maximum(ref, 0.0), S, dt, "fwd relu")
+
+
 WIDE_CASES = [  # (M, K, nnz, B, dtype, layout): batches of several 64-column passes
     (300, 700, 21000, 128, "f32", "node"),
     (300, 700, 21000, 192, "f32", "batch"),    # batch-major through the node-major copy
