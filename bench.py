@@ -300,11 +300,13 @@ def read_traffic(name, launches_bytes):
         return None
 
 
-def dense_baselines(wt, X, batches, sparse_us):
+def dense_baselines(wt, X, batches, sparse_us, read_floor_us=None):
     """Forward time of the in-repo dense and Dense+Mask kernels
     (snack_dense_fwd) on the same layer, graph-timed like the sparse products
     and cold the same way (>= 512 MB of weights, masks and activations between
-    two uses of one copy).  sparse_us: the cold sparse forward per batch."""
+    two uses of one copy).  sparse_us: the cold sparse forward per batch;
+    read_floor_us: a cold streaming read of the dense weight's bytes on this
+    box (calibration), the floor the dense kernel's own weight stream meets."""
     import torch
     import unstructured_sparse_nn_amd as snk
     M, K = wt.M, wt.K
@@ -330,6 +332,9 @@ def dense_baselines(wt, X, batches, sparse_us):
             rec = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
                    "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "rotate": R,
                    "floor_us_at_8TBps": round(nbytes / HBM_PEAK_GBPS / 1e3, 2)}
+            if read_floor_us and not use_mask:
+                rec["weight_read_floor_us"] = read_floor_us
+                rec["over_weight_read_floor"] = round(us / read_floor_us, 2)
             if B in sparse_us:
                 rec["sparse_fwd_us"] = sparse_us[B]
                 rec["sparse_fwd_speedup"] = round(us / sparse_us[B], 2)
@@ -367,10 +372,11 @@ def calibrate():
         us = time_calls(lambda s=size, h=hops: snk.snack_calibrate(B_.CALIB_CHASE, buf, s, h),
                         reps=1, warm=warm)
         out[f"dependent_load_{name}_ns"] = round(us * 1e3 / hops, 1)
-    # reads of 5.6 MB (one 4096^2 product launch's bytes) and 1.0 MB (at 99%),
-    # each over distinct regions of the buffer (cold): the best a launch that
-    # size can do, launch, ramp and drain included
-    for tag, small in (("5.6MB", 5_573_888), ("1.0MB", 1_039_616)):
+    # reads of 5.6 MB (one 4096^2 product launch's bytes), 1.0 MB (at 99%) and
+    # 33.6 MB (the dense bf16 weight of the baselines), each over distinct
+    # regions of the buffer (cold): the best a launch that size can do,
+    # launch, ramp and drain included
+    for tag, small in (("5.6MB", 5_573_888), ("1.0MB", 1_039_616), ("33.6MB", 33_554_432)):
         regions = min(64, nbytes // small)
         base = buf.data_ptr()
         fns = [(lambda a=base + k * small: snk.snack_calibrate(B_.CALIB_READ, a, small, 2048))
@@ -976,7 +982,8 @@ def run_bench(args):
         log("dense baselines (cold)")
         sparse_us = {b: grid[f"N{N}_s{sp}_B{b}"]["fwd"]["us"] for b in (1, B)
                      if f"N{N}_s{sp}_B{b}" in grid}
-        rec["baselines"] = dense_baselines(wt, w.X[0], (1, B), sparse_us)
+        rec["baselines"] = dense_baselines(wt, w.X[0], (1, B), sparse_us,
+                                           (calib or {}).get("stream_read_33.6MB_us"))
     sizes = [int(x) for x in args.sizes.split(",") if x.strip()]
     if sizes:
         rec["sweep"] = time_ops_grid(sizes, (0.95, 0.99), (1, 8, 32))
