@@ -39,6 +39,14 @@
  *     Nothing aborts or prints.
  *   - concurrency: calls that share a plan's arena, or a workspace, must
  *     not overlap (they write the same scratch).
+ *   - debug build: libsnack_debug.so exports this same ABI; before any
+ *     product kernel its product entry points check, on the device and on
+ *     the call's stream, every plan array and COO index the kernels take
+ *     indices from (offsets from 0 to nnz and non-decreasing, indices and
+ *     perm in range, tiles and cut flags well formed), reading each array
+ *     only within the size the plan gives it, and return
+ *     SNACK_E_PLAN_CORRUPT without launching anything else on a violation.
+ *     Each product call then also synchronises its stream once.
  */
 #ifndef SNACK_H_
 #define SNACK_H_
@@ -501,7 +509,7 @@ SNACK_API snack_status snack_memory_footprint(int32_t M, int32_t K, int64_t nnz,
  * workgroup each per 64 batch columns) and the inputs are staged in tiles
  * of 256, so any M and K work.  Limits: M, K >= 1, nnz <= 2^23, at most
  * 65535 bands (else SNACK_E_SHAPE).  Code size and build time grow linearly
- * with nnz: about 8 bytes of code and 0.2 ms of compilation per entry (a
+ * with nnz: 13-22 bytes of code and 0.15-0.3 ms of compilation per entry (a
  * 4096 x 4096 layer at 95% sparsity takes minutes).  The handle owns the
  * loaded code object (device memory for code, the one exception to "no
  * allocation") until snack_fixed_free.  flags: SNACK_FIXED_COMPILE_ONLY

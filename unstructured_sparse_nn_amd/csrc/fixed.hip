@@ -23,7 +23,8 @@
 //     column with the value as an immediate operand (v_fmamk_f32);
 //   * results are rounded once to the activation type and stored coalesced.
 // Everything is in one kernel (one launch per forward); code size and
-// compile time grow linearly with nnz (about 8 bytes of code per entry).
+// compile time grow linearly with nnz (13-22 bytes of code per entry: one
+// FMA, plus a staged-input read per column of a wave's rows).
 #include <hip/hip_runtime.h>
 #include <hip/hiprtc.h>
 
