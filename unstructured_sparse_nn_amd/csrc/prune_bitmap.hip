@@ -251,6 +251,154 @@ __device__ void regrow_tail(int32_t c, uint64_t stream, uint64_t MK, int32_t n_d
   if (t == 0) st->rem_final = rem;
 }
 
+// Regrow chunk 0 without device atomics, for grids of up to 2^26 positions:
+// the chunk's positions are bucketed by region (2^16 positions, 2,048
+// bitmap words) by the bucketing workgroups (extra workgroups of the build
+// kernel), and each region's workgroup (extra workgroups of the first
+// select kernel) takes its candidates against S and an LDS copy of its G
+// words, which it then stores whole.  Taking every new distinct position of
+// the chunk is order-free, so the result is the same G as the atomic
+// test-and-set over the grid.
+constexpr int RB_SHIFT = 16;                      // positions per region: 2^16
+constexpr int RB_WORDS = 1 << (RB_SHIFT - 5);     // bitmap words per region
+constexpr int RB_PER = 16;                        // candidates per bucketing thread
+constexpr int RB_CH = RB_PER * BT;                // stream indices per bucketing workgroup
+constexpr int RB_MAXREG = 1024;                   // regions at most
+constexpr int RB_MAXWG = 1024;                    // bucketing workgroups at most
+
+// Bucketing workgroup j: stream indices [j*RB_CH, min(n_drop, (j+1)*RB_CH))
+// of chunk 0 as positions, grouped by region into cand[j*RB_CH ..) (any
+// order within a region), with tab[j*(nreg+1) + g] = the start of region
+// g's group in that slice and tab[j*(nreg+1) + nreg] = the slice's count.
+// BT threads.
+__device__ void bucket_chunk0(int64_t j, uint64_t stream, uint64_t MK, int32_t n_drop,
+                              int32_t nreg, uint32_t* __restrict__ cand,
+                              int32_t* __restrict__ tab) {
+  __shared__ int32_t h[RB_MAXREG];
+  __shared__ int32_t lds[BT / SNK_WAVE];
+  const int t = threadIdx.x;
+  for (int g = t; g < nreg; g += BT) h[g] = 0;
+  __syncthreads();
+  const int64_t i0 = j * RB_CH;
+  uint32_t p[RB_PER];
+  int32_t rk[RB_PER];
+#pragma unroll
+  for (int u = 0; u < RB_PER; ++u) {
+    const int64_t i = i0 + u * BT + t;
+    p[u] = i < n_drop ? (uint32_t)sm64_position(stream, (uint64_t)i, MK) : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < RB_PER; ++u)
+    rk[u] = i0 + u * BT + t < n_drop ? atomicAdd(&h[p[u] >> RB_SHIFT], 1) : -1;
+  __syncthreads();
+  constexpr int GPT = RB_MAXREG / BT;  // regions per thread in the scan
+  int32_t v[GPT], sum = 0;
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int g = t * GPT + k;
+    v[k] = g < nreg ? h[g] : 0;
+    sum += v[k];
+  }
+  int32_t tot;
+  int32_t ex = block_excl_scan_i32<BT>(sum, lds, &tot);  // its barriers order the reads of h
+  int32_t* row_tab = tab + j * (nreg + 1);
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int g = t * GPT + k;
+    if (g < nreg) {
+      h[g] = ex;
+      row_tab[g] = ex;
+    }
+    ex += v[k];
+  }
+  if (t == 0) row_tab[nreg] = tot;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < RB_PER; ++u)
+    if (rk[u] >= 0) cand[i0 + h[p[u] >> RB_SHIFT] + rk[u]] = p[u];
+}
+
+// Region g's workgroup of chunk 0 (BT threads): its candidates from the nwg
+// bucketing slices, each taken if outside S and new in G (an LDS
+// test-and-set); the region's G words are stored whole (zeros included) and
+// the count taken is added into chunk 0's acceptance counters.
+__device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t nreg,
+                              int32_t nwg, int64_t W, const uint32_t* __restrict__ cand,
+                              const int32_t* __restrict__ tab, const uint32_t* __restrict__ sup,
+                              uint32_t* __restrict__ grown) {
+  __shared__ uint32_t Ss[RB_WORDS], Gs[RB_WORDS];
+  __shared__ int32_t run0[RB_MAXWG], start[RB_MAXWG];
+  __shared__ int32_t lds[BT / SNK_WAVE];
+  const int t = threadIdx.x;
+  const int64_t wbase = (int64_t)g * RB_WORDS;
+  for (int k = t; k < RB_WORDS; k += BT) {
+    const int64_t w = wbase + k;
+    Ss[k] = w < W ? sup[w] : 0xFFFFFFFFu;
+    Gs[k] = 0u;
+  }
+  constexpr int WPTH = RB_MAXWG / BT;  // slices per thread in the scan
+  int32_t a[WPTH], len[WPTH], sum = 0;
+#pragma unroll
+  for (int k = 0; k < WPTH; ++k) {
+    const int wgi = t * WPTH + k;
+    a[k] = wgi < nwg ? tab[(int64_t)wgi * (nreg + 1) + g] : 0;
+    len[k] = wgi < nwg ? tab[(int64_t)wgi * (nreg + 1) + g + 1] - a[k] : 0;
+    sum += len[k];
+  }
+  int32_t n_g;
+  int32_t ex = block_excl_scan_i32<BT>(sum, lds, &n_g);
+#pragma unroll
+  for (int k = 0; k < WPTH; ++k) {
+    const int wgi = t * WPTH + k;
+    if (wgi < nwg) {
+      run0[wgi] = ex;
+      start[wgi] = wgi * RB_CH + a[k];
+    }
+    ex += len[k];
+  }
+  __syncthreads();
+  int32_t taken = 0;
+  for (int32_t b0 = 0; b0 < n_g; b0 += 4 * BT) {
+    uint32_t pc[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t e = b0 + u * BT + t;
+      ok[u] = e < n_g;
+      int lo = 0, hi = nwg;  // the last slice whose run starts at or before e
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (run0[mid] <= e) lo = mid + 1;
+        else hi = mid;
+      }
+      const int wgi = lo > 0 ? lo - 1 : 0;
+      pc[u] = ok[u] ? cand[start[wgi] + (e - run0[wgi])] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!ok[u]) continue;
+      const uint32_t loc = pc[u] & ((1u << RB_SHIFT) - 1u);
+      const uint32_t bit = 1u << (loc & 31);
+      if (Ss[loc >> 5] & bit) continue;
+      if (!(atomicOr(&Gs[loc >> 5], bit) & bit)) ++taken;
+    }
+  }
+  __syncthreads();
+  for (int k = t; k < RB_WORDS; k += BT) {
+    const int64_t w = wbase + k;
+    if (w < W) grown[w] = Gs[k];
+  }
+  int32_t tot;
+  block_excl_scan_i32<BT>(taken, lds, &tot);
+  if (t == 0) {
+    if (tot) atomicAdd(&st->ch_acc[0][g % AREPL], tot);
+    if (g == 0) {
+      st->ch_start[0] = 0;
+      st->ch_rem[0] = n_drop;
+    }
+  }
+}
+
 // The entries a block needs beyond its own, loaded by every thread next to
 // the block's main loads (clamped indices, no branch, one round trip) and
 // kept by a few threads in LDS: the linear index of entry base-1 (-1 for
@@ -322,14 +470,21 @@ __device__ __forceinline__ void last_word(const int64_t (&l)[4], int n, int64_t*
   }
 }
 
-// Support bitmap S (and G cleared), a copy of the values, the NaN / index /
-// order checks and the first select histogram.  Thread t holds entries
-// base + 4t .. base + 4t + 3.
+// Support bitmap S (and G cleared, unless chunk 0 is bucketed: grown is
+// then NULL), a copy of the values, the NaN / index / order checks and the
+// first select histogram.  Thread t holds entries base + 4t .. base + 4t + 3.
+// Workgroups from nblk on bucket regrow chunk 0 (bucket_chunk0).
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_build(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
     int64_t nnz, int32_t M, int32_t K, int64_t W, int shift, int32_t vec_ok, bm_state* st,
-    uint32_t* __restrict__ sup, uint32_t* __restrict__ grown, T* __restrict__ vals_ws) {
+    uint32_t* __restrict__ sup, uint32_t* __restrict__ grown, T* __restrict__ vals_ws,
+    int64_t nblk, uint64_t stream, uint64_t MK, int32_t n_drop, int32_t nreg,
+    uint32_t* __restrict__ cand, int32_t* __restrict__ tab) {
+  if ((int64_t)blockIdx.x >= nblk) {  // bucketing workgroups of regrow chunk 0
+    bucket_chunk0((int64_t)blockIdx.x - nblk, stream, MK, n_drop, nreg, cand, tab);
+    return;
+  }
   __shared__ int32_t h[256];
   __shared__ uint32_t buf[CAP];
   __shared__ int64_t lastl[BT];
@@ -415,17 +570,24 @@ __global__ __launch_bounds__(BT) void k_bi_build(
 
 // Select pass `pass` >= 1: pick the previous pass's digit, histogram the
 // next digit of the entries matching the prefix.  Workgroups from nblk on
-// run regrow chunk c.
+// run regrow chunk c (with nwg > 0: chunk 0 by region, region_chunk0).
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64_t nnz,
                                                int64_t nblk, int pass, int prev_shift, int shift,
                                                int32_t n_drop, int32_t c, uint64_t stream,
                                                uint64_t MK, bm_state* st,
                                                const uint32_t* __restrict__ sup,
-                                               uint32_t* __restrict__ grown) {
+                                               uint32_t* __restrict__ grown, int32_t nreg,
+                                               int32_t nwg, int64_t W,
+                                               const uint32_t* __restrict__ cand,
+                                               const int32_t* __restrict__ tab) {
   __shared__ int32_t h[256];
   if ((int64_t)blockIdx.x >= nblk) {
-    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+    if (nwg > 0)  // chunk 0 from the buckets, one workgroup per region
+      region_chunk0((int32_t)(blockIdx.x - nblk), st, n_drop, nreg, nwg, W, cand, tab, sup,
+                    grown);
+    else
+      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
     return;
   }
   const int t = threadIdx.x;
@@ -1001,6 +1163,8 @@ struct bm_layout {
   int64_t nblk, W, nb, NT, nbt, rb, cbk;
   size_t res, state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
   size_t fp, ft, tsum, toff, total;  // fused prepare
+  int64_t nreg, rwg;                  // regions and bucketing workgroups (0: chunk 0 atomic)
+  size_t cand, tab;
 };
 
 bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
@@ -1032,6 +1196,14 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
   L.ft = take(4 * (size_t)L.NT);
   L.tsum = take(16 * (size_t)L.nbt);
   L.toff = take(16 * (size_t)L.nbt);
+  // chunk 0 by region: up to 2^26 positions and n_drop <= nnz (bucketing
+  // workgroups capped at RB_MAXWG)
+  const int64_t MK = (int64_t)M * K;
+  L.nreg = cdiv(MK, (int64_t)1 << RB_SHIFT);
+  L.rwg = (MK <= ((int64_t)1 << 26) && L.nreg <= RB_MAXREG)
+              ? std::min<int64_t>(cdiv(nnz, RB_CH), RB_MAXWG) : 0;
+  L.cand = take(4 * (size_t)L.rwg * RB_CH);
+  L.tab = take(4 * (size_t)L.rwg * (size_t)(L.nreg + 1));
   L.total = o;
   return L;
 }
@@ -1091,8 +1263,14 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
                           (uintptr_t)vals % (4 * sizeof(T)) == 0) ? 1 : 0;
   const int passes = sizeof(T) == 2 ? 2 : 4;
   const int top = 8 * (passes - 1);
-  hipLaunchKernelGGL(k_bi_build<T>, eb, et, 0, s, row, col, vals, nnz, M, K, L.W, top, vec_ok, st,
-                     sup, grown, vals_ws);
+  // chunk 0 bucketed by region when the layout has room for its n_drop
+  const int64_t nwg = cdiv(n_drop, (int64_t)RB_CH);
+  const bool bucket = L.rwg > 0 && nwg <= L.rwg;
+  uint32_t* cand = (uint32_t*)(ws + L.cand);
+  int32_t* tab = (int32_t*)(ws + L.tab);
+  hipLaunchKernelGGL(k_bi_build<T>, dim3((unsigned)(L.nblk + (bucket ? nwg : 0))), et, 0, s, row,
+                     col, vals, nnz, M, K, L.W, top, vec_ok, st, sup, bucket ? nullptr : grown,
+                     vals_ws, L.nblk, stream, MK, nd, (int32_t)L.nreg, cand, tab);
   // entry workgroups plus the workgroups of regrow chunk c, sized for the
   // positions expected to be missing at its start
   const double q = accept_bound((int64_t)MK, nnz, n_drop);
@@ -1102,9 +1280,13 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     return dim3((unsigned)(L.nblk + rb));
   };
   int32_t c = 0;
-  for (int p = 1; p < passes; ++p, ++c)
-    hipLaunchKernelGGL(k_bi_sel<T>, with_chunk(c), et, 0, s, vals, nnz, L.nblk, p,
-                       top - 8 * (p - 1), top - 8 * p, nd, c, stream, MK, st, sup, grown);
+  for (int p = 1; p < passes; ++p, ++c) {
+    const bool by_region = bucket && c == 0;
+    const dim3 g = by_region ? dim3((unsigned)(L.nblk + L.nreg)) : with_chunk(c);
+    hipLaunchKernelGGL(k_bi_sel<T>, g, et, 0, s, vals, nnz, L.nblk, p, top - 8 * (p - 1),
+                       top - 8 * p, nd, c, stream, MK, st, sup, grown, (int32_t)L.nreg,
+                       by_region ? (int32_t)nwg : 0, L.W, cand, tab);
+  }
   hipLaunchKernelGGL(k_bi_count<T>, with_chunk(c), et, 0, s, vals, nnz, L.nblk, passes - 1, 0, nd,
                      c, stream, MK, st, cnt_eq, sup, grown);
   ++c;
