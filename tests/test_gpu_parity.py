@@ -843,10 +843,13 @@ def test_gelu_matches_oracle(orc):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("masked", [False, True])
-@pytest.mark.parametrize("Bsz,K", [(1, 1000), (5, 1000), (32, 1024), (40, 997)])
+@pytest.mark.parametrize("Bsz,K", [(1, 1000), (1, 4096), (1, 4104), (5, 1000), (16, 4096),
+                                   (32, 1024), (40, 997)])
 def test_dense_baseline(orc, dt, masked, Bsz, K):
     """Dense and Dense+Mask reference kernels against a numpy product, on
-    every batch-tile path, aligned and ragged K."""
+    every batch-tile path (batch 1 with X held in registers up to K = 4096,
+    the weight stream beyond it and for batches up to 8, the 16-row matrix
+    core tiles from 16 on), aligned and ragged K."""
     w = synth.random_case(6, 300, K, 30000, Bsz, dt)
     wt = w.weights[0]
     rng = np.random.default_rng(1)

@@ -171,108 +171,6 @@ __global__ __launch_bounds__(NTH) void k_dense_fwd(const T* __restrict__ W,
   }
 }
 
-// bf16, batch >= 16: a 32-row x 32-batch output tile per workgroup on the
-// matrix cores (v_mfma_f32_32x32x8bf16_1k: D[i][j] += sum_k A[i][k] B[k][j]
-// with A = 32 rows of W, B[k][j] = X[b0+j][k]).  In an 8-wide step lane l
-// supplies A[l%32][4q..4q+3] and B[4q..4q+3][l%32] (q = l/32) and receives
-// rows 8(v/4) + 4q + v%4 of column l%32 in its 16 results.  Which k feeds
-// which step slot is free as long as A and B agree, so each lane loads 8
-// consecutive k (16 bytes of W and of X) and feeds them to two steps.  The
-// K axis is split over the DM_WAVES waves of the workgroup; the partial
-// tiles are summed in LDS.
-constexpr int DM_WAVES = 8;
-constexpr int DM_UNROLL = 8;  // 16-wide k groups per iteration
-
-typedef short dm_short4 __attribute__((ext_vector_type(4)));
-typedef float dm_float16 __attribute__((ext_vector_type(16)));
-
-// 8 consecutive bf16 p[base + k .. +7] (0 past K or outside the mask) as two
-// MFMA fragments.
-template <bool MASK>
-__device__ __forceinline__ void dm_load8(const bf16* __restrict__ p, const uint8_t* __restrict__ m,
-                                         int64_t base, int64_t k, int32_t K, bool ok, bool aligned,
-                                         dm_short4& lo, dm_short4& hi) {
-  lo = dm_short4{0, 0, 0, 0};
-  hi = dm_short4{0, 0, 0, 0};
-  if (!ok) return;
-  short v[8];
-  if (aligned && k + 8 <= K) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p + base + k);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = (short)(ws[e] & 0xFFFFu);
-      v[2 * e + 1] = (short)(ws[e] >> 16);
-    }
-    if (MASK) {
-      const uint2 mm = *reinterpret_cast<const uint2*>(m + base + k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((((e < 4 ? mm.x : mm.y) >> (8 * (e & 3))) & 0xFFu) == 0) v[e] = 0;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool in = k + e < K && (!MASK || m[base + k + e]);
-      v[e] = in ? (short)p[base + k + e] : (short)0;
-    }
-  }
-  lo = dm_short4{v[0], v[1], v[2], v[3]};
-  hi = dm_short4{v[4], v[5], v[6], v[7]};
-}
-
-template <bool MASK>
-__global__ __launch_bounds__(64 * DM_WAVES) void k_dense_mfma(const bf16* __restrict__ W,
-                                                              const uint8_t* __restrict__ mask,
-                                                              int32_t M, int32_t K,
-                                                              const bf16* __restrict__ X,
-                                                              int32_t B, bf16* __restrict__ Y,
-                                                              int32_t vec_ok) {
-  __shared__ float part[DM_WAVES][16][64];
-  const int wv = threadIdx.x / SNK_WAVE, l = lane_id();
-  const int32_t r0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
-  const int32_t i = l & 31, q = l >> 5;
-  const int32_t r = r0 + i, b = b0 + i;
-  const bool r_ok = r < M, b_ok = b < B;
-  const int64_t wbase = (int64_t)r * K, xbase = (int64_t)b * K;
-  const bool aligned = vec_ok && (K % 8) == 0;
-  // this wave's share of the K axis, in 16-wide groups
-  const int32_t groups = (K + 15) / 16;
-  const int32_t per = (groups + DM_WAVES - 1) / DM_WAVES;
-  const int32_t g0 = wv * per, g1 = min(groups, g0 + per);
-  dm_float16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  for (int32_t g = g0; g < g1; g += DM_UNROLL) {
-    dm_short4 alo[DM_UNROLL], ahi[DM_UNROLL], blo[DM_UNROLL], bhi[DM_UNROLL];
-#pragma unroll
-    for (int u = 0; u < DM_UNROLL; ++u) {
-      const int64_t k = (int64_t)(g + u) * 16 + 8 * q;
-      const bool ok = g + u < g1;
-      dm_load8<MASK>(W, mask, wbase, k, K, r_ok && ok, aligned, alo[u], ahi[u]);
-      dm_load8<false>(X, nullptr, xbase, k, K, b_ok && ok, aligned, blo[u], bhi[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < DM_UNROLL; ++u) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(alo[u], blo[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ahi[u], bhi[u], acc, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) part[wv][v][l] = acc[v];
-  __syncthreads();
-  // 16 x 64 results; the workgroup's 512 threads take two each
-  for (int e = threadIdx.x; e < 16 * 64; e += 64 * DM_WAVES) {
-    const int v = e / 64, ll = e % 64;
-    float sum = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < DM_WAVES; ++w2) sum += part[w2][v][ll];
-    const int32_t rr = r0 + 8 * (v / 4) + 4 * (ll >> 5) + (v % 4);
-    const int32_t bo = b0 + (ll & 31);
-    if (rr < M && bo < B) Y[(int64_t)bo * M + rr] = f32_to_bf16(sum);
-  }
-}
-
 // Small batches (B <= 8) as a weight stream: each wave owns RW rows and the
 // whole batch; per 512-wide step each lane takes 8 consecutive k (16 bytes
 // of bf16 W, 32 of fp32), and U steps' loads of W, of the mask and of X (read
@@ -372,6 +270,178 @@ __global__ __launch_bounds__(256) void k_dense_stream(const T* __restrict__ W,
   }
 }
 
+// Batch 1, bf16, K <= 4096 and a multiple of 8 (16-byte aligned rows): each
+// wave takes two rows; lane l holds x[512 j + 8 l .. +7] for every j in
+// registers, and the chunks of X and of both rows are requested together
+// (16 KB of W per wave, the whole weight in flight over the GPU), so the
+// product is one round trip of a non-temporal weight stream.
+typedef uint32_t dn_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t dn_u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 dn_bf2 __attribute__((ext_vector_type(2)));
+constexpr int G1_NC = 8;  // 512-wide chunks: K <= 4096
+
+// The bf16 halves of w (elements 2e, 2e+1 of a chunk) whose mask byte is 0
+// cleared; mm holds the chunk's 8 mask bytes.
+__device__ __forceinline__ uint32_t mask_pair(uint32_t w, dn_u32x2 mm, int e) {
+  const uint32_t mb = ((e < 2 ? mm.x : mm.y) >> (16 * (e & 1))) & 0xFFFFu;
+  const uint32_t keep = ((mb & 0xFFu) ? 0x0000FFFFu : 0u) | ((mb >> 8) ? 0xFFFF0000u : 0u);
+  return w & keep;
+}
+
+template <bool MASK>
+__global__ __launch_bounds__(256) void k_dense_gemv1(const bf16* __restrict__ W,
+                                                     const uint8_t* __restrict__ mask, int32_t M,
+                                                     int32_t K, const bf16* __restrict__ X,
+                                                     bf16* __restrict__ Y) {
+  const int wv = threadIdx.x / SNK_WAVE, l = lane_id();
+  const int32_t r0 = ((int32_t)blockIdx.x * 4 + wv) * 2;
+  if (r0 >= M) return;
+  const int32_t r1 = min(r0 + 1, M - 1);  // a missing second row repeats the first, unstored
+  const dn_u32x4 z4 = {0u, 0u, 0u, 0u};
+  const dn_u32x2 z2 = {0u, 0u};
+  dn_u32x4 x[G1_NC], w0[G1_NC], w1[G1_NC];
+  dn_u32x2 m0[G1_NC], m1[G1_NC];
+#pragma unroll
+  for (int j = 0; j < G1_NC; ++j) {
+    const int32_t k = 512 * j + 8 * l;
+    const bool ok = k < K;
+    x[j] = ok ? *reinterpret_cast<const dn_u32x4*>(X + k) : z4;
+    w0[j] = ok ? __builtin_nontemporal_load(
+                     reinterpret_cast<const dn_u32x4*>(W + (int64_t)r0 * K + k))
+               : z4;
+    w1[j] = ok ? __builtin_nontemporal_load(
+                     reinterpret_cast<const dn_u32x4*>(W + (int64_t)r1 * K + k))
+               : z4;
+    if (MASK) {
+      m0[j] = ok ? __builtin_nontemporal_load(
+                       reinterpret_cast<const dn_u32x2*>(mask + (int64_t)r0 * K + k))
+                 : z2;
+      m1[j] = ok ? __builtin_nontemporal_load(
+                       reinterpret_cast<const dn_u32x2*>(mask + (int64_t)r1 * K + k))
+                 : z2;
+    }
+  }
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < G1_NC; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // vector elements are copied out first: a bit cast of the element
+      // expression itself read element 0
+      uint32_t p0 = w0[j][e], p1 = w1[j][e];
+      const uint32_t xe = x[j][e];
+      if (MASK) {
+        p0 = mask_pair(p0, m0[j], e);
+        p1 = mask_pair(p1, m1[j], e);
+      }
+      const dn_bf2 xv = __builtin_bit_cast(dn_bf2, xe);
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dn_bf2, p0), xv, a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dn_bf2, p1), xv, a1, false);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    a0 += __shfl_xor(a0, off, SNK_WAVE);
+    a1 += __shfl_xor(a1, off, SNK_WAVE);
+  }
+  if (l == 0) {
+    Y[r0] = f32_to_bf16(a0);
+    if (r0 + 1 < M) Y[r0 + 1] = f32_to_bf16(a1);
+  }
+}
+
+// bf16 batches of 16 or more on the matrix cores with 16-row output tiles
+// (twice the workgroups of 32-row tiles, so that a 4096-row layer fills the
+// 256 CUs): each workgroup owns 16 rows x 32 batch columns, its 8 waves
+// split K, each step of 32 k is one v_mfma_f32_16x16x32_bf16 per 16 batch
+// columns (lane l: row / column l mod 16, k 8 (l / 16) .. +7; the result's
+// lane l holds column l mod 16, rows 4 (l / 16) .. +3), and the partial
+// tiles are summed in LDS.
+typedef __bf16 dn_bf8 __attribute__((ext_vector_type(8)));
+typedef float dn_f4 __attribute__((ext_vector_type(4)));
+constexpr int D16_WAVES = 8;
+constexpr int D16_UNROLL = 4;
+
+// 8 consecutive bf16 p[base + k .. +7] (0 past K or outside the mask).
+template <bool MASK>
+__device__ __forceinline__ dn_bf8 d16_load(const bf16* __restrict__ p,
+                                           const uint8_t* __restrict__ m, int64_t base,
+                                           int64_t k, int32_t K, bool ok, bool aligned) {
+  uint32_t v[4] = {0u, 0u, 0u, 0u};
+  if (ok) {
+    if (aligned && k + 8 <= K) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p + base + k);
+      v[0] = w.x;
+      v[1] = w.y;
+      v[2] = w.z;
+      v[3] = w.w;
+      if (MASK) {
+        const uint2 mm = *reinterpret_cast<const uint2*>(m + base + k);
+        const dn_u32x2 m2 = {mm.x, mm.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = mask_pair(v[e], m2, e);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = k + e < K && (!MASK || m[base + k + e]);
+        const uint32_t h = in ? (uint32_t)p[base + k + e] : 0u;
+        v[e / 2] |= h << (16 * (e & 1));
+      }
+    }
+  }
+  return __builtin_bit_cast(dn_bf8, v);
+}
+
+template <bool MASK>
+__global__ __launch_bounds__(64 * D16_WAVES) void k_dense_mfma16(
+    const bf16* __restrict__ W, const uint8_t* __restrict__ mask, int32_t M, int32_t K,
+    const bf16* __restrict__ X, int32_t B, bf16* __restrict__ Y, int32_t vec_ok) {
+  __shared__ float part[D16_WAVES][2][4][64];
+  const int wv = threadIdx.x / SNK_WAVE, l = lane_id();
+  const int32_t r0 = blockIdx.x * 16, b0 = blockIdx.y * 32;
+  const int32_t i = l & 15, q = l >> 4;
+  const int32_t r = r0 + i, bA = b0 + i, bB = b0 + 16 + i;
+  const bool r_ok = r < M, a_ok = bA < B, b_ok = bB < B;
+  const int64_t wbase = (int64_t)r * K, xa = (int64_t)bA * K, xb = (int64_t)bB * K;
+  const bool aligned = vec_ok && (K % 8) == 0;
+  const int32_t groups = (K + 31) / 32;  // 32-wide k groups
+  const int32_t per = (groups + D16_WAVES - 1) / D16_WAVES;
+  const int32_t g0 = wv * per, g1 = min(groups, g0 + per);
+  dn_f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t g = g0; g < g1; g += D16_UNROLL) {
+    dn_bf8 a[D16_UNROLL], xa8[D16_UNROLL], xb8[D16_UNROLL];
+#pragma unroll
+    for (int u = 0; u < D16_UNROLL; ++u) {
+      const int64_t k = (int64_t)(g + u) * 32 + 8 * q;
+      const bool ok = g + u < g1;
+      a[u] = d16_load<MASK>(W, mask, wbase, k, K, r_ok && ok, aligned);
+      xa8[u] = d16_load<false>(X, nullptr, xa, k, K, a_ok && ok, aligned);
+      xb8[u] = d16_load<false>(X, nullptr, xb, k, K, b_ok && ok, aligned);
+    }
+#pragma unroll
+    for (int u = 0; u < D16_UNROLL; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], xa8[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], xb8[u], acc1, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    part[wv][0][v][l] = acc0[v];
+    part[wv][1][v][l] = acc1[v];
+  }
+  __syncthreads();
+  // 16 x 32 results, one per thread: row ri, batch column bj
+  const int e = threadIdx.x;
+  const int ri = e & 15, bj = e >> 4;
+  const int half = bj >> 4, col = bj & 15;
+  const int lane = col + 16 * (ri >> 2), v = ri & 3;
+  float sum = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < D16_WAVES; ++w2) sum += part[w2][half][v][lane];
+  const int32_t rr = r0 + ri, bo = b0 + bj;
+  if (rr < M && bo < B) Y[(int64_t)bo * M + rr] = f32_to_bf16(sum);
+}
+
 // Batches up to 8 take the weight stream; wider ones stage chunks of X in
 // LDS, with rows per workgroup growing with the batch tile, so that the
 // staged chunk is shared by enough rows (16 rows for 32 batch columns).
@@ -407,15 +477,25 @@ static void launch_dense(const T* W, const uint8_t* mask, int32_t M, int32_t K, 
 hipError_t launch_dense_fwd(const void* W, const uint8_t* mask, snack_dtype dt, int32_t M,
                             int32_t K, const void* X, int32_t B, void* Y, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (dt == SNACK_BF16 && B >= 16) {
-    const dim3 grid((unsigned)cdiv(M, 32), (unsigned)cdiv(B, 32));
-    const int32_t vec_ok = ((uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0 &&
-                            (uintptr_t)mask % 8 == 0) ? 1 : 0;
+  const bool al16 = (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)mask % 8 == 0;
+  if (dt == SNACK_BF16 && B == 1 && al16 && K % 8 == 0 && K <= 512 * G1_NC) {
+    const dim3 grid((unsigned)cdiv(M, 8));
     if (mask)
-      hipLaunchKernelGGL(k_dense_mfma<true>, grid, dim3(64 * DM_WAVES), 0, s, (const bf16*)W,
+      hipLaunchKernelGGL(k_dense_gemv1<true>, grid, dim3(256), 0, s, (const bf16*)W, mask, M, K,
+                         (const bf16*)X, (bf16*)Y);
+    else
+      hipLaunchKernelGGL(k_dense_gemv1<false>, grid, dim3(256), 0, s, (const bf16*)W, mask, M, K,
+                         (const bf16*)X, (bf16*)Y);
+    return hipGetLastError();
+  }
+  if (dt == SNACK_BF16 && B >= 16) {
+    const dim3 grid((unsigned)cdiv(M, 16), (unsigned)cdiv(B, 32));
+    const int32_t vec_ok = al16 ? 1 : 0;
+    if (mask)
+      hipLaunchKernelGGL(k_dense_mfma16<true>, grid, dim3(64 * D16_WAVES), 0, s, (const bf16*)W,
                          mask, M, K, (const bf16*)X, B, (bf16*)Y, vec_ok);
     else
-      hipLaunchKernelGGL(k_dense_mfma<false>, grid, dim3(64 * DM_WAVES), 0, s, (const bf16*)W,
+      hipLaunchKernelGGL(k_dense_mfma16<false>, grid, dim3(64 * D16_WAVES), 0, s, (const bf16*)W,
                          mask, M, K, (const bf16*)X, B, (bf16*)Y, vec_ok);
     return hipGetLastError();
   }
