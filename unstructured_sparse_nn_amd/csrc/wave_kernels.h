@@ -176,6 +176,27 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
 constexpr int WL_THREADS = 1024;
 constexpr int WL_LDS = 64 * 1024;
 constexpr int WL_MIN_SEGMENTS = 16384;
+// Fewer segments still take the LDS path when the input is large enough
+// that the gathers miss the L1 cache often and segments are long enough
+// (>= 256 entries on average) to amortise the staging.  Measured: the
+// LLaMA-shaped column views' input gradient 10-22% faster (22-32 KB
+// inputs); at 16 KB (8192^2, batch 1) the value gradient 18% faster but the
+// products 5% slower, hence the two sizes; inputs of a few KB (4096^2 at
+// batch 1) and short segments (4096^2 at batch 8) lose to the cached gathers.
+constexpr int WL_MID_SEGMENTS = 2048;
+constexpr int64_t WL_MID_BYTES_SPMM = 20 * 1024;
+constexpr int64_t WL_MID_BYTES_SDDMM = 16 * 1024;
+constexpr int64_t WL_MID_AVG = 256;
+
+// Whether a view takes the LDS-staged kernels (one batch pass and no split
+// segment are checked by the caller); mid_bytes: the product's input-size
+// bound for views of fewer than WL_MIN_SEGMENTS segments.
+inline bool wave_lds_fits(const seg_view& v, int64_t x_bytes, const void* Xt,
+                          int64_t mid_bytes) {
+  if (x_bytes > WL_LDS || (uintptr_t)Xt % 16 != 0) return false;
+  if (v.S >= WL_MIN_SEGMENTS) return true;
+  return v.S >= WL_MID_SEGMENTS && x_bytes >= mid_bytes && v.nnz >= WL_MID_AVG * v.S;
+}
 
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 __global__ __launch_bounds__(WL_THREADS) void k_wave_spmm_lds(
@@ -425,8 +446,8 @@ static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
   const int32_t sblk = xb ? xb * NUM_XCD : nblk;
   const int64_t x_elems = (int64_t)v.F * B;
-  if (!v.has_split && passes == 1 && v.S >= WL_MIN_SEGMENTS &&
-      x_elems * (int64_t)sizeof(T) <= WL_LDS && (uintptr_t)Xt % 16 == 0) {
+  if (!v.has_split && passes == 1 &&
+      wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SPMM)) {
     // two workgroups per CU (their LDS), or one per 16 segments if fewer
     const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
     hipLaunchKernelGGL((k_wave_spmm_lds<T, CH, LPE, PERM, NODE_OUT, ACT>), dim3((unsigned)wl_blk),
@@ -502,8 +523,8 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
   const int32_t long_len = v.has_split ? v.tile : INT32_MAX;
   // X in LDS (see k_wave_spmm_lds): one batch pass, many rows, no split row
   const int64_t x_elems = (int64_t)v.F * B;
-  const bool lds_ok = !v.has_split && v.S >= WL_MIN_SEGMENTS &&
-                      x_elems * (int64_t)sizeof(T) <= WL_LDS && (uintptr_t)Xt % 16 == 0;
+  const bool lds_ok =
+      !v.has_split && wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SDDMM);
   const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
   const size_t lds_bytes = align_up((size_t)(x_elems * sizeof(T)), 16);
 #define SNK_WSD1(L, MULTI)                                                                      \
