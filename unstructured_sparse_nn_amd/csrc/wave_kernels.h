@@ -174,7 +174,16 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
 // stream; from LDS they cost a few LDS cycles per 64 entries.  One batch pass
 // (B <= LPE * CH); no split segments.
 constexpr int WL_THREADS = 1024;
-constexpr int WL_LDS = 64 * 1024;
+// gfx950 gives a workgroup up to 160 KB of LDS (the CU's whole LDS): inputs
+// above half of it run one workgroup per CU, smaller ones two.  With one
+// workgroup per CU only one lane per entry pays off (measured: 8192^2 at
+// B=8 and the LLaMA up input gradient at B=4 11-32% faster, the LLaMA down
+// input gradient at B=16, two lanes per entry, 9% slower).
+constexpr int WL_LDS = 160 * 1024;
+inline int32_t wave_lds_blocks(int64_t x_bytes, int32_t S) {
+  const int64_t per_cu = x_bytes > WL_LDS / 2 ? 1 : 2;
+  return (int32_t)std::min<int64_t>(per_cu * 256, cdiv(S, WL_THREADS / SNK_WAVE));
+}
 constexpr int WL_MIN_SEGMENTS = 16384;
 // Fewer segments still take the LDS path when the input is large enough
 // that the gathers miss the L1 cache often and segments are long enough
@@ -192,8 +201,9 @@ constexpr int64_t WL_MID_AVG = 256;
 // segment are checked by the caller); mid_bytes: the product's input-size
 // bound for views of fewer than WL_MIN_SEGMENTS segments.
 inline bool wave_lds_fits(const seg_view& v, int64_t x_bytes, const void* Xt,
-                          int64_t mid_bytes) {
+                          int64_t mid_bytes, int lpe) {
   if (x_bytes > WL_LDS || (uintptr_t)Xt % 16 != 0) return false;
+  if (x_bytes > WL_LDS / 2 && lpe > 1) return false;
   if (v.S >= WL_MIN_SEGMENTS) return true;
   return v.S >= WL_MID_SEGMENTS && x_bytes >= mid_bytes && v.nnz >= WL_MID_AVG * v.S;
 }
@@ -447,9 +457,9 @@ static void wave_spmm_t(const seg_view& v, const void* vals, const void* Xt, int
   const int32_t sblk = xb ? xb * NUM_XCD : nblk;
   const int64_t x_elems = (int64_t)v.F * B;
   if (!v.has_split && passes == 1 &&
-      wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SPMM)) {
+      wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SPMM, LPE)) {
     // two workgroups per CU (their LDS), or one per 16 segments if fewer
-    const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
+    const int32_t wl_blk = wave_lds_blocks(x_elems * (int64_t)sizeof(T), v.S);
     hipLaunchKernelGGL((k_wave_spmm_lds<T, CH, LPE, PERM, NODE_OUT, ACT>), dim3((unsigned)wl_blk),
                        dim3(WL_THREADS), (size_t)align_up((size_t)(x_elems * sizeof(T)), 16), s,
                        v.ptr, v.idx, v.perm, (const T*)vals, (const T*)Xt, (T*)Y, v.S, B,
@@ -524,8 +534,8 @@ static bool wave_sddmm_c(const seg_view& v, const void* dYt, const void* Xt, int
   // X in LDS (see k_wave_spmm_lds): one batch pass, many rows, no split row
   const int64_t x_elems = (int64_t)v.F * B;
   const bool lds_ok =
-      !v.has_split && wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SDDMM);
-  const int32_t wl_blk = (int32_t)std::min<int64_t>(2 * 256, cdiv(v.S, WL_THREADS / SNK_WAVE));
+      !v.has_split && wave_lds_fits(v, x_elems * (int64_t)sizeof(T), Xt, WL_MID_BYTES_SDDMM, lpe);
+  const int32_t wl_blk = wave_lds_blocks(x_elems * (int64_t)sizeof(T), v.S);
   const size_t lds_bytes = align_up((size_t)(x_elems * sizeof(T)), 16);
 #define SNK_WSD1(L, MULTI)                                                                      \
   do {                                                                                          \
