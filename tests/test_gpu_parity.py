@@ -227,7 +227,7 @@ def test_square_node_major_benchmarked_path(orc, sp, Bsz):
 
 LDS_CASES = [
     # M, K, nnz, B, dtype: layers with >= 16,384 segments whose whole
-    # node-major input fits in 64 KB of LDS take the LDS-staged wave kernel
+    # node-major input fits in LDS take the LDS-staged wave kernel
     (16384, 3001, 200000, 1, "bf16"),    # forward staged; 6,002-byte input (ragged tail)
     (3001, 20000, 300000, 4, "f32"),     # input gradient staged (dY: 3,001 x 4 fp32, 48 KB)
     (32768, 2048, 1000000, 16, "bf16"),  # forward staged, exactly 64 KB, two lanes per entry
@@ -241,6 +241,29 @@ def test_wave_lds_staged_inputs(orc, M, K, nnz, Bsz, dt):
     topo = run_products(orc, w.weights[0], w.X[0], w.dY[0], dt, "node", Bsz, repeat_check=True,
                         flags=B.PLAN_NODE_MAJOR_ONLY)
     assert topo.plan.has_split_row == 0
+
+
+LDS_MID_CASES = [
+    # M, K, nnz, B, dtype: 2,048-16,383 segments averaging >= 256 entries with
+    # inputs of 16-160 KB also take the LDS-staged kernels: rows (forward and
+    # value gradient) stage 32-64 KB, columns (input gradient) stage 128 KB,
+    # one workgroup per CU with one lane per entry
+    (8192, 2048, 2_200_000, 8, "bf16"),
+    (8192, 4096, 2_200_000, 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,K,nnz,Bsz,dt", LDS_MID_CASES)
+def test_wave_lds_staged_mid_sized_views(orc, M, K, nnz, Bsz, dt):
+    w = synth.random_case(26, M, K, nnz, Bsz, dt, "node")
+    wt = w.weights[0]
+    topo = run_products(orc, wt, w.X[0], w.dY[0], dt, "node", Bsz, repeat_check=True,
+                        flags=B.PLAN_NODE_MAJOR_ONLY)
+    assert topo.plan.has_split_row == 0 and topo.plan.has_split_col == 0
+    vals = to_dev(wt.vals, dt)
+    dX = topo.bwd_input_t(topo.gather_vals_t(vals), to_dev(w.dY[0].data, dt), Bsz, B.NODE_MAJOR)
+    ref, S = orc.spmm_bwd_input(M, K, wt.row, wt.col, wt.vals_f64(), Bsz, w.dY[0].f64(), True)
+    assert_within(from_dev(dX, dt), ref, S, dt, "bwd_input_t")
 
 
 LARGE_CASES = [  # (M, K, nnz, B, dtype, layout): >= 16,384 segments, inputs over 64 KB
