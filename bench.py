@@ -435,6 +435,9 @@ def time_config(w, B, bf16, layout, ops=("fwd", "bwd_input", "sddmm"), cold=True
             return lambda: t.fwd(d["vals"], d["X"], B, lay, out=d["Y"])
         if op == "bwd_input":
             return lambda: t.bwd_input_t(d["vt"], d["dY"], B, lay, out=d["dX"])
+        if op == "bwd_fused":  # dX and dV in one call, lr = 0 (the values stay)
+            return lambda: snk.snack_spmm_bwd_fused(t.plan, d["vals"], d["X"], d["dY"], lay, B,
+                                                    d["dX"], d["dV"], 0.0, vals_t=d["vt"])
         return lambda: t.grad_vals(d["dY"], d["X"], B, lay, out=d["dV"])
 
     plan = insts[0]["topo"].plan
@@ -455,7 +458,8 @@ def other_configs():
     """fwd, dX and dV on the other layer configurations: 256^2 at 90% (fp32,
     B=4, warm: it is launch-bound), the GPT-2-small MLP layers at 90% and 99%
     (fp32, 1024 tokens, batch-major), the LLaMA-7B-shaped projections with
-    skewed rows (bf16, B = 1, 4, 16, node-major) and the 200,000-node graph
+    skewed rows (bf16, B = 1, 4, 16, node-major; also the fused backward, the
+    layer's training path) and the 200,000-node graph
     (fp32, 128 node-major features; forward and input gradient), all cold
     but the first."""
     import synth
@@ -472,7 +476,8 @@ def other_configs():
         log(f"configs: llama {which}")
         wt = synth.llama_proj(which=which, B=1).weights[0]
         for B in (1, 4, 16):
-            out[f"llama_{which}_B{B}_bf16"] = time_config(wt, B, True, "node")
+            out[f"llama_{which}_B{B}_bf16"] = time_config(
+                wt, B, True, "node", ops=("fwd", "bwd_input", "sddmm", "bwd_fused"))
     log("configs: graph 200k")
     wt = synth.graph_layer().weights[0]
     out["graph_200k_B128_f32"] = time_config(wt, 128, False, "node", ops=("fwd", "bwd_input"))

@@ -721,6 +721,10 @@ FUSED_BWD = [
     # columns of ~750 entries kept whole (wave path over several load batches)
     ("long", "bf16", "node", 32, 2048, 0.1),
     ("long", "f32", "batch", 7, 2048, 0.0),
+    # dY staged in LDS (2,048-4,096 columns of ~500-1,100 entries, 128 KB
+    # node-major dY: one workgroup per CU)
+    ("mid_lds", "bf16", "node", 8, 0, 0.05),
+    ("mid_lds_f32", "f32", "node", 4, 0, 0.0),
 ]
 
 
@@ -732,6 +736,10 @@ def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
         w = synth.random_case(15, 300, 200, 9000, Bsz, dt, layout)
     elif name == "long":
         w = synth.random_case(18, 1500, 40, 30000, Bsz, dt, layout)
+    elif name == "mid_lds":
+        w = synth.random_case(26, 8192, 2048, 2_200_000, Bsz, dt, layout)
+    elif name == "mid_lds_f32":
+        w = synth.random_case(26, 8192, 4096, 2_200_000, Bsz, dt, layout)
     elif name == "skewed":
         lin = np.concatenate([np.arange(64) * 40 + 7, np.arange(3000) + 64 * 40])
         lin = np.unique(lin[lin < 80 * 40])
@@ -761,16 +769,22 @@ def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
         assert np.all(np.abs(new - exp) <= lr * tol * Sv + ulp * np.abs(exp) + 1e-30)
 
 
-@pytest.mark.parametrize("dt,layout,Bsz,use_vt", [("f32", "node", 8, True),
-                                                   ("f32", "batch", 5, False),
-                                                   ("bf16", "node", 32, True)])
-def test_bwd_fused_adam(orc, dt, layout, Bsz, use_vt):
+SMALL_ADAM = (512, 384, 20000)
+
+
+@pytest.mark.parametrize("dt,layout,Bsz,use_vt,shape", [
+    ("f32", "node", 8, True, SMALL_ADAM),
+    ("f32", "batch", 5, False, SMALL_ADAM),
+    ("bf16", "node", 32, True, SMALL_ADAM),
+    ("bf16", "node", 8, True, (8192, 2048, 2_200_000)),  # dY staged in LDS
+])
+def test_bwd_fused_adam(orc, dt, layout, Bsz, use_vt, shape):
     """Three Adam steps through the fused backward against the oracle's step
     (Kingma & Ba, Algorithm 1).  fp32: the returned dV is the fp32 gradient
     sum itself, so the oracle steps from it and the moments and values must
     agree to fp32 rounding; bf16: the moments against the oracle's exact
     gradient within the products' tolerance carried through the step."""
-    w = synth.random_case(25, 512, 384, 20000, Bsz, dt, layout)
+    w = synth.random_case(25, *shape, Bsz, dt, layout)
     wt = w.weights[0]
     lay = B.NODE_MAJOR if layout == "node" else B.BATCH_MAJOR
     topo = topology(wt, Bsz)
@@ -936,7 +950,8 @@ def test_sparse_linear_autograd(orc):
     assert_within(from_dev(x.grad, "f32"), ref, S, "f32", "SparseLinear dX")
     ref, S = orc.sddmm(256, 256, wt.row, wt.col, 4, w.dY[0].f64(), w.X[0].f64())
     assert_within(from_dev(layer.vals.grad, "f32"), ref, S, "f32", "SparseLinear dV")
-    # a batch above the fused backward's limit takes the two separate calls
+    # 256 columns: the two separate calls (as for a batch above the fused limit)
+    assert not snk.layer.fused_backward_pays(256, wt.nnz, 4, 4)
     xw = torch.randn(40, 256, device="cuda", requires_grad=True)
     layer(xw).backward(torch.ones(40, 256, device="cuda"))
     ref, S = orc.spmm_bwd_input(256, 256, wt.row, wt.col, wt.vals_f64(), 40,
@@ -946,6 +961,21 @@ def test_sparse_linear_autograd(orc):
     ref = orc.prune_regrow(256, 256, wt.row, wt.col, wt.vals, "f32", 655, 0, 1)
     assert np.array_equal(grown.cpu().numpy(), ref["grown"])
     assert np.array_equal(layer.topo.row.cpu().numpy(), ref["row"])
+
+
+def test_sparse_linear_autograd_fused_path(orc):
+    """A layer wide enough for the fused backward (2,048 columns, batch 32):
+    both gradients from one snack_spmm_bwd_fused call, against the oracle."""
+    w = synth.random_case(33, 2048, 2048, 200000, 32, "f32")
+    wt = w.weights[0]
+    assert snk.layer.fused_backward_pays(2048, wt.nnz, 4, 32)
+    layer = snk.SparseLinear(2048, 2048, to_dev(wt.row), to_dev(wt.col), to_dev(wt.vals), 32)
+    x = to_dev(w.X[0].data).view(32, 2048).requires_grad_(True)
+    layer(x).backward(to_dev(w.dY[0].data).view(32, 2048))
+    ref, S = orc.spmm_bwd_input(2048, 2048, wt.row, wt.col, wt.vals_f64(), 32, w.dY[0].f64())
+    assert_within(from_dev(x.grad, "f32"), ref, S, "f32", "SparseLinear fused dX")
+    ref, S = orc.sddmm(2048, 2048, wt.row, wt.col, 32, w.dY[0].f64(), w.X[0].f64())
+    assert_within(from_dev(layer.vals.grad, "f32"), ref, S, "f32", "SparseLinear fused dV")
 
 
 # ------------------------------------------------------------ memory footprint

@@ -3,6 +3,7 @@
 // groups and the butterfly reduce-scatter.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -238,6 +239,44 @@ __device__ __forceinline__ void round_dots(const vec<T, CH> (&xv)[NR], const vec
 #pragma unroll
   for (int i = 0; i < NR; ++i) part[i] = dot_acc<T, CH>(g, xv[i], 0.f);
   reduce_permute<LPE, NR>(part, lane, out);
+}
+
+// ---- LDS staging of the gathered input (shared by the products, the value
+// gradient and the fused backward): views whose whole node-major input fits
+// a workgroup's LDS copy it once per 16-wave workgroup and gather from LDS.
+constexpr int WL_THREADS = 1024;
+// gfx950 gives a workgroup up to 160 KB of LDS (the CU's whole LDS): inputs
+// above half of it run one workgroup per CU, smaller ones two.  With one
+// workgroup per CU only one lane per entry pays off (measured: 8192^2 at
+// B=8 and the LLaMA up input gradient at B=4 11-32% faster, the LLaMA down
+// input gradient at B=16, two lanes per entry, 9% slower).
+constexpr int WL_LDS = 160 * 1024;
+inline int32_t wave_lds_blocks(int64_t x_bytes, int32_t S) {
+  const int64_t per_cu = x_bytes > WL_LDS / 2 ? 1 : 2;
+  return (int32_t)std::min<int64_t>(per_cu * 256, cdiv(S, WL_THREADS / SNK_WAVE));
+}
+constexpr int WL_MIN_SEGMENTS = 16384;
+// Fewer segments still take the LDS path when the input is large enough
+// that the gathers miss the L1 cache often and segments are long enough
+// (>= 256 entries on average) to amortise the staging.  Measured: the
+// LLaMA-shaped column views' input gradient 10-22% faster (22-32 KB
+// inputs); at 16 KB (8192^2, batch 1) the value gradient 18% faster but the
+// products 5% slower, hence the two sizes; inputs of a few KB (4096^2 at
+// batch 1) and short segments (4096^2 at batch 8) lose to the cached gathers.
+constexpr int WL_MID_SEGMENTS = 2048;
+constexpr int64_t WL_MID_BYTES_SPMM = 20 * 1024;
+constexpr int64_t WL_MID_BYTES_SDDMM = 16 * 1024;
+constexpr int64_t WL_MID_AVG = 256;
+
+// Whether a view takes the LDS-staged kernels (one batch pass and no split
+// segment are checked by the caller); mid_bytes: the product's input-size
+// bound for views of fewer than WL_MIN_SEGMENTS segments.
+inline bool wave_lds_fits(const seg_view& v, int64_t x_bytes, const void* Xt,
+                          int64_t mid_bytes, int lpe) {
+  if (x_bytes > WL_LDS || (uintptr_t)Xt % 16 != 0) return false;
+  if (x_bytes > WL_LDS / 2 && lpe > 1) return false;
+  if (v.S >= WL_MIN_SEGMENTS) return true;
+  return v.S >= WL_MID_SEGMENTS && x_bytes >= mid_bytes && v.nnz >= WL_MID_AVG * v.S;
 }
 
 struct wave_shape {

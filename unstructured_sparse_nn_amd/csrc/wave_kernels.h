@@ -173,41 +173,6 @@ __global__ __launch_bounds__(WV_THREADS) void k_wave_spmm(
 // (one per entry at batch 1), which bound the launch well below the entry
 // stream; from LDS they cost a few LDS cycles per 64 entries.  One batch pass
 // (B <= LPE * CH); no split segments.
-constexpr int WL_THREADS = 1024;
-// gfx950 gives a workgroup up to 160 KB of LDS (the CU's whole LDS): inputs
-// above half of it run one workgroup per CU, smaller ones two.  With one
-// workgroup per CU only one lane per entry pays off (measured: 8192^2 at
-// B=8 and the LLaMA up input gradient at B=4 11-32% faster, the LLaMA down
-// input gradient at B=16, two lanes per entry, 9% slower).
-constexpr int WL_LDS = 160 * 1024;
-inline int32_t wave_lds_blocks(int64_t x_bytes, int32_t S) {
-  const int64_t per_cu = x_bytes > WL_LDS / 2 ? 1 : 2;
-  return (int32_t)std::min<int64_t>(per_cu * 256, cdiv(S, WL_THREADS / SNK_WAVE));
-}
-constexpr int WL_MIN_SEGMENTS = 16384;
-// Fewer segments still take the LDS path when the input is large enough
-// that the gathers miss the L1 cache often and segments are long enough
-// (>= 256 entries on average) to amortise the staging.  Measured: the
-// LLaMA-shaped column views' input gradient 10-22% faster (22-32 KB
-// inputs); at 16 KB (8192^2, batch 1) the value gradient 18% faster but the
-// products 5% slower, hence the two sizes; inputs of a few KB (4096^2 at
-// batch 1) and short segments (4096^2 at batch 8) lose to the cached gathers.
-constexpr int WL_MID_SEGMENTS = 2048;
-constexpr int64_t WL_MID_BYTES_SPMM = 20 * 1024;
-constexpr int64_t WL_MID_BYTES_SDDMM = 16 * 1024;
-constexpr int64_t WL_MID_AVG = 256;
-
-// Whether a view takes the LDS-staged kernels (one batch pass and no split
-// segment are checked by the caller); mid_bytes: the product's input-size
-// bound for views of fewer than WL_MIN_SEGMENTS segments.
-inline bool wave_lds_fits(const seg_view& v, int64_t x_bytes, const void* Xt,
-                          int64_t mid_bytes, int lpe) {
-  if (x_bytes > WL_LDS || (uintptr_t)Xt % 16 != 0) return false;
-  if (x_bytes > WL_LDS / 2 && lpe > 1) return false;
-  if (v.S >= WL_MIN_SEGMENTS) return true;
-  return v.S >= WL_MID_SEGMENTS && x_bytes >= mid_bytes && v.nnz >= WL_MID_AVG * v.S;
-}
-
 template <typename T, int CH, int LPE, bool PERM, bool NODE_OUT, int ACT>
 __global__ __launch_bounds__(WL_THREADS) void k_wave_spmm_lds(
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx,

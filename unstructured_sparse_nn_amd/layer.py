@@ -17,6 +17,22 @@ from . import binding as B
 FUSED_MAX_BATCH = 32
 
 
+def fused_backward_pays(K: int, nnz: int, elem_bytes: int, batch: int) -> bool:
+    """Whether one snack_spmm_bwd_fused call beats the two separate gradient
+    calls.  The fused pass reads the index stream once, but it runs one wave
+    per column and writes dV through perm, scattered over the row-ordered
+    array.  Measured on MI355X (cold, graph-timed): it pays with >= 2,048
+    columns and a batch of 32 (4096^2 at 80-95%: 9-15% faster), a batch of
+    8 with dV <= 2 MB, or dV <= 1 MB (2048^2 at 90%: 8-28% faster); larger
+    dV at small batches costs up to twice the separate calls (8192^2 at 95%,
+    batch 1: 33.7 against 17.1 us; LLaMA-shaped layers 40-70% slower), and 768
+    columns leave too few waves (GPT-2 W1, batch 32: 22.1 against 14.0 us)."""
+    if batch < 1 or batch > FUSED_MAX_BATCH or K < 2048:
+        return False
+    dv = nnz * elem_bytes
+    return batch >= 32 or (batch >= 8 and dv <= 2 << 20) or dv <= 1 << 20
+
+
 class Topology:
     """COO pattern (row, col int32 on the GPU) plus its prepared plan."""
 
@@ -115,7 +131,8 @@ class _SparseLinearFn(torch.autograd.Function):
         Bsz = xc.shape[0]
         g = gy.contiguous().view(-1)
         vt = layer.vals_t()  # the values in column order: read coalesced by the input gradient
-        if ctx.needs_input_grad[0] and ctx.needs_input_grad[1] and 0 < Bsz <= FUSED_MAX_BATCH:
+        if (ctx.needs_input_grad[0] and ctx.needs_input_grad[1]
+                and fused_backward_pays(topo.K, topo.nnz, vals.element_size(), Bsz)):
             # both gradients from one pass over the column view (snack_spmm_bwd_fused)
             gx = torch.empty(Bsz * topo.K, dtype=g.dtype, device=g.device)
             gv = torch.empty(topo.nnz, dtype=g.dtype, device=g.device)
