@@ -721,10 +721,10 @@ FUSED_BWD = [
     # columns of ~750 entries kept whole (wave path over several load batches)
     ("long", "bf16", "node", 32, 2048, 0.1),
     ("long", "f32", "batch", 7, 2048, 0.0),
-    # dY staged in LDS (2,048-4,096 columns of ~500-1,100 entries, 128 KB
-    # node-major dY: one workgroup per CU)
-    ("mid_lds", "bf16", "node", 8, 0, 0.05),
-    ("mid_lds_f32", "f32", "node", 4, 0, 0.0),
+    # larger layers: 2,048-4,096 columns of ~500-1,100 entries, 2.2 M values
+    # updated in place through perm
+    ("wide", "bf16", "node", 8, 0, 0.05),
+    ("wide_f32", "f32", "node", 4, 0, 0.0),
 ]
 
 
@@ -736,9 +736,9 @@ def test_bwd_fused(orc, name, dt, layout, Bsz, tile, lr):
         w = synth.random_case(15, 300, 200, 9000, Bsz, dt, layout)
     elif name == "long":
         w = synth.random_case(18, 1500, 40, 30000, Bsz, dt, layout)
-    elif name == "mid_lds":
+    elif name == "wide":
         w = synth.random_case(26, 8192, 2048, 2_200_000, Bsz, dt, layout)
-    elif name == "mid_lds_f32":
+    elif name == "wide_f32":
         w = synth.random_case(26, 8192, 4096, 2_200_000, Bsz, dt, layout)
     elif name == "skewed":
         lin = np.concatenate([np.arange(64) * 40 + 7, np.arange(3000) + 64 * 40])
@@ -776,7 +776,7 @@ SMALL_ADAM = (512, 384, 20000)
     ("f32", "node", 8, True, SMALL_ADAM),
     ("f32", "batch", 5, False, SMALL_ADAM),
     ("bf16", "node", 32, True, SMALL_ADAM),
-    ("bf16", "node", 8, True, (8192, 2048, 2_200_000)),  # dY staged in LDS
+    ("bf16", "node", 8, True, (8192, 2048, 2_200_000)),  # 2.2 M values and moments
 ])
 def test_bwd_fused_adam(orc, dt, layout, Bsz, use_vt, shape):
     """Three Adam steps through the fused backward against the oracle's step
