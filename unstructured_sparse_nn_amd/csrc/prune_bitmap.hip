@@ -1265,7 +1265,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   const int top = 8 * (passes - 1);
   // chunk 0 bucketed by region when the layout has room for its n_drop
   const int64_t nwg = cdiv(n_drop, (int64_t)RB_CH);
-  const bool bucket = L.rwg > 0 && nwg <= L.rwg;
+  const bool bucket = L.rwg > 0 && nwg >= 1 && nwg <= L.rwg;  // (n_drop = 0 never gets here)
   uint32_t* cand = (uint32_t*)(ws + L.cand);
   int32_t* tab = (int32_t*)(ws + L.tab);
   hipLaunchKernelGGL(k_bi_build<T>, dim3((unsigned)(L.nblk + (bucket ? nwg : 0))), et, 0, s, row,
