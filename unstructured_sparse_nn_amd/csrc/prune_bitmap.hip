@@ -63,6 +63,11 @@ constexpr int AREPL = 64;                 // acceptance-count replicas
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
 constexpr int WT = 512;                   // threads (= bitmap words) per write block
 constexpr int EMIT_CAP = 2048;            // new entries per write block staged in LDS
+// Set bits an emitter thread takes per batch, their gathers in flight
+// together: a 32-position word at density <= 1/4 rarely holds more, so a
+// wave's slowest lane needs one batch (with 4, three waves in four needed
+// a second round of dependent gathers at 5% density).
+constexpr int EMIT_BATCH = 8;
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
@@ -887,21 +892,21 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       r0 = (int32_t)(pw / K);
       c0 = (int32_t)(pw - (int64_t)r0 * K);
     }
-    // four set bits at a time, their survivor-value loads in flight together
+    // EMIT_BATCH set bits at a time, their survivor-value loads in flight together
     while (F) {
-      int b[4];
-      T v[4];
+      int b[EMIT_BATCH];
+      T v[EMIT_BATCH];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < EMIT_BATCH; ++u) {
         b[u] = F ? __ffs(F) - 1 : -1;
         F &= F - 1;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < EMIT_BATCH; ++u)
         v[u] = (b[u] >= 0 && ((S >> b[u]) & 1u)) ? vals_ws[qs + __popc(S & ((1u << b[u]) - 1u))]
                                                  : (T)0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < EMIT_BATCH; ++u) {
         if (b[u] < 0) break;
         if (qf < nnz) {
           int32_t r = r0, cc = c0 + b[u];
@@ -1049,8 +1054,8 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
 // first entry = block base + block scan.  Word block tb holds columns
 // [tb*WT/WM, ...); workgroup b (dispatched to XCD b mod 8) takes word block
 // (b mod 8)*ceil(nbt/8) + b/8, so each XCD gathers the FP lines of one
-// contiguous column range.  A thread takes its entries four at a time, all
-// four FP loads in flight together.  With cols_here (WM divides WT, so a
+// contiguous column range.  A thread takes its entries EMIT_BATCH at a time,
+// all their FP loads in flight together.  With cols_here (WM divides WT, so a
 // block holds whole columns) the block also writes the column tiles of its
 // columns and sets res[3] if one of them is split.
 template <typename T>
@@ -1109,29 +1114,29 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
   if (!valid) return;
   const uint32_t below = (1u << (c & 31)) - 1u;
   while (word) {
-    int j[4];
-    uint2 fp[4];
+    int j[EMIT_BATCH];
+    uint2 fp[EMIT_BATCH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < EMIT_BATCH; ++u) {
       j[u] = word ? __ffs(word) - 1 : -1;
       word &= word - 1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < EMIT_BATCH; ++u)
       fp[u] = j[u] >= 0 ? FP[(rw * 32 + j[u]) * KW + (c >> 5)] : make_uint2(0u, 0u);
-    int32_t pos[4];
+    int32_t pos[EMIT_BATCH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+    for (int u = 0; u < EMIT_BATCH; ++u) pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
     // the value of each entry in column order: one gather of the new values,
-    // the four of this batch in flight together
-    T v[4];
+    // the whole batch in flight together
+    T v[EMIT_BATCH];
     if (vals_t) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < EMIT_BATCH; ++u)
         v[u] = (j[u] >= 0 && q + u < nnz) ? vals[pos[u]] : (T)0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < EMIT_BATCH; ++u) {
       if (j[u] < 0) break;
       if (q < nnz) {
         f.row_t[q] = (int32_t)(rw * 32 + j[u]);
