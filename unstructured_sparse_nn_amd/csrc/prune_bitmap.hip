@@ -112,9 +112,10 @@ __global__ __launch_bounds__(256) void k_bi_init(bm_state* st, int32_t* __restri
 
 // Digit of select pass `pass` holding the need-th smallest remaining
 // magnitude (one digit per thread, a block scan).  Output: the select state
-// after the pass.  Block 0 records it for later kernels.  256 threads.
+// after the pass, which the block with `record` keeps for later kernels.
+// 256 threads.
 __device__ void pick_digit(bm_state* st, int pass, int shift, int32_t n_drop, uint32_t& pfx,
-                          uint32_t& msk, int32_t& need) {
+                          uint32_t& msk, int32_t& need, bool record) {
   __shared__ int32_t lds[BT / SNK_WAVE];
   __shared__ int32_t pick[2];
   const int t = threadIdx.x;
@@ -139,7 +140,7 @@ __device__ void pick_digit(bm_state* st, int pass, int shift, int32_t n_drop, ui
   pfx = p0 | ((uint32_t)pick[0] << shift);
   msk = m0 | (255u << shift);
   need = n0 - pick[1];
-  if (blockIdx.x == 0 && t == 0) {
+  if (record && t == 0) {
     st->pfx[pass] = pfx;
     st->msk[pass] = msk;
     st->need[pass] = need;
@@ -336,18 +337,34 @@ __device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t n
   __shared__ int32_t lds[BT / SNK_WAVE];
   const int t = threadIdx.x;
   const int64_t wbase = (int64_t)g * RB_WORDS;
-  for (int k = t; k < RB_WORDS; k += BT) {
-    const int64_t w = wbase + k;
-    Ss[k] = w < W ? sup[w] : 0xFFFFFFFFu;
-    Gs[k] = 0u;
-  }
+  // the region's S words and the slice table, every load in flight at once
+  // (indices clamped in range, unused values discarded afterwards)
+  constexpr int SPT = RB_WORDS / BT;   // S words per thread
   constexpr int WPTH = RB_MAXWG / BT;  // slices per thread in the scan
+  uint32_t sw[SPT];
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int64_t w = wbase + k * BT + t;
+    sw[k] = sup[w < W ? w : W - 1];
+  }
   int32_t a[WPTH], len[WPTH], sum = 0;
 #pragma unroll
   for (int k = 0; k < WPTH; ++k) {
     const int wgi = t * WPTH + k;
-    a[k] = wgi < nwg ? tab[(int64_t)wgi * (nreg + 1) + g] : 0;
-    len[k] = wgi < nwg ? tab[(int64_t)wgi * (nreg + 1) + g + 1] - a[k] : 0;
+    const int64_t ti = (int64_t)(wgi < nwg ? wgi : nwg - 1) * (nreg + 1) + g;
+    a[k] = tab[ti];
+    len[k] = tab[ti + 1];
+  }
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    Ss[k * BT + t] = wbase + k * BT + t < W ? sw[k] : 0xFFFFFFFFu;
+    Gs[k * BT + t] = 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < WPTH; ++k) {
+    const bool in = t * WPTH + k < nwg;
+    len[k] = in ? len[k] - a[k] : 0;
+    a[k] = in ? a[k] : 0;
     sum += len[k];
   }
   int32_t n_g;
@@ -362,23 +379,31 @@ __device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t n
     ex += len[k];
   }
   __syncthreads();
+  int top = 1;  // the largest power of two below nwg (1 if nwg <= 2)
+  while (2 * top < nwg) top *= 2;
   int32_t taken = 0;
   for (int32_t b0 = 0; b0 < n_g; b0 += 4 * BT) {
     uint32_t pc[4];
     bool ok[4];
+    int32_t e[4], lo[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int32_t e = b0 + u * BT + t;
-      ok[u] = e < n_g;
-      int lo = 0, hi = nwg;  // the last slice whose run starts at or before e
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (run0[mid] <= e) lo = mid + 1;
-        else hi = mid;
-      }
-      const int wgi = lo > 0 ? lo - 1 : 0;
-      pc[u] = ok[u] ? cand[start[wgi] + (e - run0[wgi])] : 0u;
+      e[u] = b0 + u * BT + t;
+      ok[u] = e[u] < n_g;
+      lo[u] = 0;  // run0[0] = 0 <= e
     }
+    // the last slice whose run starts at or before e: a branch-free search
+    // with the four candidates' LDS reads of each step in flight together
+    for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = lo[u] + step;
+        if (m < nwg && run0[m] <= e[u]) lo[u] = m;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pc[u] = cand[ok[u] ? start[lo[u]] + (e[u] - run0[lo[u]]) : 0];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (!ok[u]) continue;
@@ -478,7 +503,8 @@ __device__ __forceinline__ void last_word(const int64_t (&l)[4], int n, int64_t*
 // Support bitmap S (and G cleared, unless chunk 0 is bucketed: grown is
 // then NULL), a copy of the values, the NaN / index / order checks and the
 // first select histogram.  Thread t holds entries base + 4t .. base + 4t + 3.
-// Workgroups from nblk on bucket regrow chunk 0 (bucket_chunk0).
+// The first gridDim.x - nblk workgroups bucket regrow chunk 0 (bucket_chunk0):
+// the regrow is the longer chain, so its workgroups are dispatched first.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_build(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
@@ -486,10 +512,12 @@ __global__ __launch_bounds__(BT) void k_bi_build(
     uint32_t* __restrict__ sup, uint32_t* __restrict__ grown, T* __restrict__ vals_ws,
     int64_t nblk, uint64_t stream, uint64_t MK, int32_t n_drop, int32_t nreg,
     uint32_t* __restrict__ cand, int32_t* __restrict__ tab) {
-  if ((int64_t)blockIdx.x >= nblk) {  // bucketing workgroups of regrow chunk 0
-    bucket_chunk0((int64_t)blockIdx.x - nblk, stream, MK, n_drop, nreg, cand, tab);
+  const int64_t nx = (int64_t)gridDim.x - nblk;
+  if ((int64_t)blockIdx.x < nx) {  // bucketing workgroups of regrow chunk 0
+    bucket_chunk0((int64_t)blockIdx.x, stream, MK, n_drop, nreg, cand, tab);
     return;
   }
+  const int64_t bid = (int64_t)blockIdx.x - nx;
   __shared__ int32_t h[256];
   __shared__ uint32_t buf[CAP];
   __shared__ int64_t lastl[BT];
@@ -497,7 +525,7 @@ __global__ __launch_bounds__(BT) void k_bi_build(
   __shared__ int64_t nxt[NEXT];
   const int t = threadIdx.x;
   h[t] = 0;
-  const int64_t base = (int64_t)blockIdx.x * BE;
+  const int64_t base = bid * BE;
   const int n = (int)std::min<int64_t>(BE, nnz - base);
   const int64_t k0 = base + 4 * t;
   const bool full = vec_ok && k0 + 3 < nnz;
@@ -570,12 +598,13 @@ __global__ __launch_bounds__(BT) void k_bi_build(
   }
   write_block_words(buf, w_lo, w_hi, l, f, extra, sup, grown);
   if (err) atomicOr(&st->err, err);
-  if (h[t]) atomicAdd(&st->hist[0][blockIdx.x % HREPL][t], h[t]);
+  if (h[t]) atomicAdd(&st->hist[0][bid % HREPL][t], h[t]);
 }
 
 // Select pass `pass` >= 1: pick the previous pass's digit, histogram the
-// next digit of the entries matching the prefix.  Workgroups from nblk on
-// run regrow chunk c (with nwg > 0: chunk 0 by region, region_chunk0).
+// next digit of the entries matching the prefix.  The first gridDim.x - nblk
+// workgroups run regrow chunk c (with nwg > 0: chunk 0 by region,
+// region_chunk0).
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64_t nnz,
                                                int64_t nblk, int pass, int prev_shift, int shift,
@@ -587,32 +616,36 @@ __global__ __launch_bounds__(BT) void k_bi_sel(const T* __restrict__ vals, int64
                                                const uint32_t* __restrict__ cand,
                                                const int32_t* __restrict__ tab) {
   __shared__ int32_t h[256];
-  if ((int64_t)blockIdx.x >= nblk) {
+  const int64_t nx = (int64_t)gridDim.x - nblk;
+  if ((int64_t)blockIdx.x < nx) {
     if (nwg > 0)  // chunk 0 from the buckets, one workgroup per region
-      region_chunk0((int32_t)(blockIdx.x - nblk), st, n_drop, nreg, nwg, W, cand, tab, sup,
-                    grown);
+      region_chunk0((int32_t)blockIdx.x, st, n_drop, nreg, nwg, W, cand, tab, sup, grown);
     else
-      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, nx);
     return;
   }
+  const int64_t bid = (int64_t)blockIdx.x - nx;
   const int t = threadIdx.x;
   h[t] = 0;
-  const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * t;
+  const int64_t k0 = bid * BE + 4 * t;
   uint32_t a[4];
+  T x[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0u;
+  for (int j = 0; j < 4; ++j) x[j] = vals[k0 + j < nnz ? k0 + j : nnz - 1];  // loads in flight together
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(x[j])) : 0u;
   uint32_t pfx, msk;
   int32_t need;
-  pick_digit(st, pass - 1, prev_shift, n_drop, pfx, msk, need);
+  pick_digit(st, pass - 1, prev_shift, n_drop, pfx, msk, need, bid == 0);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     wave_hist_add(h, (a[j] >> shift) & 255u, k0 + j < nnz && (a[j] & msk) == pfx);
   __syncthreads();
-  if (h[t]) atomicAdd(&st->hist[pass][blockIdx.x % HREPL][t], h[t]);
+  if (h[t]) atomicAdd(&st->hist[pass][bid % HREPL][t], h[t]);
 }
 
 // Last pick (the threshold magnitude tau and the ties to drop), entries at
-// tau per block.  Workgroups from nblk on run regrow chunk c.
+// tau per block.  The first gridDim.x - nblk workgroups run regrow chunk c.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int64_t nnz,
                                                  int64_t nblk, int last_pass, int shift,
@@ -622,24 +655,28 @@ __global__ __launch_bounds__(BT) void k_bi_count(const T* __restrict__ vals, int
                                                  const uint32_t* __restrict__ sup,
                                                  uint32_t* __restrict__ grown) {
   __shared__ int32_t lds[BT / SNK_WAVE];
-  if ((int64_t)blockIdx.x >= nblk) {
-    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+  const int64_t nx = (int64_t)gridDim.x - nblk;
+  if ((int64_t)blockIdx.x < nx) {
+    regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, nx);
     return;
   }
-  const int64_t k0 = (int64_t)blockIdx.x * BE + 4 * threadIdx.x;
+  const int64_t bid = (int64_t)blockIdx.x - nx;
+  const int64_t k0 = bid * BE + 4 * threadIdx.x;
   uint32_t a[4];
+  T x[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(vals[k0 + j])) : 0xFFFFFFFFu;
+  for (int j = 0; j < 4; ++j) x[j] = vals[k0 + j < nnz ? k0 + j : nnz - 1];  // loads in flight together
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = k0 + j < nnz ? magnitude<T>(raw_bits(x[j])) : 0xFFFFFFFFu;
   uint32_t tau, msk;
   int32_t need;
-  pick_digit(st, last_pass, shift, n_drop, tau, msk, need);
+  pick_digit(st, last_pass, shift, n_drop, tau, msk, need, bid == 0);
   int32_t eq = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) eq += a[j] == tau ? 1 : 0;
   int32_t tot;
   block_excl_scan_i32<BT>(eq, lds, &tot);
-  if (threadIdx.x == 0) cnt_eq[blockIdx.x] = tot;
+  if (threadIdx.x == 0) cnt_eq[bid] = tot;
 }
 
 // One workgroup: base_eq[b] = entries at tau in blocks before b (used when
@@ -658,11 +695,20 @@ __global__ __launch_bounds__(1024) void k_bi_eq_scan(const int32_t* __restrict__
   }
 }
 
-// Sum of v[0..n) over the block (all threads get it).
+// Sum of v[0..n) over the block (all threads get it); four loads per thread
+// in flight per round.
 __device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ v, int64_t n) {
   __shared__ int32_t lds[32];
   int32_t s = 0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += v[i];
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 4 * (int64_t)blockDim.x) {
+    int32_t x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * (int64_t)blockDim.x;
+      x[u] = i < n ? v[i] : 0;
+    }
+    s += (x[0] + x[1]) + (x[2] + x[3]);
+  }
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, SNK_WAVE);
   if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = s;
   __syncthreads();
@@ -673,8 +719,9 @@ __device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ 
 }
 
 // Dropped bitmap D: entry k is dropped if its magnitude is below tau, or at
-// tau with tie rank (index order) below need.  Workgroups from nblk on run
-// regrow chunk c; with `tail` a single one runs chunk c and all the rest.
+// tau with tie rank (index order) below need.  The first gridDim.x - nblk
+// workgroups run regrow chunk c; with `tail` a single one runs chunk c and
+// all the rest.
 template <typename T>
 __global__ __launch_bounds__(BT) void k_bi_drop(
     const int32_t* __restrict__ row, const int32_t* __restrict__ col, const T* __restrict__ vals,
@@ -688,17 +735,19 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
   __shared__ int64_t edge_s, whi_s;
   __shared__ int64_t nxt[NEXT];
   __shared__ uint32_t nxt_mag[NEXT];
-  if ((int64_t)blockIdx.x >= nblk) {
+  const int64_t nx = (int64_t)gridDim.x - nblk;
+  if ((int64_t)blockIdx.x < nx) {
     if (tail)  // one workgroup: chunk c and every later one (no finisher launch)
       regrow_tail(c, stream, MK, n_drop, st, sup, grown);
     else
-      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x - nblk, gridDim.x - nblk);
+      regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, nx);
     return;
   }
+  const int64_t bid = (int64_t)blockIdx.x - nx;
   const int t = threadIdx.x;
   const uint32_t tau = st->pfx[last_pass];
   const int32_t need = st->need[last_pass];
-  const int64_t base = (int64_t)blockIdx.x * BE;
+  const int64_t base = bid * BE;
   const int n = (int)std::min<int64_t>(BE, nnz - base);
   const int64_t k0 = base + 4 * t;
   uint32_t a[4];
@@ -714,7 +763,7 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
   }
   stage_edges<T>(row, col, vals, nnz, M, K, base, n, &edge_s, nxt, nxt_mag);
   last_word(l, n, &whi_s);
-  const int32_t E = base_eq ? base_eq[blockIdx.x] : block_sum_prefix(cnt_eq, blockIdx.x);
+  const int32_t E = base_eq ? base_eq[bid] : block_sum_prefix(cnt_eq, bid);
   // tie ranks in index order (a block scan; its barriers also publish the
   // staged edges)
   int32_t eq = 0;
@@ -850,7 +899,11 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     bo = boff[blockIdx.x];
   } else {
     int4 s = make_int4(0, 0, 0, 0);
-    for (int64_t i = t; i < (int64_t)blockIdx.x; i += WT) s = add4(s, bsum[i]);
+    for (int64_t i = t; i < (int64_t)blockIdx.x; i += 2 * WT) {  // two loads in flight
+      const int64_t i2 = i + WT < (int64_t)blockIdx.x ? i + WT : i;
+      const int4 x = bsum[i], y = bsum[i2];
+      s = add4(s, i2 != i ? add4(x, y) : x);
+    }
     for (int off = 32; off > 0; off >>= 1) {
       s.x += __shfl_xor(s.x, off, SNK_WAVE);
       s.y += __shfl_xor(s.y, off, SNK_WAVE);
@@ -1076,7 +1129,11 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
     base = toff[tb].x;
   } else {
     int32_t sacc = 0;
-    for (int64_t i = t; i < tb; i += WT) sacc += tsum[i].x;
+    for (int64_t i = t; i < tb; i += 2 * WT) {  // two loads in flight
+      const int64_t i2 = i + WT < tb ? i + WT : i;
+      const int32_t x = tsum[i].x, y = tsum[i2].x;
+      sacc += i2 != i ? x + y : x;
+    }
     for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off, SNK_WAVE);
     if (lane_id() == 0) red[t / SNK_WAVE] = sacc;
     __syncthreads();
