@@ -62,12 +62,12 @@ constexpr int HREPL = 16;                 // select-histogram replicas
 constexpr int AREPL = 64;                 // acceptance-count replicas
 constexpr int SLOTS = 32;                 // grid-wide regrow chunks per call
 constexpr int WT = 512;                   // threads (= bitmap words) per write block
-constexpr int EMIT_CAP = 2048;            // new entries per write block staged in LDS
-// Set bits an emitter thread takes per batch, their gathers in flight
-// together: a 32-position word at density <= 1/4 rarely holds more, so a
-// wave's slowest lane needs one batch (with 4, three waves in four needed
-// a second round of dependent gathers at 5% density).
-constexpr int EMIT_BATCH = 8;
+// Entries per emitter block listed in LDS (one per thread per round): density
+// up to 1/4 over a block of WT words; a denser block takes one thread per word.
+constexpr int EMIT_CAP = 4096;
+// Set bits a thread of the one-thread-per-word emission (blocks denser than
+// EMIT_CAP) takes per batch, their gathers in flight together.
+constexpr int EMIT_BATCH = 4;
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
@@ -820,6 +820,52 @@ __device__ __forceinline__ int4 add4(int4 a, int4 b) {
   return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// Exclusive block scans of NS values (ex, with block totals tot) and block
+// sums of NR more, behind one barrier: each wave's scan totals and sums go
+// through LDS together.  lds: NT/64 * (NS + NR) ints, left as written (the
+// caller does not reuse it).  Call from all threads.
+template <int NT, int NS, int NR>
+__device__ __forceinline__ void block_scan_sum(const int32_t (&x)[NS], const int32_t (&y)[NR],
+                                               int32_t* lds, int32_t (&ex)[NS],
+                                               int32_t (&tot)[NS], int32_t (&sum)[NR]) {
+  constexpr int NW = NT / SNK_WAVE, NV = NS + NR;
+  const int w = threadIdx.x / SNK_WAVE;
+  int32_t inc[NS], ys[NR];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) inc[k] = wave_incl_scan_i32(x[k]);
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    ys[k] = y[k];
+    for (int off = 32; off > 0; off >>= 1) ys[k] += __shfl_xor(ys[k], off, SNK_WAVE);
+  }
+  if (lane_id() == SNK_WAVE - 1) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) lds[w * NV + k] = inc[k];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) lds[w * NV + NS + k] = ys[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    int32_t b = 0, t = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int32_t v = lds[i * NV + k];
+      if (i < w) b += v;
+      t += v;
+    }
+    ex[k] = b + inc[k] - x[k];
+    tot[k] = t;
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    int32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += lds[i * NV + NS + k];
+    sum[k] = t;
+  }
+}
+
 // Per block of WT words: popcounts of (new support, old support, dropped,
 // grown).
 __global__ __launch_bounds__(WT) void k_bi_wsum(const uint32_t* __restrict__ sup,
@@ -871,8 +917,8 @@ __global__ __launch_bounds__(1024) void k_bi_bscan(const int4* __restrict__ in,
 // prefix counts; one thread per bitmap word.  Block 0 reports (error,
 // positions missing) into pinned host memory; nothing else is written
 // unless both are 0.  Writes are clamped to nnz / n_drop.
-template <typename T>
-__global__ __launch_bounds__(WT) void k_bi_emit(
+template <typename T, bool LISTS>
+__global__ __launch_bounds__(WT, LISTS ? 6 : 8) void k_bi_emit(
     const uint32_t* __restrict__ sup, const uint32_t* __restrict__ dropb,
     const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
     const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
@@ -880,11 +926,31 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     uint2* __restrict__ FP, int32_t* __restrict__ row,
     int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
     int64_t* __restrict__ grown_lin) {
-  __shared__ int32_t lds[WT / SNK_WAVE];
-  __shared__ int4 red[WT / SNK_WAVE];
-  __shared__ int32_t srow[EMIT_CAP], scol[EMIT_CAP];
-  __shared__ T sval[EMIT_CAP];
+  __shared__ int32_t lds[WT / SNK_WAVE * 6];
+  __shared__ uint32_t ent[EMIT_CAP];  // (word in block << 5) | bit, in output order
+  __shared__ uint32_t sS[WT];
+  __shared__ int32_t sq[WT], sr[WT], sc[WT];
   const int t = threadIdx.x;
+  // every load that depends on nothing is issued first: the block's words,
+  // the block sums before it (up to 2 WT of them here) and the state words
+  const int64_t w = (int64_t)blockIdx.x * WT + t;
+  const int64_t wc = w < W ? w : W - 1;
+  const uint32_t S0 = sup[wc], D0 = dropb[wc], G0 = grown[wc];
+  const int64_t nb_before = (int64_t)blockIdx.x;
+  // (without the dropped and grown lists only the first two block counts
+  // are needed)
+  int4 p0 = make_int4(0, 0, 0, 0), p1 = make_int4(0, 0, 0, 0);
+  if (!boff && nb_before > 0) {
+    if constexpr (LISTS) {
+      p0 = bsum[t < nb_before ? t : 0];
+      p1 = bsum[t + WT < nb_before ? t + WT : 0];
+    } else {
+      const int2 a = *reinterpret_cast<const int2*>(&bsum[t < nb_before ? t : 0]);
+      const int2 b = *reinterpret_cast<const int2*>(&bsum[t + WT < nb_before ? t + WT : 0]);
+      p0 = make_int4(a.x, a.y, 0, 0);
+      p1 = make_int4(b.x, b.y, 0, 0);
+    }
+  }
   const int32_t err = st->err, missing = st->rem_final;
   if (blockIdx.x == 0 && t == 0) {
     store_result(&result[0], err);
@@ -893,40 +959,47 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
     store_result(&result[3], 0);
   }
   if (err || missing > 0) return;
-  // block base: the sum of the sums of earlier blocks
-  int4 bo;
-  if (boff) {
-    bo = boff[blockIdx.x];
-  } else {
-    int4 s = make_int4(0, 0, 0, 0);
-    for (int64_t i = t; i < (int64_t)blockIdx.x; i += 2 * WT) {  // two loads in flight
-      const int64_t i2 = i + WT < (int64_t)blockIdx.x ? i + WT : i;
+  // this thread's share of the block base (the sum of the sums of earlier
+  // blocks); the block reduces it with the two scans below
+  int4 part = make_int4(0, 0, 0, 0);
+  if (!boff) {
+    if (t < nb_before) part = p0;
+    if (t + WT < nb_before) part = add4(part, p1);
+    for (int64_t i = t + 2 * WT; i < nb_before; i += 2 * WT) {  // two loads in flight
+      const int64_t i2 = i + WT < nb_before ? i + WT : i;
       const int4 x = bsum[i], y = bsum[i2];
-      s = add4(s, i2 != i ? add4(x, y) : x);
+      part = add4(part, i2 != i ? add4(x, y) : x);
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      s.x += __shfl_xor(s.x, off, SNK_WAVE);
-      s.y += __shfl_xor(s.y, off, SNK_WAVE);
-      s.z += __shfl_xor(s.z, off, SNK_WAVE);
-      s.w += __shfl_xor(s.w, off, SNK_WAVE);
-    }
-    if (lane_id() == 0) red[t / SNK_WAVE] = s;
-    __syncthreads();
-    bo = make_int4(0, 0, 0, 0);
-    for (int i = 0; i < WT / SNK_WAVE; ++i) bo = add4(bo, red[i]);
   }
-  const int64_t w = (int64_t)blockIdx.x * WT + t;
-  const uint32_t S = w < W ? sup[w] : 0u, D = w < W ? dropb[w] : 0u, G = w < W ? grown[w] : 0u;
+  const uint32_t S = w < W ? S0 : 0u, D = w < W ? D0 : 0u, G = w < W ? G0 : 0u;
   const int4 c = word_counts(S, D, G);
   // a block holds at most 32 * WT = 16384 positions, so two counts share an
-  // int32 (15 bits each, no overflow) and two block scans serve all four
-  int32_t tot;
-  const int32_t fs = block_excl_scan_i32<WT>(c.x | (c.y << 16), lds, &tot);
-  // the block's new entries are [bo.x, bo.x + nblk_out): staged in LDS and
-  // written with whole-line streaming stores when they fit (block-uniform)
-  const int32_t nblk_out = tot & 0xFFFF;
-  const bool staged = nblk_out <= EMIT_CAP;
-  const int32_t dg = block_excl_scan_i32<WT>(c.z | (c.w << 16), lds, &tot);
+  // int32 (15 bits each, no overflow): two scans serve all four
+  int32_t fs, nf, dg = 0;
+  int4 bo;
+  if constexpr (LISTS) {
+    int32_t ex[2], tt[2], sm[4];
+    const int32_t xs[2] = {c.x | (c.y << 16), c.z | (c.w << 16)};
+    const int32_t ys[4] = {part.x, part.y, part.z, part.w};
+    block_scan_sum<WT, 2, 4>(xs, ys, lds, ex, tt, sm);
+    bo = boff ? boff[blockIdx.x] : make_int4(sm[0], sm[1], sm[2], sm[3]);
+    fs = ex[0];
+    dg = ex[1];
+    nf = tt[0];
+  } else {
+    int32_t ex[1], tt[1], sm[2];
+    const int32_t xs[1] = {c.x | (c.y << 16)};
+    const int32_t ys[2] = {part.x, part.y};
+    block_scan_sum<WT, 1, 2>(xs, ys, lds, ex, tt, sm);
+    bo = boff ? boff[blockIdx.x] : make_int4(sm[0], sm[1], 0, 0);
+    fs = ex[0];
+    nf = tt[0];
+  }
+  // the block's new entries are [bo.x, bo.x + nblk_out); listed in LDS when
+  // they fit (block-uniform), so that each thread takes one entry per round
+  // and the stores are coalesced
+  const int32_t nblk_out = nf & 0xFFFF;
+  const bool listed = nblk_out <= EMIT_CAP;
   int64_t qf = bo.x + (fs & 0xFFFF);
   const int64_t qs = bo.y + (fs >> 16);
   int64_t qd = bo.z + (dg & 0xFFFF);
@@ -935,9 +1008,9 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
   uint32_t F = (S & ~D) | G;
   if (FP && w < W)  // the new support and its per-word prefix, for a fused prepare
     FP[w] = make_uint2(F, (uint32_t)qf);
+  // row and column of the word's first position; the rest step from it
+  int32_t r0 = 0, c0 = 0;
   if (F) {
-    // row and column of the word's first position; the rest step from it
-    int32_t r0, c0;
     if (small_grid) {
       r0 = (int32_t)((uint32_t)pw / (uint32_t)K);
       c0 = (int32_t)((uint32_t)pw - (uint32_t)r0 * (uint32_t)K);
@@ -945,44 +1018,33 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       r0 = (int32_t)(pw / K);
       c0 = (int32_t)(pw - (int64_t)r0 * K);
     }
-    // EMIT_BATCH set bits at a time, their survivor-value loads in flight together
-    while (F) {
-      int b[EMIT_BATCH];
-      T v[EMIT_BATCH];
-#pragma unroll
-      for (int u = 0; u < EMIT_BATCH; ++u) {
-        b[u] = F ? __ffs(F) - 1 : -1;
-        F &= F - 1;
-      }
-#pragma unroll
-      for (int u = 0; u < EMIT_BATCH; ++u)
-        v[u] = (b[u] >= 0 && ((S >> b[u]) & 1u)) ? vals_ws[qs + __popc(S & ((1u << b[u]) - 1u))]
-                                                 : (T)0;
-#pragma unroll
-      for (int u = 0; u < EMIT_BATCH; ++u) {
-        if (b[u] < 0) break;
-        if (qf < nnz) {
-          int32_t r = r0, cc = c0 + b[u];
-          while (cc >= K) {
-            cc -= K;
-            ++r;
-          }
-          if (staged) {
-            const int32_t i = (int32_t)(qf - bo.x);
-            srow[i] = r;
-            scol[i] = cc;
-            sval[i] = v[u];
-          } else {
-            row[qf] = r;
-            col[qf] = cc;
-            vals[qf] = v[u];
-          }
+  }
+  if (listed) {
+    sS[t] = S;
+    sq[t] = (int32_t)qs;
+    sr[t] = r0;
+    sc[t] = c0;
+    int32_t o = fs & 0xFFFF;
+    for (uint32_t x = F; x; x &= x - 1) ent[o++] = ((uint32_t)t << 5) | (uint32_t)(__ffs(x) - 1);
+  } else {
+    // a block denser than EMIT_CAP (rare): one thread per word, bit by bit
+    for (; F; F &= F - 1) {
+      const int b = __ffs(F) - 1;
+      if (qf < nnz) {
+        const T v = ((S >> b) & 1u) ? vals_ws[qs + __popc(S & ((1u << b) - 1u))] : (T)0;
+        int32_t r = r0, cc = c0 + b;
+        while (cc >= K) {
+          cc -= K;
+          ++r;
         }
-        ++qf;
+        row[qf] = r;
+        col[qf] = cc;
+        vals[qf] = v;
       }
+      ++qf;
     }
   }
-  if (dropped_lin) {
+  if (LISTS && dropped_lin) {
     uint32_t Dw = D;
     while (Dw) {
       const int b = __ffs(Dw) - 1;
@@ -991,7 +1053,7 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       ++qd;
     }
   }
-  if (grown_lin) {
+  if (LISTS && grown_lin) {
     uint32_t Gw = G;
     while (Gw) {
       const int b = __ffs(Gw) - 1;
@@ -1000,15 +1062,43 @@ __global__ __launch_bounds__(WT) void k_bi_emit(
       ++qg;
     }
   }
-  if (staged) {
+  if (listed) {
     __syncthreads();
-    const int64_t lim = std::min<int64_t>(nblk_out, nnz - bo.x);
-    // the values with plain stores: the column emitter of a fused prepare
-    // gathers them again right after
-    for (int64_t j = t; j < lim; j += WT) {
-      __builtin_nontemporal_store(srow[j], &row[bo.x + j]);
-      __builtin_nontemporal_store(scol[j], &col[bo.x + j]);
-      vals[bo.x + j] = sval[j];
+    const int32_t lim = (int32_t)std::max<int64_t>(0, std::min<int64_t>(nblk_out, nnz - bo.x));
+    // two entries per thread per round, their survivor-value loads in flight
+    // together; row and column indices with streaming stores, the values with
+    // plain ones (the column emitter of a fused prepare gathers them again)
+    for (int32_t j0 = t; j0 < lim; j0 += 2 * WT) {
+      int32_t r[2], cc[2];
+      bool live[2], surv[2];
+      int64_t src[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int32_t j = j0 + u * WT;
+        live[u] = j < lim;
+        const uint32_t e = ent[live[u] ? j : j0];
+        const int wl = (int)(e >> 5), bt = (int)(e & 31u);
+        const uint32_t Sw = sS[wl];
+        surv[u] = (Sw >> bt) & 1u;
+        src[u] = surv[u] ? (int64_t)sq[wl] + __popc(Sw & ((1u << bt) - 1u)) : 0;
+        r[u] = sr[wl];
+        cc[u] = sc[wl] + bt;
+      }
+      T v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) v[u] = vals_ws[src[u]];  // src 0 when unused: in range
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!live[u]) continue;
+        while (cc[u] >= K) {
+          cc[u] -= K;
+          ++r[u];
+        }
+        const int64_t q = bo.x + j0 + u * WT;
+        __builtin_nontemporal_store(r[u], &row[q]);
+        __builtin_nontemporal_store(cc[u], &col[q]);
+        vals[q] = surv[u] ? v[u] : (T)0;
+      }
     }
   }
 }
@@ -1049,14 +1139,17 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
     int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rb, int32_t* __restrict__ res,
     uint32_t* __restrict__ FT, int32_t* __restrict__ tsum) {
   __shared__ int32_t tsl[TS_SPAN];
-  if (bm_failed(st)) return;
   const int64_t KW = K >> 5, WM = M >> 5;
   if ((int)blockIdx.x < rb) {
+    // the FP loads (clamped in range) go out before the state check
     const int64_t s = (int64_t)blockIdx.x * FP_THREADS + threadIdx.x;
+    const int32_t fa = (int32_t)FP[(s < M ? s : M - 1) * KW].y;
+    const int32_t fb = (int32_t)FP[(s + 1 < M ? s + 1 : M - 1) * KW].y;
+    if (bm_failed(st)) return;
     bool any = false;
     if (s < M) {
-      const int64_t a = (int32_t)FP[s * KW].y;
-      const int64_t b = s + 1 < M ? (int64_t)(int32_t)FP[(s + 1) * KW].y : nnz;
+      const int64_t a = fa;
+      const int64_t b = s + 1 < M ? (int64_t)fb : nnz;
       f.row_ptr[s] = (int32_t)a;
       any = tile_cuts(s, a, b, nnz, f.T_row, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
     } else if (s == M) {
@@ -1073,7 +1166,9 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
   const int lane = threadIdx.x & 63, l = lane & 31;
   const int64_t rw = rw0 + 2 * (threadIdx.x >> 6) + (lane >> 5);
   const bool ok = wc < KW && rw < WM;
-  const uint32_t word = ok ? FP[(rw * 32 + l) * KW + wc].x : 0u;
+  const uint32_t w0 = FP[ok ? (rw * 32 + l) * KW + wc : 0].x;  // before the state check
+  if (bm_failed(st)) return;
+  const uint32_t word = ok ? w0 : 0u;
   uint32_t out = 0;
 #pragma unroll
   for (int b = 0; b < 32; ++b) {
@@ -1112,42 +1207,63 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
 // block holds whole columns) the block also writes the column tiles of its
 // columns and sets res[3] if one of them is split.
 template <typename T>
-__global__ __launch_bounds__(WT) void k_fp_temit(
+__global__ __launch_bounds__(WT, 8) void k_fp_temit(
     const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int64_t nbt, int32_t M,
     int32_t K, const int4* __restrict__ tsum, const int4* __restrict__ toff,
     const uint2* __restrict__ FP, int64_t nnz, fuse_ptrs f, int32_t cols_here,
     int32_t* __restrict__ res, const T* __restrict__ vals, T* __restrict__ vals_t) {
-  __shared__ int32_t lds[WT / SNK_WAVE];
-  __shared__ int32_t red[WT / SNK_WAVE];
+  __shared__ int32_t lds[WT / SNK_WAVE * 2];
   __shared__ int32_t cstart[WT];
+  __shared__ uint32_t ent[EMIT_CAP];  // (word in block << 5) | bit, in output order
+  __shared__ int32_t scol[WT], srw[WT];
   const int64_t per_xcd = cdiv_dev(nbt, NUM_XCD);
   const int64_t tb = (int64_t)(blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
-  if (tb >= nbt || bm_failed(st)) return;  // uniform over the block
+  if (tb >= nbt) return;  // uniform over the block
   const int t = threadIdx.x;
-  int64_t base;
-  if (toff) {
-    base = toff[tb].x;
-  } else {
-    int32_t sacc = 0;
-    for (int64_t i = t; i < tb; i += 2 * WT) {  // two loads in flight
-      const int64_t i2 = i + WT < tb ? i + WT : i;
-      const int32_t x = tsum[i].x, y = tsum[i2].x;
-      sacc += i2 != i ? x + y : x;
-    }
-    for (int off = 32; off > 0; off >>= 1) sacc += __shfl_xor(sacc, off, SNK_WAVE);
-    if (lane_id() == 0) red[t / SNK_WAVE] = sacc;
-    __syncthreads();
-    base = 0;
-    for (int k = 0; k < WT / SNK_WAVE; ++k) base += red[k];
-  }
-  const int64_t KW = K >> 5, WM = M >> 5;
+  // loads that depend on nothing first: the thread's FT word and the block
+  // sums before it (up to 2 WT of them here), then the state words
   const int64_t i = tb * WT + t;
   const bool valid = i < NT;
-  uint32_t word = valid ? FT[i] : 0u;
-  int32_t tot;
-  int64_t q = base + block_excl_scan_i32<WT>(__popc(word), lds, &tot);
-  const int64_t c = i / WM, rw = i - c * WM;
-  const int64_t c0 = tb * WT / WM;  // first column of the block (cols_here)
+  const uint32_t word0 = FT[valid ? i : NT - 1];
+  int32_t p0 = 0, p1 = 0;
+  if (!toff && tb > 0) {
+    p0 = tsum[t < tb ? t : 0].x;
+    p1 = tsum[t + WT < tb ? t + WT : 0].x;
+  }
+  if (bm_failed(st)) return;  // uniform over the grid
+  // this thread's share of the block base (the entries of earlier blocks),
+  // reduced by the block together with the scan of its words' counts
+  int32_t part = 0;
+  if (!toff) {
+    part = (t < tb ? p0 : 0) + (t + WT < tb ? p1 : 0);
+    for (int64_t k = t + 2 * WT; k < tb; k += 2 * WT) {  // two loads in flight
+      const int64_t k2 = k + WT < tb ? k + WT : k;
+      const int32_t x = tsum[k].x, y = tsum[k2].x;
+      part += k2 != k ? x + y : x;
+    }
+  }
+  const int64_t KW = K >> 5, WM = M >> 5;
+  const uint32_t word = valid ? word0 : 0u;
+  int32_t ex1[1], tt1[1], sm1[1];
+  {
+    const int32_t xs[1] = {(int32_t)__popc(word)};
+    const int32_t ys[1] = {part};
+    block_scan_sum<WT, 1, 1>(xs, ys, lds, ex1, tt1, sm1);
+  }
+  const int64_t base = toff ? (int64_t)toff[tb].x : (int64_t)sm1[0];
+  const int32_t tot = tt1[0];
+  int64_t q = base + ex1[0];
+  // column and row word of the thread's FT word (32-bit division when the
+  // words fit)
+  int64_t c, c0;
+  if (NT + WT <= INT32_MAX) {
+    c = (int64_t)((uint32_t)i / (uint32_t)WM);
+    c0 = (int64_t)((uint32_t)(tb * WT) / (uint32_t)WM);  // first column of the block (cols_here)
+  } else {
+    c = i / WM;
+    c0 = tb * WT / WM;
+  }
+  const int64_t rw = i - c * WM;
   if (valid && rw == 0) {
     f.col_ptr[c] = (int32_t)q;
     if (cols_here) cstart[c - c0] = (int32_t)q;
@@ -1156,8 +1272,9 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
     f.col_ptr[K] = (int32_t)nnz;
     if (cols_here) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
   }
-  if (cols_here) {  // the tiles of the block's columns, before the entries
-    __syncthreads();
+  // the tiles of the block's columns (threads t < WT / WM), once cstart is
+  // published
+  auto col_tiles = [&]() {
     const int64_t ncol = WT / WM;
     const int64_t s = c0 + t;
     bool any = false;
@@ -1167,16 +1284,64 @@ __global__ __launch_bounds__(WT) void k_fp_temit(
       any = tile_cuts(s, a, b, nnz, f.T_col, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
     }
     if (__ballot(any) != 0 && lane_id() == 0) store_result(&res[3], 1);
+  };
+  if (tot <= EMIT_CAP) {  // block-uniform: the entries listed in LDS, one per thread per round
+    scol[t] = (int32_t)c;
+    srw[t] = (int32_t)rw;
+    int32_t o = (int32_t)(q - base);
+    for (uint32_t x = word; x; x &= x - 1) ent[o++] = ((uint32_t)t << 5) | (uint32_t)(__ffs(x) - 1);
+    __syncthreads();  // publishes the list and cstart
+    if (cols_here) col_tiles();
+    const int32_t lim = (int32_t)std::max<int64_t>(0, std::min<int64_t>(tot, nnz - base));
+    // two entries per thread per round: both FP gathers, then both value
+    // gathers, in flight together
+    for (int32_t j0 = t; j0 < lim; j0 += 2 * WT) {
+      int32_t r[2], cc[2];
+      bool live[2];
+      uint2 fp[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int32_t j = j0 + u * WT;
+        live[u] = j < lim;
+        const uint32_t e = ent[live[u] ? j : j0];
+        const int tl = (int)(e >> 5);
+        cc[u] = scol[tl];
+        r[u] = srw[tl] * 32 + (int)(e & 31u);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) fp[u] = FP[(int64_t)r[u] * KW + (cc[u] >> 5)];
+      int32_t pos[2];
+      T v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & ((1u << (cc[u] & 31)) - 1u));
+        if (vals_t) v[u] = vals[pos[u] < nnz ? pos[u] : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!live[u]) continue;
+        const int64_t qq = base + j0 + u * WT;
+        f.row_t[qq] = r[u];
+        f.perm[qq] = pos[u];
+        if (vals_t) vals_t[qq] = v[u];
+      }
+    }
+    return;
+  }
+  if (cols_here) {
+    __syncthreads();  // publishes cstart
+    col_tiles();
   }
   if (!valid) return;
+  uint32_t word_left = word;
   const uint32_t below = (1u << (c & 31)) - 1u;
-  while (word) {
+  while (word_left) {
     int j[EMIT_BATCH];
     uint2 fp[EMIT_BATCH];
 #pragma unroll
     for (int u = 0; u < EMIT_BATCH; ++u) {
-      j[u] = word ? __ffs(word) - 1 : -1;
-      word &= word - 1;
+      j[u] = word_left ? __ffs(word_left) - 1 : -1;
+      word_left &= word_left - 1;
     }
 #pragma unroll
     for (int u = 0; u < EMIT_BATCH; ++u)
@@ -1374,10 +1539,16 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
                      bsum);
   const bool own_base = L.nb <= PREFIX_INBLOCK_MAX;
   if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
-  hipLaunchKernelGGL(k_bi_emit<T>, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
-                     bsum, own_base ? nullptr : boff, vals_ws, K,
-                     (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
-                     col, vals, dropped_lin, grown_lin);
+  if (dropped_lin || grown_lin)
+    hipLaunchKernelGGL((k_bi_emit<T, true>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
+                       grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
+                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
+                       col, vals, dropped_lin, grown_lin);
+  else
+    hipLaunchKernelGGL((k_bi_emit<T, false>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
+                       grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
+                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
+                       col, vals, nullptr, nullptr);
   if (fuse) {
     uint32_t* FT = (uint32_t*)(ws + L.ft);
     int4* tsum = (int4*)(ws + L.tsum);

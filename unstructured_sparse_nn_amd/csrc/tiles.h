@@ -25,8 +25,15 @@ __device__ __forceinline__ bool tile_cuts(int64_t s, int64_t a, int64_t b, int64
                                           int32_t* __restrict__ cut) {
   if (a < 0 || b < a || b > nnz) return false;
   const int64_t first = a + s, last = b + s;
-  const int64_t p0 = (first + T - 1) / T;
-  const int64_t p1 = std::min<int64_t>(last / T, (int64_t)P - 1);
+  int64_t p0, pl;
+  if (last + T <= (int64_t)UINT32_MAX) {  // 32-bit division when the items fit
+    p0 = ((uint32_t)first + (uint32_t)T - 1u) / (uint32_t)T;
+    pl = (uint32_t)last / (uint32_t)T;
+  } else {
+    p0 = (first + T - 1) / T;
+    pl = last / T;
+  }
+  const int64_t p1 = std::min<int64_t>(pl, (int64_t)P - 1);
   const bool is_long = (b - a) >= T;
   bool any = false;
   for (int64_t p = p0; p <= p1; ++p) {
