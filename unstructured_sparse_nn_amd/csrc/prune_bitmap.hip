@@ -401,6 +401,7 @@ __device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t n
         if (m < nwg && run0[m] <= e[u]) lo[u] = m;
       }
     }
+    // an unused slot reads the first element (L1-resident; discarded)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       pc[u] = cand[ok[u] ? start[lo[u]] + (e[u] - run0[lo[u]]) : 0];
@@ -1080,13 +1081,14 @@ __global__ __launch_bounds__(WT, LISTS ? 6 : 8) void k_bi_emit(
         const int wl = (int)(e >> 5), bt = (int)(e & 31u);
         const uint32_t Sw = sS[wl];
         surv[u] = (Sw >> bt) & 1u;
+        // a grown entry reads the first element (L1-resident; discarded)
         src[u] = surv[u] ? (int64_t)sq[wl] + __popc(Sw & ((1u << bt) - 1u)) : 0;
         r[u] = sr[wl];
         cc[u] = sc[wl] + bt;
       }
       T v[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) v[u] = vals_ws[src[u]];  // src 0 when unused: in range
+      for (int u = 0; u < 2; ++u) v[u] = vals_ws[src[u]];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (!live[u]) continue;
@@ -1202,10 +1204,13 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_rows_transpose(
 // first entry = block base + block scan.  Word block tb holds columns
 // [tb*WT/WM, ...); workgroup b (dispatched to XCD b mod 8) takes word block
 // (b mod 8)*ceil(nbt/8) + b/8, so each XCD gathers the FP lines of one
-// contiguous column range.  A thread takes its entries EMIT_BATCH at a time,
-// all their FP loads in flight together.  With cols_here (WM divides WT, so a
-// block holds whole columns) the block also writes the column tiles of its
-// columns and sets res[3] if one of them is split.
+// contiguous column range.  The gathers of a thread's first TE_FIRST entries
+// (the FP word of each entry's row, then its value) go out before the block
+// scan, so that their round trips overlap it; further entries (rare) follow
+// in batches of EMIT_BATCH.  With cols_here (WM divides WT, so a block holds
+// whole columns) the block also writes the column tiles of its columns and
+// sets res[3] if one of them is split.
+constexpr int TE_FIRST = 4;
 template <typename T>
 __global__ __launch_bounds__(WT, 8) void k_fp_temit(
     const bm_state* st, const uint32_t* __restrict__ FT, int64_t NT, int64_t nbt, int32_t M,
@@ -1214,8 +1219,6 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
     int32_t* __restrict__ res, const T* __restrict__ vals, T* __restrict__ vals_t) {
   __shared__ int32_t lds[WT / SNK_WAVE * 2];
   __shared__ int32_t cstart[WT];
-  __shared__ uint32_t ent[EMIT_CAP];  // (word in block << 5) | bit, in output order
-  __shared__ int32_t scol[WT], srw[WT];
   const int64_t per_xcd = cdiv_dev(nbt, NUM_XCD);
   const int64_t tb = (int64_t)(blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
   if (tb >= nbt) return;  // uniform over the block
@@ -1231,28 +1234,8 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
     p1 = tsum[t + WT < tb ? t + WT : 0].x;
   }
   if (bm_failed(st)) return;  // uniform over the grid
-  // this thread's share of the block base (the entries of earlier blocks),
-  // reduced by the block together with the scan of its words' counts
-  int32_t part = 0;
-  if (!toff) {
-    part = (t < tb ? p0 : 0) + (t + WT < tb ? p1 : 0);
-    for (int64_t k = t + 2 * WT; k < tb; k += 2 * WT) {  // two loads in flight
-      const int64_t k2 = k + WT < tb ? k + WT : k;
-      const int32_t x = tsum[k].x, y = tsum[k2].x;
-      part += k2 != k ? x + y : x;
-    }
-  }
   const int64_t KW = K >> 5, WM = M >> 5;
   const uint32_t word = valid ? word0 : 0u;
-  int32_t ex1[1], tt1[1], sm1[1];
-  {
-    const int32_t xs[1] = {(int32_t)__popc(word)};
-    const int32_t ys[1] = {part};
-    block_scan_sum<WT, 1, 1>(xs, ys, lds, ex1, tt1, sm1);
-  }
-  const int64_t base = toff ? (int64_t)toff[tb].x : (int64_t)sm1[0];
-  const int32_t tot = tt1[0];
-  int64_t q = base + ex1[0];
   // column and row word of the thread's FT word (32-bit division when the
   // words fit)
   int64_t c, c0;
@@ -1264,6 +1247,51 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
     c0 = tb * WT / WM;
   }
   const int64_t rw = i - c * WM;
+  const uint32_t below = (1u << (c & 31)) - 1u;
+  // the first entries' gathers, unconditional: an unused slot reads the
+  // first element (one line, which every CU keeps in its L1; re-reading the
+  // thread's own first address instead measured 35% slower, each such read
+  // being one more L2 request) and its result is discarded
+  int32_t j[TE_FIRST], pos[TE_FIRST];
+  T v[TE_FIRST];
+  uint32_t rest = word;
+  {
+    uint2 fp[TE_FIRST];
+#pragma unroll
+    for (int u = 0; u < TE_FIRST; ++u) {
+      j[u] = rest ? __ffs(rest) - 1 : -1;
+      rest &= rest - 1;
+    }
+#pragma unroll
+    for (int u = 0; u < TE_FIRST; ++u)
+      fp[u] = FP[j[u] >= 0 ? (rw * 32 + j[u]) * KW + (c >> 5) : 0];
+#pragma unroll
+    for (int u = 0; u < TE_FIRST; ++u) pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+    // all value loads issued back to back (vals_t or not: the new values
+    // always exist), waited for only at the stores after the scan
+#pragma unroll
+    for (int u = 0; u < TE_FIRST; ++u) v[u] = vals[(j[u] >= 0 && pos[u] < nnz) ? pos[u] : 0];
+  }
+  // this thread's share of the block base (the entries of earlier blocks),
+  // reduced by the block together with the scan of its words' counts
+  int32_t part = 0;
+  if (!toff) {
+    part = (t < tb ? p0 : 0) + (t + WT < tb ? p1 : 0);
+    for (int64_t k = t + 2 * WT; k < tb; k += 2 * WT) {  // two loads in flight
+      const int64_t k2 = k + WT < tb ? k + WT : k;
+      const int32_t x = tsum[k].x, y = tsum[k2].x;
+      part += k2 != k ? x + y : x;
+    }
+  }
+  int32_t ex1[1], tt1[1], sm1[1];
+  {
+    const int32_t xs[1] = {(int32_t)__popc(word)};
+    const int32_t ys[1] = {part};
+    block_scan_sum<WT, 1, 1>(xs, ys, lds, ex1, tt1, sm1);
+  }
+  const int64_t base = toff ? (int64_t)toff[tb].x : (int64_t)sm1[0];
+  const int32_t tot = tt1[0];
+  int64_t q = base + ex1[0];
   if (valid && rw == 0) {
     f.col_ptr[c] = (int32_t)q;
     if (cols_here) cstart[c - c0] = (int32_t)q;
@@ -1272,9 +1300,46 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
     f.col_ptr[K] = (int32_t)nnz;
     if (cols_here) tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
   }
-  // the tiles of the block's columns (threads t < WT / WM), once cstart is
-  // published
-  auto col_tiles = [&]() {
+#pragma unroll
+  for (int u = 0; u < TE_FIRST; ++u) {
+    if (j[u] >= 0 && q < nnz) {
+      f.row_t[q] = (int32_t)(rw * 32 + j[u]);
+      f.perm[q] = pos[u];
+      if (vals_t) vals_t[q] = v[u];
+    }
+    q += j[u] >= 0 ? 1 : 0;
+  }
+  while (rest) {  // words with more than TE_FIRST entries
+    int jb[EMIT_BATCH];
+    uint2 fp[EMIT_BATCH];
+#pragma unroll
+    for (int u = 0; u < EMIT_BATCH; ++u) {
+      jb[u] = rest ? __ffs(rest) - 1 : -1;
+      rest &= rest - 1;
+    }
+#pragma unroll
+    for (int u = 0; u < EMIT_BATCH; ++u)
+      fp[u] = jb[u] >= 0 ? FP[(rw * 32 + jb[u]) * KW + (c >> 5)] : make_uint2(0u, 0u);
+    int32_t pb[EMIT_BATCH];
+    T vb[EMIT_BATCH];
+#pragma unroll
+    for (int u = 0; u < EMIT_BATCH; ++u) {
+      pb[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
+      if (vals_t) vb[u] = (jb[u] >= 0 && pb[u] < nnz) ? vals[pb[u]] : (T)0;
+    }
+#pragma unroll
+    for (int u = 0; u < EMIT_BATCH; ++u) {
+      if (jb[u] < 0) break;
+      if (q < nnz) {
+        f.row_t[q] = (int32_t)(rw * 32 + jb[u]);
+        f.perm[q] = pb[u];
+        if (vals_t) vals_t[q] = vb[u];
+      }
+      ++q;
+    }
+  }
+  if (cols_here) {  // the tiles of the block's columns
+    __syncthreads();  // publishes cstart
     const int64_t ncol = WT / WM;
     const int64_t s = c0 + t;
     bool any = false;
@@ -1284,89 +1349,6 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
       any = tile_cuts(s, a, b, nnz, f.T_col, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
     }
     if (__ballot(any) != 0 && lane_id() == 0) store_result(&res[3], 1);
-  };
-  if (tot <= EMIT_CAP) {  // block-uniform: the entries listed in LDS, one per thread per round
-    scol[t] = (int32_t)c;
-    srw[t] = (int32_t)rw;
-    int32_t o = (int32_t)(q - base);
-    for (uint32_t x = word; x; x &= x - 1) ent[o++] = ((uint32_t)t << 5) | (uint32_t)(__ffs(x) - 1);
-    __syncthreads();  // publishes the list and cstart
-    if (cols_here) col_tiles();
-    const int32_t lim = (int32_t)std::max<int64_t>(0, std::min<int64_t>(tot, nnz - base));
-    // two entries per thread per round: both FP gathers, then both value
-    // gathers, in flight together
-    for (int32_t j0 = t; j0 < lim; j0 += 2 * WT) {
-      int32_t r[2], cc[2];
-      bool live[2];
-      uint2 fp[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int32_t j = j0 + u * WT;
-        live[u] = j < lim;
-        const uint32_t e = ent[live[u] ? j : j0];
-        const int tl = (int)(e >> 5);
-        cc[u] = scol[tl];
-        r[u] = srw[tl] * 32 + (int)(e & 31u);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) fp[u] = FP[(int64_t)r[u] * KW + (cc[u] >> 5)];
-      int32_t pos[2];
-      T v[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & ((1u << (cc[u] & 31)) - 1u));
-        if (vals_t) v[u] = vals[pos[u] < nnz ? pos[u] : 0];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (!live[u]) continue;
-        const int64_t qq = base + j0 + u * WT;
-        f.row_t[qq] = r[u];
-        f.perm[qq] = pos[u];
-        if (vals_t) vals_t[qq] = v[u];
-      }
-    }
-    return;
-  }
-  if (cols_here) {
-    __syncthreads();  // publishes cstart
-    col_tiles();
-  }
-  if (!valid) return;
-  uint32_t word_left = word;
-  const uint32_t below = (1u << (c & 31)) - 1u;
-  while (word_left) {
-    int j[EMIT_BATCH];
-    uint2 fp[EMIT_BATCH];
-#pragma unroll
-    for (int u = 0; u < EMIT_BATCH; ++u) {
-      j[u] = word_left ? __ffs(word_left) - 1 : -1;
-      word_left &= word_left - 1;
-    }
-#pragma unroll
-    for (int u = 0; u < EMIT_BATCH; ++u)
-      fp[u] = j[u] >= 0 ? FP[(rw * 32 + j[u]) * KW + (c >> 5)] : make_uint2(0u, 0u);
-    int32_t pos[EMIT_BATCH];
-#pragma unroll
-    for (int u = 0; u < EMIT_BATCH; ++u) pos[u] = (int32_t)fp[u].y + __popc(fp[u].x & below);
-    // the value of each entry in column order: one gather of the new values,
-    // the whole batch in flight together
-    T v[EMIT_BATCH];
-    if (vals_t) {
-#pragma unroll
-      for (int u = 0; u < EMIT_BATCH; ++u)
-        v[u] = (j[u] >= 0 && q + u < nnz) ? vals[pos[u]] : (T)0;
-    }
-#pragma unroll
-    for (int u = 0; u < EMIT_BATCH; ++u) {
-      if (j[u] < 0) break;
-      if (q < nnz) {
-        f.row_t[q] = (int32_t)(rw * 32 + j[u]);
-        f.perm[q] = pos[u];
-        if (vals_t) vals_t[q] = v[u];
-      }
-      ++q;
-    }
   }
 }
 
