@@ -654,6 +654,15 @@ PREPARED_CASES = [
     # 8192 x 8448 at 2.9%: past 2^26 positions, so regrow chunk 0 takes the
     # grid-wide atomic path instead of the per-region buckets
     ("wide_grid", "bf16", 300000, 5, 3, 0),
+    # without the dropped and grown lists (the emitter instance the training
+    # step runs)
+    ("square_0.95_32_nolists", "bf16", 300000, 3, 2, 0),
+    # 12288 rows: the most the column emitter stages; 3 column words, so each
+    # workgroup writes 1,025 row pointers (more than its threads)
+    ("rows_at_max", "bf16", 300000, 8, 1, 0),
+    # 12320 rows: past it, so the transposed bitmap and its emitter run
+    ("rows_past_max", "bf16", 300000, 9, 1, 0),
+    ("rows_past_max_nolists", "f32", 300000, 9, 2, 0),
 ]
 
 
@@ -668,8 +677,13 @@ def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile)
         w = synth.random_case(12, 512, 512, 512 * 512 // 4, 1, dt).weights[0]
     elif name == "wide_grid":
         w = synth.random_case(12, 8192, 8448, 2000000, 1, dt).weights[0]
+    elif name == "rows_at_max":
+        w = synth.random_case(13, 12288, 96, 12288 * 96 // 20, 1, dt).weights[0]
+    elif name.startswith("rows_past_max"):
+        w = synth.random_case(14, 12320, 256, 12320 * 256 // 20, 1, dt).weights[0]
     else:
-        w = workload(name).weights[0]
+        w = workload(name.replace("_nolists", "")).weights[0]
+    lists = not name.endswith("_nolists")
     n_drop = orc.drop_count(w.nnz, ppm)
     ref = orc.prune_regrow(w.M, w.K, w.row, w.col, w.vals, dt, n_drop, seed, step)
     assert ref["rc"] == 0
@@ -677,15 +691,16 @@ def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile)
     v = to_dev(w.vals, dt)
     ws = torch.empty(snk.snack_prune_regrow_workspace(w.M, w.K, w.nnz, n_drop, prune_plan),
                      dtype=torch.uint8, device="cuda")
-    dl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
-    gl = torch.empty(n_drop, dtype=torch.int64, device="cuda")
+    dl = torch.empty(n_drop, dtype=torch.int64, device="cuda") if lists else None
+    gl = torch.empty(n_drop, dtype=torch.int64, device="cuda") if lists else None
     vt = torch.full_like(v, 3.0)  # receives the new values in the new column order
     snk.snack_prune_regrow_prepared(topo.plan, topo.row, topo.col, v, n_drop, seed, step, dl, gl,
                                     ws, vals_t=vt, flags=prune_plan)
     assert np.array_equal(topo.row.cpu().numpy(), ref["row"])
     assert np.array_equal(topo.col.cpu().numpy(), ref["col"])
-    assert np.array_equal(dl.cpu().numpy(), ref["dropped"])
-    assert np.array_equal(gl.cpu().numpy(), ref["grown"])
+    if lists:
+        assert np.array_equal(dl.cpu().numpy(), ref["dropped"])
+        assert np.array_equal(gl.cpu().numpy(), ref["grown"])
     w2 = synth.SparseWeight(w.M, w.K, ref["row"], ref["col"], ref["vals"], dt)
     check_prepare(orc, w2, topo)
     _, perm, _ = orc.csc(w.K, ref["row"], ref["col"])

@@ -69,6 +69,7 @@ constexpr int EMIT_CAP = 4096;
 // EMIT_CAP) takes per batch, their gathers in flight together.
 constexpr int EMIT_BATCH = 4;
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
+constexpr int FC_MAX_M = 12288;           // rows the column emitter stages in LDS
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
 // are fat (few blocks) and their counters spread over replicas.
@@ -84,6 +85,13 @@ struct bm_state {
   int32_t ch_acc[SLOTS][AREPL];  // chunk c: positions it took, over AREPL counters
   int32_t hist[4][HREPL][256];   // select histograms; block b adds into replica b % HREPL
 };
+
+// FP in 16-row tiles: word (r, cw) of a K/32-word row at
+// (r/16) * 16 K/32 + cw * 16 + r%16, so that a column word's words of 16
+// consecutive rows fill one 128-byte line.
+__host__ __device__ __forceinline__ int64_t fp_tile_index(int64_t r, int64_t cw, int64_t KW) {
+  return (r >> 4) * (16 * KW) + cw * 16 + (r & 15);
+}
 
 __device__ __forceinline__ int32_t chunk_taken(const bm_state* st, int c) {
   int32_t a = 0;
@@ -919,15 +927,15 @@ __global__ __launch_bounds__(1024) void k_bi_bscan(const int4* __restrict__ in,
 // positions missing) into pinned host memory; nothing else is written
 // unless both are 0.  Writes are clamped to nnz / n_drop.
 template <typename T, bool LISTS>
-__global__ __launch_bounds__(WT, LISTS ? 6 : 8) void k_bi_emit(
+__global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
     const uint32_t* __restrict__ sup, const uint32_t* __restrict__ dropb,
     const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
     const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
     int64_t nnz, int64_t n_drop, const bm_state* st, int32_t* __restrict__ result,
-    uint2* __restrict__ FP, int32_t* __restrict__ row,
+    uint2* __restrict__ FP, int32_t fp_tiled, int32_t* __restrict__ rs_blk, int32_t* __restrict__ row,
     int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
     int64_t* __restrict__ grown_lin) {
-  __shared__ int32_t lds[WT / SNK_WAVE * 6];
+  __shared__ int32_t lds[WT / SNK_WAVE * 7];
   __shared__ uint32_t ent[EMIT_CAP];  // (word in block << 5) | bit, in output order
   __shared__ uint32_t sS[WT];
   __shared__ int32_t sq[WT], sr[WT], sc[WT];
@@ -974,28 +982,47 @@ __global__ __launch_bounds__(WT, LISTS ? 6 : 8) void k_bi_emit(
   }
   const uint32_t S = w < W ? S0 : 0u, D = w < W ? D0 : 0u, G = w < W ? G0 : 0u;
   const int4 c = word_counts(S, D, G);
+  const uint32_t F0 = (S & ~D) | G;
+  const int64_t pw = w * 32;
+  // row and column of the word's first position; the rest step from it
+  int32_t r0 = 0, c0 = 0;
+  if (F0 || fp_tiled) {
+    if (small_grid) {
+      r0 = (int32_t)((uint32_t)pw / (uint32_t)K);
+      c0 = (int32_t)((uint32_t)pw - (uint32_t)r0 * (uint32_t)K);
+    } else {
+      r0 = (int32_t)(pw / K);
+      c0 = (int32_t)(pw - (int64_t)r0 * K);
+    }
+  }
+  // for the column emitter: the sum over rows of the new row starts equals
+  // sum_r count(r) * (M - 1 - r); each block adds its words' terms
+  const int32_t rsw = fp_tiled && w < W ? c.x * (int32_t)(W / (K >> 5) - 1 - r0) : 0;
   // a block holds at most 32 * WT = 16384 positions, so two counts share an
   // int32 (15 bits each, no overflow): two scans serve all four
-  int32_t fs, nf, dg = 0;
+  int32_t fs, nf, dg = 0, rs_sum;
   int4 bo;
   if constexpr (LISTS) {
-    int32_t ex[2], tt[2], sm[4];
+    int32_t ex[2], tt[2], sm[5];
     const int32_t xs[2] = {c.x | (c.y << 16), c.z | (c.w << 16)};
-    const int32_t ys[4] = {part.x, part.y, part.z, part.w};
-    block_scan_sum<WT, 2, 4>(xs, ys, lds, ex, tt, sm);
+    const int32_t ys[5] = {part.x, part.y, part.z, part.w, rsw};
+    block_scan_sum<WT, 2, 5>(xs, ys, lds, ex, tt, sm);
     bo = boff ? boff[blockIdx.x] : make_int4(sm[0], sm[1], sm[2], sm[3]);
     fs = ex[0];
     dg = ex[1];
     nf = tt[0];
+    rs_sum = sm[4];
   } else {
-    int32_t ex[1], tt[1], sm[2];
+    int32_t ex[1], tt[1], sm[3];
     const int32_t xs[1] = {c.x | (c.y << 16)};
-    const int32_t ys[2] = {part.x, part.y};
-    block_scan_sum<WT, 1, 2>(xs, ys, lds, ex, tt, sm);
+    const int32_t ys[3] = {part.x, part.y, rsw};
+    block_scan_sum<WT, 1, 3>(xs, ys, lds, ex, tt, sm);
     bo = boff ? boff[blockIdx.x] : make_int4(sm[0], sm[1], 0, 0);
     fs = ex[0];
     nf = tt[0];
+    rs_sum = sm[2];
   }
+  if (fp_tiled && t == 0) rs_blk[blockIdx.x] = rs_sum;
   // the block's new entries are [bo.x, bo.x + nblk_out); listed in LDS when
   // they fit (block-uniform), so that each thread takes one entry per round
   // and the stores are coalesced
@@ -1005,21 +1032,13 @@ __global__ __launch_bounds__(WT, LISTS ? 6 : 8) void k_bi_emit(
   const int64_t qs = bo.y + (fs >> 16);
   int64_t qd = bo.z + (dg & 0xFFFF);
   int64_t qg = bo.w + (dg >> 16);
-  const int64_t pw = w * 32;
-  uint32_t F = (S & ~D) | G;
-  if (FP && w < W)  // the new support and its per-word prefix, for a fused prepare
-    FP[w] = make_uint2(F, (uint32_t)qf);
-  // row and column of the word's first position; the rest step from it
-  int32_t r0 = 0, c0 = 0;
-  if (F) {
-    if (small_grid) {
-      r0 = (int32_t)((uint32_t)pw / (uint32_t)K);
-      c0 = (int32_t)((uint32_t)pw - (uint32_t)r0 * (uint32_t)K);
-    } else {
-      r0 = (int32_t)(pw / K);
-      c0 = (int32_t)(pw - (int64_t)r0 * K);
-    }
+  uint32_t F = F0;
+  if (FP && w < W) {  // the new support and its per-word prefix, for a fused prepare
+    // (row-major, or in 16-row tiles when the column emitter reads it)
+    const int64_t at = fp_tiled ? fp_tile_index(r0, c0 >> 5, (int64_t)K >> 5) : w;
+    FP[at] = make_uint2(F, (uint32_t)qf);
   }
+
   if (listed) {
     sS[t] = S;
     sq[t] = (int32_t)qs;
@@ -1352,6 +1371,185 @@ __global__ __launch_bounds__(WT, 8) void k_fp_temit(
   }
 }
 
+// Column view straight from F (up to FC_MAX_M rows): workgroup b owns FC_CPB
+// columns [ca, ca + FC_CPB) of column word cw = b / FC_SPLIT and stages that
+// word of every row (F and its row-major prefix P, from the 16-row tiles of
+// FP) in LDS.  Its entries come out in column-major order from 64-row
+// ballots of its columns' bits, so no transposed bitmap is written.  Its
+// place in the output needs no other workgroup: the entries in columns
+// before ca are, summed over rows, the row-major prefix at (r, ca) minus the
+// row's start, i.e. sum_r (P(r, cw) + popc(F(r, cw) below ca)) - sum_r
+// start(r), the last sum being the row emitter's per-block terms.  A value
+// is gathered from the new row-major values at its row-major rank.  Each
+// workgroup also writes row_ptr and the row tiles of rows
+// [b * rpb, (b + 1) * rpb) (res[2] on a split row), and its columns' col_ptr
+// and tiles (res[3] on a split column).
+constexpr int FC_THREADS = 512;
+constexpr int FC_SPLIT = 4;                       // workgroups per column word
+constexpr int FC_CPB = 32 / FC_SPLIT;             // columns per workgroup
+constexpr int FC_MAX_CH = FC_MAX_M / SNK_WAVE;    // 64-row chunks at most
+constexpr int FC_IPT = FC_CPB * FC_MAX_CH / FC_THREADS;  // (column, chunk) items per thread at most
+constexpr int FC_LOAD = 8;                        // row loads per thread in flight
+inline size_t fc_lds_bytes(int32_t M) {
+  return 8 * (size_t)FC_CPB * (size_t)cdiv((int64_t)M, SNK_WAVE) + 8 * (size_t)M;
+}
+template <typename T>
+__global__ __launch_bounds__(FC_THREADS) void k_fp_colemit(
+    const bm_state* st, const uint2* __restrict__ FP, const int32_t* __restrict__ rs_blk,
+    int64_t nb, int32_t M, int32_t K, int64_t nnz, fuse_ptrs f, int32_t rpb,
+    int32_t* __restrict__ res, const T* __restrict__ vals, T* __restrict__ vals_t) {
+  // dynamic LDS (fc_lds_bytes): the 64-row masks of the columns, then F and
+  // P of every row
+  extern __shared__ uint64_t fc_smem[];
+  __shared__ int32_t lds[FC_THREADS / SNK_WAVE * 3];
+  __shared__ int32_t cstart[FC_CPB];
+  const int nch = (M + SNK_WAVE - 1) / SNK_WAVE;
+  uint64_t* sm = fc_smem;  // [FC_CPB][nch]
+  uint32_t* sF = reinterpret_cast<uint32_t*>(fc_smem + FC_CPB * nch);
+  int32_t* sP = reinterpret_cast<int32_t*>(sF + M);
+  const int t = threadIdx.x, lane = t & (SNK_WAVE - 1), wv = t / SNK_WAVE;
+  const int64_t KW = K >> 5;
+  const int64_t cw = blockIdx.x / FC_SPLIT;
+  const int cb = (int)(blockIdx.x % FC_SPLIT) * FC_CPB;  // first column within the word
+  const int64_t ca = cw * 32 + cb;
+  const uint32_t lowmask = (1u << cb) - 1u;
+  // this workgroup's share of the rows, [row_lo, row_hi]: the start words
+  // of its first FC_THREADS go out with the staging loads, and so do the row
+  // emitter's terms (two per thread here; indices clamped in range)
+  const int64_t row_lo = (int64_t)blockIdx.x * rpb;
+  const int64_t row_hi = std::min<int64_t>(row_lo + rpb - 1, M);
+  const int64_t s_row = row_lo + t;
+  const int64_t sr0 = s_row < M ? s_row : M - 1, sr1 = s_row + 1 < M ? s_row + 1 : M - 1;
+  const int32_t ra = (int32_t)FP[fp_tile_index(sr0, 0, KW)].y;
+  const int32_t rb_ = (int32_t)FP[fp_tile_index(sr1, 0, KW)].y;
+  const int32_t rsa = rs_blk[t < nb ? t : 0];
+  const int32_t rsb = rs_blk[t + FC_THREADS < nb ? t + FC_THREADS : 0];
+  // stage column word cw of every row; each thread's share of the base
+  int64_t part = 0;
+  for (int64_t r0 = t; r0 < M; r0 += (int64_t)FC_LOAD * FC_THREADS) {
+    uint2 x[FC_LOAD];
+#pragma unroll
+    for (int u = 0; u < FC_LOAD; ++u) {
+      const int64_t r = r0 + (int64_t)u * FC_THREADS;
+      x[u] = FP[fp_tile_index(r < M ? r : M - 1, cw, KW)];
+    }
+#pragma unroll
+    for (int u = 0; u < FC_LOAD; ++u) {
+      const int64_t r = r0 + (int64_t)u * FC_THREADS;
+      if (r < M) {
+        sF[r] = x[u].x;
+        sP[r] = (int32_t)x[u].y;
+        part += (int64_t)x[u].y + __popc(x[u].x & lowmask);
+      }
+    }
+  }
+  // minus this thread's share of the row starts' sum
+  part -= (t < nb ? rsa : 0) + (t + FC_THREADS < nb ? rsb : 0);
+  for (int64_t i = t + 2 * FC_THREADS; i < nb; i += FC_THREADS) part -= rs_blk[i];
+  if (bm_failed(st)) return;  // uniform over the grid
+  __syncthreads();
+  // 64-row ballots of each column's bits: wave wv takes chunks wv, wv + 8, ..
+  for (int h = wv; h < nch; h += FC_THREADS / SNK_WAVE) {
+    const int r = h * SNK_WAVE + lane;
+    const uint32_t fr = r < M ? sF[r] : 0u;
+    uint64_t mine_m = 0;  // lane j keeps column j's mask
+#pragma unroll
+    for (int j = 0; j < FC_CPB; ++j) {
+      const uint64_t m = __ballot((fr >> (cb + j)) & 1u);
+      mine_m = lane == j ? m : mine_m;
+    }
+    if (lane < FC_CPB) sm[lane * nch + h] = mine_m;
+  }
+  __syncthreads();
+  // (column, chunk) items in column-major order, ipt (<= FC_IPT) consecutive
+  // ones per thread: one block scan of their counts, the base reduced with it
+  // (as its low 16 bits and the rest: both sums fit 32 bits)
+  const int nit = FC_CPB * nch;
+  const int ipt = (nit + FC_THREADS - 1) / FC_THREADS;
+  const int it0 = t * ipt;
+  int32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < FC_IPT; ++k) {
+    const int it = it0 + k;
+    if (k < ipt && it < nit) mine += __popcll(sm[it]);
+  }
+  int32_t ex1[1], tt1[1], sm1[2];
+  {
+    const int32_t xs[1] = {mine};
+    const int32_t ys[2] = {(int32_t)(part & 0xFFFF), (int32_t)(part >> 16)};
+    block_scan_sum<FC_THREADS, 1, 2>(xs, ys, lds, ex1, tt1, sm1);
+  }
+  const int64_t base = (int64_t)sm1[0] + ((int64_t)sm1[1] << 16);
+  const int32_t tot = tt1[0];
+  int64_t q = base + ex1[0];
+#pragma unroll
+  for (int k = 0; k < FC_IPT; ++k) {
+    const int it = it0 + k;
+    if (k >= ipt || it >= nit) break;
+    const int j = it / nch, h = it - j * nch;
+    if (h == 0) {  // the column's first entry
+      f.col_ptr[ca + j] = (int32_t)q;
+      cstart[j] = (int32_t)q;
+    }
+    const uint32_t below = (1u << (cb + j)) - 1u;
+    uint64_t m = sm[it];
+    // the item's entries (rows ascending), four value gathers in flight
+    while (m) {
+      int rr[4];
+      int32_t pos[4];
+      T v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        rr[u] = m ? h * SNK_WAVE + (__ffsll((long long)m) - 1) : -1;
+        m &= m - 1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pos[u] = rr[u] >= 0 ? sP[rr[u]] + __popc(sF[rr[u]] & below) : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = vals[pos[u] < nnz ? pos[u] : 0];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rr[u] < 0) break;
+        if (q < nnz) {
+          f.row_t[q] = rr[u];
+          f.perm[q] = pos[u];
+          if (vals_t) vals_t[q] = v[u];
+        }
+        ++q;
+      }
+    }
+  }
+  __syncthreads();  // publishes cstart
+  bool any = false;
+  if (t < FC_CPB) {
+    const int64_t c = ca + t;
+    const int64_t a = cstart[t];
+    const int64_t b = t + 1 < FC_CPB ? (int64_t)cstart[t + 1] : base + tot;
+    any = tile_cuts(c, a, b, nnz, f.T_col, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
+    if (c == K - 1) {
+      f.col_ptr[K] = (int32_t)nnz;
+      tile_close(K, nnz, f.P_col, f.cpart_seg, f.cpart_nz, f.ccut);
+    }
+  }
+  if (__ballot(any) != 0 && lane == 0) store_result(&res[3], 1);
+  bool any_r = false;
+  for (int64_t sr = s_row; sr <= row_hi; sr += FC_THREADS) {
+    if (sr < M) {
+      const bool first = sr == s_row;  // its start words were loaded up front
+      const int32_t a = first ? ra : (int32_t)FP[fp_tile_index(sr, 0, KW)].y;
+      const int64_t b = sr + 1 < M ? (int64_t)(first ? rb_ : (int32_t)FP[fp_tile_index(sr + 1, 0, KW)].y)
+                                   : nnz;
+      f.row_ptr[sr] = a;
+      any_r |= tile_cuts(sr, a, b, nnz, f.T_row, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
+    } else {
+      f.row_ptr[M] = (int32_t)nnz;
+      tile_close(M, nnz, f.P_row, f.rpart_seg, f.rpart_nz, f.rcut);
+    }
+  }
+  if (__ballot(any_r) != 0 && lane == 0) store_result(&res[2], 1);
+}
+
 // Column tiles, thread per column s in [0, K] (shapes whose columns straddle
 // the emitter's word blocks); a block with a split column sets res[3].
 __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int32_t K,
@@ -1370,7 +1568,7 @@ __global__ __launch_bounds__(FP_THREADS) void k_fp_cols(const bm_state* st, int3
 // ------------------------------------------------------------------ host
 struct bm_layout {
   int64_t nblk, W, nb, NT, nbt, rb, cbk;
-  size_t res, state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff;
+  size_t res, state, cnt_eq, base_eq, sup, dropb, grown, vals, bsum, boff, rs;
   size_t fp, ft, tsum, toff, total;  // fused prepare
   int64_t nreg, rwg;                  // regions and bucketing workgroups (0: chunk 0 atomic)
   size_t cand, tab;
@@ -1397,6 +1595,7 @@ bm_layout make_layout(int32_t M, int32_t K, int64_t nnz) {
   L.vals = take(4 * (size_t)std::max<int64_t>(nnz, 1));
   L.bsum = take(16 * (size_t)L.nb);
   L.boff = take(16 * (size_t)L.nb);
+  L.rs = take(4 * (size_t)L.nb);
   L.NT = (int64_t)K * cdiv(M, 32);
   L.nbt = std::max<int64_t>(1, cdiv(L.NT, WT));
   L.rb = cdiv((int64_t)M + 1, FP_THREADS);
@@ -1464,8 +1663,11 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (results_begin(rw, 4, s) != hipSuccess) return SNACK_E_HIP;
   uint2* FP = fuse ? (uint2*)(ws + L.fp) : nullptr;
 
-  int32_t* tsum_zero = fuse ? (int32_t*)(ws + L.tsum) : nullptr;
-  const int64_t nzero = fuse ? 4 * L.nbt : 0;
+  // the column emitter when its rows fit in LDS (then no transposed bitmap
+  // and no transpose block sums to clear)
+  const bool colemit = fuse && M <= FC_MAX_M;
+  int32_t* tsum_zero = fuse && !colemit ? (int32_t*)(ws + L.tsum) : nullptr;
+  const int64_t nzero = fuse && !colemit ? 4 * L.nbt : 0;
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(std::max<int64_t>(4 * HREPL * 256, nzero), 256)),
                      dim3(256), 0, s, st, tsum_zero, nzero);
   const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
@@ -1521,17 +1723,27 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
                      bsum);
   const bool own_base = L.nb <= PREFIX_INBLOCK_MAX;
   if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
+  // the column emitter (a few columns per workgroup, their column word of
+  // every row staged in LDS) when the rows fit; else transpose + emit
+  const int32_t fp_tiled = colemit ? 1 : 0;
+  int32_t* rs_blk = (int32_t*)(ws + L.rs);
   if (dropped_lin || grown_lin)
     hipLaunchKernelGGL((k_bi_emit<T, true>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
                        grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
-                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
-                       col, vals, dropped_lin, grown_lin);
+                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP,
+                       fp_tiled, rs_blk, row, col, vals, dropped_lin, grown_lin);
   else
     hipLaunchKernelGGL((k_bi_emit<T, false>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
                        grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
-                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP, row,
-                       col, vals, nullptr, nullptr);
-  if (fuse) {
+                       (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP,
+                       fp_tiled, rs_blk, row, col, vals, nullptr, nullptr);
+  if (colemit) {
+    const int64_t nblk = (int64_t)(K / 32) * FC_SPLIT;
+    const int32_t rpb = (int32_t)cdiv((int64_t)M + 1, nblk);
+    hipLaunchKernelGGL(k_fp_colemit<T>, dim3((unsigned)nblk), dim3(FC_THREADS),
+                       (unsigned)fc_lds_bytes(M), s, st, FP, rs_blk, L.nb, M, K, nnz, *fuse,
+                       rpb, res_dev, (const T*)vals, vals_t);
+  } else if (fuse) {
     uint32_t* FT = (uint32_t*)(ws + L.ft);
     int4* tsum = (int4*)(ws + L.tsum);
     int4* toff = (int4*)(ws + L.toff);
