@@ -1424,42 +1424,44 @@ __global__ __launch_bounds__(FC_THREADS) void k_fp_colemit(
   const int32_t rb_ = (int32_t)FP[fp_tile_index(sr1, 0, KW)].y;
   const int32_t rsa = rs_blk[t < nb ? t : 0];
   const int32_t rsb = rs_blk[t + FC_THREADS < nb ? t + FC_THREADS : 0];
-  // stage column word cw of every row; each thread's share of the base
+  // stage column word cw of every row (a wave's lanes hold 64 consecutive
+  // rows, so the 64-row ballots of the columns' bits are taken on the loaded
+  // words); each thread's share of the base.  Tile indices in 32 bits (the
+  // whole FP array fits: M * K/32 < 2^31 words).
   int64_t part = 0;
-  for (int64_t r0 = t; r0 < M; r0 += (int64_t)FC_LOAD * FC_THREADS) {
+  const uint32_t tile_stride = 16u * (uint32_t)KW, cw16 = 16u * (uint32_t)cw;
+  for (int r0 = t; r0 - lane < M; r0 += FC_LOAD * FC_THREADS) {
     uint2 x[FC_LOAD];
 #pragma unroll
     for (int u = 0; u < FC_LOAD; ++u) {
-      const int64_t r = r0 + (int64_t)u * FC_THREADS;
-      x[u] = FP[fp_tile_index(r < M ? r : M - 1, cw, KW)];
+      const int r = r0 + u * FC_THREADS;
+      const uint32_t rr = (uint32_t)(r < M ? r : M - 1);
+      x[u] = FP[(rr >> 4) * tile_stride + cw16 + (rr & 15u)];
     }
 #pragma unroll
     for (int u = 0; u < FC_LOAD; ++u) {
-      const int64_t r = r0 + (int64_t)u * FC_THREADS;
+      const int r = r0 + u * FC_THREADS;
+      const int h = (r - lane) / SNK_WAVE;  // the wave's chunk (uniform)
+      if (h >= nch) break;
+      const uint32_t fr = r < M ? x[u].x : 0u;
       if (r < M) {
-        sF[r] = x[u].x;
+        sF[r] = fr;
         sP[r] = (int32_t)x[u].y;
-        part += (int64_t)x[u].y + __popc(x[u].x & lowmask);
+        part += (int64_t)x[u].y + __popc(fr & lowmask);
       }
+      uint64_t mine_m = 0;  // lane j keeps column j's mask
+#pragma unroll
+      for (int j = 0; j < FC_CPB; ++j) {
+        const uint64_t m = __ballot((fr >> (cb + j)) & 1u);
+        mine_m = lane == j ? m : mine_m;
+      }
+      if (lane < FC_CPB) sm[lane * nch + h] = mine_m;
     }
   }
   // minus this thread's share of the row starts' sum
   part -= (t < nb ? rsa : 0) + (t + FC_THREADS < nb ? rsb : 0);
   for (int64_t i = t + 2 * FC_THREADS; i < nb; i += FC_THREADS) part -= rs_blk[i];
   if (bm_failed(st)) return;  // uniform over the grid
-  __syncthreads();
-  // 64-row ballots of each column's bits: wave wv takes chunks wv, wv + 8, ..
-  for (int h = wv; h < nch; h += FC_THREADS / SNK_WAVE) {
-    const int r = h * SNK_WAVE + lane;
-    const uint32_t fr = r < M ? sF[r] : 0u;
-    uint64_t mine_m = 0;  // lane j keeps column j's mask
-#pragma unroll
-    for (int j = 0; j < FC_CPB; ++j) {
-      const uint64_t m = __ballot((fr >> (cb + j)) & 1u);
-      mine_m = lane == j ? m : mine_m;
-    }
-    if (lane < FC_CPB) sm[lane * nch + h] = mine_m;
-  }
   __syncthreads();
   // (column, chunk) items in column-major order, ipt (<= FC_IPT) consecutive
   // ones per thread: one block scan of their counts, the base reduced with it
@@ -1665,7 +1667,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
 
   // the column emitter when its rows fit in LDS (then no transposed bitmap
   // and no transpose block sums to clear)
-  const bool colemit = fuse && M <= FC_MAX_M;
+  const bool colemit = fuse && M <= FC_MAX_M && (int64_t)M * (K / 32) < ((int64_t)1 << 31);
   int32_t* tsum_zero = fuse && !colemit ? (int32_t*)(ws + L.tsum) : nullptr;
   const int64_t nzero = fuse && !colemit ? 4 * L.nbt : 0;
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(std::max<int64_t>(4 * HREPL * 256, nzero), 256)),
