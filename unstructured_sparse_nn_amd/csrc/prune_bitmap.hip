@@ -104,6 +104,52 @@ __device__ __forceinline__ int64_t lin_of(int32_t r, int32_t c, int32_t M, int32
   return (r < 0 || r >= M || c < 0 || c >= K) ? -1 : (int64_t)r * K + c;
 }
 
+// Exclusive block scans of NS values (ex, with block totals tot) and block
+// sums of NR more, behind one barrier: each wave's scan totals and sums go
+// through LDS together.  lds: NT/64 * (NS + NR) ints, left as written (the
+// caller does not reuse it).  Call from all threads.
+template <int NT, int NS, int NR>
+__device__ __forceinline__ void block_scan_sum(const int32_t (&x)[NS], const int32_t (&y)[NR],
+                                               int32_t* lds, int32_t (&ex)[NS],
+                                               int32_t (&tot)[NS], int32_t (&sum)[NR]) {
+  constexpr int NW = NT / SNK_WAVE, NV = NS + NR;
+  const int w = threadIdx.x / SNK_WAVE;
+  int32_t inc[NS], ys[NR];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) inc[k] = wave_incl_scan_i32(x[k]);
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    ys[k] = y[k];
+    for (int off = 32; off > 0; off >>= 1) ys[k] += __shfl_xor(ys[k], off, SNK_WAVE);
+  }
+  if (lane_id() == SNK_WAVE - 1) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) lds[w * NV + k] = inc[k];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) lds[w * NV + NS + k] = ys[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    int32_t b = 0, t = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int32_t v = lds[i * NV + k];
+      if (i < w) b += v;
+      t += v;
+    }
+    ex[k] = b + inc[k] - x[k];
+    tot[k] = t;
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    int32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += lds[i * NV + NS + k];
+    sum[k] = t;
+  }
+}
+
 // Also zeroes zero[0 .. nzero) (the transposed bitmap's block sums of a fused
 // prepare, which the transposer adds into).
 __global__ __launch_bounds__(256) void k_bi_init(bm_state* st, int32_t* __restrict__ zero,
@@ -226,16 +272,19 @@ __device__ void regrow_chunk(bm_state* st, int c, uint64_t stream, uint64_t MK, 
   }
 }
 
-// One workgroup: chunks after grid chunk c-1 until nothing is missing (or
-// the stream bound).  Records the positions still missing.  Any block size
-// up to 1024.
+// One workgroup (NT threads): chunks after grid chunk c-1 until nothing is
+// missing (or the stream bound).  Records the positions still missing.
+// (A first round over a window of draws deduplicated in an LDS hash and
+// ranked in stream order by one block scan measured no faster: the window's
+// draws, loads and probes cost as much as the rounds it saves.)
 constexpr int FT = 1024;
 constexpr int FINISH_ROUNDS = 4096;
+template <int NT>
 __device__ void regrow_tail(int32_t c, uint64_t stream, uint64_t MK, int32_t n_drop,
                             bm_state* st, const uint32_t* __restrict__ sup,
                             uint32_t* __restrict__ grown) {
-  __shared__ int32_t red[1024 / SNK_WAVE];
-  const int t = threadIdx.x, nt = blockDim.x;
+  __shared__ int32_t red[NT / SNK_WAVE];
+  const int t = threadIdx.x, nt = NT;
   int64_t start = 0;
   int32_t rem = n_drop;
   if (c > 0) {
@@ -275,7 +324,7 @@ __device__ void regrow_tail(int32_t c, uint64_t stream, uint64_t MK, int32_t n_d
 // test-and-set over the grid.
 constexpr int RB_SHIFT = 16;                      // positions per region: 2^16
 constexpr int RB_WORDS = 1 << (RB_SHIFT - 5);     // bitmap words per region
-constexpr int RB_PER = 16;                        // candidates per bucketing thread
+constexpr int RB_PER = 8;                         // candidates per bucketing thread
 constexpr int RB_CH = RB_PER * BT;                // stream indices per bucketing workgroup
 constexpr int RB_MAXREG = 1024;                   // regions at most
 constexpr int RB_MAXWG = 1024;                    // bucketing workgroups at most
@@ -444,25 +493,35 @@ __device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t n
 // block 0 or an invalid entry) and of the next NEXT entries past the block
 // (-1 past nnz or invalid), with their magnitudes if mag is given.  A
 // bitmap word holds 32 positions, so at most 32 later entries can share the
-// block's last word.  Readers wait for the block's next barrier.
+// block's last word.  edge_load issues the loads; edge_store, called once
+// the caller's other loads are out, fills LDS; readers wait for the
+// block's next barrier.
 constexpr int NEXT = 32;
 template <typename T>
-__device__ __forceinline__ void stage_edges(const int32_t* __restrict__ row,
-                                            const int32_t* __restrict__ col,
-                                            const T* __restrict__ vals, int64_t nnz, int32_t M,
-                                            int32_t K, int64_t base, int n, int64_t* edge,
-                                            int64_t* nxt, uint32_t* mag) {
-  const int t = threadIdx.x;
+struct edge_vals {
+  int32_t er, ec, nr, nc;
+  T nv;
+};
+template <typename T>
+__device__ __forceinline__ edge_vals<T> edge_load(const int32_t* __restrict__ row,
+                                                  const int32_t* __restrict__ col,
+                                                  const T* __restrict__ vals, int64_t nnz,
+                                                  int64_t base, int n) {
   const int64_t eb = base > 0 ? base - 1 : 0;
-  const int64_t k = base + n + (t & (NEXT - 1));
+  const int64_t k = base + n + (threadIdx.x & (NEXT - 1));
   const int64_t kk = k < nnz ? k : nnz - 1;
-  const int32_t er = row[eb], ec = col[eb], nr = row[kk], nc = col[kk];
-  uint32_t nm = 0;
-  if (mag) nm = magnitude<T>(raw_bits(vals[kk]));
-  if (t == BT - 1) *edge = base > 0 ? lin_of(er, ec, M, K) : -1;
+  return edge_vals<T>{row[eb], col[eb], row[kk], col[kk], vals[kk]};
+}
+template <typename T>
+__device__ __forceinline__ void edge_store(const edge_vals<T>& e, int64_t nnz, int32_t M,
+                                           int32_t K, int64_t base, int n, int64_t* edge,
+                                           int64_t* nxt, uint32_t* mag) {
+  const int t = threadIdx.x;
+  const int64_t k = base + n + (t & (NEXT - 1));
+  if (t == BT - 1) *edge = base > 0 ? lin_of(e.er, e.ec, M, K) : -1;
   if (t < NEXT) {
-    nxt[t] = k < nnz ? lin_of(nr, nc, M, K) : -1;
-    if (mag) mag[t] = nm;
+    nxt[t] = k < nnz ? lin_of(e.nr, e.nc, M, K) : -1;
+    if (mag) mag[t] = magnitude<T>(raw_bits(e.nv));
   }
 }
 
@@ -557,7 +616,8 @@ __global__ __launch_bounds__(BT) void k_bi_build(
       v4[j] = ok ? vals[k0 + j] : (T)0;
     }
   }
-  stage_edges<T>(row, col, vals, nnz, M, K, base, n, &edge_s, nxt, nullptr);
+  const edge_vals<T> ev = edge_load<T>(row, col, vals, nnz, base, n);
+  edge_store<T>(ev, nnz, M, K, base, n, &edge_s, nxt, nullptr);
   __syncthreads();  // h zeroed before any wave adds to it
   int err = 0;
   int64_t l[4];
@@ -704,28 +764,6 @@ __global__ __launch_bounds__(1024) void k_bi_eq_scan(const int32_t* __restrict__
   }
 }
 
-// Sum of v[0..n) over the block (all threads get it); four loads per thread
-// in flight per round.
-__device__ __forceinline__ int32_t block_sum_prefix(const int32_t* __restrict__ v, int64_t n) {
-  __shared__ int32_t lds[32];
-  int32_t s = 0;
-  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 4 * (int64_t)blockDim.x) {
-    int32_t x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * (int64_t)blockDim.x;
-      x[u] = i < n ? v[i] : 0;
-    }
-    s += (x[0] + x[1]) + (x[2] + x[3]);
-  }
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, SNK_WAVE);
-  if (lane_id() == 0) lds[threadIdx.x / SNK_WAVE] = s;
-  __syncthreads();
-  int32_t tot = 0;
-  for (int i = 0; i < (int)(blockDim.x / SNK_WAVE); ++i) tot += lds[i];
-  __syncthreads();
-  return tot;
-}
 
 // Dropped bitmap D: entry k is dropped if its magnitude is below tau, or at
 // tau with tie rank (index order) below need.  The first gridDim.x - nblk
@@ -739,7 +777,7 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
     const int32_t* __restrict__ base_eq, int32_t n_drop, int32_t c, uint64_t stream, uint64_t MK,
     bm_state* st, uint32_t* __restrict__ dropb, const uint32_t* __restrict__ sup,
     uint32_t* __restrict__ grown, int32_t tail) {
-  __shared__ int32_t lds[BT / SNK_WAVE];
+  __shared__ int32_t lds[BT / SNK_WAVE * 2];
   __shared__ uint32_t buf[CAP];
   __shared__ int64_t edge_s, whi_s;
   __shared__ int64_t nxt[NEXT];
@@ -747,39 +785,68 @@ __global__ __launch_bounds__(BT) void k_bi_drop(
   const int64_t nx = (int64_t)gridDim.x - nblk;
   if ((int64_t)blockIdx.x < nx) {
     if (tail)  // one workgroup: chunk c and every later one (no finisher launch)
-      regrow_tail(c, stream, MK, n_drop, st, sup, grown);
+      regrow_tail<BT>(c, stream, MK, n_drop, st, sup, grown);
     else
       regrow_chunk(st, c, stream, MK, n_drop, sup, grown, blockIdx.x, nx);
     return;
   }
   const int64_t bid = (int64_t)blockIdx.x - nx;
   const int t = threadIdx.x;
-  const uint32_t tau = st->pfx[last_pass];
-  const int32_t need = st->need[last_pass];
   const int64_t base = bid * BE;
   const int n = (int)std::min<int64_t>(BE, nnz - base);
   const int64_t k0 = base + 4 * t;
+  // every load first (clamped indices): the block's entries, its edge
+  // entries, its share of the tie counts of earlier blocks (four per thread
+  // here) and the threshold state
+  int32_t r4[4], c4[4];
+  T v4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t kk = k0 + j < nnz ? k0 + j : nnz - 1;
+    v4[j] = vals[kk];
+    r4[j] = row[kk];
+    c4[j] = col[kk];
+  }
+  const edge_vals<T> ev = edge_load<T>(row, col, vals, nnz, base, n);
+  int32_t pe[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = t + (int64_t)u * BT;
+    pe[u] = base_eq ? 0 : cnt_eq[i < bid ? i : 0];
+  }
+  const int32_t e_pre = base_eq ? base_eq[bid] : 0;
+  const uint32_t tau = st->pfx[last_pass];
+  const int32_t need = st->need[last_pass];
   uint32_t a[4];
   int64_t l[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bool ok = k0 + j < nnz;
-    const int64_t kk = ok ? k0 + j : nnz - 1;
-    const uint32_t m = magnitude<T>(raw_bits(vals[kk]));
-    const int32_t r = row[kk], cc = col[kk];
-    a[j] = ok ? m : 0xFFFFFFFFu;
-    l[j] = ok ? lin_of(r, cc, M, K) : -1;
+    a[j] = ok ? magnitude<T>(raw_bits(v4[j])) : 0xFFFFFFFFu;
+    l[j] = ok ? lin_of(r4[j], c4[j], M, K) : -1;
   }
-  stage_edges<T>(row, col, vals, nnz, M, K, base, n, &edge_s, nxt, nxt_mag);
+  edge_store<T>(ev, nnz, M, K, base, n, &edge_s, nxt, nxt_mag);
   last_word(l, n, &whi_s);
-  const int32_t E = base_eq ? base_eq[bid] : block_sum_prefix(cnt_eq, bid);
-  // tie ranks in index order (a block scan; its barriers also publish the
-  // staged edges)
+  int32_t part = 0;
+  if (!base_eq) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) part += t + (int64_t)u * BT < bid ? pe[u] : 0;
+    for (int64_t i = t + 4 * (int64_t)BT; i < bid; i += BT) part += cnt_eq[i];
+  }
+  // tie ranks in index order and the entries at tau before the block, in
+  // one block scan (its barrier also publishes the staged edges)
   int32_t eq = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) eq += a[j] == tau ? 1 : 0;
-  int32_t tot;
-  int32_t er = E + block_excl_scan_i32<BT>(eq, lds, &tot);
+  int32_t ex1[1], tt1[1], sm1[1];
+  {
+    const int32_t xs[1] = {eq};
+    const int32_t ys[1] = {part};
+    block_scan_sum<BT, 1, 1>(xs, ys, lds, ex1, tt1, sm1);
+  }
+  const int32_t E = base_eq ? e_pre : sm1[0];
+  const int32_t tot = tt1[0];
+  int32_t er = E + ex1[0];
   const int32_t run = E + tot;
   bool f[4];
 #pragma unroll
@@ -818,7 +885,7 @@ __global__ __launch_bounds__(FT) void k_bi_finish(int32_t c, uint64_t stream, ui
                                                   int32_t n_drop, bm_state* st,
                                                   const uint32_t* __restrict__ sup,
                                                   uint32_t* __restrict__ grown) {
-  regrow_tail(c, stream, MK, n_drop, st, sup, grown);
+  regrow_tail<FT>(c, stream, MK, n_drop, st, sup, grown);
 }
 
 __device__ __forceinline__ int4 word_counts(uint32_t S, uint32_t D, uint32_t G) {
@@ -827,52 +894,6 @@ __device__ __forceinline__ int4 word_counts(uint32_t S, uint32_t D, uint32_t G) 
 
 __device__ __forceinline__ int4 add4(int4 a, int4 b) {
   return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// Exclusive block scans of NS values (ex, with block totals tot) and block
-// sums of NR more, behind one barrier: each wave's scan totals and sums go
-// through LDS together.  lds: NT/64 * (NS + NR) ints, left as written (the
-// caller does not reuse it).  Call from all threads.
-template <int NT, int NS, int NR>
-__device__ __forceinline__ void block_scan_sum(const int32_t (&x)[NS], const int32_t (&y)[NR],
-                                               int32_t* lds, int32_t (&ex)[NS],
-                                               int32_t (&tot)[NS], int32_t (&sum)[NR]) {
-  constexpr int NW = NT / SNK_WAVE, NV = NS + NR;
-  const int w = threadIdx.x / SNK_WAVE;
-  int32_t inc[NS], ys[NR];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) inc[k] = wave_incl_scan_i32(x[k]);
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    ys[k] = y[k];
-    for (int off = 32; off > 0; off >>= 1) ys[k] += __shfl_xor(ys[k], off, SNK_WAVE);
-  }
-  if (lane_id() == SNK_WAVE - 1) {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) lds[w * NV + k] = inc[k];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) lds[w * NV + NS + k] = ys[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    int32_t b = 0, t = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const int32_t v = lds[i * NV + k];
-      if (i < w) b += v;
-      t += v;
-    }
-    ex[k] = b + inc[k] - x[k];
-    tot[k] = t;
-  }
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    int32_t t = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) t += lds[i * NV + NS + k];
-    sum[k] = t;
-  }
 }
 
 // Per block of WT words: popcounts of (new support, old support, dropped,
