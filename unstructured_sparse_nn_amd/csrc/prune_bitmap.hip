@@ -65,8 +65,8 @@ constexpr int WT = 512;                   // threads (= bitmap words) per write 
 // Entries per emitter block listed in LDS (one per thread per round): density
 // up to 1/4 over a block of WT words; a denser block takes one thread per word.
 constexpr int EMIT_CAP = 4096;
-// Set bits a thread of the one-thread-per-word emission (blocks denser than
-// EMIT_CAP) takes per batch, their gathers in flight together.
+// Set bits per batch, their gathers in flight together, that a thread of the
+// transposed-bitmap column emitter takes beyond its first few.
 constexpr int EMIT_BATCH = 4;
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int FC_MAX_M = 12288;           // rows the column emitter stages in LDS
