@@ -654,6 +654,10 @@ PREPARED_CASES = [
     # 8192 x 8448 at 2.9%: past 2^26 positions, so regrow chunk 0 takes the
     # grid-wide atomic path instead of the per-region buckets
     ("wide_grid", "bf16", 300000, 5, 3, 0),
+    # 4096 x 4096 at 10%: 503,316 draws in chunk 0, more bucketing slices
+    # than half the region workgroup's threads, so the region pass maps its
+    # candidates by scan and search (at 5% each slice gets two threads)
+    ("square_0.9_many_slices", "bf16", 300000, 10, 1, 0),
     # without the dropped and grown lists (the emitter instance the training
     # step runs)
     ("square_0.95_32_nolists", "bf16", 300000, 3, 2, 0),
@@ -677,6 +681,8 @@ def test_prune_regrow_prepared(orc, prune_plan, name, dt, ppm, seed, step, tile)
         w = synth.random_case(12, 512, 512, 512 * 512 // 4, 1, dt).weights[0]
     elif name == "wide_grid":
         w = synth.random_case(12, 8192, 8448, 2000000, 1, dt).weights[0]
+    elif name == "square_0.9_many_slices":
+        w = synth.random_case(15, 4096, 4096, 4096 * 4096 // 10, 1, dt).weights[0]
     elif name == "rows_at_max":
         w = synth.random_case(13, 12288, 96, 12288 * 96 // 20, 1, dt).weights[0]
     elif name.startswith("rows_past_max"):

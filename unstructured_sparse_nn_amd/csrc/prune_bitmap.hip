@@ -404,71 +404,112 @@ __device__ void region_chunk0(int32_t g, bm_state* st, int32_t n_drop, int32_t n
     const int64_t w = wbase + k * BT + t;
     sw[k] = sup[w < W ? w : W - 1];
   }
+  // slice table: with slices of >= 2 threads, the thread's own slice's run
+  // bounds in a[0], a[1]; else WPTH slices per thread for the scan below
   int32_t a[WPTH], len[WPTH], sum = 0;
+  if (2 * nwg <= BT) {
+    const int sl = t / (BT / nwg);
+    const int64_t ti = (int64_t)(sl < nwg ? sl : nwg - 1) * (nreg + 1) + g;
+    a[0] = tab[ti];
+    a[1] = tab[ti + 1];
+  } else {
 #pragma unroll
-  for (int k = 0; k < WPTH; ++k) {
-    const int wgi = t * WPTH + k;
-    const int64_t ti = (int64_t)(wgi < nwg ? wgi : nwg - 1) * (nreg + 1) + g;
-    a[k] = tab[ti];
-    len[k] = tab[ti + 1];
+    for (int k = 0; k < WPTH; ++k) {
+      const int wgi = t * WPTH + k;
+      const int64_t ti = (int64_t)(wgi < nwg ? wgi : nwg - 1) * (nreg + 1) + g;
+      a[k] = tab[ti];
+      len[k] = tab[ti + 1];
+    }
   }
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     Ss[k * BT + t] = wbase + k * BT + t < W ? sw[k] : 0xFFFFFFFFu;
     Gs[k * BT + t] = 0u;
   }
-#pragma unroll
-  for (int k = 0; k < WPTH; ++k) {
-    const bool in = t * WPTH + k < nwg;
-    len[k] = in ? len[k] - a[k] : 0;
-    a[k] = in ? a[k] : 0;
-    sum += len[k];
-  }
-  int32_t n_g;
-  int32_t ex = block_excl_scan_i32<BT>(sum, lds, &n_g);
-#pragma unroll
-  for (int k = 0; k < WPTH; ++k) {
-    const int wgi = t * WPTH + k;
-    if (wgi < nwg) {
-      run0[wgi] = ex;
-      start[wgi] = wgi * RB_CH + a[k];
-    }
-    ex += len[k];
-  }
-  __syncthreads();
-  int top = 1;  // the largest power of two below nwg (1 if nwg <= 2)
-  while (2 * top < nwg) top *= 2;
   int32_t taken = 0;
-  for (int32_t b0 = 0; b0 < n_g; b0 += 4 * BT) {
+  // take candidate pc (a region position) if outside S and new in G
+  auto take = [&](uint32_t pc) {
+    const uint32_t loc = pc & ((1u << RB_SHIFT) - 1u);
+    const uint32_t bit = 1u << (loc & 31);
+    if (Ss[loc >> 5] & bit) return;
+    if (!(atomicOr(&Gs[loc >> 5], bit) & bit)) ++taken;
+  };
+  if (2 * nwg <= BT) {  // block-uniform: each slice's run split over tps threads
+    const int tps = BT / nwg;
+    const int sl = t / tps, sub = t - sl * tps;
+    const bool mine = sl < nwg;
+    const int32_t ln = mine ? a[1] - a[0] : 0;  // (a[0], a[1]): the slice's run bounds
+    const int64_t cb = (int64_t)(mine ? sl : 0) * RB_CH + a[0];
+    // the first candidates' loads go out before the barrier that publishes
+    // Ss and Gs (an unused slot reads element 0, L1-resident; discarded)
     uint32_t pc[4];
-    bool ok[4];
-    int32_t e[4], lo[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      e[u] = b0 + u * BT + t;
-      ok[u] = e[u] < n_g;
-      lo[u] = 0;  // run0[0] = 0 <= e
+      const int32_t i = sub + u * tps;
+      pc[u] = cand[i < ln ? cb + i : 0];
     }
-    // the last slice whose run starts at or before e: a branch-free search
-    // with the four candidates' LDS reads of each step in flight together
-    for (int step = top; step > 0; step >>= 1) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int m = lo[u] + step;
-        if (m < nwg && run0[m] <= e[u]) lo[u] = m;
-      }
-    }
-    // an unused slot reads the first element (L1-resident; discarded)
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      pc[u] = cand[ok[u] ? start[lo[u]] + (e[u] - run0[lo[u]]) : 0];
+      if (sub + u * tps < ln) take(pc[u]);
+    for (int32_t i0 = sub + 4 * tps; i0 < ln; i0 += 4 * tps) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!ok[u]) continue;
-      const uint32_t loc = pc[u] & ((1u << RB_SHIFT) - 1u);
-      const uint32_t bit = 1u << (loc & 31);
-      if (Ss[loc >> 5] & bit) continue;
-      if (!(atomicOr(&Gs[loc >> 5], bit) & bit)) ++taken;
+      for (int u = 0; u < 4; ++u) {
+        const int32_t i = i0 + u * tps;
+        pc[u] = cand[i < ln ? cb + i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * tps < ln) take(pc[u]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < WPTH; ++k) {
+      const bool in = t * WPTH + k < nwg;
+      len[k] = in ? len[k] - a[k] : 0;
+      a[k] = in ? a[k] : 0;
+      sum += len[k];
+    }
+    int32_t n_g;
+    int32_t ex = block_excl_scan_i32<BT>(sum, lds, &n_g);
+#pragma unroll
+    for (int k = 0; k < WPTH; ++k) {
+      const int wgi = t * WPTH + k;
+      if (wgi < nwg) {
+        run0[wgi] = ex;
+        start[wgi] = wgi * RB_CH + a[k];
+      }
+      ex += len[k];
+    }
+    __syncthreads();
+    int top = 1;  // the largest power of two below nwg (1 if nwg <= 2)
+    while (2 * top < nwg) top *= 2;
+    for (int32_t b0 = 0; b0 < n_g; b0 += 4 * BT) {
+      uint32_t pc[4];
+      bool ok[4];
+      int32_t e[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        e[u] = b0 + u * BT + t;
+        ok[u] = e[u] < n_g;
+        lo[u] = 0;  // run0[0] = 0 <= e
+      }
+      // the last slice whose run starts at or before e: a branch-free search
+      // with the four candidates' LDS reads of each step in flight together
+      for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int m = lo[u] + step;
+          if (m < nwg && run0[m] <= e[u]) lo[u] = m;
+        }
+      }
+      // an unused slot reads the first element (L1-resident; discarded)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pc[u] = cand[ok[u] ? start[lo[u]] + (e[u] - run0[lo[u]]) : 0];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ok[u]) take(pc[u]);
     }
   }
   __syncthreads();
