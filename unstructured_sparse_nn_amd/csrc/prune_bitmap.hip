@@ -1511,10 +1511,11 @@ __global__ __launch_bounds__(FC_THREADS) void k_fp_colemit(
         sP[r] = (int32_t)x[u].y;
         part += (int64_t)x[u].y + __popc(fr & lowmask);
       }
-      uint64_t mine_m = 0;  // lane j keeps column j's mask
+      const uint32_t fb = fr >> cb;  // the workgroup's columns in the low bits
+      uint64_t mine_m = 0;           // lane j keeps column j's mask
 #pragma unroll
       for (int j = 0; j < FC_CPB; ++j) {
-        const uint64_t m = __ballot((fr >> (cb + j)) & 1u);
+        const uint64_t m = __ballot(fb & (1u << j));
         mine_m = lane == j ? m : mine_m;
       }
       if (lane < FC_CPB) sm[lane * nch + h] = mine_m;
