@@ -70,6 +70,8 @@ constexpr int EMIT_CAP = 4096;
 constexpr int EMIT_BATCH = 4;
 constexpr int64_t PREFIX_INBLOCK_MAX = 4096;  // blocks up to which a block sums its own prefix
 constexpr int FC_MAX_M = 12288;           // rows the column emitter stages in LDS
+constexpr uint64_t AGG_FLAG = 1ull << 62;  // a published block count
+constexpr int AGG_SPIN_MAX = 1 << 22;      // polls of one block count before giving up
 constexpr int64_t STREAM_BOUND = 1ll << 40;
 // Same-address device atomics serialise (~0.2 us each on gfx950), so blocks
 // are fat (few blocks) and their counters spread over replicas.
@@ -994,10 +996,12 @@ __global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
     const uint32_t* __restrict__ grown, int64_t W, const int4* __restrict__ bsum,
     const int4* __restrict__ boff, const T* __restrict__ vals_ws, int32_t K, int32_t small_grid,
     int64_t nnz, int64_t n_drop, const bm_state* st, int32_t* __restrict__ result,
-    uint2* __restrict__ FP, int32_t fp_tiled, int32_t* __restrict__ rs_blk, int32_t* __restrict__ row,
+    uint2* __restrict__ FP, int32_t fp_tiled, int32_t* __restrict__ rs_blk,
+    uint64_t* __restrict__ agg, int32_t* __restrict__ row,
     int32_t* __restrict__ col, T* __restrict__ vals, int64_t* __restrict__ dropped_lin,
     int64_t* __restrict__ grown_lin) {
   __shared__ int32_t lds[WT / SNK_WAVE * 7];
+  __shared__ int32_t red2[WT / SNK_WAVE][2];
   __shared__ uint32_t ent[EMIT_CAP];  // (word in block << 5) | bit, in output order
   __shared__ uint32_t sS[WT];
   __shared__ int32_t sq[WT], sr[WT], sc[WT];
@@ -1011,7 +1015,7 @@ __global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
   // (without the dropped and grown lists only the first two block counts
   // are needed)
   int4 p0 = make_int4(0, 0, 0, 0), p1 = make_int4(0, 0, 0, 0);
-  if (!boff && nb_before > 0) {
+  if (!boff && !agg && nb_before > 0) {
     if constexpr (LISTS) {
       p0 = bsum[t < nb_before ? t : 0];
       p1 = bsum[t + WT < nb_before ? t + WT : 0];
@@ -1033,7 +1037,7 @@ __global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
   // this thread's share of the block base (the sum of the sums of earlier
   // blocks); the block reduces it with the two scans below
   int4 part = make_int4(0, 0, 0, 0);
-  if (!boff) {
+  if (!boff && !agg) {
     if (t < nb_before) part = p0;
     if (t + WT < nb_before) part = add4(part, p1);
     for (int64_t i = t + 2 * WT; i < nb_before; i += 2 * WT) {  // two loads in flight
@@ -1083,6 +1087,47 @@ __global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
     fs = ex[0];
     nf = tt[0];
     rs_sum = sm[2];
+    if (agg) {
+      // no block-sum launch: publish this block's counts (new and old
+      // entries, 16 bits each under a flag), then add up those of the blocks
+      // before it, waiting for each to appear.  Blocks start in index order,
+      // so every block waited on is running or done; the wait is bounded
+      // all the same, and a timeout is an error.
+      if (t == 0)
+        __hip_atomic_store(&agg[blockIdx.x], AGG_FLAG | (uint32_t)tt[0], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      int32_t px = 0, py = 0;
+      bool late = false;
+      for (int64_t i = t; i < nb_before; i += WT) {
+        uint64_t v = __hip_atomic_load(&agg[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int spin = 0; !(v & AGG_FLAG); ++spin) {
+          if (spin >= AGG_SPIN_MAX) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          v = __hip_atomic_load(&agg[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        px += (int32_t)(v & 0xFFFFu);
+        py += (int32_t)((v >> 16) & 0xFFFFu);
+      }
+      if (late) atomicOr(const_cast<int32_t*>(&st->err), 16);
+      for (int off = 32; off > 0; off >>= 1) {
+        px += __shfl_xor(px, off, SNK_WAVE);
+        py += __shfl_xor(py, off, SNK_WAVE);
+      }
+      if (lane_id() == 0) {
+        red2[t / SNK_WAVE][0] = px;
+        red2[t / SNK_WAVE][1] = py;
+      }
+      __syncthreads();
+      bo = make_int4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < WT / SNK_WAVE; ++i) {
+        bo.x += red2[i][0];
+        bo.y += red2[i][1];
+      }
+    }
   }
   if (fp_tiled && t == 0) rs_blk[blockIdx.x] = rs_sum;
   // the block's new entries are [bo.x, bo.x + nblk_out); listed in LDS when
@@ -1524,7 +1569,11 @@ __global__ __launch_bounds__(FC_THREADS) void k_fp_colemit(
   // minus this thread's share of the row starts' sum
   part -= (t < nb ? rsa : 0) + (t + FC_THREADS < nb ? rsb : 0);
   for (int64_t i = t + 2 * FC_THREADS; i < nb; i += FC_THREADS) part -= rs_blk[i];
-  if (bm_failed(st)) return;  // uniform over the grid
+  if (bm_failed(st)) {  // uniform over the grid; an error raised after the
+    // row emitter reported the state (a late block count) is reported here
+    if (blockIdx.x == 0 && t == 0) store_result(&res[0], st->err);
+    return;
+  }
   __syncthreads();
   // (column, chunk) items in column-major order, ipt (<= FC_IPT) consecutive
   // ones per thread: one block scan of their counts, the base reduced with it
@@ -1731,8 +1780,13 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   // the column emitter when its rows fit in LDS (then no transposed bitmap
   // and no transpose block sums to clear)
   const bool colemit = fuse && M <= FC_MAX_M && (int64_t)M * (K / 32) < ((int64_t)1 << 31);
-  int32_t* tsum_zero = fuse && !colemit ? (int32_t*)(ws + L.tsum) : nullptr;
-  const int64_t nzero = fuse && !colemit ? 4 * L.nbt : 0;
+  // with the column emitter and no lists, the row emitter finds its block
+  // bases from the counts earlier blocks publish (no block-sum launch); the
+  // published counts, over the block-sum area, start cleared
+  const bool agg_path = colemit && !dropped_lin && !grown_lin && L.nb <= PREFIX_INBLOCK_MAX;
+  int32_t* tsum_zero = fuse && !colemit ? (int32_t*)(ws + L.tsum)
+                       : agg_path      ? (int32_t*)(ws + L.bsum) : nullptr;
+  const int64_t nzero = fuse && !colemit ? 4 * L.nbt : agg_path ? 2 * L.nb : 0;
   hipLaunchKernelGGL(k_bi_init, dim3((unsigned)cdiv(std::max<int64_t>(4 * HREPL * 256, nzero), 256)),
                      dim3(256), 0, s, st, tsum_zero, nzero);
   const int32_t vec_ok = ((uintptr_t)row % 16 == 0 && (uintptr_t)col % 16 == 0 &&
@@ -1784,10 +1838,12 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
       hipLaunchKernelGGL(k_bi_chunk, dim3(cb), dim3(BT), 0, s, c, stream, MK, nd, st, sup, grown);
     hipLaunchKernelGGL(k_bi_finish, dim3(1), dim3(FT), 0, s, c, stream, MK, nd, st, sup, grown);
   }
-  hipLaunchKernelGGL(k_bi_wsum, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
-                     bsum);
   const bool own_base = L.nb <= PREFIX_INBLOCK_MAX;
-  if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
+  if (!agg_path) {
+    hipLaunchKernelGGL(k_bi_wsum, dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb, grown, L.W,
+                       bsum);
+    if (!own_base) hipLaunchKernelGGL(k_bi_bscan, dim3(1), dim3(1024), 0, s, bsum, boff, L.nb);
+  }
   // the column emitter (a few columns per workgroup, their column word of
   // every row staged in LDS) when the rows fit; else transpose + emit
   const int32_t fp_tiled = colemit ? 1 : 0;
@@ -1796,12 +1852,13 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
     hipLaunchKernelGGL((k_bi_emit<T, true>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
                        grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
                        (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP,
-                       fp_tiled, rs_blk, row, col, vals, dropped_lin, grown_lin);
+                       fp_tiled, rs_blk, nullptr, row, col, vals, dropped_lin, grown_lin);
   else
     hipLaunchKernelGGL((k_bi_emit<T, false>), dim3((unsigned)L.nb), dim3(WT), 0, s, sup, dropb,
                        grown, L.W, bsum, own_base ? nullptr : boff, vals_ws, K,
                        (int32_t)(MK + 32 <= (1ull << 32)), nnz, n_drop, st, res_dev, FP,
-                       fp_tiled, rs_blk, row, col, vals, nullptr, nullptr);
+                       fp_tiled, rs_blk, agg_path ? (uint64_t*)(ws + L.bsum) : nullptr, row, col,
+                       vals, nullptr, nullptr);
   if (colemit) {
     const int64_t nblk = (int64_t)(K / 32) * FC_SPLIT;
     const int32_t rpb = (int32_t)cdiv((int64_t)M + 1, nblk);
@@ -1833,6 +1890,7 @@ snack_status run(int32_t* row, int32_t* col, T* vals, int32_t M, int32_t K, int6
   if (err & 1) return SNACK_E_NAN;
   if (err & 2) return SNACK_E_COO_RANGE;
   if (err & 4) return SNACK_E_COO_ORDER;
+  if (err & 16) return SNACK_E_HIP;  // a block count never appeared (bounded wait)
   if ((err & 8) || missing > 0) return SNACK_E_COUNT;
   if (fuse) {
     if (res_host[2] == INT32_MIN || res_host[3] == INT32_MIN) return SNACK_E_HIP;
