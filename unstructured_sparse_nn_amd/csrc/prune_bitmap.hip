@@ -19,7 +19,9 @@
 //            than are missing, so taking every new distinct position of the
 //            chunk (atomic test-and-set on G: order-free) gives exactly the
 //            first n_drop acceptances of the stream.  The first chunks ride
-//            on the select kernels; one workgroup finishes the tail;
+//            on the select kernels (chunk 0 bucketed by grid region and
+//            taken in LDS on grids up to 2^26 positions); one workgroup
+//            finishes the tail;
 //   write    new COO = the set bits of (S & ~D) | G in position order, a
 //            survivor's value being the old value at its rank in S.
 // One readback: the last kernel writes (error, positions missing) into the
@@ -1236,11 +1238,13 @@ __global__ __launch_bounds__(WT, LISTS ? 5 : 8) void k_bi_emit(
 // derived arrays of the new COO come straight from F and its per-word
 // prefix counts pw (no sort):
 //   rows     row_ptr[s] = pw[s * K/32] (nnz at s = M); the row tiles follow;
-//   columns  FT = F transposed in 32 x 32 bit tiles (32 ballots per wave give
-//            the 32 column words of two tiles); compacting FT in
-//            column-major order lists the entries column by column, rows
-//            ascending: row_t, col_ptr, and perm = each entry's rank in F,
-//            i.e. its row-major index.
+//   columns  up to FC_MAX_M rows, k_fp_colemit: one column word of every
+//            row staged in LDS, 64-row ballots per column; taller layouts:
+//            FT = F transposed in 32 x 32 bit tiles (32 ballots per wave
+//            give the 32 column words of two tiles), compacted in
+//            column-major order.  Either way the entries come column by
+//            column, rows ascending: row_t, col_ptr, and perm = each entry's
+//            rank in F, i.e. its row-major index.
 struct fuse_ptrs {
   int32_t *row_ptr, *rpart_seg, *rpart_nz, *rcut;
   int32_t *col_ptr, *perm, *row_t, *cpart_seg, *cpart_nz, *ccut;
